@@ -1,0 +1,10 @@
+"""CPU oracle for RLA-2 causal ReLU linear attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product path never does.
+"""
+from .rla2_oracle import (  # noqa: F401
+    DEFAULT_EPS, DEFAULT_RMS_EPS, DEFAULT_ROPE_BASE,
+    rms_norm, rope_frequencies, rope_rotate_half, feature_map, documents,
+    fwd, fwd_rows, fwd_recurrent, state_from_prefix, decode_step, decode_direct,
+)

@@ -1,0 +1,291 @@
+"""Pins for the CPU oracle: closed forms, invariants, special cases and an
+independent formulation (the literal recurrence), chosen so that a plausible
+mistake anywhere in the oracle (a dropped term, a wrong sign or index, a
+transposed operand, an off-by-one in the causal range) fails at least one.
+
+The pages print no worked numeric example for RLA-2 (see tests/golden/README.md),
+so no pin is a printed value; each cites the passage whose fact it checks.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+RNG = np.random.default_rng(12345)
+
+
+# --- RMSNorm (candle "常用层" page, RmsNorm; ruDNN README §7) -----------------
+
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.3, 5.0])
+def test_rms_norm_sum_of_squares(eps):
+    # With unit weights, sum(y^2) = d * m / (m + eps), m = mean(x^2): the page's
+    # remark that the sum of squares equals the element count minus the eps effect.
+    # Catches eps outside the sqrt, a sum in place of the mean, a dropped sqrt.
+    x = RNG.normal(size=(7, 12)) * RNG.uniform(0.1, 3.0, size=(7, 1))
+    y = oracle.rms_norm(x, np.ones(12), eps)
+    m = (x ** 2).mean(axis=1)
+    np.testing.assert_allclose((y ** 2).sum(axis=1), 12 * m / (m + eps), rtol=1e-13)
+
+
+def test_rms_norm_weight_and_scale():
+    # A constant vector normalises to sign(a) per channel, times the channel's
+    # weight (catches a weight applied to the wrong axis or before the norm).
+    g = RNG.uniform(0.5, 1.5, size=16)
+    for a in (-3.0, 0.25, 7.0):
+        y = oracle.rms_norm(np.full((1, 16), a), g, 0.0)
+        np.testing.assert_allclose(y[0], np.sign(a) * g, rtol=1e-14)
+    # no mean subtraction: a constant vector does not map to zero
+    x = RNG.normal(size=(3, 8))
+    np.testing.assert_allclose(oracle.rms_norm(5.0 * x, np.ones(8), 0.0),
+                               oracle.rms_norm(x, np.ones(8), 0.0), rtol=1e-14)
+
+
+# --- RoPE, rotate-half pairing (candle "常用层" page, rotary_emb) -------------
+
+def test_rope_pairing_sign_and_frequency():
+    # d = 4, base 1e4: theta_0 = 1, theta_1 = 1e4^(-1/2) = 0.01. Dimension j pairs
+    # with j + d/2 (not 2j with 2j+1), and x_j rotates towards +x_{j+d/2}.
+    e = np.eye(4)
+    out = oracle.rope_rotate_half(e, np.ones(4, dtype=int), 10000.0)
+    np.testing.assert_allclose(out[0], [math.cos(1), 0, math.sin(1), 0], atol=1e-15)
+    np.testing.assert_allclose(out[1], [0, math.cos(0.01), 0, math.sin(0.01)], atol=1e-15)
+    np.testing.assert_allclose(out[2], [-math.sin(1), 0, math.cos(1), 0], atol=1e-15)
+    np.testing.assert_allclose(out[3], [0, -math.sin(0.01), 0, math.cos(0.01)], atol=1e-15)
+
+
+def test_rope_is_complex_multiplication():
+    # Textbook form: (y_j + i y_{j+h}) * exp(i p theta_j), theta_j = exp(-(2j/d) ln base).
+    d, n, base = 16, 40, 500.0
+    y = RNG.normal(size=(n, d))
+    p = RNG.integers(0, 70000, size=n)
+    h = d // 2
+    theta = np.exp(-(2.0 * np.arange(h) / d) * math.log(base))
+    zc = (y[:, :h] + 1j * y[:, h:]) * np.exp(1j * p[:, None] * theta[None, :])
+    ref = np.concatenate([zc.real, zc.imag], axis=1)
+    np.testing.assert_allclose(oracle.rope_rotate_half(y, p, base), ref, rtol=1e-10, atol=1e-10)
+
+
+def test_rope_identity_norm_and_composition():
+    d = 8
+    y = RNG.normal(size=(5, d))
+    np.testing.assert_array_equal(oracle.rope_rotate_half(y, np.zeros(5, dtype=int)), y)
+    r = oracle.rope_rotate_half(y, np.arange(5) * 1000)
+    pair_norm = lambda a: a[:, :4] ** 2 + a[:, 4:] ** 2  # noqa: E731
+    np.testing.assert_allclose(pair_norm(r), pair_norm(y), rtol=1e-12)
+    two = oracle.rope_rotate_half(oracle.rope_rotate_half(y, np.full(5, 3)), np.full(5, 11))
+    np.testing.assert_allclose(two, oracle.rope_rotate_half(y, np.full(5, 14)), rtol=1e-12, atol=1e-12)
+
+
+def test_feature_map_relu_after_rope():
+    # RLA page §1/§3: RoPE comes before the ReLU. x = a e_0 at position 2 rotates to
+    # angle 2 rad (cos 2 < 0), so the ReLU must drop the first component but keep sin 2.
+    a, eps = 3.0, 1e-6
+    y0 = a / math.sqrt(a * a / 4 + eps)
+    out = oracle.feature_map(np.array([[a, 0, 0, 0]]), np.ones(4), np.array([2]), eps)
+    np.testing.assert_allclose(out[0], [0, 0, y0 * math.sin(2), 0], atol=1e-15)
+    assert (oracle.feature_map(RNG.normal(size=(50, 8)), np.ones(8), np.arange(50)) >= 0).all()
+
+
+# --- the attention itself (RLA page §2.1, §3, §4.1) --------------------------
+
+def _rand_case(B, H, L, d, seed, lengths=None):
+    r = np.random.default_rng(seed)
+    q, k, v = (r.normal(size=(B, H, L, d)) for _ in range(3))
+    gq, gk = r.uniform(0.5, 1.5, size=(H, d)), r.uniform(0.5, 1.5, size=(H, d))
+    cu = None if lengths is None else np.concatenate([[0], np.cumsum(lengths)])
+    return q, k, v, gq, gk, cu
+
+
+@pytest.mark.parametrize("B,H,L,d,lengths", [
+    (2, 2, 9, 4, None), (1, 3, 17, 8, [5, 1, 0, 11]), (1, 1, 12, 6, [12]), (3, 1, 6, 2, None)])
+def test_closed_form_matches_recurrence(B, H, L, d, lengths):
+    # Two formulations of the page: the state recurrence (§3) and the direct sum.
+    # Catches a transposed S (k (x) v vs v (x) k), an exclusive causal range, a wrong
+    # reset, or a denominator built from the wrong vector.
+    q, k, v, gq, gk, cu = _rand_case(B, H, L, d, 7 + L, lengths)
+    direct = oracle.fwd(q, k, v, gq, gk, cu, row_block=4)
+    rec, fS, fz = oracle.fwd_recurrent(q, k, v, gq, gk, cu)
+    np.testing.assert_allclose(direct, rec, rtol=1e-11, atol=1e-13)
+    S, z = oracle.state_from_prefix(k, v, gk, cu)
+    np.testing.assert_allclose(S, fS, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(z, fz, rtol=1e-11, atol=1e-13)
+
+
+def test_first_token_of_document():
+    # out_0 = s v_0 / (s + eps), s = q'_0 . k'_0 (inclusive causal range, eps added).
+    # q = k = [1,1,1,1] at position 0: q' = k' = r * 1 with r = 1/sqrt(1 + rms_eps).
+    d, rms_eps, eps = 4, 1e-6, 1e-4
+    q = np.ones((1, 1, 3, d))
+    v = RNG.normal(size=(1, 1, 3, d))
+    g = np.ones((1, d))
+    out = oracle.fwd(q, q, v, g, g, cu_seqlens=np.array([0, 1, 3]), eps=eps, rms_eps=rms_eps)
+    s = d / (1 + rms_eps)
+    np.testing.assert_allclose(out[0, 0, 0], s * v[0, 0, 0] / (s + eps), rtol=1e-14)
+    np.testing.assert_allclose(out[0, 0, 1], s * v[0, 0, 1] / (s + eps), rtol=1e-14)
+
+
+def test_constant_values_give_shrunk_average():
+    # v = u for every token: out_t = u * sum(s)/(sum(s) + eps), one scalar per row for
+    # all channels; with eps = 0 the output is exactly u (Sum denominator, RLA-2 §2.3/§3).
+    q, k, _, gq, gk, _ = _rand_case(1, 2, 20, 8, 99)
+    u = RNG.normal(size=8)
+    v = np.broadcast_to(u, q.shape).copy()
+    out = oracle.fwd(q, k, v, gq, gk)
+    ratio = out / u
+    alive = np.abs(ratio).max(axis=-1) > 0
+    assert alive.mean() > 0.5
+    np.testing.assert_allclose(ratio[alive], np.repeat(ratio[alive][:, :1], 8, axis=1), rtol=1e-12)
+    assert (ratio[alive] < 1).all() and (ratio[alive] > 0).all()
+    out0 = oracle.fwd(q, k, v, gq, gk, eps=0.0)
+    np.testing.assert_allclose(out0[alive], v[alive], rtol=1e-12)
+
+
+def test_output_is_convex_combination():
+    # With eps = 0 every output channel lies between the min and max of the values in
+    # its causal same-document window (non-negative weights summing to one).
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 40, 8, 5, [13, 27])
+    with np.errstate(invalid="ignore"):
+        out = oracle.fwd(q, k, v, gq, gk, cu, eps=0.0)
+    for (b, s0, s1) in oracle.documents(1, 40, cu):
+        for t in range(s0, s1):
+            w = v[b, :, s0:t + 1]
+            ok = np.abs(out[b, :, t]).sum(axis=-1) > 0
+            lo, hi = w.min(axis=1), w.max(axis=1)
+            assert (out[b, :, t][ok] >= lo[ok] - 1e-12).all()
+            assert (out[b, :, t][ok] <= hi[ok] + 1e-12).all()
+
+
+def _disjoint_support_inputs(L, d, seed):
+    # q' positive only on channels A, k' only on the complement: build the desired
+    # post-RoPE vectors u and undo the rotation (independent complex arithmetic).
+    # RMSNorm with unit weights only rescales, so the ReLU keeps exactly the chosen signs.
+    r = np.random.default_rng(seed)
+    h = d // 2
+    A = r.permutation(d)[: d // 2]
+    mask = np.zeros(d, bool)
+    mask[A] = True
+    theta = np.power(10000.0, -2.0 * np.arange(h) / d)
+
+    def unrotate(u, p):
+        zc = (u[:h] + 1j * u[h:]) * np.exp(-1j * p * theta)
+        return np.concatenate([zc.real, zc.imag])
+
+    q = np.zeros((1, 1, L, d))
+    k = np.zeros((1, 1, L, d))
+    for t in range(L):
+        mag = r.uniform(0.5, 2.0, size=(2, d))
+        uq = np.where(mask, mag[0], -mag[0])
+        uk = np.where(mask, -mag[1], mag[1])
+        q[0, 0, t], k[0, 0, t] = unrotate(uq, t), unrotate(uk, t)
+    return q, k, mask
+
+
+def test_disjoint_supports_give_exact_zero():
+    # RLA page §1/§2.2: with disjoint positive supports every score is exactly 0,
+    # so the output is exactly 0 and the values of zero-score tokens do not matter.
+    L, d = 24, 8
+    q, k, mask = _disjoint_support_inputs(L, d, 3)
+    g = np.ones((1, d))
+    qp = oracle.feature_map(q[0, 0], g[0], np.arange(L))
+    kp = oracle.feature_map(k[0, 0], g[0], np.arange(L))
+    assert (qp[:, ~mask] == 0).all() and (kp[:, mask] == 0).all()
+    v = RNG.normal(size=(1, 1, L, d))
+    out = oracle.fwd(q, k, v, g, g)
+    assert (out == 0).all()
+
+
+def test_document_isolation_and_causality():
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 30, 8, 11, [10, 8, 12])
+    base = oracle.fwd(q, k, v, gq, gk, cu)
+    # packed == each document run alone (positions restart at each document start)
+    for (b, s0, s1) in oracle.documents(1, 30, cu):
+        alone = oracle.fwd(q[:, :, s0:s1], k[:, :, s0:s1], v[:, :, s0:s1], gq, gk)
+        np.testing.assert_allclose(base[:, :, s0:s1], alone, rtol=1e-13, atol=1e-15)
+    # perturbing document 1 leaves documents 0 and 2 bitwise unchanged
+    q2, v2 = q.copy(), v.copy()
+    q2[:, :, 10:18] += 1.0
+    v2[:, :, 10:18] *= -3.0
+    pert = oracle.fwd(q2, k, v2, gq, gk, cu)
+    np.testing.assert_array_equal(pert[:, :, :10], base[:, :, :10])
+    np.testing.assert_array_equal(pert[:, :, 18:], base[:, :, 18:])
+    # perturbing tokens after t leaves rows <= t unchanged
+    k3, v3 = k.copy(), v.copy()
+    k3[:, :, 25:] += 2.0
+    v3[:, :, 25:] -= 1.0
+    fut = oracle.fwd(q, k3, v3, gq, gk, cu)
+    np.testing.assert_allclose(fut[:, :, :25], base[:, :, :25], rtol=1e-14, atol=0)
+
+
+def test_fwd_rows_matches_full():
+    q, k, v, gq, gk, cu = _rand_case(1, 3, 50, 8, 21, [20, 3, 27])
+    full = oracle.fwd(q, k, v, gq, gk, cu)
+    rows = [0, 1, 19, 20, 22, 23, 30, 49]
+    for h in range(3):
+        np.testing.assert_allclose(oracle.fwd_rows(q, k, v, gq, gk, 0, h, rows, cu),
+                                   full[0, h, rows], rtol=1e-13, atol=1e-15)
+    q, k, v, gq, gk, _ = _rand_case(2, 2, 33, 4, 22)
+    full = oracle.fwd(q, k, v, gq, gk)
+    np.testing.assert_allclose(oracle.fwd_rows(q, k, v, gq, gk, 1, 1, [32, 0, 7]),
+                               full[1, 1, [0, 7, 32]], rtol=1e-13)
+
+
+def test_decode_step_equals_forward_last_row():
+    # RLA page §4.2/§4.4: the KV-cache path (state from the prefix, then one
+    # forward_step) reproduces the full forward's last row.
+    H, d = 2, 8
+    lens = [5, 1, 9]
+    N = len(lens)
+    r = np.random.default_rng(31)
+    gq, gk = r.uniform(0.5, 1.5, size=(H, d)), r.uniform(0.5, 1.5, size=(H, d))
+    seqs = [r.normal(size=(3, H, n + 1, d)) for n in lens]
+    pk = np.concatenate([s[1][:, :-1] for s in seqs], axis=1)[None]
+    pv = np.concatenate([s[2][:, :-1] for s in seqs], axis=1)[None]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S0, z0 = oracle.state_from_prefix(pk, pv, gk, cu)
+    qn = np.stack([s[0][:, -1] for s in seqs])
+    kn = np.stack([s[1][:, -1] for s in seqs])
+    vn = np.stack([s[2][:, -1] for s in seqs])
+    out, S1, z1 = oracle.decode_step(qn, kn, vn, np.array(lens), gq, gk, S0, z0)
+    for n, s in enumerate(seqs):
+        full = oracle.fwd(s[0][None], s[1][None], s[2][None], gq, gk)
+        np.testing.assert_allclose(out[n], full[0, :, -1], rtol=1e-12, atol=1e-14)
+        Sf, zf = oracle.state_from_prefix(s[1][None], s[2][None], gk)
+        np.testing.assert_allclose(S1[n], Sf[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(z1[n], zf[0], rtol=1e-12, atol=1e-14)
+        for h in range(H):
+            o2, S2, z2 = oracle.decode_direct(s[1][h, :-1], s[2][h, :-1], s[0][h, -1], s[1][h, -1],
+                                              s[2][h, -1], gq[h], gk[h])
+            np.testing.assert_allclose(o2, out[n, h], rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(S2, S1[n, h], rtol=1e-12, atol=1e-14)
+
+
+def test_documents_contract():
+    assert oracle.documents(3, 5) == [(0, 0, 5), (1, 0, 5), (2, 0, 5)]
+    assert oracle.documents(1, 7, [0, 0, 3, 7]) == [(0, 0, 0), (0, 0, 3), (0, 3, 7)]
+    for bad in ([1, 7], [0, 5], [0, 4, 3, 7]):
+        with pytest.raises(ValueError):
+            oracle.documents(1, 7, bad)
+
+
+# --- workloads (seeded generator module; no method arithmetic) ---------------
+
+def test_workload_generators_are_seeded_and_shaped():
+    a, b = workloads.c1_fp32_small(), workloads.c1_fp32_small()
+    assert a.q.shape == (1, 2, 256, 32) and a.q.dtype == torch.float32
+    assert torch.equal(a.q, b.q) and torch.equal(a.v, b.v)
+    assert torch.equal(a.gamma_q, torch.ones(2, 32))
+    lens = workloads.c3_lengths()
+    assert sum(lens) == 16384 and all(64 <= n <= 4096 for n in lens[:-1]) and lens[-1] >= 1
+    small = workloads.fwd_inputs(1, 2, 64, 128, seed=4, bias_frac=0.1)
+    assert small.q.dtype == torch.bfloat16
+    m = workloads.channel_mask(128, 0.1, 4, workloads.S_MASK_Q)
+    assert len(m) == 13
+    # the shifted channels have mean close to -1, the others close to 0
+    qf = small.q.float()
+    assert abs(qf[..., m].mean().item() + 1.0) < 0.1
+    dec = workloads.decode_inputs(4, 2, 16, 50, seed=5)
+    assert int(dec.cu_prefix[-1]) == dec.prefix_k.shape[2] == int(dec.prefix_lengths.sum())
