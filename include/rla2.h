@@ -1,0 +1,162 @@
+/*
+ * rla2.h -- C ABI of librla2.so: RLA-2 causal ReLU linear attention on gfx950.
+ *
+ * The method (neuralnet.cpp development page "线性注意力家族：RLA / RAPT / RLA-2 与
+ * GPU 落地", called the RLA page below):
+ *   q' = ReLU(RoPE(RMSNorm(q))), k' = ReLU(RoPE(RMSNorm(k)))   (RLA page §3; §1: no
+ *        1/sqrt(d) scaling, per-head RMSNorm, RoPE before the ReLU; v is untouched)
+ *   S_t = S_{t-1} + k'_t (x) v_t   (d x d),   z_t = z_{t-1} + k'_t   (RLA page §3)
+ *   out_t = q'_t S_t / (q'_t . z_t + eps)                             (RLA page §3)
+ * with S and z cleared at every document start (RLA page §2.2 and §4.1).
+ * RMSNorm: x * gamma / sqrt(mean(x^2) + rms_eps), fp32 statistics, F32 weight
+ * (ruDNN README §7; candle "常用层" page, RmsNorm). RoPE: rotate-half pairing of
+ * dimension j with j + d/2, angle p * base^(-2j/d) (candle "常用层" page,
+ * rotary_emb). Positions restart at 0 at each document start.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE pointers, dense row-major (C order), no strides,
+ *    16-byte aligned (RLA2_ERR_MISALIGNED otherwise; cu_seqlens and positions
+ *    need only 4-byte alignment). Descriptors, sizes and scalars are host values.
+ *  - Activations q, k, v, out use the element type given by rla2_dtype; RMSNorm
+ *    weights and states are always fp32. Every reduction accumulates in fp32.
+ *  - Every call validates all host-visible arguments first. On any error nothing
+ *    is enqueued and no output is touched. On RLA2_OK the work is enqueued on
+ *    `stream` (asynchronous; no host synchronisation) except where noted.
+ *  - The library never allocates device memory and keeps no per-call state.
+ *    The caller owns every buffer, including the workspace, and must keep them
+ *    alive until the stream has executed the call.
+ *  - `out` must not overlap any input, state or workspace (RLA2_ERR_ALIAS).
+ *    q, k and v may overlap each other (they are only read).
+ *  - NaN/Inf inputs are not checked; they propagate to the outputs.
+ *  - RLA2_ERR_HIP means a HIP launch failed; outputs are then undefined.
+ *  - Supported head dimensions: 32, 64, 128. Supported chunk: 64.
+ */
+#ifndef RLA2_H_
+#define RLA2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rla2_status {
+  RLA2_OK = 0,
+  RLA2_ERR_NULL_POINTER = 1, /* a required pointer is NULL                        */
+  RLA2_ERR_BAD_SHAPE = 2,    /* negative size, or a shape rule below is broken     */
+  RLA2_ERR_UNSUPPORTED = 3,  /* head dim, dtype or chunk outside the supported set */
+  RLA2_ERR_BAD_VALUE = 4,    /* eps/rms_eps/rope_base not finite and > 0, bad env  */
+  RLA2_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the queried size    */
+  RLA2_ERR_ALIAS = 6,        /* an output overlaps an input or another output      */
+  RLA2_ERR_HIP = 7,          /* a HIP runtime call failed                          */
+  RLA2_ERR_BAD_SEQLENS = 8,  /* RLA2_VALIDATE=1 found a cu_seqlens contract breach */
+  RLA2_ERR_MISALIGNED = 9    /* a tensor pointer is not 16-byte aligned             */
+} rla2_status;
+
+typedef enum rla2_dtype { RLA2_F32 = 0, RLA2_BF16 = 1 } rla2_dtype;
+
+/*
+ * Shape and options of a chunked forward or a state build.
+ *  B, H, L, d   logical [B, H, L, d] of q, k, v (and out). With cu_seqlens the
+ *               input is packed: B must be 1 and L is the total token count T.
+ *  dtype        element type of q, k, v, out (rla2_dtype).
+ *  chunk        tokens per chunk of the chunked evaluation; must be 64.
+ *  seg_chunks   chunks per sequential segment of the sweep (a tuning knob that
+ *               only changes fp32 summation order); 0 selects it automatically.
+ *  eps          denominator offset, RLA page §3 uses 1e-4. Finite, > 0.
+ *  rms_eps      RMSNorm epsilon (inside the square root). Finite, > 0.
+ *  rope_base    RoPE base (10000 on the RLA-2 workloads). Finite, > 0.
+ *  cu_seqlens   NULL: each of the B rows is one document [0, L).
+ *               Otherwise DEVICE int32[n_docs + 1] prefix sums of document lengths:
+ *               cu[0] == 0, non-decreasing, cu[n_docs] == L (the contract of the
+ *               CANN ops-transformer page, Compressor constraints). Contents are a
+ *               caller contract, checked (with a host synchronisation) only when
+ *               the environment variable RLA2_VALIDATE=1; out-of-range values are
+ *               clamped to [0, L] so they can never cause an out-of-bounds access.
+ *               Zero-length documents are allowed.
+ *  n_docs       number of documents when cu_seqlens != NULL (>= 0); ignored
+ *               (treated as B) when cu_seqlens == NULL.
+ * The number of documents N is n_docs with cu_seqlens, B without.
+ */
+typedef struct rla2_fwd_desc {
+  int32_t B, H, L, d;
+  int32_t dtype;
+  int32_t chunk;
+  int32_t seg_chunks;
+  float eps, rms_eps, rope_base;
+  const int32_t* cu_seqlens;
+  int32_t n_docs;
+} rla2_fwd_desc;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* rla2_status_string(rla2_status status);
+
+/* ABI version of this header (bumped on any layout or signature change). */
+int32_t rla2_abi_version(void);
+
+/*
+ * Workspace bytes rla2_fwd_chunked needs for `desc` (host call, no GPU work).
+ * Writes *bytes; returns the same validation status the forward would.
+ */
+rla2_status rla2_fwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
+
+/*
+ * Chunked RLA-2 causal forward (RLA page §3 formula; the chunking is the
+ * associativity of §1: a d x d state carried across chunks, each chunk's own
+ * causal part formed directly).
+ *  q, k, v      [B, H, L, d] dtype, read only.
+ *  gamma_q/k    [H, d] fp32 RMSNorm weights of q and k.
+ *  out          [B, H, L, d] dtype, written (every row of every document).
+ *  final_S      optional [N, H, d, d] fp32: each document's state after its last
+ *               token, S[a][c] = sum_i k'_i[a] v_i[c]; NULL = not exported.
+ *  final_z      optional [N, H, d] fp32, z = sum_i k'_i; NULL = not exported.
+ *  workspace    device scratch of at least rla2_fwd_workspace_size() bytes,
+ *               256-byte aligned; contents on entry are ignored.
+ * L == 0 or N == 0 is a valid no-op (final states of empty documents are 0).
+ */
+rla2_status rla2_fwd_chunked(const rla2_fwd_desc* desc, const void* q, const void* k,
+                             const void* v, const float* gamma_q, const float* gamma_k,
+                             void* out, float* final_S, float* final_z, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes rla2_state_from_prefix needs for `desc`. */
+rla2_status rla2_state_from_prefix_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
+
+/*
+ * State of every document after its last token, from its keys and values:
+ * S = sum_i k'_i (x) v_i, z = sum_i k'_i (RLA page §3 state; §4.2 forward_step
+ * keeps exactly this pair as its cache). q is not needed.
+ *  k, v     [B, H, L, d] dtype (packed [1, H, T, d] with cu_seqlens).
+ *  gamma_k  [H, d] fp32.
+ *  S        [N, H, d, d] fp32, written.   z  [N, H, d] fp32, written.
+ * desc->eps is validated but unused.
+ */
+rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, const void* v,
+                                   const float* gamma_k, float* S, float* z, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * One decode step for N sequences (RLA page §4.2 forward_step): the feature map
+ * of the new token at its position, then the state update first
+ * (S += k' (x) v, z += k'), then the read-out out = q' S / (q' . z + eps).
+ *  q, k, v     [N, H, d] dtype, the new token of each sequence.
+ *  positions   DEVICE int32[N]: position of the new token (its prefix length),
+ *              >= 0 (negative values are treated as 0).
+ *  gamma_q/k   [H, d] fp32.
+ *  S, z        [N, H, d, d], [N, H, d] fp32, updated IN PLACE.
+ *  out         [N, H, d] dtype, written.
+ * N == 0 is a valid no-op.
+ */
+rla2_status rla2_decode_step(int32_t N, int32_t H, int32_t d, int32_t dtype, const void* q,
+                             const void* k, const void* v, const int32_t* positions,
+                             const float* gamma_q, const float* gamma_k, float rms_eps,
+                             float rope_base, float eps, float* S, float* z, void* out,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLA2_H_ */

@@ -1,0 +1,197 @@
+"""Python binding of librla2.so (RLA-2 causal ReLU linear attention on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of librla2.so. PyTorch is used for device memory and the current
+stream. There is no CPU path: CPU tensors or a missing library raise.
+
+Entry points (same names as the C ABI in include/rla2.h):
+  fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, ...)        -> rla2_fwd_chunked
+  state_from_prefix(k, v, gamma_k, cu_seqlens=None, ...)      -> rla2_state_from_prefix
+  decode_step(q, k, v, positions, gamma_q, gamma_k, S, z,...) -> rla2_decode_step
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["fwd", "state_from_prefix", "decode_step", "fwd_workspace_size", "lib", "Rla2Error",
+           "FwdDesc", "LIB_PATH", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librla2.so")
+
+STATUS = {0: "RLA2_OK", 1: "RLA2_ERR_NULL_POINTER", 2: "RLA2_ERR_BAD_SHAPE", 3: "RLA2_ERR_UNSUPPORTED",
+          4: "RLA2_ERR_BAD_VALUE", 5: "RLA2_ERR_WORKSPACE", 6: "RLA2_ERR_ALIAS", 7: "RLA2_ERR_HIP",
+          8: "RLA2_ERR_BAD_SEQLENS", 9: "RLA2_ERR_MISALIGNED"}
+F32, BF16 = 0, 1
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class Rla2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib().rla2_status_string(status).decode()}")
+
+
+class FwdDesc(ctypes.Structure):
+    """Mirror of ``rla2_fwd_desc``."""
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
+                ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_SZ = ctypes.POINTER(ctypes.c_size_t)
+_DESC = ctypes.POINTER(FwdDesc)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librla2.so with its C signatures (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m linear_attention_rla_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.rla2_status_string.restype = ctypes.c_char_p
+        L.rla2_status_string.argtypes = [ctypes.c_int]
+        L.rla2_abi_version.restype = ctypes.c_int32
+        L.rla2_abi_version.argtypes = []
+        for name in ("rla2_fwd_workspace_size", "rla2_state_from_prefix_workspace_size"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = [_DESC, _SZ]
+        L.rla2_fwd_chunked.restype = ctypes.c_int
+        L.rla2_fwd_chunked.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.rla2_state_from_prefix.restype = ctypes.c_int
+        L.rla2_state_from_prefix.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.rla2_decode_step.restype = ctypes.c_int
+        L.rla2_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                       _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P]
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name: str, t: torch.Tensor, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def make_desc(B, H, L, d, dtype, cu_seqlens=None, n_docs=0, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
+              rope_base=10000.0) -> FwdDesc:
+    return FwdDesc(B, H, L, d, dtype, chunk, seg_chunks, eps, rms_eps, rope_base,
+                   None if cu_seqlens is None else cu_seqlens.data_ptr(), n_docs)
+
+
+def _fwd_desc(x: torch.Tensor, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base) -> FwdDesc:
+    if x.dim() != 4:
+        raise ValueError("expected [B, H, L, d]")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    B, H, L, d = x.shape
+    n_docs = 0
+    if cu_seqlens is not None:
+        _check_dev("cu_seqlens", cu_seqlens, torch.int32)
+        n_docs = cu_seqlens.numel() - 1
+    return make_desc(B, H, L, d, _DTYPES[x.dtype], cu_seqlens, n_docs, chunk, seg_chunks, eps, rms_eps, rope_base)
+
+
+def fwd_workspace_size(desc: FwdDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().rla2_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st:
+        raise Rla2Error(st, "rla2_fwd_workspace_size")
+    return n.value
+
+
+def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
+        rope_base=10000.0, return_final_state=False, out=None, workspace=None):
+    """Chunked RLA-2 causal forward. Returns ``out`` or ``(out, final_S, final_z)``."""
+    for n_, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n_, t, q.dtype)
+    _check_dev("gamma_q", gamma_q, torch.float32)
+    _check_dev("gamma_k", gamma_k, torch.float32)
+    desc = _fwd_desc(q, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base)
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v shapes differ")
+    if out is None:
+        out = torch.empty_like(q)
+    N = desc.n_docs if cu_seqlens is not None else desc.B
+    fS = fz = None
+    if return_final_state:
+        fS = torch.empty(N, desc.H, desc.d, desc.d, dtype=torch.float32, device=q.device)
+        fz = torch.empty(N, desc.H, desc.d, dtype=torch.float32, device=q.device)
+    nbytes = fwd_workspace_size(desc)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    st = lib().rla2_fwd_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q), _ptr(gamma_k),
+                                _ptr(out), _ptr(fS), _ptr(fz), _ptr(workspace), workspace.numel(), _stream(q.device))
+    if st:
+        raise Rla2Error(st, "rla2_fwd_chunked")
+    return (out, fS, fz) if return_final_state else out
+
+
+def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, rms_eps=1e-6,
+                      rope_base=10000.0, S=None, z=None, workspace=None):
+    """Per-document state after its last token. Returns ``(S, z)``."""
+    _check_dev("k", k)
+    _check_dev("v", v, k.dtype)
+    _check_dev("gamma_k", gamma_k, torch.float32)
+    desc = _fwd_desc(k, cu_seqlens, chunk, seg_chunks, 1e-4, rms_eps, rope_base)
+    N = desc.n_docs if cu_seqlens is not None else desc.B
+    if S is None:
+        S = torch.empty(N, desc.H, desc.d, desc.d, dtype=torch.float32, device=k.device)
+    if z is None:
+        z = torch.empty(N, desc.H, desc.d, dtype=torch.float32, device=k.device)
+    n = ctypes.c_size_t(0)
+    st = lib().rla2_state_from_prefix_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st:
+        raise Rla2Error(st, "rla2_state_from_prefix_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=k.device)
+    st = lib().rla2_state_from_prefix(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(gamma_k), _ptr(S), _ptr(z),
+                                      _ptr(workspace), workspace.numel(), _stream(k.device))
+    if st:
+        raise Rla2Error(st, "rla2_state_from_prefix")
+    return S, z
+
+
+def decode_step(q, k, v, positions, gamma_q, gamma_k, S, z, *, eps=1e-4, rms_eps=1e-6, rope_base=10000.0,
+                out=None):
+    """One decode token per sequence; updates ``S``, ``z`` in place. Returns ``out``."""
+    for n_, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n_, t, q.dtype)
+    if q.dim() != 3 or q.dtype not in _DTYPES:
+        raise ValueError("expected q, k, v [N, H, d] of float32 or bfloat16")
+    _check_dev("positions", positions, torch.int32)
+    _check_dev("S", S, torch.float32)
+    _check_dev("z", z, torch.float32)
+    _check_dev("gamma_q", gamma_q, torch.float32)
+    _check_dev("gamma_k", gamma_k, torch.float32)
+    N, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or S.shape != (N, H, d, d) or z.shape != (N, H, d):
+        raise ValueError("shape mismatch between q, k, v, S, z")
+    if positions.shape != (N,) or gamma_q.shape != (H, d) or gamma_k.shape != (H, d):
+        raise ValueError("shape mismatch of positions or RMSNorm weights")
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib().rla2_decode_step(N, H, d, _DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(positions),
+                                _ptr(gamma_q), _ptr(gamma_k), rms_eps, rope_base, eps, _ptr(S), _ptr(z), _ptr(out),
+                                _stream(q.device))
+    if st:
+        raise Rla2Error(st, "rla2_decode_step")
+    return out

@@ -1,0 +1,268 @@
+// Host side of librla2.so: argument validation, workspace planning and the
+// extern "C" entry points declared in include/rla2.h. Every check runs before
+// any HIP call, so every error path can be exercised on a machine with no GPU.
+#include "rla2.h"
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <initializer_list>
+#include <vector>
+
+#include "rla2_internal.h"
+
+namespace {
+
+using rla2::Plan;
+
+constexpr int32_t kAbiVersion = 1;
+
+bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+size_t align_up(size_t x) { return (x + rla2::kAlign - 1) / rla2::kAlign * rla2::kAlign; }
+size_t elem_bytes(int dtype) { return dtype == RLA2_F32 ? 4 : 2; }
+
+// RLA2_VALIDATE: unset or "0" = off, "1" = on, anything else is an error
+// (the convention of the ruDNN README §11 environment flags). Read once.
+int validate_mode() {
+  static const int mode = [] {
+    const char* s = std::getenv("RLA2_VALIDATE");
+    if (s == nullptr || std::strcmp(s, "0") == 0) return 0;
+    if (std::strcmp(s, "1") == 0) return 1;
+    return -1;
+  }();
+  return mode;
+}
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+
+bool misaligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p != nullptr && (reinterpret_cast<uintptr_t>(p) % 16) != 0) return true;
+  return false;
+}
+
+bool overlap(Range a, Range b) {
+  if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+  auto x = reinterpret_cast<uintptr_t>(a.p), y = reinterpret_cast<uintptr_t>(b.p);
+  return x < y + b.n && y < x + a.n;
+}
+
+// Shared checks of a forward / state-build descriptor. Fills the plan on success.
+rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
+  if (d == nullptr) return RLA2_ERR_NULL_POINTER;
+  if (d->B < 0 || d->H < 0 || d->L < 0 || d->d < 0) return RLA2_ERR_BAD_SHAPE;
+  if (d->cu_seqlens != nullptr && (d->B != 1 || d->n_docs < 0)) return RLA2_ERR_BAD_SHAPE;
+  if (!supported_d(d->d)) return RLA2_ERR_UNSUPPORTED;
+  if (d->dtype != RLA2_F32 && d->dtype != RLA2_BF16) return RLA2_ERR_UNSUPPORTED;
+  if (d->chunk != rla2::kChunk) return RLA2_ERR_UNSUPPORTED;
+  if (d->seg_chunks < 0 || d->seg_chunks > (1 << 20)) return RLA2_ERR_BAD_VALUE;
+  if (!finite_pos(d->eps) || !finite_pos(d->rms_eps) || !finite_pos(d->rope_base))
+    return RLA2_ERR_BAD_VALUE;
+  if (validate_mode() < 0) return RLA2_ERR_BAD_VALUE;
+  // every token index and every segment index must stay within int32 on device
+  const long long tokens = (long long)d->B * d->L;
+  if (tokens > INT32_MAX || (long long)d->B * d->H > INT32_MAX) return RLA2_ERR_BAD_SHAPE;
+  if (d->H > 65535) return RLA2_ERR_BAD_SHAPE;  // heads are the grid's y dimension
+
+  p->B = d->B;
+  p->H = d->H;
+  p->L = d->L;
+  p->d = d->d;
+  p->dtype = d->dtype;
+  p->packed = d->cu_seqlens != nullptr;
+  p->n_docs = p->packed ? d->n_docs : d->B;
+  const int rows = p->packed ? 1 : p->B;
+  const long long L = p->L;
+  // Segment length: the sweep kernels run one workgroup per (segment, head), so
+  // pick the longest segment that still gives ~1024 workgroups (fewer segments
+  // mean less fp32 state traffic through the inter-segment scan).
+  int seg = 0;
+  if (d->seg_chunks > 0) {
+    seg = d->seg_chunks * rla2::kChunk;
+  } else {
+    seg = rla2::kChunk;
+    for (int cand = 4096; cand >= rla2::kChunk; cand /= 2) {
+      long long wg = (long long)rows * ((L + cand - 1) / cand) * (p->H > 0 ? p->H : 1);
+      if (wg >= 1024) { seg = cand; break; }
+    }
+  }
+  p->seg_len = seg;
+  long long nseg = p->packed ? (L + seg - 1) / seg + p->n_docs : (long long)rows * ((L + seg - 1) / seg);
+  if (p->n_docs == 0 || p->H == 0) nseg = 0;
+  if (nseg > INT32_MAX / 8) return RLA2_ERR_BAD_SHAPE;
+  p->n_seg_max = (int)nseg;
+  p->n_hi = (int)((L + rla2::kChunk - 1) / rla2::kChunk);
+  if (p->n_hi < 1) p->n_hi = 1;
+
+  const size_t half = (size_t)p->d / 2;
+  const size_t rec = (size_t)p->d * p->d + p->d;
+  size_t off = 0;
+  p->off_tab = off;
+  off = align_up(off + (size_t)p->n_seg_max * rla2::kTabInts * 4);
+  p->off_docoff = off;
+  off = align_up(off + ((size_t)p->n_docs + 1) * 4);
+  p->off_nseg = off;
+  off = align_up(off + 4);
+  p->off_rope_lo = off;
+  off = align_up(off + (size_t)rla2::kChunk * half * 8);
+  p->off_rope_hi = off;
+  off = align_up(off + (size_t)p->n_hi * half * 8);
+  p->off_states = off;
+  off = align_up(off + (size_t)p->n_seg_max * p->H * rec * 4);
+  p->bytes = (p->n_docs == 0 || p->H == 0) ? 0 : off;  // no documents or heads: nothing to run
+  return RLA2_OK;
+}
+
+// Synchronous check of the cu_seqlens contract (only with RLA2_VALIDATE=1).
+rla2_status check_seqlens(const Plan& p, const int32_t* cu, hipStream_t stream) {
+  std::vector<int32_t> h((size_t)p.n_docs + 1);
+  if (hipStreamSynchronize(stream) != hipSuccess) return RLA2_ERR_HIP;
+  if (hipMemcpy(h.data(), cu, h.size() * 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return RLA2_ERR_HIP;
+  if (h[0] != 0 || h.back() != p.L) return RLA2_ERR_BAD_SEQLENS;
+  for (size_t j = 1; j < h.size(); ++j)
+    if (h[j] < h[j - 1]) return RLA2_ERR_BAD_SEQLENS;
+  return RLA2_OK;
+}
+
+rla2_status finish(hipError_t e) {
+  if (e != hipSuccess) return RLA2_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? RLA2_OK : RLA2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rla2_status_string(rla2_status s) {
+  switch (s) {
+    case RLA2_OK: return "RLA2_OK";
+    case RLA2_ERR_NULL_POINTER: return "RLA2_ERR_NULL_POINTER: a required pointer is NULL";
+    case RLA2_ERR_BAD_SHAPE: return "RLA2_ERR_BAD_SHAPE: negative size or inconsistent shape";
+    case RLA2_ERR_UNSUPPORTED: return "RLA2_ERR_UNSUPPORTED: head dim, dtype or chunk not supported";
+    case RLA2_ERR_BAD_VALUE: return "RLA2_ERR_BAD_VALUE: eps, rms_eps, rope_base or option out of range";
+    case RLA2_ERR_WORKSPACE: return "RLA2_ERR_WORKSPACE: workspace missing or too small";
+    case RLA2_ERR_ALIAS: return "RLA2_ERR_ALIAS: an output overlaps another buffer";
+    case RLA2_ERR_HIP: return "RLA2_ERR_HIP: a HIP runtime call failed";
+    case RLA2_ERR_BAD_SEQLENS: return "RLA2_ERR_BAD_SEQLENS: cu_seqlens breaks its contract";
+    case RLA2_ERR_MISALIGNED: return "RLA2_ERR_MISALIGNED: a tensor pointer is not 16-byte aligned";
+  }
+  return "RLA2_ERR_UNKNOWN";
+}
+
+int32_t rla2_abi_version(void) { return kAbiVersion; }
+
+rla2_status rla2_fwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return RLA2_ERR_NULL_POINTER;
+  Plan p;
+  rla2_status st = plan_desc(desc, &p);
+  if (st != RLA2_OK) return st;
+  *bytes = p.bytes;
+  return RLA2_OK;
+}
+
+rla2_status rla2_state_from_prefix_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
+  return rla2_fwd_workspace_size(desc, bytes);
+}
+
+rla2_status rla2_fwd_chunked(const rla2_fwd_desc* desc, const void* q, const void* k,
+                             const void* v, const float* gamma_q, const float* gamma_k,
+                             void* out, float* final_S, float* final_z, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  rla2_status st = plan_desc(desc, &p);
+  if (st != RLA2_OK) return st;
+  const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
+  const size_t gam = (size_t)p.H * p.d * 4;
+  const size_t fsb = (size_t)p.n_docs * p.H * p.d * p.d * 4;
+  const size_t fzb = (size_t)p.n_docs * p.H * p.d * 4;
+  if (act > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr))
+    return RLA2_ERR_NULL_POINTER;
+  if (gam > 0 && act > 0 && (gamma_q == nullptr || gamma_k == nullptr)) return RLA2_ERR_NULL_POINTER;
+  if (p.packed && desc->cu_seqlens == nullptr) return RLA2_ERR_NULL_POINTER;
+  if (p.bytes > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return RLA2_ERR_WORKSPACE;
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
+    return RLA2_ERR_WORKSPACE;
+  if (misaligned({q, k, v, out, gamma_q, gamma_k, final_S, final_z})) return RLA2_ERR_MISALIGNED;
+  const Range o{out, act}, fs{final_S, fsb}, fz{final_z, fzb}, ws{workspace, p.bytes};
+  const Range ins[] = {{q, act}, {k, act}, {v, act}, {gamma_q, gam}, {gamma_k, gam},
+                       {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4}};
+  for (const Range& r : ins)
+    if (overlap(o, r) || overlap(fs, r) || overlap(fz, r)) return RLA2_ERR_ALIAS;
+  if (overlap(o, fs) || overlap(o, fz) || overlap(fs, fz) || overlap(o, ws) || overlap(fs, ws) ||
+      overlap(fz, ws))
+    return RLA2_ERR_ALIAS;
+  if (p.packed && validate_mode() == 1) {
+    st = check_seqlens(p, desc->cu_seqlens, stream);
+    if (st != RLA2_OK) return st;
+  }
+  if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
+  rla2::FwdArgs a{desc->cu_seqlens, q, k, v, gamma_q, gamma_k, out, final_S, final_z,
+                  desc->eps, desc->rms_eps, desc->rope_base, static_cast<char*>(workspace)};
+  return finish(rla2::launch_chunked(p, a, stream));
+}
+
+rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, const void* v,
+                                   const float* gamma_k, float* S, float* z, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  rla2_status st = plan_desc(desc, &p);
+  if (st != RLA2_OK) return st;
+  const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
+  const size_t gam = (size_t)p.H * p.d * 4;
+  const size_t sb = (size_t)p.n_docs * p.H * p.d * p.d * 4;
+  const size_t zb = (size_t)p.n_docs * p.H * p.d * 4;
+  if (act > 0 && (k == nullptr || v == nullptr || gamma_k == nullptr)) return RLA2_ERR_NULL_POINTER;
+  if (sb > 0 && (S == nullptr || z == nullptr)) return RLA2_ERR_NULL_POINTER;
+  if (p.packed && desc->cu_seqlens == nullptr) return RLA2_ERR_NULL_POINTER;
+  if (p.bytes > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return RLA2_ERR_WORKSPACE;
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
+    return RLA2_ERR_WORKSPACE;
+  if (misaligned({k, v, gamma_k, S, z})) return RLA2_ERR_MISALIGNED;
+  const Range rs{S, sb}, rz{z, zb}, ws{workspace, p.bytes};
+  const Range ins[] = {{k, act}, {v, act}, {gamma_k, gam}, {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4}};
+  for (const Range& r : ins)
+    if (overlap(rs, r) || overlap(rz, r)) return RLA2_ERR_ALIAS;
+  if (overlap(rs, rz) || overlap(rs, ws) || overlap(rz, ws)) return RLA2_ERR_ALIAS;
+  if (p.packed && validate_mode() == 1) {
+    st = check_seqlens(p, desc->cu_seqlens, stream);
+    if (st != RLA2_OK) return st;
+  }
+  if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
+  rla2::FwdArgs a{desc->cu_seqlens, nullptr, k, v, nullptr, gamma_k, nullptr, S, z,
+                  desc->eps, desc->rms_eps, desc->rope_base, static_cast<char*>(workspace)};
+  return finish(rla2::launch_chunked(p, a, stream));
+}
+
+rla2_status rla2_decode_step(int32_t N, int32_t H, int32_t d, int32_t dtype, const void* q,
+                             const void* k, const void* v, const int32_t* positions,
+                             const float* gamma_q, const float* gamma_k, float rms_eps,
+                             float rope_base, float eps, float* S, float* z, void* out,
+                             hipStream_t stream) {
+  if (N < 0 || H < 0 || d < 0) return RLA2_ERR_BAD_SHAPE;
+  if (!supported_d(d)) return RLA2_ERR_UNSUPPORTED;
+  if (dtype != RLA2_F32 && dtype != RLA2_BF16) return RLA2_ERR_UNSUPPORTED;
+  if (!finite_pos(eps) || !finite_pos(rms_eps) || !finite_pos(rope_base)) return RLA2_ERR_BAD_VALUE;
+  if ((long long)N * H > INT32_MAX) return RLA2_ERR_BAD_SHAPE;
+  const size_t act = (size_t)N * H * d * elem_bytes(dtype);
+  if (act == 0) return RLA2_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || positions == nullptr || gamma_q == nullptr ||
+      gamma_k == nullptr || S == nullptr || z == nullptr || out == nullptr)
+    return RLA2_ERR_NULL_POINTER;
+  if (misaligned({q, k, v, out, gamma_q, gamma_k, S, z})) return RLA2_ERR_MISALIGNED;
+  const size_t sb = (size_t)N * H * d * d * 4, zb = (size_t)N * H * d * 4, gam = (size_t)H * d * 4;
+  const Range o{out, act}, rs{S, sb}, rz{z, zb};
+  const Range ins[] = {{q, act}, {k, act}, {v, act}, {positions, (size_t)N * 4}, {gamma_q, gam},
+                       {gamma_k, gam}};
+  for (const Range& r : ins)
+    if (overlap(o, r) || overlap(rs, r) || overlap(rz, r)) return RLA2_ERR_ALIAS;
+  if (overlap(o, rs) || overlap(o, rz) || overlap(rs, rz)) return RLA2_ERR_ALIAS;
+  return finish(rla2::launch_decode(N, H, d, dtype, q, k, v, positions, gamma_q, gamma_k, rms_eps,
+                                    rope_base, eps, S, z, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal interface between the host entry points (rla2_api.cpp) and the
+// kernel launchers (rla2_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace rla2 {
+
+constexpr int kChunk = 64;          // tokens per chunk (one MFMA-tiled block)
+constexpr int kTabInts = 8;         // int32 fields per segment-table entry
+constexpr size_t kAlign = 256;
+
+// Segment-table entry fields (int32 each).
+enum TabField { TAB_ROW = 0, TAB_START = 1, TAB_LEN = 2, TAB_POS0 = 3, TAB_DOC = 4 };
+
+// Everything a launch needs about the problem and the workspace carve-up.
+struct Plan {
+  int B, H, L, d, dtype;
+  int n_docs;          // documents (B when not packed)
+  bool packed;         // cu_seqlens given
+  int seg_len;         // tokens per segment, multiple of kChunk
+  int n_seg_max;       // upper bound on segments (grid size of the sweep kernels)
+  int n_hi;            // rows of the coarse RoPE table (positions / 64)
+  size_t off_tab, off_docoff, off_nseg, off_rope_lo, off_rope_hi, off_states;
+  size_t bytes;        // total workspace bytes
+};
+
+struct FwdArgs {
+  const int32_t* cu;   // device or null
+  const void *q, *k, *v;
+  const float *gq, *gk;
+  void* out;           // null for the state build
+  float *final_S, *final_z;
+  float eps, rms_eps, rope_base;
+  char* ws;
+};
+
+// Launch the whole chunked forward (out != null) or the state build (out == null).
+hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s);
+
+hipError_t launch_decode(int N, int H, int d, int dtype, const void* q, const void* k,
+                         const void* v, const int32_t* pos, const float* gq, const float* gk,
+                         float rms_eps, float rope_base, float eps, float* S, float* z,
+                         void* out, hipStream_t s);
+
+}  // namespace rla2

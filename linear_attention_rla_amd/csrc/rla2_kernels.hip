@@ -1,0 +1,854 @@
+// HIP kernels for RLA-2 causal ReLU linear attention on gfx950 (CDNA4, wave64).
+//
+// Method: neuralnet.cpp development page "线性注意力家族：RLA / RAPT / RLA-2 与 GPU 落地"
+// (the RLA page). §3 gives q' = ReLU(RoPE(RMSNorm(q))), k' likewise, the state
+// S_t = S_{t-1} + k'_t (x) v_t, z_t = z_{t-1} + k'_t and out_t = q'_t S_t / (q'_t . z_t + eps);
+// §1 notes that the fixed-size state lets training accumulate it chunk-parallel; §2.2/§4.1
+// clear the state at document starts.
+//
+// Chunked evaluation used here (C = 64 tokens per chunk, documents split into segments of
+// whole chunks):
+//   seg_map      cu_seqlens -> table of (row, first token, length, first position) segments
+//   rope_table   cos/sin of p*theta_j for p < 64 and for p = 64*a (angle addition rebuilds
+//                any position from the two, so no per-token transcendental is needed)
+//   chunk_state  per (segment, head): Sum over the segment of K'^T V and of K' (MFMA)
+//   state_scan   per (document, head): exclusive prefix of segment totals in fp32;
+//                the inclusive end is the document's final state
+//   chunk_out    per (segment, head): sweep the segment's chunks in order with the running
+//                state S in MFMA accumulators:
+//                  A   = causal_mask(Q'_c K'_c^T)                       (within the chunk)
+//                  num = A V_c + Q'_c S,  den = A 1 + Q'_c z + eps,  out = num / den
+//                  S  += K'_c^T V_c,      z  += sum of the rows of K'_c
+//   decode       one token per sequence: feature map, S += k' (x) v, z += k', read-out
+//
+// The feature map (RMSNorm -> rotate-half RoPE -> ReLU) runs inside chunk_state,
+// chunk_out and decode on the data just loaded, so q', k' never travel through HBM.
+//
+// MFMA operand layout. For v_mfma_f32_16x16x32_bf16 (and 16x16x4 f32) the A operand of
+// lane l carries row l%16, the B operand carries column l%16, and the D tile of lane l
+// holds rows 4*(l/16)+i, i<4, of column l%16. The contraction index is free to permute as
+// long as A and B agree, so every k-block of 32 here uses the order
+//   slot (g = l/16, j < 4) -> index 4g + j,  slot (g, j >= 4) -> index 16 + 4g + (j - 4),
+// which is exactly the set of rows a lane holds in two vertically stacked D tiles. A
+// running state kept in accumulators therefore becomes a B operand with no data movement,
+// and so does the attention tile A^T = K' Q'^T (rows = keys) as the A operand of A V.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "rla2_internal.h"
+
+namespace rla2 {
+namespace {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int NT = 256;  // threads per workgroup of the chunk kernels
+
+// ----------------------------------------------------------------------------------------
+// element helpers
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+template <bool BF>
+struct Elem;
+template <>
+struct Elem<true> {
+  using St = uint16_t;
+  __device__ static float to_f(St x) { return bf2f(x); }
+  __device__ static St from_f(float x) { return f2bf(x); }
+};
+template <>
+struct Elem<false> {
+  using St = float;
+  __device__ static float to_f(St x) { return x; }
+  __device__ static St from_f(float x) { return x; }
+};
+
+// Copy N bytes between 4-byte-aligned locations with the widest vector moves that fit.
+template <int N>
+__device__ __forceinline__ void copy_bytes(void* dst, const void* src) {
+  static_assert(N % 4 == 0, "");
+  if constexpr (N % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 16; ++i)
+      reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+  } else if constexpr (N == 8) {
+    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i)
+      reinterpret_cast<uint32_t*>(dst)[i] = reinterpret_cast<const uint32_t*>(src)[i];
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// geometry of the chunk kernels for head dim D and element type
+
+template <bool BF, int D>
+struct Geo {
+  using St = typename Elem<BF>::St;
+  static constexpr int ES = sizeof(St);
+  static constexpr int HALF = D / 2;
+  static constexpr int E = D / 16;     // dims per lane in each RoPE half (8 lanes per token)
+  static constexpr int ROWP = D + (BF ? 8 : 4);   // pitch (elements) of row-major [token][dim]
+  static constexpr int COLP = kChunk + (BF ? 8 : 4);  // pitch of transposed [dim][token]
+  static constexpr int NW = (D / 16 < 4) ? D / 16 : 4;  // waves that own state columns
+  static constexpr int DVW = D / NW;   // value columns per such wave
+  static constexpr int CT = DVW / 16;  // 16-wide column tiles per wave
+  static constexpr int RT = D / 16;    // 16-high row tiles of the state
+  static constexpr int KB = D / 32;    // 32-wide k-blocks over the head dim
+  static_assert(E >= 2 && (E * ES) % 4 == 0, "");
+};
+
+// One MFMA k-block of 32 contraction indices, in the slot order described at the top.
+template <bool BF>
+struct Frag;
+template <>
+struct Frag<true> {
+  bf16x8 v;
+};
+template <>
+struct alignas(16) Frag<false> {
+  float v[8];
+};
+
+__device__ __forceinline__ floatx4 mma(const Frag<true>& a, const Frag<true>& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4 mma(const Frag<false>& a, const Frag<false>& b, floatx4 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+  return c;
+}
+
+// Fragment of row `row` of an LDS array with element pitch `pitch`, k-block `kb`:
+// elements kb*32 + 4g + {0..3} and kb*32 + 16 + 4g + {0..3}.
+template <bool BF>
+__device__ __forceinline__ Frag<BF> lds_frag(const typename Elem<BF>::St* base, int pitch, int row,
+                                             int kb, int g) {
+  using St = typename Elem<BF>::St;
+  Frag<BF> f;
+  const St* p = base + row * pitch + kb * 32 + 4 * g;
+  copy_bytes<4 * sizeof(St)>(&f.v, p);
+  copy_bytes<4 * sizeof(St)>(reinterpret_cast<char*>(&f.v) + 4 * sizeof(St), p + 16);
+  return f;
+}
+
+// Fragment from two vertically stacked accumulator tiles (rows 0..15 and 16..31 of a block).
+__device__ __forceinline__ Frag<true> acc_frag_bf(floatx4 lo, floatx4 hi) {
+  Frag<true> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.v[j] = static_cast<__bf16>(lo[j]);
+    f.v[4 + j] = static_cast<__bf16>(hi[j]);
+  }
+  return f;
+}
+__device__ __forceinline__ Frag<false> acc_frag_f(floatx4 lo, floatx4 hi) {
+  Frag<false> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.v[j] = lo[j];
+    f.v[4 + j] = hi[j];
+  }
+  return f;
+}
+template <bool BF>
+__device__ __forceinline__ Frag<BF> acc_frag(floatx4 lo, floatx4 hi) {
+  if constexpr (BF) return acc_frag_bf(lo, hi);
+  else return acc_frag_f(lo, hi);
+}
+
+// ----------------------------------------------------------------------------------------
+// feature map of a token pair in the chunk kernels
+//
+// Lane mapping (256 threads, 64 tokens): lane l owns tokens t0 = 2*(l/8), t0 + 1 and, in each
+// RoPE half h, the E dims [h*D/2 + (l%8)*E, +E). Rotate-half RoPE pairs dim j with j + D/2,
+// so both partners of every pair sit in the same lane; the RMS statistic is a sum over the 8
+// lanes of a token (xor-shuffles 1, 2, 4).
+
+template <bool BF, int D>
+struct Raw {  // one tensor's elements for the lane's two tokens, packed in 32-bit words
+  static constexpr int W = Geo<BF, D>::E * Geo<BF, D>::ES / 4;  // words per (token, half)
+  alignas(16) uint32_t w[2][2][W];
+  __device__ __forceinline__ float get(int tok, int h, int e) const {
+    if constexpr (BF) return __uint_as_float(e & 1 ? (w[tok][h][e >> 1] & 0xffff0000u) : (w[tok][h][e >> 1] << 16));
+    else return __uint_as_float(w[tok][h][e]);
+  }
+  __device__ __forceinline__ uint32_t bits(int tok, int h, int e) const {  // raw element bits
+    if constexpr (BF) return e & 1 ? (w[tok][h][e >> 1] >> 16) : (w[tok][h][e >> 1] & 0xffffu);
+    else return w[tok][h][e];
+  }
+};
+
+template <bool BF, int D>
+__device__ __forceinline__ void load_raw(Raw<BF, D>& r, const typename Elem<BF>::St* chunk_base,
+                                         int t0, int m, int nvalid) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (t0 + tok < nvalid) {
+        copy_bytes<G::E * G::ES>(r.w[tok][h], chunk_base + (size_t)(t0 + tok) * D + h * G::HALF + m * G::E);
+      } else {
+#pragma unroll
+        for (int i = 0; i < Raw<BF, D>::W; ++i) r.w[tok][h][i] = 0u;
+      }
+    }
+  }
+}
+
+// x' = ReLU(RoPE(RMSNorm(x))) rounded to the element type (result in `o`, same layout as raw).
+// rope_lo: [64][D/2] float2 (cos, sin) of t*theta_j; rope_hi_row: the [D/2] row of 64*a*theta_j
+// for the chunk's first position 64*a. The rotation angle of token t is 64*a*theta + t*theta.
+template <bool BF, int D>
+__device__ __forceinline__ void feature_map_pair(const Raw<BF, D>& r, Raw<BF, D>& o, const float* gamma,
+                                                 const float2* rope_lo, const float2* rope_hi_row,
+                                                 int t0, int m, float rms_eps) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) {
+      const float a = r.get(tok, 0, e), b = r.get(tok, 1, e);
+      ss += a * a;
+      ss += b * b;
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / D) + rms_eps);
+    const float2* lo = rope_lo + (t0 + tok) * G::HALF;
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) {
+      const int j = m * G::E + e;
+      const float y1 = r.get(tok, 0, e) * inv * gamma[j];
+      const float y2 = r.get(tok, 1, e) * inv * gamma[j + G::HALF];
+      const float2 a = rope_hi_row[j], b = lo[j];
+      const float c = a.x * b.x - a.y * b.y;  // cos(A + B)
+      const float s = a.y * b.x + a.x * b.y;  // sin(A + B)
+      const float u1 = fmaxf(y1 * c - y2 * s, 0.f), u2 = fmaxf(y2 * c + y1 * s, 0.f);
+      if constexpr (BF) {
+        const uint32_t b1 = f2bf(u1), b2 = f2bf(u2);
+        if (e & 1) {
+          o.w[tok][0][e >> 1] |= b1 << 16;
+          o.w[tok][1][e >> 1] |= b2 << 16;
+        } else {
+          o.w[tok][0][e >> 1] = b1;
+          o.w[tok][1][e >> 1] = b2;
+        }
+      } else {
+        o.w[tok][0][e] = __float_as_uint(u1);
+        o.w[tok][1][e] = __float_as_uint(u2);
+      }
+    }
+  }
+}
+
+// Store a lane's pair tokens row-major into [64][ROWP].
+template <bool BF, int D>
+__device__ __forceinline__ void store_rows(typename Elem<BF>::St* dst, const Raw<BF, D>& o, int t0, int m) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      copy_bytes<G::E * G::ES>(dst + (t0 + tok) * G::ROWP + h * G::HALF + m * G::E, o.w[tok][h]);
+}
+
+// Store a lane's pair tokens transposed into [D][COLP]: one 2-token word per dim.
+template <bool BF, int D>
+__device__ __forceinline__ void store_cols(typename Elem<BF>::St* dst, const Raw<BF, D>& o, int t0, int m) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) {
+      const int dim = h * G::HALF + m * G::E + e;
+      if constexpr (BF) {
+        const uint32_t w = o.bits(0, h, e) | (o.bits(1, h, e) << 16);
+        *reinterpret_cast<uint32_t*>(dst + dim * G::COLP + t0) = w;
+      } else {
+        *reinterpret_cast<uint2*>(dst + dim * G::COLP + t0) = make_uint2(o.bits(0, h, e), o.bits(1, h, e));
+      }
+    }
+}
+
+struct SegInfo {
+  int row, start, len, pos0;
+};
+
+__device__ __forceinline__ SegInfo read_seg(const int32_t* tab, int seg) {
+  const int4 a = *reinterpret_cast<const int4*>(tab + (size_t)seg * kTabInts);
+  return SegInfo{a.x, a.y, a.z, a.w};
+}
+
+// ----------------------------------------------------------------------------------------
+// seg_map: documents -> segments of at most seg_len tokens (whole chunks), one workgroup.
+
+__global__ __launch_bounds__(1024) void seg_map_kernel(const int32_t* __restrict__ cu, int n_docs, int L,
+                                                       int seg_len, int n_seg_max, int32_t* __restrict__ tab,
+                                                       int32_t* __restrict__ docoff, int32_t* __restrict__ nseg) {
+  __shared__ int scan[1024];
+  __shared__ int carry_s;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < n_docs; base += 1024) {
+    const int j = base + tid;
+    int start = 0, end = 0, row = 0, cnt = 0;
+    if (j < n_docs) {
+      if (cu != nullptr) {
+        start = min(max(cu[j], 0), L);
+        end = min(max(cu[j + 1], start), L);
+      } else {
+        row = j;
+        end = L;
+      }
+      cnt = (end - start + seg_len - 1) / seg_len;
+    }
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int carry = carry_s;
+    const int first = carry + scan[tid] - cnt;
+    if (j < n_docs) {
+      docoff[j] = min(first, n_seg_max);
+      for (int s = 0; s < cnt; ++s) {
+        const int idx = first + s;
+        if (idx >= n_seg_max) break;
+        int4 e;
+        e.x = row;
+        e.y = start + s * seg_len;
+        e.z = min(seg_len, end - start - s * seg_len);
+        e.w = s * seg_len;
+        *reinterpret_cast<int4*>(tab + (size_t)idx * kTabInts) = e;
+        tab[(size_t)idx * kTabInts + TAB_DOC] = j;
+      }
+    }
+    __syncthreads();
+    if (tid == 1023) carry_s = carry + scan[1023];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int total = min(carry_s, n_seg_max);
+    docoff[n_docs] = total;
+    *nseg = total;
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// rope_table: (cos, sin) of p * theta_j, theta_j = base^(-2j/D), in fp64, rounded to fp32.
+// Rows 0..63 hold p = row; rows 64.. hold p = 64 * (row - 64).
+
+__global__ void rope_table_kernel(float2* __restrict__ lo, float2* __restrict__ hi, int half, int D,
+                                  int n_hi, float base) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int rows = kChunk + n_hi;
+  if (idx >= rows * half) return;
+  const int row = idx / half, j = idx % half;
+  const double theta = pow((double)base, -2.0 * (double)j / (double)D);
+  const double p = row < kChunk ? (double)row : (double)kChunk * (double)(row - kChunk);
+  double s, c;
+  sincos(p * theta, &s, &c);
+  const float2 v = make_float2((float)c, (float)s);
+  if (row < kChunk) lo[row * half + j] = v;
+  else hi[(row - kChunk) * half + j] = v;
+}
+
+// ----------------------------------------------------------------------------------------
+// chunk_state: per (segment, head), T = Sum_chunks K'^T V and Sum K' over the segment.
+
+template <bool BF, int D>
+__global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
+    const typename Elem<BF>::St* __restrict__ k, const typename Elem<BF>::St* __restrict__ v,
+    const float* __restrict__ gamma_k, const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg,
+    const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi, float* __restrict__ states,
+    int H, int L, float rms_eps) {
+  using G = Geo<BF, D>;
+  using St = typename G::St;
+  __shared__ __attribute__((aligned(16))) St sKT[D * G::COLP];
+  __shared__ __attribute__((aligned(16))) St sVT[D * G::COLP];
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = 2 * (tid >> 3), m = tid & 7;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const St* kb = k + tok0 * D;
+  const St* vb = v + tok0 * D;
+  const float* gk = gamma_k + (size_t)h * D;
+
+  floatx4 acc[G::RT][G::CT];
+#pragma unroll
+  for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float zacc = 0.f;
+
+  Raw<BF, D> rk, rv;
+  load_raw<BF, D>(rk, kb, t0, m, min(kChunk, si.len));
+  load_raw<BF, D>(rv, vb, t0, m, min(kChunk, si.len));
+  for (int c0 = 0; c0 < si.len; c0 += kChunk) {
+    __syncthreads();  // previous chunk's LDS reads are done
+    {
+      Raw<BF, D> o;
+      feature_map_pair<BF, D>(rk, o, gk, rope_lo, rope_hi + (size_t)((si.pos0 + c0) / kChunk) * G::HALF, t0, m,
+                              rms_eps);
+      store_cols<BF, D>(sKT, o, t0, m);
+    }
+    store_cols<BF, D>(sVT, rv, t0, m);
+    if (c0 + kChunk < si.len) {
+      const int nv = min(kChunk, si.len - c0 - kChunk);
+      load_raw<BF, D>(rk, kb + (size_t)(c0 + kChunk) * D, t0, m, nv);
+      load_raw<BF, D>(rv, vb + (size_t)(c0 + kChunk) * D, t0, m, nv);
+    }
+    __syncthreads();
+    if (tid < D) {
+      float s = 0.f;
+      const St* row = sKT + tid * G::COLP;
+#pragma unroll 8
+      for (int t = 0; t < kChunk; ++t) s += Elem<BF>::to_f(row[t]);
+      zacc += s;
+    }
+    if (wave < G::NW) {
+      Frag<BF> Vf[G::CT][2];
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) {
+        const int vrow = wave * G::DVW + ct * 16 + c16;
+        Vf[ct][0] = lds_frag<BF>(sVT, G::COLP, vrow, 0, g);
+        Vf[ct][1] = lds_frag<BF>(sVT, G::COLP, vrow, 1, g);
+      }
+#pragma unroll
+      for (int rt = 0; rt < G::RT; ++rt) {
+        const Frag<BF> a0 = lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, 0, g);
+        const Frag<BF> a1 = lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, 1, g);
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          acc[rt][ct] = mma(a0, Vf[ct][0], acc[rt][ct]);
+          acc[rt][ct] = mma(a1, Vf[ct][1], acc[rt][ct]);
+        }
+      }
+    }
+  }
+  float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  if (wave < G::NW) {
+#pragma unroll
+    for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          rec[(rt * 16 + 4 * g + i) * D + wave * G::DVW + ct * 16 + c16] = acc[rt][ct][i];
+  }
+  if (tid < D) rec[D * D + tid] = zacc;
+}
+
+// ----------------------------------------------------------------------------------------
+// state_scan: per (document, head, 1024-float tile of the state record), walk the document's
+// segments in order: optionally replace each total by the exclusive prefix, and write the
+// inclusive end as the document's final state.
+
+__global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ states, const int32_t* __restrict__ docoff,
+                                                         int H, int D, int n_tiles, int write_prefix,
+                                                         float* __restrict__ final_S, float* __restrict__ final_z) {
+  const int doc = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles, h = blockIdx.y;
+  const int R4 = (D * D + D) / 4;
+  const int e4 = tile * 256 + threadIdx.x;
+  if (e4 >= R4) return;
+  const int s0 = docoff[doc], s1 = docoff[doc + 1];
+  float4* st = reinterpret_cast<float4*>(states);
+  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = s0; s < s1; s += 8) {
+    const int cnt = min(8, s1 - s);
+    float4 val[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < cnt) val[j] = st[((size_t)(s + j) * H + h) * R4 + e4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < cnt) {
+        if (write_prefix) st[((size_t)(s + j) * H + h) * R4 + e4] = run;
+        run.x += val[j].x;
+        run.y += val[j].y;
+        run.z += val[j].z;
+        run.w += val[j].w;
+      }
+    }
+  }
+  const int e = 4 * e4;
+  if (final_S != nullptr && e < D * D)
+    *reinterpret_cast<float4*>(final_S + ((size_t)doc * H + h) * D * D + e) = run;
+  if (final_z != nullptr && e >= D * D)
+    *reinterpret_cast<float4*>(final_z + ((size_t)doc * H + h) * D + (e - D * D)) = run;
+}
+
+// ----------------------------------------------------------------------------------------
+// chunk_out: per (segment, head), sweep the chunks with the running state in accumulators.
+
+template <bool BF, int D>
+__global__ __launch_bounds__(NT, 1) void chunk_out_kernel(
+    const typename Elem<BF>::St* __restrict__ q, const typename Elem<BF>::St* __restrict__ k,
+    const typename Elem<BF>::St* __restrict__ v, const float* __restrict__ gamma_q,
+    const float* __restrict__ gamma_k, const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg,
+    const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi, const float* __restrict__ states,
+    typename Elem<BF>::St* __restrict__ out, int H, int L, float rms_eps, float eps) {
+  using G = Geo<BF, D>;
+  using St = typename G::St;
+  using EL = Elem<BF>;
+  __shared__ __attribute__((aligned(16))) St sQ[kChunk * G::ROWP];
+  __shared__ __attribute__((aligned(16))) St sK[kChunk * G::ROWP];
+  __shared__ __attribute__((aligned(16))) St sKT[D * G::COLP];
+  __shared__ __attribute__((aligned(16))) St sVT[D * G::COLP];
+  __shared__ float sZ[D];
+  __shared__ float sDen[kChunk];
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = 2 * (tid >> 3), m = tid & 7;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const St* qb = q + tok0 * D;
+  const St* kb = k + tok0 * D;
+  const St* vb = v + tok0 * D;
+  St* ob = out + tok0 * D;
+  const float* gq = gamma_q + (size_t)h * D;
+  const float* gk = gamma_k + (size_t)h * D;
+
+  // running state S (this wave's value columns) and z, from the exclusive prefix
+  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  floatx4 S[G::RT][G::CT];
+  {
+    const int wv = wave < G::NW ? wave : 0;  // waves without state columns keep a harmless copy
+#pragma unroll
+    for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[rt][ct][i] = rec[(rt * 16 + 4 * g + i) * D + wv * G::DVW + ct * 16 + c16];
+  }
+  if (tid < D) sZ[tid] = rec[D * D + tid];
+
+  Raw<BF, D> rq, rk, rv;
+  {
+    const int nv = min(kChunk, si.len);
+    load_raw<BF, D>(rq, qb, t0, m, nv);
+    load_raw<BF, D>(rk, kb, t0, m, nv);
+    load_raw<BF, D>(rv, vb, t0, m, nv);
+  }
+  for (int c0 = 0; c0 < si.len; c0 += kChunk) {
+    const int nv = min(kChunk, si.len - c0);
+    const float2* hirow = rope_hi + (size_t)((si.pos0 + c0) / kChunk) * G::HALF;
+    __syncthreads();  // B1: previous chunk's LDS reads and z update are done
+    {
+      Raw<BF, D> o;
+      feature_map_pair<BF, D>(rq, o, gq, rope_lo, hirow, t0, m, rms_eps);
+      store_rows<BF, D>(sQ, o, t0, m);
+      // q'_t . z_prev for the two tokens (rounded q' as used by the MFMA)
+#pragma unroll
+      for (int tok = 0; tok < 2; ++tok) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) {
+          const int j = m * G::E + e;
+          p += o.get(tok, 0, e) * sZ[j];
+          p += o.get(tok, 1, e) * sZ[j + G::HALF];
+        }
+        p += __shfl_xor(p, 1);
+        p += __shfl_xor(p, 2);
+        p += __shfl_xor(p, 4);
+        if (m == 0) sDen[t0 + tok] = p;
+      }
+    }
+    {
+      Raw<BF, D> o;
+      feature_map_pair<BF, D>(rk, o, gk, rope_lo, hirow, t0, m, rms_eps);
+      store_rows<BF, D>(sK, o, t0, m);
+      store_cols<BF, D>(sKT, o, t0, m);
+    }
+    store_cols<BF, D>(sVT, rv, t0, m);
+    if (c0 + kChunk < si.len) {
+      const int nn = min(kChunk, si.len - c0 - kChunk);
+      load_raw<BF, D>(rq, qb + (size_t)(c0 + kChunk) * D, t0, m, nn);
+      load_raw<BF, D>(rk, kb + (size_t)(c0 + kChunk) * D, t0, m, nn);
+      load_raw<BF, D>(rv, vb + (size_t)(c0 + kChunk) * D, t0, m, nn);
+    }
+    __syncthreads();  // B2: chunk c in LDS
+    float zsum = 0.f;
+    if (tid < D) {
+      const St* row = sKT + tid * G::COLP;
+#pragma unroll 8
+      for (int t = 0; t < kChunk; ++t) zsum += EL::to_f(row[t]);
+    }
+    if (wave < G::NW) {
+      Frag<BF> Vf[G::CT][2];
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) {
+        const int vrow = wave * G::DVW + ct * 16 + c16;
+        Vf[ct][0] = lds_frag<BF>(sVT, G::COLP, vrow, 0, g);
+        Vf[ct][1] = lds_frag<BF>(sVT, G::COLP, vrow, 1, g);
+      }
+#pragma unroll 1
+      for (int tt = 0; tt < 4; ++tt) {
+        const St* sKo = sK;
+        asm volatile("" : "+v"(sKo));  // keep the K' fragment loads inside this loop (register budget)
+        Frag<BF> Qf[G::KB];
+#pragma unroll
+        for (int kb2 = 0; kb2 < G::KB; ++kb2) Qf[kb2] = lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g);
+        // A^T tiles (rows = keys of tile kt, cols = tokens of tile tt), causal: kt <= tt
+        floatx4 At[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (kt <= tt) {
+#pragma unroll
+            for (int kb2 = 0; kb2 < G::KB; ++kb2)
+              At[kt] = mma(lds_frag<BF>(sKo, G::ROWP, kt * 16 + c16, kb2, g), Qf[kb2], At[kt]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float a = At[kt][i];
+              if (kt == tt && 4 * g + i > c16) a = 0.f;   // key after the query token
+              a = EL::to_f(EL::from_f(a));                  // the weight the MFMA will use
+              At[kt][i] = a;
+              rs += a;
+            }
+          }
+        }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);  // lanes with c16 == t hold the row sum of token 16*tt + t
+        Frag<BF> Af[2];
+        Af[0] = acc_frag<BF>(At[0], At[1]);
+        Af[1] = acc_frag<BF>(At[2], At[3]);
+        float den[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) den[i] = __shfl(rs, 4 * g + i) + sDen[tt * 16 + 4 * g + i] + eps;
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb2 = 0; kb2 < G::KB; ++kb2)  // S rounded to the element type as the B operand
+            o = mma(Qf[kb2], acc_frag<BF>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]), o);
+          o = mma(Af[0], Vf[ct][0], o);
+          if (tt >= 2) o = mma(Af[1], Vf[ct][1], o);
+          const int col = wave * G::DVW + ct * 16 + c16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = tt * 16 + 4 * g + i;
+            if (t < nv) ob[(size_t)(c0 + t) * D + col] = EL::from_f(o[i] / den[i]);
+          }
+        }
+      }
+      // S += K'^T V
+#pragma unroll
+      for (int rt = 0; rt < G::RT; ++rt) {
+        const Frag<BF> a0 = lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, 0, g);
+        const Frag<BF> a1 = lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, 1, g);
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          S[rt][ct] = mma(a0, Vf[ct][0], S[rt][ct]);
+          S[rt][ct] = mma(a1, Vf[ct][1], S[rt][ct]);
+        }
+      }
+    }
+    if (tid < D) sZ[tid] += zsum;  // read again only after the next B1
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// decode: one workgroup per (sequence, head). Wave 0 maps q, wave 1 maps k (lane j holds the
+// RoPE pair j, j + D/2), then every thread updates D/... rows of a 4-column strip of S in place
+// and accumulates its share of q' S; the partial read-outs meet in LDS.
+
+template <bool BF, int D>
+__global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St* __restrict__ q,
+                                                     const typename Elem<BF>::St* __restrict__ k,
+                                                     const typename Elem<BF>::St* __restrict__ v,
+                                                     const int32_t* __restrict__ positions,
+                                                     const float* __restrict__ gamma_q,
+                                                     const float* __restrict__ gamma_k, float rms_eps,
+                                                     float rope_base, float eps, float* __restrict__ S,
+                                                     float* __restrict__ z, typename Elem<BF>::St* __restrict__ out,
+                                                     int H) {
+  using EL = Elem<BF>;
+  constexpr int HALF = D / 2;
+  constexpr int C4 = D / 4;           // 4-column strips
+  constexpr int RG = 256 / C4;        // row groups
+  constexpr int RPT = D / RG;         // rows per thread
+  __shared__ float sq[D], sk[D], sv[D];
+  __shared__ float part[RG][D];
+  __shared__ float sden[4];
+
+  const int nh = blockIdx.x;          // n * H + h
+  const int n = nh / H, h = nh % H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t base = (size_t)nh * D;
+  float* Sp = S + (size_t)nh * D * D;
+
+  // issue the state loads first: they dominate the traffic
+  const int c4 = tid % C4, rg = tid / C4;
+  floatx4 st[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r)
+    st[r] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sp + (size_t)(rg + r * RG) * D) + c4);
+
+  if (wave < 2 && lane < HALF) {
+    const typename EL::St* x = (wave == 0 ? q : k) + base;
+    const float* gm = (wave == 0 ? gamma_q : gamma_k) + (size_t)h * D;
+    const float x1 = EL::to_f(x[lane]), x2 = EL::to_f(x[lane + HALF]);
+    float ss = x1 * x1 + x2 * x2;
+#pragma unroll
+    for (int o = 1; o < HALF; o <<= 1) ss += __shfl_xor(ss, o);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / D) + rms_eps);
+    const float y1 = x1 * inv * gm[lane], y2 = x2 * inv * gm[lane + HALF];
+    const int p = max(positions[n], 0);
+    const double theta = pow((double)rope_base, -2.0 * (double)lane / (double)D);
+    double sd, cd;
+    sincos((double)p * theta, &sd, &cd);
+    const float c = (float)cd, s = (float)sd;
+    float* dst = wave == 0 ? sq : sk;
+    dst[lane] = EL::to_f(EL::from_f(fmaxf(y1 * c - y2 * s, 0.f)));
+    dst[lane + HALF] = EL::to_f(EL::from_f(fmaxf(y2 * c + y1 * s, 0.f)));
+  }
+  if (tid < D) sv[tid] = EL::to_f(v[base + tid]);
+  __syncthreads();
+
+  const float v0 = sv[4 * c4], v1 = sv[4 * c4 + 1], v2 = sv[4 * c4 + 2], v3 = sv[4 * c4 + 3];
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int row = rg + r * RG;
+    const float kr = sk[row], qr = sq[row];
+    floatx4 x = st[r];
+    x[0] += kr * v0;
+    x[1] += kr * v1;
+    x[2] += kr * v2;
+    x[3] += kr * v3;
+    __builtin_nontemporal_store(x, reinterpret_cast<floatx4*>(Sp + (size_t)row * D) + c4);
+    a0 += qr * x[0];
+    a1 += qr * x[1];
+    a2 += qr * x[2];
+    a3 += qr * x[3];
+  }
+  part[rg][4 * c4] = a0;
+  part[rg][4 * c4 + 1] = a1;
+  part[rg][4 * c4 + 2] = a2;
+  part[rg][4 * c4 + 3] = a3;
+
+  // z += k'; den = q' . z_new
+  float dz = 0.f;
+  if (tid < D) {
+    const float zn = z[base + tid] + sk[tid];
+    z[base + tid] = zn;
+    dz = sq[tid] * zn;
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) dz += __shfl_xor(dz, o);
+  if (lane == 0) sden[wave] = dz;
+  __syncthreads();
+  if (tid < D) {
+    float num = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) num += part[r][tid];
+    const float den = sden[0] + sden[1] + sden[2] + sden[3] + eps;
+    out[base + tid] = EL::from_f(num / den);
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// launchers
+
+template <bool BF, int D>
+hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s) {
+  using St = typename Elem<BF>::St;
+  int32_t* tab = reinterpret_cast<int32_t*>(a.ws + p.off_tab);
+  int32_t* docoff = reinterpret_cast<int32_t*>(a.ws + p.off_docoff);
+  int32_t* nseg = reinterpret_cast<int32_t*>(a.ws + p.off_nseg);
+  float2* rlo = reinterpret_cast<float2*>(a.ws + p.off_rope_lo);
+  float2* rhi = reinterpret_cast<float2*>(a.ws + p.off_rope_hi);
+  float* states = reinterpret_cast<float*>(a.ws + p.off_states);
+  const int half = D / 2;
+
+  hipLaunchKernelGGL(seg_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, p.n_docs, p.L, p.seg_len, p.n_seg_max,
+                     tab, docoff, nseg);
+  const int rope_entries = (kChunk + p.n_hi) * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((rope_entries + 255) / 256), dim3(256), 0, s, rlo, rhi, half, D,
+                     p.n_hi, a.rope_base);
+  if (p.n_seg_max > 0) {
+    hipLaunchKernelGGL((chunk_state_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                       static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
+                       states, p.H, p.L, a.rms_eps);
+  }
+  const int n_tiles = ((D * D + D) / 4 + 255) / 256;
+  const bool want_final = a.final_S != nullptr || a.final_z != nullptr;
+  const bool fwd = a.out != nullptr;
+  if (want_final || (fwd && p.n_seg_max > 0)) {
+    hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
+                       n_tiles, fwd ? 1 : 0, a.final_S, a.final_z);
+  }
+  if (fwd && p.n_seg_max > 0) {
+    hipLaunchKernelGGL((chunk_out_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                       static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
+                       a.gk, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+  }
+  return hipGetLastError();
+}
+
+template <bool BF, int D>
+hipError_t run_decode(int N, int H, const void* q, const void* k, const void* v, const int32_t* pos,
+                      const float* gq, const float* gk, float rms_eps, float rope_base, float eps, float* S,
+                      float* z, void* out, hipStream_t s) {
+  using St = typename Elem<BF>::St;
+  hipLaunchKernelGGL((decode_kernel<BF, D>), dim3(N * H), dim3(256), 0, s, static_cast<const St*>(q),
+                     static_cast<const St*>(k), static_cast<const St*>(v), pos, gq, gk, rms_eps, rope_base, eps, S,
+                     z, static_cast<St*>(out), H);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s) {
+  const bool bf = p.dtype == 1;
+  switch (p.d) {
+    case 32: return bf ? run_chunked<true, 32>(p, a, s) : run_chunked<false, 32>(p, a, s);
+    case 64: return bf ? run_chunked<true, 64>(p, a, s) : run_chunked<false, 64>(p, a, s);
+    case 128: return bf ? run_chunked<true, 128>(p, a, s) : run_chunked<false, 128>(p, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(int N, int H, int d, int dtype, const void* q, const void* k, const void* v,
+                         const int32_t* pos, const float* gq, const float* gk, float rms_eps, float rope_base,
+                         float eps, float* S, float* z, void* out, hipStream_t s) {
+  const bool bf = dtype == 1;
+#define RLA2_DEC(DD)                                                                                           \
+  return bf ? run_decode<true, DD>(N, H, q, k, v, pos, gq, gk, rms_eps, rope_base, eps, S, z, out, s)         \
+            : run_decode<false, DD>(N, H, q, k, v, pos, gq, gk, rms_eps, rope_base, eps, S, z, out, s)
+  switch (d) {
+    case 32: RLA2_DEC(32);
+    case 64: RLA2_DEC(64);
+    case 128: RLA2_DEC(128);
+  }
+#undef RLA2_DEC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rla2

@@ -46,6 +46,10 @@ DEFAULT_ROPE_BASE = 10000.0
 
 
 def _f64(x) -> np.ndarray:
+    """fp64 copy of an array-like; torch CPU tensors of any float dtype (bf16 included)
+    are upcast exactly."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu").double().numpy()
     return np.asarray(x, dtype=np.float64)
 
 
@@ -181,11 +185,11 @@ def fwd_rows(q, k, v, gamma_q, gamma_k, b: int, h: int, rows, cu_seqlens=None,
             continue
         local = rows[sel] - s0
         n_keys = int(local.max()) + 1
-        kk = _f64(np.asarray(k[b, h, s0:s0 + n_keys], dtype=np.float64))
-        vv = _f64(np.asarray(v[b, h, s0:s0 + n_keys], dtype=np.float64))
-        kp = feature_map(kk, gamma_k[h], np.arange(n_keys), rms_eps, rope_base)
-        qq = _f64(np.asarray(q[b, h, s0:s1], dtype=np.float64))[local]
-        qp = feature_map(qq, gamma_q[h], local, rms_eps, rope_base)
+        kk = _f64(k[b, h, s0:s0 + n_keys])
+        vv = _f64(v[b, h, s0:s0 + n_keys])
+        kp = feature_map(kk, _f64(gamma_k)[h], np.arange(n_keys), rms_eps, rope_base)
+        qq = _f64(q[b, h, s0:s1])[local]
+        qp = feature_map(qq, _f64(gamma_q)[h], local, rms_eps, rope_base)
         for r0 in range(0, len(local), row_block):
             blk = slice(r0, r0 + row_block)
             out[sel[blk]] = _doc_attention_rows(qp[blk], kp, vv, local[blk], eps)

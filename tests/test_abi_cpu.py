@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function that
+include/rla2.h declares, and every validation error is returned before any HIP
+call (only fake, never-dereferenced device addresses are passed here)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rla2.h")
+
+pytestmark = pytest.mark.skipif(
+    not os.path.exists(os.path.join(ROOT, "linear_attention_rla_amd", "librla2.so")),
+    reason="librla2.so not built (run __graft_entry__.build())")
+
+import linear_attention_rla_amd as rla  # noqa: E402
+
+OK, NULLP, SHAPE, UNSUP, VALUE, WS, ALIAS, HIP, SEQ, MISAL = range(10)
+A = 1 << 30            # fake, 256-aligned "device" addresses; never dereferenced
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(rla2_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"rla2_fwd_chunked", "rla2_state_from_prefix", "rla2_decode_step", "rla2_fwd_workspace_size",
+            "rla2_state_from_prefix_workspace_size", "rla2_status_string", "rla2_abi_version"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", rla.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (rla2_\w+)", out))
+    assert set(names) <= exported, set(names) - exported
+    for n in names:
+        assert hasattr(rla.lib(), n)
+
+
+def test_status_strings_and_version():
+    L = rla.lib()
+    assert L.rla2_abi_version() == 1
+    for code, name in rla.STATUS.items():
+        assert L.rla2_status_string(code).decode().startswith(name)
+    assert L.rla2_status_string(99).decode() == "RLA2_ERR_UNKNOWN"
+
+
+def desc(**kw):
+    base = dict(B=2, H=4, L=300, d=64, dtype=rla.BF16, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
+                rope_base=1e4, cu_seqlens=None, n_docs=0)
+    base.update(kw)
+    cu = base.pop("cu_seqlens")
+    d = rla.FwdDesc(**{k: v for k, v in base.items()})
+    d.cu_seqlens = cu
+    return d
+
+
+def ws_size(d):
+    n = ctypes.c_size_t(0)
+    st = rla.lib().rla2_fwd_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(d=48), UNSUP), (dict(d=256), UNSUP), (dict(dtype=2), UNSUP), (dict(chunk=32), UNSUP),
+    (dict(B=-1), SHAPE), (dict(L=-5), SHAPE), (dict(H=-1), SHAPE),
+    (dict(eps=0.0), VALUE), (dict(eps=float("nan")), VALUE), (dict(rms_eps=-1.0), VALUE),
+    (dict(rope_base=float("inf")), VALUE), (dict(seg_chunks=-1), VALUE),
+    (dict(B=2, cu_seqlens=A, n_docs=3), SHAPE), (dict(B=1, cu_seqlens=A, n_docs=-1), SHAPE),
+    (dict(B=1 << 16, L=1 << 16), SHAPE),
+])
+def test_desc_validation(kw, expect):
+    assert ws_size(desc(**kw))[0] == expect
+    assert rla.lib().rla2_fwd_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == NULLP
+
+
+def test_workspace_size_grows_with_problem():
+    st, small = ws_size(desc(L=64))
+    st2, big = ws_size(desc(L=65536, B=1, H=32, d=128))
+    assert st == st2 == OK and 0 < small < big
+    # states dominate: segments * heads * (d*d + d) fp32
+    assert big >= 32 * (128 * 128 + 128) * 4
+    st3, packed = ws_size(desc(B=1, L=1000, cu_seqlens=A, n_docs=7))
+    assert st3 == OK and packed > 0
+
+
+def fwd_call(d, q=A, k=A + 64 * MB, v=A + 128 * MB, gq=A + 192 * MB, gk=A + 193 * MB, out=A + 256 * MB,
+             fS=None, fz=None, ws=A + 512 * MB, ws_bytes=1 << 30):
+    return rla.lib().rla2_fwd_chunked(ctypes.byref(d), q, k, v, gq, gk, out, fS, fz, ws, ws_bytes, None)
+
+
+def test_fwd_error_paths():
+    d = desc()
+    assert fwd_call(d, q=None) == NULLP
+    assert fwd_call(d, out=None) == NULLP
+    assert fwd_call(d, gk=None) == NULLP
+    assert fwd_call(d, ws=None) == WS
+    assert fwd_call(d, ws_bytes=100) == WS
+    assert fwd_call(d, ws=A + 512 * MB + 16) == WS          # workspace must be 256-aligned
+    assert fwd_call(d, q=A + 2) == MISAL
+    assert fwd_call(d, out=A + 256 * MB + 8) == MISAL
+    assert fwd_call(d, out=A + 1024) == ALIAS               # overlaps q
+    assert fwd_call(d, out=A + 512 * MB) == ALIAS           # overlaps the workspace
+    assert fwd_call(d, fS=A + 64 * MB) == ALIAS             # final state over k
+    assert fwd_call(d, fS=A + 300 * MB, fz=A + 300 * MB) == ALIAS
+    assert fwd_call(desc(d=40)) == UNSUP
+    assert fwd_call(desc(eps=-1.0)) == VALUE
+
+
+def test_fwd_empty_work_is_noop_without_gpu():
+    # N == 0 or H == 0 returns OK before any launch, with no pointers at all
+    assert fwd_call(desc(B=0), q=None, k=None, v=None, out=None, ws=None, ws_bytes=0) == OK
+    assert fwd_call(desc(H=0), q=None, k=None, v=None, out=None, ws=None, ws_bytes=0) == OK
+    assert fwd_call(desc(B=1, cu_seqlens=A, n_docs=0), ws=None, ws_bytes=0) == OK
+    assert ws_size(desc(B=0))[1] == 0
+
+
+def test_state_from_prefix_error_paths():
+    L = rla.lib()
+    d = desc()
+
+    def call(k=A, v=A + 64 * MB, gk=A + 192 * MB, S=A + 256 * MB, z=A + 320 * MB, ws=A + 512 * MB, n=1 << 30):
+        return L.rla2_state_from_prefix(ctypes.byref(d), k, v, gk, S, z, ws, n, None)
+
+    assert call(k=None) == NULLP
+    assert call(S=None) == NULLP
+    assert call(ws=None) == WS
+    assert call(S=A + 128) == ALIAS
+    assert call(z=A + 256 * MB + 64) == ALIAS                # z inside S
+    assert call(v=A + 64 * MB + 4) == MISAL
+
+
+def test_decode_error_paths():
+    L = rla.lib()
+
+    def call(N=4, H=2, d=128, dt=rla.BF16, q=A, k=A + MB, v=A + 2 * MB, pos=A + 3 * MB, gq=A + 4 * MB,
+             gk=A + 5 * MB, rms=1e-6, base=1e4, eps=1e-4, S=A + 64 * MB, z=A + 128 * MB, out=A + 192 * MB):
+        return L.rla2_decode_step(N, H, d, dt, q, k, v, pos, gq, gk, rms, base, eps, S, z, out, None)
+
+    assert call(N=-1) == SHAPE
+    assert call(d=96) == UNSUP
+    assert call(dt=5) == UNSUP
+    assert call(eps=0.0) == VALUE
+    assert call(rms=float("nan")) == VALUE
+    assert call(q=None) == NULLP
+    assert call(pos=None) == NULLP
+    assert call(out=A + 64 * MB) == ALIAS                    # out over S
+    assert call(z=A + 64 * MB + 4096) == ALIAS               # z inside S
+    assert call(S=A + 8) == MISAL
+    assert call(N=0, q=None, k=None, v=None, pos=None, S=None, z=None, out=None) == OK
+
+
+def test_validate_env_flag_rejects_unknown_values():
+    # RLA2_VALIDATE: unset/0 off, 1 on, anything else an error (read once per process)
+    code = ("import ctypes, linear_attention_rla_amd as r; d = r.make_desc(1, 2, 64, 64, 1);"
+            "n = ctypes.c_size_t(); print(r.lib().rla2_fwd_workspace_size(ctypes.byref(d), ctypes.byref(n)))")
+    env = dict(os.environ, RLA2_VALIDATE="yes", PYTHONPATH=ROOT)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
+    assert out.stdout.strip() == str(VALUE), out.stderr
+    env["RLA2_VALIDATE"] = "0"
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, cwd=ROOT)
+    assert out.stdout.strip() == str(OK), out.stderr
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 64, 64)
+    g = torch.ones(1, 64)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rla.fwd(x, x, x, g, g)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rla.decode_step(x[0], x[0], x[0], torch.zeros(1, dtype=torch.int32), g, g, x, x[0, 0])
