@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the RLA-2 hot path on one MI355X.
+
+One step = one chunked causal forward over the long-context workload
+(B=1, H=32, L=65536, d=128, bf16, chunk 64, 10% of q/k channels shifted by -1):
+segment map, RoPE table, chunk state, state scan and chunk output (the feature
+map runs inside the last two). The decode step over 256 sequences x 32 heads
+(d=128, fp32 state built from prefixes of length U{1..8192}) is timed in the same
+run and reported under "decode". Inputs are resident in HBM before timing.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+KERNELS = ["seg_map", "rope_table", "chunk_state", "state_scan", "chunk_out"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the stream it launches on)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.arr[i] = h
+
+    def elapsed(self, i, j):
+        assert self.hip.hipEventSynchronize(self.arr[j]) == 0
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[j]) == 0
+        return ms.value
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
+    or None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    src = os.path.join(ROOT, "linear_attention_rla_amd", "csrc", "rla2_kernels.hip")
+    try:
+        lines = [l.strip() for l in open(path) if l.strip() and not l.startswith("#")]
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if not lines or lines[0] != f"kernel_source_sha256 {digest}":
+        return None
+    for l in lines:
+        m = re.match(r"^(\w+) .* read_bytes (\S+) write_bytes (\S+)$", l)
+        if m and m.group(1) == kernel:
+            return float(m.group(2)) + float(m.group(3))
+    return None
+
+
+def fwd_algorithmic(B, H, L, d, chunk=64):
+    """Algorithmic work of the chunked forward per token-head: state build 2d^2,
+    inter-chunk read-out 2d^2, causal intra-chunk part 2*C*d flops; q, k, v read and
+    out written once (4*d*2 bytes in bf16)."""
+    th = B * H * L
+    return th * (4 * d * d + 2 * chunk * d), th * 4 * d * 2
+
+
+def decode_algorithmic(N, H, d):
+    """Per (sequence, head): S read + written (2*4*d^2), z read + written (2*4*d),
+    q, k, v read and out written in bf16 (8*d) bytes; 4*d^2 flops."""
+    u = N * H
+    return u * 4 * d * d, u * (8 * d * d + 8 * d + 8 * d)
+
+
+def cpu_baseline(inp, budget_s):
+    """The oracle as it stands on a bounded sample of the same workload: blocks of
+    1024 query rows drawn uniformly over the sequence of head 0, until the budget."""
+    import numpy as np
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas")
+    except Exception:
+        threads = os.cpu_count()
+    B, H, L, d = inp.q.shape
+    rng = np.random.default_rng(1234)
+    gq, gk = inp.gamma_q.double().numpy(), inp.gamma_k.double().numpy()
+    rows_done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and rows_done < 32768:
+        rows = np.sort(rng.choice(L, 1024, replace=False))
+        oracle.fwd_rows(inp.q, inp.k, inp.v, gq, gk, 0, 0, rows, None, inp.eps, inp.rms_eps, inp.rope_base)
+        rows_done += 1024
+    dt = time.perf_counter() - t0
+    # token-heads per second, scaled to tokens/s of the H-head workload
+    return {"value": rows_done / dt / H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} query rows of head 0 drawn uniformly over L={L} (blocks of 1024), "
+                      f"{dt:.1f} s; token-heads/s divided by H={H}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--seg-chunks", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        log("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md, sharding).")
+        sys.exit(2)
+
+    import torch
+
+    import linear_attention_rla_amd as rla
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating the long-context workload on the host ...")
+    inp = workloads.c4_long()
+    B, H, L, d = inp.q.shape
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    gq, gk = inp.gamma_q.to(dev), inp.gamma_k.to(dev)
+    out = torch.empty_like(q)
+    desc = rla.make_desc(B, H, L, d, rla.BF16, seg_chunks=args.seg_chunks)
+    ws = torch.empty(rla.fwd_workspace_size(desc), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        rla.fwd(q, k, v, gq, gk, seg_chunks=args.seg_chunks, out=out, workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} forward steps ...")
+    ev = HipEvents(2)
+    hip = ev.hip
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.steps):
+        step()
+    hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms_step = ev.elapsed(0, 1) / args.steps
+
+    # per-kernel durations over the same number of steps (events recorded on the launch stream)
+    kev = HipEvents(len(KERNELS) + 1)
+    per_kernel = [0.0] * len(KERNELS)
+    for _ in range(args.steps):
+        step(kev.arr)
+        for i in range(len(KERNELS)):
+            per_kernel[i] += kev.elapsed(i, i + 1)
+    per_kernel = [x / args.steps for x in per_kernel]
+    torch.cuda.synchronize()
+
+    flops, nbytes = fwd_algorithmic(B, H, L, d)
+    tokens_s = B * L / (ms_step * 1e-3)
+    t_out = per_kernel[KERNELS.index("chunk_out")]
+    achieved = nbytes / (t_out * 1e-3) / 1e9
+    zeros_q = zeros_k = None
+    try:  # fraction of exact zeros after the ReLU (sparse supports of this workload), on one head
+        import oracle
+        import numpy as np
+        sl = slice(0, 4096)
+        fq = oracle.feature_map(inp.q[0, 0, sl].double().numpy(), inp.gamma_q[0].double().numpy(), np.arange(4096))
+        fk = oracle.feature_map(inp.k[0, 0, sl].double().numpy(), inp.gamma_k[0].double().numpy(), np.arange(4096))
+        zeros_q, zeros_k = float((fq == 0).mean()), float((fk == 0).mean())
+    except Exception:
+        pass
+
+    result = {
+        "metric": "RLA-2 causal fwd tokens/s + MFMA TFLOP/s (L=64K, d=128); decode HBM GB/s",
+        "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1), 10% of q/k channels shifted by -1)",
+        "config": {"workload": "long-context RLA-2 causal forward, B=1 H=32 L=65536 d=128 bf16, chunk 64",
+                   "B": B, "H": H, "L": L, "d": d, "chunk": 64, "seg_chunks": args.seg_chunks or "auto"},
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "mfma_frac": flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "path_hbm_gbs": nbytes / (ms_step * 1e-3) / 1e9,
+        "kernel_ms": dict(zip(KERNELS, per_kernel)),
+        "roofline": {"kernel": "chunk_out", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic("chunk_out_kernel"), "algorithmic_bytes": nbytes},
+        "relu_zero_fraction": {"q": zeros_q, "k": zeros_k},
+    }
+
+    if not args.no_decode:
+        del q, k, v, out, ws
+        torch.cuda.empty_cache()
+        log("building the decode state from prefixes ...")
+        dec = workloads.c5_decode(device="cuda")
+        cu = dec.cu_prefix.to(dev)
+        dgq, dgk = dec.gamma_q.to(dev), dec.gamma_k.to(dev)
+        t0 = time.perf_counter()
+        S, z = rla.state_from_prefix(dec.prefix_k, dec.prefix_v, dgk, cu)
+        torch.cuda.synchronize()
+        t_prefix = time.perf_counter() - t0
+        T_prefix = int(dec.cu_prefix[-1])
+        del dec.prefix_k, dec.prefix_v
+        torch.cuda.empty_cache()
+        dq, dk, dv = dec.q.to(dev), dec.k.to(dev), dec.v.to(dev)
+        pos = dec.prefix_lengths.to(dev)
+        dout = torch.empty_like(dq)
+        for _ in range(args.warmup):
+            rla.decode_step(dq, dk, dv, pos, dgq, dgk, S, z, out=dout)
+        torch.cuda.synchronize()
+        hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(args.steps):
+            rla.decode_step(dq, dk, dv, pos, dgq, dgk, S, z, out=dout)
+        hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        ms_dec = ev.elapsed(0, 1) / args.steps
+        N, Hd, dd = dq.shape
+        dflops, dbytes = decode_algorithmic(N, Hd, dd)
+        gbs = dbytes / (ms_dec * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": "RLA-2 decode step, N=256 sequences x H=32, d=128, bf16 token, fp32 state in place",
+            "ms_per_step": ms_dec, "tokens_per_s": N / (ms_dec * 1e-3),
+            "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode_kernel"),
+                         "algorithmic_bytes": dbytes},
+            "state_from_prefix": {"prefix_tokens": T_prefix, "wall_s_first_call": t_prefix},
+        }
+
+    if args.copy_calibration:
+        # a plain streaming kernel of known size (reads 1 GiB, writes 1 GiB): the
+        # reference that scales the FETCH_SIZE / WRITE_SIZE counters to bytes
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 2.0, out=b)
+        torch.cuda.synchronize()
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).argtypes = [_DESC, _SZ]
         L.rla2_fwd_chunked.restype = ctypes.c_int
         L.rla2_fwd_chunked.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.rla2_fwd_chunked_profiled.restype = ctypes.c_int
+        L.rla2_fwd_chunked_profiled.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
         L.rla2_state_from_prefix.restype = ctypes.c_int
         L.rla2_state_from_prefix.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.rla2_decode_step.restype = ctypes.c_int
@@ -119,8 +121,11 @@ def fwd_workspace_size(desc: FwdDesc) -> int:
 
 
 def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
-        rope_base=10000.0, return_final_state=False, out=None, workspace=None):
-    """Chunked RLA-2 causal forward. Returns ``out`` or ``(out, final_S, final_z)``."""
+        rope_base=10000.0, return_final_state=False, out=None, workspace=None, events=None):
+    """Chunked RLA-2 causal forward. Returns ``out`` or ``(out, final_S, final_z)``.
+
+    ``events``: optional ctypes array of RLA2_FWD_KERNELS + 1 hipEvent_t handles; when
+    given, rla2_fwd_chunked_profiled records them around each kernel."""
     for n_, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(n_, t, q.dtype)
     _check_dev("gamma_q", gamma_q, torch.float32)
@@ -128,6 +133,8 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
     desc = _fwd_desc(q, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v shapes differ")
+    if gamma_q.shape != (desc.H, desc.d) or gamma_k.shape != (desc.H, desc.d):
+        raise ValueError("gamma_q and gamma_k must be [H, d]")
     if out is None:
         out = torch.empty_like(q)
     N = desc.n_docs if cu_seqlens is not None else desc.B
@@ -138,8 +145,12 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
     nbytes = fwd_workspace_size(desc)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    st = lib().rla2_fwd_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q), _ptr(gamma_k),
-                                _ptr(out), _ptr(fS), _ptr(fz), _ptr(workspace), workspace.numel(), _stream(q.device))
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q), _ptr(gamma_k), _ptr(out), _ptr(fS),
+            _ptr(fz), _ptr(workspace), workspace.numel(), _stream(q.device))
+    if events is None:
+        st = lib().rla2_fwd_chunked(*args)
+    else:
+        st = lib().rla2_fwd_chunked_profiled(*args, events)
     if st:
         raise Rla2Error(st, "rla2_fwd_chunked")
     return (out, fS, fz) if return_final_state else out

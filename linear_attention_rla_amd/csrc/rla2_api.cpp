@@ -16,6 +16,7 @@ namespace {
 using rla2::Plan;
 
 constexpr int32_t kAbiVersion = 1;
+static_assert(RLA2_FWD_KERNELS == rla2::kNumFwdKernels, "kernel count of the profiled forward");
 
 bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
@@ -173,6 +174,14 @@ rla2_status rla2_fwd_chunked(const rla2_fwd_desc* desc, const void* q, const voi
                              const void* v, const float* gamma_q, const float* gamma_k,
                              void* out, float* final_S, float* final_z, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
+  return rla2_fwd_chunked_profiled(desc, q, k, v, gamma_q, gamma_k, out, final_S, final_z, workspace,
+                                   workspace_bytes, stream, nullptr);
+}
+
+rla2_status rla2_fwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, const void* k,
+                                      const void* v, const float* gamma_q, const float* gamma_k,
+                                      void* out, float* final_S, float* final_z, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
@@ -203,7 +212,7 @@ rla2_status rla2_fwd_chunked(const rla2_fwd_desc* desc, const void* q, const voi
   if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
   rla2::FwdArgs a{desc->cu_seqlens, q, k, v, gamma_q, gamma_k, out, final_S, final_z,
                   desc->eps, desc->rms_eps, desc->rope_base, static_cast<char*>(workspace)};
-  return finish(rla2::launch_chunked(p, a, stream));
+  return finish(rla2::launch_chunked(p, a, stream, events));
 }
 
 rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, const void* v,

@@ -38,7 +38,9 @@ struct FwdArgs {
 };
 
 // Launch the whole chunked forward (out != null) or the state build (out == null).
-hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s);
+// `ev` (optional) gets kNumFwdKernels + 1 events recorded around the kernels.
+constexpr int kNumFwdKernels = 5;
+hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
 
 hipError_t launch_decode(int N, int H, int d, int dtype, const void* q, const void* k,
                          const void* v, const int32_t* pos, const float* gq, const float* gk,

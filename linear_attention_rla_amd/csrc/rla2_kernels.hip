@@ -777,7 +777,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St
 // launchers
 
 template <bool BF, int D>
-hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s) {
+hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   using St = typename Elem<BF>::St;
   int32_t* tab = reinterpret_cast<int32_t*>(a.ws + p.off_tab);
   int32_t* docoff = reinterpret_cast<int32_t*>(a.ws + p.off_docoff);
@@ -786,17 +786,24 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s) {
   float2* rhi = reinterpret_cast<float2*>(a.ws + p.off_rope_hi);
   float* states = reinterpret_cast<float*>(a.ws + p.off_states);
   const int half = D / 2;
+  auto mark = [&](int i) {
+    if (ev != nullptr) (void)hipEventRecord(ev[i], s);
+  };
 
+  mark(0);
   hipLaunchKernelGGL(seg_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, p.n_docs, p.L, p.seg_len, p.n_seg_max,
                      tab, docoff, nseg);
+  mark(1);
   const int rope_entries = (kChunk + p.n_hi) * half;
   hipLaunchKernelGGL(rope_table_kernel, dim3((rope_entries + 255) / 256), dim3(256), 0, s, rlo, rhi, half, D,
                      p.n_hi, a.rope_base);
+  mark(2);
   if (p.n_seg_max > 0) {
     hipLaunchKernelGGL((chunk_state_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                        static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
                        states, p.H, p.L, a.rms_eps);
   }
+  mark(3);
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
   const bool want_final = a.final_S != nullptr || a.final_z != nullptr;
   const bool fwd = a.out != nullptr;
@@ -804,11 +811,13 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
                        n_tiles, fwd ? 1 : 0, a.final_S, a.final_z);
   }
+  mark(4);
   if (fwd && p.n_seg_max > 0) {
     hipLaunchKernelGGL((chunk_out_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                        static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
                        a.gk, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
   }
+  mark(5);
   return hipGetLastError();
 }
 
@@ -825,12 +834,12 @@ hipError_t run_decode(int N, int H, const void* q, const void* k, const void* v,
 
 }  // namespace
 
-hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s) {
+hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   const bool bf = p.dtype == 1;
   switch (p.d) {
-    case 32: return bf ? run_chunked<true, 32>(p, a, s) : run_chunked<false, 32>(p, a, s);
-    case 64: return bf ? run_chunked<true, 64>(p, a, s) : run_chunked<false, 64>(p, a, s);
-    case 128: return bf ? run_chunked<true, 128>(p, a, s) : run_chunked<false, 128>(p, a, s);
+    case 32: return bf ? run_chunked<true, 32>(p, a, s, ev) : run_chunked<false, 32>(p, a, s, ev);
+    case 64: return bf ? run_chunked<true, 64>(p, a, s, ev) : run_chunked<false, 64>(p, a, s, ev);
+    case 128: return bf ? run_chunked<true, 128>(p, a, s, ev) : run_chunked<false, 128>(p, a, s, ev);
   }
   return hipErrorInvalidValue;
 }
