@@ -44,6 +44,8 @@ namespace {
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 
 constexpr int NT = 256;  // threads per workgroup of the chunk kernels
 
@@ -104,7 +106,7 @@ struct Geo {
   static constexpr int CT = DVW / 16;  // 16-wide column tiles per wave
   static constexpr int RT = D / 16;    // 16-high row tiles of the state
   static constexpr int KB = D / 32;    // 32-wide k-blocks over the head dim
-  static_assert(E >= 2 && (E * ES) % 4 == 0, "");
+  static_assert(E >= 2 && E % 2 == 0 && (E * ES) % 4 == 0, "");
 };
 
 // One MFMA k-block of 32 contraction indices, in the slot order described at the top.
@@ -206,6 +208,68 @@ __device__ __forceinline__ void load_raw(Raw<BF, D>& r, const typename Elem<BF>:
   }
 }
 
+// Feature-map arithmetic shared by every chunk kernel, so q' and k' are bitwise the same
+// wherever they are formed.
+//
+// 1/sqrt(mean(x^2) + rms_eps) of token `tok`: the lane's 2E elements plus the other 7 lanes
+// of the token (xor-shuffles 1, 2, 4).
+template <bool BF, int D>
+__device__ __forceinline__ float rms_inv(const Raw<BF, D>& r, int tok, float rms_eps) {
+  using G = Geo<BF, D>;
+  float ss = 0.f;
+  if constexpr (BF) {  // bf16 products are exact in fp32: two squares per dot instruction
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < Raw<BF, D>::W; ++i) {
+        const bf16x2 x = __builtin_bit_cast(bf16x2, r.w[tok][h][i]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(x, x, ss, false);
+      }
+  } else {
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) {
+      const float a = r.get(tok, 0, e), b = r.get(tok, 1, e);
+      ss += a * a;
+      ss += b * b;
+    }
+  }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  ss += __shfl_xor(ss, 4);
+  return rsqrtf(ss * (1.0f / D) + rms_eps);
+}
+
+// (cos, sin) of A + B from (cos A, sin A) and (cos B, sin B).
+__device__ __forceinline__ float2 angle_sum(float2 a, float2 b) {
+  return make_float2(a.x * b.x - a.y * b.y, a.y * b.x + a.x * b.y);
+}
+
+// One rotate-half pair (x1 = dim j, x2 = dim j + D/2): y = x * inv * gamma, rotate by the
+// angle with (cos, sin) = cs, then ReLU.
+__device__ __forceinline__ void rope_relu(float x1, float x2, float inv, float g1, float g2, float2 cs,
+                                          float& u1, float& u2) {
+  const float y1 = x1 * inv * g1;
+  const float y2 = x2 * inv * g2;
+  u1 = fmaxf(y1 * cs.x - y2 * cs.y, 0.f);
+  u2 = fmaxf(y2 * cs.x + y1 * cs.y, 0.f);
+}
+
+// Elements e, e + 1 of both halves of token `tok` (u?[0] at e, u?[1] at e + 1), rounded to
+// the element type (round to nearest even, two values per conversion for bf16), into `o`.
+template <bool BF, int D>
+__device__ __forceinline__ void put_pairs(Raw<BF, D>& o, int tok, int e, const float (&u1)[2],
+                                          const float (&u2)[2]) {
+  if constexpr (BF) {
+    o.w[tok][0][e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{u1[0], u1[1]}, bf16x2));
+    o.w[tok][1][e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{u2[0], u2[1]}, bf16x2));
+  } else {
+    o.w[tok][0][e] = __float_as_uint(u1[0]);
+    o.w[tok][0][e + 1] = __float_as_uint(u1[1]);
+    o.w[tok][1][e] = __float_as_uint(u2[0]);
+    o.w[tok][1][e + 1] = __float_as_uint(u2[1]);
+  }
+}
+
 // x' = ReLU(RoPE(RMSNorm(x))) rounded to the element type (result in `o`, same layout as raw).
 // rope_lo: [64][D/2] float2 (cos, sin) of t*theta_j; rope_hi_row: the [D/2] row of 64*a*theta_j
 // for the chunk's first position 64*a. The rotation angle of token t is 64*a*theta + t*theta.
@@ -216,40 +280,46 @@ __device__ __forceinline__ void feature_map_pair(const Raw<BF, D>& r, Raw<BF, D>
   using G = Geo<BF, D>;
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < G::E; ++e) {
-      const float a = r.get(tok, 0, e), b = r.get(tok, 1, e);
-      ss += a * a;
-      ss += b * b;
-    }
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
-    ss += __shfl_xor(ss, 4);
-    const float inv = 1.0f / sqrtf(ss * (1.0f / D) + rms_eps);
+    const float inv = rms_inv<BF, D>(r, tok, rms_eps);
     const float2* lo = rope_lo + (t0 + tok) * G::HALF;
 #pragma unroll
-    for (int e = 0; e < G::E; ++e) {
-      const int j = m * G::E + e;
-      const float y1 = r.get(tok, 0, e) * inv * gamma[j];
-      const float y2 = r.get(tok, 1, e) * inv * gamma[j + G::HALF];
-      const float2 a = rope_hi_row[j], b = lo[j];
-      const float c = a.x * b.x - a.y * b.y;  // cos(A + B)
-      const float s = a.y * b.x + a.x * b.y;  // sin(A + B)
-      const float u1 = fmaxf(y1 * c - y2 * s, 0.f), u2 = fmaxf(y2 * c + y1 * s, 0.f);
-      if constexpr (BF) {
-        const uint32_t b1 = f2bf(u1), b2 = f2bf(u2);
-        if (e & 1) {
-          o.w[tok][0][e >> 1] |= b1 << 16;
-          o.w[tok][1][e >> 1] |= b2 << 16;
-        } else {
-          o.w[tok][0][e >> 1] = b1;
-          o.w[tok][1][e >> 1] = b2;
-        }
-      } else {
-        o.w[tok][0][e] = __float_as_uint(u1);
-        o.w[tok][1][e] = __float_as_uint(u2);
+    for (int e = 0; e < G::E; e += 2) {
+      float u1[2], u2[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int j = m * G::E + e + x;
+        rope_relu(r.get(tok, 0, e + x), r.get(tok, 1, e + x), inv, gamma[j], gamma[j + G::HALF],
+                  angle_sum(rope_hi_row[j], lo[j]), u1[x], u2[x]);
       }
+      put_pairs<BF, D>(o, tok, e, u1, u2);
+    }
+  }
+}
+
+// q' and k' of the same two tokens: one angle per (token, pair) serves both.
+template <bool BF, int D>
+__device__ __forceinline__ void feature_map_qk(const Raw<BF, D>& rq, const Raw<BF, D>& rk, Raw<BF, D>& oq,
+                                               Raw<BF, D>& ok, const float* gq, const float* gk,
+                                               const float2* rope_lo, const float2* rope_hi_row, int t0, int m,
+                                               float rms_eps) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+    const float invq = rms_inv<BF, D>(rq, tok, rms_eps);
+    const float invk = rms_inv<BF, D>(rk, tok, rms_eps);
+    const float2* lo = rope_lo + (t0 + tok) * G::HALF;
+#pragma unroll
+    for (int e = 0; e < G::E; e += 2) {
+      float q1[2], q2[2], k1[2], k2[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int j = m * G::E + e + x;
+        const float2 cs = angle_sum(rope_hi_row[j], lo[j]);
+        rope_relu(rq.get(tok, 0, e + x), rq.get(tok, 1, e + x), invq, gq[j], gq[j + G::HALF], cs, q1[x], q2[x]);
+        rope_relu(rk.get(tok, 0, e + x), rk.get(tok, 1, e + x), invk, gk[j], gk[j + G::HALF], cs, k1[x], k2[x]);
+      }
+      put_pairs<BF, D>(oq, tok, e, q1, q2);
+      put_pairs<BF, D>(ok, tok, e, k1, k2);
     }
   }
 }
@@ -501,9 +571,20 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
 
 // ----------------------------------------------------------------------------------------
 // chunk_out: per (segment, head), sweep the chunks with the running state in accumulators.
+//
+// Per chunk, three phases separated by workgroup barriers:
+//   map   all 256 lanes: q', k' of two tokens each (shared rotation angles), q'.z per token;
+//         Q' and K' rows, K'^T and V^T columns into LDS; then the next chunk's loads are issued
+//   score wave w: the causal score tile of query tile w (16 queries x keys <= 16w+15), rounded
+//         to the element type, stored in LDS already laid out as A operands of A V; its row
+//         sums give 1/(rowsum + q'.z + eps). All lanes: column sums of K' (the z update).
+//   out   wave w < NW (value columns [w*DVW, (w+1)*DVW)): O = Q' S + A V for all 64 rows,
+//         scaled by the row reciprocals, staged in LDS (the K' rows are dead by then) and
+//         written as 16-byte row pieces; then S += K'^T V in the accumulators.
+// Registers stay under 256 and LDS under 80 KB, so two workgroups share a CU.
 
 template <bool BF, int D>
-__global__ __launch_bounds__(NT, 1) void chunk_out_kernel(
+__global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
     const typename Elem<BF>::St* __restrict__ q, const typename Elem<BF>::St* __restrict__ k,
     const typename Elem<BF>::St* __restrict__ v, const float* __restrict__ gamma_q,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg,
@@ -512,12 +593,19 @@ __global__ __launch_bounds__(NT, 1) void chunk_out_kernel(
   using G = Geo<BF, D>;
   using St = typename G::St;
   using EL = Elem<BF>;
+  constexpr int PR = G::DVW * G::ES / 16;   // 16-byte pieces per staged output row of a wave
+  constexpr int PE = 16 / G::ES;            // elements per piece
+  constexpr int ZP = NT / D;                // lanes per K'^T row in the column sums
+  constexpr int ZT = kChunk / ZP;           // tokens per such lane
   __shared__ __attribute__((aligned(16))) St sQ[kChunk * G::ROWP];
-  __shared__ __attribute__((aligned(16))) St sK[kChunk * G::ROWP];
+  __shared__ __attribute__((aligned(16))) St sK[kChunk * G::ROWP];  // K' rows; output staging after the score phase
   __shared__ __attribute__((aligned(16))) St sKT[D * G::COLP];
   __shared__ __attribute__((aligned(16))) St sVT[D * G::COLP];
+  __shared__ Frag<BF> sA[4 * 2 * 64];  // [query tile][key block][lane]: A operands of A V
   __shared__ float sZ[D];
-  __shared__ float sDen[kChunk];
+  __shared__ float sQz[kChunk];
+  __shared__ float sInv[kChunk];
+  static_assert(G::NW * kChunk * G::DVW <= kChunk * G::ROWP, "output staging must fit in the K' rows");
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;
@@ -556,33 +644,34 @@ __global__ __launch_bounds__(NT, 1) void chunk_out_kernel(
   }
   for (int c0 = 0; c0 < si.len; c0 += kChunk) {
     const int nv = min(kChunk, si.len - c0);
-    const float2* hirow = rope_hi + (size_t)((si.pos0 + c0) / kChunk) * G::HALF;
-    __syncthreads();  // B1: previous chunk's LDS reads and z update are done
+    __syncthreads();  // B1: the previous chunk's LDS reads are done; its z update is visible
+
+    // ---- map
     {
-      Raw<BF, D> o;
-      feature_map_pair<BF, D>(rq, o, gq, rope_lo, hirow, t0, m, rms_eps);
-      store_rows<BF, D>(sQ, o, t0, m);
-      // q'_t . z_prev for the two tokens (rounded q' as used by the MFMA)
+      const float2* hirow = rope_hi + (size_t)((si.pos0 + c0) / kChunk) * G::HALF;
+      const float* gqi = gq;
+      const float* gki = gk;
+      const float2* loi = rope_lo;
+      asm volatile("" : "+s"(gqi), "+s"(gki), "+s"(loi));
+      Raw<BF, D> oq, ok;
+      feature_map_qk<BF, D>(rq, rk, oq, ok, gqi, gki, loi, hirow, t0, m, rms_eps);
+      store_rows<BF, D>(sQ, oq, t0, m);
+      store_rows<BF, D>(sK, ok, t0, m);
+      store_cols<BF, D>(sKT, ok, t0, m);
 #pragma unroll
       for (int tok = 0; tok < 2; ++tok) {
         float p = 0.f;
 #pragma unroll
         for (int e = 0; e < G::E; ++e) {
           const int j = m * G::E + e;
-          p += o.get(tok, 0, e) * sZ[j];
-          p += o.get(tok, 1, e) * sZ[j + G::HALF];
+          p += oq.get(tok, 0, e) * sZ[j];
+          p += oq.get(tok, 1, e) * sZ[j + G::HALF];
         }
         p += __shfl_xor(p, 1);
         p += __shfl_xor(p, 2);
         p += __shfl_xor(p, 4);
-        if (m == 0) sDen[t0 + tok] = p;
+        if (m == 0) sQz[t0 + tok] = p;
       }
-    }
-    {
-      Raw<BF, D> o;
-      feature_map_pair<BF, D>(rk, o, gk, rope_lo, hirow, t0, m, rms_eps);
-      store_rows<BF, D>(sK, o, t0, m);
-      store_cols<BF, D>(sKT, o, t0, m);
     }
     store_cols<BF, D>(sVT, rv, t0, m);
     if (c0 + kChunk < si.len) {
@@ -591,13 +680,54 @@ __global__ __launch_bounds__(NT, 1) void chunk_out_kernel(
       load_raw<BF, D>(rk, kb + (size_t)(c0 + kChunk) * D, t0, m, nn);
       load_raw<BF, D>(rv, vb + (size_t)(c0 + kChunk) * D, t0, m, nn);
     }
-    __syncthreads();  // B2: chunk c in LDS
-    float zsum = 0.f;
-    if (tid < D) {
-      const St* row = sKT + tid * G::COLP;
-#pragma unroll 8
-      for (int t = 0; t < kChunk; ++t) zsum += EL::to_f(row[t]);
+    __syncthreads();  // B2: chunk in LDS
+
+    // ---- score: wave w owns query tile w
+    {
+      const int tt = wave;
+      Frag<BF> Qf[G::KB];
+#pragma unroll
+      for (int kb2 = 0; kb2 < G::KB; ++kb2) Qf[kb2] = lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g);
+      // A^T tiles (rows = keys of tile kt, cols = queries of tile tt), causal: kt <= tt
+      floatx4 At[4];
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (kt <= tt) {
+#pragma unroll
+          for (int kb2 = 0; kb2 < G::KB; ++kb2)
+            At[kt] = mma(lds_frag<BF>(sK, G::ROWP, kt * 16 + c16, kb2, g), Qf[kb2], At[kt]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float a = At[kt][i];
+            if (kt == tt && 4 * g + i > c16) a = 0.f;   // key after the query token
+            a = EL::to_f(EL::from_f(a));                  // the weight the MFMA will use
+            At[kt][i] = a;
+            rs += a;
+          }
+        }
+      }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);  // every lane with c16 == t holds the row sum of query 16*tt + t
+      sA[(tt * 2) * 64 + lane] = acc_frag<BF>(At[0], At[1]);
+      if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<BF>(At[2], At[3]);
+      if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + sQz[tt * 16 + c16] + eps);
     }
+    // column sums of K' (z update; sZ is read again only after the next B1)
+    {
+      const int row = tid / ZP, part = tid % ZP;
+      const St* src = sKT + row * G::COLP + part * ZT;
+      float zs = 0.f;
+#pragma unroll
+      for (int t = 0; t < ZT; ++t) zs += EL::to_f(src[t]);
+#pragma unroll
+      for (int o = 1; o < ZP; o <<= 1) zs += __shfl_xor(zs, o);
+      if (part == 0) sZ[row] += zs;
+    }
+    __syncthreads();  // B3: score tiles and row reciprocals in LDS; K' rows are free
+
+    // ---- out, then the state update
     if (wave < G::NW) {
       Frag<BF> Vf[G::CT][2];
 #pragma unroll
@@ -606,54 +736,23 @@ __global__ __launch_bounds__(NT, 1) void chunk_out_kernel(
         Vf[ct][0] = lds_frag<BF>(sVT, G::COLP, vrow, 0, g);
         Vf[ct][1] = lds_frag<BF>(sVT, G::COLP, vrow, 1, g);
       }
+      St* stage = sK + wave * (kChunk * G::DVW);
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) {
+        Frag<BF> Sb[G::KB];  // S rounded to the element type as the B operand
+#pragma unroll
+        for (int kb2 = 0; kb2 < G::KB; ++kb2) Sb[kb2] = acc_frag<BF>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
 #pragma unroll 1
-      for (int tt = 0; tt < 4; ++tt) {
-        const St* sKo = sK;
-        asm volatile("" : "+v"(sKo));  // keep the K' fragment loads inside this loop (register budget)
-        Frag<BF> Qf[G::KB];
-#pragma unroll
-        for (int kb2 = 0; kb2 < G::KB; ++kb2) Qf[kb2] = lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g);
-        // A^T tiles (rows = keys of tile kt, cols = tokens of tile tt), causal: kt <= tt
-        floatx4 At[4];
-        float rs = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-          if (kt <= tt) {
-#pragma unroll
-            for (int kb2 = 0; kb2 < G::KB; ++kb2)
-              At[kt] = mma(lds_frag<BF>(sKo, G::ROWP, kt * 16 + c16, kb2, g), Qf[kb2], At[kt]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float a = At[kt][i];
-              if (kt == tt && 4 * g + i > c16) a = 0.f;   // key after the query token
-              a = EL::to_f(EL::from_f(a));                  // the weight the MFMA will use
-              At[kt][i] = a;
-              rs += a;
-            }
-          }
-        }
-        rs += __shfl_xor(rs, 16);
-        rs += __shfl_xor(rs, 32);  // lanes with c16 == t hold the row sum of token 16*tt + t
-        Frag<BF> Af[2];
-        Af[0] = acc_frag<BF>(At[0], At[1]);
-        Af[1] = acc_frag<BF>(At[2], At[3]);
-        float den[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) den[i] = __shfl(rs, 4 * g + i) + sDen[tt * 16 + 4 * g + i] + eps;
-#pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) {
+        for (int tt = 0; tt < 4; ++tt) {
           floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kb2 = 0; kb2 < G::KB; ++kb2)  // S rounded to the element type as the B operand
-            o = mma(Qf[kb2], acc_frag<BF>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]), o);
-          o = mma(Af[0], Vf[ct][0], o);
-          if (tt >= 2) o = mma(Af[1], Vf[ct][1], o);
-          const int col = wave * G::DVW + ct * 16 + c16;
+          for (int kb2 = 0; kb2 < G::KB; ++kb2) o = mma(lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g), Sb[kb2], o);
+          o = mma(sA[(tt * 2) * 64 + lane], Vf[ct][0], o);
+          if (tt >= 2) o = mma(sA[(tt * 2 + 1) * 64 + lane], Vf[ct][1], o);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = tt * 16 + 4 * g + i;
-            if (t < nv) ob[(size_t)(c0 + t) * D + col] = EL::from_f(o[i] / den[i]);
+            stage[t * G::DVW + ct * 16 + c16] = EL::from_f(o[i] * sInv[t]);
           }
         }
       }
@@ -668,8 +767,18 @@ __global__ __launch_bounds__(NT, 1) void chunk_out_kernel(
           S[rt][ct] = mma(a1, Vf[ct][1], S[rt][ct]);
         }
       }
+      // the staged rows of this wave's columns, as 16-byte pieces (wave-local exchange)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int r = 0; r < PR; ++r) {
+        const int piece = lane + 64 * r;
+        const int t = piece / PR, pc = piece % PR;
+        if (t < nv)
+          copy_bytes<16>(ob + (size_t)(c0 + t) * D + wave * G::DVW + pc * PE, stage + t * G::DVW + pc * PE);
+      }
     }
-    if (tid < D) sZ[tid] += zsum;  // read again only after the next B1
   }
 }
 
