@@ -143,6 +143,40 @@ __device__ __forceinline__ Frag<BF> lds_frag(const typename Elem<BF>::St* base, 
   return f;
 }
 
+// The same slot order with the contraction running down the rows of a row-major bf16 LDS
+// array [k][n] (pitch in elements): lane (c16, g) gets elements [k0 + 4g + j][n0 + c16] and
+// [k0 + 16 + 4g + j][n0 + c16], j < 4. gfx950's transposing LDS read (ds_read_b64_tr_b16)
+// hands destination lane l of each 16-lane group element j of the 8 bytes read by source
+// lane 4j + l/4 at position l%4; so source lane s of group g points at row k0 + 4g + s/4,
+// columns n0 + 4(s%4) .. +3, and one read per half gives the whole fragment.
+__device__ __forceinline__ Frag<true> lds_frag_tr(const uint16_t* base, int pitch, int k0, int n0, int lane) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int c16 = lane & 15, g = lane >> 4;
+  const uint16_t* p = base + (k0 + 4 * g + (c16 >> 2)) * pitch + n0 + 4 * (c16 & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * pitch));
+  Frag<true> f;
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  f.v = __builtin_bit_cast(bf16x8, w);
+  return f;
+}
+
+// Operand whose every element is 1 (against it, K'^T gives the column sums of K').
+template <bool BF>
+__device__ __forceinline__ Frag<BF> ones_frag() {
+  Frag<BF> f;
+  if constexpr (BF) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = static_cast<__bf16>(1.0f);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = 1.0f;
+  }
+  return f;
+}
+
 // Fragment from two vertically stacked accumulator tiles (rows 0..15 and 16..31 of a block).
 __device__ __forceinline__ Frag<true> acc_frag_bf(floatx4 lo, floatx4 hi) {
   Frag<true> f;
@@ -574,13 +608,16 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
 //
 // Per chunk, three phases separated by workgroup barriers:
 //   map   all 256 lanes: q', k' of two tokens each (shared rotation angles), q'.z per token;
-//         Q' and K' rows, K'^T and V^T columns into LDS; then the next chunk's loads are issued
+//         Q', K', V rows into LDS (bf16: the K'^T and V operands are read back with the
+//         transposing LDS read; fp32: K'^T and V^T are also stored transposed); then the next
+//         chunk's loads are issued
 //   score wave w: the causal score tile of query tile w (16 queries x keys <= 16w+15), rounded
-//         to the element type, stored in LDS already laid out as A operands of A V; its row
-//         sums give 1/(rowsum + q'.z + eps). All lanes: column sums of K' (the z update).
-//   out   wave w < NW (value columns [w*DVW, (w+1)*DVW)): O = Q' S + A V for all 64 rows,
-//         scaled by the row reciprocals, staged in LDS (the K' rows are dead by then) and
-//         written as 16-byte row pieces; then S += K'^T V in the accumulators.
+//         to the element type and stored in LDS as the B operand of A V; its row sums give
+//         1/(rowsum + q'.z + eps)
+//   out   wave w < NW (value columns [w*DVW, (w+1)*DVW)): O^T = S^T Q'^T + V^T A^T, so each
+//         lane holds 4 consecutive output columns of one row and writes them directly; then
+//         S += K'^T V in the accumulators; wave 0 also forms the column sums of K' against a
+//         ones operand and adds them to z.
 // Registers stay under 256 and LDS under 80 KB, so two workgroups share a CU.
 
 template <bool BF, int D>
@@ -593,19 +630,16 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
   using G = Geo<BF, D>;
   using St = typename G::St;
   using EL = Elem<BF>;
-  constexpr int PR = G::DVW * G::ES / 16;   // 16-byte pieces per staged output row of a wave
-  constexpr int PE = 16 / G::ES;            // elements per piece
-  constexpr int ZP = NT / D;                // lanes per K'^T row in the column sums
-  constexpr int ZT = kChunk / ZP;           // tokens per such lane
+  constexpr int TD = BF ? 1 : D;  // rows of the transposed copies (fp32 only)
   __shared__ __attribute__((aligned(16))) St sQ[kChunk * G::ROWP];
-  __shared__ __attribute__((aligned(16))) St sK[kChunk * G::ROWP];  // K' rows; output staging after the score phase
-  __shared__ __attribute__((aligned(16))) St sKT[D * G::COLP];
-  __shared__ __attribute__((aligned(16))) St sVT[D * G::COLP];
-  __shared__ Frag<BF> sA[4 * 2 * 64];  // [query tile][key block][lane]: A operands of A V
+  __shared__ __attribute__((aligned(16))) St sK[kChunk * G::ROWP];
+  __shared__ __attribute__((aligned(16))) St sV[BF ? kChunk * G::ROWP : 8];
+  __shared__ __attribute__((aligned(16))) St sKT[TD * G::COLP];
+  __shared__ __attribute__((aligned(16))) St sVT[TD * G::COLP];
+  __shared__ Frag<BF> sA[4 * 2 * 64];  // [query tile][key block][lane]: B operands of V^T A^T
   __shared__ float sZ[D];
   __shared__ float sQz[kChunk];
   __shared__ float sInv[kChunk];
-  static_assert(G::NW * kChunk * G::DVW <= kChunk * G::ROWP, "output staging must fit in the K' rows");
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;
@@ -620,6 +654,17 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
   St* ob = out + tok0 * D;
   const float* gq = gamma_q + (size_t)h * D;
   const float* gk = gamma_k + (size_t)h * D;
+
+  // K'^T rows [16 rt, +16) x tokens of k-block kb2; V (as V^T rows or as the B operand of
+  // the state update, the same fragment) for value columns [n0, n0 + 16) x k-block kb2
+  auto kt_frag = [&](int rt, int kb2) -> Frag<BF> {
+    if constexpr (BF) return lds_frag_tr(sK, G::ROWP, 32 * kb2, 16 * rt, lane);
+    else return lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, kb2, g);
+  };
+  auto v_frag = [&](int n0, int kb2) -> Frag<BF> {
+    if constexpr (BF) return lds_frag_tr(sV, G::ROWP, 32 * kb2, n0, lane);
+    else return lds_frag<BF>(sVT, G::COLP, n0 + c16, kb2, g);
+  };
 
   // running state S (this wave's value columns) and z, from the exclusive prefix
   const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
@@ -649,6 +694,9 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
     // ---- map
     {
       const float2* hirow = rope_hi + (size_t)((si.pos0 + c0) / kChunk) * G::HALF;
+      // The RMSNorm weights and the in-chunk RoPE table are the same for every chunk; hiding
+      // their addresses from the optimiser keeps it from holding ~64 loaded values in
+      // registers across the whole sweep (they are re-read from cache each chunk instead).
       const float* gqi = gq;
       const float* gki = gk;
       const float2* loi = rope_lo;
@@ -657,7 +705,8 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
       feature_map_qk<BF, D>(rq, rk, oq, ok, gqi, gki, loi, hirow, t0, m, rms_eps);
       store_rows<BF, D>(sQ, oq, t0, m);
       store_rows<BF, D>(sK, ok, t0, m);
-      store_cols<BF, D>(sKT, ok, t0, m);
+      if constexpr (!BF) store_cols<BF, D>(sKT, ok, t0, m);
+      // q'_t . z_prev of the two tokens, from the rounded q' the MFMA uses
 #pragma unroll
       for (int tok = 0; tok < 2; ++tok) {
         float p = 0.f;
@@ -673,7 +722,8 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
         if (m == 0) sQz[t0 + tok] = p;
       }
     }
-    store_cols<BF, D>(sVT, rv, t0, m);
+    if constexpr (BF) store_rows<BF, D>(sV, rv, t0, m);
+    else store_cols<BF, D>(sVT, rv, t0, m);
     if (c0 + kChunk < si.len) {
       const int nn = min(kChunk, si.len - c0 - kChunk);
       load_raw<BF, D>(rq, qb + (size_t)(c0 + kChunk) * D, t0, m, nn);
@@ -714,69 +764,59 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
       if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<BF>(At[2], At[3]);
       if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + sQz[tt * 16 + c16] + eps);
     }
-    // column sums of K' (z update; sZ is read again only after the next B1)
-    {
-      const int row = tid / ZP, part = tid % ZP;
-      const St* src = sKT + row * G::COLP + part * ZT;
-      float zs = 0.f;
-#pragma unroll
-      for (int t = 0; t < ZT; ++t) zs += EL::to_f(src[t]);
-#pragma unroll
-      for (int o = 1; o < ZP; o <<= 1) zs += __shfl_xor(zs, o);
-      if (part == 0) sZ[row] += zs;
-    }
-    __syncthreads();  // B3: score tiles and row reciprocals in LDS; K' rows are free
+    __syncthreads();  // B3: score tiles and row reciprocals in LDS
 
     // ---- out, then the state update
     if (wave < G::NW) {
       Frag<BF> Vf[G::CT][2];
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) {
-        const int vrow = wave * G::DVW + ct * 16 + c16;
-        Vf[ct][0] = lds_frag<BF>(sVT, G::COLP, vrow, 0, g);
-        Vf[ct][1] = lds_frag<BF>(sVT, G::COLP, vrow, 1, g);
+        Vf[ct][0] = v_frag(wave * G::DVW + ct * 16, 0);
+        Vf[ct][1] = v_frag(wave * G::DVW + ct * 16, 1);
       }
-      St* stage = sK + wave * (kChunk * G::DVW);
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) {
-        Frag<BF> Sb[G::KB];  // S rounded to the element type as the B operand
+        Frag<BF> Sa[G::KB];  // S^T rounded to the element type as the A operand
 #pragma unroll
-        for (int kb2 = 0; kb2 < G::KB; ++kb2) Sb[kb2] = acc_frag<BF>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
+        for (int kb2 = 0; kb2 < G::KB; ++kb2) Sa[kb2] = acc_frag<BF>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
+        const int col = wave * G::DVW + ct * 16 + 4 * g;
 #pragma unroll 1
         for (int tt = 0; tt < 4; ++tt) {
           floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kb2 = 0; kb2 < G::KB; ++kb2) o = mma(lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g), Sb[kb2], o);
-          o = mma(sA[(tt * 2) * 64 + lane], Vf[ct][0], o);
-          if (tt >= 2) o = mma(sA[(tt * 2 + 1) * 64 + lane], Vf[ct][1], o);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = tt * 16 + 4 * g + i;
-            stage[t * G::DVW + ct * 16 + c16] = EL::from_f(o[i] * sInv[t]);
+          for (int kb2 = 0; kb2 < G::KB; ++kb2) o = mma(Sa[kb2], lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g), o);
+          o = mma(Vf[ct][0], sA[(tt * 2) * 64 + lane], o);
+          if (tt >= 2) o = mma(Vf[ct][1], sA[(tt * 2 + 1) * 64 + lane], o);
+          const int t = tt * 16 + c16;  // this lane's query row; columns col .. col + 3
+          const float r = sInv[t];
+          if (t < nv) {
+            St* dst = ob + (size_t)(c0 + t) * D + col;
+            if constexpr (BF) {
+              const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[0] * r, o[1] * r}, bf16x2));
+              const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[2] * r, o[3] * r}, bf16x2));
+              *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(o[0] * r, o[1] * r, o[2] * r, o[3] * r);
+            }
           }
         }
       }
-      // S += K'^T V
+      // S += K'^T V; wave 0 also adds the column sums of K' to z (read again after B1)
 #pragma unroll
       for (int rt = 0; rt < G::RT; ++rt) {
-        const Frag<BF> a0 = lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, 0, g);
-        const Frag<BF> a1 = lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, 1, g);
+        const Frag<BF> a0 = kt_frag(rt, 0);
+        const Frag<BF> a1 = kt_frag(rt, 1);
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct) {
           S[rt][ct] = mma(a0, Vf[ct][0], S[rt][ct]);
           S[rt][ct] = mma(a1, Vf[ct][1], S[rt][ct]);
         }
-      }
-      // the staged rows of this wave's columns, as 16-byte pieces (wave-local exchange)
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-      for (int r = 0; r < PR; ++r) {
-        const int piece = lane + 64 * r;
-        const int t = piece / PR, pc = piece % PR;
-        if (t < nv)
-          copy_bytes<16>(ob + (size_t)(c0 + t) * D + wave * G::DVW + pc * PE, stage + t * G::DVW + pc * PE);
+        if (wave == 0) {
+          const Frag<BF> ones = ones_frag<BF>();
+          floatx4 zc = mma(a0, ones, floatx4{0.f, 0.f, 0.f, 0.f});
+          zc = mma(a1, ones, zc);  // every column holds the sums of rows 16 rt + 4g + i
+          if (c16 < 4) sZ[rt * 16 + 4 * g + c16] += zc[c16];
+        }
       }
     }
   }
