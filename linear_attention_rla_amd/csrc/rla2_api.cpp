@@ -60,7 +60,7 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   if (!supported_d(d->d)) return RLA2_ERR_UNSUPPORTED;
   if (d->dtype != RLA2_F32 && d->dtype != RLA2_BF16) return RLA2_ERR_UNSUPPORTED;
   if (d->chunk != rla2::kChunk) return RLA2_ERR_UNSUPPORTED;
-  if (d->seg_chunks < 0 || d->seg_chunks > (1 << 20)) return RLA2_ERR_BAD_VALUE;
+  if (d->seg_chunks < 0 || d->seg_chunks > rla2::kMaxSegChunks) return RLA2_ERR_BAD_VALUE;
   if (!finite_pos(d->eps) || !finite_pos(d->rms_eps) || !finite_pos(d->rope_base))
     return RLA2_ERR_BAD_VALUE;
   if (validate_mode() < 0) return RLA2_ERR_BAD_VALUE;
@@ -86,7 +86,7 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
     seg = d->seg_chunks * rla2::kChunk;
   } else {
     seg = rla2::kChunk;
-    for (int cand = 4096; cand >= rla2::kChunk; cand /= 2) {
+    for (int cand = rla2::kMaxSegChunks * rla2::kChunk; cand >= rla2::kChunk; cand /= 2) {
       long long wg = (long long)rows * ((L + cand - 1) / cand) * (p->H > 0 ? p->H : 1);
       if (wg >= 1024) { seg = cand; break; }
     }

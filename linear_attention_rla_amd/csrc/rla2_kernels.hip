@@ -46,6 +46,9 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufFlags = 0x00020000;  // gfx9 buffer resource word 3 (32-bit raw data)
 
 constexpr int NT = 256;  // threads per workgroup of the chunk kernels
 
@@ -325,6 +328,56 @@ __device__ __forceinline__ void feature_map_pair(const Raw<BF, D>& r, Raw<BF, D>
         rope_relu(r.get(tok, 0, e + x), r.get(tok, 1, e + x), inv, gamma[j], gamma[j + G::HALF],
                   angle_sum(rope_hi_row[j], lo[j]), u1[x], u2[x]);
       }
+      put_pairs<BF, D>(o, tok, e, u1, u2);
+    }
+  }
+}
+
+// load_raw through a buffer resource covering exactly the segment's tokens: reads past the
+// segment's end return zeros without touching memory, so the load is issued
+// unconditionally (a fixed number of loads per chunk keeps the wait counts exact).
+template <int D>
+__device__ __forceinline__ void load_raw_buf(Raw<true, D>& r, __amdgpu_buffer_rsrc_t rs, int tok, int m) {
+  using G = Geo<true, D>;
+  constexpr int NB = G::E * 2;  // bytes per (token, half) of this lane
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int off = ((tok + t) * D + hh * G::HALF + m * G::E) * 2;
+      if constexpr (NB == 16) {
+        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.w[t][hh][i] = x[i];
+      } else if constexpr (NB == 8) {
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        r.w[t][hh][0] = x[0];
+        r.w[t][hh][1] = x[1];
+      } else {
+        r.w[t][hh][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+      }
+    }
+}
+
+// The same map with every per-lane constant in registers: g1[e], g2[e] = gamma of dims
+// j, j + D/2 (j = m*E + e); lo[tok][e] = (cos, sin) of (t0 + tok)*theta_j; hi[e] = (cos, sin)
+// of 64*a*theta_j for the chunk's first position 64*a.
+template <bool BF, int D>
+__device__ __forceinline__ void feature_map_lane(const Raw<BF, D>& r, Raw<BF, D>& o, const float (&g1)[Geo<BF, D>::E],
+                                                 const float (&g2)[Geo<BF, D>::E],
+                                                 const float2 (&lo)[2][Geo<BF, D>::E],
+                                                 const float2 (&hi)[Geo<BF, D>::E], float rms_eps) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+    const float inv = rms_inv<BF, D>(r, tok, rms_eps);
+#pragma unroll
+    for (int e = 0; e < G::E; e += 2) {
+      float u1[2], u2[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        rope_relu(r.get(tok, 0, e + x), r.get(tok, 1, e + x), inv, g1[e + x], g2[e + x],
+                  angle_sum(hi[e + x], lo[tok][e + x]), u1[x], u2[x]);
       put_pairs<BF, D>(o, tok, e, u1, u2);
     }
   }
@@ -822,6 +875,280 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
   }
 }
 
+// chunk_out for bf16, warp-specialised: 8 waves, one workgroup per CU.
+//
+// Waves 4..7 ("mappers") turn raw q, k, v into the chunk operands: the feature map of q
+// and k (VALU work) and the Q', K', V rows in LDS. They keep two chunks of raw input in
+// flight in registers. Waves 0..3 ("MMA waves") run the score and output phases on the
+// previous chunk from the other half of a double-buffered LDS. Each SIMD holds one wave of
+// each kind, so the mappers' VALU work overlaps the MMA waves' matrix and LDS work, and the
+// input loads overlap both.
+//
+// Step s (s = 0 .. nsteps-1): mappers map chunk s into buffer s % 2; MMA waves write chunk
+// s - 2's staged output rows to memory, then process chunk s - 1 from buffer (s - 1) % 2.
+// Two workgroup barriers per step, outside every role branch:
+//   X  after the mappers' q' and the MMA waves' score phase (score tiles and row
+//      reciprocals are complete before anyone forms outputs)
+//   Y  at the end of the step (buffer s % 2 and the staged output are complete; buffer
+//      (s - 1) % 2 is free again; the z update of chunk s - 1 is visible)
+// The MMA waves form q'.z from the Q' fragments they already hold, since z changes within
+// the step that maps the next chunk. Output tiles are staged in LDS and leave as whole
+// 256-byte rows (a 4-row, 1 KB run per store instruction) instead of 8-byte pieces.
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const float* __restrict__ gamma_q, const float* __restrict__ gamma_k, const int32_t* __restrict__ tab,
+    const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
+    const float* __restrict__ states, uint16_t* __restrict__ out, int H, int L, float rms_eps, float eps) {
+  using G = Geo<true, D>;
+  using St = uint16_t;
+  using EL = Elem<true>;
+  using R = Raw<true, D>;
+  constexpr int BUF = kChunk * G::ROWP;  // elements of one operand buffer
+  __shared__ __attribute__((aligned(16))) St sQ[2 * BUF];
+  __shared__ __attribute__((aligned(16))) St sK[2 * BUF];
+  __shared__ __attribute__((aligned(16))) St sV[2 * BUF];
+  __shared__ __attribute__((aligned(16))) St sO[BUF];  // output rows of one chunk
+  __shared__ Frag<true> sA[4 * 2 * 64];  // [query tile][key block][lane]: B operands of V^T A^T
+  __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * G::HALF];  // RoPE rows of the chunks
+  __shared__ __attribute__((aligned(16))) float sZ[D];
+  __shared__ float sDz[D];  // column sums of the chunk's K', added to z after the score phase
+  __shared__ float sInv[kChunk];
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index and chunk count in scalar registers: the role branches below are uniform
+  // per wave, so every wave executes exactly its own role's barriers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
+  // steps 0 .. nch + 1 do work (the last one writes the last chunk's output); rounded up to
+  // even for the mappers' two-step loop
+  const int nsteps = (nch + 3) & ~1;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  if (tid < D) sZ[tid] = rec[D * D + tid];
+  {
+    const float2* hi0 = rope_hi + (size_t)(si.pos0 / kChunk) * G::HALF;
+    for (int i = tid; i < min(nch, kMaxSegChunks) * G::HALF; i += 512) sHi[i] = hi0[i];
+  }
+  __syncthreads();
+
+  if (wave >= 4) {
+    // ======== mappers: nsteps steps, two barriers each
+    const int mt = tid & 255;  // two tokens per 8 lanes
+    const int t0 = 2 * (mt >> 3), m = mt & 7;
+    const int seg_bytes = si.len * D * 2;
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + tok0 * D), 0, seg_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + tok0 * D), 0, seg_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
+    // per-lane constants: RMSNorm weights of this lane's dims, in-chunk RoPE angles of its tokens
+    float gq1[G::E], gq2[G::E], gk1[G::E], gk2[G::E];
+    float2 lo[2][G::E];
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) {
+      const int j = m * G::E + e;
+      gq1[e] = gamma_q[(size_t)h * D + j];
+      gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
+      gk1[e] = gamma_k[(size_t)h * D + j];
+      gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
+      lo[0][e] = rope_lo[t0 * G::HALF + j];
+      lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
+    }
+    // Every step issues the same loads (chunks past the end read zeros from the buffer
+    // range check), so the compiler's wait counts let chunk st + 1 stay in flight while
+    // chunk st is mapped.
+    auto issue = [&](R (&r)[3], int c) {
+      load_raw_buf<D>(r[0], rq, c * kChunk + t0, m);
+      load_raw_buf<D>(r[1], rk, c * kChunk + t0, m);
+      load_raw_buf<D>(r[2], rv, c * kChunk + t0, m);
+    };
+    auto mstep = [&](int st, R (&r)[3]) {
+      const int bm = (st & 1) * BUF;
+      float2 hi[G::E];
+      if (st < nch) {  // q'
+        copy_bytes<G::E * 8>(hi, sHi + st * G::HALF + m * G::E);
+        R o;
+        feature_map_lane<true, D>(r[0], o, gq1, gq2, lo, hi, rms_eps);
+        store_rows<true, D>(sQ + bm, o, t0, m);
+      }
+      __syncthreads();  // X
+      if (st < nch) {  // k', v
+        R o;
+        feature_map_lane<true, D>(r[1], o, gk1, gk2, lo, hi, rms_eps);
+        store_rows<true, D>(sK + bm, o, t0, m);
+        store_rows<true, D>(sV + bm, r[2], t0, m);
+      }
+      issue(r, st + 2);  // into the registers just consumed
+      __syncthreads();  // Y
+    };
+    R set0[3], set1[3];
+    issue(set0, 0);
+    issue(set1, 1);
+    for (int st = 0; st < nsteps; st += 2) {
+      mstep(st, set0);
+      mstep(st + 1, set1);
+    }
+    return;
+  }
+
+  // ======== MMA waves: nsteps steps, two barriers each; step st processes chunk st - 1
+  St* ob = out + tok0 * D;
+  floatx4 S[G::RT][G::CT];  // running state, value columns of this wave
+  {
+    const int wv = wave < G::NW ? wave : 0;
+#pragma unroll
+    for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[rt][ct][i] = rec[(rt * 16 + 4 * g + i) * D + wv * G::DVW + ct * 16 + c16];
+  }
+  // Accumulation order everywhere below: the contraction block is the outer loop and the
+  // independent accumulators the inner one, so consecutive MFMAs never wait on each other.
+  for (int st = 0; st < nsteps; ++st) {
+    const St* cQ = sQ + ((st + 1) & 1) * BUF;  // buffers holding chunk st - 1
+    const St* cK = sK + ((st + 1) & 1) * BUF;
+    const St* cV = sV + ((st + 1) & 1) * BUF;
+    const int c = st - 1;
+    const bool work = st >= 1 && st <= nch;
+    if (st >= 2 && st - 2 < nch) {  // ---- write out chunk st - 2's staged rows
+      constexpr int PPR = D / 8;          // 16-byte pieces per row
+      constexpr int RPI = 64 / PPR;       // rows per wave instruction
+      const int cw = st - 2;
+      const int nvw = min(kChunk, si.len - cw * kChunk);
+      St* ow = ob + (size_t)cw * kChunk * D;
+#pragma unroll
+      for (int i = 0; i < kChunk / (4 * RPI); ++i) {
+        const int r = (i * 4 + wave) * RPI + lane / PPR, pc = lane % PPR;
+        if (r < nvw) copy_bytes<16>(ow + (size_t)r * D + pc * 8, sO + r * G::ROWP + pc * 8);
+      }
+    }
+    if (work) {  // ---- score: wave w owns query tile w
+      const int tt = wave;
+      Frag<true> Qf[G::KB];
+#pragma unroll
+      for (int kb2 = 0; kb2 < G::KB; ++kb2) Qf[kb2] = lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb2, g);
+      // A^T tiles (rows = keys of tile kt, cols = queries of tile tt), causal: kt <= tt
+      floatx4 At[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb2 = 0; kb2 < G::KB; ++kb2)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          if (kt <= tt) At[kt] = mma(lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb2, g), Qf[kb2], At[kt]);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float a = At[kt][i];
+          if (kt > tt || (kt == tt && 4 * g + i > c16)) a = 0.f;  // key after the query token
+          a = EL::to_f(EL::from_f(a));                             // the weight the MFMA will use
+          At[kt][i] = a;
+          rs += a;
+        }
+      // q'.z of query 16 tt + c16 over the 32 dimensions of this lane's fragments
+#pragma unroll
+      for (int kb2 = 0; kb2 < G::KB; ++kb2) {
+        const float4 za = *reinterpret_cast<const float4*>(sZ + kb2 * 32 + 4 * g);
+        const float4 zb = *reinterpret_cast<const float4*>(sZ + kb2 * 32 + 16 + 4 * g);
+        const bf16x8 x = Qf[kb2].v;
+        rs += static_cast<float>(x[0]) * za.x + static_cast<float>(x[1]) * za.y +
+              static_cast<float>(x[2]) * za.z + static_cast<float>(x[3]) * za.w;
+        rs += static_cast<float>(x[4]) * zb.x + static_cast<float>(x[5]) * zb.y +
+              static_cast<float>(x[6]) * zb.z + static_cast<float>(x[7]) * zb.w;
+      }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);  // lanes with c16 == t: row sum + q'.z of query 16 tt + t
+      sA[(tt * 2) * 64 + lane] = acc_frag<true>(At[0], At[1]);
+      if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<true>(At[2], At[3]);
+      if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + eps);
+      if (wave == 0) {  // column sums of K' (the least loaded score wave); applied after X
+        const Frag<true> ones = ones_frag<true>();
+        floatx4 zc[G::RT];
+#pragma unroll
+        for (int rt = 0; rt < G::RT; ++rt) zc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int rt = 0; rt < G::RT; ++rt) zc[rt] = mma(lds_frag_tr(cK, G::ROWP, 32 * kb2, 16 * rt, lane), ones, zc[rt]);
+#pragma unroll
+        for (int rt = 0; rt < G::RT; ++rt)
+          if (c16 < 4) sDz[rt * 16 + 4 * g + c16] = zc[rt][c16];
+      }
+    }
+    __syncthreads();  // X
+    if (work && wave < G::NW) {  // ---- output (staged), then the state update
+      if (wave == 0)
+        for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];  // every q'.z of this chunk is done
+      Frag<true> Vf[G::CT][2];
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) {
+        Vf[ct][0] = lds_frag_tr(cV, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
+        Vf[ct][1] = lds_frag_tr(cV, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
+      }
+      // O^T for all 64 rows and this wave's columns: each Q' fragment is read once and
+      // serves every column tile
+      floatx4 o[G::CT][4];
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) o[ct][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb2 = 0; kb2 < G::KB; ++kb2) {
+        Frag<true> sa[G::CT];  // S^T rounded to bf16 as the A operand
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) sa[ct] = acc_frag<true>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const Frag<true> qf = lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb2, g);
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(sa[ct], qf, o[ct][tt]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const Frag<true> a0 = sA[(tt * 2) * 64 + lane];
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(Vf[ct][0], a0, o[ct][tt]);
+      }
+#pragma unroll
+      for (int tt = 2; tt < 4; ++tt) {
+        const Frag<true> a1 = sA[(tt * 2 + 1) * 64 + lane];
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(Vf[ct][1], a1, o[ct][tt]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int t = tt * 16 + c16;  // this lane's query row
+        const float rr = sInv[t];
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {  // columns col .. col + 3
+          const int col = wave * G::DVW + ct * 16 + 4 * g;
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[ct][tt][0] * rr, o[ct][tt][1] * rr}, bf16x2));
+          const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[ct][tt][2] * rr, o[ct][tt][3] * rr}, bf16x2));
+          *reinterpret_cast<uint2*>(sO + t * G::ROWP + col) = make_uint2(w0, w1);
+        }
+      }
+      // S += K'^T V
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int rt = 0; rt < G::RT; ++rt) {
+          const Frag<true> a = lds_frag_tr(cK, G::ROWP, 32 * kb2, 16 * rt, lane);
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) S[rt][ct] = mma(a, Vf[ct][kb2], S[rt][ct]);
+        }
+    }
+    __syncthreads();  // Y
+  }
+}
+
 // ----------------------------------------------------------------------------------------
 // decode: one workgroup per (sequence, head). Wave 0 maps q, wave 1 maps k (lane j holds the
 // RoPE pair j, j + D/2), then every thread updates D/... rows of a 4-column strip of S in place
@@ -962,9 +1289,15 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   }
   mark(4);
   if (fwd && p.n_seg_max > 0) {
-    hipLaunchKernelGGL((chunk_out_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
-                       static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
-                       a.gk, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+    if constexpr (BF) {
+      hipLaunchKernelGGL((chunk_out_ws_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
+                         static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
+                         a.gk, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+    } else {
+      hipLaunchKernelGGL((chunk_out_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                         static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
+                         a.gk, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+    }
   }
   mark(5);
   return hipGetLastError();
