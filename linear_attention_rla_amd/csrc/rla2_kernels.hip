@@ -336,19 +336,22 @@ __device__ __forceinline__ void feature_map_pair(const Raw<BF, D>& r, Raw<BF, D>
 // load_raw through a buffer resource covering exactly the segment's tokens: reads past the
 // segment's end return zeros without touching memory, so the load is issued
 // unconditionally (a fixed number of loads per chunk keeps the wait counts exact).
-template <int D>
-__device__ __forceinline__ void load_raw_buf(Raw<true, D>& r, __amdgpu_buffer_rsrc_t rs, int tok, int m) {
-  using G = Geo<true, D>;
-  constexpr int NB = G::E * 2;  // bytes per (token, half) of this lane
+template <bool BF, int D>
+__device__ __forceinline__ void load_raw_buf(Raw<BF, D>& r, __amdgpu_buffer_rsrc_t rs, int tok, int m) {
+  using G = Geo<BF, D>;
+  constexpr int NB = G::E * G::ES;  // bytes per (token, half) of this lane
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int off = ((tok + t) * D + hh * G::HALF + m * G::E) * 2;
-      if constexpr (NB == 16) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+      const int off = ((tok + t) * D + hh * G::HALF + m * G::E) * G::ES;
+      if constexpr (NB >= 16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.w[t][hh][i] = x[i];
+        for (int p = 0; p < NB / 16; ++p) {
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * p, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) r.w[t][hh][4 * p + i] = x[i];
+        }
       } else if constexpr (NB == 8) {
         const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
         r.w[t][hh][0] = x[0];
@@ -357,6 +360,17 @@ __device__ __forceinline__ void load_raw_buf(Raw<true, D>& r, __amdgpu_buffer_rs
         r.w[t][hh][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
       }
     }
+}
+
+// Per-segment state record: d*d + d floats. S is stored fragment-native: the 4 accumulator
+// values lane l of state wave w holds in tile (rt, ct) are contiguous, at
+//   rec_frag(w, rt, ct, l) = (((w * RT + rt) * CT + ct) * 64 + l) * 4,
+// which is S[16 rt + 4 (l / 16) + i][w * DVW + 16 ct + l % 16], i < 4; z follows at d*d.
+// Writers and readers move 16 bytes per lane; only the final-state export permutes.
+template <bool BF, int D>
+__device__ __forceinline__ int rec_frag(int w, int rt, int ct, int l) {
+  using G = Geo<BF, D>;
+  return (((w * G::RT + rt) * G::CT + ct) * 64 + l) * 4;
 }
 
 // The same map with every per-lane constant in registers: g1[e], g2[e] = gamma of dims
@@ -529,6 +543,14 @@ __global__ void rope_table_kernel(float2* __restrict__ lo, float2* __restrict__ 
 
 // ----------------------------------------------------------------------------------------
 // chunk_state: per (segment, head), T = Sum_chunks K'^T V and Sum K' over the segment.
+//
+// Per chunk: every lane maps two tokens of k and stores K' and V in LDS (bf16 row-major,
+// read back through the transposing LDS read; fp32 transposed), then the state waves add
+// K'^T V to their accumulators and K'^T 1 (the column sums of K', ZR row tiles per wave).
+// Raw k, v of the next two chunks are in flight in registers throughout (range-checked
+// buffer loads, issued unconditionally so the wait counts stay exact); the RoPE rows of
+// the segment sit in LDS and the per-lane RMSNorm weights and in-chunk angles in
+// registers, so no other vector-memory load is ever waited on inside the sweep.
 
 template <bool BF, int D>
 __global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
@@ -538,83 +560,125 @@ __global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
     int H, int L, float rms_eps) {
   using G = Geo<BF, D>;
   using St = typename G::St;
-  __shared__ __attribute__((aligned(16))) St sKT[D * G::COLP];
-  __shared__ __attribute__((aligned(16))) St sVT[D * G::COLP];
+  using R = Raw<BF, D>;
+  constexpr int KR = BF ? kChunk : D;           // rows of the K' and V arrays (row-major / transposed)
+  constexpr int KP = BF ? G::ROWP : G::COLP;    // their pitch
+  constexpr int ZR = G::RT >= 4 ? G::RT / 4 : 1;  // row tiles of the column sums per wave
+  __shared__ __attribute__((aligned(16))) St sKx[KR * KP];
+  __shared__ __attribute__((aligned(16))) St sVx[KR * KP];
+  __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * G::HALF];  // RoPE rows of the chunks
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;
   const SegInfo si = read_seg(tab, seg);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
   const int t0 = 2 * (tid >> 3), m = tid & 7;
   const int c16 = lane & 15, g = lane >> 4;
   const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
-  const St* kb = k + tok0 * D;
-  const St* vb = v + tok0 * D;
-  const float* gk = gamma_k + (size_t)h * D;
+  const int seg_bytes = si.len * D * G::ES;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + tok0 * D), 0, seg_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
+  {
+    const float2* hi0 = rope_hi + (size_t)(si.pos0 / kChunk) * G::HALF;
+    for (int i = tid; i < min(nch, kMaxSegChunks) * G::HALF; i += NT) sHi[i] = hi0[i];
+  }
+  float g1[G::E], g2[G::E];
+  float2 lo[2][G::E];
+#pragma unroll
+  for (int e = 0; e < G::E; ++e) {
+    const int j = m * G::E + e;
+    g1[e] = gamma_k[(size_t)h * D + j];
+    g2[e] = gamma_k[(size_t)h * D + j + G::HALF];
+    lo[0][e] = rope_lo[t0 * G::HALF + j];
+    lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
+  }
+
+  auto kt_frag = [&](int rt, int kb2) -> Frag<BF> {  // K'^T rows [16 rt, +16), tokens of block kb2
+    if constexpr (BF) return lds_frag_tr(sKx, KP, 32 * kb2, 16 * rt, lane);
+    else return lds_frag<BF>(sKx, KP, rt * 16 + c16, kb2, g);
+  };
+  auto v_frag = [&](int n0, int kb2) -> Frag<BF> {  // V columns [n0, n0 + 16), tokens of block kb2
+    if constexpr (BF) return lds_frag_tr(sVx, KP, 32 * kb2, n0, lane);
+    else return lds_frag<BF>(sVx, KP, n0 + c16, kb2, g);
+  };
 
   floatx4 acc[G::RT][G::CT];
+  floatx4 zc[ZR];
 #pragma unroll
   for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float zacc = 0.f;
+#pragma unroll
+  for (int zr = 0; zr < ZR; ++zr) zc[zr] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const bool zwave = wave * ZR < G::RT;
 
-  Raw<BF, D> rk, rv;
-  load_raw<BF, D>(rk, kb, t0, m, min(kChunk, si.len));
-  load_raw<BF, D>(rv, vb, t0, m, min(kChunk, si.len));
-  for (int c0 = 0; c0 < si.len; c0 += kChunk) {
-    __syncthreads();  // previous chunk's LDS reads are done
-    {
-      Raw<BF, D> o;
-      feature_map_pair<BF, D>(rk, o, gk, rope_lo, rope_hi + (size_t)((si.pos0 + c0) / kChunk) * G::HALF, t0, m,
-                              rms_eps);
-      store_cols<BF, D>(sKT, o, t0, m);
+  auto issue = [&](R (&r)[2], int c) {
+    load_raw_buf<BF, D>(r[0], rk, c * kChunk + t0, m);
+    load_raw_buf<BF, D>(r[1], rv, c * kChunk + t0, m);
+  };
+  auto step = [&](int c, R (&r)[2]) {
+    __syncthreads();  // the previous chunk's LDS reads are done (the first time: sHi is written)
+    if (c < nch) {
+      float2 hi[G::E];
+      copy_bytes<G::E * 8>(hi, sHi + c * G::HALF + m * G::E);
+      R o;
+      feature_map_lane<BF, D>(r[0], o, g1, g2, lo, hi, rms_eps);
+      if constexpr (BF) {
+        store_rows<BF, D>(sKx, o, t0, m);
+        store_rows<BF, D>(sVx, r[1], t0, m);
+      } else {
+        store_cols<BF, D>(sKx, o, t0, m);
+        store_cols<BF, D>(sVx, r[1], t0, m);
+      }
     }
-    store_cols<BF, D>(sVT, rv, t0, m);
-    if (c0 + kChunk < si.len) {
-      const int nv = min(kChunk, si.len - c0 - kChunk);
-      load_raw<BF, D>(rk, kb + (size_t)(c0 + kChunk) * D, t0, m, nv);
-      load_raw<BF, D>(rv, vb + (size_t)(c0 + kChunk) * D, t0, m, nv);
-    }
+    issue(r, c + 2);  // into the registers just consumed
     __syncthreads();
-    if (tid < D) {
-      float s = 0.f;
-      const St* row = sKT + tid * G::COLP;
-#pragma unroll 8
-      for (int t = 0; t < kChunk; ++t) s += Elem<BF>::to_f(row[t]);
-      zacc += s;
-    }
-    if (wave < G::NW) {
+    if (c < nch && wave < G::NW) {
       Frag<BF> Vf[G::CT][2];
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) {
-        const int vrow = wave * G::DVW + ct * 16 + c16;
-        Vf[ct][0] = lds_frag<BF>(sVT, G::COLP, vrow, 0, g);
-        Vf[ct][1] = lds_frag<BF>(sVT, G::COLP, vrow, 1, g);
+        Vf[ct][0] = v_frag(wave * G::DVW + ct * 16, 0);
+        Vf[ct][1] = v_frag(wave * G::DVW + ct * 16, 1);
       }
 #pragma unroll
-      for (int rt = 0; rt < G::RT; ++rt) {
-        const Frag<BF> a0 = lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, 0, g);
-        const Frag<BF> a1 = lds_frag<BF>(sKT, G::COLP, rt * 16 + c16, 1, g);
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) {
-          acc[rt][ct] = mma(a0, Vf[ct][0], acc[rt][ct]);
-          acc[rt][ct] = mma(a1, Vf[ct][1], acc[rt][ct]);
+        for (int rt = 0; rt < G::RT; ++rt) {
+          const Frag<BF> a = kt_frag(rt, kb2);
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) acc[rt][ct] = mma(a, Vf[ct][kb2], acc[rt][ct]);
         }
+      if (zwave) {
+        const Frag<BF> ones = ones_frag<BF>();
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int zr = 0; zr < ZR; ++zr) zc[zr] = mma(kt_frag(wave * ZR + zr, kb2), ones, zc[zr]);
       }
     }
+  };
+  R set0[2], set1[2];
+  issue(set0, 0);
+  issue(set1, 1);
+  for (int c = 0; c < nch; c += 2) {
+    step(c, set0);
+    step(c + 1, set1);
   }
+
   float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
   if (wave < G::NW) {
 #pragma unroll
     for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          rec[(rt * 16 + 4 * g + i) * D + wave * G::DVW + ct * 16 + c16] = acc[rt][ct][i];
+        *reinterpret_cast<floatx4*>(rec + rec_frag<BF, D>(wave, rt, ct, lane)) = acc[rt][ct];
   }
-  if (tid < D) rec[D * D + tid] = zacc;
+  if (zwave && c16 < 4) {  // every column of zc holds the sums of rows 16 rt + 4g + i
+#pragma unroll
+    for (int zr = 0; zr < ZR; ++zr) rec[D * D + (wave * ZR + zr) * 16 + 4 * g + c16] = zc[zr][c16];
+  }
 }
 
 // ----------------------------------------------------------------------------------------
@@ -650,8 +714,17 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
     }
   }
   const int e = 4 * e4;
-  if (final_S != nullptr && e < D * D)
-    *reinterpret_cast<float4*>(final_S + ((size_t)doc * H + h) * D * D + e) = run;
+  if (final_S != nullptr && e < D * D) {  // fragment-native record -> row-major [d][d]
+    const int RT = D / 16, NW = D / 16 < 4 ? D / 16 : 4, CT = D / NW / 16;
+    const int ln = e4 % 64, tile = e4 / 64;
+    const int ct = tile % CT, rt = (tile / CT) % RT, w = tile / CT / RT;
+    const int row = 16 * rt + 4 * (ln / 16), col = w * (D / NW) + 16 * ct + ln % 16;
+    float* dst = final_S + ((size_t)doc * H + h) * D * D + (size_t)row * D + col;
+    dst[0] = run.x;
+    dst[D] = run.y;
+    dst[2 * D] = run.z;
+    dst[3 * D] = run.w;
+  }
   if (final_z != nullptr && e >= D * D)
     *reinterpret_cast<float4*>(final_z + ((size_t)doc * H + h) * D + (e - D * D)) = run;
 }
@@ -728,8 +801,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
     for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[rt][ct][i] = rec[(rt * 16 + 4 * g + i) * D + wv * G::DVW + ct * 16 + c16];
+        S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, rt, ct, lane));
   }
   if (tid < D) sZ[tid] = rec[D * D + tid];
 
@@ -962,9 +1034,9 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     // range check), so the compiler's wait counts let chunk st + 1 stay in flight while
     // chunk st is mapped.
     auto issue = [&](R (&r)[3], int c) {
-      load_raw_buf<D>(r[0], rq, c * kChunk + t0, m);
-      load_raw_buf<D>(r[1], rk, c * kChunk + t0, m);
-      load_raw_buf<D>(r[2], rv, c * kChunk + t0, m);
+      load_raw_buf<true, D>(r[0], rq, c * kChunk + t0, m);
+      load_raw_buf<true, D>(r[1], rk, c * kChunk + t0, m);
+      load_raw_buf<true, D>(r[2], rv, c * kChunk + t0, m);
     };
     auto mstep = [&](int st, R (&r)[3]) {
       const int bm = (st & 1) * BUF;
@@ -1004,8 +1076,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) S[rt][ct][i] = rec[(rt * 16 + 4 * g + i) * D + wv * G::DVW + ct * 16 + c16];
+        S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<true, D>(wv, rt, ct, lane));
   }
   // Accumulation order everywhere below: the contraction block is the outer loop and the
   // independent accumulators the inner one, so consecutive MFMAs never wait on each other.
