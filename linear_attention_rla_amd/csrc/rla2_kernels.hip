@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 #include <type_traits>
 
 #include "rla2_internal.h"
@@ -49,6 +51,10 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufFlags = 0x00020000;  // gfx9 buffer resource word 3 (32-bit raw data)
+// Cache policy of the streaming input loads (the slc bit: each input byte is read once per
+// kernel). Measured on the long-context forward: it keeps the segment records and the
+// reused small tables resident and speeds up every forward kernel.
+constexpr int kLoadStream = 2;
 
 constexpr int NT = 256;  // threads per workgroup of the chunk kernels
 
@@ -348,16 +354,16 @@ __device__ __forceinline__ void load_raw_buf(Raw<BF, D>& r, __amdgpu_buffer_rsrc
       if constexpr (NB >= 16) {
 #pragma unroll
         for (int p = 0; p < NB / 16; ++p) {
-          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * p, 0, 0);
+          const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 16 * p, 0, kLoadStream);
 #pragma unroll
           for (int i = 0; i < 4; ++i) r.w[t][hh][4 * p + i] = x[i];
         }
       } else if constexpr (NB == 8) {
-        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kLoadStream);
         r.w[t][hh][0] = x[0];
         r.w[t][hh][1] = x[1];
       } else {
-        r.w[t][hh][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        r.w[t][hh][0] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kLoadStream);
       }
     }
 }
@@ -673,7 +679,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
     for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct)
-        *reinterpret_cast<floatx4*>(rec + rec_frag<BF, D>(wave, rt, ct, lane)) = acc[rt][ct];
+        __builtin_nontemporal_store(acc[rt][ct], reinterpret_cast<floatx4*>(rec + rec_frag<BF, D>(wave, rt, ct, lane)));
   }
   if (zwave && c16 < 4) {  // every column of zc holds the sums of rows 16 rt + 4g + i
 #pragma unroll
@@ -1095,7 +1101,9 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
       for (int i = 0; i < kChunk / (4 * RPI); ++i) {
         const int r = (i * 4 + wave) * RPI + lane / PPR, pc = lane % PPR;
-        if (r < nvw) copy_bytes<16>(ow + (size_t)r * D + pc * 8, sO + r * G::ROWP + pc * 8);
+        if (r < nvw)  // streaming store: the output is not read again here
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sO + r * G::ROWP + pc * 8),
+                                      reinterpret_cast<u32x4*>(ow + (size_t)r * D + pc * 8));
       }
     }
     if (work) {  // ---- score: wave w owns query tile w
@@ -1221,9 +1229,16 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 }
 
 // ----------------------------------------------------------------------------------------
-// decode: one workgroup per (sequence, head). Wave 0 maps q, wave 1 maps k (lane j holds the
-// RoPE pair j, j + D/2), then every thread updates D/... rows of a 4-column strip of S in place
-// and accumulates its share of q' S; the partial read-outs meet in LDS.
+// decode: one workgroup per (sequence, head). Every global load is issued first (the fp32
+// state rows of each thread, then z, v and the new token's q, k), so the state traffic is in
+// flight while wave 0 maps q and wave 1 maps k (lane j holds the RoPE pair j, j + D/2; the
+// frequencies come from the host in fp64 and the angle is formed in fp64). Then every
+// thread updates D/RG rows of a 4-column strip of S in place and accumulates its share of
+// q'S; the partial read-outs meet in LDS.
+
+struct Theta {
+  double t[64];  // base^(-2j/d), j < d/2, computed on the host in fp64
+};
 
 template <bool BF, int D>
 __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St* __restrict__ q,
@@ -1231,10 +1246,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St
                                                      const typename Elem<BF>::St* __restrict__ v,
                                                      const int32_t* __restrict__ positions,
                                                      const float* __restrict__ gamma_q,
-                                                     const float* __restrict__ gamma_k, float rms_eps,
-                                                     float rope_base, float eps, float* __restrict__ S,
-                                                     float* __restrict__ z, typename Elem<BF>::St* __restrict__ out,
-                                                     int H) {
+                                                     const float* __restrict__ gamma_k, float rms_eps, Theta th,
+                                                     float eps, float* __restrict__ S, float* __restrict__ z,
+                                                     typename Elem<BF>::St* __restrict__ out, int H) {
   using EL = Elem<BF>;
   constexpr int HALF = D / 2;
   constexpr int C4 = D / 4;           // 4-column strips
@@ -1250,32 +1264,44 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St
   const size_t base = (size_t)nh * D;
   float* Sp = S + (size_t)nh * D * D;
 
-  // issue the state loads first: they dominate the traffic
+  // every global load first: the state dominates the traffic. Plain loads with streaming
+  // (nontemporal) stores measured fastest for this in-place read-modify-write.
   const int c4 = tid % C4, rg = tid / C4;
   floatx4 st[RPT];
 #pragma unroll
   for (int r = 0; r < RPT; ++r)
-    st[r] = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(Sp + (size_t)(rg + r * RG) * D) + c4);
-
+    st[r] = *(reinterpret_cast<const floatx4*>(Sp + (size_t)(rg + r * RG) * D) + c4);
+  float zold = 0.f, vv = 0.f;
+  if (tid < D) {
+    zold = z[base + tid];
+    vv = EL::to_f(v[base + tid]);
+  }
+  float x1 = 0.f, x2 = 0.f, gm1 = 0.f, gm2 = 0.f;
+  int p = 0;
   if (wave < 2 && lane < HALF) {
     const typename EL::St* x = (wave == 0 ? q : k) + base;
     const float* gm = (wave == 0 ? gamma_q : gamma_k) + (size_t)h * D;
-    const float x1 = EL::to_f(x[lane]), x2 = EL::to_f(x[lane + HALF]);
+    x1 = EL::to_f(x[lane]);
+    x2 = EL::to_f(x[lane + HALF]);
+    gm1 = gm[lane];
+    gm2 = gm[lane + HALF];
+    p = max(positions[n], 0);
+  }
+
+  if (wave < 2 && lane < HALF) {
     float ss = x1 * x1 + x2 * x2;
 #pragma unroll
     for (int o = 1; o < HALF; o <<= 1) ss += __shfl_xor(ss, o);
     const float inv = 1.0f / sqrtf(ss * (1.0f / D) + rms_eps);
-    const float y1 = x1 * inv * gm[lane], y2 = x2 * inv * gm[lane + HALF];
-    const int p = max(positions[n], 0);
-    const double theta = pow((double)rope_base, -2.0 * (double)lane / (double)D);
+    const float y1 = x1 * inv * gm1, y2 = x2 * inv * gm2;
     double sd, cd;
-    sincos((double)p * theta, &sd, &cd);
+    sincos((double)p * th.t[lane], &sd, &cd);
     const float c = (float)cd, s = (float)sd;
     float* dst = wave == 0 ? sq : sk;
     dst[lane] = EL::to_f(EL::from_f(fmaxf(y1 * c - y2 * s, 0.f)));
     dst[lane + HALF] = EL::to_f(EL::from_f(fmaxf(y2 * c + y1 * s, 0.f)));
   }
-  if (tid < D) sv[tid] = EL::to_f(v[base + tid]);
+  if (tid < D) sv[tid] = vv;
   __syncthreads();
 
   const float v0 = sv[4 * c4], v1 = sv[4 * c4 + 1], v2 = sv[4 * c4 + 2], v3 = sv[4 * c4 + 3];
@@ -1303,7 +1329,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St
   // z += k'; den = q' . z_new
   float dz = 0.f;
   if (tid < D) {
-    const float zn = z[base + tid] + sk[tid];
+    const float zn = zold + sk[tid];
     z[base + tid] = zn;
     dz = sq[tid] * zn;
   }
@@ -1379,9 +1405,11 @@ hipError_t run_decode(int N, int H, const void* q, const void* k, const void* v,
                       const float* gq, const float* gk, float rms_eps, float rope_base, float eps, float* S,
                       float* z, void* out, hipStream_t s) {
   using St = typename Elem<BF>::St;
+  Theta th{};
+  for (int j = 0; j < D / 2; ++j) th.t[j] = std::pow((double)rope_base, -2.0 * (double)j / (double)D);
   hipLaunchKernelGGL((decode_kernel<BF, D>), dim3(N * H), dim3(256), 0, s, static_cast<const St*>(q),
-                     static_cast<const St*>(k), static_cast<const St*>(v), pos, gq, gk, rms_eps, rope_base, eps, S,
-                     z, static_cast<St*>(out), H);
+                     static_cast<const St*>(k), static_cast<const St*>(v), pos, gq, gk, rms_eps, th, eps, S, z,
+                     static_cast<St*>(out), H);
   return hipGetLastError();
 }
 
