@@ -100,6 +100,28 @@ __device__ __forceinline__ void copy_bytes(void* dst, const void* src) {
 }
 
 // ----------------------------------------------------------------------------------------
+// cross-lane sums on the VALU (DPP and the gfx950 lane-swap instructions), no LDS traffic
+
+// Sum over each aligned group of 8 lanes, returned in all 8: quad_perm [1,0,3,2] and
+// [2,3,0,1] add the lanes of a quad, row_half_mirror (lane i <- 7 - i) adds the other quad.
+__device__ __forceinline__ float sum8(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));
+  return x;
+}
+
+// Sum of lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows), returned in all of them.
+// Swapping row pairs of a value with itself yields one copy of each row of the pair in the
+// two results, so their sum is the pair sum in every lane; rows 16 apart first, then halves.
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+  x = __int_as_float(a[0]) + __int_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
+// ----------------------------------------------------------------------------------------
 // geometry of the chunk kernels for head dim D and element type
 
 template <bool BF, int D>
@@ -276,9 +298,7 @@ __device__ __forceinline__ float rms_inv(const Raw<BF, D>& r, int tok, float rms
       ss += b * b;
     }
   }
-  ss += __shfl_xor(ss, 1);
-  ss += __shfl_xor(ss, 2);
-  ss += __shfl_xor(ss, 4);
+  ss = sum8(ss);
   return rsqrtf(ss * (1.0f / D) + rms_eps);
 }
 
@@ -847,9 +867,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
           p += oq.get(tok, 0, e) * sZ[j];
           p += oq.get(tok, 1, e) * sZ[j + G::HALF];
         }
-        p += __shfl_xor(p, 1);
-        p += __shfl_xor(p, 2);
-        p += __shfl_xor(p, 4);
+        p = sum8(p);
         if (m == 0) sQz[t0 + tok] = p;
       }
     }
@@ -889,8 +907,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
           }
         }
       }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);  // every lane with c16 == t holds the row sum of query 16*tt + t
+      rs = sum_rows4(rs);  // every lane with c16 == t holds the row sum of query 16*tt + t
       sA[(tt * 2) * 64 + lane] = acc_frag<BF>(At[0], At[1]);
       if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<BF>(At[2], At[3]);
       if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + sQz[tt * 16 + c16] + eps);
@@ -993,6 +1010,9 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   __shared__ __attribute__((aligned(16))) float sZ[D];
   __shared__ float sDz[D];  // column sums of the chunk's K', added to z after the score phase
   __shared__ float sInv[kChunk];
+  // z as an MFMA A operand: row 0 = bf16(z), row 1 = bf16(z - bf16(z)), rows 2..15 = 0, so
+  // Z Q'^T gives q'.z (to ~2^-17 relative) in rows 0 + 1 of each query column
+  __shared__ Frag<true> sZf[G::KB * 64];
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;  // the whole workgroup leaves together
@@ -1009,6 +1029,26 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
   const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
   if (tid < D) sZ[tid] = rec[D * D + tid];
+  // z operand fragments: slot (g, j) of fragment kb holds dim kb*32 + 4g + j (j < 4) or
+  // kb*32 + 16 + 4g + j - 4; lane 16g holds bf16(z) there, lane 16g + 1 the residual, every
+  // other lane zeros (written once). Wave 0 refreshes the two data lanes of each fragment:
+  // lane l converts dims 2l, 2l + 1.
+  auto put_zf = [&](const float* zsrc) {
+    uint16_t* zf16 = reinterpret_cast<uint16_t*>(sZf);
+#pragma unroll
+    for (int x = 0; x < 2 && 2 * lane + x < D; ++x) {
+      const int dim = 2 * lane + x, kb2 = dim / 32, r = dim % 32;
+      const int gg = (r & 15) >> 2, j = (r & 3) + (r >> 4) * 4;
+      const float zv = zsrc[dim];
+      const __bf16 hi = static_cast<__bf16>(zv);
+      const __bf16 lo = static_cast<__bf16>(zv - static_cast<float>(hi));
+      zf16[(kb2 * 64 + 16 * gg) * 8 + j] = __builtin_bit_cast(uint16_t, hi);
+      zf16[(kb2 * 64 + 16 * gg + 1) * 8 + j] = __builtin_bit_cast(uint16_t, lo);
+    }
+  };
+  for (int i = tid; i < G::KB * 64; i += 512) sZf[i] = Frag<true>{};
+  __syncthreads();
+  if (wave == 0) put_zf(rec + D * D);
   {
     const float2* hi0 = rope_hi + (size_t)(si.pos0 / kChunk) * G::HALF;
     for (int i = tid; i < min(nch, kMaxSegChunks) * G::HALF; i += 512) sHi[i] = hi0[i];
@@ -1047,18 +1087,18 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     auto mstep = [&](int st, R (&r)[3]) {
       const int bm = (st & 1) * BUF;
       float2 hi[G::E];
-      if (st < nch) {  // q'
+      if (st < nch) {  // q', v
         copy_bytes<G::E * 8>(hi, sHi + st * G::HALF + m * G::E);
         R o;
         feature_map_lane<true, D>(r[0], o, gq1, gq2, lo, hi, rms_eps);
         store_rows<true, D>(sQ + bm, o, t0, m);
+        store_rows<true, D>(sV + bm, r[2], t0, m);
       }
       __syncthreads();  // X
-      if (st < nch) {  // k', v
+      if (st < nch) {  // k'
         R o;
         feature_map_lane<true, D>(r[1], o, gk1, gk2, lo, hi, rms_eps);
         store_rows<true, D>(sK + bm, o, t0, m);
-        store_rows<true, D>(sV + bm, r[2], t0, m);
       }
       issue(r, st + 2);  // into the registers just consumed
       __syncthreads();  // Y
@@ -1111,15 +1151,24 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       Frag<true> Qf[G::KB];
 #pragma unroll
       for (int kb2 = 0; kb2 < G::KB; ++kb2) Qf[kb2] = lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb2, g);
-      // A^T tiles (rows = keys of tile kt, cols = queries of tile tt), causal: kt <= tt
+      // A^T tiles (rows = keys of tile kt, cols = queries of tile tt), causal: kt <= tt; and
+      // Z Q'^T for q'.z
       floatx4 At[4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      floatx4 zq = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb2 = 0; kb2 < G::KB; ++kb2)
+      for (int kb2 = 0; kb2 < G::KB; ++kb2) {
+        Frag<true> kf[4];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
-          if (kt <= tt) At[kt] = mma(lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb2, g), Qf[kb2], At[kt]);
+          if (kt <= tt) kf[kt] = lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb2, g);
+        const Frag<true> zf = sZf[kb2 * 64 + lane];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          if (kt <= tt) At[kt] = mma(kf[kt], Qf[kb2], At[kt]);
+        zq = mma(zf, Qf[kb2], zq);
+      }
       float rs = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -1131,19 +1180,8 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
           At[kt][i] = a;
           rs += a;
         }
-      // q'.z of query 16 tt + c16 over the 32 dimensions of this lane's fragments
-#pragma unroll
-      for (int kb2 = 0; kb2 < G::KB; ++kb2) {
-        const float4 za = *reinterpret_cast<const float4*>(sZ + kb2 * 32 + 4 * g);
-        const float4 zb = *reinterpret_cast<const float4*>(sZ + kb2 * 32 + 16 + 4 * g);
-        const bf16x8 x = Qf[kb2].v;
-        rs += static_cast<float>(x[0]) * za.x + static_cast<float>(x[1]) * za.y +
-              static_cast<float>(x[2]) * za.z + static_cast<float>(x[3]) * za.w;
-        rs += static_cast<float>(x[4]) * zb.x + static_cast<float>(x[5]) * zb.y +
-              static_cast<float>(x[6]) * zb.z + static_cast<float>(x[7]) * zb.w;
-      }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);  // lanes with c16 == t: row sum + q'.z of query 16 tt + t
+      if (g == 0) rs += zq[0] + zq[1];  // q'.z of query 16 tt + c16 (rows 0, 1 of Z Q'^T)
+      rs = sum_rows4(rs);  // lanes with c16 == t: row sum + q'.z of query 16 tt + t
       sA[(tt * 2) * 64 + lane] = acc_frag<true>(At[0], At[1]);
       if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<true>(At[2], At[3]);
       if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + eps);
@@ -1163,8 +1201,13 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     }
     __syncthreads();  // X
     if (work && wave < G::NW) {  // ---- output (staged), then the state update
-      if (wave == 0)
-        for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];  // every q'.z of this chunk is done
+      if (wave == 0) {  // every q'.z of this chunk is done: advance z and its operand
+        for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        put_zf(sZ);
+      }
       Frag<true> Vf[G::CT][2];
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) {
