@@ -51,9 +51,9 @@ typedef float float2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufFlags = 0x00020000;  // gfx9 buffer resource word 3 (32-bit raw data)
-// Cache policy of the streaming input loads (the slc bit: each input byte is read once per
-// kernel). Measured on the long-context forward: it keeps the segment records and the
-// reused small tables resident and speeds up every forward kernel.
+// Cache policy of the streaming input loads and output stores (the slc bit: each byte is
+// touched once per kernel). Measured on the long-context forward: it keeps the segment
+// records and the reused small tables resident and speeds up every forward kernel.
 constexpr int kLoadStream = 2;
 
 constexpr int NT = 256;  // threads per workgroup of the chunk kernels
@@ -979,8 +979,9 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
 // each kind, so the mappers' VALU work overlaps the MMA waves' matrix and LDS work, and the
 // input loads overlap both.
 //
-// Step s (s = 0 .. nsteps-1): mappers map chunk s into buffer s % 2; MMA waves write chunk
-// s - 2's staged output rows to memory, then process chunk s - 1 from buffer (s - 1) % 2.
+// Step s (s = 0 .. nsteps-1): mappers map chunk s into buffer s % 2 and write chunk s - 2's
+// output rows (staged in LDS by the MMA waves) to memory; MMA waves process chunk s - 1 from
+// buffer (s - 1) % 2.
 // Two workgroup barriers per step, outside every role branch:
 //   X  after the mappers' q' and the MMA waves' score phase (score tiles and row
 //      reciprocals are complete before anyone forms outputs)
@@ -1063,6 +1064,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + tok0 * D), 0, seg_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + tok0 * D), 0, seg_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + tok0 * D), 0, seg_bytes, kBufFlags);
     // per-lane constants: RMSNorm weights of this lane's dims, in-chunk RoPE angles of its tokens
     float gq1[G::E], gq2[G::E], gk1[G::E], gk2[G::E];
     float2 lo[2][G::E];
@@ -1093,6 +1095,21 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
         feature_map_lane<true, D>(r[0], o, gq1, gq2, lo, hi, rms_eps);
         store_rows<true, D>(sQ + bm, o, t0, m);
         store_rows<true, D>(sV + bm, r[2], t0, m);
+      }
+      {  // chunk st - 2's output rows, staged by the MMA waves, leave as whole rows. The same
+         // stores are issued every step: rows past the segment (and every row when there is
+         // no such chunk) fall outside the buffer range and are dropped.
+        constexpr int PPR = D / 8;     // 16-byte pieces per row
+        constexpr int RPI = 64 / PPR;  // rows per wave instruction
+        const int cw = st - 2;
+        const bool any = cw >= 0 && cw < nch;
+#pragma unroll
+        for (int i = 0; i < kChunk / (4 * RPI); ++i) {
+          const int rr = (i * 4 + wave - 4) * RPI + lane / PPR, pc = lane % PPR;
+          const int off = any ? ((cw * kChunk + rr) * D + pc * 8) * 2 : seg_bytes;
+          __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(sO + rr * G::ROWP + pc * 8), ro, off, 0,
+                                                 kLoadStream);
+        }
       }
       __syncthreads();  // X
       if (st < nch) {  // k'
@@ -1132,20 +1149,6 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const St* cV = sV + ((st + 1) & 1) * BUF;
     const int c = st - 1;
     const bool work = st >= 1 && st <= nch;
-    if (st >= 2 && st - 2 < nch) {  // ---- write out chunk st - 2's staged rows
-      constexpr int PPR = D / 8;          // 16-byte pieces per row
-      constexpr int RPI = 64 / PPR;       // rows per wave instruction
-      const int cw = st - 2;
-      const int nvw = min(kChunk, si.len - cw * kChunk);
-      St* ow = ob + (size_t)cw * kChunk * D;
-#pragma unroll
-      for (int i = 0; i < kChunk / (4 * RPI); ++i) {
-        const int r = (i * 4 + wave) * RPI + lane / PPR, pc = lane % PPR;
-        if (r < nvw)  // streaming store: the output is not read again here
-          __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(sO + r * G::ROWP + pc * 8),
-                                      reinterpret_cast<u32x4*>(ow + (size_t)r * D + pc * 8));
-      }
-    }
     if (work) {  // ---- score: wave w owns query tile w
       const int tt = wave;
       Frag<true> Qf[G::KB];
