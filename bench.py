@@ -200,7 +200,7 @@ def main():
         "kernel_ms": dict(zip(KERNELS, per_kernel)),
         "roofline": {"kernel": "chunk_out", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("chunk_out_kernel"), "algorithmic_bytes": nbytes},
+                     "traffic": measured_traffic("chunk_out_ws_kernel"), "algorithmic_bytes": nbytes},
         "relu_zero_fraction": {"q": zeros_q, "k": zeros_k},
     }
 
