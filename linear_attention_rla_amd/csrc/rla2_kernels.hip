@@ -722,14 +722,15 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
   const int s0 = docoff[doc], s1 = docoff[doc + 1];
   float4* st = reinterpret_cast<float4*>(states);
   float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = s0; s < s1; s += 8) {
-    const int cnt = min(8, s1 - s);
-    float4 val[8];
+  constexpr int kBatch = 16;  // records in flight per thread
+  for (int s = s0; s < s1; s += kBatch) {
+    const int cnt = min(kBatch, s1 - s);
+    float4 val[kBatch];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kBatch; ++j)
       if (j < cnt) val[j] = st[((size_t)(s + j) * H + h) * R4 + e4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kBatch; ++j) {
       if (j < cnt) {
         if (write_prefix) st[((size_t)(s + j) * H + h) * R4 + e4] = run;
         run.x += val[j].x;
