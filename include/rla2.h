@@ -63,7 +63,7 @@ typedef enum rla2_dtype { RLA2_F32 = 0, RLA2_BF16 = 1 } rla2_dtype;
  *               input is packed: B must be 1 and L is the total token count T.
  *  dtype        element type of q, k, v, out (rla2_dtype).
  *  chunk        tokens per chunk of the chunked evaluation; must be 64.
- *  seg_chunks   chunks per sequential segment of the sweep, 0..32 (a tuning knob
+ *  seg_chunks   chunks per sequential segment of the sweep, 0..64 (a tuning knob
  *               that only changes fp32 summation order); 0 selects it
  *               automatically. Larger values return RLA2_ERR_BAD_VALUE.
  *  eps          denominator offset, RLA page §3 uses 1e-4. Finite, > 0.

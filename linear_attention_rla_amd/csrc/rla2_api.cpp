@@ -79,8 +79,10 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   const int rows = p->packed ? 1 : p->B;
   const long long L = p->L;
   // Segment length: the sweep kernels run one workgroup per (segment, head), so
-  // pick the longest segment that still gives ~1024 workgroups (fewer segments
-  // mean less fp32 state traffic through the inter-segment scan).
+  // pick the longest segment that still gives 512 workgroups, two per CU of the
+  // 256-CU part (fewer segments mean less fp32 state traffic through the
+  // inter-segment scan and fewer pipeline fills; measured on the long-context
+  // forward: 64-chunk segments 651 us, 32-chunk 693 us, 16-chunk 754 us).
   int seg = 0;
   if (d->seg_chunks > 0) {
     seg = d->seg_chunks * rla2::kChunk;
@@ -88,7 +90,7 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
     seg = rla2::kChunk;
     for (int cand = rla2::kMaxSegChunks * rla2::kChunk; cand >= rla2::kChunk; cand /= 2) {
       long long wg = (long long)rows * ((L + cand - 1) / cand) * (p->H > 0 ? p->H : 1);
-      if (wg >= 1024) { seg = cand; break; }
+      if (wg >= 512) { seg = cand; break; }
     }
   }
   p->seg_len = seg;

@@ -9,7 +9,7 @@
 namespace rla2 {
 
 constexpr int kChunk = 64;          // tokens per chunk (one MFMA-tiled block)
-constexpr int kMaxSegChunks = 32;   // chunks per segment at most (the output kernel keeps a
+constexpr int kMaxSegChunks = 64;   // chunks per segment at most (the state kernel keeps a
                                     // segment's RoPE rows in LDS)
 constexpr int kTabInts = 8;         // int32 fields per segment-table entry
 constexpr size_t kAlign = 256;

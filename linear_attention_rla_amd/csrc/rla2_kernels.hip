@@ -50,6 +50,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufFlags = 0x00020000;  // gfx9 buffer resource word 3 (32-bit raw data)
 // Cache policy of the streaming input loads and output stores (the slc bit: each byte is
 // touched once per kernel). Measured on the long-context forward: it keeps the segment
@@ -299,37 +300,47 @@ __device__ __forceinline__ float rms_inv(const Raw<BF, D>& r, int tok, float rms
     }
   }
   ss = sum8(ss);
-  return rsqrtf(ss * (1.0f / D) + rms_eps);
+  return rsqrtf(__builtin_fmaf(ss, 1.0f / D, rms_eps));
 }
 
+// The feature-map arithmetic below is written with explicit fused multiply-adds and no
+// implicit contraction, so every kernel that forms q' or k' rounds identically.
+//
 // (cos, sin) of A + B from (cos A, sin A) and (cos B, sin B).
 __device__ __forceinline__ float2 angle_sum(float2 a, float2 b) {
-  return make_float2(a.x * b.x - a.y * b.y, a.y * b.x + a.x * b.y);
+#pragma clang fp contract(off)
+  return make_float2(__builtin_fmaf(a.x, b.x, -(a.y * b.y)), __builtin_fmaf(a.y, b.x, a.x * b.y));
 }
 
-// One rotate-half pair (x1 = dim j, x2 = dim j + D/2): y = x * inv * gamma, rotate by the
-// angle with (cos, sin) = cs, then ReLU.
-__device__ __forceinline__ void rope_relu(float x1, float x2, float inv, float g1, float g2, float2 cs,
+// One rotate-half pair (x1 = dim j, x2 = dim j + D/2): y = x * inv * gamma, rotated by the
+// angle with (cos, sin) = cs. The ReLU follows in put_pairs.
+__device__ __forceinline__ void rope_pair(float x1, float x2, float inv, float g1, float g2, float2 cs,
                                           float& u1, float& u2) {
-  const float y1 = x1 * inv * g1;
-  const float y2 = x2 * inv * g2;
-  u1 = fmaxf(y1 * cs.x - y2 * cs.y, 0.f);
-  u2 = fmaxf(y2 * cs.x + y1 * cs.y, 0.f);
+#pragma clang fp contract(off)
+  const float y1 = (x1 * inv) * g1;
+  const float y2 = (x2 * inv) * g2;
+  u1 = __builtin_fmaf(y1, cs.x, -(y2 * cs.y));
+  u2 = __builtin_fmaf(y2, cs.x, y1 * cs.y);
 }
 
-// Elements e, e + 1 of both halves of token `tok` (u?[0] at e, u?[1] at e + 1), rounded to
-// the element type (round to nearest even, two values per conversion for bf16), into `o`.
+// ReLU of elements e, e + 1 of both halves of token `tok` (u?[0] at e, u?[1] at e + 1),
+// rounded to the element type, into `o`. bf16: two values per RNE conversion, then the ReLU
+// on the packed pair as a 16-bit signed max with 0 (a bf16 value is negative exactly when
+// its sign bit is set, and rounding never changes a sign, so this equals rounding max(u, 0)).
 template <bool BF, int D>
 __device__ __forceinline__ void put_pairs(Raw<BF, D>& o, int tok, int e, const float (&u1)[2],
                                           const float (&u2)[2]) {
   if constexpr (BF) {
-    o.w[tok][0][e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{u1[0], u1[1]}, bf16x2));
-    o.w[tok][1][e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{u2[0], u2[1]}, bf16x2));
+    const i16x2 zero = i16x2{0, 0};
+    o.w[tok][0][e >> 1] = __builtin_bit_cast(
+        uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2, __builtin_convertvector(float2v{u1[0], u1[1]}, bf16x2)), zero));
+    o.w[tok][1][e >> 1] = __builtin_bit_cast(
+        uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2, __builtin_convertvector(float2v{u2[0], u2[1]}, bf16x2)), zero));
   } else {
-    o.w[tok][0][e] = __float_as_uint(u1[0]);
-    o.w[tok][0][e + 1] = __float_as_uint(u1[1]);
-    o.w[tok][1][e] = __float_as_uint(u2[0]);
-    o.w[tok][1][e + 1] = __float_as_uint(u2[1]);
+    o.w[tok][0][e] = __float_as_uint(fmaxf(u1[0], 0.f));
+    o.w[tok][0][e + 1] = __float_as_uint(fmaxf(u1[1], 0.f));
+    o.w[tok][1][e] = __float_as_uint(fmaxf(u2[0], 0.f));
+    o.w[tok][1][e + 1] = __float_as_uint(fmaxf(u2[1], 0.f));
   }
 }
 
@@ -351,7 +362,7 @@ __device__ __forceinline__ void feature_map_pair(const Raw<BF, D>& r, Raw<BF, D>
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const int j = m * G::E + e + x;
-        rope_relu(r.get(tok, 0, e + x), r.get(tok, 1, e + x), inv, gamma[j], gamma[j + G::HALF],
+        rope_pair(r.get(tok, 0, e + x), r.get(tok, 1, e + x), inv, gamma[j], gamma[j + G::HALF],
                   angle_sum(rope_hi_row[j], lo[j]), u1[x], u2[x]);
       }
       put_pairs<BF, D>(o, tok, e, u1, u2);
@@ -416,7 +427,7 @@ __device__ __forceinline__ void feature_map_lane(const Raw<BF, D>& r, Raw<BF, D>
       float u1[2], u2[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x)
-        rope_relu(r.get(tok, 0, e + x), r.get(tok, 1, e + x), inv, g1[e + x], g2[e + x],
+        rope_pair(r.get(tok, 0, e + x), r.get(tok, 1, e + x), inv, g1[e + x], g2[e + x],
                   angle_sum(hi[e + x], lo[tok][e + x]), u1[x], u2[x]);
       put_pairs<BF, D>(o, tok, e, u1, u2);
     }
@@ -442,8 +453,8 @@ __device__ __forceinline__ void feature_map_qk(const Raw<BF, D>& rq, const Raw<B
       for (int x = 0; x < 2; ++x) {
         const int j = m * G::E + e + x;
         const float2 cs = angle_sum(rope_hi_row[j], lo[j]);
-        rope_relu(rq.get(tok, 0, e + x), rq.get(tok, 1, e + x), invq, gq[j], gq[j + G::HALF], cs, q1[x], q2[x]);
-        rope_relu(rk.get(tok, 0, e + x), rk.get(tok, 1, e + x), invk, gk[j], gk[j + G::HALF], cs, k1[x], k2[x]);
+        rope_pair(rq.get(tok, 0, e + x), rq.get(tok, 1, e + x), invq, gq[j], gq[j + G::HALF], cs, q1[x], q2[x]);
+        rope_pair(rk.get(tok, 0, e + x), rk.get(tok, 1, e + x), invk, gk[j], gk[j + G::HALF], cs, k1[x], k2[x]);
       }
       put_pairs<BF, D>(oq, tok, e, q1, q2);
       put_pairs<BF, D>(ok, tok, e, k1, k2);
@@ -974,23 +985,30 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
 // chunk_out for bf16, warp-specialised: 8 waves, one workgroup per CU.
 //
 // Waves 4..7 ("mappers") turn raw q, k, v into the chunk operands: the feature map of q
-// and k (VALU work) and the Q', K', V rows in LDS. They keep two chunks of raw input in
-// flight in registers. Waves 0..3 ("MMA waves") run the score and output phases on the
-// previous chunk from the other half of a double-buffered LDS. Each SIMD holds one wave of
-// each kind, so the mappers' VALU work overlaps the MMA waves' matrix and LDS work, and the
-// input loads overlap both.
+// and k (VALU work; both share the rotation angles) and the Q', K', V rows in LDS. They keep
+// two chunks of raw input in flight in registers. Waves 0..3 ("MMA waves") run the score and
+// output phases on the previous chunk from the other half of a double-buffered LDS and write
+// the outputs. Each SIMD holds one wave of each kind, so the mappers' VALU work overlaps the
+// MMA waves' matrix and LDS work, and the input loads overlap both.
 //
-// Step s (s = 0 .. nsteps-1): mappers map chunk s into buffer s % 2 and write chunk s - 2's
-// output rows (staged in LDS by the MMA waves) to memory; MMA waves process chunk s - 1 from
-// buffer (s - 1) % 2.
-// Two workgroup barriers per step, outside every role branch:
-//   X  after the mappers' q' and the MMA waves' score phase (score tiles and row
-//      reciprocals are complete before anyone forms outputs)
-//   Y  at the end of the step (buffer s % 2 and the staged output are complete; buffer
-//      (s - 1) % 2 is free again; the z update of chunk s - 1 is visible)
-// The MMA waves form q'.z from the Q' fragments they already hold, since z changes within
-// the step that maps the next chunk. Output tiles are staged in LDS and leave as whole
-// 256-byte rows (a 4-row, 1 KB run per store instruction) instead of 8-byte pieces.
+// Step s (s = 0 .. nsteps-1): mappers map chunk s into buffer s % 2; MMA waves process chunk
+// s - 1 from buffer (s - 1) % 2. One workgroup barrier per step (Y, at its end: buffer s % 2
+// is complete, buffer (s - 1) % 2 is free again, the z update of chunk s - 1 is visible).
+// Inside the step the MMA waves also meet among themselves (score tiles and row reciprocals
+// of every query tile are complete before anyone forms outputs) on an LDS arrival counter,
+// which the mappers never wait on.
+
+// Arrival counter of the four MMA waves: each wave adds 1 with release semantics (its LDS
+// writes land first), then polls with acquire semantics until all four have arrived for
+// this step. The count only grows, so step st waits for 4 (st + 1). The poll is bounded
+// (about 0.1 s) so that a wave can never spin forever.
+__device__ __forceinline__ void mma_wave_sync(unsigned* cnt, unsigned target, int lane) {
+  if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (int spin = 0; spin < (1 << 21); ++spin) {
+    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
@@ -1006,15 +1024,15 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   __shared__ __attribute__((aligned(16))) St sQ[2 * BUF];
   __shared__ __attribute__((aligned(16))) St sK[2 * BUF];
   __shared__ __attribute__((aligned(16))) St sV[2 * BUF];
-  __shared__ __attribute__((aligned(16))) St sO[BUF];  // output rows of one chunk
+  __shared__ __attribute__((aligned(16))) St sO[2 * BUF];  // output rows of chunk c in buffer c % 2
   __shared__ Frag<true> sA[4 * 2 * 64];  // [query tile][key block][lane]: B operands of V^T A^T
-  __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * G::HALF];  // RoPE rows of the chunks
   __shared__ __attribute__((aligned(16))) float sZ[D];
   __shared__ float sDz[D];  // column sums of the chunk's K', added to z after the score phase
   __shared__ float sInv[kChunk];
   // z as an MFMA A operand: row 0 = bf16(z), row 1 = bf16(z - bf16(z)), rows 2..15 = 0, so
   // Z Q'^T gives q'.z (to ~2^-17 relative) in rows 0 + 1 of each query column
   __shared__ Frag<true> sZf[G::KB * 64];
+  __shared__ unsigned sArrive;  // MMA-wave arrivals (mma_wave_sync)
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;  // the whole workgroup leaves together
@@ -1024,13 +1042,15 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   // per wave, so every wave executes exactly its own role's barriers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
-  // steps 0 .. nch + 1 do work (the last one writes the last chunk's output); rounded up to
-  // even for the mappers' two-step loop
+  // steps 0 .. nch do work (the last one forms the last chunk's output); rounded up to even
+  // for the mappers' two-step loop
   const int nsteps = (nch + 3) & ~1;
   const int c16 = lane & 15, g = lane >> 4;
   const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * 2;
   const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
   if (tid < D) sZ[tid] = rec[D * D + tid];
+  if (tid == 0) sArrive = 0u;
   // z operand fragments: slot (g, j) of fragment kb holds dim kb*32 + 4g + j (j < 4) or
   // kb*32 + 16 + 4g + j - 4; lane 16g holds bf16(z) there, lane 16g + 1 the residual, every
   // other lane zeros (written once). Wave 0 refreshes the two data lanes of each fragment:
@@ -1051,17 +1071,12 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   for (int i = tid; i < G::KB * 64; i += 512) sZf[i] = Frag<true>{};
   __syncthreads();
   if (wave == 0) put_zf(rec + D * D);
-  {
-    const float2* hi0 = rope_hi + (size_t)(si.pos0 / kChunk) * G::HALF;
-    for (int i = tid; i < min(nch, kMaxSegChunks) * G::HALF; i += 512) sHi[i] = hi0[i];
-  }
   __syncthreads();
 
   if (wave >= 4) {
-    // ======== mappers: nsteps steps, two barriers each
+    // ======== mappers: nsteps steps, one barrier each
     const int mt = tid & 255;  // two tokens per 8 lanes
     const int t0 = 2 * (mt >> 3), m = mt & 7;
-    const int seg_bytes = si.len * D * 2;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + tok0 * D), 0, seg_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + tok0 * D), 0, seg_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
@@ -1082,57 +1097,69 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     // Every step issues the same loads (chunks past the end read zeros from the buffer
     // range check), so the compiler's wait counts let chunk st + 1 stay in flight while
     // chunk st is mapped.
-    auto issue = [&](R (&r)[3], int c) {
+    const float2* hi0 = rope_hi + (size_t)(si.pos0 / kChunk) * G::HALF + m * G::E;
+    auto issue = [&](R (&r)[3], float2 (&hi)[G::E], int c) {
+      copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
       load_raw_buf<true, D>(r[0], rq, c * kChunk + t0, m);
       load_raw_buf<true, D>(r[1], rk, c * kChunk + t0, m);
       load_raw_buf<true, D>(r[2], rv, c * kChunk + t0, m);
     };
-    auto mstep = [&](int st, R (&r)[3]) {
+    auto mstep = [&](int st, R (&r)[3], float2 (&hi)[G::E]) {
       const int bm = (st & 1) * BUF;
-      float2 hi[G::E];
-      if (st < nch) {  // q', v
-        copy_bytes<G::E * 8>(hi, sHi + st * G::HALF + m * G::E);
-        R o;
-        feature_map_lane<true, D>(r[0], o, gq1, gq2, lo, hi, rms_eps);
-        store_rows<true, D>(sQ + bm, o, t0, m);
+      if (st < nch) {
+        R oq, ok;
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {
+          const float invq = rms_inv<true, D>(r[0], tok, rms_eps);
+          const float invk = rms_inv<true, D>(r[1], tok, rms_eps);
+#pragma unroll
+          for (int e = 0; e < G::E; e += 2) {
+            float q1[2], q2[2], k1[2], k2[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
+              rope_pair(r[0].get(tok, 0, e + x), r[0].get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs, q1[x], q2[x]);
+              rope_pair(r[1].get(tok, 0, e + x), r[1].get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs, k1[x], k2[x]);
+            }
+            put_pairs<true, D>(oq, tok, e, q1, q2);
+            put_pairs<true, D>(ok, tok, e, k1, k2);
+          }
+        }
+        store_rows<true, D>(sQ + bm, oq, t0, m);
         store_rows<true, D>(sV + bm, r[2], t0, m);
+        store_rows<true, D>(sK + bm, ok, t0, m);
       }
-      {  // chunk st - 2's output rows, staged by the MMA waves, leave as whole rows. The same
-         // stores are issued every step: rows past the segment (and every row when there is
-         // no such chunk) fall outside the buffer range and are dropped.
+      {  // chunk st - 2's output rows, staged by the MMA waves in sO[st % 2], leave as whole
+         // rows. The same stores are issued every step: rows past the segment (and every row
+         // when there is no such chunk) fall outside the buffer range and are dropped.
         constexpr int PPR = D / 8;     // 16-byte pieces per row
         constexpr int RPI = 64 / PPR;  // rows per wave instruction
         const int cw = st - 2;
         const bool any = cw >= 0 && cw < nch;
+        const St* so = sO + (st & 1) * BUF;
 #pragma unroll
         for (int i = 0; i < kChunk / (4 * RPI); ++i) {
           const int rr = (i * 4 + wave - 4) * RPI + lane / PPR, pc = lane % PPR;
           const int off = any ? ((cw * kChunk + rr) * D + pc * 8) * 2 : seg_bytes;
-          __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(sO + rr * G::ROWP + pc * 8), ro, off, 0,
+          __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(so + rr * G::ROWP + pc * 8), ro, off, 0,
                                                  kLoadStream);
         }
       }
-      __syncthreads();  // X
-      if (st < nch) {  // k'
-        R o;
-        feature_map_lane<true, D>(r[1], o, gk1, gk2, lo, hi, rms_eps);
-        store_rows<true, D>(sK + bm, o, t0, m);
-      }
-      issue(r, st + 2);  // into the registers just consumed
+      issue(r, hi, st + 2);  // into the registers just consumed
       __syncthreads();  // Y
     };
     R set0[3], set1[3];
-    issue(set0, 0);
-    issue(set1, 1);
+    float2 hi0r[G::E], hi1r[G::E];
+    issue(set0, hi0r, 0);
+    issue(set1, hi1r, 1);
     for (int st = 0; st < nsteps; st += 2) {
-      mstep(st, set0);
-      mstep(st + 1, set1);
+      mstep(st, set0, hi0r);
+      mstep(st + 1, set1, hi1r);
     }
     return;
   }
 
-  // ======== MMA waves: nsteps steps, two barriers each; step st processes chunk st - 1
-  St* ob = out + tok0 * D;
+  // ======== MMA waves: nsteps steps, one workgroup barrier each; step st processes chunk st - 1
   floatx4 S[G::RT][G::CT];  // running state, value columns of this wave
   {
     const int wv = wave < G::NW ? wave : 0;
@@ -1149,7 +1176,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const St* cK = sK + ((st + 1) & 1) * BUF;
     const St* cV = sV + ((st + 1) & 1) * BUF;
     const int c = st - 1;
-    const bool work = st >= 1 && st <= nch;
+    const bool work = st >= 1 && st <= nch;  // uniform over the MMA waves
     if (work) {  // ---- score: wave w owns query tile w
       const int tt = wave;
       Frag<true> Qf[G::KB];
@@ -1189,7 +1216,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       sA[(tt * 2) * 64 + lane] = acc_frag<true>(At[0], At[1]);
       if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<true>(At[2], At[3]);
       if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + eps);
-      if (wave == 0) {  // column sums of K' (the least loaded score wave); applied after X
+      if (wave == 0) {  // column sums of K' (the least loaded score wave); applied after the sync
         const Frag<true> ones = ones_frag<true>();
         floatx4 zc[G::RT];
 #pragma unroll
@@ -1203,8 +1230,8 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
           if (c16 < 4) sDz[rt * 16 + 4 * g + c16] = zc[rt][c16];
       }
     }
-    __syncthreads();  // X
-    if (work && wave < G::NW) {  // ---- output (staged), then the state update
+    mma_wave_sync(&sArrive, 4u * (unsigned)(st + 1), lane);
+    if (work && wave < G::NW) {  // ---- output, then the state update
       if (wave == 0) {  // every q'.z of this chunk is done: advance z and its operand
         for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1249,6 +1276,8 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(Vf[ct][1], a1, o[ct][tt]);
       }
+      // each lane holds 4 consecutive columns of one row: 8-byte range-checked stores (rows
+      // past the segment fall outside the buffer range and are dropped)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int t = tt * 16 + c16;  // this lane's query row
@@ -1258,7 +1287,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
           const int col = wave * G::DVW + ct * 16 + 4 * g;
           const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[ct][tt][0] * rr, o[ct][tt][1] * rr}, bf16x2));
           const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[ct][tt][2] * rr, o[ct][tt][3] * rr}, bf16x2));
-          *reinterpret_cast<uint2*>(sO + t * G::ROWP + col) = make_uint2(w0, w1);
+          *reinterpret_cast<uint2*>(sO + (c & 1) * BUF + t * G::ROWP + col) = make_uint2(w0, w1);
         }
       }
       // S += K'^T V

@@ -67,7 +67,7 @@ def ws_size(d):
     (dict(d=48), UNSUP), (dict(d=256), UNSUP), (dict(dtype=2), UNSUP), (dict(chunk=32), UNSUP),
     (dict(B=-1), SHAPE), (dict(L=-5), SHAPE), (dict(H=-1), SHAPE),
     (dict(eps=0.0), VALUE), (dict(eps=float("nan")), VALUE), (dict(rms_eps=-1.0), VALUE),
-    (dict(rope_base=float("inf")), VALUE), (dict(seg_chunks=-1), VALUE), (dict(seg_chunks=33), VALUE),
+    (dict(rope_base=float("inf")), VALUE), (dict(seg_chunks=-1), VALUE), (dict(seg_chunks=65), VALUE),
     (dict(B=2, cu_seqlens=A, n_docs=3), SHAPE), (dict(B=1, cu_seqlens=A, n_docs=-1), SHAPE),
     (dict(B=1 << 16, L=1 << 16), SHAPE),
 ])
