@@ -22,7 +22,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, 2.5 PFLOP/s
-KERNELS = ["seg_map", "rope_table", "chunk_state", "state_scan", "chunk_out"]
+KERNELS = ["prep", "chunk_state", "state_scan", "chunk_out"]
 
 
 def log(*a):

@@ -123,13 +123,13 @@ rla2_status rla2_fwd_chunked(const rla2_fwd_desc* desc, const void* q, const voi
                              size_t workspace_bytes, hipStream_t stream);
 
 /* Number of kernels one forward launches (see rla2_fwd_chunked_profiled). */
-#define RLA2_FWD_KERNELS 5
+#define RLA2_FWD_KERNELS 4
 
 /*
  * rla2_fwd_chunked for measurement tools. `events` holds RLA2_FWD_KERNELS + 1
  * events created by the caller (hipEventCreate). events[i] is recorded on
- * `stream` right before kernel i of the forward -- 0 segment map, 1 RoPE table,
- * 2 chunk state, 3 state scan, 4 chunk output -- and events[RLA2_FWD_KERNELS]
+ * `stream` right before kernel i of the forward -- 0 set-up (segment map and
+ * RoPE tables), 1 chunk state, 2 state scan, 3 chunk output -- and events[RLA2_FWD_KERNELS]
  * after the last, so hipEventElapsedTime(events[i], events[i + 1]) is kernel i's
  * duration (0 when the kernel is not needed). NULL `events` behaves exactly like
  * rla2_fwd_chunked. Same arguments, ownership and errors otherwise.

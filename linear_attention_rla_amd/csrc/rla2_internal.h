@@ -41,7 +41,7 @@ struct FwdArgs {
 
 // Launch the whole chunked forward (out != null) or the state build (out == null).
 // `ev` (optional) gets kNumFwdKernels + 1 events recorded around the kernels.
-constexpr int kNumFwdKernels = 5;
+constexpr int kNumFwdKernels = 4;
 hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
 
 hipError_t launch_decode(int N, int H, int d, int dtype, const void* q, const void* k,

@@ -8,8 +8,8 @@
 //
 // Chunked evaluation used here (C = 64 tokens per chunk, documents split into segments of
 // whole chunks):
-//   seg_map      cu_seqlens -> table of (row, first token, length, first position) segments
-//   rope_table   cos/sin of p*theta_j for p < 64 and for p = 64*a (angle addition rebuilds
+//   prep         cu_seqlens -> table of (row, first token, length, first position) segments,
+//                and cos/sin of p*theta_j for p < 64 and for p = 64*a (angle addition rebuilds
 //                any position from the two, so no per-token transcendental is needed)
 //   chunk_state  per (segment, head): Sum over the segment of K'^T V and of K' (MFMA)
 //   state_scan   per (document, head): exclusive prefix of segment totals in fp32;
@@ -503,9 +503,9 @@ __device__ __forceinline__ SegInfo read_seg(const int32_t* tab, int seg) {
 // ----------------------------------------------------------------------------------------
 // seg_map: documents -> segments of at most seg_len tokens (whole chunks), one workgroup.
 
-__global__ __launch_bounds__(1024) void seg_map_kernel(const int32_t* __restrict__ cu, int n_docs, int L,
-                                                       int seg_len, int n_seg_max, int32_t* __restrict__ tab,
-                                                       int32_t* __restrict__ docoff, int32_t* __restrict__ nseg) {
+__device__ __forceinline__ void seg_map_block(const int32_t* __restrict__ cu, int n_docs, int L, int seg_len,
+                                              int n_seg_max, int32_t* __restrict__ tab, int32_t* __restrict__ docoff,
+                                              int32_t* __restrict__ nseg) {
   __shared__ int scan[1024];
   __shared__ int carry_s;
   const int tid = threadIdx.x;
@@ -563,9 +563,8 @@ __global__ __launch_bounds__(1024) void seg_map_kernel(const int32_t* __restrict
 // rope_table: (cos, sin) of p * theta_j, theta_j = base^(-2j/D), in fp64, rounded to fp32.
 // Rows 0..63 hold p = row; rows 64.. hold p = 64 * (row - 64).
 
-__global__ void rope_table_kernel(float2* __restrict__ lo, float2* __restrict__ hi, int half, int D,
-                                  int n_hi, float base) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void rope_entry(int idx, float2* __restrict__ lo, float2* __restrict__ hi, int half, int D,
+                                           int n_hi, float base) {
   const int rows = kChunk + n_hi;
   if (idx >= rows * half) return;
   const int row = idx / half, j = idx % half;
@@ -576,6 +575,16 @@ __global__ void rope_table_kernel(float2* __restrict__ lo, float2* __restrict__ 
   const float2 v = make_float2((float)c, (float)s);
   if (row < kChunk) lo[row * half + j] = v;
   else hi[(row - kChunk) * half + j] = v;
+}
+
+// prep: block 0 builds the segment table, blocks 1.. the RoPE tables (one launch for both).
+__global__ __launch_bounds__(1024) void prep_kernel(const int32_t* __restrict__ cu, int n_docs, int L, int seg_len,
+                                                    int n_seg_max, int32_t* __restrict__ tab,
+                                                    int32_t* __restrict__ docoff, int32_t* __restrict__ nseg,
+                                                    float2* __restrict__ lo, float2* __restrict__ hi, int half, int D,
+                                                    int n_hi, float base) {
+  if (blockIdx.x == 0) seg_map_block(cu, n_docs, L, seg_len, n_seg_max, tab, docoff, nseg);
+  else rope_entry((blockIdx.x - 1) * 1024 + threadIdx.x, lo, hi, half, D, n_hi, base);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1010,6 +1019,79 @@ __device__ __forceinline__ void mma_wave_sync(unsigned* cnt, unsigned target, in
   }
 }
 
+// Score phase of MMA wave TT (query tile TT of the chunk): the causal tiles K'_kt Q'_TT^T
+// (kt <= TT) and Z Q'_TT^T, the diagonal tile masked, every weight rounded to bf16 once
+// (pairs of tiles packed as the B operands of V^T A^T); the row sums are taken from the
+// packed weights with a bf16 dot against ones, so numerator and denominator use the same
+// weights. The wave also forms the column sums of K' for row tiles [Z0, Z1). Every LDS
+// operand is requested before the first MFMA.
+template <int D, int TT, int Z0, int Z1>
+__device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK, const Frag<true>* sZf,
+                                         Frag<true>* sA, float* sInv, float* sDz, float eps, int lane) {
+  using G = Geo<true, D>;
+  constexpr int KB = G::KB, NZ = Z1 - Z0, NP = TT / 2 + 1;
+  const int c16 = lane & 15, g = lane >> 4;
+  Frag<true> Qf[KB], Kf[TT + 1][KB], Zf[KB], Ct[NZ > 0 ? NZ : 1][2];
+#pragma unroll
+  for (int kb2 = 0; kb2 < KB; ++kb2) Qf[kb2] = lds_frag<true>(cQ, G::ROWP, TT * 16 + c16, kb2, g);
+#pragma unroll
+  for (int kt = 0; kt <= TT; ++kt)
+#pragma unroll
+    for (int kb2 = 0; kb2 < KB; ++kb2) Kf[kt][kb2] = lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb2, g);
+#pragma unroll
+  for (int kb2 = 0; kb2 < KB; ++kb2) Zf[kb2] = sZf[kb2 * 64 + lane];
+#pragma unroll
+  for (int z = 0; z < NZ; ++z) {
+    Ct[z][0] = lds_frag_tr(cK, G::ROWP, 0, 16 * (Z0 + z), lane);
+    Ct[z][1] = lds_frag_tr(cK, G::ROWP, 32, 16 * (Z0 + z), lane);
+  }
+  floatx4 At[TT + 1];
+#pragma unroll
+  for (int kt = 0; kt <= TT; ++kt) At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 zq = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb2 = 0; kb2 < KB; ++kb2) {
+#pragma unroll
+    for (int kt = 0; kt <= TT; ++kt) At[kt] = mma(Kf[kt][kb2], Qf[kb2], At[kt]);
+    zq = mma(Zf[kb2], Qf[kb2], zq);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (4 * g + i > c16) At[TT][i] = 0.f;  // key after the query token
+  // packed bf16 weights, word i of pair b: rows 2i, 2i + 1 of tile 2b (i < 2) or of tile
+  // 2b + 1 (i >= 2), the slot order of acc_frag
+  uint32_t pw[NP][4];
+#pragma unroll
+  for (int b = 0; b < NP; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int kt = 2 * b + (i >> 1), r = 2 * (i & 1);
+      pw[b][i] = kt <= TT ? __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{At[kt % (TT + 1)][r], At[kt % (TT + 1)][r + 1]}, bf16x2))
+                          : 0u;
+    }
+  float rs = 0.f;
+  const bf16x2 ones2 = bf16x2{static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+#pragma unroll
+  for (int b = 0; b < NP; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[b][i]), ones2, rs, false);
+  if (g == 0) rs += zq[0] + zq[1];  // q'.z of query 16 TT + c16 (rows 0, 1 of Z Q'^T)
+  rs = sum_rows4(rs);  // lanes with c16 == t: row sum + q'.z of query 16 TT + t
+#pragma unroll
+  for (int b = 0; b < NP; ++b)
+    *reinterpret_cast<u32x4*>(&sA[(TT * 2 + b) * 64 + lane]) = u32x4{pw[b][0], pw[b][1], pw[b][2], pw[b][3]};
+  if (g == 0) sInv[TT * 16 + c16] = 1.0f / (rs + eps);
+  if constexpr (NZ > 0) {
+    const Frag<true> ones = ones_frag<true>();
+#pragma unroll
+    for (int z = 0; z < NZ; ++z) {
+      floatx4 zc = mma(Ct[z][0], ones, floatx4{0.f, 0.f, 0.f, 0.f});
+      zc = mma(Ct[z][1], ones, zc);  // every column holds the sums of rows 16 (Z0 + z) + 4g + i
+      if (c16 < 4) sDz[(Z0 + z) * 16 + 4 * g + c16] = zc[c16];
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -1171,6 +1253,8 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   }
   // Accumulation order everywhere below: the contraction block is the outer loop and the
   // independent accumulators the inner one, so consecutive MFMAs never wait on each other.
+  // column sums of K': row tiles [0, ZS) on wave 0, [ZS, RT) on wave 1 (the lighter score waves)
+  constexpr int ZS = G::RT - (3 * G::RT) / 8;
   for (int st = 0; st < nsteps; ++st) {
     const St* cQ = sQ + ((st + 1) & 1) * BUF;  // buffers holding chunk st - 1
     const St* cK = sK + ((st + 1) & 1) * BUF;
@@ -1178,56 +1262,11 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const int c = st - 1;
     const bool work = st >= 1 && st <= nch;  // uniform over the MMA waves
     if (work) {  // ---- score: wave w owns query tile w
-      const int tt = wave;
-      Frag<true> Qf[G::KB];
-#pragma unroll
-      for (int kb2 = 0; kb2 < G::KB; ++kb2) Qf[kb2] = lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb2, g);
-      // A^T tiles (rows = keys of tile kt, cols = queries of tile tt), causal: kt <= tt; and
-      // Z Q'^T for q'.z
-      floatx4 At[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      floatx4 zq = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb2 = 0; kb2 < G::KB; ++kb2) {
-        Frag<true> kf[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          if (kt <= tt) kf[kt] = lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb2, g);
-        const Frag<true> zf = sZf[kb2 * 64 + lane];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          if (kt <= tt) At[kt] = mma(kf[kt], Qf[kb2], At[kt]);
-        zq = mma(zf, Qf[kb2], zq);
-      }
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float a = At[kt][i];
-          if (kt > tt || (kt == tt && 4 * g + i > c16)) a = 0.f;  // key after the query token
-          a = EL::to_f(EL::from_f(a));                             // the weight the MFMA will use
-          At[kt][i] = a;
-          rs += a;
-        }
-      if (g == 0) rs += zq[0] + zq[1];  // q'.z of query 16 tt + c16 (rows 0, 1 of Z Q'^T)
-      rs = sum_rows4(rs);  // lanes with c16 == t: row sum + q'.z of query 16 tt + t
-      sA[(tt * 2) * 64 + lane] = acc_frag<true>(At[0], At[1]);
-      if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<true>(At[2], At[3]);
-      if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + eps);
-      if (wave == 0) {  // column sums of K' (the least loaded score wave); applied after the sync
-        const Frag<true> ones = ones_frag<true>();
-        floatx4 zc[G::RT];
-#pragma unroll
-        for (int rt = 0; rt < G::RT; ++rt) zc[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int rt = 0; rt < G::RT; ++rt) zc[rt] = mma(lds_frag_tr(cK, G::ROWP, 32 * kb2, 16 * rt, lane), ones, zc[rt]);
-#pragma unroll
-        for (int rt = 0; rt < G::RT; ++rt)
-          if (c16 < 4) sDz[rt * 16 + 4 * g + c16] = zc[rt][c16];
+      switch (wave) {
+        case 0: ws_score<D, 0, 0, ZS>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+        case 1: ws_score<D, 1, ZS, G::RT>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+        case 2: ws_score<D, 2, 0, 0>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+        default: ws_score<D, 3, 0, 0>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
       }
     }
     mma_wave_sync(&sArrive, 4u * (unsigned)(st + 1), lane);
@@ -1440,19 +1479,16 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   };
 
   mark(0);
-  hipLaunchKernelGGL(seg_map_kernel, dim3(1), dim3(1024), 0, s, a.cu, p.n_docs, p.L, p.seg_len, p.n_seg_max,
-                     tab, docoff, nseg);
-  mark(1);
   const int rope_entries = (kChunk + p.n_hi) * half;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((rope_entries + 255) / 256), dim3(256), 0, s, rlo, rhi, half, D,
-                     p.n_hi, a.rope_base);
-  mark(2);
+  hipLaunchKernelGGL(prep_kernel, dim3(1 + (rope_entries + 1023) / 1024), dim3(1024), 0, s, a.cu, p.n_docs, p.L,
+                     p.seg_len, p.n_seg_max, tab, docoff, nseg, rlo, rhi, half, D, p.n_hi, a.rope_base);
+  mark(1);
   if (p.n_seg_max > 0) {
     hipLaunchKernelGGL((chunk_state_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                        static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
                        states, p.H, p.L, a.rms_eps);
   }
-  mark(3);
+  mark(2);
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
   const bool want_final = a.final_S != nullptr || a.final_z != nullptr;
   const bool fwd = a.out != nullptr;
@@ -1460,7 +1496,7 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
                        n_tiles, fwd ? 1 : 0, a.final_S, a.final_z);
   }
-  mark(4);
+  mark(3);
   if (fwd && p.n_seg_max > 0) {
     if constexpr (BF) {
       hipLaunchKernelGGL((chunk_out_ws_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
@@ -1472,7 +1508,7 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
                          a.gk, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
     }
   }
-  mark(5);
+  mark(4);
   return hipGetLastError();
 }
 
