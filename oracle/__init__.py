@@ -5,6 +5,6 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 """
 from .rla2_oracle import (  # noqa: F401
     DEFAULT_EPS, DEFAULT_RMS_EPS, DEFAULT_ROPE_BASE,
-    rms_norm, rope_frequencies, rope_rotate_half, feature_map, documents,
+    rms_norm, rope_frequencies, rope_rotate_half, feature_map, documents, first_documents,
     fwd, fwd_rows, fwd_recurrent, state_from_prefix, decode_step, decode_direct,
 )

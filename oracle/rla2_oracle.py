@@ -25,13 +25,23 @@ page "线性注意力家族：RLA / RAPT / RLA-2 与 GPU 落地", called *RLA pa
   (closed form of the original RLA) with the Sum denominator that RLA-2
   substitutes for the L2 one (§2.3 table, §3 table);
 * the single-token decode step: update the state first, then read it --
-  RLA page §4.2 (``forward_step``).
+  RLA page §4.2 (``forward_step``);
+* an initial state ``(S_0, z_0)`` per head that starts the first document of
+  each row -- RLA page §4.1 (the prefix scan's ``A0/B0`` inputs, shape
+  ``(H*dk, dk)`` shared by the batch rows, take effect for the first document
+  only);
+* the bidirectional mode, where every token reads its whole document's state --
+  RLA page §4.1 (``causal=false``: the scan output is one constant for the
+  whole set) and §4.2 (the layer's bidirectional branch).
 
 Readings where the pages leave a step open (each is listed in the design doc):
 the RMSNorm epsilon sits inside the square root; RoPE frequencies are
 ``theta_j = base^(-2j/d)`` with the standard rotate-half sign convention;
 positions restart at 0 at every document start; the causal sum includes the
-query's own token; eps is added to the denominator (not a clamp).
+query's own token; eps is added to the denominator (not a clamp); an initial
+state continues an earlier context, so the first document of each row may
+start at a position offset ``initial_pos``; in the bidirectional mode the
+document boundaries still isolate documents.
 
 Every function below is pinned by ``tests/test_oracle_pins.py`` against
 closed forms, invariants and an independent formulation (the recurrence).
@@ -119,104 +129,141 @@ def documents(B: int, L: int, cu_seqlens=None):
     return [(0, cu[j], cu[j + 1]) for j in range(len(cu) - 1)]
 
 
-def _doc_attention_rows(qp, kp, v, rows, eps):
-    """Direct causal sum for query rows ``rows`` of one document (fp64).
+def first_documents(B: int, L: int, cu_seqlens=None):
+    """Indices (into ``documents()``) of the documents an initial state starts:
+    the first document of each row. Without ``cu_seqlens`` every row is one
+    document, so all of them; packed input has one row, so document 0 only
+    (RLA page §4.1: ``A0/B0`` take effect for the first document only)."""
+    n = len(documents(B, L, cu_seqlens))
+    return set(range(n)) if cu_seqlens is None else ({0} if n else set())
 
-    ``out_t = sum_{i<=t} s_ti v_i / (sum_{i<=t} s_ti + eps)``,
-    ``s_ti = q'_t . k'_i``. ``qp`` holds the feature-mapped queries of
-    ``rows`` only; ``kp, v`` hold the document's keys/values from its start.
+
+def _initial(initial_S, initial_z, H, d):
+    """The per-head initial state ``(S_0 [H, d, d], z_0 [H, d])`` in fp64 (zeros if absent).
+    ``S_0[a, c]`` pairs key dimension a with value dimension c, like the state."""
+    S0 = np.zeros((H, d, d)) if initial_S is None else _f64(initial_S).reshape(H, d, d)
+    z0 = np.zeros((H, d)) if initial_z is None else _f64(initial_z).reshape(H, d)
+    return S0, z0
+
+
+def _doc_rows_general(qp, kp, v, rows, eps, S0, z0, causal):
+    """Direct sum for query rows ``rows`` of one document with an initial state
+    and either key range (fp64):
+
+    ``out_t = (q'_t S_0 + sum_{i in K(t)} s_ti v_i) / (q'_t . z_0 + sum_{i in K(t)} s_ti + eps)``,
+    ``K(t) = {i <= t}`` (causal) or every token of the document (bidirectional).
     """
     rows = np.asarray(rows)
-    n_keys = int(rows.max()) + 1
-    s = qp @ kp[:n_keys].T                                   # [r, n_keys], all >= 0
-    s = np.where(np.arange(n_keys)[None, :] <= rows[:, None], s, 0.0)
-    num = s @ v[:n_keys]
-    den = s.sum(axis=1) + eps
+    n_keys = int(rows.max()) + 1 if causal else kp.shape[0]
+    s = qp @ kp[:n_keys].T
+    if causal:
+        s = np.where(np.arange(n_keys)[None, :] <= rows[:, None], s, 0.0)
+    num = s @ v[:n_keys] + qp @ S0
+    den = s.sum(axis=1) + qp @ z0 + eps
     return num / den[:, None]
 
 
 def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps: float = DEFAULT_EPS,
         rms_eps: float = DEFAULT_RMS_EPS, rope_base: float = DEFAULT_ROPE_BASE,
-        row_block: int = 512) -> np.ndarray:
-    """Closed-form RLA-2 causal forward over ``[B, H, L, d]`` (fp64 output).
+        row_block: int = 512, initial_S=None, initial_z=None, initial_pos: int = 0,
+        causal: bool = True) -> np.ndarray:
+    """Closed-form RLA-2 forward over ``[B, H, L, d]`` (fp64 output).
 
-    Positions restart at 0 at each document start. Query rows are processed
-    in blocks of ``row_block`` only to bound memory; every row is still the
-    direct sum over its own causal, same-document key range.
+    Positions restart at 0 at each document start; the first document of each
+    row starts at ``initial_pos`` instead and from the state ``(initial_S,
+    initial_z)`` (``[H, d, d]``, ``[H, d]``; absent = zero). ``causal=False``
+    is the bidirectional mode: each row reads its whole document. Query rows
+    are processed in blocks of ``row_block`` only to bound memory; every row is
+    still the direct sum over its own same-document key range.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, L, d = q.shape
+    S0, z0 = _initial(initial_S, initial_z, H, d)
+    first = first_documents(B, L, cu_seqlens)
     out = np.zeros((B, H, L, d), dtype=np.float64)
-    for (b, s0, s1) in documents(B, L, cu_seqlens):
+    for j, (b, s0, s1) in enumerate(documents(B, L, cu_seqlens)):
         n = s1 - s0
         if n <= 0:
             continue
-        pos = np.arange(n)
+        start = initial_pos if j in first else 0
+        pos = start + np.arange(n)
         for h in range(H):
             qp = feature_map(q[b, h, s0:s1], gamma_q[h], pos, rms_eps, rope_base)
             kp = feature_map(k[b, h, s0:s1], gamma_k[h], pos, rms_eps, rope_base)
             vv = v[b, h, s0:s1]
+            Sh, zh = (S0[h], z0[h]) if j in first else (np.zeros((d, d)), np.zeros(d))
             for r0 in range(0, n, row_block):
                 rows = np.arange(r0, min(n, r0 + row_block))
-                out[b, h, s0 + rows] = _doc_attention_rows(qp[rows], kp, vv, rows, eps)
+                out[b, h, s0 + rows] = _doc_rows_general(qp[rows], kp, vv, rows, eps, Sh, zh, causal)
     return out
 
 
 def fwd_rows(q, k, v, gamma_q, gamma_k, b: int, h: int, rows, cu_seqlens=None,
              eps: float = DEFAULT_EPS, rms_eps: float = DEFAULT_RMS_EPS,
-             rope_base: float = DEFAULT_ROPE_BASE, row_block: int = 256) -> np.ndarray:
+             rope_base: float = DEFAULT_ROPE_BASE, row_block: int = 256, initial_S=None,
+             initial_z=None, initial_pos: int = 0, causal: bool = True) -> np.ndarray:
     """Closed form for selected token rows of one (row b, head h).
 
     ``rows`` are token indices within row b (packed: within the T tokens).
     Used for sampled parity at sizes where the full O(L^2 d) sum is too slow.
     Inputs may be torch CPU tensors or numpy arrays of any float dtype; only
-    the slices needed are upcast.
+    the slices needed are upcast. Initial state, position offset and
+    ``causal`` as in ``fwd``.
     """
-    B = q.shape[0]
-    L = q.shape[2]
+    B, H, L, d = q.shape
     rows = np.sort(np.asarray(rows, dtype=np.int64))
-    out = np.zeros((len(rows), q.shape[3]), dtype=np.float64)
+    out = np.zeros((len(rows), d), dtype=np.float64)
     docs = documents(B, L, cu_seqlens)
-    for (bb, s0, s1) in docs:
+    first = first_documents(B, L, cu_seqlens)
+    S0, z0 = _initial(initial_S, initial_z, H, d)
+    for j, (bb, s0, s1) in enumerate(docs):
         if bb != b or s1 <= s0:
             continue
         sel = np.nonzero((rows >= s0) & (rows < s1))[0]
         if sel.size == 0:
             continue
+        start = initial_pos if j in first else 0
+        Sh, zh = (S0[h], z0[h]) if j in first else (np.zeros((d, d)), np.zeros(d))
         local = rows[sel] - s0
-        n_keys = int(local.max()) + 1
+        n_keys = int(local.max()) + 1 if causal else s1 - s0
         kk = _f64(k[b, h, s0:s0 + n_keys])
         vv = _f64(v[b, h, s0:s0 + n_keys])
-        kp = feature_map(kk, _f64(gamma_k)[h], np.arange(n_keys), rms_eps, rope_base)
+        kp = feature_map(kk, _f64(gamma_k)[h], start + np.arange(n_keys), rms_eps, rope_base)
         qq = _f64(q[b, h, s0:s1])[local]
-        qp = feature_map(qq, _f64(gamma_q)[h], local, rms_eps, rope_base)
+        qp = feature_map(qq, _f64(gamma_q)[h], start + local, rms_eps, rope_base)
         for r0 in range(0, len(local), row_block):
             blk = slice(r0, r0 + row_block)
-            out[sel[blk]] = _doc_attention_rows(qp[blk], kp, vv, local[blk], eps)
+            out[sel[blk]] = _doc_rows_general(qp[blk], kp, vv, local[blk], eps, Sh, zh, causal)
     return out
 
 
 def fwd_recurrent(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps: float = DEFAULT_EPS,
-                  rms_eps: float = DEFAULT_RMS_EPS, rope_base: float = DEFAULT_ROPE_BASE):
+                  rms_eps: float = DEFAULT_RMS_EPS, rope_base: float = DEFAULT_ROPE_BASE,
+                  initial_S=None, initial_z=None, initial_pos: int = 0):
     """The RLA page's recurrence taken literally (tiny inputs only).
 
     RLA page §3: ``S_t = S_{t-1} + k'_t (x) v_t`` (d x d), ``z_t = z_{t-1} +
     k'_t``, ``out_t = q'_t S_t / (q'_t . z_t + eps)``; §2.2/§4.1: S and z
-    are cleared at each document start. Returns ``(out, final_S, final_z)``
-    with the final states per document ``[n_docs, H, d, d]``, ``[n_docs, H, d]``.
+    are cleared at each document start, except that the first document of
+    each row starts from ``(initial_S, initial_z)`` at position ``initial_pos``
+    (§4.1, ``A0/B0``). Returns ``(out, final_S, final_z)`` with the final
+    states per document ``[n_docs, H, d, d]``, ``[n_docs, H, d]``.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, L, d = q.shape
     docs = documents(B, L, cu_seqlens)
+    first = first_documents(B, L, cu_seqlens)
+    S0, z0 = _initial(initial_S, initial_z, H, d)
     out = np.zeros((B, H, L, d))
     fS = np.zeros((len(docs), H, d, d))
     fz = np.zeros((len(docs), H, d))
     for j, (b, s0, s1) in enumerate(docs):
+        start = initial_pos if j in first else 0
         for h in range(H):
-            S = np.zeros((d, d))
-            z = np.zeros(d)
+            S = S0[h].copy() if j in first else np.zeros((d, d))
+            z = z0[h].copy() if j in first else np.zeros(d)
             for t in range(s0, s1):
-                p = np.array([t - s0])
+                p = np.array([start + t - s0])
                 qp = feature_map(q[b, h, t:t + 1], gamma_q[h], p, rms_eps, rope_base)[0]
                 kp = feature_map(k[b, h, t:t + 1], gamma_k[h], p, rms_eps, rope_base)[0]
                 for a in range(d):              # outer product k' (x) v, one row at a time
@@ -232,27 +279,35 @@ def fwd_recurrent(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps: float = DEFAU
 
 
 def state_from_prefix(k, v, gamma_k, cu_seqlens=None, rms_eps: float = DEFAULT_RMS_EPS,
-                      rope_base: float = DEFAULT_ROPE_BASE):
+                      rope_base: float = DEFAULT_ROPE_BASE, initial_S=None, initial_z=None,
+                      initial_pos: int = 0):
     """Per-document state after its last token: ``S = sum_i k'_i (x) v_i``,
     ``z = sum_i k'_i`` (RLA page §3 state definition; §1 associativity: the
     state is the sum of key/value outer products). Matrix form ``K'^T V``.
+    The first document of each row adds the initial state and starts at
+    position ``initial_pos`` (as in ``fwd``).
 
     ``k, v``: ``[B, H, L, d]``; returns ``S [n_docs, H, d, d]``, ``z [n_docs, H, d]``.
     """
     k, v = _f64(k), _f64(v)
     B, H, L, d = k.shape
     docs = documents(B, L, cu_seqlens)
+    first = first_documents(B, L, cu_seqlens)
+    S0, z0 = _initial(initial_S, initial_z, H, d)
     S = np.zeros((len(docs), H, d, d))
     z = np.zeros((len(docs), H, d))
     for j, (b, s0, s1) in enumerate(docs):
+        if j in first:
+            S[j] = S0
+            z[j] = z0
         n = s1 - s0
         if n <= 0:
             continue
-        pos = np.arange(n)
+        pos = (initial_pos if j in first else 0) + np.arange(n)
         for h in range(H):
             kp = feature_map(k[b, h, s0:s1], gamma_k[h], pos, rms_eps, rope_base)
-            S[j, h] = kp.T @ v[b, h, s0:s1]
-            z[j, h] = kp.sum(axis=0)
+            S[j, h] += kp.T @ v[b, h, s0:s1]
+            z[j, h] += kp.sum(axis=0)
     return S, z
 
 

@@ -289,3 +289,82 @@ def test_workload_generators_are_seeded_and_shaped():
     assert abs(qf[..., m].mean().item() + 1.0) < 0.1
     dec = workloads.decode_inputs(4, 2, 16, 50, seed=5)
     assert int(dec.cu_prefix[-1]) == dec.prefix_k.shape[2] == int(dec.prefix_lengths.sum())
+
+
+# --- initial state and the bidirectional mode (RLA page §4.1, §4.2) -----------
+
+def test_initial_state_continues_the_sequence():
+    # RLA page §4.1: the prefix scan starts the first document from A0/B0. A state
+    # built from a prefix P, with positions continuing at len(P), must reproduce the
+    # plain forward over P ++ X on the rows of X (one shared per-head state, so both
+    # rows carry the same prefix). Catches the initial term dropped from the
+    # numerator or the denominator, and positions restarting at 0.
+    r = np.random.default_rng(41)
+    B, H, d, p, n = 2, 2, 8, 7, 9
+    P = [r.normal(size=(1, H, p, d)).repeat(B, axis=0) for _ in range(3)]
+    X = [r.normal(size=(B, H, n, d)) for _ in range(3)]
+    gq, gk = r.uniform(0.5, 1.5, size=(H, d)), r.uniform(0.5, 1.5, size=(H, d))
+    full = oracle.fwd(*(np.concatenate([a, b], axis=2) for a, b in zip(P, X)), gq, gk)
+    S0, z0 = oracle.state_from_prefix(P[1][:1], P[2][:1], gk)
+    cont = oracle.fwd(*X, gq, gk, initial_S=S0[0], initial_z=z0[0], initial_pos=p)
+    np.testing.assert_allclose(cont, full[:, :, p:], rtol=1e-12, atol=1e-14)
+    # the literal recurrence from the same initial state agrees, and its final state
+    # is the state of the whole sequence
+    rec, fS, fz = oracle.fwd_recurrent(*X, gq, gk, initial_S=S0[0], initial_z=z0[0], initial_pos=p)
+    np.testing.assert_allclose(rec, cont, rtol=1e-12, atol=1e-14)
+    Sall, zall = oracle.state_from_prefix(np.concatenate([P[1], X[1]], axis=2),
+                                          np.concatenate([P[2], X[2]], axis=2), gk)
+    np.testing.assert_allclose(fS, Sall, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(fz, zall, rtol=1e-12, atol=1e-13)
+    s2, z2 = oracle.state_from_prefix(X[1], X[2], gk, initial_S=S0[0], initial_z=z0[0], initial_pos=p)
+    np.testing.assert_allclose(s2, Sall, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(z2, zall, rtol=1e-12, atol=1e-13)
+
+
+def test_initial_state_applies_to_first_packed_document_only():
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 26, 8, 43, [9, 0, 6, 11])
+    r = np.random.default_rng(44)
+    S0, z0 = np.abs(r.normal(size=(2, 8, 8))), np.abs(r.normal(size=(2, 8)))
+    out = oracle.fwd(q, k, v, gq, gk, cu, initial_S=S0, initial_z=z0, initial_pos=5)
+    docs = oracle.documents(1, 26, cu)
+    assert oracle.first_documents(1, 26, cu) == {0} and oracle.first_documents(3, 4) == {0, 1, 2}
+    for j, (_, s0, s1) in enumerate(docs):
+        sl = (slice(None), slice(None), slice(s0, s1))
+        alone = oracle.fwd(q[sl], k[sl], v[sl], gq, gk, **(dict(initial_S=S0, initial_z=z0, initial_pos=5)
+                                                          if j == 0 else {}))
+        np.testing.assert_allclose(out[sl], alone, rtol=1e-13, atol=1e-15)
+    # a zero initial state at offset 0 is the plain forward, bitwise
+    np.testing.assert_array_equal(oracle.fwd(q, k, v, gq, gk, cu, initial_S=np.zeros((2, 8, 8)),
+                                             initial_z=np.zeros((2, 8))), oracle.fwd(q, k, v, gq, gk, cu))
+
+
+def test_bidirectional_mode():
+    # RLA page §4.1 (causal=false: one constant state per document) and §4.2. Every
+    # row is the read-out of its document's whole state, computed here the other way
+    # round (state first, K'^T V, then q' S / (q' . z + eps)); the last row of each
+    # document equals the causal output there; rows still never see other documents.
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 23, 8, 45, [7, 16])
+    r = np.random.default_rng(46)
+    S0, z0 = np.abs(r.normal(size=(2, 8, 8))), np.abs(r.normal(size=(2, 8)))
+    for init in ({}, dict(initial_S=S0, initial_z=z0, initial_pos=3)):
+        bi = oracle.fwd(q, k, v, gq, gk, cu, causal=False, **init)
+        ca = oracle.fwd(q, k, v, gq, gk, cu, **init)
+        St, zt = oracle.state_from_prefix(k, v, gk, cu, **init)
+        for j, (_, s0, s1) in enumerate(oracle.documents(1, 23, cu)):
+            start = init.get("initial_pos", 0) if j == 0 else 0
+            for h in range(2):
+                qp = oracle.feature_map(q[0, h, s0:s1], gq[h], start + np.arange(s1 - s0))
+                ref = (qp @ St[j, h]) / (qp @ zt[j, h] + oracle.DEFAULT_EPS)[:, None]
+                np.testing.assert_allclose(bi[0, h, s0:s1], ref, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(bi[0, :, s1 - 1], ca[0, :, s1 - 1], rtol=1e-12, atol=1e-14)
+        rows = [0, 6, 7, 15, 22]
+        for h in range(2):
+            np.testing.assert_allclose(oracle.fwd_rows(q, k, v, gq, gk, 0, h, rows, cu, causal=False, **init),
+                                       bi[0, h, rows], rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(oracle.fwd_rows(q, k, v, gq, gk, 0, h, rows, cu, **init),
+                                       ca[0, h, rows], rtol=1e-13, atol=1e-15)
+    # a later token of the same document now changes an earlier row
+    v2 = v.copy()
+    v2[0, :, 20] += 5.0
+    assert not np.allclose(oracle.fwd(q, k, v2, gq, gk, cu, causal=False)[0, :, 8],
+                           oracle.fwd(q, k, v, gq, gk, cu, causal=False)[0, :, 8])
