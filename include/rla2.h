@@ -79,7 +79,26 @@ typedef enum rla2_dtype { RLA2_F32 = 0, RLA2_BF16 = 1 } rla2_dtype;
  *               Zero-length documents are allowed.
  *  n_docs       number of documents when cu_seqlens != NULL (>= 0); ignored
  *               (treated as B) when cu_seqlens == NULL.
+ *  bidirectional  0: causal, out_t reads the state after token t (RLA page §3).
+ *               1: every token reads its whole document's state, out_t =
+ *               q'_t S_doc / (q'_t . z_doc + eps) (RLA page §4.1, the scan's
+ *               causal=false mode: one constant state per document). Other
+ *               values return RLA2_ERR_BAD_VALUE.
+ *  initial_S, initial_z  optional DEVICE fp32 [H, d, d] and [H, d] (both or
+ *               neither; one of them NULL returns RLA2_ERR_NULL_POINTER): a state
+ *               that starts the first document of each row -- every row when
+ *               cu_seqlens == NULL, document 0 when packed -- as the prefix scan's
+ *               A0/B0 inputs of RLA page §4.1 do (one per head, shared by the
+ *               batch rows, first document only). Layout as final_S:
+ *               initial_S[h][a][c] pairs key dim a with value dim c. Read only;
+ *               outputs must not overlap them (RLA2_ERR_ALIAS).
+ *  initial_pos  position of the first token of the first document of each row
+ *               (>= 0; a continuation passes the length of the context its
+ *               initial state summarises). Other documents start at 0.
+ *               initial_pos + L must fit in int32 (RLA2_ERR_BAD_VALUE otherwise).
  * The number of documents N is n_docs with cu_seqlens, B without.
+ * A zero-initialised descriptor tail (bidirectional = initial_pos = 0, NULL
+ * initial state) is the plain causal forward.
  */
 typedef struct rla2_fwd_desc {
   int32_t B, H, L, d;
@@ -89,6 +108,10 @@ typedef struct rla2_fwd_desc {
   float eps, rms_eps, rope_base;
   const int32_t* cu_seqlens;
   int32_t n_docs;
+  int32_t bidirectional;
+  int32_t initial_pos;
+  const float* initial_S;
+  const float* initial_z;
 } rla2_fwd_desc;
 
 /* Human-readable name of a status code (static storage; never NULL). */
@@ -104,14 +127,16 @@ int32_t rla2_abi_version(void);
 rla2_status rla2_fwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
 
 /*
- * Chunked RLA-2 causal forward (RLA page §3 formula; the chunking is the
+ * Chunked RLA-2 forward (RLA page §3 formula; the chunking is the
  * associativity of §1: a d x d state carried across chunks, each chunk's own
- * causal part formed directly).
+ * causal part formed directly). Causal, or bidirectional per desc->bidirectional;
+ * an optional initial state per desc->initial_S/initial_z.
  *  q, k, v      [B, H, L, d] dtype, read only.
  *  gamma_q/k    [H, d] fp32 RMSNorm weights of q and k.
  *  out          [B, H, L, d] dtype, written (every row of every document).
  *  final_S      optional [N, H, d, d] fp32: each document's state after its last
- *               token, S[a][c] = sum_i k'_i[a] v_i[c]; NULL = not exported.
+ *               token, S[a][c] = sum_i k'_i[a] v_i[c] (plus the initial state for
+ *               the first document of each row); NULL = not exported.
  *  final_z      optional [N, H, d] fp32, z = sum_i k'_i; NULL = not exported.
  *  workspace    device scratch of at least rla2_fwd_workspace_size() bytes,
  *               256-byte aligned; contents on entry are ignored.
@@ -146,7 +171,9 @@ rla2_status rla2_state_from_prefix_workspace_size(const rla2_fwd_desc* desc, siz
 /*
  * State of every document after its last token, from its keys and values:
  * S = sum_i k'_i (x) v_i, z = sum_i k'_i (RLA page §3 state; §4.2 forward_step
- * keeps exactly this pair as its cache). q is not needed.
+ * keeps exactly this pair as its cache). q is not needed. The first document of
+ * each row starts from desc->initial_S/initial_z at desc->initial_pos, as in the
+ * forward; desc->bidirectional is validated but does not change the result.
  *  k, v     [B, H, L, d] dtype (packed [1, H, T, d] with cu_seqlens).
  *  gamma_k  [H, d] fp32.
  *  S        [N, H, d, d] fp32, written.   z  [N, H, d] fp32, written.

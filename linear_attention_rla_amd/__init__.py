@@ -40,7 +40,9 @@ class FwdDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("chunk", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
                 ("eps", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
-                ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32)]
+                ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
+                ("bidirectional", ctypes.c_int32), ("initial_pos", ctypes.c_int32),
+                ("initial_S", ctypes.c_void_p), ("initial_z", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -94,12 +96,27 @@ def _stream(dev: torch.device):
 
 
 def make_desc(B, H, L, d, dtype, cu_seqlens=None, n_docs=0, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
-              rope_base=10000.0) -> FwdDesc:
+              rope_base=10000.0, bidirectional=False, initial_pos=0, initial_S=None, initial_z=None) -> FwdDesc:
     return FwdDesc(B, H, L, d, dtype, chunk, seg_chunks, eps, rms_eps, rope_base,
-                   None if cu_seqlens is None else cu_seqlens.data_ptr(), n_docs)
+                   None if cu_seqlens is None else cu_seqlens.data_ptr(), n_docs, int(bool(bidirectional)),
+                   initial_pos, None if initial_S is None else initial_S.data_ptr(),
+                   None if initial_z is None else initial_z.data_ptr())
 
 
-def _fwd_desc(x: torch.Tensor, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base) -> FwdDesc:
+def _initial_state(x: torch.Tensor, initial_S, initial_z):
+    """Checks of the optional initial state ([H, d, d], [H, d] fp32 on x's device)."""
+    if (initial_S is None) != (initial_z is None):
+        raise ValueError("initial_S and initial_z go together")
+    if initial_S is not None:
+        _, H, _, d = x.shape
+        _check_dev("initial_S", initial_S, torch.float32)
+        _check_dev("initial_z", initial_z, torch.float32)
+        if initial_S.shape != (H, d, d) or initial_z.shape != (H, d):
+            raise ValueError("initial_S must be [H, d, d] and initial_z [H, d]")
+
+
+def _fwd_desc(x: torch.Tensor, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base, bidirectional=False,
+              initial_pos=0, initial_S=None, initial_z=None) -> FwdDesc:
     if x.dim() != 4:
         raise ValueError("expected [B, H, L, d]")
     if x.dtype not in _DTYPES:
@@ -109,7 +126,9 @@ def _fwd_desc(x: torch.Tensor, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope
     if cu_seqlens is not None:
         _check_dev("cu_seqlens", cu_seqlens, torch.int32)
         n_docs = cu_seqlens.numel() - 1
-    return make_desc(B, H, L, d, _DTYPES[x.dtype], cu_seqlens, n_docs, chunk, seg_chunks, eps, rms_eps, rope_base)
+    _initial_state(x, initial_S, initial_z)
+    return make_desc(B, H, L, d, _DTYPES[x.dtype], cu_seqlens, n_docs, chunk, seg_chunks, eps, rms_eps, rope_base,
+                     bidirectional, initial_pos, initial_S, initial_z)
 
 
 def fwd_workspace_size(desc: FwdDesc) -> int:
@@ -121,16 +140,21 @@ def fwd_workspace_size(desc: FwdDesc) -> int:
 
 
 def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
-        rope_base=10000.0, return_final_state=False, out=None, workspace=None, events=None):
-    """Chunked RLA-2 causal forward. Returns ``out`` or ``(out, final_S, final_z)``.
+        rope_base=10000.0, return_final_state=False, out=None, workspace=None, events=None,
+        bidirectional=False, initial_S=None, initial_z=None, initial_pos=0):
+    """Chunked RLA-2 forward (causal, or bidirectional). Returns ``out`` or
+    ``(out, final_S, final_z)``.
 
+    ``initial_S [H, d, d]``, ``initial_z [H, d]`` (fp32, optional, together) start the
+    first document of each row, whose positions begin at ``initial_pos``.
     ``events``: optional ctypes array of RLA2_FWD_KERNELS + 1 hipEvent_t handles; when
     given, rla2_fwd_chunked_profiled records them around each kernel."""
     for n_, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(n_, t, q.dtype)
     _check_dev("gamma_q", gamma_q, torch.float32)
     _check_dev("gamma_k", gamma_k, torch.float32)
-    desc = _fwd_desc(q, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base)
+    desc = _fwd_desc(q, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base, bidirectional, initial_pos,
+                     initial_S, initial_z)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v shapes differ")
     if gamma_q.shape != (desc.H, desc.d) or gamma_k.shape != (desc.H, desc.d):
@@ -157,12 +181,15 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
 
 
 def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, rms_eps=1e-6,
-                      rope_base=10000.0, S=None, z=None, workspace=None):
-    """Per-document state after its last token. Returns ``(S, z)``."""
+                      rope_base=10000.0, S=None, z=None, workspace=None, initial_S=None, initial_z=None,
+                      initial_pos=0):
+    """Per-document state after its last token (starting from the optional initial
+    state for the first document of each row). Returns ``(S, z)``."""
     _check_dev("k", k)
     _check_dev("v", v, k.dtype)
     _check_dev("gamma_k", gamma_k, torch.float32)
-    desc = _fwd_desc(k, cu_seqlens, chunk, seg_chunks, 1e-4, rms_eps, rope_base)
+    desc = _fwd_desc(k, cu_seqlens, chunk, seg_chunks, 1e-4, rms_eps, rope_base, False, initial_pos,
+                     initial_S, initial_z)
     N = desc.n_docs if cu_seqlens is not None else desc.B
     if S is None:
         S = torch.empty(N, desc.H, desc.d, desc.d, dtype=torch.float32, device=k.device)

@@ -15,7 +15,7 @@ namespace {
 
 using rla2::Plan;
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 static_assert(RLA2_FWD_KERNELS == rla2::kNumFwdKernels, "kernel count of the profiled forward");
 
 bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
@@ -64,6 +64,9 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   if (!finite_pos(d->eps) || !finite_pos(d->rms_eps) || !finite_pos(d->rope_base))
     return RLA2_ERR_BAD_VALUE;
   if (validate_mode() < 0) return RLA2_ERR_BAD_VALUE;
+  if (d->bidirectional != 0 && d->bidirectional != 1) return RLA2_ERR_BAD_VALUE;
+  if (d->initial_pos < 0 || (long long)d->initial_pos + d->L > INT32_MAX) return RLA2_ERR_BAD_VALUE;
+  if ((d->initial_S == nullptr) != (d->initial_z == nullptr)) return RLA2_ERR_NULL_POINTER;
   // every token index and every segment index must stay within int32 on device
   const long long tokens = (long long)d->B * d->L;
   if (tokens > INT32_MAX || (long long)d->B * d->H > INT32_MAX) return RLA2_ERR_BAD_SHAPE;
@@ -74,6 +77,8 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   p->L = d->L;
   p->d = d->d;
   p->dtype = d->dtype;
+  p->bidirectional = d->bidirectional == 1;
+  p->initial_pos = d->initial_pos;
   p->packed = d->cu_seqlens != nullptr;
   p->n_docs = p->packed ? d->n_docs : d->B;
   const int rows = p->packed ? 1 : p->B;
@@ -100,6 +105,9 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   p->n_seg_max = (int)nseg;
   p->n_hi = (int)((L + rla2::kChunk - 1) / rla2::kChunk);
   if (p->n_hi < 1) p->n_hi = 1;
+  // with a position offset the first documents read a second set of chunk rows,
+  // (initial_pos + 64 a) * theta, right after the plain set
+  p->hi_off = p->initial_pos != 0 ? p->n_hi : 0;
 
   const size_t half = (size_t)p->d / 2;
   const size_t rec = (size_t)p->d * p->d + p->d;
@@ -113,7 +121,7 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   p->off_rope_lo = off;
   off = align_up(off + (size_t)rla2::kChunk * half * 8);
   p->off_rope_hi = off;
-  off = align_up(off + (size_t)p->n_hi * half * 8);
+  off = align_up(off + (size_t)(p->n_hi + p->hi_off) * half * 8);
   p->off_states = off;
   off = align_up(off + (size_t)p->n_seg_max * p->H * rec * 4);
   p->bytes = (p->n_docs == 0 || p->H == 0) ? 0 : off;  // no documents or heads: nothing to run
@@ -198,12 +206,14 @@ rla2_status rla2_fwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   if (p.bytes > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return RLA2_ERR_WORKSPACE;
   if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
     return RLA2_ERR_WORKSPACE;
-  if (misaligned({q, k, v, out, gamma_q, gamma_k, final_S, final_z})) return RLA2_ERR_MISALIGNED;
+  if (misaligned({q, k, v, out, gamma_q, gamma_k, final_S, final_z, desc->initial_S, desc->initial_z}))
+    return RLA2_ERR_MISALIGNED;
   const Range o{out, act}, fs{final_S, fsb}, fz{final_z, fzb}, ws{workspace, p.bytes};
   const Range ins[] = {{q, act}, {k, act}, {v, act}, {gamma_q, gam}, {gamma_k, gam},
-                       {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4}};
+                       {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4},
+                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4}};
   for (const Range& r : ins)
-    if (overlap(o, r) || overlap(fs, r) || overlap(fz, r)) return RLA2_ERR_ALIAS;
+    if (overlap(o, r) || overlap(fs, r) || overlap(fz, r) || overlap(ws, r)) return RLA2_ERR_ALIAS;
   if (overlap(o, fs) || overlap(o, fz) || overlap(fs, fz) || overlap(o, ws) || overlap(fs, ws) ||
       overlap(fz, ws))
     return RLA2_ERR_ALIAS;
@@ -213,7 +223,8 @@ rla2_status rla2_fwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   }
   if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
   rla2::FwdArgs a{desc->cu_seqlens, q, k, v, gamma_q, gamma_k, out, final_S, final_z,
-                  desc->eps, desc->rms_eps, desc->rope_base, static_cast<char*>(workspace)};
+                  desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
+                  static_cast<char*>(workspace)};
   return finish(rla2::launch_chunked(p, a, stream, events));
 }
 
@@ -233,11 +244,12 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
   if (p.bytes > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return RLA2_ERR_WORKSPACE;
   if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
     return RLA2_ERR_WORKSPACE;
-  if (misaligned({k, v, gamma_k, S, z})) return RLA2_ERR_MISALIGNED;
+  if (misaligned({k, v, gamma_k, S, z, desc->initial_S, desc->initial_z})) return RLA2_ERR_MISALIGNED;
   const Range rs{S, sb}, rz{z, zb}, ws{workspace, p.bytes};
-  const Range ins[] = {{k, act}, {v, act}, {gamma_k, gam}, {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4}};
+  const Range ins[] = {{k, act}, {v, act}, {gamma_k, gam}, {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4},
+                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4}};
   for (const Range& r : ins)
-    if (overlap(rs, r) || overlap(rz, r)) return RLA2_ERR_ALIAS;
+    if (overlap(rs, r) || overlap(rz, r) || overlap(ws, r)) return RLA2_ERR_ALIAS;
   if (overlap(rs, rz) || overlap(rs, ws) || overlap(rz, ws)) return RLA2_ERR_ALIAS;
   if (p.packed && validate_mode() == 1) {
     st = check_seqlens(p, desc->cu_seqlens, stream);
@@ -245,7 +257,8 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
   }
   if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
   rla2::FwdArgs a{desc->cu_seqlens, nullptr, k, v, nullptr, gamma_k, nullptr, S, z,
-                  desc->eps, desc->rms_eps, desc->rope_base, static_cast<char*>(workspace)};
+                  desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
+                  static_cast<char*>(workspace)};
   return finish(rla2::launch_chunked(p, a, stream));
 }
 

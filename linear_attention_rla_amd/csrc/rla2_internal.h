@@ -15,16 +15,19 @@ constexpr int kTabInts = 8;         // int32 fields per segment-table entry
 constexpr size_t kAlign = 256;
 
 // Segment-table entry fields (int32 each).
-enum TabField { TAB_ROW = 0, TAB_START = 1, TAB_LEN = 2, TAB_POS0 = 3, TAB_DOC = 4 };
+enum TabField { TAB_ROW = 0, TAB_START = 1, TAB_LEN = 2, TAB_POS0 = 3, TAB_DOC = 4, TAB_HIROW = 5 };
 
 // Everything a launch needs about the problem and the workspace carve-up.
 struct Plan {
   int B, H, L, d, dtype;
+  bool bidirectional;  // every token reads its whole document's state
+  int initial_pos;     // first position of the first document of each row
   int n_docs;          // documents (B when not packed)
   bool packed;         // cu_seqlens given
   int seg_len;         // tokens per segment, multiple of kChunk
   int n_seg_max;       // upper bound on segments (grid size of the sweep kernels)
   int n_hi;            // rows of the coarse RoPE table (positions / 64)
+  int hi_off;          // 0, or n_hi when the first documents use the offset rows
   size_t off_tab, off_docoff, off_nseg, off_rope_lo, off_rope_hi, off_states;
   size_t bytes;        // total workspace bytes
 };
@@ -35,6 +38,7 @@ struct FwdArgs {
   const float *gq, *gk;
   void* out;           // null for the state build
   float *final_S, *final_z;
+  const float *init_S, *init_z;  // optional initial state, [H, d, d] and [H, d]
   float eps, rms_eps, rope_base;
   char* ws;
 };

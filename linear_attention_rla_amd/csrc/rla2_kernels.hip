@@ -493,19 +493,20 @@ __device__ __forceinline__ void store_cols(typename Elem<BF>::St* dst, const Raw
 
 struct SegInfo {
   int row, start, len, pos0;
+  int hirow;  // RoPE chunk row of the segment's first chunk
 };
 
 __device__ __forceinline__ SegInfo read_seg(const int32_t* tab, int seg) {
   const int4 a = *reinterpret_cast<const int4*>(tab + (size_t)seg * kTabInts);
-  return SegInfo{a.x, a.y, a.z, a.w};
+  return SegInfo{a.x, a.y, a.z, a.w, tab[(size_t)seg * kTabInts + TAB_HIROW]};
 }
 
 // ----------------------------------------------------------------------------------------
 // seg_map: documents -> segments of at most seg_len tokens (whole chunks), one workgroup.
 
 __device__ __forceinline__ void seg_map_block(const int32_t* __restrict__ cu, int n_docs, int L, int seg_len,
-                                              int n_seg_max, int32_t* __restrict__ tab, int32_t* __restrict__ docoff,
-                                              int32_t* __restrict__ nseg) {
+                                              int n_seg_max, int hi_off, int32_t* __restrict__ tab,
+                                              int32_t* __restrict__ docoff, int32_t* __restrict__ nseg) {
   __shared__ int scan[1024];
   __shared__ int carry_s;
   const int tid = threadIdx.x;
@@ -546,6 +547,9 @@ __device__ __forceinline__ void seg_map_block(const int32_t* __restrict__ cu, in
         e.w = s * seg_len;
         *reinterpret_cast<int4*>(tab + (size_t)idx * kTabInts) = e;
         tab[(size_t)idx * kTabInts + TAB_DOC] = j;
+        // the first document of each row (every row when unpacked) reads the offset rows
+        const bool first = cu == nullptr || j == 0;
+        tab[(size_t)idx * kTabInts + TAB_HIROW] = (first ? hi_off : 0) + e.w / kChunk;
       }
     }
     __syncthreads();
@@ -561,15 +565,19 @@ __device__ __forceinline__ void seg_map_block(const int32_t* __restrict__ cu, in
 
 // ----------------------------------------------------------------------------------------
 // rope_table: (cos, sin) of p * theta_j, theta_j = base^(-2j/D), in fp64, rounded to fp32.
-// Rows 0..63 hold p = row; rows 64.. hold p = 64 * (row - 64).
+// lo rows 0..63 hold p = row; hi rows a < n_hi hold p = 64 a, and rows n_hi + a (present
+// when the first documents start at an offset) hold p = pos_off + 64 a.
 
 __device__ __forceinline__ void rope_entry(int idx, float2* __restrict__ lo, float2* __restrict__ hi, int half, int D,
-                                           int n_hi, float base) {
-  const int rows = kChunk + n_hi;
+                                           int n_hi, int hi_off, int pos_off, float base) {
+  const int rows = kChunk + n_hi + hi_off;
   if (idx >= rows * half) return;
   const int row = idx / half, j = idx % half;
   const double theta = pow((double)base, -2.0 * (double)j / (double)D);
-  const double p = row < kChunk ? (double)row : (double)kChunk * (double)(row - kChunk);
+  double p;
+  if (row < kChunk) p = (double)row;
+  else if (row < kChunk + n_hi) p = (double)kChunk * (double)(row - kChunk);
+  else p = (double)pos_off + (double)kChunk * (double)(row - kChunk - n_hi);
   double s, c;
   sincos(p * theta, &s, &c);
   const float2 v = make_float2((float)c, (float)s);
@@ -582,9 +590,9 @@ __global__ __launch_bounds__(1024) void prep_kernel(const int32_t* __restrict__ 
                                                     int n_seg_max, int32_t* __restrict__ tab,
                                                     int32_t* __restrict__ docoff, int32_t* __restrict__ nseg,
                                                     float2* __restrict__ lo, float2* __restrict__ hi, int half, int D,
-                                                    int n_hi, float base) {
-  if (blockIdx.x == 0) seg_map_block(cu, n_docs, L, seg_len, n_seg_max, tab, docoff, nseg);
-  else rope_entry((blockIdx.x - 1) * 1024 + threadIdx.x, lo, hi, half, D, n_hi, base);
+                                                    int n_hi, int hi_off, int pos_off, float base) {
+  if (blockIdx.x == 0) seg_map_block(cu, n_docs, L, seg_len, n_seg_max, hi_off, tab, docoff, nseg);
+  else rope_entry((blockIdx.x - 1) * 1024 + threadIdx.x, lo, hi, half, D, n_hi, hi_off, pos_off, base);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -627,7 +635,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + tok0 * D), 0, seg_bytes, kBufFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
   {
-    const float2* hi0 = rope_hi + (size_t)(si.pos0 / kChunk) * G::HALF;
+    const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF;
     for (int i = tid; i < min(nch, kMaxSegChunks) * G::HALF; i += NT) sHi[i] = hi0[i];
   }
   float g1[G::E], g2[G::E];
@@ -729,19 +737,45 @@ __global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
 
 // ----------------------------------------------------------------------------------------
 // state_scan: per (document, head, 1024-float tile of the state record), walk the document's
-// segments in order: optionally replace each total by the exclusive prefix, and write the
-// inclusive end as the document's final state.
+// segments in order, starting from the initial state for the first document of each row
+// (every document when unpacked, document 0 when packed) and from zero otherwise. Mode
+// SCAN_PREFIX replaces each segment total by its exclusive prefix (the causal forward),
+// SCAN_TOTAL writes the document's total into every one of its segment records (the
+// bidirectional forward), SCAN_NONE leaves the records alone (the state build). The
+// inclusive end is the document's final state.
+
+enum ScanMode { SCAN_NONE = 0, SCAN_PREFIX = 1, SCAN_TOTAL = 2 };
 
 __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ states, const int32_t* __restrict__ docoff,
-                                                         int H, int D, int n_tiles, int write_prefix,
-                                                         float* __restrict__ final_S, float* __restrict__ final_z) {
+                                                         int H, int D, int n_tiles, int mode,
+                                                         float* __restrict__ final_S, float* __restrict__ final_z,
+                                                         const float* __restrict__ init_S,
+                                                         const float* __restrict__ init_z, int init_all) {
   const int doc = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles, h = blockIdx.y;
   const int R4 = (D * D + D) / 4;
   const int e4 = tile * 256 + threadIdx.x;
   if (e4 >= R4) return;
+  const int e = 4 * e4;
+  // S part of the record: the 4 floats at e4 are S[row + i][col], i < 4 (fragment-native)
+  int row = 0, col = 0;
+  if (e < D * D) {
+    const int RT = D / 16, NW = D / 16 < 4 ? D / 16 : 4, CT = D / NW / 16;
+    const int ln = e4 % 64, t = e4 / 64;
+    const int ct = t % CT, rt = (t / CT) % RT, w = t / CT / RT;
+    row = 16 * rt + 4 * (ln / 16);
+    col = w * (D / NW) + 16 * ct + ln % 16;
+  }
   const int s0 = docoff[doc], s1 = docoff[doc + 1];
   float4* st = reinterpret_cast<float4*>(states);
   float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (init_S != nullptr && (init_all || doc == 0)) {
+    if (e < D * D) {
+      const float* src = init_S + (size_t)h * D * D + (size_t)row * D + col;
+      run = make_float4(src[0], src[D], src[2 * D], src[3 * D]);
+    } else {
+      run = *reinterpret_cast<const float4*>(init_z + (size_t)h * D + (e - D * D));
+    }
+  }
   constexpr int kBatch = 16;  // records in flight per thread
   for (int s = s0; s < s1; s += kBatch) {
     const int cnt = min(kBatch, s1 - s);
@@ -752,7 +786,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (j < cnt) {
-        if (write_prefix) st[((size_t)(s + j) * H + h) * R4 + e4] = run;
+        if (mode == SCAN_PREFIX) st[((size_t)(s + j) * H + h) * R4 + e4] = run;
         run.x += val[j].x;
         run.y += val[j].y;
         run.z += val[j].z;
@@ -760,12 +794,9 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
       }
     }
   }
-  const int e = 4 * e4;
+  if (mode == SCAN_TOTAL)
+    for (int s = s0; s < s1; ++s) st[((size_t)s * H + h) * R4 + e4] = run;
   if (final_S != nullptr && e < D * D) {  // fragment-native record -> row-major [d][d]
-    const int RT = D / 16, NW = D / 16 < 4 ? D / 16 : 4, CT = D / NW / 16;
-    const int ln = e4 % 64, tile = e4 / 64;
-    const int ct = tile % CT, rt = (tile / CT) % RT, w = tile / CT / RT;
-    const int row = 16 * rt + 4 * (ln / 16), col = w * (D / NW) + 16 * ct + ln % 16;
     float* dst = final_S + ((size_t)doc * H + h) * D * D + (size_t)row * D + col;
     dst[0] = run.x;
     dst[D] = run.y;
@@ -865,7 +896,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
 
     // ---- map
     {
-      const float2* hirow = rope_hi + (size_t)((si.pos0 + c0) / kChunk) * G::HALF;
+      const float2* hirow = rope_hi + (size_t)(si.hirow + c0 / kChunk) * G::HALF;
       // The RMSNorm weights and the in-chunk RoPE table are the same for every chunk; hiding
       // their addresses from the optimiser keeps it from holding ~64 loaded values in
       // registers across the whole sweep (they are re-read from cache each chunk instead).
@@ -1179,7 +1210,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     // Every step issues the same loads (chunks past the end read zeros from the buffer
     // range check), so the compiler's wait counts let chunk st + 1 stay in flight while
     // chunk st is mapped.
-    const float2* hi0 = rope_hi + (size_t)(si.pos0 / kChunk) * G::HALF + m * G::E;
+    const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * G::E;
     auto issue = [&](R (&r)[3], float2 (&hi)[G::E], int c) {
       copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
       load_raw_buf<true, D>(r[0], rq, c * kChunk + t0, m);
@@ -1344,6 +1375,142 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 }
 
 // ----------------------------------------------------------------------------------------
+// readout (bidirectional forward): per (segment, head), every token reads its document's
+// whole state, out_t = q'_t S_doc / (q'_t . z_doc + eps). The document state arrives in the
+// segment's record (fragment-native S, then z); the state waves round it once to the MFMA
+// operand type and keep it in registers. Per chunk every lane maps q for two tokens into LDS
+// rows and forms q'.z in fp32 against z in LDS (from the rounded q' the MFMA uses); then the
+// state waves form O^T = S^T Q'^T for their value columns, scale each row by 1/(q'.z + eps)
+// and stage the rows in LDS, and all lanes write them out as whole rows (range-checked buffer
+// stores). Raw q and the RoPE row of the next two chunks are in flight in registers.
+
+template <bool BF, int D>
+__global__ __launch_bounds__(NT, 2) void readout_kernel(
+    const typename Elem<BF>::St* __restrict__ q, const float* __restrict__ gamma_q, const int32_t* __restrict__ tab,
+    const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
+    const float* __restrict__ states, typename Elem<BF>::St* __restrict__ out, int H, int L, float rms_eps,
+    float eps) {
+  using G = Geo<BF, D>;
+  using St = typename G::St;
+  using R = Raw<BF, D>;
+  constexpr int EPP = 16 / G::ES;           // elements per 16-byte piece
+  constexpr int PPR = D / EPP;              // 16-byte pieces per row
+  __shared__ __attribute__((aligned(16))) St sQ[kChunk * G::ROWP];
+  __shared__ __attribute__((aligned(16))) St sO[kChunk * G::ROWP];
+  __shared__ __attribute__((aligned(16))) float sZ[D];
+  __shared__ float sInv[kChunk];
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
+  const int t0 = 2 * (tid >> 3), m = tid & 7;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * G::ES;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + tok0 * D), 0, seg_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + tok0 * D), 0, seg_bytes, kBufFlags);
+  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  if (tid < D) sZ[tid] = rec[D * D + tid];
+  float g1[G::E], g2[G::E];
+  float2 lo[2][G::E];
+#pragma unroll
+  for (int e = 0; e < G::E; ++e) {
+    const int j = m * G::E + e;
+    g1[e] = gamma_q[(size_t)h * D + j];
+    g2[e] = gamma_q[(size_t)h * D + j + G::HALF];
+    lo[0][e] = rope_lo[t0 * G::HALF + j];
+    lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
+  }
+  // S^T as the A operand of O^T = S^T Q'^T, value columns of this wave
+  Frag<BF> sa[G::KB][G::CT];
+  {
+    const int wv = wave < G::NW ? wave : 0;
+#pragma unroll
+    for (int kb2 = 0; kb2 < G::KB; ++kb2)
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+        sa[kb2][ct] = acc_frag<BF>(*reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, 2 * kb2, ct, lane)),
+                                   *reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, 2 * kb2 + 1, ct, lane)));
+  }
+  const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * G::E;
+  auto issue = [&](R& r, float2 (&hi)[G::E], int c) {
+    copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
+    load_raw_buf<BF, D>(r, rq, c * kChunk + t0, m);
+  };
+  auto step = [&](int c, R& r, float2 (&hi)[G::E]) {
+    {  // ---- map q, q'.z
+      R o;
+      feature_map_lane<BF, D>(r, o, g1, g2, lo, hi, rms_eps);
+      store_rows<BF, D>(sQ, o, t0, m);
+#pragma unroll
+      for (int tok = 0; tok < 2; ++tok) {
+        float p = 0.f;
+#pragma unroll
+        for (int e = 0; e < G::E; ++e) {
+          p = __builtin_fmaf(o.get(tok, 0, e), sZ[m * G::E + e], p);
+          p = __builtin_fmaf(o.get(tok, 1, e), sZ[G::HALF + m * G::E + e], p);
+        }
+        p = sum8(p);
+        if (m == 0) sInv[t0 + tok] = 1.0f / (p + eps);
+      }
+    }
+    issue(r, hi, c + 2);  // into the registers just consumed
+    __syncthreads();  // Q' rows and row reciprocals complete
+    if (wave < G::NW) {  // ---- O^T for this wave's value columns, all 64 rows
+      floatx4 o4[G::CT][4];
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) o4[ct][t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb2 = 0; kb2 < G::KB; ++kb2)
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const Frag<BF> qf = lds_frag<BF>(sQ, G::ROWP, t4 * 16 + c16, kb2, g);
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) o4[ct][t4] = mma(sa[kb2][ct], qf, o4[ct][t4]);
+        }
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int t = t4 * 16 + c16;  // this lane's row; columns col .. col + 3
+        const float rr = sInv[t];
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          const int col = wave * G::DVW + ct * 16 + 4 * g;
+          if constexpr (BF) {
+            const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o4[ct][t4][0] * rr, o4[ct][t4][1] * rr}, bf16x2));
+            const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o4[ct][t4][2] * rr, o4[ct][t4][3] * rr}, bf16x2));
+            *reinterpret_cast<uint2*>(sO + t * G::ROWP + col) = make_uint2(w0, w1);
+          } else {
+            *reinterpret_cast<float4*>(sO + t * G::ROWP + col) =
+                make_float4(o4[ct][t4][0] * rr, o4[ct][t4][1] * rr, o4[ct][t4][2] * rr, o4[ct][t4][3] * rr);
+          }
+        }
+      }
+    }
+    __syncthreads();  // output rows staged
+#pragma unroll
+    for (int i = tid; i < kChunk * PPR; i += NT) {  // rows past the segment are dropped
+      const int rr = i / PPR, pc = i % PPR;
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(sO + rr * G::ROWP + pc * EPP), ro,
+                                             ((c * kChunk + rr) * D + pc * EPP) * G::ES, 0, kLoadStream);
+    }
+  };
+  R set0, set1;
+  float2 hs0[G::E], hs1[G::E];
+  issue(set0, hs0, 0);
+  issue(set1, hs1, 1);
+  __syncthreads();  // z in LDS
+  for (int c = 0; c < nch; c += 2) {
+    step(c, set0, hs0);
+    if (c + 1 < nch) step(c + 1, set1, hs1);  // uniform over the workgroup
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // decode: one workgroup per (sequence, head). Every global load is issued first (the fp32
 // state rows of each thread, then z, v and the new token's q, k), so the state traffic is in
 // flight while wave 0 maps q and wave 1 maps k (lane j holds the RoPE pair j, j + D/2; the
@@ -1479,9 +1646,10 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   };
 
   mark(0);
-  const int rope_entries = (kChunk + p.n_hi) * half;
+  const int rope_entries = (kChunk + p.n_hi + p.hi_off) * half;
   hipLaunchKernelGGL(prep_kernel, dim3(1 + (rope_entries + 1023) / 1024), dim3(1024), 0, s, a.cu, p.n_docs, p.L,
-                     p.seg_len, p.n_seg_max, tab, docoff, nseg, rlo, rhi, half, D, p.n_hi, a.rope_base);
+                     p.seg_len, p.n_seg_max, tab, docoff, nseg, rlo, rhi, half, D, p.n_hi, p.hi_off, p.initial_pos,
+                     a.rope_base);
   mark(1);
   if (p.n_seg_max > 0) {
     hipLaunchKernelGGL((chunk_state_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
@@ -1493,11 +1661,15 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   const bool want_final = a.final_S != nullptr || a.final_z != nullptr;
   const bool fwd = a.out != nullptr;
   if (want_final || (fwd && p.n_seg_max > 0)) {
+    const int mode = !fwd ? SCAN_NONE : (p.bidirectional ? SCAN_TOTAL : SCAN_PREFIX);
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
-                       n_tiles, fwd ? 1 : 0, a.final_S, a.final_z);
+                       n_tiles, mode, a.final_S, a.final_z, a.init_S, a.init_z, p.packed ? 0 : 1);
   }
   mark(3);
-  if (fwd && p.n_seg_max > 0) {
+  if (fwd && p.n_seg_max > 0 && p.bidirectional) {
+    hipLaunchKernelGGL((readout_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s, static_cast<const St*>(a.q),
+                       a.gq, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+  } else if (fwd && p.n_seg_max > 0) {
     if constexpr (BF) {
       hipLaunchKernelGGL((chunk_out_ws_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
                          static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,

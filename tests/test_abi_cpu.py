@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = rla.lib()
-    assert L.rla2_abi_version() == 1
+    assert L.rla2_abi_version() == 2
     for code, name in rla.STATUS.items():
         assert L.rla2_status_string(code).decode().startswith(name)
     assert L.rla2_status_string(99).decode() == "RLA2_ERR_UNKNOWN"
@@ -52,8 +52,10 @@ def desc(**kw):
                 rope_base=1e4, cu_seqlens=None, n_docs=0)
     base.update(kw)
     cu = base.pop("cu_seqlens")
+    init_S, init_z = base.pop("initial_S", None), base.pop("initial_z", None)
     d = rla.FwdDesc(**{k: v for k, v in base.items()})
     d.cu_seqlens = cu
+    d.initial_S, d.initial_z = init_S, init_z
     return d
 
 
@@ -70,6 +72,8 @@ def ws_size(d):
     (dict(rope_base=float("inf")), VALUE), (dict(seg_chunks=-1), VALUE), (dict(seg_chunks=65), VALUE),
     (dict(B=2, cu_seqlens=A, n_docs=3), SHAPE), (dict(B=1, cu_seqlens=A, n_docs=-1), SHAPE),
     (dict(B=1 << 16, L=1 << 16), SHAPE),
+    (dict(bidirectional=2), VALUE), (dict(bidirectional=-1), VALUE), (dict(initial_pos=-1), VALUE),
+    (dict(initial_pos=(1 << 31) - 300), VALUE), (dict(initial_S=A), NULLP), (dict(initial_z=A), NULLP),
 ])
 def test_desc_validation(kw, expect):
     assert ws_size(desc(**kw))[0] == expect
@@ -107,6 +111,13 @@ def test_fwd_error_paths():
     assert fwd_call(d, fS=A + 300 * MB, fz=A + 300 * MB) == ALIAS
     assert fwd_call(desc(d=40)) == UNSUP
     assert fwd_call(desc(eps=-1.0)) == VALUE
+    # initial state ([H, d, d] = 4 * 64 * 64 * 4 B = 64 KiB, [H, d] = 1 KiB)
+    init = dict(initial_S=A + 400 * MB, initial_z=A + 401 * MB)
+    assert fwd_call(desc(initial_S=A + 400 * MB + 4, initial_z=A + 401 * MB)) == MISAL
+    assert fwd_call(desc(**init), out=A + 400 * MB) == ALIAS     # output over the initial state
+    assert fwd_call(desc(**init), fz=A + 401 * MB) == ALIAS      # final state over the initial state
+    assert fwd_call(desc(initial_S=A + 512 * MB, initial_z=A + 401 * MB)) == ALIAS  # inside the workspace
+    assert desc(**init).initial_S == A + 400 * MB
 
 
 def test_fwd_empty_work_is_noop_without_gpu():

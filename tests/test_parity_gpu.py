@@ -289,3 +289,82 @@ def test_c5_decode_full_size():
                                            np.array([s1 - s0]), f64(dec.gamma_q), f64(dec.gamma_k), S_ref, z_ref)
         assert row_rel_err(out[n], o_ref[0]) <= TOL_BF16, f"decode output of sequence {n}"
         assert mat_rel_err(S[n], S1[0]) <= TOL_BF16 and mat_rel_err(z[n], z1[0], 1) <= TOL_BF16
+
+
+# --- initial state with a position offset, and the bidirectional mode ------------------
+
+def _oracle_opts(inp, **kw):
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.numpy()
+    return oracle.fwd(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.gamma_q), f64(inp.gamma_k), cu, inp.eps,
+                      inp.rms_eps, inp.rope_base, **kw)
+
+
+@pytest.mark.parametrize("B,H,L,d,dtype,lengths,bidir,pos,seg_chunks", [
+    (2, 2, 300, 64, torch.bfloat16, None, False, 1000, 2),
+    (2, 2, 300, 64, torch.bfloat16, None, True, 0, 0),
+    (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], True, 37, 1),
+    (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], False, 65, 1),
+    (1, 1, 190, 64, torch.float32, None, True, 0, 2),
+    (1, 2, 150, 32, torch.float32, [20, 130], False, 12345, 1),
+    (2, 1, 129, 32, torch.bfloat16, None, True, 70000, 0),
+])
+@pytest.mark.parametrize("with_init", [False, True])
+def test_initial_state_and_bidirectional(B, H, L, d, dtype, lengths, bidir, pos, seg_chunks, with_init):
+    inp = workloads.fwd_inputs(B, H, L, d, dtype, seed=300 + L + d + pos % 97, lengths=lengths)
+    q, k, v, gq, gk, cu = on_gpu(inp)
+    S0 = z0 = None
+    kw = dict(causal=not bidir, initial_pos=pos)
+    if with_init:
+        S0, z0 = workloads.initial_state(H, d, seed=L + d)
+        kw.update(initial_S=f64(S0), initial_z=f64(z0))
+        S0, z0 = S0.to(DEV), z0.to(DEV)
+    out, fS, fz = rla.fwd(q, k, v, gq, gk, cu, seg_chunks=seg_chunks, return_final_state=True, bidirectional=bidir,
+                          initial_S=S0, initial_z=z0, initial_pos=pos)
+    torch.cuda.synchronize()
+    ref = _oracle_opts(inp, **kw)
+    err = row_rel_err(out, ref)
+    print(f"[{B},{H},{L},{d}] {dtype} docs={lengths} bidir={bidir} pos={pos} init={with_init}: max row rel err {err:.3e}")
+    assert err <= tol(inp)
+    cu_np = None if lengths is None else inp.cu_seqlens.numpy()
+    St, zt = oracle.state_from_prefix(f64(inp.k), f64(inp.v), f64(inp.gamma_k), cu_np, inp.rms_eps, inp.rope_base,
+                                      kw.get("initial_S"), kw.get("initial_z"), pos)
+    assert mat_rel_err(fS, St) <= tol(inp)
+    assert mat_rel_err(fz, zt, 1) <= tol(inp)
+    if with_init:  # the state build takes the same initial state and offset
+        S1, z1 = rla.state_from_prefix(k, v, gk, cu, seg_chunks=seg_chunks, initial_S=S0, initial_z=z0,
+                                       initial_pos=pos)
+        assert torch.equal(S1, fS) and torch.equal(z1, fz)
+
+
+def test_prefill_continuation_matches_whole_sequence():
+    # A context P summarised by the state build, then X run from that state with positions
+    # continuing at len(P), equals the rows of X in one forward over P ++ X.
+    H, d, p, n = 2, 128, 333, 200
+    whole = workloads.fwd_inputs(1, H, p + n, d, torch.bfloat16, seed=77)
+    q, k, v, gq, gk, _ = on_gpu(whole)
+    S0, z0 = rla.state_from_prefix(k[:, :, :p].contiguous(), v[:, :, :p].contiguous(), gk)
+    out = rla.fwd(q[:, :, p:].contiguous(), k[:, :, p:].contiguous(), v[:, :, p:].contiguous(), gq, gk,
+                  initial_S=S0[0].contiguous(), initial_z=z0[0].contiguous(), initial_pos=p)
+    torch.cuda.synchronize()
+    ref = oracle_full(whole)[:, :, p:]
+    err = row_rel_err(out, ref)
+    print(f"continuation after {p} tokens: max row rel err {err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_bidirectional_c3_size_sampled():
+    # the packed 16384-token, 16-head, d = 128 workload in the bidirectional mode, sampled rows
+    inp = workloads.c3_packed()
+    q, k, v, gq, gk, cu = on_gpu(inp)
+    out = rla.fwd(q, k, v, gq, gk, cu, bidirectional=True)
+    torch.cuda.synchronize()
+    T = inp.q.shape[2]
+    rows = sample_rows(T, 24, seed=5)
+    cu_np = inp.cu_seqlens.numpy()
+    worst = 0.0
+    for h in (0, 7, 15):
+        ref = oracle.fwd_rows(inp.q, inp.k, inp.v, f64(inp.gamma_q), f64(inp.gamma_k), 0, h, rows, cu_np, inp.eps,
+                              inp.rms_eps, inp.rope_base, causal=False)
+        worst = max(worst, row_rel_err(out[0, h, rows], ref))
+    print(f"bidirectional packed T={T}: max row rel err {worst:.3e}")
+    assert worst <= TOL_BF16

@@ -19,7 +19,7 @@ from typing import Optional
 import torch
 
 # stream numbers (fixed order)
-S_LENGTHS, S_MASK_Q, S_MASK_K, S_GAMMA_Q, S_GAMMA_K, S_Q, S_K, S_V, S_PREFIX_K, S_PREFIX_V = range(10)
+S_LENGTHS, S_MASK_Q, S_MASK_K, S_GAMMA_Q, S_GAMMA_K, S_Q, S_K, S_V, S_PREFIX_K, S_PREFIX_V, S_INIT_S, S_INIT_Z = range(12)
 
 
 def _gen(seed: int, stream: int, device: str = "cpu") -> torch.Generator:
@@ -54,6 +54,14 @@ def doc_lengths(total: int, lo: int, hi: int, seed: int) -> list:
         out.append(n)
         acc += n
     return out
+
+
+def initial_state(H: int, d: int, seed: int, scale: float = 1.0):
+    """A synthetic fp32 state ``(S0 [H, d, d], z0 [H, d])``: S0 ~ scale * N(0,1) and
+    z0 ~ scale * |N(0,1)| (a key-sum vector is non-negative)."""
+    S0 = scale * torch.randn(H, d, d, generator=_gen(seed, S_INIT_S), dtype=torch.float32)
+    z0 = scale * torch.randn(H, d, generator=_gen(seed, S_INIT_Z), dtype=torch.float32).abs()
+    return S0, z0
 
 
 def cu_from_lengths(lengths) -> torch.Tensor:
