@@ -111,6 +111,57 @@ def cpu_baseline(inp, budget_s):
                       f"{dt:.1f} s; token-heads/s divided by H={H}"}
 
 
+def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc):
+    """The same long-context workload in the bidirectional mode (every token reads its
+    document's whole state; the output kernel is the read-out) and as a continuation
+    (causal, from a synthetic initial state, positions starting at 65536)."""
+    import workloads
+    B, H, L, d = q.shape
+    steps = min(args.steps, 20)
+    S0, z0 = workloads.initial_state(H, d, seed=9, scale=0.1)
+    S0, z0 = S0.to(q.device), z0.to(q.device)
+    modes = {
+        "bidirectional": dict(bidirectional=True),
+        "continuation": dict(initial_S=S0, initial_z=z0, initial_pos=L),
+    }
+    res = {}
+    for name, kw in modes.items():
+        def run(events=None):
+            rla.fwd(q, k, v, gq, gk, seg_chunks=args.seg_chunks, out=out, workspace=ws, events=events, **kw)
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(steps):
+            run()
+        hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        ms = ev.elapsed(0, 1) / steps
+        kev = HipEvents(len(KERNELS) + 1)
+        per = [0.0] * len(KERNELS)
+        for _ in range(steps):
+            run(kev.arr)
+            for i in range(len(KERNELS)):
+                per[i] += kev.elapsed(i, i + 1)
+        per = [x / steps for x in per]
+        t_out = per[KERNELS.index("chunk_out")]
+        if name == "bidirectional":  # read-out: q read and out written once, bf16
+            nbytes = B * H * L * d * 2 * 2
+            kern = "readout"
+        else:
+            nbytes = fwd_algorithmic(B, H, L, d)[1]
+            kern = "chunk_out"
+        gbs = nbytes / (t_out * 1e-3) / 1e9
+        res[name] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3), "steps": steps,
+                     "kernel_ms": dict(zip(KERNELS[:-1] + [kern], per)),
+                     "roofline": {"kernel": kern, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+    res["bidirectional"]["workload"] = "long-context bidirectional forward, B=1 H=32 L=65536 d=128 bf16"
+    res["continuation"]["workload"] = ("long-context causal forward continuing a 65536-token context "
+                                       "(initial state per head, positions 65536..131071)")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +170,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-modes", action="store_true",
+                    help="skip the bidirectional and continuation forwards of the same workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--seg-chunks", type=int, default=0)
@@ -203,6 +256,9 @@ def main():
                      "traffic": measured_traffic("chunk_out_ws_kernel"), "algorithmic_bytes": nbytes},
         "relu_zero_fraction": {"q": zeros_q, "k": zeros_k},
     }
+
+    if not args.no_modes:
+        result["modes"] = time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc)
 
     if not args.no_decode:
         del q, k, v, out, ws

@@ -1378,11 +1378,13 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 // readout (bidirectional forward): per (segment, head), every token reads its document's
 // whole state, out_t = q'_t S_doc / (q'_t . z_doc + eps). The document state arrives in the
 // segment's record (fragment-native S, then z); the state waves round it once to the MFMA
-// operand type and keep it in registers. Per chunk every lane maps q for two tokens into LDS
-// rows and forms q'.z in fp32 against z in LDS (from the rounded q' the MFMA uses); then the
-// state waves form O^T = S^T Q'^T for their value columns, scale each row by 1/(q'.z + eps)
-// and stage the rows in LDS, and all lanes write them out as whole rows (range-checked buffer
-// stores). Raw q and the RoPE row of the next two chunks are in flight in registers.
+// operand type and keep it in registers. Software-pipelined over the chunks with one barrier
+// per step: step c maps q of chunk c + 1 (every lane, two tokens per 8 lanes, with q'.z in
+// fp32 against z in LDS from the rounded q' the MFMA uses) into one half of a double-buffered
+// LDS, the state waves form O^T = S^T Q'^T of chunk c from the other half, scale each row by
+// 1/(q'.z + eps) and stage it, and every lane writes the staged rows of chunk c - 1 as whole
+// rows (range-checked buffer stores). Raw q and the RoPE row of the next two chunks are in
+// flight in registers.
 
 template <bool BF, int D>
 __global__ __launch_bounds__(NT, 2) void readout_kernel(
@@ -1393,12 +1395,13 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
   using G = Geo<BF, D>;
   using St = typename G::St;
   using R = Raw<BF, D>;
+  constexpr int BUF = kChunk * G::ROWP;     // elements of one row buffer
   constexpr int EPP = 16 / G::ES;           // elements per 16-byte piece
   constexpr int PPR = D / EPP;              // 16-byte pieces per row
-  __shared__ __attribute__((aligned(16))) St sQ[kChunk * G::ROWP];
-  __shared__ __attribute__((aligned(16))) St sO[kChunk * G::ROWP];
+  __shared__ __attribute__((aligned(16))) St sQ[2 * BUF];
+  __shared__ __attribute__((aligned(16))) St sO[2 * BUF];
   __shared__ __attribute__((aligned(16))) float sZ[D];
-  __shared__ float sInv[kChunk];
+  __shared__ float sInv[2 * kChunk];
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;  // the whole workgroup leaves together
@@ -1440,62 +1443,66 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
     copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
     load_raw_buf<BF, D>(r, rq, c * kChunk + t0, m);
   };
-  auto step = [&](int c, R& r, float2 (&hi)[G::E]) {
-    {  // ---- map q, q'.z
-      R o;
-      feature_map_lane<BF, D>(r, o, g1, g2, lo, hi, rms_eps);
-      store_rows<BF, D>(sQ, o, t0, m);
+  // q' of chunk c into sQ[c % 2] with its row reciprocals; then the registers load chunk c + 2
+  auto map_chunk = [&](int c, R& r, float2 (&hi)[G::E]) {
+    R o;
+    feature_map_lane<BF, D>(r, o, g1, g2, lo, hi, rms_eps);
+    store_rows<BF, D>(sQ + (c & 1) * BUF, o, t0, m);
 #pragma unroll
-      for (int tok = 0; tok < 2; ++tok) {
-        float p = 0.f;
+    for (int tok = 0; tok < 2; ++tok) {
+      float p = 0.f;
 #pragma unroll
-        for (int e = 0; e < G::E; ++e) {
-          p = __builtin_fmaf(o.get(tok, 0, e), sZ[m * G::E + e], p);
-          p = __builtin_fmaf(o.get(tok, 1, e), sZ[G::HALF + m * G::E + e], p);
-        }
-        p = sum8(p);
-        if (m == 0) sInv[t0 + tok] = 1.0f / (p + eps);
+      for (int e = 0; e < G::E; ++e) {
+        p = __builtin_fmaf(o.get(tok, 0, e), sZ[m * G::E + e], p);
+        p = __builtin_fmaf(o.get(tok, 1, e), sZ[G::HALF + m * G::E + e], p);
       }
+      p = sum8(p);
+      if (m == 0) sInv[(c & 1) * kChunk + t0 + tok] = 1.0f / (p + eps);
     }
-    issue(r, hi, c + 2);  // into the registers just consumed
-    __syncthreads();  // Q' rows and row reciprocals complete
-    if (wave < G::NW) {  // ---- O^T for this wave's value columns, all 64 rows
-      floatx4 o4[G::CT][4];
+    issue(r, hi, c + 2);
+  };
+  // O^T of chunk c for this wave's value columns, all 64 rows, staged in sO[c % 2]
+  auto mma_chunk = [&](int c) {
+    const St* cQ = sQ + (c & 1) * BUF;
+    St* cO = sO + (c & 1) * BUF;
+    floatx4 o4[G::CT][4];
 #pragma unroll
-      for (int ct = 0; ct < G::CT; ++ct)
+    for (int ct = 0; ct < G::CT; ++ct)
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) o4[ct][t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int t4 = 0; t4 < 4; ++t4) o4[ct][t4] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb2 = 0; kb2 < G::KB; ++kb2)
-#pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
-          const Frag<BF> qf = lds_frag<BF>(sQ, G::ROWP, t4 * 16 + c16, kb2, g);
-#pragma unroll
-          for (int ct = 0; ct < G::CT; ++ct) o4[ct][t4] = mma(sa[kb2][ct], qf, o4[ct][t4]);
-        }
+    for (int kb2 = 0; kb2 < G::KB; ++kb2)
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const int t = t4 * 16 + c16;  // this lane's row; columns col .. col + 3
-        const float rr = sInv[t];
+        const Frag<BF> qf = lds_frag<BF>(cQ, G::ROWP, t4 * 16 + c16, kb2, g);
 #pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) {
-          const int col = wave * G::DVW + ct * 16 + 4 * g;
-          if constexpr (BF) {
-            const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o4[ct][t4][0] * rr, o4[ct][t4][1] * rr}, bf16x2));
-            const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o4[ct][t4][2] * rr, o4[ct][t4][3] * rr}, bf16x2));
-            *reinterpret_cast<uint2*>(sO + t * G::ROWP + col) = make_uint2(w0, w1);
-          } else {
-            *reinterpret_cast<float4*>(sO + t * G::ROWP + col) =
-                make_float4(o4[ct][t4][0] * rr, o4[ct][t4][1] * rr, o4[ct][t4][2] * rr, o4[ct][t4][3] * rr);
-          }
+        for (int ct = 0; ct < G::CT; ++ct) o4[ct][t4] = mma(sa[kb2][ct], qf, o4[ct][t4]);
+      }
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int t = t4 * 16 + c16;  // this lane's row; columns col .. col + 3
+      const float rr = sInv[(c & 1) * kChunk + t];
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) {
+        const int col = wave * G::DVW + ct * 16 + 4 * g;
+        if constexpr (BF) {
+          const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o4[ct][t4][0] * rr, o4[ct][t4][1] * rr}, bf16x2));
+          const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o4[ct][t4][2] * rr, o4[ct][t4][3] * rr}, bf16x2));
+          *reinterpret_cast<uint2*>(cO + t * G::ROWP + col) = make_uint2(w0, w1);
+        } else {
+          *reinterpret_cast<float4*>(cO + t * G::ROWP + col) =
+              make_float4(o4[ct][t4][0] * rr, o4[ct][t4][1] * rr, o4[ct][t4][2] * rr, o4[ct][t4][3] * rr);
         }
       }
     }
-    __syncthreads();  // output rows staged
+  };
+  // the staged rows of chunk c (rows past the segment are dropped by the range check)
+  auto store_chunk = [&](int c) {
+    const St* cO = sO + (c & 1) * BUF;
 #pragma unroll
-    for (int i = tid; i < kChunk * PPR; i += NT) {  // rows past the segment are dropped
+    for (int i = tid; i < kChunk * PPR; i += NT) {
       const int rr = i / PPR, pc = i % PPR;
-      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(sO + rr * G::ROWP + pc * EPP), ro,
+      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(cO + rr * G::ROWP + pc * EPP), ro,
                                              ((c * kChunk + rr) * D + pc * EPP) * G::ES, 0, kLoadStream);
     }
   };
@@ -1504,9 +1511,20 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
   issue(set0, hs0, 0);
   issue(set1, hs1, 1);
   __syncthreads();  // z in LDS
-  for (int c = 0; c < nch; c += 2) {
-    step(c, set0, hs0);
-    if (c + 1 < nch) step(c + 1, set1, hs1);  // uniform over the workgroup
+  map_chunk(0, set0, hs0);
+  __syncthreads();
+  // steps s = 0 .. nch: map chunk s + 1, MMA of chunk s, store of chunk s - 1. Every
+  // condition below is uniform over the workgroup, so all waves meet every barrier.
+  for (int c = 0; c <= nch; c += 2) {
+    if (c + 1 < nch) map_chunk(c + 1, set1, hs1);
+    if (c < nch && wave < G::NW) mma_chunk(c);
+    if (c >= 1) store_chunk(c - 1);
+    __syncthreads();
+    if (c + 1 > nch) break;
+    if (c + 2 < nch) map_chunk(c + 2, set0, hs0);
+    if (c + 1 < nch && wave < G::NW) mma_chunk(c + 1);
+    store_chunk(c);
+    __syncthreads();
   }
 }
 
