@@ -183,6 +183,26 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
                                    const float* gamma_k, float* S, float* z, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes rla2_feature_map needs for `desc` (segment table and RoPE tables). */
+rla2_status rla2_feature_map_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
+
+/*
+ * The shared preamble of the layer on its own (RLA page §4.2: Q/K -> RMSNorm ->
+ * RoPE -> ReLU; §3: q' = ReLU(RoPE(RMSNorm(q))), k' likewise), materialised:
+ *  q, k          [B, H, L, d] dtype, read; either may be NULL (then its gamma
+ *                and output are ignored), not both.
+ *  gamma_q/k     [H, d] fp32.
+ *  q_out, k_out  [B, H, L, d] dtype, written with q' and k', rounded once to the
+ *                element type. Bitwise the values the forward forms internally.
+ * Positions follow desc exactly as in the forward (restart at each document
+ * start; the first document of each row starts at desc->initial_pos);
+ * desc->eps, bidirectional and the initial state are validated but unused.
+ * Outputs must not overlap any input, each other or the workspace.
+ */
+rla2_status rla2_feature_map(const rla2_fwd_desc* desc, const void* q, const void* k,
+                             const float* gamma_q, const float* gamma_k, void* q_out, void* k_out,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /*
  * One decode step for N sequences (RLA page §4.2 forward_step): the feature map
  * of the new token at its position, then the state update first

@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
         L.rla2_fwd_chunked_profiled.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
         L.rla2_state_from_prefix.restype = ctypes.c_int
         L.rla2_state_from_prefix.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.rla2_feature_map_workspace_size.restype = ctypes.c_int
+        L.rla2_feature_map_workspace_size.argtypes = [_DESC, _SZ]
+        L.rla2_feature_map.restype = ctypes.c_int
+        L.rla2_feature_map.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.rla2_decode_step.restype = ctypes.c_int
         L.rla2_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                        _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P]
@@ -206,6 +210,39 @@ def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0,
     if st:
         raise Rla2Error(st, "rla2_state_from_prefix")
     return S, z
+
+
+def feature_map(q, k, gamma_q, gamma_k, cu_seqlens=None, *, rms_eps=1e-6, rope_base=10000.0, initial_pos=0,
+                q_out=None, k_out=None, workspace=None):
+    """q' = ReLU(RoPE(RMSNorm(q))) and k' likewise, materialised (either input may be
+    None). Positions as in the forward. Returns ``(q_out, k_out)``."""
+    x = q if q is not None else k
+    if x is None:
+        raise ValueError("q and k are both None")
+    for n_, t, g in (("q", q, gamma_q), ("k", k, gamma_k)):
+        if t is not None:
+            _check_dev(n_, t, x.dtype)
+            _check_dev("gamma_" + n_, g, torch.float32)
+            if t.shape != x.shape:
+                raise ValueError("q and k shapes differ")
+    desc = _fwd_desc(x, cu_seqlens, 64, 0, 1e-4, rms_eps, rope_base, False, initial_pos)
+    if gamma_q is not None and gamma_q.shape != (desc.H, desc.d) or gamma_k is not None and gamma_k.shape != (desc.H, desc.d):
+        raise ValueError("gamma_q and gamma_k must be [H, d]")
+    if q is not None and q_out is None:
+        q_out = torch.empty_like(q)
+    if k is not None and k_out is None:
+        k_out = torch.empty_like(k)
+    n = ctypes.c_size_t(0)
+    st = lib().rla2_feature_map_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st:
+        raise Rla2Error(st, "rla2_feature_map_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=x.device)
+    st = lib().rla2_feature_map(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(gamma_q), _ptr(gamma_k), _ptr(q_out),
+                                _ptr(k_out), _ptr(workspace), workspace.numel(), _stream(x.device))
+    if st:
+        raise Rla2Error(st, "rla2_feature_map")
+    return q_out, k_out
 
 
 def decode_step(q, k, v, positions, gamma_q, gamma_k, S, z, *, eps=1e-4, rms_eps=1e-6, rope_base=10000.0,

@@ -123,6 +123,7 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   p->off_rope_hi = off;
   off = align_up(off + (size_t)(p->n_hi + p->hi_off) * half * 8);
   p->off_states = off;
+  p->bytes_tables = (p->n_docs == 0 || p->H == 0) ? 0 : off;
   off = align_up(off + (size_t)p->n_seg_max * p->H * rec * 4);
   p->bytes = (p->n_docs == 0 || p->H == 0) ? 0 : off;  // no documents or heads: nothing to run
   return RLA2_OK;
@@ -260,6 +261,49 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
                   desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
                   static_cast<char*>(workspace)};
   return finish(rla2::launch_chunked(p, a, stream));
+}
+
+rla2_status rla2_feature_map_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
+  if (bytes == nullptr) return RLA2_ERR_NULL_POINTER;
+  Plan p;
+  rla2_status st = plan_desc(desc, &p);
+  if (st != RLA2_OK) return st;
+  *bytes = p.bytes_tables;
+  return RLA2_OK;
+}
+
+rla2_status rla2_feature_map(const rla2_fwd_desc* desc, const void* q, const void* k, const float* gamma_q,
+                             const float* gamma_k, void* q_out, void* k_out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  rla2_status st = plan_desc(desc, &p);
+  if (st != RLA2_OK) return st;
+  const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
+  const size_t gam = (size_t)p.H * p.d * 4;
+  if (q == nullptr && k == nullptr) return RLA2_ERR_NULL_POINTER;
+  if (act > 0 && q != nullptr && (q_out == nullptr || gamma_q == nullptr)) return RLA2_ERR_NULL_POINTER;
+  if (act > 0 && k != nullptr && (k_out == nullptr || gamma_k == nullptr)) return RLA2_ERR_NULL_POINTER;
+  if (q == nullptr) q_out = nullptr;
+  if (k == nullptr) k_out = nullptr;
+  if (p.packed && desc->cu_seqlens == nullptr) return RLA2_ERR_NULL_POINTER;
+  if (p.bytes_tables > 0 && (workspace == nullptr || workspace_bytes < p.bytes_tables)) return RLA2_ERR_WORKSPACE;
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
+    return RLA2_ERR_WORKSPACE;
+  if (misaligned({q, k, gamma_q, gamma_k, q_out, k_out})) return RLA2_ERR_MISALIGNED;
+  const Range oq{q_out, act}, ok{k_out, act}, ws{workspace, p.bytes_tables};
+  const Range ins[] = {{q, act}, {k, act}, {gamma_q, gam}, {gamma_k, gam},
+                       {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4}};
+  for (const Range& r : ins)
+    if (overlap(oq, r) || overlap(ok, r) || overlap(ws, r)) return RLA2_ERR_ALIAS;
+  if (overlap(oq, ok) || overlap(oq, ws) || overlap(ok, ws)) return RLA2_ERR_ALIAS;
+  if (p.packed && validate_mode() == 1) {
+    st = check_seqlens(p, desc->cu_seqlens, stream);
+    if (st != RLA2_OK) return st;
+  }
+  if (p.n_docs == 0 || p.H == 0 || act == 0) return RLA2_OK;
+  rla2::FwdArgs a{desc->cu_seqlens, q, k, nullptr, gamma_q, gamma_k, nullptr, nullptr, nullptr, nullptr, nullptr,
+                  desc->eps, desc->rms_eps, desc->rope_base, static_cast<char*>(workspace)};
+  return finish(rla2::launch_feature_map(p, a, q_out, k_out, stream));
 }
 
 rla2_status rla2_decode_step(int32_t N, int32_t H, int32_t d, int32_t dtype, const void* q,

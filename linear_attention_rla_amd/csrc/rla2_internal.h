@@ -30,6 +30,7 @@ struct Plan {
   int hi_off;          // 0, or n_hi when the first documents use the offset rows
   size_t off_tab, off_docoff, off_nseg, off_rope_lo, off_rope_hi, off_states;
   size_t bytes;        // total workspace bytes
+  size_t bytes_tables; // bytes up to the state records (what the feature map alone needs)
 };
 
 struct FwdArgs {
@@ -47,6 +48,9 @@ struct FwdArgs {
 // `ev` (optional) gets kNumFwdKernels + 1 events recorded around the kernels.
 constexpr int kNumFwdKernels = 4;
 hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
+
+// The feature map alone: prep, then q' and k' (either input may be null).
+hipError_t launch_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void* k_out, hipStream_t s);
 
 hipError_t launch_decode(int N, int H, int d, int dtype, const void* q, const void* k,
                          const void* v, const int32_t* pos, const float* gq, const float* gk,

@@ -1529,6 +1529,89 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
 }
 
 // ----------------------------------------------------------------------------------------
+// feature_map: the preamble alone, x' = ReLU(RoPE(RMSNorm(x))) materialised. Per (segment,
+// head, tensor): the same lane mapping and device functions as the chunk kernels (two
+// tokens per 8 lanes), so x' is bitwise what the forward forms internally; raw x and the
+// RoPE row of the next two chunks in flight in registers; each lane writes its elements back
+// with range-checked buffer stores (tokens past the segment are dropped).
+
+template <bool BF, int D>
+__device__ __forceinline__ void store_raw_buf(const Raw<BF, D>& r, __amdgpu_buffer_rsrc_t rs, int tok, int m) {
+  using G = Geo<BF, D>;
+  constexpr int NB = G::E * G::ES;  // bytes per (token, half) of this lane
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int off = ((tok + t) * D + hh * G::HALF + m * G::E) * G::ES;
+      if constexpr (NB >= 16) {
+#pragma unroll
+        for (int p = 0; p < NB / 16; ++p)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{r.w[t][hh][4 * p], r.w[t][hh][4 * p + 1], r.w[t][hh][4 * p + 2], r.w[t][hh][4 * p + 3]}, rs,
+              off + 16 * p, 0, kLoadStream);
+      } else if constexpr (NB == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{r.w[t][hh][0], r.w[t][hh][1]}, rs, off, 0, kLoadStream);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(r.w[t][hh][0], rs, off, 0, kLoadStream);
+      }
+    }
+}
+
+template <bool BF, int D>
+__global__ __launch_bounds__(NT, 2) void feature_map_kernel(
+    const typename Elem<BF>::St* __restrict__ q, const typename Elem<BF>::St* __restrict__ k,
+    const float* __restrict__ gamma_q, const float* __restrict__ gamma_k, const int32_t* __restrict__ tab,
+    const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
+    typename Elem<BF>::St* __restrict__ q_out, typename Elem<BF>::St* __restrict__ k_out, int H, int L,
+    float rms_eps) {
+  using G = Geo<BF, D>;
+  using R = Raw<BF, D>;
+  const int seg = blockIdx.x, h = blockIdx.y;
+  const auto* x = blockIdx.z == 0 ? q : k;
+  auto* y = blockIdx.z == 0 ? q_out : k_out;
+  const float* gamma = blockIdx.z == 0 ? gamma_q : gamma_k;
+  if (seg >= *nseg || x == nullptr) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x;
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
+  const int t0 = 2 * (tid >> 3), m = tid & 7;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * G::ES;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + tok0 * D), 0, seg_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc((void*)(y + tok0 * D), 0, seg_bytes, kBufFlags);
+  float g1[G::E], g2[G::E];
+  float2 lo[2][G::E];
+#pragma unroll
+  for (int e = 0; e < G::E; ++e) {
+    const int j = m * G::E + e;
+    g1[e] = gamma[(size_t)h * D + j];
+    g2[e] = gamma[(size_t)h * D + j + G::HALF];
+    lo[0][e] = rope_lo[t0 * G::HALF + j];
+    lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
+  }
+  const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * G::E;
+  auto issue = [&](R& r, float2 (&hi)[G::E], int c) {
+    copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
+    load_raw_buf<BF, D>(r, rx, c * kChunk + t0, m);
+  };
+  auto step = [&](int c, R& r, float2 (&hi)[G::E]) {
+    R o;
+    feature_map_lane<BF, D>(r, o, g1, g2, lo, hi, rms_eps);
+    store_raw_buf<BF, D>(o, ry, c * kChunk + t0, m);
+    issue(r, hi, c + 2);
+  };
+  R set0, set1;
+  float2 hs0[G::E], hs1[G::E];
+  issue(set0, hs0, 0);
+  issue(set1, hs1, 1);
+  for (int c = 0; c < nch; c += 2) {
+    step(c, set0, hs0);
+    if (c + 1 < nch) step(c + 1, set1, hs1);
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // decode: one workgroup per (sequence, head). Every global load is issued first (the fp32
 // state rows of each thread, then z, v and the new token's q, k), so the state traffic is in
 // flight while wave 0 maps q and wave 1 maps k (lane j holds the RoPE pair j, j + D/2; the
@@ -1703,6 +1786,27 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
 }
 
 template <bool BF, int D>
+hipError_t run_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void* k_out, hipStream_t s) {
+  using St = typename Elem<BF>::St;
+  int32_t* tab = reinterpret_cast<int32_t*>(a.ws + p.off_tab);
+  int32_t* docoff = reinterpret_cast<int32_t*>(a.ws + p.off_docoff);
+  int32_t* nseg = reinterpret_cast<int32_t*>(a.ws + p.off_nseg);
+  float2* rlo = reinterpret_cast<float2*>(a.ws + p.off_rope_lo);
+  float2* rhi = reinterpret_cast<float2*>(a.ws + p.off_rope_hi);
+  const int half = D / 2;
+  const int rope_entries = (kChunk + p.n_hi + p.hi_off) * half;
+  hipLaunchKernelGGL(prep_kernel, dim3(1 + (rope_entries + 1023) / 1024), dim3(1024), 0, s, a.cu, p.n_docs, p.L,
+                     p.seg_len, p.n_seg_max, tab, docoff, nseg, rlo, rhi, half, D, p.n_hi, p.hi_off, p.initial_pos,
+                     a.rope_base);
+  if (p.n_seg_max > 0) {
+    hipLaunchKernelGGL((feature_map_kernel<BF, D>), dim3(p.n_seg_max, p.H, 2), dim3(NT), 0, s,
+                       static_cast<const St*>(a.q), static_cast<const St*>(a.k), a.gq, a.gk, tab, nseg, rlo, rhi,
+                       static_cast<St*>(q_out), static_cast<St*>(k_out), p.H, p.L, a.rms_eps);
+  }
+  return hipGetLastError();
+}
+
+template <bool BF, int D>
 hipError_t run_decode(int N, int H, const void* q, const void* k, const void* v, const int32_t* pos,
                       const float* gq, const float* gk, float rms_eps, float rope_base, float eps, float* S,
                       float* z, void* out, hipStream_t s) {
@@ -1723,6 +1827,16 @@ hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEve
     case 32: return bf ? run_chunked<true, 32>(p, a, s, ev) : run_chunked<false, 32>(p, a, s, ev);
     case 64: return bf ? run_chunked<true, 64>(p, a, s, ev) : run_chunked<false, 64>(p, a, s, ev);
     case 128: return bf ? run_chunked<true, 128>(p, a, s, ev) : run_chunked<false, 128>(p, a, s, ev);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void* k_out, hipStream_t s) {
+  const bool bf = p.dtype == 1;
+  switch (p.d) {
+    case 32: return bf ? run_feature_map<true, 32>(p, a, q_out, k_out, s) : run_feature_map<false, 32>(p, a, q_out, k_out, s);
+    case 64: return bf ? run_feature_map<true, 64>(p, a, q_out, k_out, s) : run_feature_map<false, 64>(p, a, q_out, k_out, s);
+    case 128: return bf ? run_feature_map<true, 128>(p, a, q_out, k_out, s) : run_feature_map<false, 128>(p, a, q_out, k_out, s);
   }
   return hipErrorInvalidValue;
 }

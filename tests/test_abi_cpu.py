@@ -183,3 +183,29 @@ def test_binding_refuses_cpu_tensors():
         rla.fwd(x, x, x, g, g)
     with pytest.raises(ValueError, match="GPU tensor"):
         rla.decode_step(x[0], x[0], x[0], torch.zeros(1, dtype=torch.int32), g, g, x, x[0, 0])
+
+
+def test_feature_map_error_paths():
+    L = rla.lib()
+
+    def call(d=None, q=A, k=A + 64 * MB, gq=A + 192 * MB, gk=A + 193 * MB, qo=A + 256 * MB, ko=A + 320 * MB,
+             ws=A + 512 * MB, ws_bytes=1 << 30):
+        d = d or desc()
+        return L.rla2_feature_map(ctypes.byref(d), q, k, gq, gk, qo, ko, ws, ws_bytes, None)
+
+    n = ctypes.c_size_t(0)
+    assert L.rla2_feature_map_workspace_size(ctypes.byref(desc()), ctypes.byref(n)) == OK
+    full = ctypes.c_size_t(0)
+    assert L.rla2_fwd_workspace_size(ctypes.byref(desc()), ctypes.byref(full)) == OK
+    assert 0 < n.value < full.value                       # no state records needed
+    assert L.rla2_feature_map_workspace_size(ctypes.byref(desc(d=48)), ctypes.byref(n)) == UNSUP
+    assert call(q=None, k=None) == NULLP
+    assert call(qo=None) == NULLP
+    assert call(gk=None) == NULLP
+    assert call(ws=None) == WS
+    assert call(ws_bytes=16) == WS
+    assert call(q=A + 8) == MISAL
+    assert call(qo=A + 64 * MB) == ALIAS                  # q' over k
+    assert call(ko=A + 256 * MB) == ALIAS                 # k' over q'
+    assert call(ko=A + 512 * MB) == ALIAS                 # k' over the workspace
+    assert call(d=desc(rms_eps=0.0)) == VALUE

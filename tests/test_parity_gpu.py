@@ -368,3 +368,58 @@ def test_bidirectional_c3_size_sampled():
         worst = max(worst, row_rel_err(out[0, h, rows], ref))
     print(f"bidirectional packed T={T}: max row rel err {worst:.3e}")
     assert worst <= TOL_BF16
+
+
+# --- the feature map alone (RMSNorm -> RoPE -> ReLU, materialised) ------------------------
+
+def _check_feature_map(got, x, gamma, pos, dtype):
+    """got vs the oracle's fp64 feature map: within one bf16 ulp (fp32: the row tolerance);
+    a zero of the oracle is a zero on the GPU unless its pre-activation is tiny."""
+    ref = oracle.feature_map(x, gamma, pos)
+    pre = oracle.rope_rotate_half(oracle.rms_norm(x, gamma), pos)
+    g = f64(got)
+    if dtype == torch.float32:
+        assert row_rel_err(g, ref) <= TOL_F32
+    else:
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+        bad = np.abs(g - ref) > ulp
+        assert not bad.any(), f"{bad.sum()} elements beyond one bf16 ulp"
+    stray = (ref == 0) & (g != 0) & (np.abs(pre) > 1e-5 * np.abs(pre).max(axis=-1, keepdims=True))
+    assert not stray.any()
+    return float((g == 0).mean())
+
+
+@pytest.mark.parametrize("B,H,L,d,dtype,lengths,pos", [
+    (2, 3, 300, 64, torch.bfloat16, None, 0), (2, 3, 300, 64, torch.bfloat16, None, 70000),
+    (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], 37), (1, 2, 190, 32, torch.float32, None, 5),
+    (1, 1, 129, 128, torch.float32, [64, 65], 0)])
+def test_feature_map_small(B, H, L, d, dtype, lengths, pos):
+    inp = workloads.fwd_inputs(B, H, L, d, dtype, seed=500 + L + d, lengths=lengths)
+    q, k, v, gq, gk, cu = on_gpu(inp)
+    qo, ko = rla.feature_map(q, k, gq, gk, cu, initial_pos=pos)
+    only_k = rla.feature_map(None, k, None, gk, cu, initial_pos=pos)[1]
+    torch.cuda.synchronize()
+    assert torch.equal(only_k, ko)
+    docs = oracle.documents(B, L, None if lengths is None else inp.cu_seqlens.numpy())
+    first = oracle.first_documents(B, L, None if lengths is None else inp.cu_seqlens.numpy())
+    for j, (b, s0, s1) in enumerate(docs):
+        if s1 == s0:
+            continue
+        p = (pos if j in first else 0) + np.arange(s1 - s0)
+        for h in range(H):
+            _check_feature_map(qo[b, h, s0:s1], f64(inp.q[b, h, s0:s1]), f64(inp.gamma_q[h]), p, dtype)
+            _check_feature_map(ko[b, h, s0:s1], f64(inp.k[b, h, s0:s1]), f64(inp.gamma_k[h]), p, dtype)
+
+
+def test_feature_map_c4_size_sampled():
+    # the long-context workload (sparse supports: 13 of 128 channels shifted by -1), sampled rows
+    inp = workloads.c4_long()
+    q, k, gq, gk = inp.q.to(DEV), inp.k.to(DEV), inp.gamma_q.to(DEV), inp.gamma_k.to(DEV)
+    qo, ko = rla.feature_map(q, k, gq, gk)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp.q.shape[2], 200, seed=9)
+    zq = []
+    for h in (0, 13, 31):
+        zq.append(_check_feature_map(qo[0, h, rows], f64(inp.q[0, h, rows]), f64(inp.gamma_q[h]), rows, torch.bfloat16))
+        _check_feature_map(ko[0, h, rows], f64(inp.k[0, h, rows]), f64(inp.gamma_k[h]), rows, torch.bfloat16)
+    print(f"long-context feature map: fraction of exact zeros in q' {np.mean(zq):.3f}")
