@@ -8,3 +8,4 @@ from .rla2_oracle import (  # noqa: F401
     rms_norm, rope_frequencies, rope_rotate_half, feature_map, documents, first_documents,
     fwd, fwd_rows, fwd_recurrent, state_from_prefix, decode_step, decode_direct,
 )
+from .rla2_backward import fwd_torch, bwd, bwd_qk_prime, feature_map_torch  # noqa: F401,E402

@@ -1,0 +1,100 @@
+"""CPU oracle of the RLA-2 causal backward (fp64, plain PyTorch CPU ops + autograd).
+
+TEST INFRASTRUCTURE ONLY, like ``rla2_oracle``: only the tests, ``smoke()`` and the
+bench's ``cpu_baseline`` leg may use it; it shares no code with the HIP path.
+
+``fwd_torch`` writes the causal closed form out directly (RLA page §3 formula with
+the Sum denominator of §2.3; the preamble q' = ReLU(RoPE(RMSNorm(q))) of §1/§3; the
+causal, same-document key range of §4.1), and ``bwd`` differentiates it with
+autograd: the gradients of ``sum(out * dout)`` with respect to q, k, v and the two
+RMSNorm weights. ``bwd_qk_prime`` restates the layer backward the RLA page gives in
+§4.2 (gnum = g / (q.z + eps), scale = -r / (q.z + eps)^2 with r = g . num,
+gQ = B^T gnum + scale * z, and the suffix sums for the key and value gradients) for
+the gradients with respect to q' and k' and v, as an independent formulation that the
+pins compare against autograd. The ReLU gate is q' > 0 (RLA page §4.2: select(Qp > 0)).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from .rla2_oracle import DEFAULT_EPS, DEFAULT_RMS_EPS, DEFAULT_ROPE_BASE, documents, rope_frequencies
+
+
+def _t(x) -> torch.Tensor:
+    if isinstance(x, torch.Tensor):
+        return x.detach().to("cpu", torch.float64)
+    return torch.as_tensor(np.asarray(x, dtype=np.float64))
+
+
+def feature_map_torch(x, gamma, positions, rms_eps=DEFAULT_RMS_EPS, base=DEFAULT_ROPE_BASE):
+    """x' = ReLU(RoPE(RMSNorm(x))) in torch fp64 (differentiable); ``x [n, d]``."""
+    d = x.shape[-1]
+    h = d // 2
+    y = x * gamma / torch.sqrt((x * x).mean(dim=-1, keepdim=True) + rms_eps)
+    theta = torch.as_tensor(rope_frequencies(d, base))
+    phi = torch.as_tensor(np.asarray(positions, dtype=np.float64))[:, None] * theta[None, :]
+    c, s = torch.cos(phi), torch.sin(phi)
+    y1, y2 = y[:, :h], y[:, h:]
+    u = torch.cat([y1 * c - y2 * s, y2 * c + y1 * s], dim=-1)
+    return torch.relu(u)
+
+
+def attention_torch(qp, kp, v, eps=DEFAULT_EPS):
+    """Causal closed form for one document: out_t = sum_{i<=t} s_ti v_i / (sum_{i<=t} s_ti + eps)."""
+    n = qp.shape[0]
+    s = qp @ kp.T
+    s = torch.where(torch.tril(torch.ones(n, n, dtype=torch.bool)), s, torch.zeros_like(s))
+    return (s @ v) / (s.sum(dim=1, keepdim=True) + eps)
+
+
+def fwd_torch(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
+              rope_base=DEFAULT_ROPE_BASE):
+    """Differentiable closed-form causal forward over [B, H, L, d] (torch fp64 tensors)."""
+    B, H, L, d = q.shape
+    out = torch.zeros(B, H, L, d, dtype=torch.float64)
+    for (b, s0, s1) in documents(B, L, cu_seqlens):
+        if s1 <= s0:
+            continue
+        pos = np.arange(s1 - s0)
+        for h in range(H):
+            qp = feature_map_torch(q[b, h, s0:s1], gamma_q[h], pos, rms_eps, rope_base)
+            kp = feature_map_torch(k[b, h, s0:s1], gamma_k[h], pos, rms_eps, rope_base)
+            out[b, h, s0:s1] = attention_torch(qp, kp, v[b, h, s0:s1], eps)
+    return out
+
+
+def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
+        rope_base=DEFAULT_ROPE_BASE):
+    """Gradients (dq, dk, dv, dgamma_q, dgamma_k) of sum(out * dout), fp64 numpy arrays."""
+    leaves = [_t(x).requires_grad_(True) for x in (q, k, v, gamma_q, gamma_k)]
+    out = fwd_torch(*leaves, cu_seqlens, eps, rms_eps, rope_base)
+    grads = torch.autograd.grad((out * _t(dout)).sum(), leaves, allow_unused=True)
+    return tuple(np.zeros(tuple(x.shape)) if g is None else g.numpy() for g, x in zip(grads, leaves))
+
+
+def bwd_qk_prime(qp, kp, v, g, eps=DEFAULT_EPS):
+    """The RLA page §4.2 backward for one document, from q', k' (fp64 numpy, [n, d]):
+    states S_t = sum_{i<=t} k'_i v_i^T, z_t = sum_{i<=t} k'_i, num_t = S_t^T q'_t,
+    gnum_t = g_t / (q'_t . z_t + eps), scale_t = -(g_t . num_t) / (q'_t . z_t + eps)^2;
+    dq'_t = S_t gnum_t + scale_t z_t; with the suffix sums P_i = sum_{t>=i} q'_t gnum_t^T
+    and p_i = sum_{t>=i} scale_t q'_t: dk'_i = P_i v_i + p_i, dv_i = P_i^T k'_i."""
+    n, d = qp.shape
+    dqp, dkp, dv = np.zeros((n, d)), np.zeros((n, d)), np.zeros((n, d))
+    S, z = np.zeros((d, d)), np.zeros(d)
+    gnum, scale = np.zeros((n, d)), np.zeros(n)
+    for t in range(n):                                   # forward recursion
+        S += np.outer(kp[t], v[t])
+        z += kp[t]
+        den = qp[t] @ z + eps
+        num = S.T @ qp[t]
+        gnum[t] = g[t] / den
+        scale[t] = -(g[t] @ num) / den ** 2
+        dqp[t] = S @ gnum[t] + scale[t] * z
+    P, p = np.zeros((d, d)), np.zeros(d)
+    for i in range(n - 1, -1, -1):                       # suffix (reverse) recursion
+        P += np.outer(qp[i], gnum[i])
+        p += scale[i] * qp[i]
+        dkp[i] = P @ v[i] + p
+        dv[i] = P.T @ kp[i]
+    return dqp, dkp, dv

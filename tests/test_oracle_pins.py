@@ -368,3 +368,54 @@ def test_bidirectional_mode():
     v2[0, :, 20] += 5.0
     assert not np.allclose(oracle.fwd(q, k, v2, gq, gk, cu, causal=False)[0, :, 8],
                            oracle.fwd(q, k, v, gq, gk, cu, causal=False)[0, :, 8])
+
+
+# --- the backward oracle (RLA page §4.2 backward) ---------------------------------
+
+def test_backward_matches_finite_differences():
+    # autograd of the closed form against central finite differences of the same forward
+    # (torch.autograd.gradcheck), on a tiny packed case with two documents
+    r = np.random.default_rng(51)
+    B, H, L, d = 1, 1, 7, 4
+    cu = np.array([0, 3, 7])
+    args = [torch.tensor(r.normal(size=(B, H, L, d)), requires_grad=True) for _ in range(3)]
+    args += [torch.tensor(r.uniform(0.5, 1.5, size=(H, d)), requires_grad=True) for _ in range(2)]
+    assert torch.autograd.gradcheck(lambda *a: oracle.fwd_torch(*a, cu), args, eps=1e-6, atol=1e-8, rtol=1e-6)
+
+
+def test_backward_matches_page_formulas():
+    # dq', dk', dv from the page's own backward recursions (gnum, scale, suffix sums)
+    # equal autograd's gradients with respect to q', k', v of the attention part
+    r = np.random.default_rng(52)
+    n, d = 13, 6
+    qp, kp = np.abs(r.normal(size=(n, d))), np.maximum(r.normal(size=(n, d)), 0)
+    v, g = r.normal(size=(n, d)), r.normal(size=(n, d))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (qp, kp, v))
+    out = oracle.rla2_backward.attention_torch(tq, tk, tv)
+    gq, gk, gv = torch.autograd.grad((out * torch.tensor(g)).sum(), (tq, tk, tv))
+    dqp, dkp, dv = oracle.bwd_qk_prime(qp, kp, v, g)
+    np.testing.assert_allclose(dqp, gq.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dkp, gk.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, gv.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_backward_value_gradient_closed_form_and_isolation():
+    # out is linear in v: dv_i = sum_{t>=i} s_ti / den_t * g_t (same document); and a
+    # cotangent on one document changes no gradient of another document's tokens
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 20, 8, 53, [8, 12])
+    r = np.random.default_rng(54)
+    g = r.normal(size=q.shape)
+    dq, dk, dv, dgq, dgk = oracle.bwd(q, k, v, gq, gk, g, cu)
+    for (b, s0, s1) in oracle.documents(1, 20, cu):
+        for h in range(2):
+            pos = np.arange(s1 - s0)
+            qp = oracle.feature_map(q[b, h, s0:s1], gq[h], pos)
+            kp = oracle.feature_map(k[b, h, s0:s1], gk[h], pos)
+            s = np.tril(qp @ kp.T)
+            a = s / (s.sum(axis=1, keepdims=True) + oracle.DEFAULT_EPS)
+            np.testing.assert_allclose(dv[b, h, s0:s1], a.T @ g[b, h, s0:s1], rtol=1e-11, atol=1e-13)
+    g2 = g.copy()
+    g2[:, :, 8:] += r.normal(size=g2[:, :, 8:].shape)
+    dq2, dk2, dv2, _, _ = oracle.bwd(q, k, v, gq, gk, g2, cu)
+    for a, b2 in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        np.testing.assert_array_equal(a[:, :, :8], b2[:, :, :8])
