@@ -18,7 +18,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from .rla2_oracle import DEFAULT_EPS, DEFAULT_RMS_EPS, DEFAULT_ROPE_BASE, documents, rope_frequencies
+from .rla2_oracle import (DEFAULT_EPS, DEFAULT_RMS_EPS, DEFAULT_ROPE_BASE, _initial, documents, first_documents,
+                          rope_frequencies)
 
 
 def _t(x) -> torch.Tensor:
@@ -40,35 +41,49 @@ def feature_map_torch(x, gamma, positions, rms_eps=DEFAULT_RMS_EPS, base=DEFAULT
     return torch.relu(u)
 
 
-def attention_torch(qp, kp, v, eps=DEFAULT_EPS):
-    """Causal closed form for one document: out_t = sum_{i<=t} s_ti v_i / (sum_{i<=t} s_ti + eps)."""
+def attention_torch(qp, kp, v, eps=DEFAULT_EPS, S0=None, z0=None):
+    """Causal closed form for one document: out_t = sum_{i<=t} s_ti v_i / (sum_{i<=t} s_ti + eps),
+    with an initial state (S0 [d, d], z0 [d]) adding q'_t S0 to the numerator and q'_t . z0 to
+    the denominator (the scan's starting value, RLA page §4.1)."""
     n = qp.shape[0]
     s = qp @ kp.T
     s = torch.where(torch.tril(torch.ones(n, n, dtype=torch.bool)), s, torch.zeros_like(s))
-    return (s @ v) / (s.sum(dim=1, keepdim=True) + eps)
+    num, den = s @ v, s.sum(dim=1, keepdim=True) + eps
+    if S0 is not None:
+        num = num + qp @ S0
+        den = den + (qp @ z0)[:, None]
+    return num / den
 
 
 def fwd_torch(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
-              rope_base=DEFAULT_ROPE_BASE):
-    """Differentiable closed-form causal forward over [B, H, L, d] (torch fp64 tensors)."""
+              rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0):
+    """Differentiable closed-form causal forward over [B, H, L, d] (torch fp64 tensors).
+    The first document of each row starts at position ``initial_pos`` and from the
+    initial state (constants here: no gradient flows to them), as the forward oracle."""
     B, H, L, d = q.shape
     out = torch.zeros(B, H, L, d, dtype=torch.float64)
-    for (b, s0, s1) in documents(B, L, cu_seqlens):
+    first = first_documents(B, L, cu_seqlens)
+    with_init = initial_S is not None or initial_z is not None
+    S0, z0 = (torch.as_tensor(x) for x in _initial(initial_S, initial_z, H, d))
+    for j, (b, s0, s1) in enumerate(documents(B, L, cu_seqlens)):
         if s1 <= s0:
             continue
-        pos = np.arange(s1 - s0)
+        start = initial_pos if j in first else 0
+        pos = start + np.arange(s1 - s0)
+        init = with_init and j in first
         for h in range(H):
             qp = feature_map_torch(q[b, h, s0:s1], gamma_q[h], pos, rms_eps, rope_base)
             kp = feature_map_torch(k[b, h, s0:s1], gamma_k[h], pos, rms_eps, rope_base)
-            out[b, h, s0:s1] = attention_torch(qp, kp, v[b, h, s0:s1], eps)
+            out[b, h, s0:s1] = attention_torch(qp, kp, v[b, h, s0:s1], eps, S0[h] if init else None,
+                                               z0[h] if init else None)
     return out
 
 
 def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
-        rope_base=DEFAULT_ROPE_BASE):
+        rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0):
     """Gradients (dq, dk, dv, dgamma_q, dgamma_k) of sum(out * dout), fp64 numpy arrays."""
     leaves = [_t(x).requires_grad_(True) for x in (q, k, v, gamma_q, gamma_k)]
-    out = fwd_torch(*leaves, cu_seqlens, eps, rms_eps, rope_base)
+    out = fwd_torch(*leaves, cu_seqlens, eps, rms_eps, rope_base, initial_S, initial_z, initial_pos)
     grads = torch.autograd.grad((out * _t(dout)).sum(), leaves, allow_unused=True)
     return tuple(np.zeros(tuple(x.shape)) if g is None else g.numpy() for g, x in zip(grads, leaves))
 

@@ -419,3 +419,31 @@ def test_backward_value_gradient_closed_form_and_isolation():
     dq2, dk2, dv2, _, _ = oracle.bwd(q, k, v, gq, gk, g2, cu)
     for a, b2 in ((dq, dq2), (dk, dk2), (dv, dv2)):
         np.testing.assert_array_equal(a[:, :, :8], b2[:, :, :8])
+
+
+def test_backward_initial_state_is_a_continuation():
+    # The gradient with respect to the tokens of X, of a loss on X's outputs only, is the
+    # same whether X follows its prefix P in one sequence (no initial state, positions
+    # from 0) or runs from the prefix's summary state (S_P, z_P) at position offset |P|
+    # (RLA page §4.1 scan inputs A0/B0): the forward of X is the same function of X's
+    # tokens in both. The first checks the initial-state terms of the closed form (q' S0
+    # in the numerator, q' . z0 in the denominator) and the shifted RoPE positions.
+    r = np.random.default_rng(55)
+    H, d, nP, nX = 2, 8, 9, 7
+    q, k, v, gq, gk, _ = _rand_case(1, H, nP + nX, d, 56, None)
+    g = r.normal(size=q.shape)
+    g[:, :, :nP] = 0.0
+    whole = oracle.bwd(q, k, v, gq, gk, g)
+    S, z = oracle.state_from_prefix(k[:, :, :nP], v[:, :, :nP], gk)
+    X = (slice(None), slice(None), slice(nP, None))
+    cont = oracle.bwd(q[X], k[X], v[X], gq, gk, g[X], initial_S=S[0], initial_z=z[0], initial_pos=nP)
+    for a, b2 in zip(whole[:3], cont[:3]):
+        np.testing.assert_allclose(a[X], b2, rtol=1e-10, atol=1e-12)
+    # the forward of the differentiable oracle with an initial state equals the forward oracle
+    S0, z0 = workloads.initial_state(H, d, seed=57)
+    S0, z0 = S0.double().numpy(), z0.double().numpy()
+    cu = np.array([0, 5, 16])
+    out = oracle.fwd_torch(*(torch.tensor(x) for x in (q, k, v, gq, gk)), cu, initial_S=S0, initial_z=z0,
+                           initial_pos=40)
+    ref = oracle.fwd(q, k, v, gq, gk, cu, initial_S=S0, initial_z=z0, initial_pos=40)
+    np.testing.assert_allclose(out.numpy(), ref, rtol=1e-11, atol=1e-13)
