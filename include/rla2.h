@@ -183,6 +183,33 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
                                    const float* gamma_k, float* S, float* z, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace bytes rla2_bwd_chunked needs for `desc`. */
+rla2_status rla2_bwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
+
+/*
+ * Chunked backward of the causal forward (RLA page §4.2 backward of the layer): with
+ * g = dL/dout, gnum_t = g_t / (q'_t . z_t + eps), scale_t = -(g_t . num_t) / (q'_t . z_t +
+ * eps)^2, dq'_t = S_t gnum_t + scale_t z_t and, with the suffix sums P_i = sum_{t >= i}
+ * q'_t gnum_t^T and p_i = sum_{t >= i} scale_t q'_t (same document), dk'_i = P_i v_i + p_i,
+ * dv_i = P_i^T k'_i; then through the ReLU (gate q' > 0), RoPE and RMSNorm to dq, dk and
+ * the RMSNorm weights. The forward's states and g . num are recomputed from q, k, v (the
+ * forward output is not an input). bf16 activations only (RLA2_ERR_UNSUPPORTED otherwise),
+ * causal only (desc->bidirectional must be 0). An initial state and position offset in
+ * desc are taken into account; the gradient with respect to the initial state is not formed.
+ *  q, k, v       [B, H, L, d] bf16, the forward's inputs.
+ *  gamma_q/k     [H, d] fp32.
+ *  dout          [B, H, L, d] bf16, dL/dout (read).
+ *  dq, dk, dv    [B, H, L, d] bf16, written.
+ *  dgamma_q/k    optional [H, d] fp32, written (NULL = not formed).
+ *  workspace     at least rla2_bwd_workspace_size() bytes, 256-byte aligned.
+ * Outputs must not overlap any input, each other or the workspace (RLA2_ERR_ALIAS).
+ */
+rla2_status rla2_bwd_chunked(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v,
+                             const float* gamma_q, const float* gamma_k, const void* dout,
+                             void* dq, void* dk, void* dv, float* dgamma_q,
+                             float* dgamma_k, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* Workspace bytes rla2_feature_map needs for `desc` (segment table and RoPE tables). */
 rla2_status rla2_feature_map_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
 

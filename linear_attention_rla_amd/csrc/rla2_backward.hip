@@ -1,0 +1,929 @@
+// HIP kernels of the RLA-2 causal backward on gfx950 (bf16 activations, fp32 states).
+//
+// Method: neuralnet.cpp development page "线性注意力家族：RLA / RAPT / RLA-2 与 GPU 落地"
+// (the RLA page), §4.2 backward of the layer. With g_t = dL/dout_t, den_t = q'_t . z_t + eps,
+// num_t = S_t^T q'_t and the page's gnum_t = g_t / den_t, scale_t = gd_t = -(g_t . num_t) / den_t^2:
+//   dq'_t = S_t gnum_t + gd_t z_t                                  (forward states S_t, z_t)
+//   dk'_i = P_i v_i + p_i,   dv_i = P_i^T k'_i                     (reverse states, same document)
+//   P_i = sum_{t >= i} q'_t gnum_t^T = sum_{t >= i} (q'_t / den_t) g_t^T
+//   p_i = sum_{t >= i} gd_t q'_t     = sum_{t >= i} (q'_t / den_t) (gd_t den_t)
+// then through the ReLU (gate q' > 0), the inverse RoPE rotation and the RMSNorm backward
+// to dq, dk and the RMSNorm weight gradients; dv needs no map.
+//
+// Numerics. g_t . num_t is formed in fp32 from the states and the chunk's scores (no rounded
+// forward output is read). The weight of a query on its own key, B_tt = g_t . v_t / den_t +
+// gd_t, is formed as (g_t . v_t (den_t - s_tt) - (g_t . num_t - s_tt g_t . v_t)) / den_t^2
+// with both brackets summed without the self term, so a token that sees only itself (the
+// first token of a document without an initial state, den - s_tt = eps) keeps its eps-sized
+// gradient instead of the rounding noise of two cancelling O(1) terms. The running states
+// enter the MFMA as a pair of bf16 operands (the rounded value and the rounded remainder);
+// the reverse states are built from Q^ = bf16(q'/den) against the exact bf16 g and the fp32
+// gd den, so P v_i and p_i share one rounding of each query.
+//
+// Chunked like the forward (C = 64 tokens, documents cut into segments of whole chunks):
+//   (forward state pass)  prefix records of S, z per (segment, head)
+//   bwd_dq       per (segment, head), chunks in order, S and z running:
+//                  A^T = mask(K' Q'^T), Bv^T = V G^T (keys x queries), den, g . num, gd, B_tt
+//                  dQ'^T = (S G^T) / den + z gd^T + K'^T B^T,  B^T = mask(Bv^T / den + gd) (B_tt on
+//                  the diagonal); the map backward of q; den, gd and B_tt per token to memory
+//   bwd_pstate   per (segment, head): sums of Q^^T G and Q^^T (gd den) over the segment
+//   (suffix scan) exclusive sums over the later segments of each document
+//   bwd_dkv      per (segment, head), chunks in reverse order, P and p running:
+//                  A = mask(Q' K'^T), B = mask(G V^T / den + gd) (queries x keys, B_tt on the diagonal)
+//                  dK'^T = P V^T + Q'^T B + p 1^T,  dV^T = P^T K'^T + G^T (A / den)
+//                then the map backward of k
+//   bwd_dgamma   sums the per-segment RMSNorm-weight partials
+// Operand layout conventions are those of rla2_device.h; running states live in MFMA
+// accumulators (value columns split over the waves) and as a transposed bf16 pair in LDS,
+// from which both contraction orders are read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rla2_device.h"
+#include "rla2_internal.h"
+
+namespace rla2 {
+namespace {
+
+// bf16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2));
+}
+// the two bf16 halves of a packed word as floats
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Write the running state (accumulator tiles of this wave's value columns) as its transpose,
+// row-major [c][a] with pitch D + 8, rounded to bf16 into `hi` and the remainder, rounded,
+// into `lo`: lane (c16, g) of tile (rt, ct) holds X[16 rt + 4g + i][col] for i < 4, i.e. four
+// consecutive entries of row `col` of X^T.
+template <int D>
+__device__ __forceinline__ void put_state_tr(uint16_t* hi, uint16_t* lo,
+                                             const floatx4 (&X)[Geo<true, D>::RT][Geo<true, D>::CT], int wave,
+                                             int lane) {
+  using G = Geo<true, D>;
+  constexpr int SP = D + 8;
+  const int c16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+      const int off = (wave * G::DVW + ct * 16 + c16) * SP + 16 * rt + 4 * g;
+      const floatx4 x = X[rt][ct];
+      const uint32_t h0 = pack_bf2(x[0], x[1]), h1 = pack_bf2(x[2], x[3]);
+      *reinterpret_cast<uint2*>(hi + off) = make_uint2(h0, h1);
+      *reinterpret_cast<uint2*>(lo + off) =
+          make_uint2(pack_bf2(x[0] - bf_lo(h0), x[1] - bf_hi(h0)), pack_bf2(x[2] - bf_lo(h1), x[3] - bf_hi(h1)));
+    }
+}
+
+// q'/den per token, rounded to bf16 (the query operand of the reverse states); inv = 1/den.
+template <int D>
+__device__ __forceinline__ void scale_raw(const Raw<true, D>& x, Raw<true, D>& o, const float (&inv)[2]) {
+  constexpr int E = Geo<true, D>::E;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int e = 0; e < E; e += 2)
+        o.w[tok][hh][e >> 1] = pack_bf2(x.get(tok, hh, e) * inv[tok], x.get(tok, hh, e + 1) * inv[tok]);
+}
+
+// Operand whose every column holds the per-token values w[32 kb + slot] (slot order of
+// rla2_device.h), as a bf16 pair: hi = the rounded values, lo = the rounded remainders.
+__device__ __forceinline__ void token_col_frags(const float* w, int kb, int g, Frag<true>& fhi, Frag<true>& flo) {
+  const float* a = w + 32 * kb + 4 * g;
+  const float* b = a + 16;
+  const uint32_t h0 = pack_bf2(a[0], a[1]), h1 = pack_bf2(a[2], a[3]);
+  const uint32_t h2 = pack_bf2(b[0], b[1]), h3 = pack_bf2(b[2], b[3]);
+  fhi.v = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+  flo.v = __builtin_bit_cast(bf16x8, u32x4{pack_bf2(a[0] - bf_lo(h0), a[1] - bf_hi(h0)),
+                                           pack_bf2(a[2] - bf_lo(h1), a[3] - bf_hi(h1)),
+                                           pack_bf2(b[0] - bf_lo(h2), b[1] - bf_hi(h2)),
+                                           pack_bf2(b[2] - bf_lo(h3), b[3] - bf_hi(h3))});
+}
+
+// one fp32 value per token from a [rows, H, L] plane (0 past the segment)
+__device__ __forceinline__ float load_tok(__amdgpu_buffer_rsrc_t r, int tok) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, tok * 4, 0, 0));
+}
+
+// Map backward of the lane's two tokens (RMSNorm -> rotate-half RoPE -> ReLU, reversed):
+// dx' from fp32 rows `dxp` ([64][FP]); the pre-activation is formed again exactly as the
+// forward forms it, so the ReLU gate u > 0 matches the forward's q' > 0. Accumulates the
+// RMSNorm-weight gradient of the lane's dims in dg1 (dims m E + e) and dg2 (+ D/2), and
+// returns dx rounded to bf16 in the lane's raw layout.
+template <int D>
+__device__ __forceinline__ void map_backward(const Raw<true, D>& r, Raw<true, D>& dx, const float* dxp, int fp,
+                                             const float (&g1)[Geo<true, D>::E], const float (&g2)[Geo<true, D>::E],
+                                             const float2 (&lo)[2][Geo<true, D>::E],
+                                             const float2 (&hi)[Geo<true, D>::E], float rms_eps, int t0, int m,
+                                             float (&dg1)[Geo<true, D>::E], float (&dg2)[Geo<true, D>::E]) {
+  using G = Geo<true, D>;
+  constexpr int E = G::E;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+    const float inv = rms_inv<true, D>(r, tok, rms_eps);
+    float dy1[E], dy2[E];
+    float T = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float2 cs = angle_sum(hi[e], lo[tok][e]);
+      const float x1 = r.get(tok, 0, e), x2 = r.get(tok, 1, e);
+      float u1, u2;
+      rope_pair(x1, x2, inv, g1[e], g2[e], cs, u1, u2);
+      const float d1 = u1 > 0.f ? dxp[(t0 + tok) * fp + m * E + e] : 0.f;
+      const float d2 = u2 > 0.f ? dxp[(t0 + tok) * fp + G::HALF + m * E + e] : 0.f;
+      dy1[e] = __builtin_fmaf(d1, cs.x, d2 * cs.y);     // inverse rotation
+      dy2[e] = __builtin_fmaf(d2, cs.x, -(d1 * cs.y));
+      T = __builtin_fmaf(g1[e] * dy1[e], x1, T);
+      T = __builtin_fmaf(g2[e] * dy2[e], x2, T);
+      dg1[e] = __builtin_fmaf(dy1[e], x1 * inv, dg1[e]);
+      dg2[e] = __builtin_fmaf(dy2[e], x2 * inv, dg2[e]);
+    }
+    T = sum8(T);
+    const float coef = inv * inv * inv * T * (1.0f / D);
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const float a0 = __builtin_fmaf(inv * g1[e], dy1[e], -(coef * r.get(tok, 0, e)));
+      const float a1 = __builtin_fmaf(inv * g1[e + 1], dy1[e + 1], -(coef * r.get(tok, 0, e + 1)));
+      const float b0 = __builtin_fmaf(inv * g2[e], dy2[e], -(coef * r.get(tok, 1, e)));
+      const float b1 = __builtin_fmaf(inv * g2[e + 1], dy2[e + 1], -(coef * r.get(tok, 1, e + 1)));
+      dx.w[tok][0][e >> 1] = pack_bf2(a0, a1);
+      dx.w[tok][1][e >> 1] = pack_bf2(b0, b1);
+    }
+  }
+}
+
+// Sum the lane's RMSNorm-weight partials over the 32 lanes and 4 waves sharing its dims and
+// write them (D floats) to dst. `scratch` holds at least 4 * D floats of LDS.
+template <int D>
+__device__ __forceinline__ void reduce_dgamma(float* scratch, float* dst, int tid, float (&dg1)[Geo<true, D>::E],
+                                              float (&dg2)[Geo<true, D>::E]) {
+  using G = Geo<true, D>;
+  const int wave = tid >> 6, lane = tid & 63, m = tid & 7;
+#pragma unroll
+  for (int e = 0; e < G::E; ++e) {
+#pragma unroll
+    for (int o = 8; o < 64; o <<= 1) {
+      dg1[e] += __shfl_xor(dg1[e], o);
+      dg2[e] += __shfl_xor(dg2[e], o);
+    }
+  }
+  __syncthreads();
+  if (lane < 8) {
+#pragma unroll
+    for (int e = 0; e < G::E; ++e) {
+      scratch[wave * D + m * G::E + e] = dg1[e];
+      scratch[wave * D + G::HALF + m * G::E + e] = dg2[e];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < D; i += 256) dst[i] = scratch[i] + scratch[D + i] + scratch[2 * D + i] + scratch[3 * D + i];
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_dq: per (segment, head), chunks in order with S (accumulators + bf16 pair of S^T in
+// LDS) and z running from the segment's prefix record. Phases per chunk, four workgroup
+// barriers:
+//   P1  all lanes: q', k' rows (the forward's map), V and dout rows, q' . z
+//   P2  wave w, query tile w: scores, den, g . num, gd, B_tt (to memory for the later
+//       passes), B^T and the dQ'^T tiles in registers; after a barrier the tiles go to fp32
+//       LDS rows over the q' and dout rows, which are consumed by then
+//   P3  all lanes: map backward of q -> dq; P4 state waves: S += K'^T V, z += colsum(K'),
+//       refresh of the S^T pair
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
+    const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
+    const float2* __restrict__ rope_hi, const float* __restrict__ states, uint16_t* __restrict__ dq,
+    float* __restrict__ den_out, float* __restrict__ gd_out, float* __restrict__ bd_out, float* __restrict__ dg_part,
+    int H, int L, float rms_eps, float eps) {
+  using G = Geo<true, D>;
+  using R = Raw<true, D>;
+  constexpr int BUF = kChunk * G::ROWP;
+  constexpr int SP = D + 8;  // pitch of the bf16 S^T pair
+  constexpr int FP = D + 4;  // pitch of the fp32 dQ' rows
+  constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E;
+  static_assert(kChunk * FP * 4 <= 2 * BUF * 2, "dq' rows must fit over the q' and dout rows");
+  __shared__ __attribute__((aligned(16))) uint16_t sQG[2 * BUF];  // q' rows, dout rows; then dq' rows
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sSh[D * SP];
+  __shared__ __attribute__((aligned(16))) uint16_t sSl[D * SP];
+  __shared__ __attribute__((aligned(16))) float sZ[D];
+  __shared__ float sDz[D];
+  __shared__ float sQz[kChunk];
+  uint16_t* const sQ = sQG;
+  uint16_t* const sG = sQG + BUF;
+  float* const sdQ = reinterpret_cast<float*>(sQG);
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
+  const int t0 = 2 * (tid >> 3), m = tid & 7;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * 2;
+  auto rsrc = [&](const uint16_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0 * D), 0, seg_bytes, kBufFlags);
+  };
+  const __amdgpu_buffer_rsrc_t rq = rsrc(q), rk = rsrc(k), rv = rsrc(v), rg = rsrc(dout);
+  const __amdgpu_buffer_rsrc_t rdq = rsrc(dq);
+  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+
+  floatx4 S[RT][CT];  // S_prev, value columns [wave DVW, +DVW)
+  {
+    const int wv = wave < G::NW ? wave : 0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<true, D>(wv, rt, ct, lane));
+  }
+  if (tid < D) sZ[tid] = rec[D * D + tid];
+  if (wave < G::NW) put_state_tr<D>(sSh, sSl, S, wave, lane);
+
+  float gq1[E], gq2[E], gk1[E], gk2[E], dg1[E], dg2[E];
+  float2 lo[2][E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = m * E + e;
+    gq1[e] = gamma_q[(size_t)h * D + j];
+    gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
+    gk1[e] = gamma_k[(size_t)h * D + j];
+    gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
+    lo[0][e] = rope_lo[t0 * G::HALF + j];
+    lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
+    dg1[e] = 0.f;
+    dg2[e] = 0.f;
+  }
+  const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * E;
+  R xq, xk, xv, xg;
+  float2 hi[E];
+  auto load_q = [&](int c) {
+    copy_bytes<E * 8>(hi, hi0 + (size_t)c * G::HALF);
+    load_raw_buf<true, D>(xq, rq, c * kChunk + t0, m);
+  };
+  auto load_rest = [&](int c) {
+    load_raw_buf<true, D>(xk, rk, c * kChunk + t0, m);
+    load_raw_buf<true, D>(xv, rv, c * kChunk + t0, m);
+    load_raw_buf<true, D>(xg, rg, c * kChunk + t0, m);
+  };
+  load_q(0);
+  load_rest(0);
+  __syncthreads();  // z, S^T in LDS
+
+  for (int c = 0; c < nch; ++c) {
+    const int nv = min(kChunk, si.len - c * kChunk);
+    {  // ---- P1
+      R oq, ok;
+#pragma unroll
+      for (int tok = 0; tok < 2; ++tok) {
+        const float invq = rms_inv<true, D>(xq, tok, rms_eps);
+        const float invk = rms_inv<true, D>(xk, tok, rms_eps);
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          float q1[2], q2[2], k1[2], k2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
+            rope_pair(xq.get(tok, 0, e + x), xq.get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs, q1[x], q2[x]);
+            rope_pair(xk.get(tok, 0, e + x), xk.get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs, k1[x], k2[x]);
+          }
+          put_pairs<true, D>(oq, tok, e, q1, q2);
+          put_pairs<true, D>(ok, tok, e, k1, k2);
+        }
+      }
+      store_rows<true, D>(sQ, oq, t0, m);
+      store_rows<true, D>(sK, ok, t0, m);
+      store_rows<true, D>(sV, xv, t0, m);
+      store_rows<true, D>(sG, xg, t0, m);
+#pragma unroll
+      for (int tok = 0; tok < 2; ++tok) {
+        float qz = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < E; ++e) qz = __builtin_fmaf(oq.get(tok, hh, e), sZ[hh * G::HALF + m * E + e], qz);
+        qz = sum8(qz);
+        if (m == 0) sQz[t0 + tok] = qz;
+      }
+    }
+    if (c + 1 < nch) load_rest(c + 1);  // k, v, dout are in LDS now
+    __syncthreads();  // B1
+
+    floatx4 X[RT];  // S g, then dQ'^T: rows a = 16 at + 4g + i, this lane's query
+    {  // ---- P2: query tile tt = wave
+      const int tt = wave;
+      const int t = tt * 16 + c16;
+      Frag<true> Qf[KB], Gf[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        Qf[kb] = lds_frag<true>(sQ, G::ROWP, t, kb, g);
+        Gf[kb] = lds_frag<true>(sG, G::ROWP, t, kb, g);
+      }
+      uint2 qa[RT];  // q'_t at the rows of the S g tiles
+#pragma unroll
+      for (int at = 0; at < RT; ++at) qa[at] = *reinterpret_cast<const uint2*>(sQ + t * G::ROWP + 16 * at + 4 * g);
+      floatx4 At[4], Bt[4];  // rows = keys of tile kt, column = this lane's query
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        Bt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (kt <= tt) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            At[kt] = mma(lds_frag<true>(sK, G::ROWP, kt * 16 + c16, kb, g), Qf[kb], At[kt]);
+            Bt[kt] = mma(lds_frag<true>(sV, G::ROWP, kt * 16 + c16, kb, g), Gf[kb], Bt[kt]);
+          }
+        }
+      }
+      float idot = 0.f;  // q'_t . (S g_t) = g_t . (S^T q'_t)
+#pragma unroll
+      for (int at = 0; at < RT; ++at) {
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          acc = mma(lds_frag_tr(sSh, SP, 32 * kb, 16 * at, lane), Gf[kb], acc);
+          acc = mma(lds_frag_tr(sSl, SP, 32 * kb, 16 * at, lane), Gf[kb], acc);
+        }
+        X[at] = acc;
+        idot = __builtin_fmaf(bf_lo(qa[at].x), acc[0], idot);
+        idot = __builtin_fmaf(bf_hi(qa[at].x), acc[1], idot);
+        idot = __builtin_fmaf(bf_lo(qa[at].y), acc[2], idot);
+        idot = __builtin_fmaf(bf_hi(qa[at].y), acc[3], idot);
+      }
+      // fp32 scores; the earlier keys and the self term apart
+      float rs_o = 0.f, dot_o = 0.f, sself = 0.f, bself = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sc = At[kt][i];
+          const bool before = kt < tt || (kt == tt && 4 * g + i < c16);
+          const bool self = kt == tt && 4 * g + i == c16;
+          rs_o += before ? sc : 0.f;
+          dot_o = __builtin_fmaf(before ? sc : 0.f, Bt[kt][i], dot_o);
+          sself += self ? sc : 0.f;
+          bself += self ? Bt[kt][i] : 0.f;
+        }
+      rs_o = sum_rows4(rs_o);
+      dot_o = sum_rows4(dot_o + idot);  // g . num without the self term
+      sself = sum_rows4(sself);
+      bself = sum_rows4(bself);
+      const float den_o = rs_o + sQz[t] + eps;  // den without the self score
+      const float den = den_o + sself;
+      const float inv = 1.0f / den;
+      const float inv2 = inv * inv;
+      const float gdv = -__builtin_fmaf(sself, bself, dot_o) * inv2;
+      const float bdv = __builtin_fmaf(bself, den_o, -dot_o) * inv2;
+      if (g == 0 && t < nv) {
+        const size_t ix = tok0 + (size_t)c * kChunk + t;
+        den_out[ix] = den;
+        gd_out[ix] = gdv;
+        bd_out[ix] = bdv;
+      }
+      Frag<true> Bp[2];  // B^T of key blocks 0, 1 (keys x queries), masked
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        floatx4 x[2];
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int kt = 2 * b + hlf;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool before = kt < tt || (kt == tt && 4 * g + i < c16);
+            const bool self = kt == tt && 4 * g + i == c16;
+            x[hlf][i] = before ? __builtin_fmaf(Bt[kt][i], inv, gdv) : (self ? bdv : 0.f);
+          }
+        }
+        Bp[b] = acc_frag<true>(x[0], x[1]);
+      }
+#pragma unroll
+      for (int at = 0; at < RT; ++at) {
+        floatx4 acc = X[at];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc[i], inv, gdv * sZ[16 * at + 4 * g + i]);
+        acc = mma(lds_frag_tr(sK, G::ROWP, 0, 16 * at, lane), Bp[0], acc);
+        if (tt >= 2) acc = mma(lds_frag_tr(sK, G::ROWP, 32, 16 * at, lane), Bp[1], acc);
+        X[at] = acc;
+      }
+    }
+    __syncthreads();  // B2a: the q' and dout rows are consumed
+#pragma unroll
+    for (int at = 0; at < RT; ++at)
+      *reinterpret_cast<floatx4*>(sdQ + (wave * 16 + c16) * FP + 16 * at + 4 * g) = X[at];
+    __syncthreads();  // B2
+
+    {  // ---- P3: map backward of q
+      R dx;
+      map_backward<D>(xq, dx, sdQ, FP, gq1, gq2, lo, hi, rms_eps, t0, m, dg1, dg2);
+      store_raw_buf<true, D>(dx, rdq, c * kChunk + t0, m);
+    }
+    if (wave < G::NW) {  // ---- P4: S += K'^T V
+      Frag<true> Vf[CT][2];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        Vf[ct][0] = lds_frag_tr(sV, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
+        Vf[ct][1] = lds_frag_tr(sV, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const Frag<true> a = lds_frag_tr(sK, G::ROWP, 32 * kb, 16 * rt, lane);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mma(a, Vf[ct][kb], S[rt][ct]);
+        }
+      put_state_tr<D>(sSh, sSl, S, wave, lane);
+    }
+    if (wave == 0) {  // z += column sums of K'
+      const Frag<true> ones = ones_frag<true>();
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        floatx4 zc = mma(lds_frag_tr(sK, G::ROWP, 0, 16 * rt, lane), ones, floatx4{0.f, 0.f, 0.f, 0.f});
+        zc = mma(lds_frag_tr(sK, G::ROWP, 32, 16 * rt, lane), ones, zc);
+        if (c16 < 4) sDz[rt * 16 + 4 * g + c16] = zc[c16];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];
+    }
+    if (c + 1 < nch) load_q(c + 1);
+    __syncthreads();  // B3
+  }
+  reduce_dgamma<D>(sdQ, dg_part + ((size_t)seg * H + h) * 2 * D, tid, dg1, dg2);
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_pstate: per (segment, head), the segment's totals of the reverse states,
+// sum_t Q^_t g_t^T (d x d, fragment-native like the forward records) and sum_t Q^_t gd_t den_t
+// (where the z of a forward record sits); Q^_t = bf16(q'_t / den_t), den and gd from bwd_dq.
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q,
+    const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
+    const float2* __restrict__ rope_hi, const float* __restrict__ den, const float* __restrict__ gd,
+    float* __restrict__ pstates, int H, int L, float rms_eps) {
+  using G = Geo<true, D>;
+  using R = Raw<true, D>;
+  constexpr int BUF = kChunk * G::ROWP;
+  constexpr int RT = G::RT, CT = G::CT, E = G::E;
+  constexpr int ZR = RT >= 4 ? RT / 4 : 1;  // row tiles of p per wave
+  __shared__ __attribute__((aligned(16))) uint16_t sH[BUF];  // Q^ rows
+  __shared__ __attribute__((aligned(16))) uint16_t sG[BUF];  // dout rows
+  __shared__ float sW[kChunk];                                // gd den
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
+  const int t0 = 2 * (tid >> 3), m = tid & 7;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + tok0 * D), 0, seg_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc((void*)(dout + tok0 * D), 0, seg_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)(den + tok0), 0, si.len * 4, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(gd + tok0), 0, si.len * 4, kBufFlags);
+  float g1[E], g2[E];
+  float2 lo[2][E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = m * E + e;
+    g1[e] = gamma_q[(size_t)h * D + j];
+    g2[e] = gamma_q[(size_t)h * D + j + G::HALF];
+    lo[0][e] = rope_lo[t0 * G::HALF + j];
+    lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
+  }
+  const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * E;
+  floatx4 P[RT][CT], pz[ZR];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) P[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int z = 0; z < ZR; ++z) pz[z] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const bool zwave = wave * ZR < RT;
+
+  for (int c = 0; c < nch; ++c) {
+    R xq, xg;
+    float2 hi[E];
+    copy_bytes<E * 8>(hi, hi0 + (size_t)c * G::HALF);
+    load_raw_buf<true, D>(xq, rq, c * kChunk + t0, m);
+    load_raw_buf<true, D>(xg, rg, c * kChunk + t0, m);
+    float dn[2], w[2];
+#pragma unroll
+    for (int tok = 0; tok < 2; ++tok) {  // tokens past the segment read 0 and weigh nothing
+      dn[tok] = load_tok(rd, c * kChunk + t0 + tok);
+      w[tok] = load_tok(rw, c * kChunk + t0 + tok);
+    }
+    __syncthreads();  // the previous chunk's operands are consumed
+    {
+      R oq, oh;
+      feature_map_lane<true, D>(xq, oq, g1, g2, lo, hi, rms_eps);
+      const float inv[2] = {dn[0] > 0.f ? 1.0f / dn[0] : 0.f, dn[1] > 0.f ? 1.0f / dn[1] : 0.f};
+      scale_raw<D>(oq, oh, inv);
+      store_rows<true, D>(sH, oh, t0, m);
+      store_rows<true, D>(sG, xg, t0, m);
+      if (m == 0) {
+        sW[t0] = w[0] * dn[0];
+        sW[t0 + 1] = w[1] * dn[1];
+      }
+    }
+    __syncthreads();
+    if (wave < G::NW) {
+      Frag<true> Nf[CT][2];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        Nf[ct][0] = lds_frag_tr(sG, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
+        Nf[ct][1] = lds_frag_tr(sG, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const Frag<true> a = lds_frag_tr(sH, G::ROWP, 32 * kb, 16 * rt, lane);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) P[rt][ct] = mma(a, Nf[ct][kb], P[rt][ct]);
+        }
+    }
+    if (zwave) {  // p += Q^^T (gd den) against an operand holding it in every column
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<true> w_hi, w_lo;
+        token_col_frags(sW, kb, g, w_hi, w_lo);
+#pragma unroll
+        for (int z = 0; z < ZR; ++z) {
+          const Frag<true> a = lds_frag_tr(sH, G::ROWP, 32 * kb, 16 * (wave * ZR + z), lane);
+          pz[z] = mma(a, w_hi, pz[z]);
+          pz[z] = mma(a, w_lo, pz[z]);
+        }
+      }
+    }
+  }
+  float* rec = pstates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  if (wave < G::NW) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        __builtin_nontemporal_store(P[rt][ct], reinterpret_cast<floatx4*>(rec + rec_frag<true, D>(wave, rt, ct, lane)));
+  }
+  if (zwave && c16 < 4) {  // every column of pz holds the sums of rows 16 rt + 4g + i
+#pragma unroll
+    for (int z = 0; z < ZR; ++z) rec[D * D + (wave * ZR + z) * 16 + 4 * g + c16] = pz[z][c16];
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_dkv: per (segment, head), chunks in reverse order with P (accumulators + bf16 pair of
+// P^T in LDS) and p running from the segment's suffix record. Phases per chunk as in bwd_dq:
+//   P1  all lanes: q', k' rows, V and dout rows, Q^ rows, 1/den, gd, B_tt, gd den per token
+//   P2  wave w, key tile w: A and B (queries x keys, queries at or after the key); dV^T goes
+//       out from the accumulators (4 consecutive dims per lane); the dK'^T tiles go, after a
+//       barrier, to fp32 LDS rows over the k' and v rows
+//   P3  all lanes: map backward of k -> dk; P4 state waves: P += Q^^T G, p += Q^^T (gd den),
+//       refresh of the P^T pair
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
+    const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
+    const float2* __restrict__ rope_hi, const float* __restrict__ pstates, const float* __restrict__ den,
+    const float* __restrict__ gd, const float* __restrict__ bd, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dg_part, int H, int L, float rms_eps) {
+  using G = Geo<true, D>;
+  using R = Raw<true, D>;
+  constexpr int BUF = kChunk * G::ROWP;
+  constexpr int SP = D + 8;
+  constexpr int FP = D + 4;
+  constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E;
+  static_assert(kChunk * FP * 4 <= 2 * BUF * 2, "dk' rows must fit over the k' and v rows");
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * BUF];  // k' rows, v rows; then dk' rows
+  __shared__ __attribute__((aligned(16))) uint16_t sG[BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sH[BUF];       // Q^ rows
+  __shared__ __attribute__((aligned(16))) uint16_t sPh[D * SP];
+  __shared__ __attribute__((aligned(16))) uint16_t sPl[D * SP];
+  __shared__ __attribute__((aligned(16))) float sP[D];
+  __shared__ float sDp[D];
+  __shared__ float sI[kChunk], sGd[kChunk], sBd[kChunk], sW[kChunk];
+  uint16_t* const sK = sKV;
+  uint16_t* const sV = sKV + BUF;
+  float* const sdK = reinterpret_cast<float*>(sKV);
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
+  const int t0 = 2 * (tid >> 3), m = tid & 7;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * 2;
+  auto rsrc = [&](const uint16_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0 * D), 0, seg_bytes, kBufFlags);
+  };
+  auto rsrc_tok = [&](const float* base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0), 0, si.len * 4, kBufFlags);
+  };
+  const __amdgpu_buffer_rsrc_t rq = rsrc(q), rk = rsrc(k), rv = rsrc(v), rg = rsrc(dout);
+  const __amdgpu_buffer_rsrc_t rdk = rsrc(dk), rdv = rsrc(dv);
+  const __amdgpu_buffer_rsrc_t rd = rsrc_tok(den), rw = rsrc_tok(gd), rb = rsrc_tok(bd);
+  const float* rec = pstates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+
+  floatx4 P[RT][CT];  // P_next, value columns [wave DVW, +DVW)
+  {
+    const int wv = wave < G::NW ? wave : 0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        P[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<true, D>(wv, rt, ct, lane));
+  }
+  if (tid < D) sP[tid] = rec[D * D + tid];
+  if (wave < G::NW) put_state_tr<D>(sPh, sPl, P, wave, lane);
+
+  float gq1[E], gq2[E], gk1[E], gk2[E], dg1[E], dg2[E];
+  float2 lo[2][E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = m * E + e;
+    gq1[e] = gamma_q[(size_t)h * D + j];
+    gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
+    gk1[e] = gamma_k[(size_t)h * D + j];
+    gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
+    lo[0][e] = rope_lo[t0 * G::HALF + j];
+    lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
+    dg1[e] = 0.f;
+    dg2[e] = 0.f;
+  }
+  const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * E;
+  R xq, xk, xv, xg;
+  float2 hi[E];
+  float dn[2], gdl[2], bdl[2];
+  auto load_k = [&](int c) {
+    copy_bytes<E * 8>(hi, hi0 + (size_t)c * G::HALF);
+    load_raw_buf<true, D>(xk, rk, c * kChunk + t0, m);
+  };
+  auto load_rest = [&](int c) {
+    load_raw_buf<true, D>(xq, rq, c * kChunk + t0, m);
+    load_raw_buf<true, D>(xv, rv, c * kChunk + t0, m);
+    load_raw_buf<true, D>(xg, rg, c * kChunk + t0, m);
+#pragma unroll
+    for (int tok = 0; tok < 2; ++tok) {
+      dn[tok] = load_tok(rd, c * kChunk + t0 + tok);
+      gdl[tok] = load_tok(rw, c * kChunk + t0 + tok);
+      bdl[tok] = load_tok(rb, c * kChunk + t0 + tok);
+    }
+  };
+  load_k(nch - 1);
+  load_rest(nch - 1);
+  __syncthreads();  // p, P^T in LDS
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const int nv = min(kChunk, si.len - c * kChunk);
+    {  // ---- P1
+      R oq, ok, oh;
+#pragma unroll
+      for (int tok = 0; tok < 2; ++tok) {
+        const float invq = rms_inv<true, D>(xq, tok, rms_eps);
+        const float invk = rms_inv<true, D>(xk, tok, rms_eps);
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          float q1[2], q2[2], k1[2], k2[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
+            rope_pair(xq.get(tok, 0, e + x), xq.get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs, q1[x], q2[x]);
+            rope_pair(xk.get(tok, 0, e + x), xk.get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs, k1[x], k2[x]);
+          }
+          put_pairs<true, D>(oq, tok, e, q1, q2);
+          put_pairs<true, D>(ok, tok, e, k1, k2);
+        }
+      }
+      const float inv[2] = {dn[0] > 0.f ? 1.0f / dn[0] : 0.f, dn[1] > 0.f ? 1.0f / dn[1] : 0.f};
+      scale_raw<D>(oq, oh, inv);
+      store_rows<true, D>(sQ, oq, t0, m);
+      store_rows<true, D>(sK, ok, t0, m);
+      store_rows<true, D>(sV, xv, t0, m);
+      store_rows<true, D>(sG, xg, t0, m);
+      store_rows<true, D>(sH, oh, t0, m);
+      if (m == 0) {
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {
+          sI[t0 + tok] = inv[tok];
+          sGd[t0 + tok] = gdl[tok];
+          sBd[t0 + tok] = bdl[tok];
+          sW[t0 + tok] = gdl[tok] * dn[tok];
+        }
+      }
+    }
+    if (c > 0) load_rest(c - 1);
+    __syncthreads();  // B1
+
+    floatx4 Y[RT];  // dK'^T: rows a = 16 at + 4g + i, this lane's key
+    {  // ---- P2: key tile kt = wave
+      const int kt = wave;
+      const int key = kt * 16 + c16;
+      Frag<true> Kf[KB], Vf[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        Kf[kb] = lds_frag<true>(sK, G::ROWP, key, kb, g);
+        Vf[kb] = lds_frag<true>(sV, G::ROWP, key, kb, g);
+      }
+      floatx4 Aq[4], Bq[4];  // rows = queries of tile tt, column = this lane's key
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        Aq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        Bq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (tt >= kt) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            Aq[tt] = mma(lds_frag<true>(sQ, G::ROWP, tt * 16 + c16, kb, g), Kf[kb], Aq[tt]);
+            Bq[tt] = mma(lds_frag<true>(sG, G::ROWP, tt * 16 + c16, kb, g), Vf[kb], Bq[tt]);
+          }
+        }
+      }
+      Frag<true> Ap[2], Bp[2];  // query blocks 0, 1 as the B operands (queries x keys)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        floatx4 xa[2], xb[2];
+#pragma unroll
+        for (int hlf = 0; hlf < 2; ++hlf) {
+          const int tt = 2 * b + hlf;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = tt * 16 + 4 * g + i;
+            const bool after = tt > kt || (tt == kt && 4 * g + i > c16);
+            const bool self = tt == kt && 4 * g + i == c16;
+            const float ri = sI[t];
+            xa[hlf][i] = (after || self) ? Aq[tt][i] * ri : 0.f;
+            xb[hlf][i] = after ? __builtin_fmaf(Bq[tt][i], ri, sGd[t]) : (self ? sBd[t] : 0.f);
+          }
+        }
+        Ap[b] = acc_frag<true>(xa[0], xa[1]);
+        Bp[b] = acc_frag<true>(xb[0], xb[1]);
+      }
+      // dV^T: rows = value dims, this lane's key; four consecutive dims per lane go out directly
+#pragma unroll
+      for (int ct = 0; ct < RT; ++ct) {
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          acc = mma(lds_frag<true>(sPh, SP, 16 * ct + c16, kb, g), Kf[kb], acc);
+          acc = mma(lds_frag<true>(sPl, SP, 16 * ct + c16, kb, g), Kf[kb], acc);
+        }
+        if (kt <= 1) acc = mma(lds_frag_tr(sG, G::ROWP, 0, 16 * ct, lane), Ap[0], acc);
+        acc = mma(lds_frag_tr(sG, G::ROWP, 32, 16 * ct, lane), Ap[1], acc);
+        const int off = ((c * kChunk + key) * D + 16 * ct + 4 * g) * 2;  // keys past the segment are dropped
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])}, rdv,
+                                              key < nv ? off : seg_bytes, 0, kLoadStream);
+      }
+      // dK'^T
+#pragma unroll
+      for (int at = 0; at < RT; ++at) {
+        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          acc = mma(lds_frag_tr(sPh, SP, 32 * kb, 16 * at, lane), Vf[kb], acc);
+          acc = mma(lds_frag_tr(sPl, SP, 32 * kb, 16 * at, lane), Vf[kb], acc);
+        }
+        if (kt <= 1) acc = mma(lds_frag_tr(sQ, G::ROWP, 0, 16 * at, lane), Bp[0], acc);
+        acc = mma(lds_frag_tr(sQ, G::ROWP, 32, 16 * at, lane), Bp[1], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += sP[16 * at + 4 * g + i];
+        Y[at] = acc;
+      }
+    }
+    __syncthreads();  // B2a: the k' and v rows are consumed
+#pragma unroll
+    for (int at = 0; at < RT; ++at)
+      *reinterpret_cast<floatx4*>(sdK + (wave * 16 + c16) * FP + 16 * at + 4 * g) = Y[at];
+    __syncthreads();  // B2
+
+    {  // ---- P3: map backward of k
+      R dx;
+      map_backward<D>(xk, dx, sdK, FP, gk1, gk2, lo, hi, rms_eps, t0, m, dg1, dg2);
+      store_raw_buf<true, D>(dx, rdk, c * kChunk + t0, m);
+    }
+    if (wave < G::NW) {  // ---- P4: P += Q^^T G
+      Frag<true> Nf[CT][2];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        Nf[ct][0] = lds_frag_tr(sG, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
+        Nf[ct][1] = lds_frag_tr(sG, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const Frag<true> a = lds_frag_tr(sH, G::ROWP, 32 * kb, 16 * rt, lane);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) P[rt][ct] = mma(a, Nf[ct][kb], P[rt][ct]);
+        }
+      put_state_tr<D>(sPh, sPl, P, wave, lane);
+    }
+    if (wave == 0) {  // p += Q^^T (gd den), as a bf16 pair in every column
+      Frag<true> w_hi[2], w_lo[2];
+      token_col_frags(sW, 0, g, w_hi[0], w_lo[0]);
+      token_col_frags(sW, 1, g, w_hi[1], w_lo[1]);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        floatx4 pc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const Frag<true> a = lds_frag_tr(sH, G::ROWP, 32 * kb, 16 * rt, lane);
+          pc = mma(a, w_hi[kb], pc);
+          pc = mma(a, w_lo[kb], pc);
+        }
+        if (c16 < 4) sDp[rt * 16 + 4 * g + c16] = pc[c16];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int i = lane; i < D; i += 64) sP[i] += sDp[i];
+    }
+    if (c > 0) load_k(c - 1);
+    __syncthreads();  // B3
+  }
+  reduce_dgamma<D>(sdK, dg_part + ((size_t)seg * H + h) * 2 * D + D, tid, dg1, dg2);
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_dgamma: RMSNorm-weight gradients, the per-segment partials summed in segment order
+// (deterministic): part[(seg H + h) 2D + j] (q: j < D, k: D + j).
+
+__global__ void bwd_dgamma_kernel(const float* __restrict__ part, const int32_t* __restrict__ nseg, int H, int D,
+                                  float* __restrict__ dgq, float* __restrict__ dgk) {
+  const int h = blockIdx.x, j = threadIdx.x;
+  if (j >= 2 * D) return;
+  const int n = *nseg;
+  float acc = 0.f;
+  for (int s = 0; s < n; ++s) acc += part[((size_t)s * H + h) * 2 * D + j];
+  if (j < D) {
+    if (dgq != nullptr) dgq[(size_t)h * D + j] = acc;
+  } else if (dgk != nullptr) {
+    dgk[(size_t)h * D + j - D] = acc;
+  }
+}
+
+template <int D>
+hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
+  hipError_t e = launch_fwd_states(p, a, s);
+  if (e != hipSuccess || p.n_seg_max == 0) return e;
+  int32_t* tab = reinterpret_cast<int32_t*>(a.ws + p.off_tab);
+  int32_t* nseg = reinterpret_cast<int32_t*>(a.ws + p.off_nseg);
+  float2* rlo = reinterpret_cast<float2*>(a.ws + p.off_rope_lo);
+  float2* rhi = reinterpret_cast<float2*>(a.ws + p.off_rope_hi);
+  float* states = reinterpret_cast<float*>(a.ws + p.off_states);
+  float* pstates = reinterpret_cast<float*>(a.ws + p.off_pstates);
+  float* den = reinterpret_cast<float*>(a.ws + p.off_den);
+  float* gd = reinterpret_cast<float*>(a.ws + p.off_gd);
+  float* bd = reinterpret_cast<float*>(a.ws + p.off_bd);
+  float* dgp = reinterpret_cast<float*>(a.ws + p.off_dgpart);
+  const auto* q = static_cast<const uint16_t*>(a.q);
+  const auto* k = static_cast<const uint16_t*>(a.k);
+  const auto* v = static_cast<const uint16_t*>(a.v);
+  const auto* g = static_cast<const uint16_t*>(b.dout);
+  const dim3 grid(p.n_seg_max, p.H);
+  hipLaunchKernelGGL((bwd_dq_kernel<D>), grid, dim3(256), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi, states,
+                     static_cast<uint16_t*>(b.dq), den, gd, bd, dgp, p.H, p.L, a.rms_eps, a.eps);
+  hipLaunchKernelGGL((bwd_pstate_kernel<D>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
+                     pstates, p.H, p.L, a.rms_eps);
+  e = launch_scan_suffix(p, a.ws, pstates, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkv_kernel<D>), grid, dim3(256), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
+                     pstates, den, gd, bd, static_cast<uint16_t*>(b.dk), static_cast<uint16_t*>(b.dv), dgp, p.H, p.L,
+                     a.rms_eps);
+  if (b.dgamma_q != nullptr || b.dgamma_k != nullptr)
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3(p.H), dim3(2 * D), 0, s, dgp, nseg, p.H, D, b.dgamma_q, b.dgamma_k);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
+  switch (p.d) {
+    case 32: return run_backward<32>(p, a, b, s);
+    case 64: return run_backward<64>(p, a, b, s);
+    case 128: return run_backward<128>(p, a, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rla2

@@ -31,6 +31,11 @@ struct Plan {
   size_t off_tab, off_docoff, off_nseg, off_rope_lo, off_rope_hi, off_states;
   size_t bytes;        // total workspace bytes
   size_t bytes_tables; // bytes up to the state records (what the feature map alone needs)
+  // backward: a second set of segment records (reverse states); den, gd and the query's
+  // weight on its own key per token-head; per-(segment, head) partial RMSNorm-weight
+  // gradients of q and k
+  size_t off_pstates, off_den, off_gd, off_bd, off_dgpart;
+  size_t bytes_bwd;    // total backward workspace bytes
 };
 
 struct FwdArgs {
@@ -48,6 +53,20 @@ struct FwdArgs {
 // `ev` (optional) gets kNumFwdKernels + 1 events recorded around the kernels.
 constexpr int kNumFwdKernels = 4;
 hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
+
+// Backward arguments (bf16 activations).
+struct BwdArgs {
+  const void* dout;            // cotangent of the forward output, [B, H, L, d]
+  void *dq, *dk, *dv;          // written, [B, H, L, d]
+  float *dgamma_q, *dgamma_k;  // written, [H, d] (null: not formed)
+};
+
+// prep + chunk state + exclusive-prefix scan of the records (what the backward needs of the
+// forward's state pass); the reverse scan of a second record set.
+hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s);
+hipError_t launch_scan_suffix(const Plan& p, char* ws, float* states, hipStream_t s);
+// the whole chunked backward (rla2_backward.hip)
+hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s);
 
 // The feature map alone: prep, then q' and k' (either input may be null).
 hipError_t launch_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void* k_out, hipStream_t s);

@@ -5,6 +5,11 @@ import torch
 # Tolerances of the parity bar: max per-row relative error (see row_rel_err).
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
+# Gradient rows are sums of terms of the typical row size that can cancel to far below it;
+# with bf16 features (relative rounding 2^-9 of q' and k', as in the forward) their absolute
+# error stays at the typical scale, so rows under GRAD_FLOOR of the median row size are
+# held to an absolute bound instead (see grad_row_err).
+GRAD_FLOOR = 0.05
 
 
 def f64(t) -> np.ndarray:
@@ -30,6 +35,26 @@ def row_rel_err(got, ref) -> float:
     if (~zero).sum() == 0:
         return 0.0
     return float((num[~zero] / den[~zero]).max())
+
+
+def grad_row_err(got, ref, floor: float = GRAD_FLOOR) -> float:
+    """Max over rows of ||got - ref||_inf / max(||ref_row||_inf, floor * m), m = the median
+    of ||ref_row||_inf over the tensor's nonzero rows: the per-row relative error for every
+    row at least ``floor`` of the typical row size, an absolute error in units of
+    ``floor * m`` below that. A row whose reference is exactly zero must be exactly zero."""
+    got, ref = f64(got), f64(ref)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    g = got.reshape(-1, got.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    num = np.abs(g - r).max(axis=1)
+    den = np.abs(r).max(axis=1)
+    zero = den == 0
+    if (num[zero] != 0).any():
+        return float("inf")
+    if (~zero).sum() == 0:
+        return 0.0
+    scale = np.maximum(den, floor * np.median(den[~zero]))
+    return float((num[~zero] / scale[~zero]).max())
 
 
 def mat_rel_err(got, ref, mat_dims: int = 2) -> float:

@@ -209,3 +209,32 @@ def test_feature_map_error_paths():
     assert call(ko=A + 256 * MB) == ALIAS                 # k' over q'
     assert call(ko=A + 512 * MB) == ALIAS                 # k' over the workspace
     assert call(d=desc(rms_eps=0.0)) == VALUE
+
+
+def test_backward_error_paths():
+    L = rla.lib()
+
+    def call(d=None, q=A, k=A + 64 * MB, v=A + 128 * MB, gq=A + 192 * MB, gk=A + 193 * MB,
+             dout=A + 264 * MB, dq=A + 328 * MB, dk=A + 392 * MB, dv=A + 456 * MB, dgq=A + 194 * MB,
+             dgk=A + 195 * MB, ws=A + 1024 * MB, ws_bytes=1 << 30):
+        d = d or desc()
+        return L.rla2_bwd_chunked(ctypes.byref(d), q, k, v, gq, gk, dout, dq, dk, dv, dgq, dgk, ws, ws_bytes, None)
+
+    n = ctypes.c_size_t(0)
+    assert L.rla2_bwd_workspace_size(ctypes.byref(desc()), ctypes.byref(n)) == OK
+    full = ctypes.c_size_t(0)
+    assert L.rla2_fwd_workspace_size(ctypes.byref(desc()), ctypes.byref(full)) == OK
+    assert n.value > full.value                          # a second record set, den, gd and B_tt
+    assert L.rla2_bwd_workspace_size(ctypes.byref(desc(dtype=rla.F32)), ctypes.byref(n)) == UNSUP
+    assert L.rla2_bwd_workspace_size(ctypes.byref(desc(bidirectional=1)), ctypes.byref(n)) == UNSUP
+    assert call(d=desc(dtype=rla.F32)) == UNSUP
+    assert call(d=desc(bidirectional=1)) == UNSUP
+    assert call(dout=None) == NULLP
+    assert call(dv=None) == NULLP
+    assert call(ws=None) == WS
+    assert call(ws_bytes=1024) == WS
+    assert call(dk=A + 392 * MB + 2) == MISAL
+    assert call(dq=A + 64 * MB) == ALIAS                  # dq over k
+    assert call(dv=A + 328 * MB) == ALIAS                 # dv over dq
+    assert call(dgk=A + 192 * MB) == ALIAS                # dgamma_k over gamma_q
+    assert call(dout=A + 1024 * MB) == ALIAS              # an input inside the workspace
