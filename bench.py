@@ -6,7 +6,8 @@ One step = one chunked causal forward over the long-context workload
 segment map, RoPE table, chunk state, state scan and chunk output (the feature
 map runs inside the last two). The decode step over 256 sequences x 32 heads
 (d=128, fp32 state built from prefixes of length U{1..8192}) is timed in the same
-run and reported under "decode". Inputs are resident in HBM before timing.
+run and reported under "decode", and the chunked backward of the long-context
+workload under "backward". Inputs are resident in HBM before timing.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -50,16 +51,27 @@ class HipEvents:
         return ms.value
 
 
+KERNEL_SOURCES = ("rla2_device.h", "rla2_kernels.hip", "rla2_backward.hip")
+
+
+def kernel_source_digest():
+    """sha256 over the device-code sources, in a fixed order."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "linear_attention_rla_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary,
-    or None when the kernel source has changed since the counters were taken."""
-    import hashlib
+    or None when the kernel sources have changed since the counters were taken."""
     import re
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-    src = os.path.join(ROOT, "linear_attention_rla_amd", "csrc", "rla2_kernels.hip")
     try:
         lines = [l.strip() for l in open(path) if l.strip() and not l.startswith("#")]
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = kernel_source_digest()
     except OSError:
         return None
     if not lines or lines[0] != f"kernel_source_sha256 {digest}":
@@ -190,6 +202,64 @@ def time_prologue(args, rla, torch, hip, ev, stream, q, k, gq, gk):
                          "algorithmic_bytes": nbytes}}
 
 
+BWD_KERNELS = ["prep", "chunk_state", "state_scan", "bwd_dq", "bwd_pstate", "suffix_scan", "bwd_dkv", "bwd_dgamma"]
+
+
+def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
+    """The chunked backward of the same workload: dq, dk, dv and the RMSNorm-weight
+    gradients from q, k, v and a seeded cotangent. Whole call and per kernel (events on
+    the launch stream); HBM rooflines of the two sweep kernels and of the whole call
+    against the bytes the gradients need at least (read q, k, v, dout; write dq, dk, dv)."""
+    B, H, L, d = q.shape
+    dout = workloads.cotangent(q.shape, seed=4, device=str(q.device))
+    outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(gq), torch.empty_like(gk))
+    desc = rla.make_desc(B, H, L, d, rla.BF16)
+    n = ctypes.c_size_t(0)
+    rla.lib().rla2_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    steps = min(args.steps, 20)
+
+    def run(events=None):
+        rla.bwd(q, k, v, gq, gk, dout, out=outs, workspace=ws, events=events)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = HipEvents(len(BWD_KERNELS) + 1)
+    ev.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    ev.hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        run()
+    ev.hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms = ev.elapsed(0, 1) / steps
+    per = [0.0] * len(BWD_KERNELS)
+    for _ in range(steps):
+        run(ev.arr)
+        for i in range(len(BWD_KERNELS)):
+            per[i] += ev.elapsed(i, i + 1)
+    per = [x / steps for x in per]
+    th = B * H * L
+    row = d * 2  # bytes of one bf16 token row
+    need = 7 * row * th
+    res = {"workload": "backward of the long-context causal forward (B=1 H=32 L=65536 d=128 bf16), "
+                       "seeded N(0,1) cotangent",
+           "ms_per_call": ms, "tokens_per_s": B * L / (ms * 1e-3), "steps": steps,
+           "kernel_ms": dict(zip(BWD_KERNELS, per)),
+           "roofline": {"kernel": "whole backward", "bound": "hbm", "achieved": need / (ms * 1e-3) / 1e9,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": need / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": need}}
+    # per sweep kernel: the token rows it must move (dq: q, k, v, dout in, dq out; dk dv:
+    # q, k, v, dout in, dk, dv out) plus its fp32 per-token values (den, gd, B_tt)
+    for name, nbytes in (("bwd_dq", (5 * row + 12) * th), ("bwd_dkv", (6 * row + 12) * th)):
+        t = per[BWD_KERNELS.index(name)]
+        gbs = nbytes / (t * 1e-3) / 1e9
+        res[name] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                     "traffic": measured_traffic(name + "_kernel")}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -198,6 +268,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-modes", action="store_true",
                     help="skip the bidirectional and continuation forwards of the same workload")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -288,6 +359,11 @@ def main():
     if not args.no_modes:
         result["modes"] = time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc)
         result["prologue"] = time_prologue(args, rla, torch, hip, ev, stream, q, k, gq, gk)
+
+    if not args.no_backward:
+        log("timing the backward ...")
+        result["backward"] = time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk)
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         del q, k, v, out, ws

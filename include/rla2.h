@@ -210,6 +210,24 @@ rla2_status rla2_bwd_chunked(const rla2_fwd_desc* desc, const void* q, const voi
                              float* dgamma_k, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
 
+#define RLA2_BWD_KERNELS 8
+
+/*
+ * rla2_bwd_chunked with hipEvent_t markers, for measurement tools. `events` holds
+ * RLA2_BWD_KERNELS + 1 events created by the caller; event i is recorded on `stream`
+ * right before kernel i -- 0 set-up, 1 chunk state, 2 prefix scan of the states, 3 dq,
+ * 4 reverse-state totals, 5 suffix scan, 6 dk and dv, 7 RMSNorm-weight sums -- and
+ * events[RLA2_BWD_KERNELS] after the last (a kernel that is not needed takes no time).
+ * NULL `events` behaves exactly like rla2_bwd_chunked. Same arguments, ownership and
+ * errors otherwise.
+ */
+rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, const void* k,
+                                      const void* v, const float* gamma_q, const float* gamma_k,
+                                      const void* dout, void* dq, void* dk, void* dv,
+                                      float* dgamma_q, float* dgamma_k, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream,
+                                      hipEvent_t* events);
+
 /* Workspace bytes rla2_feature_map needs for `desc` (segment table and RoPE tables). */
 rla2_status rla2_feature_map_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
 

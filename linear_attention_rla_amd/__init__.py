@@ -73,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.rla2_state_from_prefix.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.rla2_bwd_workspace_size.restype = ctypes.c_int
         L.rla2_bwd_workspace_size.argtypes = [_DESC, _SZ]
+        L.rla2_bwd_chunked_profiled.restype = ctypes.c_int
+        L.rla2_bwd_chunked_profiled.argtypes = [_DESC] + [_P] * 12 + [ctypes.c_size_t, _P, _P]
         L.rla2_bwd_chunked.restype = ctypes.c_int
         L.rla2_bwd_chunked.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.rla2_feature_map_workspace_size.restype = ctypes.c_int
@@ -217,9 +219,12 @@ def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0,
 
 
 def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
-        rope_base=10000.0, initial_S=None, initial_z=None, initial_pos=0, want_dgamma=True, workspace=None):
+        rope_base=10000.0, initial_S=None, initial_z=None, initial_pos=0, want_dgamma=True, workspace=None,
+        out=None, events=None):
     """Backward of the causal forward (bf16) for the same inputs; ``dout`` = dL/dout.
-    Returns ``(dq, dk, dv, dgamma_q, dgamma_k)`` (the last two None unless ``want_dgamma``)."""
+    Returns ``(dq, dk, dv, dgamma_q, dgamma_k)`` (the last two None unless ``want_dgamma``).
+    ``out``: optional preallocated ``(dq, dk, dv, dgamma_q, dgamma_k)``; ``events``: optional
+    ctypes array of RLA2_BWD_KERNELS + 1 hipEvent_t handles (rla2_bwd_chunked_profiled)."""
     for n_, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _check_dev(n_, t, torch.bfloat16)
         if t.shape != q.shape:
@@ -230,20 +235,37 @@ def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunk
                      initial_S, initial_z)
     if gamma_q.shape != (desc.H, desc.d) or gamma_k.shape != (desc.H, desc.d):
         raise ValueError("gamma_q and gamma_k must be [H, d]")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    dgq = dgk = None
-    if want_dgamma:
-        dgq = torch.empty_like(gamma_q)
-        dgk = torch.empty_like(gamma_k)
+    if out is not None:
+        dq, dk, dv, dgq, dgk = out
+        for n_, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _check_dev(n_, t, torch.bfloat16)
+            if t.shape != q.shape:
+                raise ValueError(f"{n_} must have the shape of q")
+        for n_, t in (("dgamma_q", dgq), ("dgamma_k", dgk)):
+            if t is not None:
+                _check_dev(n_, t, torch.float32)
+                if t.shape != gamma_q.shape:
+                    raise ValueError(f"{n_} must be [H, d]")
+        if not want_dgamma:
+            dgq = dgk = None
+    else:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dgq = dgk = None
+        if want_dgamma:
+            dgq = torch.empty_like(gamma_q)
+            dgk = torch.empty_like(gamma_k)
     n = ctypes.c_size_t(0)
     st = lib().rla2_bwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
     if st:
         raise Rla2Error(st, "rla2_bwd_workspace_size")
     if workspace is None or workspace.numel() < n.value:
         workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
-    st = lib().rla2_bwd_chunked(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q), _ptr(gamma_k),
-                                _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgq), _ptr(dgk),
-                                _ptr(workspace), workspace.numel(), _stream(q.device))
+    args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q), _ptr(gamma_k), _ptr(dout), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(dgq), _ptr(dgk), _ptr(workspace), workspace.numel(), _stream(q.device))
+    if events is None:
+        st = lib().rla2_bwd_chunked(*args)
+    else:
+        st = lib().rla2_bwd_chunked_profiled(*args, events)
     if st:
         raise Rla2Error(st, "rla2_bwd_chunked")
     return dq, dk, dv, dgq, dgk

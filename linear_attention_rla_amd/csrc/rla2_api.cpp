@@ -17,6 +17,7 @@ using rla2::Plan;
 
 constexpr int32_t kAbiVersion = 2;
 static_assert(RLA2_FWD_KERNELS == rla2::kNumFwdKernels, "kernel count of the profiled forward");
+static_assert(RLA2_BWD_KERNELS == rla2::kNumBwdKernels, "kernel count of the profiled backward");
 
 bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
@@ -289,6 +290,14 @@ rla2_status rla2_bwd_chunked(const rla2_fwd_desc* desc, const void* q, const voi
                              const float* gamma_q, const float* gamma_k, const void* dout,
                              void* dq, void* dk, void* dv, float* dgamma_q, float* dgamma_k, void* workspace,
                              size_t workspace_bytes, hipStream_t stream) {
+  return rla2_bwd_chunked_profiled(desc, q, k, v, gamma_q, gamma_k, dout, dq, dk, dv, dgamma_q, dgamma_k,
+                                   workspace, workspace_bytes, stream, nullptr);
+}
+
+rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v,
+                                      const float* gamma_q, const float* gamma_k, const void* dout, void* dq,
+                                      void* dk, void* dv, float* dgamma_q, float* dgamma_k, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
@@ -329,7 +338,7 @@ rla2_status rla2_bwd_chunked(const rla2_fwd_desc* desc, const void* q, const voi
                   desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
                   static_cast<char*>(workspace)};
   rla2::BwdArgs b{dout, dq, dk, dv, dgamma_q, dgamma_k};
-  return finish(rla2::launch_backward(p, a, b, stream));
+  return finish(rla2::launch_backward(p, a, b, stream, events));
 }
 
 rla2_status rla2_feature_map_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {

@@ -883,9 +883,16 @@ __global__ void bwd_dgamma_kernel(const float* __restrict__ part, const int32_t*
 }
 
 template <int D>
-hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
-  hipError_t e = launch_fwd_states(p, a, s);
-  if (e != hipSuccess || p.n_seg_max == 0) return e;
+hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s, hipEvent_t* ev) {
+  auto mark = [&](int i) {
+    if (ev != nullptr) (void)hipEventRecord(ev[i], s);
+  };
+  hipError_t e = launch_fwd_states(p, a, s, ev);
+  if (e != hipSuccess) return e;
+  if (p.n_seg_max == 0) {
+    for (int i = 3; i <= kNumBwdKernels; ++i) mark(i);
+    return hipGetLastError();
+  }
   int32_t* tab = reinterpret_cast<int32_t*>(a.ws + p.off_tab);
   int32_t* nseg = reinterpret_cast<int32_t*>(a.ws + p.off_nseg);
   float2* rlo = reinterpret_cast<float2*>(a.ws + p.off_rope_lo);
@@ -901,27 +908,33 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   const auto* v = static_cast<const uint16_t*>(a.v);
   const auto* g = static_cast<const uint16_t*>(b.dout);
   const dim3 grid(p.n_seg_max, p.H);
+  mark(3);
   hipLaunchKernelGGL((bwd_dq_kernel<D>), grid, dim3(256), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi, states,
                      static_cast<uint16_t*>(b.dq), den, gd, bd, dgp, p.H, p.L, a.rms_eps, a.eps);
+  mark(4);
   hipLaunchKernelGGL((bwd_pstate_kernel<D>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
                      pstates, p.H, p.L, a.rms_eps);
+  mark(5);
   e = launch_scan_suffix(p, a.ws, pstates, s);
   if (e != hipSuccess) return e;
+  mark(6);
   hipLaunchKernelGGL((bwd_dkv_kernel<D>), grid, dim3(256), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
                      pstates, den, gd, bd, static_cast<uint16_t*>(b.dk), static_cast<uint16_t*>(b.dv), dgp, p.H, p.L,
                      a.rms_eps);
+  mark(7);
   if (b.dgamma_q != nullptr || b.dgamma_k != nullptr)
     hipLaunchKernelGGL(bwd_dgamma_kernel, dim3(p.H), dim3(2 * D), 0, s, dgp, nseg, p.H, D, b.dgamma_q, b.dgamma_k);
+  mark(8);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s) {
+hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s, hipEvent_t* ev) {
   switch (p.d) {
-    case 32: return run_backward<32>(p, a, b, s);
-    case 64: return run_backward<64>(p, a, b, s);
-    case 128: return run_backward<128>(p, a, b, s);
+    case 32: return run_backward<32>(p, a, b, s, ev);
+    case 64: return run_backward<64>(p, a, b, s, ev);
+    case 128: return run_backward<128>(p, a, b, s, ev);
   }
   return hipErrorInvalidValue;
 }

@@ -62,11 +62,15 @@ struct BwdArgs {
 };
 
 // prep + chunk state + exclusive-prefix scan of the records (what the backward needs of the
-// forward's state pass); the reverse scan of a second record set.
-hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s);
+// forward's state pass; `ev`, optional, gets events 0..2 before the three launches); the
+// reverse scan of a second record set.
+hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
 hipError_t launch_scan_suffix(const Plan& p, char* ws, float* states, hipStream_t s);
-// the whole chunked backward (rla2_backward.hip)
-hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s);
+// the whole chunked backward (rla2_backward.hip); `ev` (optional) gets kNumBwdKernels + 1
+// events recorded around the kernels
+constexpr int kNumBwdKernels = 8;
+hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s,
+                           hipEvent_t* ev = nullptr);
 
 // The feature map alone: prep, then q' and k' (either input may be null).
 hipError_t launch_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void* k_out, hipStream_t s);

@@ -1383,12 +1383,12 @@ hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEve
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev) {
   const bool bf = p.dtype == 1;
   switch (p.d) {
-    case 32: return bf ? run_states<true, 32>(p, a, s, nullptr, SCAN_PREFIX) : run_states<false, 32>(p, a, s, nullptr, SCAN_PREFIX);
-    case 64: return bf ? run_states<true, 64>(p, a, s, nullptr, SCAN_PREFIX) : run_states<false, 64>(p, a, s, nullptr, SCAN_PREFIX);
-    case 128: return bf ? run_states<true, 128>(p, a, s, nullptr, SCAN_PREFIX) : run_states<false, 128>(p, a, s, nullptr, SCAN_PREFIX);
+    case 32: return bf ? run_states<true, 32>(p, a, s, ev, SCAN_PREFIX) : run_states<false, 32>(p, a, s, ev, SCAN_PREFIX);
+    case 64: return bf ? run_states<true, 64>(p, a, s, ev, SCAN_PREFIX) : run_states<false, 64>(p, a, s, ev, SCAN_PREFIX);
+    case 128: return bf ? run_states<true, 128>(p, a, s, ev, SCAN_PREFIX) : run_states<false, 128>(p, a, s, ev, SCAN_PREFIX);
   }
   return hipErrorInvalidValue;
 }

@@ -19,7 +19,8 @@ from typing import Optional
 import torch
 
 # stream numbers (fixed order)
-S_LENGTHS, S_MASK_Q, S_MASK_K, S_GAMMA_Q, S_GAMMA_K, S_Q, S_K, S_V, S_PREFIX_K, S_PREFIX_V, S_INIT_S, S_INIT_Z = range(12)
+(S_LENGTHS, S_MASK_Q, S_MASK_K, S_GAMMA_Q, S_GAMMA_K, S_Q, S_K, S_V, S_PREFIX_K, S_PREFIX_V, S_INIT_S, S_INIT_Z,
+ S_DOUT) = range(13)
 
 
 def _gen(seed: int, stream: int, device: str = "cpu") -> torch.Generator:
@@ -62,6 +63,11 @@ def initial_state(H: int, d: int, seed: int, scale: float = 1.0):
     S0 = scale * torch.randn(H, d, d, generator=_gen(seed, S_INIT_S), dtype=torch.float32)
     z0 = scale * torch.randn(H, d, generator=_gen(seed, S_INIT_Z), dtype=torch.float32).abs()
     return S0, z0
+
+
+def cotangent(shape, seed: int, device: str = "cpu") -> torch.Tensor:
+    """A loss gradient dL/dout for the backward: N(0,1) bf16 of the output's shape."""
+    return normal(shape, seed, S_DOUT, torch.bfloat16, device)
 
 
 def cu_from_lengths(lengths) -> torch.Tensor:
