@@ -447,3 +447,75 @@ def test_backward_initial_state_is_a_continuation():
                            initial_pos=40)
     ref = oracle.fwd(q, k, v, gq, gk, cu, initial_S=S0, initial_z=z0, initial_pos=40)
     np.testing.assert_allclose(out.numpy(), ref, rtol=1e-11, atol=1e-13)
+
+
+# --- the original RLA's L2 denominator (RLA page §2.1 closed form, §4.1 A state) -------
+
+@pytest.mark.parametrize("B,H,L,d,lengths", [(1, 2, 11, 6, [4, 7]), (2, 1, 9, 4, None), (1, 1, 8, 8, [1, 0, 7])])
+def test_l2_closed_form_matches_two_state_recurrence(B, H, L, d, lengths):
+    # the direct sum sqrt(sum s^2) against the recurrence through A_t = sum k' k'^T:
+    # catches a missing square or square root, a transposed A, a wrong causal range
+    q, k, v, gq, gk, cu = _rand_case(B, H, L, d, 61, lengths)
+    a = oracle.fwd_l2(q, k, v, gq, gk, cu)
+    b = oracle.fwd_l2_recurrent(q, k, v, gq, gk, cu)
+    np.testing.assert_allclose(a, b, rtol=1e-11, atol=1e-13)
+
+
+def test_l2_first_token_and_equal_keys():
+    # one key: sqrt(s^2) = s, so the first token of a document is s v0 / (s + eps), the Sum
+    # mode's value with the same eps; n identical tokens (same q', k', s; v = u) give
+    # n s u / (sqrt(n) s + eps), i.e. about sqrt(n) u where the Sum mode gives about u
+    r = np.random.default_rng(62)
+    d, n = 8, 9
+    x = np.abs(r.normal(size=(1, 1, 1, d)))   # positive: the supports overlap fully
+    k = np.abs(r.normal(size=(1, 1, 1, d)))
+    u = r.normal(size=d)
+    v = np.broadcast_to(u, (1, 1, n, d)).copy()
+    g = np.ones((1, d))
+    eps = 1e-3
+    # positions 0..n-1 rotate dimension pair 0 by t radians whatever the base, so the tokens
+    # are built unrotated: token t holds R(-t) x, which RoPE turns back into x
+    out = oracle.fwd_l2(*_unrotated_copies(x, k[:, :, :1], n), v, g, g, eps=eps)
+    qp = oracle.feature_map(x[0, 0], g[0], np.zeros(1))[0]
+    kp = oracle.feature_map(k[0, 0], g[0], np.zeros(1))[0]
+    s = qp @ kp
+    assert s > 0
+    for t in range(n):
+        m = t + 1
+        np.testing.assert_allclose(out[0, 0, t], m * s * u / (np.sqrt(m) * s + eps), rtol=1e-9)
+    q2, k2, v2, gq2, gk2, cu2 = _rand_case(1, 2, 12, 6, 63, [5, 7])
+    l2 = oracle.fwd_l2(q2, k2, v2, gq2, gk2, cu2, eps=1e-4)
+    sm = oracle.fwd(q2, k2, v2, gq2, gk2, cu2, eps=1e-4)
+    for t0 in (0, 5):
+        np.testing.assert_allclose(l2[0, :, t0], sm[0, :, t0], rtol=1e-12)
+
+
+def test_l2_cauchy_schwarz_bound_zeros_and_isolation():
+    # |out_tc| <= sqrt(sum_{i<=t} v_ic^2) for every component (Cauchy-Schwarz over the key
+    # sum); disjoint supports give exact zeros; a perturbation of one document changes no
+    # output of another
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 30, 8, 64, [13, 17])
+    out = oracle.fwd_l2(q, k, v, gq, gk, cu)
+    for (b, s0, s1) in oracle.documents(1, 30, cu):
+        bound = np.sqrt(np.cumsum(v[b, :, s0:s1] ** 2, axis=1))
+        assert (np.abs(out[b, :, s0:s1]) <= bound * (1 + 1e-12)).all()
+    k2 = k.copy()
+    k2[:, :, 13:] += 1.0
+    out2 = oracle.fwd_l2(q, k2, v, gq, gk, cu)
+    np.testing.assert_array_equal(out[:, :, :13], out2[:, :, :13])
+    L, d = 24, 8
+    qd, kd, _ = _disjoint_support_inputs(L, d, 3)
+    ones = np.ones((1, d))
+    z = oracle.fwd_l2(qd, kd, RNG.normal(size=(1, 1, L, d)), ones, ones)
+    assert (z == 0).all()
+
+
+def _unrotated_copies(xq, xk, n):
+    """n tokens whose RoPE'd RMSNorm is the same for every position: token t holds the
+    rotation by -t of the unit-RMS x (RMSNorm commutes with the rotation)."""
+    out = []
+    for x in (xq, xk):
+        y = oracle.rms_norm(x[0, 0], np.ones(x.shape[-1]))
+        toks = np.concatenate([oracle.rope_rotate_half(y, np.array([-t])) for t in range(n)])
+        out.append(toks[None, None])
+    return out
