@@ -96,9 +96,19 @@ typedef enum rla2_dtype { RLA2_F32 = 0, RLA2_BF16 = 1 } rla2_dtype;
  *               (>= 0; a continuation passes the length of the context its
  *               initial state summarises). Other documents start at 0.
  *               initial_pos + L must fit in int32 (RLA2_ERR_BAD_VALUE otherwise).
+ *  denominator  RLA2_DEN_SUM (0): the RLA-2 denominator q'_t . z_t + eps (RLA page
+ *               §3). RLA2_DEN_L2 (1): the original RLA's L2 denominator (RLA page
+ *               §2.1), out_t = sum_{i<=t} s_ti v_i / (sqrt(sum_{i<=t} s_ti^2) + eps),
+ *               s_ti = q'_t . k'_i over the same causal same-document range, formed
+ *               from the second state A_t = sum_{i<=t} k'_i k'_i^T (RLA page §4.1):
+ *               sum_i s_ti^2 = q'_t^T A_t q'_t; the page's eps for it is 1e-6. The L2
+ *               mode is a causal forward only: with bidirectional = 1, an initial
+ *               state or initial_pos != 0 the forward returns RLA2_ERR_UNSUPPORTED,
+ *               and so does the backward. The state build ignores it (S and z do not
+ *               depend on the denominator). Other values return RLA2_ERR_BAD_VALUE.
  * The number of documents N is n_docs with cu_seqlens, B without.
  * A zero-initialised descriptor tail (bidirectional = initial_pos = 0, NULL
- * initial state) is the plain causal forward.
+ * initial state, denominator = RLA2_DEN_SUM) is the plain causal forward.
  */
 typedef struct rla2_fwd_desc {
   int32_t B, H, L, d;
@@ -112,7 +122,11 @@ typedef struct rla2_fwd_desc {
   int32_t initial_pos;
   const float* initial_S;
   const float* initial_z;
+  int32_t denominator;
 } rla2_fwd_desc;
+
+#define RLA2_DEN_SUM 0
+#define RLA2_DEN_L2 1
 
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* rla2_status_string(rla2_status status);

@@ -26,6 +26,8 @@ STATUS = {0: "RLA2_OK", 1: "RLA2_ERR_NULL_POINTER", 2: "RLA2_ERR_BAD_SHAPE", 3: 
           4: "RLA2_ERR_BAD_VALUE", 5: "RLA2_ERR_WORKSPACE", 6: "RLA2_ERR_ALIAS", 7: "RLA2_ERR_HIP",
           8: "RLA2_ERR_BAD_SEQLENS", 9: "RLA2_ERR_MISALIGNED"}
 F32, BF16 = 0, 1
+DEN_SUM, DEN_L2 = 0, 1          # rla2_fwd_desc.denominator
+L2_EPS = 1e-6                   # the original RLA's eps (RLA page §2.1)
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 
@@ -42,7 +44,7 @@ class FwdDesc(ctypes.Structure):
                 ("eps", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
                 ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
                 ("bidirectional", ctypes.c_int32), ("initial_pos", ctypes.c_int32),
-                ("initial_S", ctypes.c_void_p), ("initial_z", ctypes.c_void_p)]
+                ("initial_S", ctypes.c_void_p), ("initial_z", ctypes.c_void_p), ("denominator", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -106,11 +108,12 @@ def _stream(dev: torch.device):
 
 
 def make_desc(B, H, L, d, dtype, cu_seqlens=None, n_docs=0, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
-              rope_base=10000.0, bidirectional=False, initial_pos=0, initial_S=None, initial_z=None) -> FwdDesc:
+              rope_base=10000.0, bidirectional=False, initial_pos=0, initial_S=None, initial_z=None,
+              denominator=DEN_SUM) -> FwdDesc:
     return FwdDesc(B, H, L, d, dtype, chunk, seg_chunks, eps, rms_eps, rope_base,
                    None if cu_seqlens is None else cu_seqlens.data_ptr(), n_docs, int(bool(bidirectional)),
                    initial_pos, None if initial_S is None else initial_S.data_ptr(),
-                   None if initial_z is None else initial_z.data_ptr())
+                   None if initial_z is None else initial_z.data_ptr(), denominator)
 
 
 def _initial_state(x: torch.Tensor, initial_S, initial_z):
@@ -126,7 +129,7 @@ def _initial_state(x: torch.Tensor, initial_S, initial_z):
 
 
 def _fwd_desc(x: torch.Tensor, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base, bidirectional=False,
-              initial_pos=0, initial_S=None, initial_z=None) -> FwdDesc:
+              initial_pos=0, initial_S=None, initial_z=None, denominator=DEN_SUM) -> FwdDesc:
     if x.dim() != 4:
         raise ValueError("expected [B, H, L, d]")
     if x.dtype not in _DTYPES:
@@ -138,7 +141,7 @@ def _fwd_desc(x: torch.Tensor, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope
         n_docs = cu_seqlens.numel() - 1
     _initial_state(x, initial_S, initial_z)
     return make_desc(B, H, L, d, _DTYPES[x.dtype], cu_seqlens, n_docs, chunk, seg_chunks, eps, rms_eps, rope_base,
-                     bidirectional, initial_pos, initial_S, initial_z)
+                     bidirectional, initial_pos, initial_S, initial_z, denominator)
 
 
 def fwd_workspace_size(desc: FwdDesc) -> int:
@@ -149,11 +152,15 @@ def fwd_workspace_size(desc: FwdDesc) -> int:
     return n.value
 
 
-def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
+def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=None, rms_eps=1e-6,
         rope_base=10000.0, return_final_state=False, out=None, workspace=None, events=None,
-        bidirectional=False, initial_S=None, initial_z=None, initial_pos=0):
+        bidirectional=False, initial_S=None, initial_z=None, initial_pos=0, l2_denominator=False):
     """Chunked RLA-2 forward (causal, or bidirectional). Returns ``out`` or
     ``(out, final_S, final_z)``.
+
+    ``l2_denominator``: the original RLA's ``sqrt(sum_i s_ti^2) + eps`` in place of the Sum
+    denominator (causal, no initial state or offset). ``eps`` defaults to 1e-4 (Sum) or
+    1e-6 (L2).
 
     ``initial_S [H, d, d]``, ``initial_z [H, d]`` (fp32, optional, together) start the
     first document of each row, whose positions begin at ``initial_pos``.
@@ -163,8 +170,10 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
         _check_dev(n_, t, q.dtype)
     _check_dev("gamma_q", gamma_q, torch.float32)
     _check_dev("gamma_k", gamma_k, torch.float32)
+    if eps is None:
+        eps = L2_EPS if l2_denominator else 1e-4
     desc = _fwd_desc(q, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base, bidirectional, initial_pos,
-                     initial_S, initial_z)
+                     initial_S, initial_z, DEN_L2 if l2_denominator else DEN_SUM)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v shapes differ")
     if gamma_q.shape != (desc.H, desc.d) or gamma_k.shape != (desc.H, desc.d):

@@ -15,7 +15,7 @@ namespace {
 
 using rla2::Plan;
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 static_assert(RLA2_FWD_KERNELS == rla2::kNumFwdKernels, "kernel count of the profiled forward");
 static_assert(RLA2_BWD_KERNELS == rla2::kNumBwdKernels, "kernel count of the profiled backward");
 
@@ -68,6 +68,7 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   if (d->bidirectional != 0 && d->bidirectional != 1) return RLA2_ERR_BAD_VALUE;
   if (d->initial_pos < 0 || (long long)d->initial_pos + d->L > INT32_MAX) return RLA2_ERR_BAD_VALUE;
   if ((d->initial_S == nullptr) != (d->initial_z == nullptr)) return RLA2_ERR_NULL_POINTER;
+  if (d->denominator != RLA2_DEN_SUM && d->denominator != RLA2_DEN_L2) return RLA2_ERR_BAD_VALUE;
   // every token index and every segment index must stay within int32 on device
   const long long tokens = (long long)d->B * d->L;
   if (tokens > INT32_MAX || (long long)d->B * d->H > INT32_MAX) return RLA2_ERR_BAD_SHAPE;
@@ -79,6 +80,7 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   p->d = d->d;
   p->dtype = d->dtype;
   p->bidirectional = d->bidirectional == 1;
+  p->l2 = d->denominator == RLA2_DEN_L2;
   p->initial_pos = d->initial_pos;
   p->packed = d->cu_seqlens != nullptr;
   p->n_docs = p->packed ? d->n_docs : d->B;
@@ -126,6 +128,8 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   p->off_states = off;
   p->bytes_tables = (p->n_docs == 0 || p->H == 0) ? 0 : off;
   off = align_up(off + (size_t)p->n_seg_max * p->H * rec * 4);
+  p->off_astates = off;  // the L2 mode's second record set (A = sum k'k'^T), same layout
+  if (p->l2) off = align_up(off + (size_t)p->n_seg_max * p->H * rec * 4);
   p->bytes = (p->n_docs == 0 || p->H == 0) ? 0 : off;  // no documents or heads: nothing to run
   const size_t tokh = (size_t)rows * p->H * (size_t)p->L;
   p->off_pstates = off;
@@ -209,6 +213,8 @@ rla2_status rla2_fwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
+  // the L2 denominator is built for the plain causal forward only
+  if (p.l2 && (p.bidirectional || desc->initial_S != nullptr || p.initial_pos != 0)) return RLA2_ERR_UNSUPPORTED;
   const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
   const size_t gam = (size_t)p.H * p.d * 4;
   const size_t fsb = (size_t)p.n_docs * p.H * p.d * p.d * 4;
@@ -281,7 +287,7 @@ rla2_status rla2_bwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
-  if (p.dtype != RLA2_BF16 || p.bidirectional) return RLA2_ERR_UNSUPPORTED;
+  if (p.dtype != RLA2_BF16 || p.bidirectional || p.l2) return RLA2_ERR_UNSUPPORTED;
   *bytes = p.bytes_bwd;
   return RLA2_OK;
 }
@@ -301,7 +307,7 @@ rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
-  if (p.dtype != RLA2_BF16 || p.bidirectional) return RLA2_ERR_UNSUPPORTED;
+  if (p.dtype != RLA2_BF16 || p.bidirectional || p.l2) return RLA2_ERR_UNSUPPORTED;
   const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
   const size_t gam = (size_t)p.H * p.d * 4;
   if (act > 0 && (q == nullptr || k == nullptr || v == nullptr || dout == nullptr ||

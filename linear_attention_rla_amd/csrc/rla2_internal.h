@@ -28,7 +28,9 @@ struct Plan {
   int n_seg_max;       // upper bound on segments (grid size of the sweep kernels)
   int n_hi;            // rows of the coarse RoPE table (positions / 64)
   int hi_off;          // 0, or n_hi when the first documents use the offset rows
+  bool l2;             // the original RLA's L2 denominator (second state A = sum k'k'^T)
   size_t off_tab, off_docoff, off_nseg, off_rope_lo, off_rope_hi, off_states;
+  size_t off_astates;  // L2 mode: records of A, after those of S
   size_t bytes;        // total workspace bytes
   size_t bytes_tables; // bytes up to the state records (what the feature map alone needs)
   // backward: a second set of segment records (reverse states); den, gd and the query's

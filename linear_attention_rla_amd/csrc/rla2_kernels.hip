@@ -142,12 +142,15 @@ __global__ __launch_bounds__(1024) void prep_kernel(const int32_t* __restrict__ 
 // the segment sit in LDS and the per-lane RMSNorm weights and in-chunk angles in
 // registers, so no other vector-memory load is ever waited on inside the sweep.
 
-template <bool BF, int D>
-__global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
+// With L2 (the original RLA's denominator) the kernel also accumulates the second state
+// A = sum K'^T K' for the same value-column split, K' standing in for V, into `astates`
+// (same record layout; the z slot is zero).
+template <bool BF, int D, bool L2 = false>
+__global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_state_kernel(
     const typename Elem<BF>::St* __restrict__ k, const typename Elem<BF>::St* __restrict__ v,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg,
     const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi, float* __restrict__ states,
-    int H, int L, float rms_eps) {
+    float* __restrict__ astates, int H, int L, float rms_eps) {
   using G = Geo<BF, D>;
   using St = typename G::St;
   using R = Raw<BF, D>;
@@ -195,11 +198,18 @@ __global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
   };
 
   floatx4 acc[G::RT][G::CT];
+  floatx4 accA[L2 ? G::RT : 1][G::CT];
   floatx4 zc[ZR];
 #pragma unroll
   for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (L2) {
+#pragma unroll
+    for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) accA[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 #pragma unroll
   for (int zr = 0; zr < ZR; ++zr) zc[zr] = floatx4{0.f, 0.f, 0.f, 0.f};
   const bool zwave = wave * ZR < G::RT;
@@ -240,6 +250,20 @@ __global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
 #pragma unroll
           for (int ct = 0; ct < G::CT; ++ct) acc[rt][ct] = mma(a, Vf[ct][kb2], acc[rt][ct]);
         }
+      if constexpr (L2) {  // A += K'^T K' for this wave's columns (K' columns as the value operand)
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          Frag<BF> Kc[G::CT];
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) Kc[ct] = kt_frag(wave * G::CT + ct, kb2);
+#pragma unroll
+          for (int rt = 0; rt < G::RT; ++rt) {
+            const Frag<BF> a = kt_frag(rt, kb2);
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) accA[rt][ct] = mma(a, Kc[ct], accA[rt][ct]);
+          }
+        }
+      }
       if (zwave) {
         const Frag<BF> ones = ones_frag<BF>();
 #pragma unroll
@@ -268,6 +292,18 @@ __global__ __launch_bounds__(NT, 2) void chunk_state_kernel(
   if (zwave && c16 < 4) {  // every column of zc holds the sums of rows 16 rt + 4g + i
 #pragma unroll
     for (int zr = 0; zr < ZR; ++zr) rec[D * D + (wave * ZR + zr) * 16 + 4 * g + c16] = zc[zr][c16];
+  }
+  if constexpr (L2) {
+    float* arec = astates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+    if (wave < G::NW) {
+#pragma unroll
+      for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct)
+          __builtin_nontemporal_store(accA[rt][ct],
+                                      reinterpret_cast<floatx4*>(arec + rec_frag<BF, D>(wave, rt, ct, lane)));
+    }
+    if (tid < D) arec[D * D + tid] = 0.f;
   }
 }
 
@@ -381,14 +417,21 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
 //         S += K'^T V in the accumulators; wave 0 also forms the column sums of K' against a
 //         ones operand and adds them to z.
 // Registers stay under 256 and LDS under 80 KB, so two workgroups share a CU.
+//
+// L2 (the original RLA's denominator, sqrt(sum_i s_ti^2) + eps): the waves also carry the
+// second state A = sum k'k'^T (same column split), the score phase keeps the sum of the
+// squared weights, and a phase between score and out forms q'_t^T A_prev q'_t as
+// A_prev^T Q'^T (the shape of the S^T Q'^T term) dotted with q'_t, summed over the waves in
+// LDS (one more barrier); A advances with K' as the value operand. One workgroup per CU.
 
-template <bool BF, int D>
-__global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
+template <bool BF, int D, bool L2 = false>
+__global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
     const typename Elem<BF>::St* __restrict__ q, const typename Elem<BF>::St* __restrict__ k,
     const typename Elem<BF>::St* __restrict__ v, const float* __restrict__ gamma_q,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg,
     const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi, const float* __restrict__ states,
-    typename Elem<BF>::St* __restrict__ out, int H, int L, float rms_eps, float eps) {
+    const float* __restrict__ astates, typename Elem<BF>::St* __restrict__ out, int H, int L, float rms_eps,
+    float eps) {
   using G = Geo<BF, D>;
   using St = typename G::St;
   using EL = Elem<BF>;
@@ -402,6 +445,8 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
   __shared__ float sZ[D];
   __shared__ float sQz[kChunk];
   __shared__ float sInv[kChunk];
+  __shared__ float sQuad[L2 ? 4 * kChunk : 1];  // L2: each state wave's part of q'^T A_prev q'
+  __shared__ float sRs2[L2 ? kChunk : 1];       // L2: sum of the squared weights
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;
@@ -440,6 +485,16 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
         S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, rt, ct, lane));
   }
   if (tid < D) sZ[tid] = rec[D * D + tid];
+  floatx4 Ak[L2 ? G::RT : 1][G::CT];  // L2: A_prev, this wave's columns
+  if constexpr (L2) {
+    const float* arec = astates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+    const int wv = wave < G::NW ? wave : 0;
+#pragma unroll
+    for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+        Ak[rt][ct] = *reinterpret_cast<const floatx4*>(arec + rec_frag<BF, D>(wv, rt, ct, lane));
+  }
 
   Raw<BF, D> rq, rk, rv;
   {
@@ -499,7 +554,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
       for (int kb2 = 0; kb2 < G::KB; ++kb2) Qf[kb2] = lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g);
       // A^T tiles (rows = keys of tile kt, cols = queries of tile tt), causal: kt <= tt
       floatx4 At[4];
-      float rs = 0.f;
+      float rs = 0.f, rs2 = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -514,15 +569,59 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
             a = EL::to_f(EL::from_f(a));                  // the weight the MFMA will use
             At[kt][i] = a;
             rs += a;
+            if constexpr (L2) rs2 = __builtin_fmaf(a, a, rs2);
           }
         }
       }
       rs = sum_rows4(rs);  // every lane with c16 == t holds the row sum of query 16*tt + t
       sA[(tt * 2) * 64 + lane] = acc_frag<BF>(At[0], At[1]);
       if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<BF>(At[2], At[3]);
-      if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + sQz[tt * 16 + c16] + eps);
+      if constexpr (L2) {
+        rs2 = sum_rows4(rs2);
+        if (g == 0) sRs2[tt * 16 + c16] = rs2;
+      } else {
+        if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + sQz[tt * 16 + c16] + eps);
+      }
     }
     __syncthreads();  // B3: score tiles and row reciprocals in LDS
+
+    if constexpr (L2) {  // ---- q'_t^T A_prev q'_t: this wave's columns a, all 64 queries
+      if (wave < G::NW) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          Frag<BF> Aa[G::KB];  // A_prev^T (= A_prev) rounded to the element type as the A operand
+#pragma unroll
+          for (int kb2 = 0; kb2 < G::KB; ++kb2) Aa[kb2] = acc_frag<BF>(Ak[2 * kb2][ct], Ak[2 * kb2 + 1][ct]);
+          const int col = wave * G::DVW + ct * 16 + 4 * g;
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            floatx4 y = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb2 = 0; kb2 < G::KB; ++kb2) y = mma(Aa[kb2], lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g), y);
+            const St* qrow = sQ + (tt * 16 + c16) * G::ROWP + col;  // q'_t at dims col .. col + 3
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[tt] = __builtin_fmaf(EL::to_f(qrow[i]), y[i], part[tt]);
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const float p = sum_rows4(part[tt]);
+          if (g == 0) sQuad[wave * kChunk + tt * 16 + c16] = p;
+        }
+      }
+      __syncthreads();  // B4: every wave's part of the quadratic form in LDS
+    }
+    auto row_scale = [&](int t) -> float {  // 1 / den of query row t
+      if constexpr (L2) {
+        float quad = sRs2[t];
+#pragma unroll
+        for (int w = 0; w < G::NW; ++w) quad += sQuad[w * kChunk + t];
+        return 1.0f / (__builtin_sqrtf(quad) + eps);
+      } else {
+        return sInv[t];
+      }
+    };
 
     // ---- out, then the state update
     if (wave < G::NW) {
@@ -546,7 +645,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
           o = mma(Vf[ct][0], sA[(tt * 2) * 64 + lane], o);
           if (tt >= 2) o = mma(Vf[ct][1], sA[(tt * 2 + 1) * 64 + lane], o);
           const int t = tt * 16 + c16;  // this lane's query row; columns col .. col + 3
-          const float r = sInv[t];
+          const float r = row_scale(t);
           if (t < nv) {
             St* dst = ob + (size_t)(c0 + t) * D + col;
             if constexpr (BF) {
@@ -574,6 +673,13 @@ __global__ __launch_bounds__(NT, 2) void chunk_out_kernel(
           floatx4 zc = mma(a0, ones, floatx4{0.f, 0.f, 0.f, 0.f});
           zc = mma(a1, ones, zc);  // every column holds the sums of rows 16 rt + 4g + i
           if (c16 < 4) sZ[rt * 16 + 4 * g + c16] += zc[c16];
+        }
+        if constexpr (L2) {  // A += K'^T K' (K' columns of this wave as the value operand)
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) {
+            Ak[rt][ct] = mma(a0, kt_frag(wave * G::CT + ct, 0), Ak[rt][ct]);
+            Ak[rt][ct] = mma(a1, kt_frag(wave * G::CT + ct, 1), Ak[rt][ct]);
+          }
         }
       }
     }
@@ -1288,10 +1394,19 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
                      p.seg_len, p.n_seg_max, tab, docoff, nseg, rlo, rhi, half, D, p.n_hi, p.hi_off, p.initial_pos,
                      a.rope_base);
   mark(1);
+  // the L2 forward also needs the records of A = sum k'k'^T
+  const bool l2 = p.l2 && a.out != nullptr;
+  float* astates = reinterpret_cast<float*>(a.ws + p.off_astates);
   if (p.n_seg_max > 0) {
-    hipLaunchKernelGGL((chunk_state_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
-                       static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
-                       states, p.H, p.L, a.rms_eps);
+    if (l2) {
+      hipLaunchKernelGGL((chunk_state_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                         static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
+                         states, astates, p.H, p.L, a.rms_eps);
+    } else {
+      hipLaunchKernelGGL((chunk_state_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                         static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
+                         states, static_cast<float*>(nullptr), p.H, p.L, a.rms_eps);
+    }
   }
   mark(2);
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
@@ -1299,6 +1414,11 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
   if (want_final || (mode != SCAN_NONE && p.n_seg_max > 0)) {
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
                        n_tiles, mode, a.final_S, a.final_z, a.init_S, a.init_z, p.packed ? 0 : 1);
+  }
+  if (l2 && mode == SCAN_PREFIX && p.n_seg_max > 0) {  // exclusive prefixes of A as well
+    hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, astates, docoff, p.H, D,
+                       n_tiles, (int)SCAN_PREFIX, (float*)nullptr, (float*)nullptr, (const float*)nullptr,
+                       (const float*)nullptr, 0);
   }
   return hipGetLastError();
 }
@@ -1322,6 +1442,11 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   if (fwd && p.n_seg_max > 0 && p.bidirectional) {
     hipLaunchKernelGGL((readout_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s, static_cast<const St*>(a.q),
                        a.gq, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+  } else if (fwd && p.n_seg_max > 0 && p.l2) {
+    hipLaunchKernelGGL((chunk_out_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                       static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
+                       a.gk, tab, nseg, rlo, rhi, states, reinterpret_cast<const float*>(a.ws + p.off_astates),
+                       static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
   } else if (fwd && p.n_seg_max > 0) {
     if constexpr (BF) {
       hipLaunchKernelGGL((chunk_out_ws_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
@@ -1330,7 +1455,8 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
     } else {
       hipLaunchKernelGGL((chunk_out_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                          static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
-                         a.gk, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+                         a.gk, tab, nseg, rlo, rhi, states, static_cast<const float*>(nullptr),
+                         static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
     }
   }
   mark(4);

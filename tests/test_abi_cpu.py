@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = rla.lib()
-    assert L.rla2_abi_version() == 2
+    assert L.rla2_abi_version() == 3
     for code, name in rla.STATUS.items():
         assert L.rla2_status_string(code).decode().startswith(name)
     assert L.rla2_status_string(99).decode() == "RLA2_ERR_UNKNOWN"
@@ -74,6 +74,7 @@ def ws_size(d):
     (dict(B=1 << 16, L=1 << 16), SHAPE),
     (dict(bidirectional=2), VALUE), (dict(bidirectional=-1), VALUE), (dict(initial_pos=-1), VALUE),
     (dict(initial_pos=(1 << 31) - 300), VALUE), (dict(initial_S=A), NULLP), (dict(initial_z=A), NULLP),
+    (dict(denominator=2), VALUE), (dict(denominator=-1), VALUE),
 ])
 def test_desc_validation(kw, expect):
     assert ws_size(desc(**kw))[0] == expect
@@ -118,6 +119,23 @@ def test_fwd_error_paths():
     assert fwd_call(desc(**init), fz=A + 401 * MB) == ALIAS      # final state over the initial state
     assert fwd_call(desc(initial_S=A + 512 * MB, initial_z=A + 401 * MB)) == ALIAS  # inside the workspace
     assert desc(**init).initial_S == A + 400 * MB
+
+
+def test_l2_denominator_paths():
+    # the L2 mode needs a second record set (A = sum k'k'^T): a larger workspace; it is a plain
+    # causal forward only, and the backward rejects it
+    st, plain = ws_size(desc())
+    st2, l2 = ws_size(desc(denominator=rla.DEN_L2))
+    assert st == st2 == OK and l2 > plain
+    assert fwd_call(desc(denominator=rla.DEN_L2), ws_bytes=plain) == WS
+    assert fwd_call(desc(denominator=rla.DEN_L2, bidirectional=1)) == UNSUP
+    assert fwd_call(desc(denominator=rla.DEN_L2, initial_pos=5)) == UNSUP
+    assert fwd_call(desc(denominator=rla.DEN_L2, initial_S=A + 400 * MB, initial_z=A + 401 * MB)) == UNSUP
+    n = ctypes.c_size_t(0)
+    assert rla.lib().rla2_bwd_workspace_size(ctypes.byref(desc(denominator=rla.DEN_L2)), ctypes.byref(n)) == UNSUP
+    # the state build does not depend on the denominator
+    assert rla.lib().rla2_state_from_prefix(ctypes.byref(desc(denominator=rla.DEN_L2, B=0)), None, None, None, None,
+                                            None, None, 0, None) == OK
 
 
 def test_fwd_empty_work_is_noop_without_gpu():

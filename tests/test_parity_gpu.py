@@ -104,11 +104,11 @@ def test_packed_equals_unpacked_bitwise():
         s0 += n
 
 
-def test_disjoint_supports_give_exact_zero():
-    # q' positive only on channels A and k' only off A (after RoPE): every score is 0,
-    # so every output is exactly 0 (RLA page §1/§2.2).
-    L, d = 200, 64
-    r = np.random.default_rng(3)
+def disjoint_qk(L, d, seed=3):
+    """bf16 q, k [1, 1, L, d] (on the GPU) whose features have disjoint positive supports:
+    after RoPE, q is positive exactly on a seeded half A of the channels and k exactly off A
+    (each token is built as the inverse rotation of the wanted pattern)."""
+    r = np.random.default_rng(seed)
     h = d // 2
     mask = np.zeros(d, bool)
     mask[r.permutation(d)[: d // 2]] = True
@@ -121,9 +121,15 @@ def test_disjoint_supports_give_exact_zero():
             u = np.where(mask, sign * mag[0 if sign > 0 else 1], -sign * mag[0 if sign > 0 else 1])
             zc = (u[:h] + 1j * u[h:]) * np.exp(-1j * t * theta)
             x[0, 0, t] = np.concatenate([zc.real, zc.imag])
+    return (torch.tensor(q, dtype=torch.bfloat16, device=DEV), torch.tensor(k, dtype=torch.bfloat16, device=DEV))
+
+
+def test_disjoint_supports_give_exact_zero():
+    # q' positive only on channels A and k' only off A (after RoPE): every score is 0,
+    # so every output is exactly 0 (RLA page §1/§2.2).
+    L, d = 200, 64
+    qt, kt = disjoint_qk(L, d)
     g = torch.ones(1, d, device=DEV)
-    qt = torch.tensor(q, dtype=torch.bfloat16, device=DEV)
-    kt = torch.tensor(k, dtype=torch.bfloat16, device=DEV)
     vt = torch.randn(1, 1, L, d, device=DEV).to(torch.bfloat16)
     out = rla.fwd(qt, kt, vt, g, g, seg_chunks=1)
     torch.cuda.synchronize()
