@@ -125,8 +125,9 @@ def cpu_baseline(inp, budget_s):
 
 def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc):
     """The same long-context workload in the bidirectional mode (every token reads its
-    document's whole state; the output kernel is the read-out) and as a continuation
-    (causal, from a synthetic initial state, positions starting at 65536)."""
+    document's whole state; the output kernel is the read-out), as a continuation
+    (causal, from a synthetic initial state, positions starting at 65536), and with the
+    original RLA's L2 denominator (second state A = sum k'k'^T, eps 1e-6)."""
     import workloads
     B, H, L, d = q.shape
     steps = min(args.steps, 20)
@@ -135,11 +136,16 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
     modes = {
         "bidirectional": dict(bidirectional=True),
         "continuation": dict(initial_S=S0, initial_z=z0, initial_pos=L),
+        "l2_denominator": dict(l2_denominator=True),
     }
+    l2_desc = rla.make_desc(B, H, L, d, rla.BF16, seg_chunks=args.seg_chunks, denominator=rla.DEN_L2)
+    ws_l2 = torch.empty(rla.fwd_workspace_size(l2_desc), dtype=torch.uint8, device=q.device)
     res = {}
     for name, kw in modes.items():
+        wsm = ws_l2 if name == "l2_denominator" else ws
+
         def run(events=None):
-            rla.fwd(q, k, v, gq, gk, seg_chunks=args.seg_chunks, out=out, workspace=ws, events=events, **kw)
+            rla.fwd(q, k, v, gq, gk, seg_chunks=args.seg_chunks, out=out, workspace=wsm, events=events, **kw)
         for _ in range(5):
             run()
         torch.cuda.synchronize()
@@ -171,6 +177,8 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
     res["bidirectional"]["workload"] = "long-context bidirectional forward, B=1 H=32 L=65536 d=128 bf16"
     res["continuation"]["workload"] = ("long-context causal forward continuing a 65536-token context "
                                        "(initial state per head, positions 65536..131071)")
+    res["l2_denominator"]["workload"] = ("long-context causal forward with the L2 denominator "
+                                         "sqrt(sum s^2) + 1e-6, B=1 H=32 L=65536 d=128 bf16")
     return res
 
 
