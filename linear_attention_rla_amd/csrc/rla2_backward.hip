@@ -265,18 +265,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
     dg2[e] = 0.f;
   }
   const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * E;
-  R xq, xk, xv, xg;
-  float2 hi[E];
-  auto load_q = [&](int c) {
-    copy_bytes<E * 8>(hi, hi0 + (size_t)c * G::HALF);
-    load_raw_buf<true, D>(xq, rq, c * kChunk + t0, m);
+  // raw q and its RoPE row are needed again by the map backward (P3), so chunk c + 1's go
+  // into a second set, issued with the other loads right after P1 and moved over at the end
+  R xq, xk, xv, xg, xqn;
+  float2 hi[E], hin[E];
+  auto load_q = [&](R& x, float2 (&hr)[E], int c) {
+    copy_bytes<E * 8>(hr, hi0 + (size_t)min(c, nch - 1) * G::HALF);
+    load_raw_buf<true, D>(x, rq, c * kChunk + t0, m);
   };
   auto load_rest = [&](int c) {
     load_raw_buf<true, D>(xk, rk, c * kChunk + t0, m);
     load_raw_buf<true, D>(xv, rv, c * kChunk + t0, m);
     load_raw_buf<true, D>(xg, rg, c * kChunk + t0, m);
   };
-  load_q(0);
+  load_q(xq, hi, 0);
   load_rest(0);
   __syncthreads();  // z, S^T in LDS
 
@@ -316,7 +318,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
         if (m == 0) sQz[t0 + tok] = qz;
       }
     }
-    if (c + 1 < nch) load_rest(c + 1);  // k, v, dout are in LDS now
+    // chunk c + 1's inputs (past the end: the range check reads zeros); k, v, dout are in LDS
+    load_rest(c + 1);
+    load_q(xqn, hin, c + 1);
     __syncthreads();  // B1
 
     floatx4 X[RT];  // S g, then dQ'^T: rows a = 16 at + 4g + i, this lane's query
@@ -457,7 +461,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];
     }
-    if (c + 1 < nch) load_q(c + 1);
+    xq = xqn;
+#pragma unroll
+    for (int e = 0; e < E; ++e) hi[e] = hin[e];
     __syncthreads();  // B3
   }
   reduce_dgamma<D>(sdQ, dg_part + ((size_t)seg * H + h) * 2 * D, tid, dg1, dg2);
@@ -517,18 +523,21 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
   for (int z = 0; z < ZR; ++z) pz[z] = floatx4{0.f, 0.f, 0.f, 0.f};
   const bool zwave = wave * ZR < RT;
 
-  for (int c = 0; c < nch; ++c) {
-    R xq, xg;
-    float2 hi[E];
-    copy_bytes<E * 8>(hi, hi0 + (size_t)c * G::HALF);
+  R xq, xg;
+  float2 hi[E];
+  float dn[2], w[2];
+  auto issue = [&](int c) {  // chunk c's inputs; tokens past the segment read 0 and weigh nothing
+    copy_bytes<E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);
     load_raw_buf<true, D>(xq, rq, c * kChunk + t0, m);
     load_raw_buf<true, D>(xg, rg, c * kChunk + t0, m);
-    float dn[2], w[2];
 #pragma unroll
-    for (int tok = 0; tok < 2; ++tok) {  // tokens past the segment read 0 and weigh nothing
+    for (int tok = 0; tok < 2; ++tok) {
       dn[tok] = load_tok(rd, c * kChunk + t0 + tok);
       w[tok] = load_tok(rw, c * kChunk + t0 + tok);
     }
+  };
+  issue(0);
+  for (int c = 0; c < nch; ++c) {
     __syncthreads();  // the previous chunk's operands are consumed
     {
       R oq, oh;
@@ -542,6 +551,7 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
         sW[t0 + 1] = w[1] * dn[1];
       }
     }
+    issue(c + 1);  // into the registers just consumed: in flight during the MFMA work
     __syncthreads();
     if (wave < G::NW) {
       Frag<true> Nf[CT][2];
@@ -673,12 +683,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
     dg2[e] = 0.f;
   }
   const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * E;
-  R xq, xk, xv, xg;
-  float2 hi[E];
+  // raw k and its RoPE row are needed again by the map backward (P3): chunk c - 1's go into
+  // a second set, issued right after P1 and moved over at the end of the step
+  R xq, xk, xv, xg, xkn;
+  float2 hi[E], hin[E];
   float dn[2], gdl[2], bdl[2];
-  auto load_k = [&](int c) {
-    copy_bytes<E * 8>(hi, hi0 + (size_t)c * G::HALF);
-    load_raw_buf<true, D>(xk, rk, c * kChunk + t0, m);
+  auto load_k = [&](R& x, float2 (&hr)[E], int c) {
+    copy_bytes<E * 8>(hr, hi0 + (size_t)max(c, 0) * G::HALF);
+    load_raw_buf<true, D>(x, rk, c * kChunk + t0, m);
   };
   auto load_rest = [&](int c) {
     load_raw_buf<true, D>(xq, rq, c * kChunk + t0, m);
@@ -691,7 +703,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
       bdl[tok] = load_tok(rb, c * kChunk + t0 + tok);
     }
   };
-  load_k(nch - 1);
+  load_k(xk, hi, nch - 1);
   load_rest(nch - 1);
   __syncthreads();  // p, P^T in LDS
 
@@ -733,7 +745,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
         }
       }
     }
-    if (c > 0) load_rest(c - 1);
+    if (c > 0) {
+      load_rest(c - 1);
+      load_k(xkn, hin, c - 1);
+    }
     __syncthreads();  // B1
 
     floatx4 Y[RT];  // dK'^T: rows a = 16 at + 4g + i, this lane's key
@@ -858,7 +873,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       for (int i = lane; i < D; i += 64) sP[i] += sDp[i];
     }
-    if (c > 0) load_k(c - 1);
+    if (c > 0) {
+      xk = xkn;
+#pragma unroll
+      for (int e = 0; e < E; ++e) hi[e] = hin[e];
+    }
     __syncthreads();  // B3
   }
   reduce_dgamma<D>(sdK, dg_part + ((size_t)seg * H + h) * 2 * D + D, tid, dg1, dg2);
