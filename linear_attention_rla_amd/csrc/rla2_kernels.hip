@@ -720,11 +720,13 @@ __device__ __forceinline__ void mma_wave_sync(unsigned* cnt, unsigned target, in
 // packed weights with a bf16 dot against ones, so numerator and denominator use the same
 // weights. The wave also forms the column sums of K' for row tiles [Z0, Z1). Every LDS
 // operand is requested before the first MFMA.
-template <int D, int TT, int Z0, int Z1>
+// L2: no q'.z and no column sums; the row's sum of squared weights goes to sInv instead.
+template <int D, int TT, int Z0, int Z1, bool L2 = false>
 __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK, const Frag<true>* sZf,
                                          Frag<true>* sA, float* sInv, float* sDz, float eps, int lane) {
   using G = Geo<true, D>;
   constexpr int KB = G::KB, NZ = Z1 - Z0, NP = TT / 2 + 1;
+  static_assert(!L2 || NZ == 0, "");
   const int c16 = lane & 15, g = lane >> 4;
   Frag<true> Qf[KB], Kf[TT + 1][KB], Zf[KB], Ct[NZ > 0 ? NZ : 1][2];
 #pragma unroll
@@ -733,8 +735,10 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
   for (int kt = 0; kt <= TT; ++kt)
 #pragma unroll
     for (int kb2 = 0; kb2 < KB; ++kb2) Kf[kt][kb2] = lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb2, g);
+  if constexpr (!L2) {
 #pragma unroll
-  for (int kb2 = 0; kb2 < KB; ++kb2) Zf[kb2] = sZf[kb2 * 64 + lane];
+    for (int kb2 = 0; kb2 < KB; ++kb2) Zf[kb2] = sZf[kb2 * 64 + lane];
+  }
 #pragma unroll
   for (int z = 0; z < NZ; ++z) {
     Ct[z][0] = lds_frag_tr(cK, G::ROWP, 0, 16 * (Z0 + z), lane);
@@ -748,7 +752,7 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
   for (int kb2 = 0; kb2 < KB; ++kb2) {
 #pragma unroll
     for (int kt = 0; kt <= TT; ++kt) At[kt] = mma(Kf[kt][kb2], Qf[kb2], At[kt]);
-    zq = mma(Zf[kb2], Qf[kb2], zq);
+    if constexpr (!L2) zq = mma(Zf[kb2], Qf[kb2], zq);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -769,13 +773,19 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
 #pragma unroll
   for (int b = 0; b < NP; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[b][i]), ones2, rs, false);
-  if (g == 0) rs += zq[0] + zq[1];  // q'.z of query 16 TT + c16 (rows 0, 1 of Z Q'^T)
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 w2 = __builtin_bit_cast(bf16x2, pw[b][i]);
+      // Sum: the weights against ones; L2: the weights against themselves (sum of squares)
+      rs = __builtin_amdgcn_fdot2_f32_bf16(w2, L2 ? w2 : ones2, rs, false);
+    }
+  if constexpr (!L2) {
+    if (g == 0) rs += zq[0] + zq[1];  // q'.z of query 16 TT + c16 (rows 0, 1 of Z Q'^T)
+  }
   rs = sum_rows4(rs);  // lanes with c16 == t: row sum + q'.z of query 16 TT + t
 #pragma unroll
   for (int b = 0; b < NP; ++b)
     *reinterpret_cast<u32x4*>(&sA[(TT * 2 + b) * 64 + lane]) = u32x4{pw[b][0], pw[b][1], pw[b][2], pw[b][3]};
-  if (g == 0) sInv[TT * 16 + c16] = 1.0f / (rs + eps);
+  if (g == 0) sInv[TT * 16 + c16] = L2 ? rs : 1.0f / (rs + eps);
   if constexpr (NZ > 0) {
     const Frag<true> ones = ones_frag<true>();
 #pragma unroll
@@ -787,12 +797,20 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
   }
 }
 
-template <int D>
+// L2 (the original RLA's denominator sqrt(sum_i s_ti^2) + eps): the mapper waves also own the
+// second state A = sum k'k'^T (value-column split as S, mapper m holding the columns of MMA
+// wave m). In step st, after mapping chunk st, they form chunk st - 1's q'^T A_prev q' as
+// A_prev^T Q'^T dotted with q' (their parts go to LDS) and advance A with its K'; the MMA
+// waves write that chunk's numerators unnormalised and keep the rows' sums of squared
+// weights; one step later the mappers scale each output row by 1 / (sqrt(sum) + eps) as they
+// store it. Nothing new waits inside a step.
+template <int D, bool L2 = false>
 __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ gamma_q, const float* __restrict__ gamma_k, const int32_t* __restrict__ tab,
     const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
-    const float* __restrict__ states, uint16_t* __restrict__ out, int H, int L, float rms_eps, float eps) {
+    const float* __restrict__ states, const float* __restrict__ astates, uint16_t* __restrict__ out, int H, int L,
+    float rms_eps, float eps) {
   using G = Geo<true, D>;
   using St = uint16_t;
   using EL = Elem<true>;
@@ -810,6 +828,11 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   // Z Q'^T gives q'.z (to ~2^-17 relative) in rows 0 + 1 of each query column
   __shared__ Frag<true> sZf[G::KB * 64];
   __shared__ unsigned sArrive;  // MMA-wave arrivals (mma_wave_sync)
+  // L2, by step parity: rows' sums of squared weights (MMA waves) and the mappers' parts of
+  // q'^T A_prev q', for the chunk the MMA waves processed in that step
+  __shared__ float sRs2[L2 ? 2 * kChunk : 1];
+  __shared__ float sQuad[L2 ? 2 * 4 * kChunk : 1];
+  __shared__ float sGam[L2 ? 2 * D : 1];  // L2: the mappers read the RMSNorm weights here
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;  // the whole workgroup leaves together
@@ -846,6 +869,9 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     }
   };
   for (int i = tid; i < G::KB * 64; i += 512) sZf[i] = Frag<true>{};
+  if constexpr (L2) {
+    for (int i = tid; i < 2 * D; i += 512) sGam[i] = i < D ? gamma_q[(size_t)h * D + i] : gamma_k[(size_t)h * D + i - D];
+  }
   __syncthreads();
   if (wave == 0) put_zf(rec + D * D);
   __syncthreads();
@@ -859,17 +885,36 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + tok0 * D), 0, seg_bytes, kBufFlags);
     // per-lane constants: RMSNorm weights of this lane's dims, in-chunk RoPE angles of its tokens
-    float gq1[G::E], gq2[G::E], gk1[G::E], gk2[G::E];
+    // (L2: the weights are read from LDS at each use, which frees their registers for A)
+    constexpr int GE = L2 ? 1 : G::E;
+    float gq1[GE], gq2[GE], gk1[GE], gk2[GE];
     float2 lo[2][G::E];
 #pragma unroll
     for (int e = 0; e < G::E; ++e) {
       const int j = m * G::E + e;
-      gq1[e] = gamma_q[(size_t)h * D + j];
-      gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
-      gk1[e] = gamma_k[(size_t)h * D + j];
-      gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
+      if constexpr (!L2) {
+        gq1[e] = gamma_q[(size_t)h * D + j];
+        gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
+        gk1[e] = gamma_k[(size_t)h * D + j];
+        gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
+      }
       lo[0][e] = rope_lo[t0 * G::HALF + j];
       lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
+    }
+    auto gam = [&](const float (&reg)[GE], int base, int e) -> float {  // weight of dim base + m E + e
+      if constexpr (L2) return sGam[base + m * G::E + e];
+      else return reg[e];
+    };
+    const int mw = wave - 4;  // L2: this mapper's A columns are those of MMA wave mw
+    floatx4 Am[L2 ? G::RT : 1][G::CT];
+    if constexpr (L2) {
+      const float* arec = astates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+      const int wv = mw < G::NW ? mw : 0;
+#pragma unroll
+      for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct)
+          Am[rt][ct] = *reinterpret_cast<const floatx4*>(arec + rec_frag<true, D>(wv, rt, ct, lane));
     }
     // Every step issues the same loads (chunks past the end read zeros from the buffer
     // range check), so the compiler's wait counts let chunk st + 1 stay in flight while
@@ -895,8 +940,10 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
               const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
-              rope_pair(r[0].get(tok, 0, e + x), r[0].get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs, q1[x], q2[x]);
-              rope_pair(r[1].get(tok, 0, e + x), r[1].get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs, k1[x], k2[x]);
+              rope_pair(r[0].get(tok, 0, e + x), r[0].get(tok, 1, e + x), invq, gam(gq1, 0, e + x),
+                        gam(gq2, G::HALF, e + x), cs, q1[x], q2[x]);
+              rope_pair(r[1].get(tok, 0, e + x), r[1].get(tok, 1, e + x), invk, gam(gk1, D, e + x),
+                        gam(gk2, D + G::HALF, e + x), cs, k1[x], k2[x]);
             }
             put_pairs<true, D>(oq, tok, e, q1, q2);
             put_pairs<true, D>(ok, tok, e, k1, k2);
@@ -918,20 +965,79 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
         for (int i = 0; i < kChunk / (4 * RPI); ++i) {
           const int rr = (i * 4 + wave - 4) * RPI + lane / PPR, pc = lane % PPR;
           const int off = any ? ((cw * kChunk + rr) * D + pc * 8) * 2 : seg_bytes;
-          __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(so + rr * G::ROWP + pc * 8), ro, off, 0,
-                                                 kLoadStream);
+          u32x4 piece = *reinterpret_cast<const u32x4*>(so + rr * G::ROWP + pc * 8);
+          if constexpr (L2) {  // the row's 1 / (sqrt(sum of squared scores) + eps), from step st - 1
+            const int par = (st + 1) & 1;
+            float quad = sRs2[par * kChunk + rr];
+#pragma unroll
+            for (int w = 0; w < G::NW; ++w) quad += sQuad[(par * 4 + w) * kChunk + rr];
+            const float rsc = 1.0f / (__builtin_sqrtf(quad) + eps);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              piece[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                  float2v{__uint_as_float(piece[j] << 16) * rsc, __uint_as_float(piece[j] & 0xffff0000u) * rsc}, bf16x2));
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(piece, ro, off, 0, kLoadStream);
         }
       }
-      issue(r, hi, st + 2);  // into the registers just consumed
+      issue(r, hi, st + (L2 ? 1 : 2));  // into the registers just consumed
+      if constexpr (L2) {  // chunk st - 1 (the MMA waves' chunk of this step): A-side of its denominators
+        const int cc = st - 1;
+        if (cc >= 0 && cc < nch && mw < G::NW) {
+          const St* cQ = sQ + ((st + 1) & 1) * BUF;
+          const St* cK = sK + ((st + 1) & 1) * BUF;
+          const int c16 = lane & 15, g = lane >> 4;
+          // one query tile at a time (a rolled loop keeps the mappers' registers for A)
+#pragma unroll 1
+          for (int tt = 0; tt < 4; ++tt) {
+            float part = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) {
+              floatx4 y = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int kb2 = 0; kb2 < G::KB; ++kb2)  // A_prev (symmetric) rounded to bf16 as the A operand
+                y = mma(acc_frag<true>(Am[2 * kb2][ct], Am[2 * kb2 + 1][ct]),
+                        lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb2, g), y);
+              const int col = mw * G::DVW + ct * 16 + 4 * g;
+              const uint2 qa = *reinterpret_cast<const uint2*>(cQ + (tt * 16 + c16) * G::ROWP + col);
+              part = __builtin_fmaf(__uint_as_float(qa.x << 16), y[0], part);
+              part = __builtin_fmaf(__uint_as_float(qa.x & 0xffff0000u), y[1], part);
+              part = __builtin_fmaf(__uint_as_float(qa.y << 16), y[2], part);
+              part = __builtin_fmaf(__uint_as_float(qa.y & 0xffff0000u), y[3], part);
+            }
+            part = sum_rows4(part);
+            if (g == 0) sQuad[((st & 1) * 4 + mw) * kChunk + tt * 16 + c16] = part;
+          }
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2) {  // A += K'^T K' (this mapper's columns)
+            Frag<true> Kc[G::CT];
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) Kc[ct] = lds_frag_tr(cK, G::ROWP, 32 * kb2, mw * G::DVW + ct * 16, lane);
+#pragma unroll
+            for (int rt = 0; rt < G::RT; ++rt) {
+              const Frag<true> a = lds_frag_tr(cK, G::ROWP, 32 * kb2, 16 * rt, lane);
+#pragma unroll
+              for (int ct = 0; ct < G::CT; ++ct) Am[rt][ct] = mma(a, Kc[ct], Am[rt][ct]);
+            }
+          }
+        }
+      }
       __syncthreads();  // Y
     };
-    R set0[3], set1[3];
-    float2 hi0r[G::E], hi1r[G::E];
-    issue(set0, hi0r, 0);
-    issue(set1, hi1r, 1);
-    for (int st = 0; st < nsteps; st += 2) {
-      mstep(st, set0, hi0r);
-      mstep(st + 1, set1, hi1r);
+    if constexpr (L2) {  // the A state takes the registers of the second chunk in flight
+      R set0[3];
+      float2 hi0r[G::E];
+      issue(set0, hi0r, 0);
+      for (int st = 0; st < nsteps; ++st) mstep(st, set0, hi0r);
+    } else {
+      R set0[3], set1[3];
+      float2 hi0r[G::E], hi1r[G::E];
+      issue(set0, hi0r, 0);
+      issue(set1, hi1r, 1);
+      for (int st = 0; st < nsteps; st += 2) {
+        mstep(st, set0, hi0r);
+        mstep(st + 1, set1, hi1r);
+      }
     }
     return;
   }
@@ -957,16 +1063,26 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const int c = st - 1;
     const bool work = st >= 1 && st <= nch;  // uniform over the MMA waves
     if (work) {  // ---- score: wave w owns query tile w
-      switch (wave) {
-        case 0: ws_score<D, 0, 0, ZS>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
-        case 1: ws_score<D, 1, ZS, G::RT>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
-        case 2: ws_score<D, 2, 0, 0>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
-        default: ws_score<D, 3, 0, 0>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+      if constexpr (L2) {
+        float* rs2 = sRs2 + (st & 1) * kChunk;
+        switch (wave) {
+          case 0: ws_score<D, 0, 0, 0, true>(cQ, cK, sZf, sA, rs2, sDz, eps, lane); break;
+          case 1: ws_score<D, 1, 0, 0, true>(cQ, cK, sZf, sA, rs2, sDz, eps, lane); break;
+          case 2: ws_score<D, 2, 0, 0, true>(cQ, cK, sZf, sA, rs2, sDz, eps, lane); break;
+          default: ws_score<D, 3, 0, 0, true>(cQ, cK, sZf, sA, rs2, sDz, eps, lane); break;
+        }
+      } else {
+        switch (wave) {
+          case 0: ws_score<D, 0, 0, ZS>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+          case 1: ws_score<D, 1, ZS, G::RT>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+          case 2: ws_score<D, 2, 0, 0>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+          default: ws_score<D, 3, 0, 0>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+        }
       }
     }
     mma_wave_sync(&sArrive, 4u * (unsigned)(st + 1), lane);
     if (work && wave < G::NW) {  // ---- output, then the state update
-      if (wave == 0) {  // every q'.z of this chunk is done: advance z and its operand
+      if (!L2 && wave == 0) {  // every q'.z of this chunk is done: advance z and its operand
         for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -1015,7 +1131,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int t = tt * 16 + c16;  // this lane's query row
-        const float rr = sInv[t];
+        const float rr = L2 ? 1.0f : sInv[t];  // L2: the mappers normalise at the store
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct) {  // columns col .. col + 3
           const int col = wave * G::DVW + ct * 16 + 4 * g;
@@ -1443,15 +1559,24 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
     hipLaunchKernelGGL((readout_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s, static_cast<const St*>(a.q),
                        a.gq, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
   } else if (fwd && p.n_seg_max > 0 && p.l2) {
-    hipLaunchKernelGGL((chunk_out_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
-                       static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
-                       a.gk, tab, nseg, rlo, rhi, states, reinterpret_cast<const float*>(a.ws + p.off_astates),
-                       static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+    const float* astates = reinterpret_cast<const float*>(a.ws + p.off_astates);
+    if constexpr (BF) {
+      hipLaunchKernelGGL((chunk_out_ws_kernel<D, true>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
+                         static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
+                         a.gk, tab, nseg, rlo, rhi, states, astates, static_cast<St*>(a.out), p.H, p.L, a.rms_eps,
+                         a.eps);
+    } else {
+      hipLaunchKernelGGL((chunk_out_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                         static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
+                         a.gk, tab, nseg, rlo, rhi, states, astates, static_cast<St*>(a.out), p.H, p.L, a.rms_eps,
+                         a.eps);
+    }
   } else if (fwd && p.n_seg_max > 0) {
     if constexpr (BF) {
       hipLaunchKernelGGL((chunk_out_ws_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
                          static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
-                         a.gk, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+                         a.gk, tab, nseg, rlo, rhi, states, static_cast<const float*>(nullptr),
+                         static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
     } else {
       hipLaunchKernelGGL((chunk_out_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                          static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
