@@ -165,15 +165,17 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
         t_out = per[KERNELS.index("chunk_out")]
         if name == "bidirectional":  # read-out: q read and out written once, bf16
             nbytes = B * H * L * d * 2 * 2
-            kern = "readout"
+            kern, traffic = "readout", measured_traffic("readout_kernel")
         else:
             nbytes = fwd_algorithmic(B, H, L, d)[1]
             kern = "chunk_out"
+            traffic = measured_traffic("chunk_out_ws_kernel_l2" if name == "l2_denominator" else "chunk_out_ws_kernel")
         gbs = nbytes / (t_out * 1e-3) / 1e9
         res[name] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3), "steps": steps,
                      "kernel_ms": dict(zip(KERNELS[:-1] + [kern], per)),
                      "roofline": {"kernel": kern, "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes}}
+                                  "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
+                                  "traffic": traffic}}
     res["bidirectional"]["workload"] = "long-context bidirectional forward, B=1 H=32 L=65536 d=128 bf16"
     res["continuation"]["workload"] = ("long-context causal forward continuing a 65536-token context "
                                        "(initial state per head, positions 65536..131071)")
@@ -207,7 +209,7 @@ def time_prologue(args, rla, torch, hip, ev, stream, q, k, gq, gk):
             "ms_per_call": ms, "steps": steps,
             "roofline": {"kernel": "feature_map (with the set-up launch)", "bound": "hbm", "achieved": gbs,
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                         "algorithmic_bytes": nbytes}}
+                         "algorithmic_bytes": nbytes, "traffic": measured_traffic("feature_map_kernel")}}
 
 
 BWD_KERNELS = ["prep", "chunk_state", "state_scan", "bwd_dq", "bwd_pstate", "suffix_scan", "bwd_dkv", "bwd_dgamma"]
