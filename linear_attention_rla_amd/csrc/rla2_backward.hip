@@ -22,7 +22,8 @@
 //
 // Chunked like the forward (C = 64 tokens, documents cut into segments of whole chunks):
 //   (forward state pass)  prefix records of S, z per (segment, head)
-//   bwd_dq       per (segment, head), chunks in order, S and z running:
+//   bwd_dq_ws    per (segment, head), 32-token steps in order, S and z running (warp-
+//                specialised: mappers for q', k' and for the map backward, MMA waves between):
 //                  A^T = mask(K' Q'^T), Bv^T = V G^T (keys x queries), den, g . num, gd, B_tt
 //                  dQ'^T = (S G^T) / den + z gd^T + K'^T B^T,  B^T = mask(Bv^T / den + gd) (B_tt on
 //                  the diagonal); the map backward of q; den, gd and B_tt per token to memory
@@ -181,292 +182,6 @@ __device__ __forceinline__ void reduce_dgamma(float* scratch, float* dst, int ti
   }
   __syncthreads();
   for (int i = tid; i < D; i += 256) dst[i] = scratch[i] + scratch[D + i] + scratch[2 * D + i] + scratch[3 * D + i];
-}
-
-// ----------------------------------------------------------------------------------------
-// bwd_dq: per (segment, head), chunks in order with S (accumulators + bf16 pair of S^T in
-// LDS) and z running from the segment's prefix record. Phases per chunk, four workgroup
-// barriers:
-//   P1  all lanes: q', k' rows (the forward's map), V and dout rows, q' . z
-//   P2  wave w, query tile w: scores, den, g . num, gd, B_tt (to memory for the later
-//       passes), B^T and the dQ'^T tiles in registers; after a barrier the tiles go to fp32
-//       LDS rows over the q' and dout rows, which are consumed by then
-//   P3  all lanes: map backward of q -> dq; P4 state waves: S += K'^T V, z += colsum(K'),
-//       refresh of the S^T pair
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
-    const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
-    const float2* __restrict__ rope_hi, const float* __restrict__ states, uint16_t* __restrict__ dq,
-    float* __restrict__ den_out, float* __restrict__ gd_out, float* __restrict__ bd_out, float* __restrict__ dg_part,
-    int H, int L, float rms_eps, float eps) {
-  using G = Geo<true, D>;
-  using R = Raw<true, D>;
-  constexpr int BUF = kChunk * G::ROWP;
-  constexpr int SP = D + 8;  // pitch of the bf16 S^T pair
-  constexpr int FP = D + 4;  // pitch of the fp32 dQ' rows
-  constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E;
-  static_assert(kChunk * FP * 4 <= 2 * BUF * 2, "dq' rows must fit over the q' and dout rows");
-  __shared__ __attribute__((aligned(16))) uint16_t sQG[2 * BUF];  // q' rows, dout rows; then dq' rows
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sSh[D * SP];
-  __shared__ __attribute__((aligned(16))) uint16_t sSl[D * SP];
-  __shared__ __attribute__((aligned(16))) float sZ[D];
-  __shared__ float sDz[D];
-  __shared__ float sQz[kChunk];
-  uint16_t* const sQ = sQG;
-  uint16_t* const sG = sQG + BUF;
-  float* const sdQ = reinterpret_cast<float*>(sQG);
-
-  const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= *nseg) return;  // the whole workgroup leaves together
-  const SegInfo si = read_seg(tab, seg);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
-  const int t0 = 2 * (tid >> 3), m = tid & 7;
-  const int c16 = lane & 15, g = lane >> 4;
-  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
-  const int seg_bytes = si.len * D * 2;
-  auto rsrc = [&](const uint16_t* base) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0 * D), 0, seg_bytes, kBufFlags);
-  };
-  const __amdgpu_buffer_rsrc_t rq = rsrc(q), rk = rsrc(k), rv = rsrc(v), rg = rsrc(dout);
-  const __amdgpu_buffer_rsrc_t rdq = rsrc(dq);
-  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
-
-  floatx4 S[RT][CT];  // S_prev, value columns [wave DVW, +DVW)
-  {
-    const int wv = wave < G::NW ? wave : 0;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<true, D>(wv, rt, ct, lane));
-  }
-  if (tid < D) sZ[tid] = rec[D * D + tid];
-  if (wave < G::NW) put_state_tr<D>(sSh, sSl, S, wave, lane);
-
-  float gq1[E], gq2[E], gk1[E], gk2[E], dg1[E], dg2[E];
-  float2 lo[2][E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = m * E + e;
-    gq1[e] = gamma_q[(size_t)h * D + j];
-    gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
-    gk1[e] = gamma_k[(size_t)h * D + j];
-    gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
-    lo[0][e] = rope_lo[t0 * G::HALF + j];
-    lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
-    dg1[e] = 0.f;
-    dg2[e] = 0.f;
-  }
-  const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * E;
-  // raw q and its RoPE row are needed again by the map backward (P3), so chunk c + 1's go
-  // into a second set, issued with the other loads right after P1 and moved over at the end
-  R xq, xk, xv, xg, xqn;
-  float2 hi[E], hin[E];
-  auto load_q = [&](R& x, float2 (&hr)[E], int c) {
-    copy_bytes<E * 8>(hr, hi0 + (size_t)min(c, nch - 1) * G::HALF);
-    load_raw_buf<true, D>(x, rq, c * kChunk + t0, m);
-  };
-  auto load_rest = [&](int c) {
-    load_raw_buf<true, D>(xk, rk, c * kChunk + t0, m);
-    load_raw_buf<true, D>(xv, rv, c * kChunk + t0, m);
-    load_raw_buf<true, D>(xg, rg, c * kChunk + t0, m);
-  };
-  load_q(xq, hi, 0);
-  load_rest(0);
-  __syncthreads();  // z, S^T in LDS
-
-  for (int c = 0; c < nch; ++c) {
-    const int nv = min(kChunk, si.len - c * kChunk);
-    {  // ---- P1
-      R oq, ok;
-#pragma unroll
-      for (int tok = 0; tok < 2; ++tok) {
-        const float invq = rms_inv<true, D>(xq, tok, rms_eps);
-        const float invk = rms_inv<true, D>(xk, tok, rms_eps);
-#pragma unroll
-        for (int e = 0; e < E; e += 2) {
-          float q1[2], q2[2], k1[2], k2[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
-            rope_pair(xq.get(tok, 0, e + x), xq.get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs, q1[x], q2[x]);
-            rope_pair(xk.get(tok, 0, e + x), xk.get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs, k1[x], k2[x]);
-          }
-          put_pairs<true, D>(oq, tok, e, q1, q2);
-          put_pairs<true, D>(ok, tok, e, k1, k2);
-        }
-      }
-      store_rows<true, D>(sQ, oq, t0, m);
-      store_rows<true, D>(sK, ok, t0, m);
-      store_rows<true, D>(sV, xv, t0, m);
-      store_rows<true, D>(sG, xg, t0, m);
-#pragma unroll
-      for (int tok = 0; tok < 2; ++tok) {
-        float qz = 0.f;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < E; ++e) qz = __builtin_fmaf(oq.get(tok, hh, e), sZ[hh * G::HALF + m * E + e], qz);
-        qz = sum8(qz);
-        if (m == 0) sQz[t0 + tok] = qz;
-      }
-    }
-    // chunk c + 1's inputs (past the end: the range check reads zeros); k, v, dout are in LDS
-    load_rest(c + 1);
-    load_q(xqn, hin, c + 1);
-    __syncthreads();  // B1
-
-    floatx4 X[RT];  // S g, then dQ'^T: rows a = 16 at + 4g + i, this lane's query
-    {  // ---- P2: query tile tt = wave
-      const int tt = wave;
-      const int t = tt * 16 + c16;
-      Frag<true> Qf[KB], Gf[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        Qf[kb] = lds_frag<true>(sQ, G::ROWP, t, kb, g);
-        Gf[kb] = lds_frag<true>(sG, G::ROWP, t, kb, g);
-      }
-      uint2 qa[RT];  // q'_t at the rows of the S g tiles
-#pragma unroll
-      for (int at = 0; at < RT; ++at) qa[at] = *reinterpret_cast<const uint2*>(sQ + t * G::ROWP + 16 * at + 4 * g);
-      floatx4 At[4], Bt[4];  // rows = keys of tile kt, column = this lane's query
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        Bt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (kt <= tt) {
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            At[kt] = mma(lds_frag<true>(sK, G::ROWP, kt * 16 + c16, kb, g), Qf[kb], At[kt]);
-            Bt[kt] = mma(lds_frag<true>(sV, G::ROWP, kt * 16 + c16, kb, g), Gf[kb], Bt[kt]);
-          }
-        }
-      }
-      float idot = 0.f;  // q'_t . (S g_t) = g_t . (S^T q'_t)
-#pragma unroll
-      for (int at = 0; at < RT; ++at) {
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          acc = mma(lds_frag_tr(sSh, SP, 32 * kb, 16 * at, lane), Gf[kb], acc);
-          acc = mma(lds_frag_tr(sSl, SP, 32 * kb, 16 * at, lane), Gf[kb], acc);
-        }
-        X[at] = acc;
-        idot = __builtin_fmaf(bf_lo(qa[at].x), acc[0], idot);
-        idot = __builtin_fmaf(bf_hi(qa[at].x), acc[1], idot);
-        idot = __builtin_fmaf(bf_lo(qa[at].y), acc[2], idot);
-        idot = __builtin_fmaf(bf_hi(qa[at].y), acc[3], idot);
-      }
-      // fp32 scores; the earlier keys and the self term apart
-      float rs_o = 0.f, dot_o = 0.f, sself = 0.f, bself = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float sc = At[kt][i];
-          const bool before = kt < tt || (kt == tt && 4 * g + i < c16);
-          const bool self = kt == tt && 4 * g + i == c16;
-          rs_o += before ? sc : 0.f;
-          dot_o = __builtin_fmaf(before ? sc : 0.f, Bt[kt][i], dot_o);
-          sself += self ? sc : 0.f;
-          bself += self ? Bt[kt][i] : 0.f;
-        }
-      rs_o = sum_rows4(rs_o);
-      dot_o = sum_rows4(dot_o + idot);  // g . num without the self term
-      sself = sum_rows4(sself);
-      bself = sum_rows4(bself);
-      const float den_o = rs_o + sQz[t] + eps;  // den without the self score
-      const float den = den_o + sself;
-      const float inv = 1.0f / den;
-      const float inv2 = inv * inv;
-      const float gdv = -__builtin_fmaf(sself, bself, dot_o) * inv2;
-      const float bdv = __builtin_fmaf(bself, den_o, -dot_o) * inv2;
-      if (g == 0 && t < nv) {
-        const size_t ix = tok0 + (size_t)c * kChunk + t;
-        den_out[ix] = den;
-        gd_out[ix] = gdv;
-        bd_out[ix] = bdv;
-      }
-      Frag<true> Bp[2];  // B^T of key blocks 0, 1 (keys x queries), masked
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        floatx4 x[2];
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const int kt = 2 * b + hlf;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool before = kt < tt || (kt == tt && 4 * g + i < c16);
-            const bool self = kt == tt && 4 * g + i == c16;
-            x[hlf][i] = before ? __builtin_fmaf(Bt[kt][i], inv, gdv) : (self ? bdv : 0.f);
-          }
-        }
-        Bp[b] = acc_frag<true>(x[0], x[1]);
-      }
-#pragma unroll
-      for (int at = 0; at < RT; ++at) {
-        floatx4 acc = X[at];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc[i], inv, gdv * sZ[16 * at + 4 * g + i]);
-        acc = mma(lds_frag_tr(sK, G::ROWP, 0, 16 * at, lane), Bp[0], acc);
-        if (tt >= 2) acc = mma(lds_frag_tr(sK, G::ROWP, 32, 16 * at, lane), Bp[1], acc);
-        X[at] = acc;
-      }
-    }
-    __syncthreads();  // B2a: the q' and dout rows are consumed
-#pragma unroll
-    for (int at = 0; at < RT; ++at)
-      *reinterpret_cast<floatx4*>(sdQ + (wave * 16 + c16) * FP + 16 * at + 4 * g) = X[at];
-    __syncthreads();  // B2
-
-    {  // ---- P3: map backward of q
-      R dx;
-      map_backward<D>(xq, dx, sdQ, FP, gq1, gq2, lo, hi, rms_eps, t0, m, dg1, dg2);
-      store_raw_buf<true, D>(dx, rdq, c * kChunk + t0, m);
-    }
-    if (wave < G::NW) {  // ---- P4: S += K'^T V
-      Frag<true> Vf[CT][2];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        Vf[ct][0] = lds_frag_tr(sV, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
-        Vf[ct][1] = lds_frag_tr(sV, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const Frag<true> a = lds_frag_tr(sK, G::ROWP, 32 * kb, 16 * rt, lane);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) S[rt][ct] = mma(a, Vf[ct][kb], S[rt][ct]);
-        }
-      put_state_tr<D>(sSh, sSl, S, wave, lane);
-    }
-    if (wave == 0) {  // z += column sums of K'
-      const Frag<true> ones = ones_frag<true>();
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        floatx4 zc = mma(lds_frag_tr(sK, G::ROWP, 0, 16 * rt, lane), ones, floatx4{0.f, 0.f, 0.f, 0.f});
-        zc = mma(lds_frag_tr(sK, G::ROWP, 32, 16 * rt, lane), ones, zc);
-        if (c16 < 4) sDz[rt * 16 + 4 * g + c16] = zc[c16];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];
-    }
-    xq = xqn;
-#pragma unroll
-    for (int e = 0; e < E; ++e) hi[e] = hin[e];
-    __syncthreads();  // B3
-  }
-  reduce_dgamma<D>(sdQ, dg_part + ((size_t)seg * H + h) * 2 * D, tid, dg1, dg2);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -884,6 +599,394 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
 }
 
 // ----------------------------------------------------------------------------------------
+// bwd_dq_ws: the dq sweep, warp-specialised, 8 waves, one workgroup per CU, steps of 32 tokens (half
+// a chunk; the RoPE row of the chunk serves both halves, the in-chunk angles are rows 0..31 or
+// 32..63 of the small table).
+//   waves 4, 5 ("forward mappers"): q', k' of sub-chunk st and the raw v and dout rows into
+//          buffer st % 2;
+//   waves 0..3 ("MMA waves"): sub-chunk st - 1 from the other buffer. The running state lives
+//          only in accumulators, as S^T (rows = value dims, columns = key dims a; wave w holds
+//          the key dims of the forward's value-column split): an accumulator tile is at once an
+//          A operand whose rows are its columns and a B operand whose columns are its columns,
+//          both with the contraction over its rows, so (S g)[a] = sum_v S^T[v][a] g[v] and
+//          S^T += V^T K' need no transposed copy. Per step: the wave's rows of (S G^T) (the
+//          state as a bf16 pair) and its part of q' . (S g) for all 32 queries; waves 0, 1 also
+//          the score tiles of query tile w (A^T, V G^T, q' . z); meeting; waves 0, 1: den, g.num,
+//          gd, B_tt and B^T (to LDS and to the per-token planes); meeting; every wave: its rows
+//          of dQ'^T = (S G^T)/den + z gd^T + K'^T B^T as fp32 rows of the dq' buffer of the
+//          sub-chunk, S^T += V^T K', and (wave 0) z for the next sub-chunk;
+//   waves 6, 7 ("backward mappers"): the map backward of sub-chunk st - 2 from its dq' rows.
+// One workgroup barrier per step; the MMA waves also meet twice among themselves.
+
+template <int D>
+__device__ __forceinline__ void split_frag(floatx4 a, floatx4 b, Frag<true>& hi, Frag<true>& lo) {
+  // the accumulator pair (rows 0..15, 16..31 of a k-block) as bf16 operands: value + remainder
+  const uint32_t h0 = pack_bf2(a[0], a[1]), h1 = pack_bf2(a[2], a[3]);
+  const uint32_t h2 = pack_bf2(b[0], b[1]), h3 = pack_bf2(b[2], b[3]);
+  hi.v = __builtin_bit_cast(bf16x8, u32x4{h0, h1, h2, h3});
+  lo.v = __builtin_bit_cast(bf16x8, u32x4{pack_bf2(a[0] - bf_lo(h0), a[1] - bf_hi(h0)),
+                                          pack_bf2(a[2] - bf_lo(h1), a[3] - bf_hi(h1)),
+                                          pack_bf2(b[0] - bf_lo(h2), b[1] - bf_hi(h2)),
+                                          pack_bf2(b[2] - bf_lo(h3), b[3] - bf_hi(h3))});
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
+    const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
+    const float2* __restrict__ rope_hi, const float* __restrict__ states, uint16_t* __restrict__ dq,
+    float* __restrict__ den_out, float* __restrict__ gd_out, float* __restrict__ bd_out, float* __restrict__ dg_part,
+    int H, int L, float rms_eps, float eps) {
+  using G = Geo<true, D>;
+  using R = Raw<true, D>;
+  constexpr int C2 = 32;                 // tokens per step
+  constexpr int BUF = C2 * G::ROWP;      // elements of one operand buffer
+  constexpr int FP = D + 4;              // pitch of the fp32 dq' rows
+  constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E, NW = G::NW;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2 * BUF];
+  __shared__ __attribute__((aligned(16))) float sdQ[2 * C2 * FP];
+  __shared__ Frag<true> sB[2 * 64];                    // B^T operands of query tiles 0, 1
+  __shared__ __attribute__((aligned(16))) float sZ[2 * D];  // z before the sub-chunk, by parity
+  __shared__ float sIdot[4 * C2];                      // each MMA wave's part of q' . (S g)
+  __shared__ float sInv[C2], sGd[C2];
+  __shared__ unsigned sArrive;
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ns = __builtin_amdgcn_readfirstlane((si.len + C2 - 1) / C2);  // steps of work
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * 2;
+  auto rsrc = [&](const uint16_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0 * D), 0, seg_bytes, kBufFlags);
+  };
+  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  if (tid < D) sZ[tid] = rec[D * D + tid];
+  if (tid == 0) sArrive = 0u;
+  __syncthreads();
+  float dg1[E], dg2[E];  // RMSNorm-weight partials (backward mappers)
+#pragma unroll
+  for (int e = 0; e < E; ++e) dg1[e] = dg2[e] = 0.f;
+
+  if (wave >= 6) {
+    // ======== backward mappers: the map backward of sub-chunk st - 2
+    const int mt = tid & 127, t0 = 2 * (mt >> 3), m = mt & 7;
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q), rdq = rsrc(dq);
+    float gq1[E], gq2[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gq1[e] = gamma_q[(size_t)h * D + m * E + e];
+      gq2[e] = gamma_q[(size_t)h * D + G::HALF + m * E + e];
+    }
+    R xq;
+    float2 hi[E], lo[2][E];
+    auto issue = [&](int c) {  // raw q and angles of sub-chunk c (past the end: zeros / clamped rows)
+      const int cc = min(c, ns - 1);
+      copy_bytes<E * 8>(hi, rope_hi + (size_t)(si.hirow + (cc >> 1)) * G::HALF + m * E);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        lo[0][e] = rope_lo[(size_t)((cc & 1) * C2 + t0) * G::HALF + m * E + e];
+        lo[1][e] = rope_lo[(size_t)((cc & 1) * C2 + t0 + 1) * G::HALF + m * E + e];
+      }
+      load_raw_buf<true, D>(xq, rq, c * C2 + t0, m);
+    };
+    issue(0);
+    for (int st = 0; st < ns + 2; ++st) {
+      const int c = st - 2;
+      if (c >= 0) {
+        R dx;
+        map_backward<D>(xq, dx, sdQ + (c & 1) * C2 * FP, FP, gq1, gq2, lo, hi, rms_eps, t0, m, dg1, dg2);
+        store_raw_buf<true, D>(dx, rdq, c * C2 + t0, m);  // rows past the segment are dropped
+        issue(c + 1);
+      }
+      __syncthreads();  // Y
+    }
+  } else if (wave >= 4) {
+    // ======== forward mappers: q', k', v, dout rows of sub-chunk st into buffer st % 2
+    const int mt = tid & 127, t0 = 2 * (mt >> 3), m = mt & 7;
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q), rk = rsrc(k), rv = rsrc(v), rg = rsrc(dout);
+    float gq1[E], gq2[E], gk1[E], gk2[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gq1[e] = gamma_q[(size_t)h * D + m * E + e];
+      gq2[e] = gamma_q[(size_t)h * D + G::HALF + m * E + e];
+      gk1[e] = gamma_k[(size_t)h * D + m * E + e];
+      gk2[e] = gamma_k[(size_t)h * D + G::HALF + m * E + e];
+    }
+    R xq, xk, xv, xg;
+    float2 hi[E], lo[2][E];
+    auto issue = [&](int c) {
+      const int cc = min(c, ns - 1);
+      copy_bytes<E * 8>(hi, rope_hi + (size_t)(si.hirow + (cc >> 1)) * G::HALF + m * E);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        lo[0][e] = rope_lo[(size_t)((cc & 1) * C2 + t0) * G::HALF + m * E + e];
+        lo[1][e] = rope_lo[(size_t)((cc & 1) * C2 + t0 + 1) * G::HALF + m * E + e];
+      }
+      load_raw_buf<true, D>(xq, rq, c * C2 + t0, m);
+      load_raw_buf<true, D>(xk, rk, c * C2 + t0, m);
+      load_raw_buf<true, D>(xv, rv, c * C2 + t0, m);
+      load_raw_buf<true, D>(xg, rg, c * C2 + t0, m);
+    };
+    issue(0);
+    for (int st = 0; st < ns + 2; ++st) {
+      if (st < ns) {
+        const int b = (st & 1) * BUF;
+        R oq, ok;
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {
+          const float invq = rms_inv<true, D>(xq, tok, rms_eps);
+          const float invk = rms_inv<true, D>(xk, tok, rms_eps);
+#pragma unroll
+          for (int e = 0; e < E; e += 2) {
+            float q1[2], q2[2], k1[2], k2[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
+              rope_pair(xq.get(tok, 0, e + x), xq.get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs, q1[x], q2[x]);
+              rope_pair(xk.get(tok, 0, e + x), xk.get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs, k1[x], k2[x]);
+            }
+            put_pairs<true, D>(oq, tok, e, q1, q2);
+            put_pairs<true, D>(ok, tok, e, k1, k2);
+          }
+        }
+        store_rows<true, D>(sQ + b, oq, t0, m);
+        store_rows<true, D>(sK + b, ok, t0, m);
+        store_rows<true, D>(sV + b, xv, t0, m);
+        store_rows<true, D>(sG + b, xg, t0, m);
+        issue(st + 1);  // into the registers just consumed
+      }
+      __syncthreads();  // Y
+    }
+  } else {
+  // ======== MMA waves: step st processes sub-chunk c = st - 1
+  floatx4 ST[RT][CT];  // S^T: rows v = 16 rt + 4g + i, columns a = wave DVW + 16 ct + c16
+  {
+    const int wv = wave < NW ? wave : 0;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int a = wv * G::DVW + 16 * ct + c16;  // record: S[a][v] at its fragment-native place
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int vv = 16 * rt + 4 * g + i;
+          const int w2 = vv / G::DVW, ct2 = (vv % G::DVW) / 16, l2 = 16 * ((a % 16) / 4) + vv % 16;
+          ST[rt][ct][i] = rec[rec_frag<true, D>(w2, a / 16, ct2, l2) + a % 4];
+        }
+      }
+  }
+  unsigned meet = 0;
+  for (int st = 0; st < ns + 2; ++st) {
+    const int c = st - 1;
+    if (c >= 0 && c < ns) {  // uniform over the MMA waves
+      const int nv = min(C2, si.len - c * C2);
+      const uint16_t* cQ = sQ + (c & 1) * BUF;
+      const uint16_t* cK = sK + (c & 1) * BUF;
+      const uint16_t* cV = sV + (c & 1) * BUF;
+      const uint16_t* cG = sG + (c & 1) * BUF;
+      const float* zc = sZ + (c & 1) * D;
+      // ---- phase A: this wave's rows of S G^T (state as a bf16 pair) and its part of q'.(S g)
+      floatx4 Y[CT][2];
+      Frag<true> Gf[2][KB];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) Gf[tt][kb] = lds_frag<true>(cG, G::ROWP, tt * 16 + c16, kb, g);
+      if (wave < NW) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          Y[ct][0] = Y[ct][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            Frag<true> sh, sl;
+            split_frag<D>(ST[2 * kb][ct], ST[2 * kb + 1][ct], sh, sl);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+              Y[ct][tt] = mma(sh, Gf[tt][kb], Y[ct][tt]);
+              Y[ct][tt] = mma(sl, Gf[tt][kb], Y[ct][tt]);
+            }
+          }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          float part = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const uint2 qa = *reinterpret_cast<const uint2*>(cQ + (tt * 16 + c16) * G::ROWP + wave * G::DVW + 16 * ct + 4 * g);
+            part = __builtin_fmaf(bf_lo(qa.x), Y[ct][tt][0], part);
+            part = __builtin_fmaf(bf_hi(qa.x), Y[ct][tt][1], part);
+            part = __builtin_fmaf(bf_lo(qa.y), Y[ct][tt][2], part);
+            part = __builtin_fmaf(bf_hi(qa.y), Y[ct][tt][3], part);
+          }
+          part = sum_rows4(part);
+          if (g == 0) sIdot[wave * C2 + tt * 16 + c16] = part;
+        }
+      }
+      // score tiles of query tile tt = wave (waves 0, 1)
+      const int tt = wave & 1;
+      const int t = tt * 16 + c16;  // this lane's query
+      floatx4 At[2], Bt[2];
+      float rs_o = 0.f, dot_o = 0.f, sself = 0.f, bself = 0.f, qz = 0.f;
+      if (wave < 2) {
+        Frag<true> Qf[KB], Gt[KB];  // the query tile's rows (read again: no runtime register index)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          Qf[kb] = lds_frag<true>(cQ, G::ROWP, t, kb, g);
+          Gt[kb] = lds_frag<true>(cG, G::ROWP, t, kb, g);
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          At[kt] = Bt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (kt <= tt) {
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              At[kt] = mma(lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb, g), Qf[kb], At[kt]);
+              Bt[kt] = mma(lds_frag<true>(cV, G::ROWP, kt * 16 + c16, kb, g), Gt[kb], Bt[kt]);
+            }
+          }
+        }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sc = At[kt][i];
+            const bool before = kt < tt || (kt == tt && 4 * g + i < c16);
+            const bool self = kt == tt && 4 * g + i == c16;
+            rs_o += before ? sc : 0.f;
+            dot_o = __builtin_fmaf(before ? sc : 0.f, Bt[kt][i], dot_o);
+            sself += self ? sc : 0.f;
+            bself += self ? Bt[kt][i] : 0.f;
+          }
+        // q'_t . z over the lane's quarter of the dims, a in [D/4 g, D/4 (g + 1))
+        {
+          constexpr int QD = D / 4;
+          const uint16_t* qrow = cQ + t * G::ROWP + QD * g;
+#pragma unroll
+          for (int j = 0; j < QD; j += 2) {
+            const uint32_t w2 = *reinterpret_cast<const uint32_t*>(qrow + j);
+            qz = __builtin_fmaf(bf_lo(w2), zc[QD * g + j], qz);
+            qz = __builtin_fmaf(bf_hi(w2), zc[QD * g + j + 1], qz);
+          }
+        }
+        rs_o = sum_rows4(rs_o);
+        dot_o = sum_rows4(dot_o);
+        sself = sum_rows4(sself);
+        bself = sum_rows4(bself);
+        qz = sum_rows4(qz);
+      }
+      meet += 4;
+      mma_wave_sync(&sArrive, meet, lane);
+      // ---- phase B (waves 0, 1): den, g.num, gd, B_tt, the B^T operand of query tile tt
+      if (wave < 2) {
+        float idot = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) idot += sIdot[w * C2 + t];
+        dot_o += idot;  // g . num without the self term
+        const float den_o = rs_o + qz + eps;
+        const float den = den_o + sself;
+        const float inv = 1.0f / den;
+        const float inv2 = inv * inv;
+        const float gdv = -__builtin_fmaf(sself, bself, dot_o) * inv2;
+        const float bdv = __builtin_fmaf(bself, den_o, -dot_o) * inv2;
+        if (g == 0) {
+          sInv[t] = inv;
+          sGd[t] = gdv;
+          if (t < nv) {
+            const size_t ix = tok0 + (size_t)c * C2 + t;
+            den_out[ix] = den;
+            gd_out[ix] = gdv;
+            bd_out[ix] = bdv;
+          }
+        }
+        floatx4 x[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool before = kt < tt || (kt == tt && 4 * g + i < c16);
+            const bool self = kt == tt && 4 * g + i == c16;
+            x[kt][i] = before ? __builtin_fmaf(Bt[kt][i], inv, gdv) : (self ? bdv : 0.f);
+          }
+        sB[tt * 64 + lane] = acc_frag<true>(x[0], x[1]);
+      }
+      meet += 4;
+      mma_wave_sync(&sArrive, meet, lane);
+      // ---- phase C: this wave's rows of dQ'^T, then the state
+      if (wave < NW) {
+        float* dqb = sdQ + (c & 1) * C2 * FP;
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+          const int tc = tq * 16 + c16;  // query column of the tiles
+          const float inv = sInv[tc], gdv = sGd[tc];
+          const Frag<true> bf = sB[tq * 64 + lane];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int a0 = wave * G::DVW + 16 * ct + 4 * g;
+            floatx4 acc = Y[ct][tq];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc[i], inv, gdv * zc[a0 + i]);
+            acc = mma(lds_frag_tr(cK, G::ROWP, 0, wave * G::DVW + 16 * ct, lane), bf, acc);
+            *reinterpret_cast<floatx4*>(dqb + tc * FP + a0) = acc;
+          }
+        }
+        // S^T += V^T K' (the 32 tokens are one k-block)
+        Frag<true> Kc[CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Kc[ct] = lds_frag_tr(cK, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const Frag<true> av = lds_frag_tr(cV, G::ROWP, 0, 16 * rt, lane);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) ST[rt][ct] = mma(av, Kc[ct], ST[rt][ct]);
+        }
+      }
+      if (wave == 0) {  // z after this sub-chunk, into the other parity
+        const Frag<true> ones = ones_frag<true>();
+        float* zn = sZ + ((c + 1) & 1) * D;
+#pragma unroll
+        for (int at = 0; at < RT; ++at) {
+          const floatx4 zs = mma(lds_frag_tr(cK, G::ROWP, 0, 16 * at, lane), ones, floatx4{0.f, 0.f, 0.f, 0.f});
+          if (c16 < 4) zn[at * 16 + 4 * g + c16] = zc[at * 16 + 4 * g + c16] + zs[c16];
+        }
+      }
+    }
+    __syncthreads();  // Y
+  }
+  }
+  // RMSNorm-weight partials of the two backward-mapper waves: lanes sharing m, then the waves
+  __syncthreads();  // every wave is done with LDS
+  if (wave >= 6) {
+    const int m = tid & 7;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1) {
+        dg1[e] += __shfl_xor(dg1[e], o);
+        dg2[e] += __shfl_xor(dg2[e], o);
+      }
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        sdQ[(wave - 6) * D + m * E + e] = dg1[e];
+        sdQ[(wave - 6) * D + G::HALF + m * E + e] = dg2[e];
+      }
+    }
+  }
+  __syncthreads();
+  float* dst = dg_part + ((size_t)seg * H + h) * 2 * D;
+  for (int i = tid; i < D; i += 512) dst[i] = sdQ[i] + sdQ[D + i];
+}
+
+// ----------------------------------------------------------------------------------------
 // bwd_dgamma: RMSNorm-weight gradients, the per-segment partials summed in segment order
 // (deterministic): part[(seg H + h) 2D + j] (q: j < D, k: D + j).
 
@@ -928,8 +1031,8 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   const auto* g = static_cast<const uint16_t*>(b.dout);
   const dim3 grid(p.n_seg_max, p.H);
   mark(3);
-  hipLaunchKernelGGL((bwd_dq_kernel<D>), grid, dim3(256), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi, states,
-                     static_cast<uint16_t*>(b.dq), den, gd, bd, dgp, p.H, p.L, a.rms_eps, a.eps);
+  hipLaunchKernelGGL((bwd_dq_ws_kernel<D>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
+                     states, static_cast<uint16_t*>(b.dq), den, gd, bd, dgp, p.H, p.L, a.rms_eps, a.eps);
   mark(4);
   hipLaunchKernelGGL((bwd_pstate_kernel<D>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
                      pstates, p.H, p.L, a.rms_eps);

@@ -468,6 +468,19 @@ __device__ __forceinline__ void store_cols(typename Elem<BF>::St* dst, const Raw
     }
 }
 
+// Arrival counter of the four MMA waves of a warp-specialised kernel: each wave adds 1 with
+// release semantics (its LDS writes land first), then polls with acquire semantics until the
+// count reaches `target` (all four have arrived at this meeting: the count only grows, so the
+// n-th meeting waits for 4 n). The poll is bounded (about 0.1 s) so that a wave can never spin
+// forever.
+__device__ __forceinline__ void mma_wave_sync(unsigned* cnt, unsigned target, int lane) {
+  if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  for (int spin = 0; spin < (1 << 21); ++spin) {
+    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 struct SegInfo {
   int row, start, len, pos0;
   int hirow;  // RoPE chunk row of the segment's first chunk

@@ -702,18 +702,6 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
 // of every query tile are complete before anyone forms outputs) on an LDS arrival counter,
 // which the mappers never wait on.
 
-// Arrival counter of the four MMA waves: each wave adds 1 with release semantics (its LDS
-// writes land first), then polls with acquire semantics until all four have arrived for
-// this step. The count only grows, so step st waits for 4 (st + 1). The poll is bounded
-// (about 0.1 s) so that a wave can never spin forever.
-__device__ __forceinline__ void mma_wave_sync(unsigned* cnt, unsigned target, int lane) {
-  if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  for (int spin = 0; spin < (1 << 21); ++spin) {
-    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
-    __builtin_amdgcn_s_sleep(1);
-  }
-}
-
 // Score phase of MMA wave TT (query tile TT of the chunk): the causal tiles K'_kt Q'_TT^T
 // (kt <= TT) and Z Q'_TT^T, the diagonal tile masked, every weight rounded to bf16 once
 // (pairs of tiles packed as the B operands of V^T A^T); the row sums are taken from the
