@@ -105,6 +105,17 @@ __device__ __forceinline__ void token_col_frags(const float* w, int kb, int g, F
                                            pack_bf2(b[2] - bf_lo(h3), b[3] - bf_hi(h3))});
 }
 
+// The lane's pair of tokens back from row-major [32][ROWP] LDS rows (the inverse of store_rows).
+template <int D>
+__device__ __forceinline__ void load_rows(const uint16_t* src, int t0, int m, Raw<true, D>& r) {
+  using G = Geo<true, D>;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      copy_bytes<G::E * 2>(r.w[tok][hh], src + (t0 + tok) * G::ROWP + hh * G::HALF + m * G::E);
+}
+
 // one fp32 value per token from a [rows, H, L] plane (0 past the segment)
 __device__ __forceinline__ float load_tok(__amdgpu_buffer_rsrc_t r, int tok) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, tok * 4, 0, 0));
@@ -602,8 +613,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
 // bwd_dq_ws: the dq sweep, warp-specialised, 8 waves, one workgroup per CU, steps of 32 tokens (half
 // a chunk; the RoPE row of the chunk serves both halves, the in-chunk angles are rows 0..31 or
 // 32..63 of the small table).
-//   waves 4, 5 ("forward mappers"): q', k' of sub-chunk st and the raw v and dout rows into
-//          buffer st % 2;
+//   waves 4, 5 ("forward mappers"): q', k' and the raw v rows of sub-chunk st into buffer st % 2,
+//          its raw q into a ring of three (raw q, k, v of two sub-chunks in flight);
 //   waves 0..3 ("MMA waves"): sub-chunk st - 1 from the other buffer. The running state lives
 //          only in accumulators, as S^T (rows = value dims, columns = key dims a; wave w holds
 //          the key dims of the forward's value-column split): an accumulator tile is at once an
@@ -615,7 +626,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
 //          gd, B_tt and B^T (to LDS and to the per-token planes); meeting; every wave: its rows
 //          of dQ'^T = (S G^T)/den + z gd^T + K'^T B^T as fp32 rows of the dq' buffer of the
 //          sub-chunk, S^T += V^T K', and (wave 0) z for the next sub-chunk;
-//   waves 6, 7 ("backward mappers"): the map backward of sub-chunk st - 2 from its dq' rows.
+//   waves 6, 7 ("backward mappers"): the raw dout rows of sub-chunk st into buffer st % 2
+//          (two sub-chunks in flight), then the map backward of sub-chunk st - 2 from its dq'
+//          rows and the raw q in the ring.
 // One workgroup barrier per step; the MMA waves also meet twice among themselves.
 
 template <int D>
@@ -648,6 +661,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BUF];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUF];
   __shared__ __attribute__((aligned(16))) uint16_t sG[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sRq[3 * BUF];  // raw q rows, ring of three
   __shared__ __attribute__((aligned(16))) float sdQ[2 * C2 * FP];
   __shared__ Frag<true> sB[2 * 64];                    // B^T operands of query tiles 0, 1
   __shared__ __attribute__((aligned(16))) float sZ[2 * D];  // z before the sub-chunk, by parity
@@ -660,7 +674,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
   const SegInfo si = read_seg(tab, seg);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int ns = __builtin_amdgcn_readfirstlane((si.len + C2 - 1) / C2);  // steps of work
+  const int ns = __builtin_amdgcn_readfirstlane((si.len + C2 - 1) / C2);  // sub-chunks
+  const int nsteps = (ns + 3) & ~1;  // >= ns + 2, even for the mappers' two-step turns
   const int c16 = lane & 15, g = lane >> 4;
   const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
   const int seg_bytes = si.len * D * 2;
@@ -675,43 +690,59 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
 #pragma unroll
   for (int e = 0; e < E; ++e) dg1[e] = dg2[e] = 0.f;
 
+  // in-chunk RoPE angles of a mapper lane's tokens for even (rows t0, t0 + 1) and odd
+  // (rows 32 + t0, 33 + t0) sub-chunks; the mapper loops take two steps per turn, so the
+  // parity, and with it the array, is known at compile time
+  auto load_lo2 = [&](float2 (&lo)[2][E], int row, int m) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      lo[0][e] = rope_lo[(size_t)row * G::HALF + m * E + e];
+      lo[1][e] = rope_lo[(size_t)(row + 1) * G::HALF + m * E + e];
+    }
+  };
+  auto hi_row = [&](float2 (&hr)[E], int c, int m) {  // RoPE row of sub-chunk c's chunk
+    copy_bytes<E * 8>(hr, rope_hi + (size_t)(si.hirow + (min(c, ns - 1) >> 1)) * G::HALF + m * E);
+  };
+
   if (wave >= 6) {
-    // ======== backward mappers: the map backward of sub-chunk st - 2
+    // ======== backward mappers: the raw v and dout rows of sub-chunk st (two sub-chunks in
+    // flight), then the map backward of sub-chunk st - 2 with its raw q from the ring
     const int mt = tid & 127, t0 = 2 * (mt >> 3), m = mt & 7;
-    const __amdgpu_buffer_rsrc_t rq = rsrc(q), rdq = rsrc(dq);
+    const __amdgpu_buffer_rsrc_t rg = rsrc(dout), rdq = rsrc(dq);
     float gq1[E], gq2[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       gq1[e] = gamma_q[(size_t)h * D + m * E + e];
       gq2[e] = gamma_q[(size_t)h * D + G::HALF + m * E + e];
     }
-    R xq;
-    float2 hi[E], lo[2][E];
-    auto issue = [&](int c) {  // raw q and angles of sub-chunk c (past the end: zeros / clamped rows)
-      const int cc = min(c, ns - 1);
-      copy_bytes<E * 8>(hi, rope_hi + (size_t)(si.hirow + (cc >> 1)) * G::HALF + m * E);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        lo[0][e] = rope_lo[(size_t)((cc & 1) * C2 + t0) * G::HALF + m * E + e];
-        lo[1][e] = rope_lo[(size_t)((cc & 1) * C2 + t0 + 1) * G::HALF + m * E + e];
-      }
-      load_raw_buf<true, D>(xq, rq, c * C2 + t0, m);
-    };
-    issue(0);
-    for (int st = 0; st < ns + 2; ++st) {
-      const int c = st - 2;
-      if (c >= 0) {
-        R dx;
-        map_backward<D>(xq, dx, sdQ + (c & 1) * C2 * FP, FP, gq1, gq2, lo, hi, rms_eps, t0, m, dg1, dg2);
+    float2 lo[2][E], hr[E];  // angles of the sub-chunk mapped back next, loaded a step ahead
+    R va, vb;  // raw dout of an even / odd sub-chunk
+    auto issue = [&](R& x, int c) { load_raw_buf<true, D>(x, rg, c * C2 + t0, m); };
+    auto bstep = [&](int st, R& x) {
+      if (st < ns) store_rows<true, D>(sG + (st & 1) * BUF, x, t0, m);
+      issue(x, st + 2);  // into the registers just consumed
+      const int c = st - 2;  // same parity as st
+      if (c >= 0 && c < ns) {
+        R xq, dx;
+        load_rows<D>(sRq + (c % 3) * BUF, t0, m, xq);
+        map_backward<D>(xq, dx, sdQ + (c & 1) * C2 * FP, FP, gq1, gq2, lo, hr, rms_eps, t0, m, dg1, dg2);
         store_raw_buf<true, D>(dx, rdq, c * C2 + t0, m);  // rows past the segment are dropped
-        issue(c + 1);
       }
+      hi_row(hr, st - 1, m);  // the angles of sub-chunk st - 1, mapped back in the next step
+      load_lo2(lo, ((st - 1) & 1) * C2 + t0, m);
       __syncthreads();  // Y
+    };
+    issue(va, 0);
+    issue(vb, 1);
+    for (int st = 0; st < nsteps; st += 2) {
+      bstep(st, va);
+      bstep(st + 1, vb);
     }
   } else if (wave >= 4) {
-    // ======== forward mappers: q', k', v, dout rows of sub-chunk st into buffer st % 2
+    // ======== forward mappers: q', k' of sub-chunk st into buffer st % 2 and its raw q into
+    // the ring (two sub-chunks of raw q, k in flight)
     const int mt = tid & 127, t0 = 2 * (mt >> 3), m = mt & 7;
-    const __amdgpu_buffer_rsrc_t rq = rsrc(q), rk = rsrc(k), rv = rsrc(v), rg = rsrc(dout);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q), rk = rsrc(k), rv = rsrc(v);
     float gq1[E], gq2[E], gk1[E], gk2[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -720,38 +751,31 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       gk1[e] = gamma_k[(size_t)h * D + m * E + e];
       gk2[e] = gamma_k[(size_t)h * D + G::HALF + m * E + e];
     }
-    R xq, xk, xv, xg;
-    float2 hi[E], lo[2][E];
-    auto issue = [&](int c) {
-      const int cc = min(c, ns - 1);
-      copy_bytes<E * 8>(hi, rope_hi + (size_t)(si.hirow + (cc >> 1)) * G::HALF + m * E);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        lo[0][e] = rope_lo[(size_t)((cc & 1) * C2 + t0) * G::HALF + m * E + e];
-        lo[1][e] = rope_lo[(size_t)((cc & 1) * C2 + t0 + 1) * G::HALF + m * E + e];
-      }
-      load_raw_buf<true, D>(xq, rq, c * C2 + t0, m);
-      load_raw_buf<true, D>(xk, rk, c * C2 + t0, m);
-      load_raw_buf<true, D>(xv, rv, c * C2 + t0, m);
-      load_raw_buf<true, D>(xg, rg, c * C2 + t0, m);
+    float2 lo[2][E], hia[E], hib[E];  // lo: angles of the sub-chunk mapped next
+    load_lo2(lo, t0, m);
+    R qa[3], qb[3];  // raw q, k, v of an even / odd sub-chunk
+    auto issue = [&](R (&x)[3], float2 (&hr)[E], int c) {
+      hi_row(hr, c, m);
+      load_raw_buf<true, D>(x[0], rq, c * C2 + t0, m);
+      load_raw_buf<true, D>(x[1], rk, c * C2 + t0, m);
+      load_raw_buf<true, D>(x[2], rv, c * C2 + t0, m);
     };
-    issue(0);
-    for (int st = 0; st < ns + 2; ++st) {
+    auto fstep = [&](int st, R (&x)[3], float2 (&hr)[E]) {
       if (st < ns) {
         const int b = (st & 1) * BUF;
         R oq, ok;
 #pragma unroll
         for (int tok = 0; tok < 2; ++tok) {
-          const float invq = rms_inv<true, D>(xq, tok, rms_eps);
-          const float invk = rms_inv<true, D>(xk, tok, rms_eps);
+          const float invq = rms_inv<true, D>(x[0], tok, rms_eps);
+          const float invk = rms_inv<true, D>(x[1], tok, rms_eps);
 #pragma unroll
           for (int e = 0; e < E; e += 2) {
             float q1[2], q2[2], k1[2], k2[2];
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-              const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
-              rope_pair(xq.get(tok, 0, e + x), xq.get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs, q1[x], q2[x]);
-              rope_pair(xk.get(tok, 0, e + x), xk.get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs, k1[x], k2[x]);
+            for (int y = 0; y < 2; ++y) {
+              const float2 cs = angle_sum(hr[e + y], lo[tok][e + y]);
+              rope_pair(x[0].get(tok, 0, e + y), x[0].get(tok, 1, e + y), invq, gq1[e + y], gq2[e + y], cs, q1[y], q2[y]);
+              rope_pair(x[1].get(tok, 0, e + y), x[1].get(tok, 1, e + y), invk, gk1[e + y], gk2[e + y], cs, k1[y], k2[y]);
             }
             put_pairs<true, D>(oq, tok, e, q1, q2);
             put_pairs<true, D>(ok, tok, e, k1, k2);
@@ -759,11 +783,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         }
         store_rows<true, D>(sQ + b, oq, t0, m);
         store_rows<true, D>(sK + b, ok, t0, m);
-        store_rows<true, D>(sV + b, xv, t0, m);
-        store_rows<true, D>(sG + b, xg, t0, m);
-        issue(st + 1);  // into the registers just consumed
+        store_rows<true, D>(sV + b, x[2], t0, m);
+        store_rows<true, D>(sRq + (st % 3) * BUF, x[0], t0, m);
       }
+      issue(x, hr, st + 2);  // into the registers just consumed
+      load_lo2(lo, ((st + 1) & 1) * C2 + t0, m);
       __syncthreads();  // Y
+    };
+    issue(qa, hia, 0);
+    issue(qb, hib, 1);
+    for (int st = 0; st < nsteps; st += 2) {
+      fstep(st, qa, hia);
+      fstep(st + 1, qb, hib);
     }
   } else {
   // ======== MMA waves: step st processes sub-chunk c = st - 1
@@ -784,7 +815,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       }
   }
   unsigned meet = 0;
-  for (int st = 0; st < ns + 2; ++st) {
+  for (int st = 0; st < nsteps; ++st) {
     const int c = st - 1;
     if (c >= 0 && c < ns) {  // uniform over the MMA waves
       const int nv = min(C2, si.len - c * C2);
