@@ -29,14 +29,17 @@
 //                  the diagonal); the map backward of q; den, gd and B_tt per token to memory
 //   bwd_pstate   per (segment, head): sums of Q^^T G and Q^^T (gd den) over the segment
 //   (suffix scan) exclusive sums over the later segments of each document
-//   bwd_dkv      per (segment, head), chunks in reverse order, P and p running:
+//   bwd_dkv_ws   per (segment, head), 32-token steps in reverse order, P and p running (warp-
+//                specialised as bwd_dq_ws):
 //                  A = mask(Q' K'^T), B = mask(G V^T / den + gd) (queries x keys, B_tt on the diagonal)
 //                  dK'^T = P V^T + Q'^T B + p 1^T,  dV^T = P^T K'^T + G^T (A / den)
 //                then the map backward of k
 //   bwd_dgamma   sums the per-segment RMSNorm-weight partials
-// Operand layout conventions are those of rla2_device.h; running states live in MFMA
-// accumulators (value columns split over the waves) and as a transposed bf16 pair in LDS,
-// from which both contraction orders are read.
+// Operand layout conventions are those of rla2_device.h. The running states live only in MFMA
+// accumulators: an accumulator tile is at once an A operand whose rows are its columns and a
+// B operand whose columns are its columns, both contracting over its rows, so a state held
+// with the right orientation serves its products directly (the dk, dv sweep keeps P in both
+// orientations, one per product); as operands they enter as a bf16 pair (value + remainder).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,30 +56,6 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
 // the two bf16 halves of a packed word as floats
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Write the running state (accumulator tiles of this wave's value columns) as its transpose,
-// row-major [c][a] with pitch D + 8, rounded to bf16 into `hi` and the remainder, rounded,
-// into `lo`: lane (c16, g) of tile (rt, ct) holds X[16 rt + 4g + i][col] for i < 4, i.e. four
-// consecutive entries of row `col` of X^T.
-template <int D>
-__device__ __forceinline__ void put_state_tr(uint16_t* hi, uint16_t* lo,
-                                             const floatx4 (&X)[Geo<true, D>::RT][Geo<true, D>::CT], int wave,
-                                             int lane) {
-  using G = Geo<true, D>;
-  constexpr int SP = D + 8;
-  const int c16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int rt = 0; rt < G::RT; ++rt)
-#pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct) {
-      const int off = (wave * G::DVW + ct * 16 + c16) * SP + 16 * rt + 4 * g;
-      const floatx4 x = X[rt][ct];
-      const uint32_t h0 = pack_bf2(x[0], x[1]), h1 = pack_bf2(x[2], x[3]);
-      *reinterpret_cast<uint2*>(hi + off) = make_uint2(h0, h1);
-      *reinterpret_cast<uint2*>(lo + off) =
-          make_uint2(pack_bf2(x[0] - bf_lo(h0), x[1] - bf_hi(h0)), pack_bf2(x[2] - bf_lo(h1), x[3] - bf_hi(h1)));
-    }
-}
 
 // q'/den per token, rounded to bf16 (the query operand of the reverse states); inv = 1/den.
 template <int D>
@@ -321,292 +300,6 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
 #pragma unroll
     for (int z = 0; z < ZR; ++z) rec[D * D + (wave * ZR + z) * 16 + 4 * g + c16] = pz[z][c16];
   }
-}
-
-// ----------------------------------------------------------------------------------------
-// bwd_dkv: per (segment, head), chunks in reverse order with P (accumulators + bf16 pair of
-// P^T in LDS) and p running from the segment's suffix record. Phases per chunk as in bwd_dq:
-//   P1  all lanes: q', k' rows, V and dout rows, Q^ rows, 1/den, gd, B_tt, gd den per token
-//   P2  wave w, key tile w: A and B (queries x keys, queries at or after the key); dV^T goes
-//       out from the accumulators (4 consecutive dims per lane); the dK'^T tiles go, after a
-//       barrier, to fp32 LDS rows over the k' and v rows
-//   P3  all lanes: map backward of k -> dk; P4 state waves: P += Q^^T G, p += Q^^T (gd den),
-//       refresh of the P^T pair
-
-template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
-    const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
-    const float2* __restrict__ rope_hi, const float* __restrict__ pstates, const float* __restrict__ den,
-    const float* __restrict__ gd, const float* __restrict__ bd, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    float* __restrict__ dg_part, int H, int L, float rms_eps) {
-  using G = Geo<true, D>;
-  using R = Raw<true, D>;
-  constexpr int BUF = kChunk * G::ROWP;
-  constexpr int SP = D + 8;
-  constexpr int FP = D + 4;
-  constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E;
-  static_assert(kChunk * FP * 4 <= 2 * BUF * 2, "dk' rows must fit over the k' and v rows");
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[2 * BUF];  // k' rows, v rows; then dk' rows
-  __shared__ __attribute__((aligned(16))) uint16_t sG[BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sH[BUF];       // Q^ rows
-  __shared__ __attribute__((aligned(16))) uint16_t sPh[D * SP];
-  __shared__ __attribute__((aligned(16))) uint16_t sPl[D * SP];
-  __shared__ __attribute__((aligned(16))) float sP[D];
-  __shared__ float sDp[D];
-  __shared__ float sI[kChunk], sGd[kChunk], sBd[kChunk], sW[kChunk];
-  uint16_t* const sK = sKV;
-  uint16_t* const sV = sKV + BUF;
-  float* const sdK = reinterpret_cast<float*>(sKV);
-
-  const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= *nseg) return;
-  const SegInfo si = read_seg(tab, seg);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
-  const int t0 = 2 * (tid >> 3), m = tid & 7;
-  const int c16 = lane & 15, g = lane >> 4;
-  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
-  const int seg_bytes = si.len * D * 2;
-  auto rsrc = [&](const uint16_t* base) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0 * D), 0, seg_bytes, kBufFlags);
-  };
-  auto rsrc_tok = [&](const float* base) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0), 0, si.len * 4, kBufFlags);
-  };
-  const __amdgpu_buffer_rsrc_t rq = rsrc(q), rk = rsrc(k), rv = rsrc(v), rg = rsrc(dout);
-  const __amdgpu_buffer_rsrc_t rdk = rsrc(dk), rdv = rsrc(dv);
-  const __amdgpu_buffer_rsrc_t rd = rsrc_tok(den), rw = rsrc_tok(gd), rb = rsrc_tok(bd);
-  const float* rec = pstates + ((size_t)seg * H + h) * (size_t)(D * D + D);
-
-  floatx4 P[RT][CT];  // P_next, value columns [wave DVW, +DVW)
-  {
-    const int wv = wave < G::NW ? wave : 0;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-        P[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<true, D>(wv, rt, ct, lane));
-  }
-  if (tid < D) sP[tid] = rec[D * D + tid];
-  if (wave < G::NW) put_state_tr<D>(sPh, sPl, P, wave, lane);
-
-  float gq1[E], gq2[E], gk1[E], gk2[E], dg1[E], dg2[E];
-  float2 lo[2][E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = m * E + e;
-    gq1[e] = gamma_q[(size_t)h * D + j];
-    gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
-    gk1[e] = gamma_k[(size_t)h * D + j];
-    gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
-    lo[0][e] = rope_lo[t0 * G::HALF + j];
-    lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
-    dg1[e] = 0.f;
-    dg2[e] = 0.f;
-  }
-  const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * E;
-  // raw k and its RoPE row are needed again by the map backward (P3): chunk c - 1's go into
-  // a second set, issued right after P1 and moved over at the end of the step
-  R xq, xk, xv, xg, xkn;
-  float2 hi[E], hin[E];
-  float dn[2], gdl[2], bdl[2];
-  auto load_k = [&](R& x, float2 (&hr)[E], int c) {
-    copy_bytes<E * 8>(hr, hi0 + (size_t)max(c, 0) * G::HALF);
-    load_raw_buf<true, D>(x, rk, c * kChunk + t0, m);
-  };
-  auto load_rest = [&](int c) {
-    load_raw_buf<true, D>(xq, rq, c * kChunk + t0, m);
-    load_raw_buf<true, D>(xv, rv, c * kChunk + t0, m);
-    load_raw_buf<true, D>(xg, rg, c * kChunk + t0, m);
-#pragma unroll
-    for (int tok = 0; tok < 2; ++tok) {
-      dn[tok] = load_tok(rd, c * kChunk + t0 + tok);
-      gdl[tok] = load_tok(rw, c * kChunk + t0 + tok);
-      bdl[tok] = load_tok(rb, c * kChunk + t0 + tok);
-    }
-  };
-  load_k(xk, hi, nch - 1);
-  load_rest(nch - 1);
-  __syncthreads();  // p, P^T in LDS
-
-  for (int c = nch - 1; c >= 0; --c) {
-    const int nv = min(kChunk, si.len - c * kChunk);
-    {  // ---- P1
-      R oq, ok, oh;
-#pragma unroll
-      for (int tok = 0; tok < 2; ++tok) {
-        const float invq = rms_inv<true, D>(xq, tok, rms_eps);
-        const float invk = rms_inv<true, D>(xk, tok, rms_eps);
-#pragma unroll
-        for (int e = 0; e < E; e += 2) {
-          float q1[2], q2[2], k1[2], k2[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
-            rope_pair(xq.get(tok, 0, e + x), xq.get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs, q1[x], q2[x]);
-            rope_pair(xk.get(tok, 0, e + x), xk.get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs, k1[x], k2[x]);
-          }
-          put_pairs<true, D>(oq, tok, e, q1, q2);
-          put_pairs<true, D>(ok, tok, e, k1, k2);
-        }
-      }
-      const float inv[2] = {dn[0] > 0.f ? 1.0f / dn[0] : 0.f, dn[1] > 0.f ? 1.0f / dn[1] : 0.f};
-      scale_raw<D>(oq, oh, inv);
-      store_rows<true, D>(sQ, oq, t0, m);
-      store_rows<true, D>(sK, ok, t0, m);
-      store_rows<true, D>(sV, xv, t0, m);
-      store_rows<true, D>(sG, xg, t0, m);
-      store_rows<true, D>(sH, oh, t0, m);
-      if (m == 0) {
-#pragma unroll
-        for (int tok = 0; tok < 2; ++tok) {
-          sI[t0 + tok] = inv[tok];
-          sGd[t0 + tok] = gdl[tok];
-          sBd[t0 + tok] = bdl[tok];
-          sW[t0 + tok] = gdl[tok] * dn[tok];
-        }
-      }
-    }
-    if (c > 0) {
-      load_rest(c - 1);
-      load_k(xkn, hin, c - 1);
-    }
-    __syncthreads();  // B1
-
-    floatx4 Y[RT];  // dK'^T: rows a = 16 at + 4g + i, this lane's key
-    {  // ---- P2: key tile kt = wave
-      const int kt = wave;
-      const int key = kt * 16 + c16;
-      Frag<true> Kf[KB], Vf[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        Kf[kb] = lds_frag<true>(sK, G::ROWP, key, kb, g);
-        Vf[kb] = lds_frag<true>(sV, G::ROWP, key, kb, g);
-      }
-      floatx4 Aq[4], Bq[4];  // rows = queries of tile tt, column = this lane's key
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        Aq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        Bq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (tt >= kt) {
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            Aq[tt] = mma(lds_frag<true>(sQ, G::ROWP, tt * 16 + c16, kb, g), Kf[kb], Aq[tt]);
-            Bq[tt] = mma(lds_frag<true>(sG, G::ROWP, tt * 16 + c16, kb, g), Vf[kb], Bq[tt]);
-          }
-        }
-      }
-      Frag<true> Ap[2], Bp[2];  // query blocks 0, 1 as the B operands (queries x keys)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        floatx4 xa[2], xb[2];
-#pragma unroll
-        for (int hlf = 0; hlf < 2; ++hlf) {
-          const int tt = 2 * b + hlf;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = tt * 16 + 4 * g + i;
-            const bool after = tt > kt || (tt == kt && 4 * g + i > c16);
-            const bool self = tt == kt && 4 * g + i == c16;
-            const float ri = sI[t];
-            xa[hlf][i] = (after || self) ? Aq[tt][i] * ri : 0.f;
-            xb[hlf][i] = after ? __builtin_fmaf(Bq[tt][i], ri, sGd[t]) : (self ? sBd[t] : 0.f);
-          }
-        }
-        Ap[b] = acc_frag<true>(xa[0], xa[1]);
-        Bp[b] = acc_frag<true>(xb[0], xb[1]);
-      }
-      // dV^T: rows = value dims, this lane's key; four consecutive dims per lane go out directly
-#pragma unroll
-      for (int ct = 0; ct < RT; ++ct) {
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          acc = mma(lds_frag<true>(sPh, SP, 16 * ct + c16, kb, g), Kf[kb], acc);
-          acc = mma(lds_frag<true>(sPl, SP, 16 * ct + c16, kb, g), Kf[kb], acc);
-        }
-        if (kt <= 1) acc = mma(lds_frag_tr(sG, G::ROWP, 0, 16 * ct, lane), Ap[0], acc);
-        acc = mma(lds_frag_tr(sG, G::ROWP, 32, 16 * ct, lane), Ap[1], acc);
-        const int off = ((c * kChunk + key) * D + 16 * ct + 4 * g) * 2;  // keys past the segment are dropped
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3])}, rdv,
-                                              key < nv ? off : seg_bytes, 0, kLoadStream);
-      }
-      // dK'^T
-#pragma unroll
-      for (int at = 0; at < RT; ++at) {
-        floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          acc = mma(lds_frag_tr(sPh, SP, 32 * kb, 16 * at, lane), Vf[kb], acc);
-          acc = mma(lds_frag_tr(sPl, SP, 32 * kb, 16 * at, lane), Vf[kb], acc);
-        }
-        if (kt <= 1) acc = mma(lds_frag_tr(sQ, G::ROWP, 0, 16 * at, lane), Bp[0], acc);
-        acc = mma(lds_frag_tr(sQ, G::ROWP, 32, 16 * at, lane), Bp[1], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += sP[16 * at + 4 * g + i];
-        Y[at] = acc;
-      }
-    }
-    __syncthreads();  // B2a: the k' and v rows are consumed
-#pragma unroll
-    for (int at = 0; at < RT; ++at)
-      *reinterpret_cast<floatx4*>(sdK + (wave * 16 + c16) * FP + 16 * at + 4 * g) = Y[at];
-    __syncthreads();  // B2
-
-    {  // ---- P3: map backward of k
-      R dx;
-      map_backward<D>(xk, dx, sdK, FP, gk1, gk2, lo, hi, rms_eps, t0, m, dg1, dg2);
-      store_raw_buf<true, D>(dx, rdk, c * kChunk + t0, m);
-    }
-    if (wave < G::NW) {  // ---- P4: P += Q^^T G
-      Frag<true> Nf[CT][2];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        Nf[ct][0] = lds_frag_tr(sG, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
-        Nf[ct][1] = lds_frag_tr(sG, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const Frag<true> a = lds_frag_tr(sH, G::ROWP, 32 * kb, 16 * rt, lane);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) P[rt][ct] = mma(a, Nf[ct][kb], P[rt][ct]);
-        }
-      put_state_tr<D>(sPh, sPl, P, wave, lane);
-    }
-    if (wave == 0) {  // p += Q^^T (gd den), as a bf16 pair in every column
-      Frag<true> w_hi[2], w_lo[2];
-      token_col_frags(sW, 0, g, w_hi[0], w_lo[0]);
-      token_col_frags(sW, 1, g, w_hi[1], w_lo[1]);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        floatx4 pc = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const Frag<true> a = lds_frag_tr(sH, G::ROWP, 32 * kb, 16 * rt, lane);
-          pc = mma(a, w_hi[kb], pc);
-          pc = mma(a, w_lo[kb], pc);
-        }
-        if (c16 < 4) sDp[rt * 16 + 4 * g + c16] = pc[c16];
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      for (int i = lane; i < D; i += 64) sP[i] += sDp[i];
-    }
-    if (c > 0) {
-      xk = xkn;
-#pragma unroll
-      for (int e = 0; e < E; ++e) hi[e] = hin[e];
-    }
-    __syncthreads();  // B3
-  }
-  reduce_dgamma<D>(sdK, dg_part + ((size_t)seg * H + h) * 2 * D + D, tid, dg1, dg2);
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1018,6 +711,387 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
 }
 
 // ----------------------------------------------------------------------------------------
+// bwd_dkv_ws: the dk, dv sweep, warp-specialised like bwd_dq_ws (8 waves, one workgroup per CU,
+// 32-token steps), sub-chunks in reverse order.
+//   waves 4, 5 ("forward mappers"): q', k', the raw v rows and Q^ = bf16(q'/den) of sub-chunk
+//          j (the j-th from the end) into buffer j % 2, with 1/den, gd, B_tt and gd den per token
+//          (from the planes bwd_dq wrote); its raw k into a ring of three;
+//   waves 0..3 ("MMA waves"): sub-chunk j - 1. The reverse state lives only in accumulators,
+//          twice: P^T (rows = value dims v, columns = the wave's slice of the query dims a) for
+//          dK'^T = P V^T, and P (rows a, columns = the wave's slice of v) for dV^T = P^T K'^T, so
+//          each product contracts over the rows of its accumulator tiles and no transposed copy
+//          is needed. Per step: waves 0, 1, key tile w: A = mask(Q' K'^T) and B = mask(G V^T /
+//          den + gd) (B_tt on the diagonal) as the B operands A/den and B (queries x keys);
+//          meeting; every wave: its rows of dK'^T = P V^T + Q'^T B + p (fp32 rows of the dk'
+//          buffer) and of dV^T = P^T K'^T + G^T (A/den) (stored), then P^T += G^T Q^,
+//          P += Q^^T G, and (wave 0) p for the next sub-chunk, all states as bf16 operand pairs;
+//   waves 6, 7 ("backward mappers"): the raw dout rows of sub-chunk j into buffer j % 2, then
+//          the map backward of k for sub-chunk j - 2 from its dk' rows and the ring.
+// One workgroup barrier per step; the MMA waves also meet once among themselves.
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
+    const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
+    const float2* __restrict__ rope_hi, const float* __restrict__ pstates, const float* __restrict__ den,
+    const float* __restrict__ gd, const float* __restrict__ bd, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    float* __restrict__ dg_part, int H, int L, float rms_eps) {
+  using G = Geo<true, D>;
+  using R = Raw<true, D>;
+  constexpr int C2 = 32;
+  constexpr int BUF = C2 * G::ROWP;
+  constexpr int FP = D + 4;
+  constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E, NW = G::NW;
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sH[2 * BUF];   // Q^ rows
+  __shared__ __attribute__((aligned(16))) uint16_t sRk[3 * BUF];  // raw k rows, ring of three
+  __shared__ __attribute__((aligned(16))) float sdK[2 * C2 * FP];
+  __shared__ Frag<true> sAp[2 * 64], sBp[2 * 64];  // per key tile: A/den and B (queries x keys)
+  __shared__ __attribute__((aligned(16))) float sP[2 * D];   // p after the sub-chunk, by parity
+  __shared__ __attribute__((aligned(16))) float sI[2 * C2];
+  __shared__ __attribute__((aligned(16))) float sGd[2 * C2];
+  __shared__ __attribute__((aligned(16))) float sBd[2 * C2];
+  __shared__ __attribute__((aligned(16))) float sW[2 * C2];
+  __shared__ unsigned sArrive;
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ns = __builtin_amdgcn_readfirstlane((si.len + C2 - 1) / C2);  // sub-chunks
+  const int nsteps = (ns + 3) & ~1;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * 2;
+  auto rsrc = [&](const uint16_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0 * D), 0, seg_bytes, kBufFlags);
+  };
+  auto rsrc_tok = [&](const float* base) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tok0), 0, si.len * 4, kBufFlags);
+  };
+  const float* rec = pstates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  if (tid < D) sP[tid] = rec[D * D + tid];
+  if (tid == 0) sArrive = 0u;
+  __syncthreads();
+  float dg1[E], dg2[E];  // RMSNorm-weight partials of k (backward mappers)
+#pragma unroll
+  for (int e = 0; e < E; ++e) dg1[e] = dg2[e] = 0.f;
+  auto sub = [&](int j) { return ns - 1 - j; };  // the j-th sub-chunk from the end
+  // the same for loads: j past the last step gives the sub-chunk just past the segment, which
+  // the buffer range check turns into zeros
+  auto sub_ld = [&](int j) { return j < ns ? ns - 1 - j : ns; };
+  auto load_lo2 = [&](float2 (&lo)[2][E], int row, int m) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      lo[0][e] = rope_lo[(size_t)row * G::HALF + m * E + e];
+      lo[1][e] = rope_lo[(size_t)(row + 1) * G::HALF + m * E + e];
+    }
+  };
+  auto hi_row = [&](float2 (&hr)[E], int c, int m) {  // RoPE row of sub-chunk c's chunk
+    copy_bytes<E * 8>(hr, rope_hi + (size_t)(si.hirow + (min(max(c, 0), ns - 1) >> 1)) * G::HALF + m * E);
+  };
+
+  if (wave >= 6) {
+    // ======== backward mappers: dout rows of sub-chunk j, map backward of k for j - 2
+    const int mt = tid & 127, t0 = 2 * (mt >> 3), m = mt & 7;
+    const __amdgpu_buffer_rsrc_t rg = rsrc(dout), rdk = rsrc(dk);
+    float gk1[E], gk2[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gk1[e] = gamma_k[(size_t)h * D + m * E + e];
+      gk2[e] = gamma_k[(size_t)h * D + G::HALF + m * E + e];
+    }
+    float2 lo[2][E], hr[E];  // angles of the sub-chunk mapped back next, loaded a step ahead
+    R ga, gb;  // raw dout of an even / odd step
+    auto issue = [&](R& x, int j) { load_raw_buf<true, D>(x, rg, sub_ld(j) * C2 + t0, m); };
+    auto bstep = [&](int st, R& x) {
+      if (st < ns) store_rows<true, D>(sG + (st & 1) * BUF, x, t0, m);
+      issue(x, st + 2);
+      const int j = st - 2;
+      if (j >= 0 && j < ns) {
+        R xk, dx;
+        load_rows<D>(sRk + (j % 3) * BUF, t0, m, xk);
+        map_backward<D>(xk, dx, sdK + (j & 1) * C2 * FP, FP, gk1, gk2, lo, hr, rms_eps, t0, m, dg1, dg2);
+        store_raw_buf<true, D>(dx, rdk, sub(j) * C2 + t0, m);  // rows past the segment are dropped
+      }
+      hi_row(hr, sub(st - 1), m);  // the angles of step st - 1's sub-chunk, mapped back next step
+      load_lo2(lo, (sub(st - 1) & 1) * C2 + t0, m);
+      __syncthreads();  // Y
+    };
+    issue(ga, 0);
+    issue(gb, 1);
+    for (int st = 0; st < nsteps; st += 2) {
+      bstep(st, ga);
+      bstep(st + 1, gb);
+    }
+  } else if (wave >= 4) {
+    // ======== forward mappers: q', k', v, Q^ rows and per-token values of sub-chunk j
+    const int mt = tid & 127, t0 = 2 * (mt >> 3), m = mt & 7;
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q), rk = rsrc(k), rv = rsrc(v);
+    const __amdgpu_buffer_rsrc_t rd = rsrc_tok(den), rw = rsrc_tok(gd), rb = rsrc_tok(bd);
+    float gq1[E], gq2[E], gk1[E], gk2[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gq1[e] = gamma_q[(size_t)h * D + m * E + e];
+      gq2[e] = gamma_q[(size_t)h * D + G::HALF + m * E + e];
+      gk1[e] = gamma_k[(size_t)h * D + m * E + e];
+      gk2[e] = gamma_k[(size_t)h * D + G::HALF + m * E + e];
+    }
+    float2 lo[2][E], hia[E], hib[E];
+    load_lo2(lo, (sub(0) & 1) * C2 + t0, m);
+    R xa[3], xb[3];  // raw q, k, v of an even / odd step
+    auto issue = [&](R (&x)[3], float2 (&hr)[E], int j) {
+      hi_row(hr, sub(j), m);
+      load_raw_buf<true, D>(x[0], rq, sub_ld(j) * C2 + t0, m);
+      load_raw_buf<true, D>(x[1], rk, sub_ld(j) * C2 + t0, m);
+      load_raw_buf<true, D>(x[2], rv, sub_ld(j) * C2 + t0, m);
+    };
+    auto fstep = [&](int st, R (&x)[3], float2 (&hr)[E]) {
+      if (st < ns) {
+        const int c = sub(st), b = (st & 1) * BUF;
+        R oq, ok, oh;
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {
+          const float invq = rms_inv<true, D>(x[0], tok, rms_eps);
+          const float invk = rms_inv<true, D>(x[1], tok, rms_eps);
+#pragma unroll
+          for (int e = 0; e < E; e += 2) {
+            float q1[2], q2[2], k1[2], k2[2];
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+              const float2 cs = angle_sum(hr[e + y], lo[tok][e + y]);
+              rope_pair(x[0].get(tok, 0, e + y), x[0].get(tok, 1, e + y), invq, gq1[e + y], gq2[e + y], cs, q1[y], q2[y]);
+              rope_pair(x[1].get(tok, 0, e + y), x[1].get(tok, 1, e + y), invk, gk1[e + y], gk2[e + y], cs, k1[y], k2[y]);
+            }
+            put_pairs<true, D>(oq, tok, e, q1, q2);
+            put_pairs<true, D>(ok, tok, e, k1, k2);
+          }
+        }
+        float dn[2], gdl[2], bdl[2];
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {  // tokens past the segment read 0 and weigh nothing
+          dn[tok] = load_tok(rd, c * C2 + t0 + tok);
+          gdl[tok] = load_tok(rw, c * C2 + t0 + tok);
+          bdl[tok] = load_tok(rb, c * C2 + t0 + tok);
+        }
+        const float inv[2] = {dn[0] > 0.f ? 1.0f / dn[0] : 0.f, dn[1] > 0.f ? 1.0f / dn[1] : 0.f};
+        scale_raw<D>(oq, oh, inv);
+        store_rows<true, D>(sQ + b, oq, t0, m);
+        store_rows<true, D>(sK + b, ok, t0, m);
+        store_rows<true, D>(sV + b, x[2], t0, m);
+        store_rows<true, D>(sH + b, oh, t0, m);
+        store_rows<true, D>(sRk + (st % 3) * BUF, x[1], t0, m);
+        if (m == 0) {
+#pragma unroll
+          for (int tok = 0; tok < 2; ++tok) {
+            const int ix = (st & 1) * C2 + t0 + tok;
+            sI[ix] = inv[tok];
+            sGd[ix] = gdl[tok];
+            sBd[ix] = bdl[tok];
+            sW[ix] = gdl[tok] * dn[tok];
+          }
+        }
+      }
+      issue(x, hr, st + 2);  // into the registers just consumed
+      load_lo2(lo, (sub(st + 1) & 1) * C2 + t0, m);
+      __syncthreads();  // Y
+    };
+    issue(xa, hia, 0);
+    issue(xb, hib, 1);
+    for (int st = 0; st < nsteps; st += 2) {
+      fstep(st, xa, hia);
+      fstep(st + 1, xb, hib);
+    }
+  } else {
+    // ======== MMA waves: step st processes sub-chunk sub(st - 1)
+    floatx4 PT[RT][CT];  // P^T: rows v = 16 rt + 4g + i, columns a = wave DVW + 16 ct + c16
+    floatx4 PM[RT][CT];  // P: rows a = 16 rt + 4g + i, columns v = wave DVW + 16 ct + c16
+    {
+      const int wv = wave < NW ? wave : 0;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          PM[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<true, D>(wv, rt, ct, lane));
+          const int a = wv * G::DVW + 16 * ct + c16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int vv = 16 * rt + 4 * g + i;
+            const int w2 = vv / G::DVW, ct2 = (vv % G::DVW) / 16, l2 = 16 * ((a % 16) / 4) + vv % 16;
+            PT[rt][ct][i] = rec[rec_frag<true, D>(w2, a / 16, ct2, l2) + a % 4];
+          }
+        }
+    }
+    const __amdgpu_buffer_rsrc_t rdv = rsrc(dv);
+    unsigned meet = 0;
+    for (int st = 0; st < nsteps; ++st) {
+      const int j = st - 1;
+      if (j >= 0 && j < ns) {  // uniform over the MMA waves
+        const int c = sub(j), nv = min(C2, si.len - c * C2);
+        const int pb = (j & 1);
+        const uint16_t* cQ = sQ + pb * BUF;
+        const uint16_t* cK = sK + pb * BUF;
+        const uint16_t* cV = sV + pb * BUF;
+        const uint16_t* cG = sG + pb * BUF;
+        const uint16_t* cH = sH + pb * BUF;
+        const float* cI = sI + pb * C2;
+        const float* pc = sP + pb * D;
+        // ---- phase A (waves 0, 1): key tile kt = wave
+        if (wave < 2) {
+          const int kt = wave;
+          const int key = kt * 16 + c16;
+          Frag<true> Kf[KB], Vf[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            Kf[kb] = lds_frag<true>(cK, G::ROWP, key, kb, g);
+            Vf[kb] = lds_frag<true>(cV, G::ROWP, key, kb, g);
+          }
+          floatx4 Aq[2], Bq[2];  // rows = queries of tile tt, column = this lane's key
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            Aq[tt] = Bq[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (tt >= kt) {
+#pragma unroll
+              for (int kb = 0; kb < KB; ++kb) {
+                Aq[tt] = mma(lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb, g), Kf[kb], Aq[tt]);
+                Bq[tt] = mma(lds_frag<true>(cG, G::ROWP, tt * 16 + c16, kb, g), Vf[kb], Bq[tt]);
+              }
+            }
+          }
+          floatx4 xa[2], xb[2];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int t = tt * 16 + 4 * g + i;
+              const bool after = tt > kt || (tt == kt && 4 * g + i > c16);
+              const bool self = tt == kt && 4 * g + i == c16;
+              const float ri = cI[t];
+              xa[tt][i] = (after || self) ? Aq[tt][i] * ri : 0.f;
+              xb[tt][i] = after ? __builtin_fmaf(Bq[tt][i], ri, sGd[pb * C2 + t]) : (self ? sBd[pb * C2 + t] : 0.f);
+            }
+          sAp[kt * 64 + lane] = acc_frag<true>(xa[0], xa[1]);
+          sBp[kt * 64 + lane] = acc_frag<true>(xb[0], xb[1]);
+        }
+        meet += 4;
+        mma_wave_sync(&sArrive, meet, lane);
+        // ---- phase B: this wave's rows of dK'^T and dV^T, then the states
+        if (wave < NW) {
+          float* dkb = sdK + pb * C2 * FP;
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            floatx4 y[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              Frag<true> ph, pl;
+              split_frag<D>(PT[2 * kb][ct], PT[2 * kb + 1][ct], ph, pl);
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt) {
+                const Frag<true> vr = lds_frag<true>(cV, G::ROWP, kt * 16 + c16, kb, g);
+                y[kt] = mma(ph, vr, y[kt]);
+                y[kt] = mma(pl, vr, y[kt]);
+              }
+            }
+            const int a0 = wave * G::DVW + 16 * ct + 4 * g;
+            const Frag<true> qt = lds_frag_tr(cQ, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              y[kt] = mma(qt, sBp[kt * 64 + lane], y[kt]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) y[kt][i] += pc[a0 + i];
+              *reinterpret_cast<floatx4*>(dkb + (kt * 16 + c16) * FP + a0) = y[kt];
+            }
+          }
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            floatx4 z[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              Frag<true> ph, pl;
+              split_frag<D>(PM[2 * kb][ct], PM[2 * kb + 1][ct], ph, pl);
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt) {
+                const Frag<true> kr = lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb, g);
+                z[kt] = mma(ph, kr, z[kt]);
+                z[kt] = mma(pl, kr, z[kt]);
+              }
+            }
+            const int v0 = wave * G::DVW + 16 * ct + 4 * g;
+            const Frag<true> gt = lds_frag_tr(cG, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              z[kt] = mma(gt, sAp[kt * 64 + lane], z[kt]);
+              const int key = kt * 16 + c16;
+              const int off = ((c * C2 + key) * D + v0) * 2;  // keys past the segment are dropped
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(z[kt][0], z[kt][1]), pack_bf2(z[kt][2], z[kt][3])},
+                                                    rdv, key < nv ? off : seg_bytes, 0, kLoadStream);
+            }
+          }
+          // P^T += G^T Q^ and P += Q^^T G (the 32 tokens are one k-block)
+          Frag<true> Hc[CT], Gc[CT];
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            Hc[ct] = lds_frag_tr(cH, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+            Gc[ct] = lds_frag_tr(cG, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+          }
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const Frag<true> gr = lds_frag_tr(cG, G::ROWP, 0, 16 * rt, lane);
+            const Frag<true> hr = lds_frag_tr(cH, G::ROWP, 0, 16 * rt, lane);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+              PT[rt][ct] = mma(gr, Hc[ct], PT[rt][ct]);
+              PM[rt][ct] = mma(hr, Gc[ct], PM[rt][ct]);
+            }
+          }
+        }
+        if (wave == 0) {  // p after this sub-chunk, into the other parity: p += Q^^T (gd den)
+          Frag<true> w_hi, w_lo;
+          token_col_frags(sW + pb * C2, 0, g, w_hi, w_lo);
+          float* pn = sP + ((j + 1) & 1) * D;
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const Frag<true> hr = lds_frag_tr(cH, G::ROWP, 0, 16 * rt, lane);
+            floatx4 pv = mma(hr, w_hi, floatx4{0.f, 0.f, 0.f, 0.f});
+            pv = mma(hr, w_lo, pv);
+            if (c16 < 4) pn[rt * 16 + 4 * g + c16] = pc[rt * 16 + 4 * g + c16] + pv[c16];
+          }
+        }
+      }
+      __syncthreads();  // Y
+    }
+  }
+  // RMSNorm-weight partials of k from the two backward-mapper waves
+  __syncthreads();  // every wave is done with LDS
+  if (wave >= 6) {
+    const int m = tid & 7;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1) {
+        dg1[e] += __shfl_xor(dg1[e], o);
+        dg2[e] += __shfl_xor(dg2[e], o);
+      }
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        sdK[(wave - 6) * D + m * E + e] = dg1[e];
+        sdK[(wave - 6) * D + G::HALF + m * E + e] = dg2[e];
+      }
+    }
+  }
+  __syncthreads();
+  float* dst = dg_part + ((size_t)seg * H + h) * 2 * D + D;
+  for (int i = tid; i < D; i += 512) dst[i] = sdK[i] + sdK[D + i];
+}
+
+// ----------------------------------------------------------------------------------------
 // bwd_dgamma: RMSNorm-weight gradients, the per-segment partials summed in segment order
 // (deterministic): part[(seg H + h) 2D + j] (q: j < D, k: D + j).
 
@@ -1071,7 +1145,7 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   e = launch_scan_suffix(p, a.ws, pstates, s);
   if (e != hipSuccess) return e;
   mark(6);
-  hipLaunchKernelGGL((bwd_dkv_kernel<D>), grid, dim3(256), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
+  hipLaunchKernelGGL((bwd_dkv_ws_kernel<D>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
                      pstates, den, gd, bd, static_cast<uint16_t*>(b.dk), static_cast<uint16_t*>(b.dv), dgp, p.H, p.L,
                      a.rms_eps);
   mark(7);
