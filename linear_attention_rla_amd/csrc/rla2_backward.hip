@@ -147,32 +147,6 @@ __device__ __forceinline__ void map_backward(const Raw<true, D>& r, Raw<true, D>
   }
 }
 
-// Sum the lane's RMSNorm-weight partials over the 32 lanes and 4 waves sharing its dims and
-// write them (D floats) to dst. `scratch` holds at least 4 * D floats of LDS.
-template <int D>
-__device__ __forceinline__ void reduce_dgamma(float* scratch, float* dst, int tid, float (&dg1)[Geo<true, D>::E],
-                                              float (&dg2)[Geo<true, D>::E]) {
-  using G = Geo<true, D>;
-  const int wave = tid >> 6, lane = tid & 63, m = tid & 7;
-#pragma unroll
-  for (int e = 0; e < G::E; ++e) {
-#pragma unroll
-    for (int o = 8; o < 64; o <<= 1) {
-      dg1[e] += __shfl_xor(dg1[e], o);
-      dg2[e] += __shfl_xor(dg2[e], o);
-    }
-  }
-  __syncthreads();
-  if (lane < 8) {
-#pragma unroll
-    for (int e = 0; e < G::E; ++e) {
-      scratch[wave * D + m * G::E + e] = dg1[e];
-      scratch[wave * D + G::HALF + m * G::E + e] = dg2[e];
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < D; i += 256) dst[i] = scratch[i] + scratch[D + i] + scratch[2 * D + i] + scratch[3 * D + i];
-}
 
 // ----------------------------------------------------------------------------------------
 // bwd_pstate: per (segment, head), the segment's totals of the reverse states,
