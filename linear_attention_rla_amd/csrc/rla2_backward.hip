@@ -986,14 +986,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
             floatx4 z[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-              Frag<true> ph, pl;
-              split_frag<D>(PM[2 * kb][ct], PM[2 * kb + 1][ct], ph, pl);
+              // the value gradient has no cancelling terms: P rounded to bf16 once is enough here
+              const Frag<true> ph = acc_frag<true>(PM[2 * kb][ct], PM[2 * kb + 1][ct]);
 #pragma unroll
-              for (int kt = 0; kt < 2; ++kt) {
-                const Frag<true> kr = lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb, g);
-                z[kt] = mma(ph, kr, z[kt]);
-                z[kt] = mma(pl, kr, z[kt]);
-              }
+              for (int kt = 0; kt < 2; ++kt) z[kt] = mma(ph, lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb, g), z[kt]);
             }
             const int v0 = wave * G::DVW + 16 * ct + 4 * g;
             const Frag<true> gt = lds_frag_tr(cG, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
