@@ -332,6 +332,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
   __shared__ __attribute__((aligned(16))) float sdQ[2 * C2 * FP];
   __shared__ Frag<true> sB[2 * 64];                    // B^T operands of query tiles 0, 1
   __shared__ __attribute__((aligned(16))) float sZ[2 * D];  // z before the sub-chunk, by parity
+  // z as an MFMA A operand, by parity: row 0 = bf16(z), row 1 = bf16(z - bf16(z)), other rows 0,
+  // so Z Q'^T gives q'.z (to ~2^-17 relative) in rows 0 + 1 of each query column
+  __shared__ Frag<true> sZf[2 * KB * 64];
   __shared__ float sIdot[4 * C2];                      // each MMA wave's part of q' . (S g)
   __shared__ float sInv[C2], sGd[C2];
   __shared__ unsigned sArrive;
@@ -352,7 +355,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
   const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
   if (tid < D) sZ[tid] = rec[D * D + tid];
   if (tid == 0) sArrive = 0u;
+  for (int i = tid; i < 2 * KB * 64; i += 512) sZf[i] = Frag<true>{};
   __syncthreads();
+  // the two data lanes of each z fragment: slot (g, j) of fragment kb holds dim kb 32 + 4g + j
+  // (j < 4) or kb 32 + 16 + 4g + j - 4; lane 16g holds bf16(z), lane 16g + 1 the remainder.
+  // Called by one wave: lane l converts dims 2l, 2l + 1.
+  auto put_zf = [&](Frag<true>* zf, const float* zsrc) {
+    uint16_t* zf16 = reinterpret_cast<uint16_t*>(zf);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int dim = 2 * lane + x;
+      if (dim < D) {
+        const int kb2 = dim / 32, r = dim % 32;
+        const int gg = (r & 15) >> 2, jj = (r & 3) + (r >> 4) * 4;
+        const float zv = zsrc[dim];
+        const uint32_t hw = pack_bf2(zv, 0.f);
+        zf16[(kb2 * 64 + 16 * gg) * 8 + jj] = static_cast<uint16_t>(hw & 0xffffu);
+        zf16[(kb2 * 64 + 16 * gg + 1) * 8 + jj] = static_cast<uint16_t>(pack_bf2(zv - bf_lo(hw), 0.f) & 0xffffu);
+      }
+    }
+  };
   float dg1[E], dg2[E];  // RMSNorm-weight partials (backward mappers)
 #pragma unroll
   for (int e = 0; e < E; ++e) dg1[e] = dg2[e] = 0.f;
@@ -481,6 +503,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         }
       }
   }
+  if (wave == 0) put_zf(sZf, sZ);  // parity 0: z before the first sub-chunk
   unsigned meet = 0;
   for (int st = 0; st < nsteps; ++st) {
     const int c = st - 1;
@@ -535,11 +558,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       float rs_o = 0.f, dot_o = 0.f, sself = 0.f, bself = 0.f, qz = 0.f;
       if (wave < 2) {
         Frag<true> Qf[KB], Gt[KB];  // the query tile's rows (read again: no runtime register index)
+        floatx4 zq = floatx4{0.f, 0.f, 0.f, 0.f};
+        const Frag<true>* zf = sZf + (c & 1) * KB * 64;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           Qf[kb] = lds_frag<true>(cQ, G::ROWP, t, kb, g);
           Gt[kb] = lds_frag<true>(cG, G::ROWP, t, kb, g);
+          zq = mma(zf[kb * 64 + lane], Qf[kb], zq);
         }
+        if (g == 0) qz = zq[0] + zq[1];  // q'_t . z (rows 0, 1 of Z Q'^T)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           At[kt] = Bt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -563,17 +590,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
             sself += self ? sc : 0.f;
             bself += self ? Bt[kt][i] : 0.f;
           }
-        // q'_t . z over the lane's quarter of the dims, a in [D/4 g, D/4 (g + 1))
-        {
-          constexpr int QD = D / 4;
-          const uint16_t* qrow = cQ + t * G::ROWP + QD * g;
-#pragma unroll
-          for (int j = 0; j < QD; j += 2) {
-            const uint32_t w2 = *reinterpret_cast<const uint32_t*>(qrow + j);
-            qz = __builtin_fmaf(bf_lo(w2), zc[QD * g + j], qz);
-            qz = __builtin_fmaf(bf_hi(w2), zc[QD * g + j + 1], qz);
-          }
-        }
         rs_o = sum_rows4(rs_o);
         dot_o = sum_rows4(dot_o);
         sself = sum_rows4(sself);
@@ -646,7 +662,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
           for (int ct = 0; ct < CT; ++ct) ST[rt][ct] = mma(av, Kc[ct], ST[rt][ct]);
         }
       }
-      if (wave == 0) {  // z after this sub-chunk, into the other parity
+      if (wave == 0) {  // z after this sub-chunk and its operand form, into the other parity
         const Frag<true> ones = ones_frag<true>();
         float* zn = sZ + ((c + 1) & 1) * D;
 #pragma unroll
@@ -654,6 +670,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
           const floatx4 zs = mma(lds_frag_tr(cK, G::ROWP, 0, 16 * at, lane), ones, floatx4{0.f, 0.f, 0.f, 0.f});
           if (c16 < 4) zn[at * 16 + 4 * g + c16] = zc[at * 16 + 4 * g + c16] + zs[c16];
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        put_zf(sZf + ((c + 1) & 1) * KB * 64, zn);
       }
     }
     __syncthreads();  // Y
