@@ -172,6 +172,33 @@ __device__ __forceinline__ Frag<true> lds_frag_tr(const uint16_t* base, int pitc
   return f;
 }
 
+// Row fragment in the contiguous slot order: lane (c16, g) gets elements [row][32 kb + 8g + j],
+// j < 8, in one 16-byte read. Both operands of a contraction must use the same slot order;
+// for accumulator-born operands this is arranged by the tile-to-dim map of the accumulators.
+__device__ __forceinline__ Frag<true> lds_frag_c(const uint16_t* base, int pitch, int row, int kb, int g) {
+  Frag<true> f;
+  copy_bytes<16>(&f.v, base + row * pitch + kb * 32 + 8 * g);
+  return f;
+}
+
+// lds_frag_tr for the contiguous slot order: the 16 operand rows are columns c0 + 8a + b
+// (row 4a + b, a, b < 4) of the row-major array, so an accumulator tile built from it holds,
+// in lane (c, g), the columns c0 + 8g + i. Tiles c0 = 32 kb and c0 = 32 kb + 4 then pair up
+// (acc_frag) into a contiguous-order operand over columns 32 kb .. 32 kb + 31.
+__device__ __forceinline__ Frag<true> lds_frag_tr_s8(const uint16_t* base, int pitch, int k0, int c0, int lane) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const int c16 = lane & 15, g = lane >> 4;
+  const uint16_t* p = base + (k0 + 4 * g + (c16 >> 2)) * pitch + c0 + 8 * (c16 & 3);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * pitch));
+  Frag<true> f;
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  const v8i16 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  f.v = __builtin_bit_cast(bf16x8, w);
+  return f;
+}
+
 // Operand whose every element is 1 (against it, K'^T gives the column sums of K').
 template <bool BF>
 __device__ __forceinline__ Frag<BF> ones_frag() {
@@ -387,6 +414,15 @@ __device__ __forceinline__ int rec_frag(int w, int rt, int ct, int l) {
   return (((w * G::RT + rt) * G::CT + ct) * 64 + l) * 4;
 }
 
+// The record read into the contiguous-order tile map (lds_frag_tr_s8): in tile pt, lane (c, g)
+// row i holds dim 32 (pt / 2) + 8g + 4 (pt % 2) + i, which the record keeps in tile
+// 2 (pt / 2) + g / 2 at lane (c, 2 (g % 2) + pt % 2), row i.
+template <int D>
+__device__ __forceinline__ int rec_frag_c(int w, int pt, int ct, int lane) {
+  const int c16 = lane & 15, g = lane >> 4;
+  return rec_frag<true, D>(w, 2 * (pt / 2) + g / 2, ct, 16 * (2 * (g % 2) + pt % 2) + c16);
+}
+
 // The same map with every per-lane constant in registers: g1[e], g2[e] = gamma of dims
 // j, j + D/2 (j = m*E + e); lo[tok][e] = (cos, sin) of (t0 + tok)*theta_j; hi[e] = (cos, sin)
 // of 64*a*theta_j for the chunk's first position 64*a.
@@ -441,13 +477,14 @@ __device__ __forceinline__ void feature_map_qk(const Raw<BF, D>& rq, const Raw<B
 
 // Store a lane's pair tokens row-major into [64][ROWP].
 template <bool BF, int D>
-__device__ __forceinline__ void store_rows(typename Elem<BF>::St* dst, const Raw<BF, D>& o, int t0, int m) {
+__device__ __forceinline__ void store_rows(typename Elem<BF>::St* dst, const Raw<BF, D>& o, int t0, int m,
+                                           int pitch = Geo<BF, D>::ROWP) {
   using G = Geo<BF, D>;
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      copy_bytes<G::E * G::ES>(dst + (t0 + tok) * G::ROWP + h * G::HALF + m * G::E, o.w[tok][h]);
+      copy_bytes<G::E * G::ES>(dst + (t0 + tok) * pitch + h * G::HALF + m * G::E, o.w[tok][h]);
 }
 
 // Store a lane's pair tokens transposed into [D][COLP]: one 2-token word per dim.

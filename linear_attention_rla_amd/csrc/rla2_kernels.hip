@@ -697,7 +697,8 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
 //
 // Step s (s = 0 .. nsteps-1): mappers map chunk s into buffer s % 2; MMA waves process chunk
 // s - 1 from buffer (s - 1) % 2. One workgroup barrier per step (Y, at its end: buffer s % 2
-// is complete, buffer (s - 1) % 2 is free again, the z update of chunk s - 1 is visible).
+// is complete, buffer (s - 1) % 2 is free again, the z operand for chunk s, written in the
+// score phase of chunk s - 1, is visible).
 // Inside the step the MMA waves also meet among themselves (score tiles and row reciprocals
 // of every query tile are complete before anyone forms outputs) on an LDS arrival counter,
 // which the mappers never wait on.
@@ -706,31 +707,35 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
 // (kt <= TT) and Z Q'_TT^T, the diagonal tile masked, every weight rounded to bf16 once
 // (pairs of tiles packed as the B operands of V^T A^T); the row sums are taken from the
 // packed weights with a bf16 dot against ones, so numerator and denominator use the same
-// weights. The wave also forms the column sums of K' for row tiles [Z0, Z1). Every LDS
+// weights. The wave also forms the column sums of K' for row tiles [Z0, Z1): lane (i, g),
+// i < 4, keeps z of dim 16 tile + 4g + i in zreg, adds the chunk's column sum and writes the
+// result as the next chunk's z operand (zf_next, the other buffer of the pair). Every LDS
 // operand is requested before the first MFMA.
 // L2: no q'.z and no column sums; the row's sum of squared weights goes to sInv instead.
-template <int D, int TT, int Z0, int Z1, bool L2 = false>
-__device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK, const Frag<true>* sZf,
-                                         Frag<true>* sA, float* sInv, float* sDz, float eps, int lane) {
+template <int D, int TT, int Z0, int Z1, int NZR, bool L2 = false>
+__device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK, int qp, const Frag<true>* sZf,
+                                         Frag<true>* zf_next, float (&zreg)[NZR], Frag<true>* sA, float* sInv,
+                                         float eps, int lane) {
   using G = Geo<true, D>;
   constexpr int KB = G::KB, NZ = Z1 - Z0, NP = TT / 2 + 1;
   static_assert(!L2 || NZ == 0, "");
+  static_assert(NZ <= NZR, "");
   const int c16 = lane & 15, g = lane >> 4;
   Frag<true> Qf[KB], Kf[TT + 1][KB], Zf[KB], Ct[NZ > 0 ? NZ : 1][2];
 #pragma unroll
-  for (int kb2 = 0; kb2 < KB; ++kb2) Qf[kb2] = lds_frag<true>(cQ, G::ROWP, TT * 16 + c16, kb2, g);
+  for (int kb2 = 0; kb2 < KB; ++kb2) Qf[kb2] = lds_frag_c(cQ, qp, TT * 16 + c16, kb2, g);
 #pragma unroll
   for (int kt = 0; kt <= TT; ++kt)
 #pragma unroll
-    for (int kb2 = 0; kb2 < KB; ++kb2) Kf[kt][kb2] = lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb2, g);
+    for (int kb2 = 0; kb2 < KB; ++kb2) Kf[kt][kb2] = lds_frag_c(cK, qp, kt * 16 + c16, kb2, g);
   if constexpr (!L2) {
 #pragma unroll
     for (int kb2 = 0; kb2 < KB; ++kb2) Zf[kb2] = sZf[kb2 * 64 + lane];
   }
 #pragma unroll
   for (int z = 0; z < NZ; ++z) {
-    Ct[z][0] = lds_frag_tr(cK, G::ROWP, 0, 16 * (Z0 + z), lane);
-    Ct[z][1] = lds_frag_tr(cK, G::ROWP, 32, 16 * (Z0 + z), lane);
+    Ct[z][0] = lds_frag_tr(cK, qp, 0, 16 * (Z0 + z), lane);
+    Ct[z][1] = lds_frag_tr(cK, qp, 32, 16 * (Z0 + z), lane);
   }
   floatx4 At[TT + 1];
 #pragma unroll
@@ -780,7 +785,17 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
     for (int z = 0; z < NZ; ++z) {
       floatx4 zc = mma(Ct[z][0], ones, floatx4{0.f, 0.f, 0.f, 0.f});
       zc = mma(Ct[z][1], ones, zc);  // every column holds the sums of rows 16 (Z0 + z) + 4g + i
-      if (c16 < 4) sDz[(Z0 + z) * 16 + 4 * g + c16] = zc[c16];
+      if (c16 < 4) {
+        // dim 16 T + 4g + i (T = Z0 + z) sits in fragment T / 2, slot 4 (g % 2) + i of lane
+        // 16 (2 (T % 2) + g / 2) (bf16 of z) and of the lane after it (the remainder)
+        const int T = Z0 + z;
+        zreg[z] += c16 == 0 ? zc[0] : c16 == 1 ? zc[1] : c16 == 2 ? zc[2] : zc[3];
+        const __bf16 hi = static_cast<__bf16>(zreg[z]);
+        const __bf16 lo = static_cast<__bf16>(zreg[z] - static_cast<float>(hi));
+        uint16_t* zf16 = reinterpret_cast<uint16_t*>(zf_next + (T / 2) * 64 + 16 * (2 * (T % 2) + g / 2));
+        zf16[4 * (g % 2) + c16] = __builtin_bit_cast(uint16_t, hi);
+        zf16[8 + 4 * (g % 2) + c16] = __builtin_bit_cast(uint16_t, lo);
+      }
     }
   }
 }
@@ -803,18 +818,20 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   using St = uint16_t;
   using EL = Elem<true>;
   using R = Raw<true, D>;
-  constexpr int BUF = kChunk * G::ROWP;  // elements of one operand buffer
-  __shared__ __attribute__((aligned(16))) St sQ[2 * BUF];
-  __shared__ __attribute__((aligned(16))) St sK[2 * BUF];
+  constexpr int BUF = kChunk * G::ROWP;  // elements of one V or output buffer
+  // Q' and K' rows at a pitch of D + 16: the 16-byte row-fragment reads (lds_frag_c) and the
+  // transposing reads of K' are then free of bank conflicts
+  constexpr int QP = D + 16, BUFQ = kChunk * QP;
+  __shared__ __attribute__((aligned(16))) St sQ[2 * BUFQ];
+  __shared__ __attribute__((aligned(16))) St sK[2 * BUFQ];
   __shared__ __attribute__((aligned(16))) St sV[2 * BUF];
   __shared__ __attribute__((aligned(16))) St sO[2 * BUF];  // output rows of chunk c in buffer c % 2
   __shared__ Frag<true> sA[4 * 2 * 64];  // [query tile][key block][lane]: B operands of V^T A^T
-  __shared__ __attribute__((aligned(16))) float sZ[D];
-  __shared__ float sDz[D];  // column sums of the chunk's K', added to z after the score phase
   __shared__ float sInv[kChunk];
   // z as an MFMA A operand: row 0 = bf16(z), row 1 = bf16(z - bf16(z)), rows 2..15 = 0, so
-  // Z Q'^T gives q'.z (to ~2^-17 relative) in rows 0 + 1 of each query column
-  __shared__ Frag<true> sZf[G::KB * 64];
+  // Z Q'^T gives q'.z (to ~2^-17 relative) in rows 0 + 1 of each query column; z before
+  // chunk c in buffer c % 2
+  __shared__ Frag<true> sZf[2 * G::KB * 64];
   __shared__ unsigned sArrive;  // MMA-wave arrivals (mma_wave_sync)
   // L2, by step parity: rows' sums of squared weights (MMA waves) and the mappers' parts of
   // q'^T A_prev q', for the chunk the MMA waves processed in that step
@@ -837,18 +854,17 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
   const int seg_bytes = si.len * D * 2;
   const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
-  if (tid < D) sZ[tid] = rec[D * D + tid];
   if (tid == 0) sArrive = 0u;
-  // z operand fragments: slot (g, j) of fragment kb holds dim kb*32 + 4g + j (j < 4) or
-  // kb*32 + 16 + 4g + j - 4; lane 16g holds bf16(z) there, lane 16g + 1 the residual, every
-  // other lane zeros (written once). Wave 0 refreshes the two data lanes of each fragment:
-  // lane l converts dims 2l, 2l + 1.
+  // z operand fragments (contiguous slot order): slot (g, j) of fragment kb holds dim
+  // kb*32 + 8g + j; lane 16g holds bf16(z) there, lane 16g + 1 the residual, every other lane
+  // zeros (written once). The initial z goes to buffer 0 (lane l converts dims 2l, 2l + 1);
+  // later buffers are written by the column-sum lanes in the score phase.
   auto put_zf = [&](const float* zsrc) {
     uint16_t* zf16 = reinterpret_cast<uint16_t*>(sZf);
 #pragma unroll
     for (int x = 0; x < 2 && 2 * lane + x < D; ++x) {
       const int dim = 2 * lane + x, kb2 = dim / 32, r = dim % 32;
-      const int gg = (r & 15) >> 2, j = (r & 3) + (r >> 4) * 4;
+      const int gg = r >> 3, j = r & 7;
       const float zv = zsrc[dim];
       const __bf16 hi = static_cast<__bf16>(zv);
       const __bf16 lo = static_cast<__bf16>(zv - static_cast<float>(hi));
@@ -856,7 +872,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       zf16[(kb2 * 64 + 16 * gg + 1) * 8 + j] = __builtin_bit_cast(uint16_t, lo);
     }
   };
-  for (int i = tid; i < G::KB * 64; i += 512) sZf[i] = Frag<true>{};
+  for (int i = tid; i < 2 * G::KB * 64; i += 512) sZf[i] = Frag<true>{};
   if constexpr (L2) {
     for (int i = tid; i < 2 * D; i += 512) sGam[i] = i < D ? gamma_q[(size_t)h * D + i] : gamma_k[(size_t)h * D + i - D];
   }
@@ -902,7 +918,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct)
-          Am[rt][ct] = *reinterpret_cast<const floatx4*>(arec + rec_frag<true, D>(wv, rt, ct, lane));
+          Am[rt][ct] = *reinterpret_cast<const floatx4*>(arec + rec_frag_c<D>(wv, rt, ct, lane));
     }
     // Every step issues the same loads (chunks past the end read zeros from the buffer
     // range check), so the compiler's wait counts let chunk st + 1 stay in flight while
@@ -937,9 +953,9 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
             put_pairs<true, D>(ok, tok, e, k1, k2);
           }
         }
-        store_rows<true, D>(sQ + bm, oq, t0, m);
+        store_rows<true, D>(sQ + (st & 1) * BUFQ, oq, t0, m, QP);
         store_rows<true, D>(sV + bm, r[2], t0, m);
-        store_rows<true, D>(sK + bm, ok, t0, m);
+        store_rows<true, D>(sK + (st & 1) * BUFQ, ok, t0, m, QP);
       }
       {  // chunk st - 2's output rows, staged by the MMA waves in sO[st % 2], leave as whole
          // rows. The same stores are issued every step: rows past the segment (and every row
@@ -972,8 +988,8 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       if constexpr (L2) {  // chunk st - 1 (the MMA waves' chunk of this step): A-side of its denominators
         const int cc = st - 1;
         if (cc >= 0 && cc < nch && mw < G::NW) {
-          const St* cQ = sQ + ((st + 1) & 1) * BUF;
-          const St* cK = sK + ((st + 1) & 1) * BUF;
+          const St* cQ = sQ + ((st + 1) & 1) * BUFQ;
+          const St* cK = sK + ((st + 1) & 1) * BUFQ;
           const int c16 = lane & 15, g = lane >> 4;
           // one query tile at a time (a rolled loop keeps the mappers' registers for A)
 #pragma unroll 1
@@ -985,9 +1001,9 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
               for (int kb2 = 0; kb2 < G::KB; ++kb2)  // A_prev (symmetric) rounded to bf16 as the A operand
                 y = mma(acc_frag<true>(Am[2 * kb2][ct], Am[2 * kb2 + 1][ct]),
-                        lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb2, g), y);
+                        lds_frag_c(cQ, QP, tt * 16 + c16, kb2, g), y);
               const int col = mw * G::DVW + ct * 16 + 4 * g;
-              const uint2 qa = *reinterpret_cast<const uint2*>(cQ + (tt * 16 + c16) * G::ROWP + col);
+              const uint2 qa = *reinterpret_cast<const uint2*>(cQ + (tt * 16 + c16) * QP + col);
               part = __builtin_fmaf(__uint_as_float(qa.x << 16), y[0], part);
               part = __builtin_fmaf(__uint_as_float(qa.x & 0xffff0000u), y[1], part);
               part = __builtin_fmaf(__uint_as_float(qa.y << 16), y[2], part);
@@ -1000,10 +1016,10 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
           for (int kb2 = 0; kb2 < 2; ++kb2) {  // A += K'^T K' (this mapper's columns)
             Frag<true> Kc[G::CT];
 #pragma unroll
-            for (int ct = 0; ct < G::CT; ++ct) Kc[ct] = lds_frag_tr(cK, G::ROWP, 32 * kb2, mw * G::DVW + ct * 16, lane);
+            for (int ct = 0; ct < G::CT; ++ct) Kc[ct] = lds_frag_tr(cK, QP, 32 * kb2, mw * G::DVW + ct * 16, lane);
 #pragma unroll
             for (int rt = 0; rt < G::RT; ++rt) {
-              const Frag<true> a = lds_frag_tr(cK, G::ROWP, 32 * kb2, 16 * rt, lane);
+              const Frag<true> a = lds_frag_tr_s8(cK, QP, 32 * kb2, 32 * (rt / 2) + 4 * (rt % 2), lane);
 #pragma unroll
               for (int ct = 0; ct < G::CT; ++ct) Am[rt][ct] = mma(a, Kc[ct], Am[rt][ct]);
             }
@@ -1031,22 +1047,35 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   }
 
   // ======== MMA waves: nsteps steps, one workgroup barrier each; step st processes chunk st - 1
-  floatx4 S[G::RT][G::CT];  // running state, value columns of this wave
+  // running state, value columns of this wave, in the contiguous-order tile map: tiles 2kb and
+  // 2kb + 1 pair up (acc_frag) into S^T operands whose slots match the 16-byte Q' fragments
+  floatx4 S[G::RT][G::CT];
   {
     const int wv = wave < G::NW ? wave : 0;
 #pragma unroll
     for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct)
-        S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<true, D>(wv, rt, ct, lane));
+        S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag_c<D>(wv, rt, ct, lane));
   }
   // Accumulation order everywhere below: the contraction block is the outer loop and the
   // independent accumulators the inner one, so consecutive MFMAs never wait on each other.
-  // column sums of K': row tiles [0, ZS) on wave 0, [ZS, RT) on wave 1 (the lighter score waves)
+  // column sums of K': row tiles [0, ZS) on wave 0, [ZS, RT) on wave 1 (the lighter score
+  // waves); their lanes (i, g), i < 4, hold z of dims 16 tile + 4g + i
   constexpr int ZS = G::RT - (3 * G::RT) / 8;
+  constexpr int NZR = ZS > G::RT - ZS ? ZS : G::RT - ZS;
+  float zreg[NZR];
+  {
+    const int z0 = wave == 1 ? ZS : 0;
+#pragma unroll
+    for (int z = 0; z < NZR; ++z) {
+      const int dim = min(16 * (z0 + z) + 4 * g + (c16 & 3), D - 1);
+      zreg[z] = L2 ? 0.f : rec[D * D + dim];
+    }
+  }
   for (int st = 0; st < nsteps; ++st) {
-    const St* cQ = sQ + ((st + 1) & 1) * BUF;  // buffers holding chunk st - 1
-    const St* cK = sK + ((st + 1) & 1) * BUF;
+    const St* cQ = sQ + ((st + 1) & 1) * BUFQ;  // buffers holding chunk st - 1
+    const St* cK = sK + ((st + 1) & 1) * BUFQ;
     const St* cV = sV + ((st + 1) & 1) * BUF;
     const int c = st - 1;
     const bool work = st >= 1 && st <= nch;  // uniform over the MMA waves
@@ -1054,29 +1083,24 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       if constexpr (L2) {
         float* rs2 = sRs2 + (st & 1) * kChunk;
         switch (wave) {
-          case 0: ws_score<D, 0, 0, 0, true>(cQ, cK, sZf, sA, rs2, sDz, eps, lane); break;
-          case 1: ws_score<D, 1, 0, 0, true>(cQ, cK, sZf, sA, rs2, sDz, eps, lane); break;
-          case 2: ws_score<D, 2, 0, 0, true>(cQ, cK, sZf, sA, rs2, sDz, eps, lane); break;
-          default: ws_score<D, 3, 0, 0, true>(cQ, cK, sZf, sA, rs2, sDz, eps, lane); break;
+          case 0: ws_score<D, 0, 0, 0, NZR, true>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
+          case 1: ws_score<D, 1, 0, 0, NZR, true>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
+          case 2: ws_score<D, 2, 0, 0, NZR, true>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
+          default: ws_score<D, 3, 0, 0, NZR, true>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
         }
       } else {
+        const Frag<true>* zf = sZf + (c & 1) * G::KB * 64;  // z before chunk c
+        Frag<true>* zn = sZf + ((c + 1) & 1) * G::KB * 64;  // z before chunk c + 1
         switch (wave) {
-          case 0: ws_score<D, 0, 0, ZS>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
-          case 1: ws_score<D, 1, ZS, G::RT>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
-          case 2: ws_score<D, 2, 0, 0>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
-          default: ws_score<D, 3, 0, 0>(cQ, cK, sZf, sA, sInv, sDz, eps, lane); break;
+          case 0: ws_score<D, 0, 0, ZS, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          case 1: ws_score<D, 1, ZS, G::RT, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          case 2: ws_score<D, 2, 0, 0, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          default: ws_score<D, 3, 0, 0, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
         }
       }
     }
     mma_wave_sync(&sArrive, 4u * (unsigned)(st + 1), lane);
     if (work && wave < G::NW) {  // ---- output, then the state update
-      if (!L2 && wave == 0) {  // every q'.z of this chunk is done: advance z and its operand
-        for (int i = lane; i < D; i += 64) sZ[i] += sDz[i];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        put_zf(sZ);
-      }
       Frag<true> Vf[G::CT][2];
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) {
@@ -1097,7 +1121,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
         for (int ct = 0; ct < G::CT; ++ct) sa[ct] = acc_frag<true>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          const Frag<true> qf = lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb2, g);
+          const Frag<true> qf = lds_frag_c(cQ, QP, tt * 16 + c16, kb2, g);
 #pragma unroll
           for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(sa[ct], qf, o[ct][tt]);
         }
@@ -1133,7 +1157,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int rt = 0; rt < G::RT; ++rt) {
-          const Frag<true> a = lds_frag_tr(cK, G::ROWP, 32 * kb2, 16 * rt, lane);
+          const Frag<true> a = lds_frag_tr_s8(cK, QP, 32 * kb2, 32 * (rt / 2) + 4 * (rt % 2), lane);
 #pragma unroll
           for (int ct = 0; ct < G::CT; ++ct) S[rt][ct] = mma(a, Vf[ct][kb2], S[rt][ct]);
         }
