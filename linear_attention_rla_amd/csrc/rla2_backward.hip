@@ -321,13 +321,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
   using G = Geo<true, D>;
   using R = Raw<true, D>;
   constexpr int C2 = 32;                 // tokens per step
-  constexpr int BUF = C2 * G::ROWP;      // elements of one operand buffer
+  constexpr int BUF = C2 * G::ROWP;      // elements of one raw-q ring buffer
+  // operand rows (q', k', v, dout) at a pitch of D + 16: the 16-byte row-fragment reads
+  // (lds_frag_c) and the transposing reads are then free of bank conflicts
+  constexpr int QP = D + 16, BUFQ = C2 * QP;
   constexpr int FP = D + 4;              // pitch of the fp32 dq' rows
   constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E, NW = G::NW;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * BUFQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BUFQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUFQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2 * BUFQ];
   __shared__ __attribute__((aligned(16))) uint16_t sRq[3 * BUF];  // raw q rows, ring of three
   __shared__ __attribute__((aligned(16))) float sdQ[2 * C2 * FP];
   __shared__ Frag<true> sB[2 * 64];                    // B^T operands of query tiles 0, 1
@@ -357,8 +360,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
   if (tid == 0) sArrive = 0u;
   for (int i = tid; i < 2 * KB * 64; i += 512) sZf[i] = Frag<true>{};
   __syncthreads();
-  // the two data lanes of each z fragment: slot (g, j) of fragment kb holds dim kb 32 + 4g + j
-  // (j < 4) or kb 32 + 16 + 4g + j - 4; lane 16g holds bf16(z), lane 16g + 1 the remainder.
+  // the two data lanes of each z fragment (contiguous slot order): slot (g, j) of fragment kb
+  // holds dim kb 32 + 8g + j; lane 16g holds bf16(z), lane 16g + 1 the remainder.
   // Called by one wave: lane l converts dims 2l, 2l + 1.
   auto put_zf = [&](Frag<true>* zf, const float* zsrc) {
     uint16_t* zf16 = reinterpret_cast<uint16_t*>(zf);
@@ -367,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       const int dim = 2 * lane + x;
       if (dim < D) {
         const int kb2 = dim / 32, r = dim % 32;
-        const int gg = (r & 15) >> 2, jj = (r & 3) + (r >> 4) * 4;
+        const int gg = r >> 3, jj = r & 7;
         const float zv = zsrc[dim];
         const uint32_t hw = pack_bf2(zv, 0.f);
         zf16[(kb2 * 64 + 16 * gg) * 8 + jj] = static_cast<uint16_t>(hw & 0xffffu);
@@ -408,7 +411,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
     R va, vb;  // raw dout of an even / odd sub-chunk
     auto issue = [&](R& x, int c) { load_raw_buf<true, D>(x, rg, c * C2 + t0, m); };
     auto bstep = [&](int st, R& x) {
-      if (st < ns) store_rows<true, D>(sG + (st & 1) * BUF, x, t0, m);
+      if (st < ns) store_rows<true, D>(sG + (st & 1) * BUFQ, x, t0, m, QP);
       issue(x, st + 2);  // into the registers just consumed
       const int c = st - 2;  // same parity as st
       if (c >= 0 && c < ns) {
@@ -451,7 +454,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
     };
     auto fstep = [&](int st, R (&x)[3], float2 (&hr)[E]) {
       if (st < ns) {
-        const int b = (st & 1) * BUF;
+        const int b = (st & 1) * BUFQ;
         R oq, ok;
 #pragma unroll
         for (int tok = 0; tok < 2; ++tok) {
@@ -470,9 +473,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
             put_pairs<true, D>(ok, tok, e, k1, k2);
           }
         }
-        store_rows<true, D>(sQ + b, oq, t0, m);
-        store_rows<true, D>(sK + b, ok, t0, m);
-        store_rows<true, D>(sV + b, x[2], t0, m);
+        store_rows<true, D>(sQ + b, oq, t0, m, QP);
+        store_rows<true, D>(sK + b, ok, t0, m, QP);
+        store_rows<true, D>(sV + b, x[2], t0, m, QP);
         store_rows<true, D>(sRq + (st % 3) * BUF, x[0], t0, m);
       }
       issue(x, hr, st + 2);  // into the registers just consumed
@@ -487,7 +490,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
     }
   } else {
   // ======== MMA waves: step st processes sub-chunk c = st - 1
-  floatx4 ST[RT][CT];  // S^T: rows v = 16 rt + 4g + i, columns a = wave DVW + 16 ct + c16
+  // S^T in the contiguous-order tile map: tile rt, lane (c, g), row i is v = 32 (rt / 2) + 8g +
+  // 4 (rt % 2) + i; columns a = wave DVW + 16 ct + c. Tiles 2kb, 2kb + 1 pair up into operands
+  // whose slots match the 16-byte dout fragments.
+  floatx4 ST[RT][CT];
   {
     const int wv = wave < NW ? wave : 0;
 #pragma unroll
@@ -497,7 +503,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         const int a = wv * G::DVW + 16 * ct + c16;  // record: S[a][v] at its fragment-native place
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int vv = 16 * rt + 4 * g + i;
+          const int vv = 32 * (rt / 2) + 8 * g + 4 * (rt % 2) + i;
           const int w2 = vv / G::DVW, ct2 = (vv % G::DVW) / 16, l2 = 16 * ((a % 16) / 4) + vv % 16;
           ST[rt][ct][i] = rec[rec_frag<true, D>(w2, a / 16, ct2, l2) + a % 4];
         }
@@ -509,10 +515,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
     const int c = st - 1;
     if (c >= 0 && c < ns) {  // uniform over the MMA waves
       const int nv = min(C2, si.len - c * C2);
-      const uint16_t* cQ = sQ + (c & 1) * BUF;
-      const uint16_t* cK = sK + (c & 1) * BUF;
-      const uint16_t* cV = sV + (c & 1) * BUF;
-      const uint16_t* cG = sG + (c & 1) * BUF;
+      const uint16_t* cQ = sQ + (c & 1) * BUFQ;
+      const uint16_t* cK = sK + (c & 1) * BUFQ;
+      const uint16_t* cV = sV + (c & 1) * BUFQ;
+      const uint16_t* cG = sG + (c & 1) * BUFQ;
       const float* zc = sZ + (c & 1) * D;
       // ---- phase A: this wave's rows of S G^T (state as a bf16 pair) and its part of q'.(S g)
       floatx4 Y[CT][2];
@@ -520,7 +526,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) Gf[tt][kb] = lds_frag<true>(cG, G::ROWP, tt * 16 + c16, kb, g);
+        for (int kb = 0; kb < KB; ++kb) Gf[tt][kb] = lds_frag_c(cG, QP, tt * 16 + c16, kb, g);
       if (wave < NW) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -541,7 +547,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
           float part = 0.f;
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
-            const uint2 qa = *reinterpret_cast<const uint2*>(cQ + (tt * 16 + c16) * G::ROWP + wave * G::DVW + 16 * ct + 4 * g);
+            const uint2 qa = *reinterpret_cast<const uint2*>(cQ + (tt * 16 + c16) * QP + wave * G::DVW + 16 * ct + 4 * g);
             part = __builtin_fmaf(bf_lo(qa.x), Y[ct][tt][0], part);
             part = __builtin_fmaf(bf_hi(qa.x), Y[ct][tt][1], part);
             part = __builtin_fmaf(bf_lo(qa.y), Y[ct][tt][2], part);
@@ -562,8 +568,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         const Frag<true>* zf = sZf + (c & 1) * KB * 64;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          Qf[kb] = lds_frag<true>(cQ, G::ROWP, t, kb, g);
-          Gt[kb] = lds_frag<true>(cG, G::ROWP, t, kb, g);
+          Qf[kb] = lds_frag_c(cQ, QP, t, kb, g);
+          Gt[kb] = lds_frag_c(cG, QP, t, kb, g);
           zq = mma(zf[kb * 64 + lane], Qf[kb], zq);
         }
         if (g == 0) qz = zq[0] + zq[1];  // q'_t . z (rows 0, 1 of Z Q'^T)
@@ -573,8 +579,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
           if (kt <= tt) {
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-              At[kt] = mma(lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb, g), Qf[kb], At[kt]);
-              Bt[kt] = mma(lds_frag<true>(cV, G::ROWP, kt * 16 + c16, kb, g), Gt[kb], Bt[kt]);
+              At[kt] = mma(lds_frag_c(cK, QP, kt * 16 + c16, kb, g), Qf[kb], At[kt]);
+              Bt[kt] = mma(lds_frag_c(cV, QP, kt * 16 + c16, kb, g), Gt[kb], Bt[kt]);
             }
           }
         }
@@ -647,17 +653,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
             floatx4 acc = Y[ct][tq];
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc[i], inv, gdv * zc[a0 + i]);
-            acc = mma(lds_frag_tr(cK, G::ROWP, 0, wave * G::DVW + 16 * ct, lane), bf, acc);
+            acc = mma(lds_frag_tr(cK, QP, 0, wave * G::DVW + 16 * ct, lane), bf, acc);
             *reinterpret_cast<floatx4*>(dqb + tc * FP + a0) = acc;
           }
         }
         // S^T += V^T K' (the 32 tokens are one k-block)
         Frag<true> Kc[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) Kc[ct] = lds_frag_tr(cK, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+        for (int ct = 0; ct < CT; ++ct) Kc[ct] = lds_frag_tr(cK, QP, 0, wave * G::DVW + 16 * ct, lane);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const Frag<true> av = lds_frag_tr(cV, G::ROWP, 0, 16 * rt, lane);
+          const Frag<true> av = lds_frag_tr_s8(cV, QP, 0, 32 * (rt / 2) + 4 * (rt % 2), lane);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) ST[rt][ct] = mma(av, Kc[ct], ST[rt][ct]);
         }
@@ -667,7 +673,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         float* zn = sZ + ((c + 1) & 1) * D;
 #pragma unroll
         for (int at = 0; at < RT; ++at) {
-          const floatx4 zs = mma(lds_frag_tr(cK, G::ROWP, 0, 16 * at, lane), ones, floatx4{0.f, 0.f, 0.f, 0.f});
+          const floatx4 zs = mma(lds_frag_tr(cK, QP, 0, 16 * at, lane), ones, floatx4{0.f, 0.f, 0.f, 0.f});
           if (c16 < 4) zn[at * 16 + 4 * g + c16] = zc[at * 16 + 4 * g + c16] + zs[c16];
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
