@@ -740,14 +740,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
   using G = Geo<true, D>;
   using R = Raw<true, D>;
   constexpr int C2 = 32;
-  constexpr int BUF = C2 * G::ROWP;
+  constexpr int BUF = C2 * G::ROWP;  // raw-k ring buffer
+  // operand rows (q', k', v, dout, Q^) at a pitch of D + 16 (conflict-free 16-byte row-fragment
+  // and transposing reads)
+  constexpr int QP = D + 16, BUFQ = C2 * QP;
   constexpr int FP = D + 4;
   constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E, NW = G::NW;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[2 * BUF];
-  __shared__ __attribute__((aligned(16))) uint16_t sH[2 * BUF];   // Q^ rows
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2 * BUFQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BUFQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUFQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sG[2 * BUFQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sH[2 * BUFQ];  // Q^ rows
   __shared__ __attribute__((aligned(16))) uint16_t sRk[3 * BUF];  // raw k rows, ring of three
   __shared__ __attribute__((aligned(16))) float sdK[2 * C2 * FP];
   __shared__ Frag<true> sAp[2 * 64], sBp[2 * 64];  // per key tile: A/den and B (queries x keys)
@@ -810,7 +813,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
     R ga, gb;  // raw dout of an even / odd step
     auto issue = [&](R& x, int j) { load_raw_buf<true, D>(x, rg, sub_ld(j) * C2 + t0, m); };
     auto bstep = [&](int st, R& x) {
-      if (st < ns) store_rows<true, D>(sG + (st & 1) * BUF, x, t0, m);
+      if (st < ns) store_rows<true, D>(sG + (st & 1) * BUFQ, x, t0, m, QP);
       issue(x, st + 2);
       const int j = st - 2;
       if (j >= 0 && j < ns) {
@@ -853,7 +856,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
     };
     auto fstep = [&](int st, R (&x)[3], float2 (&hr)[E]) {
       if (st < ns) {
-        const int c = sub(st), b = (st & 1) * BUF;
+        const int c = sub(st), b = (st & 1) * BUFQ;
         R oq, ok, oh;
 #pragma unroll
         for (int tok = 0; tok < 2; ++tok) {
@@ -881,10 +884,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
         }
         const float inv[2] = {dn[0] > 0.f ? 1.0f / dn[0] : 0.f, dn[1] > 0.f ? 1.0f / dn[1] : 0.f};
         scale_raw<D>(oq, oh, inv);
-        store_rows<true, D>(sQ + b, oq, t0, m);
-        store_rows<true, D>(sK + b, ok, t0, m);
-        store_rows<true, D>(sV + b, x[2], t0, m);
-        store_rows<true, D>(sH + b, oh, t0, m);
+        store_rows<true, D>(sQ + b, oq, t0, m, QP);
+        store_rows<true, D>(sK + b, ok, t0, m, QP);
+        store_rows<true, D>(sV + b, x[2], t0, m, QP);
+        store_rows<true, D>(sH + b, oh, t0, m, QP);
         store_rows<true, D>(sRk + (st % 3) * BUF, x[1], t0, m);
         if (m == 0) {
 #pragma unroll
@@ -909,19 +912,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
     }
   } else {
     // ======== MMA waves: step st processes sub-chunk sub(st - 1)
-    floatx4 PT[RT][CT];  // P^T: rows v = 16 rt + 4g + i, columns a = wave DVW + 16 ct + c16
-    floatx4 PM[RT][CT];  // P: rows a = 16 rt + 4g + i, columns v = wave DVW + 16 ct + c16
+    // both in the contiguous-order tile map: in tile rt, lane (c, g), row i is dim
+    // 32 (rt / 2) + 8g + 4 (rt % 2) + i, so tiles 2kb, 2kb + 1 pair up into operands whose
+    // slots match the 16-byte row fragments
+    floatx4 PT[RT][CT];  // P^T: rows v, columns a = wave DVW + 16 ct + c16
+    floatx4 PM[RT][CT];  // P: rows a, columns v = wave DVW + 16 ct + c16
     {
       const int wv = wave < NW ? wave : 0;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-          PM[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<true, D>(wv, rt, ct, lane));
+          PM[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag_c<D>(wv, rt, ct, lane));
           const int a = wv * G::DVW + 16 * ct + c16;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int vv = 16 * rt + 4 * g + i;
+            const int vv = 32 * (rt / 2) + 8 * g + 4 * (rt % 2) + i;
             const int w2 = vv / G::DVW, ct2 = (vv % G::DVW) / 16, l2 = 16 * ((a % 16) / 4) + vv % 16;
             PT[rt][ct][i] = rec[rec_frag<true, D>(w2, a / 16, ct2, l2) + a % 4];
           }
@@ -934,11 +940,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
       if (j >= 0 && j < ns) {  // uniform over the MMA waves
         const int c = sub(j), nv = min(C2, si.len - c * C2);
         const int pb = (j & 1);
-        const uint16_t* cQ = sQ + pb * BUF;
-        const uint16_t* cK = sK + pb * BUF;
-        const uint16_t* cV = sV + pb * BUF;
-        const uint16_t* cG = sG + pb * BUF;
-        const uint16_t* cH = sH + pb * BUF;
+        const uint16_t* cQ = sQ + pb * BUFQ;
+        const uint16_t* cK = sK + pb * BUFQ;
+        const uint16_t* cV = sV + pb * BUFQ;
+        const uint16_t* cG = sG + pb * BUFQ;
+        const uint16_t* cH = sH + pb * BUFQ;
         const float* cI = sI + pb * C2;
         const float* pc = sP + pb * D;
         // ---- phase A (waves 0, 1): key tile kt = wave
@@ -948,8 +954,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           Frag<true> Kf[KB], Vf[KB];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
-            Kf[kb] = lds_frag<true>(cK, G::ROWP, key, kb, g);
-            Vf[kb] = lds_frag<true>(cV, G::ROWP, key, kb, g);
+            Kf[kb] = lds_frag_c(cK, QP, key, kb, g);
+            Vf[kb] = lds_frag_c(cV, QP, key, kb, g);
           }
           floatx4 Aq[2], Bq[2];  // rows = queries of tile tt, column = this lane's key
 #pragma unroll
@@ -958,8 +964,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
             if (tt >= kt) {
 #pragma unroll
               for (int kb = 0; kb < KB; ++kb) {
-                Aq[tt] = mma(lds_frag<true>(cQ, G::ROWP, tt * 16 + c16, kb, g), Kf[kb], Aq[tt]);
-                Bq[tt] = mma(lds_frag<true>(cG, G::ROWP, tt * 16 + c16, kb, g), Vf[kb], Bq[tt]);
+                Aq[tt] = mma(lds_frag_c(cQ, QP, tt * 16 + c16, kb, g), Kf[kb], Aq[tt]);
+                Bq[tt] = mma(lds_frag_c(cG, QP, tt * 16 + c16, kb, g), Vf[kb], Bq[tt]);
               }
             }
           }
@@ -992,13 +998,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
               split_frag<D>(PT[2 * kb][ct], PT[2 * kb + 1][ct], ph, pl);
 #pragma unroll
               for (int kt = 0; kt < 2; ++kt) {
-                const Frag<true> vr = lds_frag<true>(cV, G::ROWP, kt * 16 + c16, kb, g);
+                const Frag<true> vr = lds_frag_c(cV, QP, kt * 16 + c16, kb, g);
                 y[kt] = mma(ph, vr, y[kt]);
                 y[kt] = mma(pl, vr, y[kt]);
               }
             }
             const int a0 = wave * G::DVW + 16 * ct + 4 * g;
-            const Frag<true> qt = lds_frag_tr(cQ, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+            const Frag<true> qt = lds_frag_tr(cQ, QP, 0, wave * G::DVW + 16 * ct, lane);
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
               y[kt] = mma(qt, sBp[kt * 64 + lane], y[kt]);
@@ -1015,10 +1021,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
               // the value gradient has no cancelling terms: P rounded to bf16 once is enough here
               const Frag<true> ph = acc_frag<true>(PM[2 * kb][ct], PM[2 * kb + 1][ct]);
 #pragma unroll
-              for (int kt = 0; kt < 2; ++kt) z[kt] = mma(ph, lds_frag<true>(cK, G::ROWP, kt * 16 + c16, kb, g), z[kt]);
+              for (int kt = 0; kt < 2; ++kt) z[kt] = mma(ph, lds_frag_c(cK, QP, kt * 16 + c16, kb, g), z[kt]);
             }
             const int v0 = wave * G::DVW + 16 * ct + 4 * g;
-            const Frag<true> gt = lds_frag_tr(cG, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+            const Frag<true> gt = lds_frag_tr(cG, QP, 0, wave * G::DVW + 16 * ct, lane);
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
               z[kt] = mma(gt, sAp[kt * 64 + lane], z[kt]);
@@ -1032,13 +1038,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           Frag<true> Hc[CT], Gc[CT];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
-            Hc[ct] = lds_frag_tr(cH, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
-            Gc[ct] = lds_frag_tr(cG, G::ROWP, 0, wave * G::DVW + 16 * ct, lane);
+            Hc[ct] = lds_frag_tr(cH, QP, 0, wave * G::DVW + 16 * ct, lane);
+            Gc[ct] = lds_frag_tr(cG, QP, 0, wave * G::DVW + 16 * ct, lane);
           }
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            const Frag<true> gr = lds_frag_tr(cG, G::ROWP, 0, 16 * rt, lane);
-            const Frag<true> hr = lds_frag_tr(cH, G::ROWP, 0, 16 * rt, lane);
+            const Frag<true> gr = lds_frag_tr_s8(cG, QP, 0, 32 * (rt / 2) + 4 * (rt % 2), lane);
+            const Frag<true> hr = lds_frag_tr_s8(cH, QP, 0, 32 * (rt / 2) + 4 * (rt % 2), lane);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
               PT[rt][ct] = mma(gr, Hc[ct], PT[rt][ct]);
@@ -1052,7 +1058,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           float* pn = sP + ((j + 1) & 1) * D;
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            const Frag<true> hr = lds_frag_tr(cH, G::ROWP, 0, 16 * rt, lane);
+            const Frag<true> hr = lds_frag_tr(cH, QP, 0, 16 * rt, lane);
             floatx4 pv = mma(hr, w_hi, floatx4{0.f, 0.f, 0.f, 0.f});
             pv = mma(hr, w_lo, pv);
             if (c16 < 4) pn[rt * 16 + 4 * g + c16] = pc[rt * 16 + 4 * g + c16] + pv[c16];
