@@ -377,7 +377,8 @@ __device__ __forceinline__ void feature_map_pair(const Raw<BF, D>& r, Raw<BF, D>
 // load_raw through a buffer resource covering exactly the segment's tokens: reads past the
 // segment's end return zeros without touching memory, so the load is issued
 // unconditionally (a fixed number of loads per chunk keeps the wait counts exact).
-template <bool BF, int D>
+// ONLY >= 0: that token of the pair alone.
+template <bool BF, int D, int ONLY = -1>
 __device__ __forceinline__ void load_raw_buf(Raw<BF, D>& r, __amdgpu_buffer_rsrc_t rs, int tok, int m) {
   using G = Geo<BF, D>;
   constexpr int NB = G::E * G::ES;  // bytes per (token, half) of this lane
@@ -385,6 +386,7 @@ __device__ __forceinline__ void load_raw_buf(Raw<BF, D>& r, __amdgpu_buffer_rsrc
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+      if (ONLY >= 0 && t != ONLY) continue;
       const int off = ((tok + t) * D + hh * G::HALF + m * G::E) * G::ES;
       if constexpr (NB >= 16) {
 #pragma unroll
@@ -476,7 +478,7 @@ __device__ __forceinline__ void feature_map_qk(const Raw<BF, D>& rq, const Raw<B
 }
 
 // Store a lane's pair tokens row-major into [64][ROWP].
-template <bool BF, int D>
+template <bool BF, int D, int ONLY = -1>
 __device__ __forceinline__ void store_rows(typename Elem<BF>::St* dst, const Raw<BF, D>& o, int t0, int m,
                                            int pitch = Geo<BF, D>::ROWP) {
   using G = Geo<BF, D>;
@@ -484,7 +486,7 @@ __device__ __forceinline__ void store_rows(typename Elem<BF>::St* dst, const Raw
   for (int tok = 0; tok < 2; ++tok)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      copy_bytes<G::E * G::ES>(dst + (t0 + tok) * pitch + h * G::HALF + m * G::E, o.w[tok][h]);
+      if (ONLY < 0 || tok == ONLY) copy_bytes<G::E * G::ES>(dst + (t0 + tok) * pitch + h * G::HALF + m * G::E, o.w[tok][h]);
 }
 
 // Store a lane's pair tokens transposed into [D][COLP]: one 2-token word per dim.

@@ -924,18 +924,25 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     // range check), so the compiler's wait counts let chunk st + 1 stay in flight while
     // chunk st is mapped.
     const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * G::E;
-    auto issue = [&](R (&r)[3], float2 (&hi)[G::E], int c) {
-      copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
-      load_raw_buf<true, D>(r[0], rq, c * kChunk + t0, m);
-      load_raw_buf<true, D>(r[1], rk, c * kChunk + t0, m);
+    auto issue = [&](R (&r)[3], float2 (&hi)[G::E], int c) {  // in the order mstep refills
       load_raw_buf<true, D>(r[2], rv, c * kChunk + t0, m);
+      load_raw_buf<true, D, 0>(r[0], rq, c * kChunk + t0, m);
+      load_raw_buf<true, D, 0>(r[1], rk, c * kChunk + t0, m);
+      load_raw_buf<true, D, 1>(r[0], rq, c * kChunk + t0, m);
+      load_raw_buf<true, D, 1>(r[1], rk, c * kChunk + t0, m);
+      copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
     };
     auto mstep = [&](int st, R (&r)[3], float2 (&hi)[G::E]) {
       const int bm = (st & 1) * BUF;
-      if (st < nch) {
-        R oq, ok;
-#pragma unroll
-        for (int tok = 0; tok < 2; ++tok) {
+      // The registers of chunk st are refilled with chunk cn as they free up: v (no mapping)
+      // first, then q and k one token at a time, then the RoPE row, so the loads leave early.
+      const int cn = st + (L2 ? 1 : 2);
+      if (st < nch) store_rows<true, D>(sV + bm, r[2], t0, m);
+      load_raw_buf<true, D>(r[2], rv, cn * kChunk + t0, m);
+      auto map_tok = [&](auto tok_c) {
+        constexpr int tok = decltype(tok_c)::value;
+        if (st < nch) {
+          R oq, ok;  // token tok only
           const float invq = rms_inv<true, D>(r[0], tok, rms_eps);
           const float invk = rms_inv<true, D>(r[1], tok, rms_eps);
 #pragma unroll
@@ -952,11 +959,15 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
             put_pairs<true, D>(oq, tok, e, q1, q2);
             put_pairs<true, D>(ok, tok, e, k1, k2);
           }
+          store_rows<true, D, tok>(sQ + (st & 1) * BUFQ, oq, t0, m, QP);
+          store_rows<true, D, tok>(sK + (st & 1) * BUFQ, ok, t0, m, QP);
         }
-        store_rows<true, D>(sQ + (st & 1) * BUFQ, oq, t0, m, QP);
-        store_rows<true, D>(sV + bm, r[2], t0, m);
-        store_rows<true, D>(sK + (st & 1) * BUFQ, ok, t0, m, QP);
-      }
+        load_raw_buf<true, D, tok>(r[0], rq, cn * kChunk + t0, m);
+        load_raw_buf<true, D, tok>(r[1], rk, cn * kChunk + t0, m);
+      };
+      map_tok(std::integral_constant<int, 0>{});
+      map_tok(std::integral_constant<int, 1>{});
+      copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(cn, nch - 1) * G::HALF);
       {  // chunk st - 2's output rows, staged by the MMA waves in sO[st % 2], leave as whole
          // rows. The same stores are issued every step: rows past the segment (and every row
          // when there is no such chunk) fall outside the buffer range and are dropped.
@@ -984,7 +995,6 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
           __builtin_amdgcn_raw_buffer_store_b128(piece, ro, off, 0, kLoadStream);
         }
       }
-      issue(r, hi, st + (L2 ? 1 : 2));  // into the registers just consumed
       if constexpr (L2) {  // chunk st - 1 (the MMA waves' chunk of this step): A-side of its denominators
         const int cc = st - 1;
         if (cc >= 0 && cc < nch && mw < G::NW) {
