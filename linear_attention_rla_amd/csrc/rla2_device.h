@@ -428,7 +428,7 @@ __device__ __forceinline__ int rec_frag_c(int w, int pt, int ct, int lane) {
 // The same map with every per-lane constant in registers: g1[e], g2[e] = gamma of dims
 // j, j + D/2 (j = m*E + e); lo[tok][e] = (cos, sin) of (t0 + tok)*theta_j; hi[e] = (cos, sin)
 // of 64*a*theta_j for the chunk's first position 64*a.
-template <bool BF, int D>
+template <bool BF, int D, int ONLY = -1>  // ONLY >= 0: that token of the pair alone
 __device__ __forceinline__ void feature_map_lane(const Raw<BF, D>& r, Raw<BF, D>& o, const float (&g1)[Geo<BF, D>::E],
                                                  const float (&g2)[Geo<BF, D>::E],
                                                  const float2 (&lo)[2][Geo<BF, D>::E],
@@ -436,6 +436,7 @@ __device__ __forceinline__ void feature_map_lane(const Raw<BF, D>& r, Raw<BF, D>
   using G = Geo<BF, D>;
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok) {
+    if (ONLY >= 0 && tok != ONLY) continue;
     const float inv = rms_inv<BF, D>(r, tok, rms_eps);
 #pragma unroll
     for (int e = 0; e < G::E; e += 2) {

@@ -214,26 +214,41 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_state_kernel(
   for (int zr = 0; zr < ZR; ++zr) zc[zr] = floatx4{0.f, 0.f, 0.f, 0.f};
   const bool zwave = wave * ZR < G::RT;
 
-  auto issue = [&](R (&r)[2], int c) {
-    load_raw_buf<BF, D>(r[0], rk, c * kChunk + t0, m);
+  auto issue = [&](R (&r)[2], int c) {  // bf16: in the order step refills
     load_raw_buf<BF, D>(r[1], rv, c * kChunk + t0, m);
+    load_raw_buf<BF, D>(r[0], rk, c * kChunk + t0, m);
   };
   auto step = [&](int c, R (&r)[2]) {
     __syncthreads();  // the previous chunk's LDS reads are done (the first time: sHi is written)
-    if (c < nch) {
+    if constexpr (BF) {
+      // the registers of chunk c are refilled with chunk c + 2 as they free up: v first, then k
+      // one token at a time
+      if (c < nch) store_rows<BF, D>(sVx, r[1], t0, m);
+      load_raw_buf<BF, D>(r[1], rv, (c + 2) * kChunk + t0, m);
       float2 hi[G::E];
-      copy_bytes<G::E * 8>(hi, sHi + c * G::HALF + m * G::E);
-      R o;
-      feature_map_lane<BF, D>(r[0], o, g1, g2, lo, hi, rms_eps);
-      if constexpr (BF) {
-        store_rows<BF, D>(sKx, o, t0, m);
-        store_rows<BF, D>(sVx, r[1], t0, m);
-      } else {
+      if (c < nch) copy_bytes<G::E * 8>(hi, sHi + c * G::HALF + m * G::E);
+      auto map_tok = [&](auto tok_c) {
+        constexpr int tok = decltype(tok_c)::value;
+        if (c < nch) {
+          R o;
+          feature_map_lane<BF, D, tok>(r[0], o, g1, g2, lo, hi, rms_eps);
+          store_rows<BF, D, tok>(sKx, o, t0, m);
+        }
+        load_raw_buf<BF, D, tok>(r[0], rk, (c + 2) * kChunk + t0, m);
+      };
+      map_tok(std::integral_constant<int, 0>{});
+      map_tok(std::integral_constant<int, 1>{});
+    } else {
+      if (c < nch) {
+        float2 hi[G::E];
+        copy_bytes<G::E * 8>(hi, sHi + c * G::HALF + m * G::E);
+        R o;
+        feature_map_lane<BF, D>(r[0], o, g1, g2, lo, hi, rms_eps);
         store_cols<BF, D>(sKx, o, t0, m);
         store_cols<BF, D>(sVx, r[1], t0, m);
       }
+      issue(r, c + 2);  // into the registers just consumed
     }
-    issue(r, c + 2);  // into the registers just consumed
     __syncthreads();
     if (c < nch && wave < G::NW) {
       Frag<BF> Vf[G::CT][2];
