@@ -531,7 +531,7 @@ __device__ __forceinline__ SegInfo read_seg(const int32_t* tab, int seg) {
   return SegInfo{a.x, a.y, a.z, a.w, tab[(size_t)seg * kTabInts + TAB_HIROW]};
 }
 
-template <bool BF, int D>
+template <bool BF, int D, int ONLY = -1>  // ONLY >= 0: that token of the pair alone
 __device__ __forceinline__ void store_raw_buf(const Raw<BF, D>& r, __amdgpu_buffer_rsrc_t rs, int tok, int m) {
   using G = Geo<BF, D>;
   constexpr int NB = G::E * G::ES;  // bytes per (token, half) of this lane
@@ -539,6 +539,7 @@ __device__ __forceinline__ void store_raw_buf(const Raw<BF, D>& r, __amdgpu_buff
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
+      if (ONLY >= 0 && t != ONLY) continue;
       const int off = ((tok + t) * D + hh * G::HALF + m * G::E) * G::ES;
       if constexpr (NB >= 16) {
 #pragma unroll

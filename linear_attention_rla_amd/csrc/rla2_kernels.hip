@@ -1212,10 +1212,12 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
   using G = Geo<BF, D>;
   using St = typename G::St;
   using R = Raw<BF, D>;
-  constexpr int BUF = kChunk * G::ROWP;     // elements of one row buffer
+  constexpr int BUF = kChunk * G::ROWP;     // elements of one output row buffer
   constexpr int EPP = 16 / G::ES;           // elements per 16-byte piece
   constexpr int PPR = D / EPP;              // 16-byte pieces per row
-  __shared__ __attribute__((aligned(16))) St sQ[2 * BUF];
+  // bf16: Q' rows at a pitch of D + 16 for conflict-free 16-byte row-fragment reads
+  constexpr int QP = BF ? D + 16 : G::ROWP, BUFQ = kChunk * QP;
+  __shared__ __attribute__((aligned(16))) St sQ[2 * BUFQ];
   __shared__ __attribute__((aligned(16))) St sO[2 * BUF];
   __shared__ __attribute__((aligned(16))) float sZ[D];
   __shared__ float sInv[2 * kChunk];
@@ -1244,29 +1246,33 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
     lo[0][e] = rope_lo[t0 * G::HALF + j];
     lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
   }
-  // S^T as the A operand of O^T = S^T Q'^T, value columns of this wave
+  // S^T as the A operand of O^T = S^T Q'^T, value columns of this wave (bf16: read into the
+  // contiguous-order tile map, whose slots match the 16-byte Q' fragments)
   Frag<BF> sa[G::KB][G::CT];
   {
     const int wv = wave < G::NW ? wave : 0;
+    auto tile = [&](int rt, int ct) {
+      if constexpr (BF) return *reinterpret_cast<const floatx4*>(rec + rec_frag_c<D>(wv, rt, ct, lane));
+      else return *reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, rt, ct, lane));
+    };
 #pragma unroll
     for (int kb2 = 0; kb2 < G::KB; ++kb2)
 #pragma unroll
-      for (int ct = 0; ct < G::CT; ++ct)
-        sa[kb2][ct] = acc_frag<BF>(*reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, 2 * kb2, ct, lane)),
-                                   *reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, 2 * kb2 + 1, ct, lane)));
+      for (int ct = 0; ct < G::CT; ++ct) sa[kb2][ct] = acc_frag<BF>(tile(2 * kb2, ct), tile(2 * kb2 + 1, ct));
   }
   const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * G::E;
-  auto issue = [&](R& r, float2 (&hi)[G::E], int c) {
-    copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
+  auto issue = [&](R& r, float2 (&hi)[G::E], int c) {  // in the order map_chunk refills
     load_raw_buf<BF, D>(r, rq, c * kChunk + t0, m);
+    copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
   };
-  // q' of chunk c into sQ[c % 2] with its row reciprocals; then the registers load chunk c + 2
+  // q' of chunk c into sQ[c % 2] with its row reciprocals; the registers are refilled with
+  // chunk c + 2 one token at a time as they free up, then the RoPE row
   auto map_chunk = [&](int c, R& r, float2 (&hi)[G::E]) {
-    R o;
-    feature_map_lane<BF, D>(r, o, g1, g2, lo, hi, rms_eps);
-    store_rows<BF, D>(sQ + (c & 1) * BUF, o, t0, m);
-#pragma unroll
-    for (int tok = 0; tok < 2; ++tok) {
+    auto map_tok = [&](auto tok_c) {
+      constexpr int tok = decltype(tok_c)::value;
+      R o;
+      feature_map_lane<BF, D, tok>(r, o, g1, g2, lo, hi, rms_eps);
+      store_rows<BF, D, tok>(sQ + (c & 1) * BUFQ, o, t0, m, QP);
       float p = 0.f;
 #pragma unroll
       for (int e = 0; e < G::E; ++e) {
@@ -1275,12 +1281,15 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
       }
       p = sum8(p);
       if (m == 0) sInv[(c & 1) * kChunk + t0 + tok] = 1.0f / (p + eps);
-    }
-    issue(r, hi, c + 2);
+      load_raw_buf<BF, D, tok>(r, rq, (c + 2) * kChunk + t0, m);
+    };
+    map_tok(std::integral_constant<int, 0>{});
+    map_tok(std::integral_constant<int, 1>{});
+    copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c + 2, nch - 1) * G::HALF);
   };
   // O^T of chunk c for this wave's value columns, all 64 rows, staged in sO[c % 2]
   auto mma_chunk = [&](int c) {
-    const St* cQ = sQ + (c & 1) * BUF;
+    const St* cQ = sQ + (c & 1) * BUFQ;
     St* cO = sO + (c & 1) * BUF;
     floatx4 o4[G::CT][4];
 #pragma unroll
@@ -1291,7 +1300,9 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
     for (int kb2 = 0; kb2 < G::KB; ++kb2)
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const Frag<BF> qf = lds_frag<BF>(cQ, G::ROWP, t4 * 16 + c16, kb2, g);
+        Frag<BF> qf;
+        if constexpr (BF) qf = lds_frag_c(cQ, QP, t4 * 16 + c16, kb2, g);
+        else qf = lds_frag<BF>(cQ, QP, t4 * 16 + c16, kb2, g);
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct) o4[ct][t4] = mma(sa[kb2][ct], qf, o4[ct][t4]);
       }
@@ -1385,15 +1396,23 @@ __global__ __launch_bounds__(NT, 2) void feature_map_kernel(
     lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
   }
   const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * G::E;
-  auto issue = [&](R& r, float2 (&hi)[G::E], int c) {
-    copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
+  auto issue = [&](R& r, float2 (&hi)[G::E], int c) {  // in the order step refills
     load_raw_buf<BF, D>(r, rx, c * kChunk + t0, m);
+    copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
   };
   auto step = [&](int c, R& r, float2 (&hi)[G::E]) {
-    R o;
-    feature_map_lane<BF, D>(r, o, g1, g2, lo, hi, rms_eps);
-    store_raw_buf<BF, D>(o, ry, c * kChunk + t0, m);
-    issue(r, hi, c + 2);
+    // the registers of chunk c are refilled with chunk c + 2 one token at a time, then the
+    // RoPE row, so the loads leave while the other token is still being mapped
+    auto map_tok = [&](auto tok_c) {
+      constexpr int tok = decltype(tok_c)::value;
+      R o;
+      feature_map_lane<BF, D, tok>(r, o, g1, g2, lo, hi, rms_eps);
+      store_raw_buf<BF, D, tok>(o, ry, c * kChunk + t0, m);
+      load_raw_buf<BF, D, tok>(r, rx, (c + 2) * kChunk + t0, m);
+    };
+    map_tok(std::integral_constant<int, 0>{});
+    map_tok(std::integral_constant<int, 1>{});
+    copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c + 2, nch - 1) * G::HALF);
   };
   R set0, set1;
   float2 hs0[G::E], hs1[G::E];
