@@ -848,15 +848,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
     float2 lo[2][E], hia[E], hib[E];
     load_lo2(lo, (sub(0) & 1) * C2 + t0, m);
     R xa[3], xb[3];  // raw q, k, v of an even / odd step
-    auto issue = [&](R (&x)[3], float2 (&hr)[E], int j) {
+    auto issue = [&](R (&x)[3], float2 (&hr)[E], float (&tv)[3][2], int j) {
       hi_row(hr, sub(j), m);
       load_raw_buf<true, D>(x[0], rq, sub_ld(j) * C2 + t0, m);
       load_raw_buf<true, D>(x[1], rk, sub_ld(j) * C2 + t0, m);
       load_raw_buf<true, D>(x[2], rv, sub_ld(j) * C2 + t0, m);
+#pragma unroll
+      for (int tok = 0; tok < 2; ++tok) {  // den, gd, bd (tokens past the segment read 0 and weigh nothing)
+        tv[0][tok] = load_tok(rd, sub_ld(j) * C2 + t0 + tok);
+        tv[1][tok] = load_tok(rw, sub_ld(j) * C2 + t0 + tok);
+        tv[2][tok] = load_tok(rb, sub_ld(j) * C2 + t0 + tok);
+      }
     };
-    auto fstep = [&](int st, R (&x)[3], float2 (&hr)[E]) {
+    auto fstep = [&](int st, R (&x)[3], float2 (&hr)[E], float (&tv)[3][2]) {
       if (st < ns) {
-        const int c = sub(st), b = (st & 1) * BUFQ;
+        const int b = (st & 1) * BUFQ;
         R oq, ok, oh;
 #pragma unroll
         for (int tok = 0; tok < 2; ++tok) {
@@ -875,13 +881,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
             put_pairs<true, D>(ok, tok, e, k1, k2);
           }
         }
-        float dn[2], gdl[2], bdl[2];
-#pragma unroll
-        for (int tok = 0; tok < 2; ++tok) {  // tokens past the segment read 0 and weigh nothing
-          dn[tok] = load_tok(rd, c * C2 + t0 + tok);
-          gdl[tok] = load_tok(rw, c * C2 + t0 + tok);
-          bdl[tok] = load_tok(rb, c * C2 + t0 + tok);
-        }
+        const float dn[2] = {tv[0][0], tv[0][1]}, gdl[2] = {tv[1][0], tv[1][1]}, bdl[2] = {tv[2][0], tv[2][1]};
         const float inv[2] = {dn[0] > 0.f ? 1.0f / dn[0] : 0.f, dn[1] > 0.f ? 1.0f / dn[1] : 0.f};
         scale_raw<D>(oq, oh, inv);
         store_rows<true, D>(sQ + b, oq, t0, m, QP);
@@ -900,15 +900,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           }
         }
       }
-      issue(x, hr, st + 2);  // into the registers just consumed
+      issue(x, hr, tv, st + 2);  // into the registers just consumed
       load_lo2(lo, (sub(st + 1) & 1) * C2 + t0, m);
       __syncthreads();  // Y
     };
-    issue(xa, hia, 0);
-    issue(xb, hib, 1);
+    float ta[3][2], tb[3][2];
+    issue(xa, hia, ta, 0);
+    issue(xb, hib, tb, 1);
     for (int st = 0; st < nsteps; st += 2) {
-      fstep(st, xa, hia);
-      fstep(st + 1, xb, hib);
+      fstep(st, xa, hia, ta);
+      fstep(st + 1, xb, hib, tb);
     }
   } else {
     // ======== MMA waves: step st processes sub-chunk sub(st - 1)
