@@ -58,11 +58,12 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // q'/den per token, rounded to bf16 (the query operand of the reverse states); inv = 1/den.
-template <int D>
+template <int D, int ONLY = -1>  // ONLY >= 0: that token of the pair alone
 __device__ __forceinline__ void scale_raw(const Raw<true, D>& x, Raw<true, D>& o, const float (&inv)[2]) {
   constexpr int E = Geo<true, D>::E;
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok)
+    if (ONLY < 0 || tok == ONLY)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -167,6 +168,7 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sH[BUF];  // Q^ rows
   __shared__ __attribute__((aligned(16))) uint16_t sG[BUF];  // dout rows
   __shared__ float sW[kChunk];                                // gd den
+  __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * G::HALF];  // RoPE rows of the chunks
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;
@@ -192,7 +194,10 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
     lo[0][e] = rope_lo[t0 * G::HALF + j];
     lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
   }
-  const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * E;
+  {
+    const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF;
+    for (int i = tid; i < min(nch, kMaxSegChunks) * G::HALF; i += 256) sHi[i] = hi0[i];
+  }
   floatx4 P[RT][CT], pz[ZR];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -202,35 +207,50 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
   for (int z = 0; z < ZR; ++z) pz[z] = floatx4{0.f, 0.f, 0.f, 0.f};
   const bool zwave = wave * ZR < RT;
 
-  R xq, xg;
-  float2 hi[E];
-  float dn[2], w[2];
-  auto issue = [&](int c) {  // chunk c's inputs; tokens past the segment read 0 and weigh nothing
-    copy_bytes<E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);
-    load_raw_buf<true, D>(xq, rq, c * kChunk + t0, m);
-    load_raw_buf<true, D>(xg, rg, c * kChunk + t0, m);
+  // two chunks of inputs in flight: register set c % 2 holds chunk c and is refilled with
+  // chunk c + 2 as it frees up (dout first, then q one token at a time)
+  struct In {
+    R xq, xg;
+    float dn[2], w[2];
+  };
+  auto issue = [&](In& in, int c) {  // chunk c's inputs; tokens past the segment read 0 and weigh nothing
+    load_raw_buf<true, D>(in.xg, rg, c * kChunk + t0, m);
 #pragma unroll
     for (int tok = 0; tok < 2; ++tok) {
-      dn[tok] = load_tok(rd, c * kChunk + t0 + tok);
-      w[tok] = load_tok(rw, c * kChunk + t0 + tok);
+      in.dn[tok] = load_tok(rd, c * kChunk + t0 + tok);
+      in.w[tok] = load_tok(rw, c * kChunk + t0 + tok);
     }
+    load_raw_buf<true, D>(in.xq, rq, c * kChunk + t0, m);
   };
-  issue(0);
-  for (int c = 0; c < nch; ++c) {
-    __syncthreads();  // the previous chunk's operands are consumed
-    {
-      R oq, oh;
-      feature_map_lane<true, D>(xq, oq, g1, g2, lo, hi, rms_eps);
-      const float inv[2] = {dn[0] > 0.f ? 1.0f / dn[0] : 0.f, dn[1] > 0.f ? 1.0f / dn[1] : 0.f};
-      scale_raw<D>(oq, oh, inv);
-      store_rows<true, D>(sH, oh, t0, m);
-      store_rows<true, D>(sG, xg, t0, m);
-      if (m == 0) {
-        sW[t0] = w[0] * dn[0];
-        sW[t0 + 1] = w[1] * dn[1];
-      }
+  In set0, set1;
+  issue(set0, 0);
+  issue(set1, 1);
+  auto step = [&](int c, In& in) {
+    __syncthreads();  // the previous chunk's operands are consumed (the first time: sHi is written)
+    float2 hi[E];
+    copy_bytes<E * 8>(hi, sHi + c * G::HALF + m * E);
+    store_rows<true, D>(sG, in.xg, t0, m);
+    load_raw_buf<true, D>(in.xg, rg, (c + 2) * kChunk + t0, m);
+    const float inv[2] = {in.dn[0] > 0.f ? 1.0f / in.dn[0] : 0.f, in.dn[1] > 0.f ? 1.0f / in.dn[1] : 0.f};
+    if (m == 0) {
+      sW[t0] = in.w[0] * in.dn[0];
+      sW[t0 + 1] = in.w[1] * in.dn[1];
     }
-    issue(c + 1);  // into the registers just consumed: in flight during the MFMA work
+#pragma unroll
+    for (int tok = 0; tok < 2; ++tok) {
+      in.dn[tok] = load_tok(rd, (c + 2) * kChunk + t0 + tok);
+      in.w[tok] = load_tok(rw, (c + 2) * kChunk + t0 + tok);
+    }
+    auto map_tok = [&](auto tok_c) {
+      constexpr int tok = decltype(tok_c)::value;
+      R oq, oh;
+      feature_map_lane<true, D, tok>(in.xq, oq, g1, g2, lo, hi, rms_eps);
+      scale_raw<D, tok>(oq, oh, inv);
+      store_rows<true, D, tok>(sH, oh, t0, m);
+      load_raw_buf<true, D, tok>(in.xq, rq, (c + 2) * kChunk + t0, m);
+    };
+    map_tok(std::integral_constant<int, 0>{});
+    map_tok(std::integral_constant<int, 1>{});
     __syncthreads();
     if (wave < G::NW) {
       Frag<true> Nf[CT][2];
@@ -261,6 +281,10 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
         }
       }
     }
+  };
+  for (int c = 0; c < nch; c += 2) {
+    step(c, set0);
+    if (c + 1 < nch) step(c + 1, set1);
   }
   float* rec = pstates + ((size_t)seg * H + h) * (size_t)(D * D + D);
   if (wave < G::NW) {
