@@ -1085,13 +1085,15 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   }
   // Accumulation order everywhere below: the contraction block is the outer loop and the
   // independent accumulators the inner one, so consecutive MFMAs never wait on each other.
-  // column sums of K': row tiles [0, ZS) on wave 0, [ZS, RT) on wave 1 (the lighter score
-  // waves); their lanes (i, g), i < 4, hold z of dims 16 tile + 4g + i
-  constexpr int ZS = G::RT - (3 * G::RT) / 8;
-  constexpr int NZR = ZS > G::RT - ZS ? ZS : G::RT - ZS;
+  // column sums of K': row tiles [Z_w, Z_w+1) on wave w, more on the waves with fewer score
+  // tiles (measured: a column-sum tile costs about 2.5 key tiles); their lanes (i, g), i < 4,
+  // hold z of dims 16 tile + 4g + i
+  constexpr int Z1 = G::RT == 8 ? 3 : G::RT / 2, Z2 = G::RT == 8 ? 5 : G::RT == 4 ? 3 : 2;
+  constexpr int Z3 = G::RT == 8 ? 7 : G::RT;
+  constexpr int NZR = G::RT == 8 ? 3 : G::RT / 2;
   float zreg[NZR];
   {
-    const int z0 = wave == 1 ? ZS : 0;
+    const int z0 = wave == 0 ? 0 : wave == 1 ? Z1 : wave == 2 ? Z2 : Z3;
 #pragma unroll
     for (int z = 0; z < NZR; ++z) {
       const int dim = min(16 * (z0 + z) + 4 * g + (c16 & 3), D - 1);
@@ -1117,10 +1119,10 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
         const Frag<true>* zf = sZf + (c & 1) * G::KB * 64;  // z before chunk c
         Frag<true>* zn = sZf + ((c + 1) & 1) * G::KB * 64;  // z before chunk c + 1
         switch (wave) {
-          case 0: ws_score<D, 0, 0, ZS, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
-          case 1: ws_score<D, 1, ZS, G::RT, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
-          case 2: ws_score<D, 2, 0, 0, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
-          default: ws_score<D, 3, 0, 0, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          case 0: ws_score<D, 0, 0, Z1, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          case 1: ws_score<D, 1, Z1, Z2, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          case 2: ws_score<D, 2, Z2, Z3, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          default: ws_score<D, 3, Z3, G::RT, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
         }
       }
     }
