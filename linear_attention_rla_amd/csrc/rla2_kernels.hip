@@ -820,8 +820,8 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
 // wave m). In step st, after mapping chunk st, they form chunk st - 1's q'^T A_prev q' as
 // A_prev^T Q'^T dotted with q' (their parts go to LDS) and advance A with its K'; the MMA
 // waves write that chunk's numerators unnormalised and keep the rows' sums of squared
-// weights; one step later the mappers scale each output row by 1 / (sqrt(sum) + eps) as they
-// store it. Nothing new waits inside a step.
+// weights; one step later each output row is scaled by 1 / (sqrt(sum) + eps) as it leaves
+// for memory. Nothing new waits inside a step.
 template <int D, bool L2 = false>
 __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -895,6 +895,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   if (wave == 0) put_zf(rec + D * D);
   __syncthreads();
 
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + tok0 * D), 0, seg_bytes, kBufFlags);
   if (wave >= 4) {
     // ======== mappers: nsteps steps, one barrier each
     const int mt = tid & 255;  // two tokens per 8 lanes
@@ -902,7 +903,6 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + tok0 * D), 0, seg_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + tok0 * D), 0, seg_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + tok0 * D), 0, seg_bytes, kBufFlags);
     // per-lane constants: RMSNorm weights of this lane's dims, in-chunk RoPE angles of its tokens
     // (L2: the weights are read from LDS at each use, which frees their registers for A)
     constexpr int GE = L2 ? 1 : G::E;
@@ -983,33 +983,6 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       map_tok(std::integral_constant<int, 0>{});
       map_tok(std::integral_constant<int, 1>{});
       copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(cn, nch - 1) * G::HALF);
-      {  // chunk st - 2's output rows, staged by the MMA waves in sO[st % 2], leave as whole
-         // rows. The same stores are issued every step: rows past the segment (and every row
-         // when there is no such chunk) fall outside the buffer range and are dropped.
-        constexpr int PPR = D / 8;     // 16-byte pieces per row
-        constexpr int RPI = 64 / PPR;  // rows per wave instruction
-        const int cw = st - 2;
-        const bool any = cw >= 0 && cw < nch;
-        const St* so = sO + (st & 1) * BUF;
-#pragma unroll
-        for (int i = 0; i < kChunk / (4 * RPI); ++i) {
-          const int rr = (i * 4 + wave - 4) * RPI + lane / PPR, pc = lane % PPR;
-          const int off = any ? ((cw * kChunk + rr) * D + pc * 8) * 2 : seg_bytes;
-          u32x4 piece = *reinterpret_cast<const u32x4*>(so + rr * G::ROWP + pc * 8);
-          if constexpr (L2) {  // the row's 1 / (sqrt(sum of squared scores) + eps), from step st - 1
-            const int par = (st + 1) & 1;
-            float quad = sRs2[par * kChunk + rr];
-#pragma unroll
-            for (int w = 0; w < G::NW; ++w) quad += sQuad[(par * 4 + w) * kChunk + rr];
-            const float rsc = 1.0f / (__builtin_sqrtf(quad) + eps);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              piece[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                  float2v{__uint_as_float(piece[j] << 16) * rsc, __uint_as_float(piece[j] & 0xffff0000u) * rsc}, bf16x2));
-          }
-          __builtin_amdgcn_raw_buffer_store_b128(piece, ro, off, 0, kLoadStream);
-        }
-      }
       if constexpr (L2) {  // chunk st - 1 (the MMA waves' chunk of this step): A-side of its denominators
         const int cc = st - 1;
         if (cc >= 0 && cc < nch && mw < G::NW) {
@@ -1170,7 +1143,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
         const int t = tt * 16 + c16;  // this lane's query row
-        const float rr = L2 ? 1.0f : sInv[t];  // L2: the mappers normalise at the store
+        const float rr = L2 ? 1.0f : sInv[t];  // L2: normalised when the row leaves, a step later
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct) {  // columns col .. col + 3
           const int col = wave * G::DVW + ct * 16 + 4 * g;
@@ -1188,6 +1161,34 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
           for (int ct = 0; ct < G::CT; ++ct) S[rt][ct] = mma(a, Vf[ct][kb2], S[rt][ct]);
         }
+    }
+    {  // chunk st - 2's output rows, staged in sO[st % 2] in the previous step, leave as whole
+       // rows (the MMA waves have the slack at the end of the step). The same stores are
+       // issued every step: rows past the segment (and every row when there is no such
+       // chunk) fall outside the buffer range and are dropped.
+      constexpr int PPR = D / 8;     // 16-byte pieces per row
+      constexpr int RPI = 64 / PPR;  // rows per wave instruction
+      const int cw = st - 2;
+      const bool any = cw >= 0 && cw < nch;
+      const St* so = sO + (st & 1) * BUF;
+#pragma unroll
+      for (int i = 0; i < kChunk / (4 * RPI); ++i) {
+        const int rr = (i * 4 + wave) * RPI + lane / PPR, pc = lane % PPR;
+        const int off = any ? ((cw * kChunk + rr) * D + pc * 8) * 2 : seg_bytes;
+        u32x4 piece = *reinterpret_cast<const u32x4*>(so + rr * G::ROWP + pc * 8);
+        if constexpr (L2) {  // the row's 1 / (sqrt(sum of squared scores) + eps), from step st - 1
+          const int par = (st + 1) & 1;
+          float quad = sRs2[par * kChunk + rr];
+#pragma unroll
+          for (int w = 0; w < G::NW; ++w) quad += sQuad[(par * 4 + w) * kChunk + rr];
+          const float rsc = 1.0f / (__builtin_sqrtf(quad) + eps);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            piece[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                float2v{__uint_as_float(piece[j] << 16) * rsc, __uint_as_float(piece[j] & 0xffff0000u) * rsc}, bf16x2));
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(piece, ro, off, 0, kLoadStream);
+      }
     }
     __syncthreads();  // Y
   }
