@@ -815,13 +815,12 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
   }
 }
 
-// L2 (the original RLA's denominator sqrt(sum_i s_ti^2) + eps): the mapper waves also own the
-// second state A = sum k'k'^T (value-column split as S, mapper m holding the columns of MMA
-// wave m). In step st, after mapping chunk st, they form chunk st - 1's q'^T A_prev q' as
-// A_prev^T Q'^T dotted with q' (their parts go to LDS) and advance A with its K'; the MMA
-// waves write that chunk's numerators unnormalised and keep the rows' sums of squared
-// weights; one step later each output row is scaled by 1 / (sqrt(sum) + eps) as it leaves
-// for memory. Nothing new waits inside a step.
+// L2 (the original RLA's denominator sqrt(sum_i s_ti^2) + eps): the MMA waves also hold the
+// second state A = sum k'k'^T (the same value-column split and tile map as S). After the
+// state update of chunk c they form its q'^T A_prev q' as A_prev^T Q'^T dotted with q' (their
+// parts go to LDS) and advance A with its K'; the chunk's numerators are staged unnormalised
+// with the rows' sums of squared weights, and one step later each output row is scaled by
+// 1 / (sqrt(sum) + eps) as it leaves for memory. Nothing new waits inside a step.
 template <int D, bool L2 = false>
 __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
@@ -852,7 +851,6 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   // q'^T A_prev q', for the chunk the MMA waves processed in that step
   __shared__ float sRs2[L2 ? 2 * kChunk : 1];
   __shared__ float sQuad[L2 ? 2 * 4 * kChunk : 1];
-  __shared__ float sGam[L2 ? 2 * D : 1];  // L2: the mappers read the RMSNorm weights here
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;  // the whole workgroup leaves together
@@ -888,9 +886,6 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     }
   };
   for (int i = tid; i < 2 * G::KB * 64; i += 512) sZf[i] = Frag<true>{};
-  if constexpr (L2) {
-    for (int i = tid; i < 2 * D; i += 512) sGam[i] = i < D ? gamma_q[(size_t)h * D + i] : gamma_k[(size_t)h * D + i - D];
-  }
   __syncthreads();
   if (wave == 0) put_zf(rec + D * D);
   __syncthreads();
@@ -904,36 +899,17 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + tok0 * D), 0, seg_bytes, kBufFlags);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
     // per-lane constants: RMSNorm weights of this lane's dims, in-chunk RoPE angles of its tokens
-    // (L2: the weights are read from LDS at each use, which frees their registers for A)
-    constexpr int GE = L2 ? 1 : G::E;
-    float gq1[GE], gq2[GE], gk1[GE], gk2[GE];
+    float gq1[G::E], gq2[G::E], gk1[G::E], gk2[G::E];
     float2 lo[2][G::E];
 #pragma unroll
     for (int e = 0; e < G::E; ++e) {
       const int j = m * G::E + e;
-      if constexpr (!L2) {
-        gq1[e] = gamma_q[(size_t)h * D + j];
-        gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
-        gk1[e] = gamma_k[(size_t)h * D + j];
-        gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
-      }
+      gq1[e] = gamma_q[(size_t)h * D + j];
+      gq2[e] = gamma_q[(size_t)h * D + j + G::HALF];
+      gk1[e] = gamma_k[(size_t)h * D + j];
+      gk2[e] = gamma_k[(size_t)h * D + j + G::HALF];
       lo[0][e] = rope_lo[t0 * G::HALF + j];
       lo[1][e] = rope_lo[(t0 + 1) * G::HALF + j];
-    }
-    auto gam = [&](const float (&reg)[GE], int base, int e) -> float {  // weight of dim base + m E + e
-      if constexpr (L2) return sGam[base + m * G::E + e];
-      else return reg[e];
-    };
-    const int mw = wave - 4;  // L2: this mapper's A columns are those of MMA wave mw
-    floatx4 Am[L2 ? G::RT : 1][G::CT];
-    if constexpr (L2) {
-      const float* arec = astates + ((size_t)seg * H + h) * (size_t)(D * D + D);
-      const int wv = mw < G::NW ? mw : 0;
-#pragma unroll
-      for (int rt = 0; rt < G::RT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct)
-          Am[rt][ct] = *reinterpret_cast<const floatx4*>(arec + rec_frag_c<D>(wv, rt, ct, lane));
     }
     // Every step issues the same loads (chunks past the end read zeros from the buffer
     // range check), so the compiler's wait counts let chunk st + 1 stay in flight while
@@ -951,7 +927,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       const int bm = (st & 1) * BUF;
       // The registers of chunk st are refilled with chunk cn as they free up: v (no mapping)
       // first, then q and k one token at a time, then the RoPE row, so the loads leave early.
-      const int cn = st + (L2 ? 1 : 2);
+      const int cn = st + 2;
       if (st < nch) store_rows<true, D>(sV + bm, r[2], t0, m);
       load_raw_buf<true, D>(r[2], rv, cn * kChunk + t0, m);
       auto map_tok = [&](auto tok_c) {
@@ -966,10 +942,10 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
               const float2 cs = angle_sum(hi[e + x], lo[tok][e + x]);
-              rope_pair(r[0].get(tok, 0, e + x), r[0].get(tok, 1, e + x), invq, gam(gq1, 0, e + x),
-                        gam(gq2, G::HALF, e + x), cs, q1[x], q2[x]);
-              rope_pair(r[1].get(tok, 0, e + x), r[1].get(tok, 1, e + x), invk, gam(gk1, D, e + x),
-                        gam(gk2, D + G::HALF, e + x), cs, k1[x], k2[x]);
+              rope_pair(r[0].get(tok, 0, e + x), r[0].get(tok, 1, e + x), invq, gq1[e + x], gq2[e + x], cs,
+                        q1[x], q2[x]);
+              rope_pair(r[1].get(tok, 0, e + x), r[1].get(tok, 1, e + x), invk, gk1[e + x], gk2[e + x], cs,
+                        k1[x], k2[x]);
             }
             put_pairs<true, D>(oq, tok, e, q1, q2);
             put_pairs<true, D>(ok, tok, e, k1, k2);
@@ -983,63 +959,15 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       map_tok(std::integral_constant<int, 0>{});
       map_tok(std::integral_constant<int, 1>{});
       copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(cn, nch - 1) * G::HALF);
-      if constexpr (L2) {  // chunk st - 1 (the MMA waves' chunk of this step): A-side of its denominators
-        const int cc = st - 1;
-        if (cc >= 0 && cc < nch && mw < G::NW) {
-          const St* cQ = sQ + ((st + 1) & 1) * BUFQ;
-          const St* cK = sK + ((st + 1) & 1) * BUFQ;
-          const int c16 = lane & 15, g = lane >> 4;
-          // one query tile at a time (a rolled loop keeps the mappers' registers for A)
-#pragma unroll 1
-          for (int tt = 0; tt < 4; ++tt) {
-            float part = 0.f;
-#pragma unroll
-            for (int ct = 0; ct < G::CT; ++ct) {
-              floatx4 y = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-              for (int kb2 = 0; kb2 < G::KB; ++kb2)  // A_prev (symmetric) rounded to bf16 as the A operand
-                y = mma(acc_frag<true>(Am[2 * kb2][ct], Am[2 * kb2 + 1][ct]),
-                        lds_frag_c(cQ, QP, tt * 16 + c16, kb2, g), y);
-              const int col = mw * G::DVW + ct * 16 + 4 * g;
-              const uint2 qa = *reinterpret_cast<const uint2*>(cQ + (tt * 16 + c16) * QP + col);
-              part = __builtin_fmaf(__uint_as_float(qa.x << 16), y[0], part);
-              part = __builtin_fmaf(__uint_as_float(qa.x & 0xffff0000u), y[1], part);
-              part = __builtin_fmaf(__uint_as_float(qa.y << 16), y[2], part);
-              part = __builtin_fmaf(__uint_as_float(qa.y & 0xffff0000u), y[3], part);
-            }
-            part = sum_rows4(part);
-            if (g == 0) sQuad[((st & 1) * 4 + mw) * kChunk + tt * 16 + c16] = part;
-          }
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2) {  // A += K'^T K' (this mapper's columns)
-            Frag<true> Kc[G::CT];
-#pragma unroll
-            for (int ct = 0; ct < G::CT; ++ct) Kc[ct] = lds_frag_tr(cK, QP, 32 * kb2, mw * G::DVW + ct * 16, lane);
-#pragma unroll
-            for (int rt = 0; rt < G::RT; ++rt) {
-              const Frag<true> a = lds_frag_tr_s8(cK, QP, 32 * kb2, 32 * (rt / 2) + 4 * (rt % 2), lane);
-#pragma unroll
-              for (int ct = 0; ct < G::CT; ++ct) Am[rt][ct] = mma(a, Kc[ct], Am[rt][ct]);
-            }
-          }
-        }
-      }
       __syncthreads();  // Y
     };
-    if constexpr (L2) {  // the A state takes the registers of the second chunk in flight
-      R set0[3];
-      float2 hi0r[G::E];
-      issue(set0, hi0r, 0);
-      for (int st = 0; st < nsteps; ++st) mstep(st, set0, hi0r);
-    } else {
-      R set0[3], set1[3];
-      float2 hi0r[G::E], hi1r[G::E];
-      issue(set0, hi0r, 0);
-      issue(set1, hi1r, 1);
-      for (int st = 0; st < nsteps; st += 2) {
-        mstep(st, set0, hi0r);
-        mstep(st + 1, set1, hi1r);
-      }
+    R set0[3], set1[3];
+    float2 hi0r[G::E], hi1r[G::E];
+    issue(set0, hi0r, 0);
+    issue(set1, hi1r, 1);
+    for (int st = 0; st < nsteps; st += 2) {
+      mstep(st, set0, hi0r);
+      mstep(st + 1, set1, hi1r);
     }
     return;
   }
@@ -1048,13 +976,17 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   // running state, value columns of this wave, in the contiguous-order tile map: tiles 2kb and
   // 2kb + 1 pair up (acc_frag) into S^T operands whose slots match the 16-byte Q' fragments
   floatx4 S[G::RT][G::CT];
+  floatx4 Am[L2 ? G::RT : 1][G::CT];  // L2: A = sum k'k'^T, the same columns and tile map as S
   {
     const int wv = wave < G::NW ? wave : 0;
+    const float* arec = L2 ? astates + ((size_t)seg * H + h) * (size_t)(D * D + D) : nullptr;
 #pragma unroll
     for (int rt = 0; rt < G::RT; ++rt)
 #pragma unroll
-      for (int ct = 0; ct < G::CT; ++ct)
+      for (int ct = 0; ct < G::CT; ++ct) {
         S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag_c<D>(wv, rt, ct, lane));
+        if constexpr (L2) Am[rt][ct] = *reinterpret_cast<const floatx4*>(arec + rec_frag_c<D>(wv, rt, ct, lane));
+      }
   }
   // Accumulation order everywhere below: the contraction block is the outer loop and the
   // independent accumulators the inner one, so consecutive MFMAs never wait on each other.
@@ -1161,6 +1093,43 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 #pragma unroll
           for (int ct = 0; ct < G::CT; ++ct) S[rt][ct] = mma(a, Vf[ct][kb2], S[rt][ct]);
         }
+      if constexpr (L2) {  // q'^T A_prev q' of chunk c (this wave's columns, to LDS), then A += K'^T K'
+        Frag<true> aa[G::KB][G::CT];  // A_prev (symmetric) rounded to bf16 as the A operand
+#pragma unroll
+        for (int kb2 = 0; kb2 < G::KB; ++kb2)
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) aa[kb2][ct] = acc_frag<true>(Am[2 * kb2][ct], Am[2 * kb2 + 1][ct]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          float part = 0.f;
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) {
+            floatx4 y = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb2 = 0; kb2 < G::KB; ++kb2) y = mma(aa[kb2][ct], lds_frag_c(cQ, QP, tt * 16 + c16, kb2, g), y);
+            const int col = wave * G::DVW + ct * 16 + 4 * g;
+            const uint2 qa = *reinterpret_cast<const uint2*>(cQ + (tt * 16 + c16) * QP + col);
+            part = __builtin_fmaf(__uint_as_float(qa.x << 16), y[0], part);
+            part = __builtin_fmaf(__uint_as_float(qa.x & 0xffff0000u), y[1], part);
+            part = __builtin_fmaf(__uint_as_float(qa.y << 16), y[2], part);
+            part = __builtin_fmaf(__uint_as_float(qa.y & 0xffff0000u), y[3], part);
+          }
+          part = sum_rows4(part);
+          if (g == 0) sQuad[((st & 1) * 4 + wave) * kChunk + tt * 16 + c16] = part;
+        }
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          Frag<true> Kc[G::CT];
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) Kc[ct] = lds_frag_tr(cK, QP, 32 * kb2, wave * G::DVW + ct * 16, lane);
+#pragma unroll
+          for (int rt = 0; rt < G::RT; ++rt) {
+            const Frag<true> a = lds_frag_tr_s8(cK, QP, 32 * kb2, 32 * (rt / 2) + 4 * (rt % 2), lane);
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) Am[rt][ct] = mma(a, Kc[ct], Am[rt][ct]);
+          }
+        }
+      }
     }
     {  // chunk st - 2's output rows, staged in sO[st % 2] in the previous step, leave as whole
        // rows (the MMA waves have the slack at the end of the step). The same stores are
