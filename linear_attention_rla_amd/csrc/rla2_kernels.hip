@@ -891,6 +891,36 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   __syncthreads();
 
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + tok0 * D), 0, seg_bytes, kBufFlags);
+  // Chunk st - 2's output rows, staged in sO[st % 2] in the previous step, leave as whole rows,
+  // issued by the four waves of one role (w4 = 0..3): the MMA waves, which have the slack at
+  // the end of the step, or, with the L2 denominator (the MMA waves also carry the A state),
+  // the mappers. The same stores are issued every step: rows past the segment (and every row
+  // when there is no such chunk) fall outside the buffer range and are dropped.
+  auto store_rows_out = [&](int st, int w4) {
+    constexpr int PPR = D / 8;     // 16-byte pieces per row
+    constexpr int RPI = 64 / PPR;  // rows per wave instruction
+    const int cw = st - 2;
+    const bool any = cw >= 0 && cw < nch;
+    const St* so = sO + (st & 1) * BUF;
+#pragma unroll
+    for (int i = 0; i < kChunk / (4 * RPI); ++i) {
+      const int rr = (i * 4 + w4) * RPI + lane / PPR, pc = lane % PPR;
+      const int off = any ? ((cw * kChunk + rr) * D + pc * 8) * 2 : seg_bytes;
+      u32x4 piece = *reinterpret_cast<const u32x4*>(so + rr * G::ROWP + pc * 8);
+      if constexpr (L2) {  // the row's 1 / (sqrt(sum of squared scores) + eps), from step st - 1
+        const int par = (st + 1) & 1;
+        float quad = sRs2[par * kChunk + rr];
+#pragma unroll
+        for (int w = 0; w < G::NW; ++w) quad += sQuad[(par * 4 + w) * kChunk + rr];
+        const float rsc = 1.0f / (__builtin_sqrtf(quad) + eps);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          piece[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+              float2v{__uint_as_float(piece[j] << 16) * rsc, __uint_as_float(piece[j] & 0xffff0000u) * rsc}, bf16x2));
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(piece, ro, off, 0, kLoadStream);
+    }
+  };
   if (wave >= 4) {
     // ======== mappers: nsteps steps, one barrier each
     const int mt = tid & 255;  // two tokens per 8 lanes
@@ -959,6 +989,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       map_tok(std::integral_constant<int, 0>{});
       map_tok(std::integral_constant<int, 1>{});
       copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(cn, nch - 1) * G::HALF);
+      if constexpr (L2) store_rows_out(st, wave - 4);
       __syncthreads();  // Y
     };
     R set0[3], set1[3];
@@ -1131,34 +1162,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
         }
       }
     }
-    {  // chunk st - 2's output rows, staged in sO[st % 2] in the previous step, leave as whole
-       // rows (the MMA waves have the slack at the end of the step). The same stores are
-       // issued every step: rows past the segment (and every row when there is no such
-       // chunk) fall outside the buffer range and are dropped.
-      constexpr int PPR = D / 8;     // 16-byte pieces per row
-      constexpr int RPI = 64 / PPR;  // rows per wave instruction
-      const int cw = st - 2;
-      const bool any = cw >= 0 && cw < nch;
-      const St* so = sO + (st & 1) * BUF;
-#pragma unroll
-      for (int i = 0; i < kChunk / (4 * RPI); ++i) {
-        const int rr = (i * 4 + wave) * RPI + lane / PPR, pc = lane % PPR;
-        const int off = any ? ((cw * kChunk + rr) * D + pc * 8) * 2 : seg_bytes;
-        u32x4 piece = *reinterpret_cast<const u32x4*>(so + rr * G::ROWP + pc * 8);
-        if constexpr (L2) {  // the row's 1 / (sqrt(sum of squared scores) + eps), from step st - 1
-          const int par = (st + 1) & 1;
-          float quad = sRs2[par * kChunk + rr];
-#pragma unroll
-          for (int w = 0; w < G::NW; ++w) quad += sQuad[(par * 4 + w) * kChunk + rr];
-          const float rsc = 1.0f / (__builtin_sqrtf(quad) + eps);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            piece[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
-                float2v{__uint_as_float(piece[j] << 16) * rsc, __uint_as_float(piece[j] & 0xffff0000u) * rsc}, bf16x2));
-        }
-        __builtin_amdgcn_raw_buffer_store_b128(piece, ro, off, 0, kLoadStream);
-      }
-    }
+    if constexpr (!L2) store_rows_out(st, wave);
     __syncthreads();  // Y
   }
 }
