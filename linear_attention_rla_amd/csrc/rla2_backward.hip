@@ -316,7 +316,7 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
 //          the score tiles of query tile w (A^T, V G^T, q' . z); meeting; waves 0, 1: den, g.num,
 //          gd, B_tt and B^T (to LDS and to the per-token planes); meeting; every wave: its rows
 //          of dQ'^T = (S G^T)/den + z gd^T + K'^T B^T as fp32 rows of the dq' buffer of the
-//          sub-chunk, S^T += V^T K', and (wave 0) z for the next sub-chunk;
+//          sub-chunk and S^T += V^T K'; waves 2, 3 form z for the next sub-chunk during the scores;
 //   waves 6, 7 ("backward mappers"): the raw dout rows of sub-chunk st into buffer st % 2
 //          (two sub-chunks in flight), then the map backward of sub-chunk st - 2 from its dq'
 //          rows and the raw q in the ring.
@@ -534,6 +534,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       }
   }
   if (wave == 0) put_zf(sZf, sZ);  // parity 0: z before the first sub-chunk
+  // waves 2, 3 form the column sums of K' (row tiles 4 (w - 2) .. + 3) while waves 0, 1 do the
+  // score tiles; their lanes (i, g), i < 4, hold z of dims 16 tile + 4g + i in registers and
+  // write z and its operand form for the next sub-chunk straight into the other parity
+  constexpr int ZT = RT / 2;  // column-sum tiles per wave
+  float zreg[ZT];
+#pragma unroll
+  for (int z = 0; z < ZT; ++z) zreg[z] = rec[D * D + min(16 * ((wave & 1) * ZT + z) + 4 * g + (c16 & 3), D - 1)];
   unsigned meet = 0;
   for (int st = 0; st < nsteps; ++st) {
     const int c = st - 1;
@@ -579,6 +586,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
           }
           part = sum_rows4(part);
           if (g == 0) sIdot[wave * C2 + tt * 16 + c16] = part;
+        }
+      }
+      if (wave >= 2) {  // z after this sub-chunk, into the other parity
+        const Frag<true> ones = ones_frag<true>();
+        float* zn = sZ + ((c + 1) & 1) * D;
+        uint16_t* zf16 = reinterpret_cast<uint16_t*>(sZf + ((c + 1) & 1) * KB * 64);
+#pragma unroll
+        for (int z = 0; z < ZT; ++z) {
+          const int T = (wave & 1) * ZT + z;
+          const floatx4 zs = mma(lds_frag_tr(cK, QP, 0, 16 * T, lane), ones, floatx4{0.f, 0.f, 0.f, 0.f});
+          if (c16 < 4) {
+            // dim 16 T + 4g + i: fragment T / 2, slot 4 (g % 2) + i of lane 16 (2 (T % 2) + g / 2)
+            // (bf16 of z) and of the lane after it (the remainder)
+            zreg[z] += c16 == 0 ? zs[0] : c16 == 1 ? zs[1] : c16 == 2 ? zs[2] : zs[3];
+            zn[16 * T + 4 * g + c16] = zreg[z];
+            const uint32_t hw = pack_bf2(zreg[z], 0.f);
+            uint16_t* dst = zf16 + ((T / 2) * 64 + 16 * (2 * (T % 2) + g / 2)) * 8 + 4 * (g % 2) + c16;
+            dst[0] = static_cast<uint16_t>(hw & 0xffffu);
+            dst[8] = static_cast<uint16_t>(pack_bf2(zreg[z] - bf_lo(hw), 0.f) & 0xffffu);
+          }
         }
       }
       // score tiles of query tile tt = wave (waves 0, 1)
@@ -691,19 +718,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) ST[rt][ct] = mma(av, Kc[ct], ST[rt][ct]);
         }
-      }
-      if (wave == 0) {  // z after this sub-chunk and its operand form, into the other parity
-        const Frag<true> ones = ones_frag<true>();
-        float* zn = sZ + ((c + 1) & 1) * D;
-#pragma unroll
-        for (int at = 0; at < RT; ++at) {
-          const floatx4 zs = mma(lds_frag_tr(cK, QP, 0, 16 * at, lane), ones, floatx4{0.f, 0.f, 0.f, 0.f});
-          if (c16 < 4) zn[at * 16 + 4 * g + c16] = zc[at * 16 + 4 * g + c16] + zs[c16];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        put_zf(sZf + ((c + 1) & 1) * KB * 64, zn);
       }
     }
     __syncthreads();  // Y
