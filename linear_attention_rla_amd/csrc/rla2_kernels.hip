@@ -322,6 +322,137 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_state_kernel(
   }
 }
 
+// chunk_state with the L2 denominator's second state, bf16: 8 waves, one workgroup per CU.
+// Waves 0..3 accumulate S = sum K'^T V and the column sums of K' (the value-column split of S),
+// waves 4..7 accumulate A = sum K'^T K' (the same split of A's columns), so each wave carries one
+// state (the 4-wave kernel carrying both ran at one wave per SIMD). Every wave also maps one
+// token per 8 lanes: step st maps chunk st into buffer st % 2 while the MFMAs run on chunk
+// st - 1 from the other buffer; one barrier per step. Two chunks of raw k, v are in flight per
+// lane, refilled as they free up.
+template <int D>
+__global__ __launch_bounds__(512, 1) void chunk_state_l2_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ gamma_k,
+    const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
+    const float2* __restrict__ rope_hi, float* __restrict__ states, float* __restrict__ astates, int H, int L,
+    float rms_eps) {
+  using G = Geo<true, D>;
+  using R = Raw<true, D>;
+  constexpr int BUF = kChunk * G::ROWP;
+  constexpr int ZR = G::RT >= 4 ? G::RT / 4 : 1;  // row tiles of the column sums per S wave
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUF];
+  __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * G::HALF];  // RoPE rows of the chunks
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
+  const int tg = tid >> 3, m = tid & 7;  // this lane group's token of the chunk (0..63)
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(k + tok0 * D), 0, seg_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(v + tok0 * D), 0, seg_bytes, kBufFlags);
+  {
+    const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF;
+    for (int i = tid; i < min(nch, kMaxSegChunks) * G::HALF; i += 512) sHi[i] = hi0[i];
+  }
+  float g1[G::E], g2[G::E];
+  float2 lo[2][G::E];  // slot 0: the in-chunk angles of token tg (the lane maps token slot 0 only)
+#pragma unroll
+  for (int e = 0; e < G::E; ++e) {
+    const int j = m * G::E + e;
+    g1[e] = gamma_k[(size_t)h * D + j];
+    g2[e] = gamma_k[(size_t)h * D + j + G::HALF];
+    lo[0][e] = rope_lo[tg * G::HALF + j];
+    lo[1][e] = lo[0][e];
+  }
+  const bool swave = wave < 4;                        // S (and z) or A
+  const int cw = swave ? wave : wave - 4;             // the wave's column block
+  const bool owns = cw < G::NW;
+  const bool zwave = swave && cw * ZR < G::RT;
+  floatx4 acc[G::RT][G::CT];
+  floatx4 zc[ZR];
+#pragma unroll
+  for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) acc[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int zr = 0; zr < ZR; ++zr) zc[zr] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  struct In {
+    R xk, xv;
+  };
+  auto issue = [&](In& in, int c) {  // in the order step refills
+    load_raw_buf<true, D, 0>(in.xv, rv, c * kChunk + tg, m);
+    load_raw_buf<true, D, 0>(in.xk, rk, c * kChunk + tg, m);
+  };
+  auto step = [&](int st, In& in) {
+    if (st < nch) {  // chunk st into buffer st % 2
+      uint16_t* bK = sK + (st & 1) * BUF;
+      uint16_t* bV = sV + (st & 1) * BUF;
+      store_rows<true, D, 0>(bV, in.xv, tg, m);
+      load_raw_buf<true, D, 0>(in.xv, rv, (st + 2) * kChunk + tg, m);
+      float2 hi[G::E];
+      copy_bytes<G::E * 8>(hi, sHi + st * G::HALF + m * G::E);
+      R o;
+      feature_map_lane<true, D, 0>(in.xk, o, g1, g2, lo, hi, rms_eps);
+      store_rows<true, D, 0>(bK, o, tg, m);
+      load_raw_buf<true, D, 0>(in.xk, rk, (st + 2) * kChunk + tg, m);
+    }
+    if (st >= 1 && owns) {  // chunk st - 1 from the other buffer
+      const uint16_t* cK = sK + ((st + 1) & 1) * BUF;
+      const uint16_t* cV = sV + ((st + 1) & 1) * BUF;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        Frag<true> B[G::CT];  // V columns (S waves) or K' columns (A waves) of this wave
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct)
+          B[ct] = lds_frag_tr(swave ? cV : cK, G::ROWP, 32 * kb2, cw * G::DVW + ct * 16, lane);
+#pragma unroll
+        for (int rt = 0; rt < G::RT; ++rt) {
+          const Frag<true> a = lds_frag_tr(cK, G::ROWP, 32 * kb2, 16 * rt, lane);
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) acc[rt][ct] = mma(a, B[ct], acc[rt][ct]);
+        }
+      }
+      if (zwave) {
+        const Frag<true> ones = ones_frag<true>();
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int zr = 0; zr < ZR; ++zr)
+            zc[zr] = mma(lds_frag_tr(cK, G::ROWP, 32 * kb2, 16 * (cw * ZR + zr), lane), ones, zc[zr]);
+      }
+    }
+    __syncthreads();
+  };
+  In set0, set1;
+  issue(set0, 0);
+  issue(set1, 1);
+  __syncthreads();  // sHi
+  for (int st = 0; st <= nch; st += 2) {
+    step(st, set0);
+    if (st + 1 <= nch) step(st + 1, set1);
+  }
+
+  float* rec = (swave ? states : astates) + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  if (owns) {
+#pragma unroll
+    for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct)
+        __builtin_nontemporal_store(acc[rt][ct], reinterpret_cast<floatx4*>(rec + rec_frag<true, D>(cw, rt, ct, lane)));
+  }
+  if (zwave && c16 < 4) {  // every column of zc holds the sums of rows 16 rt + 4g + i
+#pragma unroll
+    for (int zr = 0; zr < ZR; ++zr) rec[D * D + (cw * ZR + zr) * 16 + 4 * g + c16] = zc[zr][c16];
+  }
+  if (!swave && tid - 256 < D) rec[D * D + tid - 256] = 0.f;
+}
+
 // ----------------------------------------------------------------------------------------
 // state_scan: per (document, head, 1024-float tile of the state record), walk the document's
 // segments in order, starting from the initial state for the first document of each row
@@ -1546,7 +1677,11 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
   const bool l2 = p.l2 && a.out != nullptr;
   float* astates = reinterpret_cast<float*>(a.ws + p.off_astates);
   if (p.n_seg_max > 0) {
-    if (l2) {
+    if (l2 && BF) {
+      hipLaunchKernelGGL((chunk_state_l2_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
+                         static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.gk, tab, nseg, rlo,
+                         rhi, states, astates, p.H, p.L, a.rms_eps);
+    } else if (l2) {
       hipLaunchKernelGGL((chunk_state_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                          static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
                          states, astates, p.H, p.L, a.rms_eps);
