@@ -173,6 +173,7 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;
   const SegInfo si = read_seg(tab, seg);
+  if (si.pos0 == 0) return;  // a document's first segment: no earlier segment reads its total
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);

@@ -15,7 +15,8 @@ constexpr int kTabInts = 8;         // int32 fields per segment-table entry
 constexpr size_t kAlign = 256;
 
 // Segment-table entry fields (int32 each).
-enum TabField { TAB_ROW = 0, TAB_START = 1, TAB_LEN = 2, TAB_POS0 = 3, TAB_DOC = 4, TAB_HIROW = 5 };
+// TAB_LAST: 1 for the last segment of its document.
+enum TabField { TAB_ROW = 0, TAB_START = 1, TAB_LEN = 2, TAB_POS0 = 3, TAB_DOC = 4, TAB_HIROW = 5, TAB_LAST = 6 };
 
 // Everything a launch needs about the problem and the workspace carve-up.
 struct Plan {

@@ -11,7 +11,8 @@
 //   prep         cu_seqlens -> table of (row, first token, length, first position) segments,
 //                and cos/sin of p*theta_j for p < 64 and for p = 64*a (angle addition rebuilds
 //                any position from the two, so no per-token transcendental is needed)
-//   chunk_state  per (segment, head): Sum over the segment of K'^T V and of K' (MFMA)
+//   chunk_state  per (segment, head): Sum over the segment of K'^T V and of K' (MFMA); the
+//                last segment of a document is skipped unless final states are exported
 //   state_scan   per (document, head): exclusive prefix of segment totals in fp32;
 //                the inclusive end is the document's final state
 //   chunk_out    per (segment, head): sweep the segment's chunks in order with the running
@@ -83,6 +84,7 @@ __device__ __forceinline__ void seg_map_block(const int32_t* __restrict__ cu, in
         e.w = s * seg_len;
         *reinterpret_cast<int4*>(tab + (size_t)idx * kTabInts) = e;
         tab[(size_t)idx * kTabInts + TAB_DOC] = j;
+        tab[(size_t)idx * kTabInts + TAB_LAST] = s == cnt - 1;
         // the first document of each row (every row when unpacked) reads the offset rows
         const bool first = cu == nullptr || j == 0;
         tab[(size_t)idx * kTabInts + TAB_HIROW] = (first ? hi_off : 0) + e.w / kChunk;
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_state_kernel(
     const typename Elem<BF>::St* __restrict__ k, const typename Elem<BF>::St* __restrict__ v,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg,
     const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi, float* __restrict__ states,
-    float* __restrict__ astates, int H, int L, float rms_eps) {
+    float* __restrict__ astates, int H, int L, float rms_eps, int skip_last) {
   using G = Geo<BF, D>;
   using St = typename G::St;
   using R = Raw<BF, D>;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_state_kernel(
   __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * G::HALF];  // RoPE rows of the chunks
 
   const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= *nseg) return;
+  if (seg >= *nseg || (skip_last && tab[(size_t)seg * kTabInts + TAB_LAST])) return;
   const SegInfo si = read_seg(tab, seg);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(512, 1) void chunk_state_l2_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ gamma_k,
     const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
     const float2* __restrict__ rope_hi, float* __restrict__ states, float* __restrict__ astates, int H, int L,
-    float rms_eps) {
+    float rms_eps, int skip_last) {
   using G = Geo<true, D>;
   using R = Raw<true, D>;
   constexpr int BUF = kChunk * G::ROWP;
@@ -344,7 +346,7 @@ __global__ __launch_bounds__(512, 1) void chunk_state_l2_kernel(
   __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * G::HALF];  // RoPE rows of the chunks
 
   const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= *nseg) return;
+  if (seg >= *nseg || (skip_last && tab[(size_t)seg * kTabInts + TAB_LAST])) return;
   const SegInfo si = read_seg(tab, seg);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -502,8 +504,10 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
       const int cnt = min(kBatch, s - s0 + 1);
       float4 val[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j)
-        if (j < cnt) val[j] = st[((size_t)(s - j) * H + h) * R4 + e4];
+      for (int j = 0; j < kBatch; ++j) {  // the first record's total is never needed (it may be unset)
+        val[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < cnt && s - j > s0) val[j] = st[((size_t)(s - j) * H + h) * R4 + e4];
+      }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         if (j < cnt) {
@@ -517,12 +521,16 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
     }
     return;
   }
+  // the prefix mode without an export never needs the last record's total (it may be unset)
+  const int s_read = mode == SCAN_PREFIX && final_S == nullptr && final_z == nullptr ? s1 - 1 : s1;
   for (int s = s0; s < s1; s += kBatch) {
     const int cnt = min(kBatch, s1 - s);
     float4 val[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      if (j < cnt) val[j] = st[((size_t)(s + j) * H + h) * R4 + e4];
+    for (int j = 0; j < kBatch; ++j) {
+      val[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j < cnt && s + j < s_read) val[j] = st[((size_t)(s + j) * H + h) * R4 + e4];
+    }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (j < cnt) {
@@ -1023,26 +1031,31 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + tok0 * D), 0, seg_bytes, kBufFlags);
   // Chunk st - 2's output rows, staged in sO[st % 2] in the previous step, leave as whole rows,
-  // issued by the four waves of one role (w4 = 0..3): the MMA waves, which have the slack at
-  // the end of the step, or, with the L2 denominator (the MMA waves also carry the A state),
-  // the mappers. The same stores are issued every step: rows past the segment (and every row
-  // when there is no such chunk) fall outside the buffer range and are dropped.
-  auto store_rows_out = [&](int st, int w4) {
+  // issued by NWAY waves (w = 0 .. NWAY - 1). In the sum mode all eight waves share them at
+  // the end of the step (each role has some slack there, neither enough for all the stores;
+  // at d = 32 one wave instruction covers 16 rows and the four MMA waves issue them);
+  // with the L2 denominator the four mappers issue them (the MMA waves also carry the A
+  // state). The same stores are issued every step: rows past the segment (and every row when
+  // there is no such chunk) fall outside the buffer range and are dropped.
+  constexpr int NWS = D >= 64 ? 8 : 4;  // waves sharing the stores in the sum mode
+  auto store_rows_out = [&](int st, int w, auto nway_c) {
+    constexpr int NWAY = decltype(nway_c)::value;
     constexpr int PPR = D / 8;     // 16-byte pieces per row
     constexpr int RPI = 64 / PPR;  // rows per wave instruction
+    static_assert(kChunk % (NWAY * RPI) == 0, "whole rows per wave");
     const int cw = st - 2;
     const bool any = cw >= 0 && cw < nch;
     const St* so = sO + (st & 1) * BUF;
 #pragma unroll
-    for (int i = 0; i < kChunk / (4 * RPI); ++i) {
-      const int rr = (i * 4 + w4) * RPI + lane / PPR, pc = lane % PPR;
+    for (int i = 0; i < kChunk / (NWAY * RPI); ++i) {
+      const int rr = (i * NWAY + w) * RPI + lane / PPR, pc = lane % PPR;
       const int off = any ? ((cw * kChunk + rr) * D + pc * 8) * 2 : seg_bytes;
       u32x4 piece = *reinterpret_cast<const u32x4*>(so + rr * G::ROWP + pc * 8);
       if constexpr (L2) {  // the row's 1 / (sqrt(sum of squared scores) + eps), from step st - 1
         const int par = (st + 1) & 1;
         float quad = sRs2[par * kChunk + rr];
 #pragma unroll
-        for (int w = 0; w < G::NW; ++w) quad += sQuad[(par * 4 + w) * kChunk + rr];
+        for (int wv = 0; wv < G::NW; ++wv) quad += sQuad[(par * 4 + wv) * kChunk + rr];
         const float rsc = 1.0f / (__builtin_sqrtf(quad) + eps);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -1120,7 +1133,8 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       map_tok(std::integral_constant<int, 0>{});
       map_tok(std::integral_constant<int, 1>{});
       copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(cn, nch - 1) * G::HALF);
-      if constexpr (L2) store_rows_out(st, wave - 4);
+      if constexpr (L2) store_rows_out(st, wave - 4, std::integral_constant<int, 4>{});
+      else if constexpr (NWS == 8) store_rows_out(st, wave, std::integral_constant<int, 8>{});
       __syncthreads();  // Y
     };
     R set0[3], set1[3];
@@ -1293,7 +1307,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
         }
       }
     }
-    if constexpr (!L2) store_rows_out(st, wave);
+    if constexpr (!L2) store_rows_out(st, wave, std::integral_constant<int, NWS>{});
     __syncthreads();  // Y
   }
 }
@@ -1676,24 +1690,27 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
   // the L2 forward also needs the records of A = sum k'k'^T
   const bool l2 = p.l2 && a.out != nullptr;
   float* astates = reinterpret_cast<float*>(a.ws + p.off_astates);
+  // The exclusive prefixes never read the total of a document's last segment: unless the
+  // final states are exported, that segment's state is not formed.
+  const bool want_final = a.final_S != nullptr || a.final_z != nullptr;
+  const int skip_last = mode == SCAN_PREFIX && !want_final;
   if (p.n_seg_max > 0) {
     if (l2 && BF) {
       hipLaunchKernelGGL((chunk_state_l2_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
                          static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.gk, tab, nseg, rlo,
-                         rhi, states, astates, p.H, p.L, a.rms_eps);
+                         rhi, states, astates, p.H, p.L, a.rms_eps, skip_last);
     } else if (l2) {
       hipLaunchKernelGGL((chunk_state_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                          static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
-                         states, astates, p.H, p.L, a.rms_eps);
+                         states, astates, p.H, p.L, a.rms_eps, skip_last);
     } else {
       hipLaunchKernelGGL((chunk_state_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                          static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gk, tab, nseg, rlo, rhi,
-                         states, static_cast<float*>(nullptr), p.H, p.L, a.rms_eps);
+                         states, static_cast<float*>(nullptr), p.H, p.L, a.rms_eps, skip_last);
     }
   }
   mark(2);
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
-  const bool want_final = a.final_S != nullptr || a.final_z != nullptr;
   if (want_final || (mode != SCAN_NONE && p.n_seg_max > 0)) {
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
                        n_tiles, mode, a.final_S, a.final_z, a.init_S, a.init_z, p.packed ? 0 : 1);
