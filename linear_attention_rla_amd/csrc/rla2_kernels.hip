@@ -1317,12 +1317,13 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 // whole state, out_t = q'_t S_doc / (q'_t . z_doc + eps). The document state arrives in the
 // segment's record (fragment-native S, then z); the state waves round it once to the MFMA
 // operand type and keep it in registers. Software-pipelined over the chunks with one barrier
-// per step: step c maps q of chunk c + 1 (every lane, two tokens per 8 lanes, with q'.z in
-// fp32 against z in LDS from the rounded q' the MFMA uses) into one half of a double-buffered
-// LDS, the state waves form O^T = S^T Q'^T of chunk c from the other half, scale each row by
-// 1/(q'.z + eps) and stage it, and every lane writes the staged rows of chunk c - 1 as whole
-// rows (range-checked buffer stores). Raw q and the RoPE row of the next two chunks are in
-// flight in registers.
+// per step: step c maps q of chunk c + 1 (every lane, two tokens per 8 lanes) into one half of
+// a double-buffered LDS, the state waves form O^T = S^T Q'^T of chunk c from the other half,
+// scale each row by 1/(q'.z + eps) and stage it, and every lane writes the staged rows of
+// chunk c - 1 as whole rows (range-checked buffer stores). Raw q and the RoPE row of the next
+// two chunks are in flight in registers. q'.z: bf16, one more MFMA tile per state wave, z as
+// the bf16 pair hi + lo (rows 4i hold hi, rows 4i + 1 lo, so every lane's accumulator has
+// both for its token; products exact, fp32 sums); fp32, a dot product in the map step.
 
 template <bool BF, int D>
 __global__ __launch_bounds__(NT, 2) void readout_kernel(
@@ -1381,12 +1382,26 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) sa[kb2][ct] = acc_frag<BF>(tile(2 * kb2, ct), tile(2 * kb2 + 1, ct));
   }
+  // bf16: z as the A operand of the q'.z tile, contiguous slot order (slot (g, j) of k-block kb
+  // is dim 32 kb + 8g + j): rows 4i hold bf16(z), rows 4i + 1 the residual, the rest zeros
+  Frag<true> zfr[BF ? G::KB : 1];
+  if constexpr (BF) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < G::KB; ++kb2)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float zv = rec[D * D + 32 * kb2 + 8 * g + j];
+        const __bf16 zh = static_cast<__bf16>(zv);
+        const __bf16 zl = static_cast<__bf16>(zv - static_cast<float>(zh));
+        zfr[kb2].v[j] = (c16 & 3) == 0 ? zh : (c16 & 3) == 1 ? zl : static_cast<__bf16>(0.f);
+      }
+  }
   const float2* hi0 = rope_hi + (size_t)si.hirow * G::HALF + m * G::E;
   auto issue = [&](R& r, float2 (&hi)[G::E], int c) {  // in the order map_chunk refills
     load_raw_buf<BF, D>(r, rq, c * kChunk + t0, m);
     copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(c, nch - 1) * G::HALF);  // RoPE row of the chunk's start
   };
-  // q' of chunk c into sQ[c % 2] with its row reciprocals; the registers are refilled with
+  // q' of chunk c into sQ[c % 2] (fp32: with its row reciprocals); the registers are refilled with
   // chunk c + 2 one token at a time as they free up, then the RoPE row
   auto map_chunk = [&](int c, R& r, float2 (&hi)[G::E]) {
     auto map_tok = [&](auto tok_c) {
@@ -1394,14 +1409,16 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
       R o;
       feature_map_lane<BF, D, tok>(r, o, g1, g2, lo, hi, rms_eps);
       store_rows<BF, D, tok>(sQ + (c & 1) * BUFQ, o, t0, m, QP);
-      float p = 0.f;
+      if constexpr (!BF) {  // fp32: q'.z here, against z in LDS
+        float p = 0.f;
 #pragma unroll
-      for (int e = 0; e < G::E; ++e) {
-        p = __builtin_fmaf(o.get(tok, 0, e), sZ[m * G::E + e], p);
-        p = __builtin_fmaf(o.get(tok, 1, e), sZ[G::HALF + m * G::E + e], p);
+        for (int e = 0; e < G::E; ++e) {
+          p = __builtin_fmaf(o.get(tok, 0, e), sZ[m * G::E + e], p);
+          p = __builtin_fmaf(o.get(tok, 1, e), sZ[G::HALF + m * G::E + e], p);
+        }
+        p = sum8(p);
+        if (m == 0) sInv[(c & 1) * kChunk + t0 + tok] = 1.0f / (p + eps);
       }
-      p = sum8(p);
-      if (m == 0) sInv[(c & 1) * kChunk + t0 + tok] = 1.0f / (p + eps);
       load_raw_buf<BF, D, tok>(r, rq, (c + 2) * kChunk + t0, m);
     };
     map_tok(std::integral_constant<int, 0>{});
@@ -1412,11 +1429,13 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
   auto mma_chunk = [&](int c) {
     const St* cQ = sQ + (c & 1) * BUFQ;
     St* cO = sO + (c & 1) * BUF;
-    floatx4 o4[G::CT][4];
+    floatx4 o4[G::CT][4], dn[4];
 #pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct)
+    for (int t4 = 0; t4 < 4; ++t4) {
+      dn[t4] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) o4[ct][t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < G::CT; ++ct) o4[ct][t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int kb2 = 0; kb2 < G::KB; ++kb2)
 #pragma unroll
@@ -1426,11 +1445,14 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
         else qf = lds_frag<BF>(cQ, QP, t4 * 16 + c16, kb2, g);
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct) o4[ct][t4] = mma(sa[kb2][ct], qf, o4[ct][t4]);
+        if constexpr (BF) dn[t4] = mma(zfr[kb2], qf, dn[t4]);
       }
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const int t = t4 * 16 + c16;  // this lane's row; columns col .. col + 3
-      const float rr = sInv[(c & 1) * kChunk + t];
+      float rr;
+      if constexpr (BF) rr = 1.0f / (dn[t4][0] + dn[t4][1] + eps);
+      else rr = sInv[(c & 1) * kChunk + t];
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) {
         const int col = wave * G::DVW + ct * 16 + 4 * g;
