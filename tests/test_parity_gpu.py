@@ -104,6 +104,41 @@ def test_packed_equals_unpacked_bitwise():
         s0 += n
 
 
+@pytest.mark.parametrize("dtype,l2,with_init", [
+    (torch.bfloat16, False, False),
+    (torch.bfloat16, False, True),
+    (torch.float32, False, True),
+    (torch.bfloat16, True, False),
+    (torch.float32, True, False),
+])
+def test_outputs_independent_of_final_state_export(dtype, l2, with_init):
+    # Without a final-state export the state pass skips each document's last segment (no
+    # exclusive prefix reads its total); the outputs must be bitwise those of a call that forms
+    # every segment's state. Empty documents, one-segment documents, several segments, and a
+    # ragged last segment (128-token segments).
+    lengths = [0, 64, 300, 1, 0, 700, 129]
+    H, d = 2, 64
+    inp = workloads.fwd_inputs(1, H, sum(lengths), d, dtype, seed=42, lengths=lengths)
+    q, k, v, gq, gk, cu = on_gpu(inp)
+    kw, okw = {}, {}
+    if with_init:
+        S0, z0 = workloads.initial_state(H, d, seed=5)
+        kw = dict(initial_S=S0.to(DEV), initial_z=z0.to(DEV), initial_pos=100)
+        okw = dict(initial_S=f64(S0), initial_z=f64(z0), initial_pos=100)
+    if l2:
+        kw["l2_denominator"] = True
+    a = rla.fwd(q, k, v, gq, gk, cu, seg_chunks=2, **kw)
+    b, fS, fz = rla.fwd(q, k, v, gq, gk, cu, seg_chunks=2, return_final_state=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    if l2:
+        ref = oracle.fwd_l2(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.gamma_q), f64(inp.gamma_k),
+                            inp.cu_seqlens.numpy(), oracle.DEFAULT_L2_EPS, inp.rms_eps, inp.rope_base)
+    else:
+        ref = _oracle_opts(inp, **okw)
+    assert row_rel_err(a, ref) <= tol(inp)
+
+
 def disjoint_qk(L, d, seed=3):
     """bf16 q, k [1, 1, L, d] (on the GPU) whose features have disjoint positive supports:
     after RoPE, q is positive exactly on a seeded half A of the channels and k exactly off A
