@@ -267,6 +267,25 @@ def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
         res[name] = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes": nbytes,
                      "traffic": measured_traffic(name + "_kernel")}
+    # the training form: the forward's workspace (its prefix states) is kept and read by the
+    # backward instead of a second state pass (rla2_bwd_chunked_saved; bitwise the same grads)
+    fws = torch.empty(max(rla.fwd_workspace_size(desc), 1), dtype=torch.uint8, device=q.device)
+    rla.fwd(q, k, v, gq, gk, workspace=fws)
+
+    def run_saved():
+        rla.bwd(q, k, v, gq, gk, dout, out=outs, workspace=ws, fwd_workspace=fws)
+
+    for _ in range(3):
+        run_saved()
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        run_saved()
+    ev.hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms_saved = ev.elapsed(0, 1) / steps
+    res["with_forward_states"] = {"ms_per_call": ms_saved, "tokens_per_s": B * L / (ms_saved * 1e-3),
+                                  "steps": steps, "note": "states read from the forward's workspace"}
     return res
 
 

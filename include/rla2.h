@@ -153,7 +153,10 @@ rla2_status rla2_fwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
  *               the first document of each row); NULL = not exported.
  *  final_z      optional [N, H, d] fp32, z = sum_i k'_i; NULL = not exported.
  *  workspace    device scratch of at least rla2_fwd_workspace_size() bytes,
- *               256-byte aligned; contents on entry are ignored.
+ *               256-byte aligned; contents on entry are ignored. After a causal
+ *               forward with the Sum denominator it holds the segment table, the
+ *               RoPE tables and every segment's prefix state, which
+ *               rla2_bwd_chunked_saved reads in place of forming them again.
  * L == 0 or N == 0 is a valid no-op (final states of empty documents are 0).
  */
 rla2_status rla2_fwd_chunked(const rla2_fwd_desc* desc, const void* q, const void* k,
@@ -241,6 +244,30 @@ rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
                                       float* dgamma_q, float* dgamma_k, void* workspace,
                                       size_t workspace_bytes, hipStream_t stream,
                                       hipEvent_t* events);
+
+/*
+ * rla2_bwd_chunked without its state pass: the forward's states S_t, z_t (RLA page §4.2,
+ * the states the backward of the layer reads) are taken from `fwd_workspace`, the
+ * workspace of an rla2_fwd_chunked call with the same desc (causal, Sum denominator) and
+ * the same k, v, gamma_k and initial state, not written since. What it holds is not
+ * checked; it is only read, so one forward's workspace serves any number of backward
+ * calls. Results are bitwise those of rla2_bwd_chunked.
+ *  fwd_workspace        device pointer, 256-byte aligned, at least
+ *                       rla2_fwd_workspace_size() bytes (fwd_workspace_bytes); it may
+ *                       not overlap the outputs or `workspace` (RLA2_ERR_ALIAS).
+ *  events               NULL, or RLA2_BWD_KERNELS + 1 events as for
+ *                       rla2_bwd_chunked_profiled (kernels 0..2 are not run).
+ * Other arguments, ownership and errors as for rla2_bwd_chunked; RLA2_ERR_WORKSPACE when
+ * fwd_workspace is too small or misaligned, RLA2_ERR_NULL_POINTER when it is NULL and
+ * the problem is not empty.
+ */
+rla2_status rla2_bwd_chunked_saved(const rla2_fwd_desc* desc, const void* q, const void* k,
+                                   const void* v, const float* gamma_q, const float* gamma_k,
+                                   const void* dout, void* dq, void* dk, void* dv,
+                                   float* dgamma_q, float* dgamma_k, void* workspace,
+                                   size_t workspace_bytes, const void* fwd_workspace,
+                                   size_t fwd_workspace_bytes, hipStream_t stream,
+                                   hipEvent_t* events);
 
 /* Workspace bytes rla2_feature_map needs for `desc` (segment table and RoPE tables). */
 rla2_status rla2_feature_map_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);

@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         L.rla2_bwd_workspace_size.argtypes = [_DESC, _SZ]
         L.rla2_bwd_chunked_profiled.restype = ctypes.c_int
         L.rla2_bwd_chunked_profiled.argtypes = [_DESC] + [_P] * 12 + [ctypes.c_size_t, _P, _P]
+        L.rla2_bwd_chunked_saved.restype = ctypes.c_int
+        L.rla2_bwd_chunked_saved.argtypes = [_DESC] + [_P] * 12 + [ctypes.c_size_t, _P, ctypes.c_size_t, _P, _P]
         L.rla2_bwd_chunked.restype = ctypes.c_int
         L.rla2_bwd_chunked.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.rla2_feature_map_workspace_size.restype = ctypes.c_int
@@ -229,11 +231,14 @@ def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0,
 
 def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
         rope_base=10000.0, initial_S=None, initial_z=None, initial_pos=0, want_dgamma=True, workspace=None,
-        out=None, events=None):
+        out=None, events=None, fwd_workspace=None):
     """Backward of the causal forward (bf16) for the same inputs; ``dout`` = dL/dout.
     Returns ``(dq, dk, dv, dgamma_q, dgamma_k)`` (the last two None unless ``want_dgamma``).
     ``out``: optional preallocated ``(dq, dk, dv, dgamma_q, dgamma_k)``; ``events``: optional
-    ctypes array of RLA2_BWD_KERNELS + 1 hipEvent_t handles (rla2_bwd_chunked_profiled)."""
+    ctypes array of RLA2_BWD_KERNELS + 1 hipEvent_t handles (rla2_bwd_chunked_profiled).
+    ``fwd_workspace``: the ``workspace`` tensor of the matching ``fwd`` call (same inputs and
+    options, causal, Sum denominator), untouched since: its states are read instead of being
+    formed again (rla2_bwd_chunked_saved; bitwise the same gradients)."""
     for n_, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _check_dev(n_, t, torch.bfloat16)
         if t.shape != q.shape:
@@ -271,7 +276,12 @@ def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunk
         workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
     args = (ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q), _ptr(gamma_k), _ptr(dout), _ptr(dq),
             _ptr(dk), _ptr(dv), _ptr(dgq), _ptr(dgk), _ptr(workspace), workspace.numel(), _stream(q.device))
-    if events is None:
+    if fwd_workspace is not None:
+        _check_dev("fwd_workspace", fwd_workspace, torch.uint8)
+        st = lib().rla2_bwd_chunked_saved(*args[:-1], _ptr(fwd_workspace), fwd_workspace.numel(), args[-1], events)
+        if st:
+            raise Rla2Error(st, "rla2_bwd_chunked_saved")
+    elif events is None:
         st = lib().rla2_bwd_chunked(*args)
     else:
         st = lib().rla2_bwd_chunked_profiled(*args, events)

@@ -292,18 +292,14 @@ rla2_status rla2_bwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
   return RLA2_OK;
 }
 
-rla2_status rla2_bwd_chunked(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v,
-                             const float* gamma_q, const float* gamma_k, const void* dout,
-                             void* dq, void* dk, void* dv, float* dgamma_q, float* dgamma_k, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
-  return rla2_bwd_chunked_profiled(desc, q, k, v, gamma_q, gamma_k, dout, dq, dk, dv, dgamma_q, dgamma_k,
-                                   workspace, workspace_bytes, stream, nullptr);
-}
+namespace {
 
-rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v,
-                                      const float* gamma_q, const float* gamma_k, const void* dout, void* dq,
-                                      void* dk, void* dv, float* dgamma_q, float* dgamma_k, void* workspace,
-                                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+// The backward entry points; `saved` (with `saved_bytes`) is the matching forward's workspace,
+// or null.
+rla2_status bwd_impl(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v, const float* gamma_q,
+                     const float* gamma_k, const void* dout, void* dq, void* dk, void* dv, float* dgamma_q,
+                     float* dgamma_k, void* workspace, size_t workspace_bytes, const void* saved,
+                     size_t saved_bytes, hipStream_t stream, hipEvent_t* events) {
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
@@ -317,6 +313,9 @@ rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   if (p.bytes_bwd > 0 && (workspace == nullptr || workspace_bytes < p.bytes_bwd)) return RLA2_ERR_WORKSPACE;
   if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
     return RLA2_ERR_WORKSPACE;
+  // the forward's workspace holds its records up to p.bytes (the Sum mode has no second set)
+  if (saved != nullptr && (saved_bytes < p.bytes || (reinterpret_cast<uintptr_t>(saved) % rla2::kAlign) != 0))
+    return RLA2_ERR_WORKSPACE;
   if (misaligned({q, k, v, dout, dq, dk, dv, gamma_q, gamma_k, dgamma_q, dgamma_k, desc->initial_S,
                   desc->initial_z}))
     return RLA2_ERR_MISALIGNED;
@@ -324,7 +323,8 @@ rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   const Range ws{workspace, p.bytes_bwd};
   const Range ins[] = {{q, act}, {k, act}, {v, act}, {dout, act}, {gamma_q, gam}, {gamma_k, gam},
                        {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4},
-                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4}};
+                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4},
+                       {saved, saved != nullptr ? p.bytes : 0}};
   for (const Range& r : ins) {
     if (overlap(ws, r)) return RLA2_ERR_ALIAS;
     for (const Range& o : outs)
@@ -343,8 +343,39 @@ rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   rla2::FwdArgs a{desc->cu_seqlens, q, k, v, gamma_q, gamma_k, nullptr, nullptr, nullptr,
                   desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
                   static_cast<char*>(workspace)};
-  rla2::BwdArgs b{dout, dq, dk, dv, dgamma_q, dgamma_k};
+  rla2::BwdArgs b{dout, dq, dk, dv, dgamma_q, dgamma_k, static_cast<const char*>(saved)};
   return finish(rla2::launch_backward(p, a, b, stream, events));
+}
+
+}  // namespace
+
+rla2_status rla2_bwd_chunked(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v,
+                             const float* gamma_q, const float* gamma_k, const void* dout,
+                             void* dq, void* dk, void* dv, float* dgamma_q, float* dgamma_k, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(desc, q, k, v, gamma_q, gamma_k, dout, dq, dk, dv, dgamma_q, dgamma_k, workspace,
+                  workspace_bytes, nullptr, 0, stream, nullptr);
+}
+
+rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v,
+                                      const float* gamma_q, const float* gamma_k, const void* dout, void* dq,
+                                      void* dk, void* dv, float* dgamma_q, float* dgamma_k, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  return bwd_impl(desc, q, k, v, gamma_q, gamma_k, dout, dq, dk, dv, dgamma_q, dgamma_k, workspace,
+                  workspace_bytes, nullptr, 0, stream, events);
+}
+
+rla2_status rla2_bwd_chunked_saved(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v,
+                                   const float* gamma_q, const float* gamma_k, const void* dout, void* dq,
+                                   void* dk, void* dv, float* dgamma_q, float* dgamma_k, void* workspace,
+                                   size_t workspace_bytes, const void* fwd_workspace,
+                                   size_t fwd_workspace_bytes, hipStream_t stream, hipEvent_t* events) {
+  Plan p;
+  rla2_status st = plan_desc(desc, &p);
+  if (st != RLA2_OK) return st;
+  if (p.bytes > 0 && fwd_workspace == nullptr) return RLA2_ERR_NULL_POINTER;
+  return bwd_impl(desc, q, k, v, gamma_q, gamma_k, dout, dq, dk, dv, dgamma_q, dgamma_k, workspace,
+                  workspace_bytes, p.bytes > 0 ? fwd_workspace : nullptr, fwd_workspace_bytes, stream, events);
 }
 
 rla2_status rla2_feature_map_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {

@@ -1156,17 +1156,25 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   auto mark = [&](int i) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
-  hipError_t e = launch_fwd_states(p, a, s, ev);
-  if (e != hipSuccess) return e;
+  // the forward's segment table, RoPE tables and prefix records: formed again, or read from
+  // the workspace of the matching forward (same plan, so the same offsets)
+  hipError_t e = hipSuccess;
+  if (b.saved == nullptr) {
+    e = launch_fwd_states(p, a, s, ev);
+    if (e != hipSuccess) return e;
+  } else {
+    for (int i = 0; i < 3; ++i) mark(i);
+  }
+  const char* fw = b.saved != nullptr ? b.saved : a.ws;
   if (p.n_seg_max == 0) {
     for (int i = 3; i <= kNumBwdKernels; ++i) mark(i);
     return hipGetLastError();
   }
-  int32_t* tab = reinterpret_cast<int32_t*>(a.ws + p.off_tab);
-  int32_t* nseg = reinterpret_cast<int32_t*>(a.ws + p.off_nseg);
-  float2* rlo = reinterpret_cast<float2*>(a.ws + p.off_rope_lo);
-  float2* rhi = reinterpret_cast<float2*>(a.ws + p.off_rope_hi);
-  float* states = reinterpret_cast<float*>(a.ws + p.off_states);
+  const int32_t* tab = reinterpret_cast<const int32_t*>(fw + p.off_tab);
+  const int32_t* nseg = reinterpret_cast<const int32_t*>(fw + p.off_nseg);
+  const float2* rlo = reinterpret_cast<const float2*>(fw + p.off_rope_lo);
+  const float2* rhi = reinterpret_cast<const float2*>(fw + p.off_rope_hi);
+  const float* states = reinterpret_cast<const float*>(fw + p.off_states);
   float* pstates = reinterpret_cast<float*>(a.ws + p.off_pstates);
   float* den = reinterpret_cast<float*>(a.ws + p.off_den);
   float* gd = reinterpret_cast<float*>(a.ws + p.off_gd);
@@ -1184,7 +1192,7 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   hipLaunchKernelGGL((bwd_pstate_kernel<D>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
                      pstates, p.H, p.L, a.rms_eps);
   mark(5);
-  e = launch_scan_suffix(p, a.ws, pstates, s);
+  e = launch_scan_suffix(p, fw, pstates, s);
   if (e != hipSuccess) return e;
   mark(6);
   hipLaunchKernelGGL((bwd_dkv_ws_kernel<D>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,

@@ -62,13 +62,15 @@ struct BwdArgs {
   const void* dout;            // cotangent of the forward output, [B, H, L, d]
   void *dq, *dk, *dv;          // written, [B, H, L, d]
   float *dgamma_q, *dgamma_k;  // written, [H, d] (null: not formed)
+  const char* saved;           // the matching causal forward's workspace (segment table, RoPE
+                               // tables, prefix records), or null: the state pass runs again
 };
 
 // prep + chunk state + exclusive-prefix scan of the records (what the backward needs of the
 // forward's state pass; `ev`, optional, gets events 0..2 before the three launches); the
 // reverse scan of a second record set.
 hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
-hipError_t launch_scan_suffix(const Plan& p, char* ws, float* states, hipStream_t s);
+hipError_t launch_scan_suffix(const Plan& p, const char* ws, float* states, hipStream_t s);
 // the whole chunked backward (rla2_backward.hip); `ev` (optional) gets kNumBwdKernels + 1
 // events recorded around the kernels
 constexpr int kNumBwdKernels = 8;

@@ -845,9 +845,11 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
 // Waves 4..7 ("mappers") turn raw q, k, v into the chunk operands: the feature map of q
 // and k (VALU work; both share the rotation angles) and the Q', K', V rows in LDS. They keep
 // two chunks of raw input in flight in registers. Waves 0..3 ("MMA waves") run the score and
-// output phases on the previous chunk from the other half of a double-buffered LDS and write
-// the outputs. Each SIMD holds one wave of each kind, so the mappers' VALU work overlaps the
-// MMA waves' matrix and LDS work, and the input loads overlap both.
+// output phases on the previous chunk from the other half of a double-buffered LDS and stage
+// the output rows; the rows of the chunk before leave for memory at the end of the step, half
+// from each role (L2: from the mappers). Each SIMD holds one wave of each kind, so the
+// mappers' VALU work overlaps the MMA waves' matrix and LDS work, and the input loads overlap
+// both.
 //
 // Step s (s = 0 .. nsteps-1): mappers map chunk s into buffer s % 2; MMA waves process chunk
 // s - 1 from buffer (s - 1) % 2. One workgroup barrier per step (Y, at its end: buffer s % 2
@@ -1850,8 +1852,8 @@ hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hip
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_suffix(const Plan& p, char* ws, float* states, hipStream_t s) {
-  int32_t* docoff = reinterpret_cast<int32_t*>(ws + p.off_docoff);
+hipError_t launch_scan_suffix(const Plan& p, const char* ws, float* states, hipStream_t s) {
+  const int32_t* docoff = reinterpret_cast<const int32_t*>(ws + p.off_docoff);
   const int D = p.d;
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
   hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,

@@ -170,3 +170,52 @@ def test_backward_c4_size_heads():
             worst[n_] = max(worst.get(n_, 0.0), e)
     print("bwd long context L=65536 heads 0, 29: " + " ".join(f"{n_} {e:.2e}" for n_, e in worst.items()))
     _assert_bar(worst)
+
+
+@pytest.mark.parametrize("lengths,seg_chunks,pos,with_init,final", [
+    (None, 0, 0, False, False),
+    ([70, 0, 1, 179], 1, 0, False, True),
+    ([3, 193, 64], 2, 65, True, False),
+    ([300, 700], 1, 0, False, False),
+])
+def test_backward_from_the_forward_workspace(lengths, seg_chunks, pos, with_init, final):
+    # The causal forward leaves the segment table, the RoPE tables and every segment's prefix
+    # state in its workspace; the backward that reads them (rla2_bwd_chunked_saved) must give
+    # bitwise the gradients of the one that forms them again, also when read a second time.
+    H, d = 2, 64
+    L = 300 if lengths is None else sum(lengths)
+    inp = workloads.fwd_inputs(1, H, L, d, torch.bfloat16, seed=900 + L, lengths=lengths)
+    dout = _dout(inp.q.shape, seed=L)
+    cu = None if inp.cu_seqlens is None else inp.cu_seqlens.to(DEV)
+    q, k, v, gq, gk = (x.to(DEV) for x in (inp.q, inp.k, inp.v, inp.gamma_q, inp.gamma_k))
+    S0 = z0 = None
+    if with_init:
+        S0, z0 = (x.to(DEV) for x in workloads.initial_state(H, d, seed=L))
+    n_docs = 0 if cu is None else cu.numel() - 1
+    desc = rla.make_desc(1, H, L, d, rla.BF16, cu, n_docs, seg_chunks=seg_chunks, initial_pos=pos,
+                         initial_S=S0, initial_z=z0)
+    fws = torch.empty(rla.fwd_workspace_size(desc), dtype=torch.uint8, device=DEV)
+    rla.fwd(q, k, v, gq, gk, cu, seg_chunks=seg_chunks, workspace=fws, initial_S=S0, initial_z=z0,
+            initial_pos=pos, return_final_state=final)
+    kw = dict(seg_chunks=seg_chunks, initial_S=S0, initial_z=z0, initial_pos=pos)
+    ref = rla.bwd(q, k, v, gq, gk, dout.to(DEV), cu, **kw)
+    for _ in range(2):
+        got = rla.bwd(q, k, v, gq, gk, dout.to(DEV), cu, fwd_workspace=fws, **kw)
+        torch.cuda.synchronize()
+        for x, y in zip(got, ref):
+            assert torch.equal(x, y)
+
+
+def test_backward_from_the_forward_workspace_rejects_bad_buffers():
+    inp = workloads.fwd_inputs(1, 1, 128, 64, torch.bfloat16, seed=91)
+    q, k, v, gq, gk = (x.to(DEV) for x in (inp.q, inp.k, inp.v, inp.gamma_q, inp.gamma_k))
+    dout = _dout(inp.q.shape, seed=92).to(DEV)
+    desc = rla.make_desc(1, 1, 128, 64, rla.BF16)
+    n = rla.fwd_workspace_size(desc)
+    with pytest.raises(rla.Rla2Error):  # too small
+        rla.bwd(q, k, v, gq, gk, dout, fwd_workspace=torch.zeros(n - 256, dtype=torch.uint8, device=DEV))
+    with pytest.raises(rla.Rla2Error):  # misaligned
+        rla.bwd(q, k, v, gq, gk, dout, fwd_workspace=torch.zeros(n + 256, dtype=torch.uint8, device=DEV)[1:n + 1])
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device=DEV)
+    with pytest.raises(rla.Rla2Error):  # the backward's own workspace
+        rla.bwd(q, k, v, gq, gk, dout, workspace=ws, fwd_workspace=ws[:n])
