@@ -165,6 +165,63 @@ rla2_status finish(hipError_t e) {
 
 }  // namespace
 
+namespace {
+
+// The backward entry points; `saved` (with `saved_bytes`) is the matching forward's workspace,
+// or null.
+rla2_status bwd_impl(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v, const float* gamma_q,
+                     const float* gamma_k, const void* dout, void* dq, void* dk, void* dv, float* dgamma_q,
+                     float* dgamma_k, void* workspace, size_t workspace_bytes, const void* saved,
+                     size_t saved_bytes, hipStream_t stream, hipEvent_t* events) {
+  Plan p;
+  rla2_status st = plan_desc(desc, &p);
+  if (st != RLA2_OK) return st;
+  if (p.dtype != RLA2_BF16 || p.bidirectional || p.l2) return RLA2_ERR_UNSUPPORTED;
+  const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
+  const size_t gam = (size_t)p.H * p.d * 4;
+  if (act > 0 && (q == nullptr || k == nullptr || v == nullptr || dout == nullptr ||
+                  dq == nullptr || dk == nullptr || dv == nullptr || gamma_q == nullptr || gamma_k == nullptr))
+    return RLA2_ERR_NULL_POINTER;
+  if (p.packed && desc->cu_seqlens == nullptr) return RLA2_ERR_NULL_POINTER;
+  if (p.bytes_bwd > 0 && (workspace == nullptr || workspace_bytes < p.bytes_bwd)) return RLA2_ERR_WORKSPACE;
+  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
+    return RLA2_ERR_WORKSPACE;
+  // the forward's workspace holds its records up to p.bytes (the Sum mode has no second set)
+  if (saved != nullptr && (saved_bytes < p.bytes || (reinterpret_cast<uintptr_t>(saved) % rla2::kAlign) != 0))
+    return RLA2_ERR_WORKSPACE;
+  if (misaligned({q, k, v, dout, dq, dk, dv, gamma_q, gamma_k, dgamma_q, dgamma_k, desc->initial_S,
+                  desc->initial_z}))
+    return RLA2_ERR_MISALIGNED;
+  const Range outs[] = {{dq, act}, {dk, act}, {dv, act}, {dgamma_q, gam}, {dgamma_k, gam}};
+  const Range ws{workspace, p.bytes_bwd};
+  const Range ins[] = {{q, act}, {k, act}, {v, act}, {dout, act}, {gamma_q, gam}, {gamma_k, gam},
+                       {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4},
+                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4},
+                       {saved, saved != nullptr ? p.bytes : 0}};
+  for (const Range& r : ins) {
+    if (overlap(ws, r)) return RLA2_ERR_ALIAS;
+    for (const Range& o : outs)
+      if (overlap(o, r)) return RLA2_ERR_ALIAS;
+  }
+  for (size_t i = 0; i < 5; ++i) {
+    if (overlap(outs[i], ws)) return RLA2_ERR_ALIAS;
+    for (size_t j = i + 1; j < 5; ++j)
+      if (overlap(outs[i], outs[j])) return RLA2_ERR_ALIAS;
+  }
+  if (p.packed && validate_mode() == 1) {
+    st = check_seqlens(p, desc->cu_seqlens, stream);
+    if (st != RLA2_OK) return st;
+  }
+  if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
+  rla2::FwdArgs a{desc->cu_seqlens, q, k, v, gamma_q, gamma_k, nullptr, nullptr, nullptr,
+                  desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
+                  static_cast<char*>(workspace)};
+  rla2::BwdArgs b{dout, dq, dk, dv, dgamma_q, dgamma_k, static_cast<const char*>(saved)};
+  return finish(rla2::launch_backward(p, a, b, stream, events));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* rla2_status_string(rla2_status s) {
@@ -291,63 +348,6 @@ rla2_status rla2_bwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
   *bytes = p.bytes_bwd;
   return RLA2_OK;
 }
-
-namespace {
-
-// The backward entry points; `saved` (with `saved_bytes`) is the matching forward's workspace,
-// or null.
-rla2_status bwd_impl(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v, const float* gamma_q,
-                     const float* gamma_k, const void* dout, void* dq, void* dk, void* dv, float* dgamma_q,
-                     float* dgamma_k, void* workspace, size_t workspace_bytes, const void* saved,
-                     size_t saved_bytes, hipStream_t stream, hipEvent_t* events) {
-  Plan p;
-  rla2_status st = plan_desc(desc, &p);
-  if (st != RLA2_OK) return st;
-  if (p.dtype != RLA2_BF16 || p.bidirectional || p.l2) return RLA2_ERR_UNSUPPORTED;
-  const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
-  const size_t gam = (size_t)p.H * p.d * 4;
-  if (act > 0 && (q == nullptr || k == nullptr || v == nullptr || dout == nullptr ||
-                  dq == nullptr || dk == nullptr || dv == nullptr || gamma_q == nullptr || gamma_k == nullptr))
-    return RLA2_ERR_NULL_POINTER;
-  if (p.packed && desc->cu_seqlens == nullptr) return RLA2_ERR_NULL_POINTER;
-  if (p.bytes_bwd > 0 && (workspace == nullptr || workspace_bytes < p.bytes_bwd)) return RLA2_ERR_WORKSPACE;
-  if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
-    return RLA2_ERR_WORKSPACE;
-  // the forward's workspace holds its records up to p.bytes (the Sum mode has no second set)
-  if (saved != nullptr && (saved_bytes < p.bytes || (reinterpret_cast<uintptr_t>(saved) % rla2::kAlign) != 0))
-    return RLA2_ERR_WORKSPACE;
-  if (misaligned({q, k, v, dout, dq, dk, dv, gamma_q, gamma_k, dgamma_q, dgamma_k, desc->initial_S,
-                  desc->initial_z}))
-    return RLA2_ERR_MISALIGNED;
-  const Range outs[] = {{dq, act}, {dk, act}, {dv, act}, {dgamma_q, gam}, {dgamma_k, gam}};
-  const Range ws{workspace, p.bytes_bwd};
-  const Range ins[] = {{q, act}, {k, act}, {v, act}, {dout, act}, {gamma_q, gam}, {gamma_k, gam},
-                       {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4},
-                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4},
-                       {saved, saved != nullptr ? p.bytes : 0}};
-  for (const Range& r : ins) {
-    if (overlap(ws, r)) return RLA2_ERR_ALIAS;
-    for (const Range& o : outs)
-      if (overlap(o, r)) return RLA2_ERR_ALIAS;
-  }
-  for (size_t i = 0; i < 5; ++i) {
-    if (overlap(outs[i], ws)) return RLA2_ERR_ALIAS;
-    for (size_t j = i + 1; j < 5; ++j)
-      if (overlap(outs[i], outs[j])) return RLA2_ERR_ALIAS;
-  }
-  if (p.packed && validate_mode() == 1) {
-    st = check_seqlens(p, desc->cu_seqlens, stream);
-    if (st != RLA2_OK) return st;
-  }
-  if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
-  rla2::FwdArgs a{desc->cu_seqlens, q, k, v, gamma_q, gamma_k, nullptr, nullptr, nullptr,
-                  desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
-                  static_cast<char*>(workspace)};
-  rla2::BwdArgs b{dout, dq, dk, dv, dgamma_q, dgamma_k, static_cast<const char*>(saved)};
-  return finish(rla2::launch_backward(p, a, b, stream, events));
-}
-
-}  // namespace
 
 rla2_status rla2_bwd_chunked(const rla2_fwd_desc* desc, const void* q, const void* k, const void* v,
                              const float* gamma_q, const float* gamma_k, const void* dout,
