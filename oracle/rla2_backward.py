@@ -113,3 +113,22 @@ def bwd_qk_prime(qp, kp, v, g, eps=DEFAULT_EPS):
         dkp[i] = P @ v[i] + p
         dv[i] = P.T @ kp[i]
     return dqp, dkp, dv
+
+
+def bwd_one_document(q, k, v, g, gamma_q, gamma_k, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
+                     rope_base=DEFAULT_ROPE_BASE):
+    """Gradients (dq, dk, dv, dgamma_q, dgamma_k) of sum(out * g) for ONE head's single
+    document ``[n, d]`` (positions 0..n-1, no initial state), in time linear in n: the
+    RLA page §4.2 recursions (``bwd_qk_prime``) give the gradients with respect to q', k'
+    and v, and autograd of the fp64 preamble (``feature_map_torch``) carries the first two
+    back through ReLU, RoPE and RMSNorm. The long-document counterpart of ``bwd``, which
+    differentiates the quadratic closed form."""
+    n = q.shape[0]
+    pos = np.arange(n)
+    xq, xk, tq, tk = (_t(x).requires_grad_(True) for x in (q, k, gamma_q, gamma_k))
+    qp = feature_map_torch(xq, tq, pos, rms_eps, rope_base)
+    kp = feature_map_torch(xk, tk, pos, rms_eps, rope_base)
+    dqp, dkp, dv = bwd_qk_prime(qp.detach().numpy(), kp.detach().numpy(), _t(v).numpy(), _t(g).numpy(), eps)
+    dq, dgq = torch.autograd.grad(qp, (xq, tq), torch.as_tensor(dqp))
+    dk, dgk = torch.autograd.grad(kp, (xk, tk), torch.as_tensor(dkp))
+    return dq.numpy(), dk.numpy(), dv, dgq.numpy(), dgk.numpy()

@@ -140,21 +140,6 @@ def test_backward_c3_size_sampled():
     _assert_bar(worst)
 
 
-def _head_oracle(q, k, v, g, gq, gk, eps, rms_eps, rope_base):
-    """Gradients of one head's single document through the page's backward recursions
-    (oracle.bwd_qk_prime, linear in the length) and autograd of the fp64 feature map."""
-    n = q.shape[0]
-    pos = np.arange(n)
-    xq, xk = (torch.tensor(f64(x), requires_grad=True) for x in (q, k))
-    tq, tk = (torch.tensor(f64(x), requires_grad=True) for x in (gq, gk))
-    qp = oracle.rla2_backward.feature_map_torch(xq, tq, pos, rms_eps, rope_base)
-    kp = oracle.rla2_backward.feature_map_torch(xk, tk, pos, rms_eps, rope_base)
-    dqp, dkp, dv = oracle.bwd_qk_prime(qp.detach().numpy(), kp.detach().numpy(), f64(v), f64(g), eps)
-    dq, dgq = torch.autograd.grad(qp, (xq, tq), torch.tensor(dqp))
-    dk, dgk = torch.autograd.grad(kp, (xk, tk), torch.tensor(dkp))
-    return dq.numpy(), dk.numpy(), dv, dgq.numpy(), dgk.numpy()
-
-
 def test_backward_c4_size_heads():
     # the long-context workload (one 65536-token document per head, 32 heads, d = 128, 10% of
     # the q, k channels biased negative); every row of two heads against the recursions
@@ -163,8 +148,8 @@ def test_backward_c4_size_heads():
     got = _run(inp, dout)
     worst = {}
     for h in (0, 29):
-        ref = _head_oracle(inp.q[0, h], inp.k[0, h], inp.v[0, h], dout[0, h], inp.gamma_q[h], inp.gamma_k[h], inp.eps,
-                           inp.rms_eps, inp.rope_base)
+        ref = oracle.bwd_one_document(f64(inp.q[0, h]), f64(inp.k[0, h]), f64(inp.v[0, h]), f64(dout[0, h]),
+                                      f64(inp.gamma_q[h]), f64(inp.gamma_k[h]), inp.eps, inp.rms_eps, inp.rope_base)
         errs = _errors([x[0, h] for x in got[:3]] + [got[3][h], got[4][h]], ref)
         for n_, e in errs.items():
             worst[n_] = max(worst.get(n_, 0.0), e)

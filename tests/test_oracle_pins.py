@@ -449,6 +449,24 @@ def test_backward_initial_state_is_a_continuation():
     np.testing.assert_allclose(out.numpy(), ref, rtol=1e-11, atol=1e-13)
 
 
+
+def test_backward_one_document_matches_autograd():
+    # The linear-time gradient of one head's single document (the page's §4.2 recursions
+    # for q', k', v, then autograd of the preamble) equals autograd of the quadratic
+    # closed form: the same five gradients, so it can stand in for it at long lengths.
+    r = np.random.default_rng(58)
+    n, d = 40, 8
+    q, k, v, gq, gk, _ = _rand_case(1, 1, n, d, 59, None)
+    q[..., :2] -= 1.0    # some negative pre-activations, so the ReLU gate matters
+    g = r.normal(size=q.shape)
+    ref = oracle.bwd(q, k, v, gq, gk, g, eps=1e-3, rope_base=100.0)
+    got = oracle.bwd_one_document(q[0, 0], k[0, 0], v[0, 0], g[0, 0], gq[0], gk[0], eps=1e-3, rope_base=100.0)
+    for a, b2 in zip(got[:3], ref[:3]):
+        np.testing.assert_allclose(a, b2[0, 0], rtol=1e-10, atol=1e-12)
+    for a, b2 in zip(got[3:], ref[3:]):
+        np.testing.assert_allclose(a, b2[0], rtol=1e-10, atol=1e-12)
+    assert (ref[1] == 0).sum() == 0 and np.abs(ref[4]).min() > 0   # every gradient is exercised
+
 # --- the original RLA's L2 denominator (RLA page §2.1 closed form, §4.1 A state) -------
 
 @pytest.mark.parametrize("B,H,L,d,lengths", [(1, 2, 11, 6, [4, 7]), (2, 1, 9, 4, None), (1, 1, 8, 8, [1, 0, 7])])
@@ -519,3 +537,21 @@ def _unrotated_copies(xq, xk, n):
         toks = np.concatenate([oracle.rope_rotate_half(y, np.array([-t])) for t in range(n)])
         out.append(toks[None, None])
     return out
+
+
+
+def test_l2_rows_matches_full():
+    # the sampled-row form of the L2 closed form (used at full sizes) equals the whole
+    # forward on the same rows: packed with an empty document, several heads, rows on both
+    # sides of every document boundary, rows given out of order; and a dense batch
+    q, k, v, gq, gk, cu = _rand_case(1, 3, 50, 8, 65, [20, 0, 3, 27])
+    full = oracle.fwd_l2(q, k, v, gq, gk, cu)
+    rows = [49, 0, 1, 19, 20, 21, 22, 23, 30]
+    for h in range(3):
+        np.testing.assert_allclose(oracle.fwd_l2_rows(q, k, v, gq, gk, 0, h, rows, cu),
+                                   full[0, h, sorted(rows)], rtol=1e-13, atol=1e-15)
+    q, k, v, gq, gk, _ = _rand_case(2, 2, 33, 4, 66)
+    full = oracle.fwd_l2(q, k, v, gq, gk, eps=1e-3)
+    for b in range(2):
+        np.testing.assert_allclose(oracle.fwd_l2_rows(q, k, v, gq, gk, b, 1, [32, 0, 7], eps=1e-3),
+                                   full[b, 1, [0, 7, 32]], rtol=1e-13)
