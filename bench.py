@@ -101,26 +101,31 @@ def decode_algorithmic(N, H, d):
 def cpu_baseline(inp, budget_s):
     """The oracle as it stands on a bounded sample of the same workload: blocks of
     1024 query rows drawn uniformly over the sequence of head 0, until the budget."""
+    import contextlib
+
     import numpy as np
     import oracle
-    try:
+    cores = len(os.sched_getaffinity(0))
+    try:  # the oracle's BLAS runs on exactly the cores this process may use
         import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info() if i["user_api"] == "blas")
+        limit = threadpoolctl.threadpool_limits(limits=cores, user_api="blas")
     except Exception:
-        threads = os.cpu_count()
+        limit = contextlib.nullcontext()
     B, H, L, d = inp.q.shape
     rng = np.random.default_rng(1234)
     gq, gk = inp.gamma_q.double().numpy(), inp.gamma_k.double().numpy()
     rows_done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s and rows_done < 32768:
-        rows = np.sort(rng.choice(L, 1024, replace=False))
-        oracle.fwd_rows(inp.q, inp.k, inp.v, gq, gk, 0, 0, rows, None, inp.eps, inp.rms_eps, inp.rope_base)
-        rows_done += 1024
+    with limit:
+        while time.perf_counter() - t0 < budget_s and rows_done < 32768:
+            rows = np.sort(rng.choice(L, 1024, replace=False))
+            oracle.fwd_rows(inp.q, inp.k, inp.v, gq, gk, 0, 0, rows, None, inp.eps, inp.rms_eps, inp.rope_base)
+            rows_done += 1024
     dt = time.perf_counter() - t0
     # token-heads per second, scaled to tokens/s of the H-head workload
-    return {"value": rows_done / dt / H, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": rows_done / dt / H, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows_done} query rows of head 0 drawn uniformly over L={L} (blocks of 1024), "
-                      f"{dt:.1f} s; token-heads/s divided by H={H}"}
+                      f"{dt:.1f} s; token-heads/s divided by H={H}; fp64 BLAS on the {cores} cores of the "
+                      f"process's CPU affinity"}
 
 
 def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc):
@@ -289,11 +294,124 @@ def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
     return res
 
 
+def settle(step, torch, ms_target):
+    """Untimed steps for at least ``ms_target`` ms of wall time, so that the clocks have
+    settled under load before anything is timed. Returns the number of steps run."""
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+        n += 4
+        if (time.perf_counter() - t0) * 1e3 >= ms_target:
+            return n
+
+
+def timed_ms(hip, ev, stream, fn, steps, torch):
+    """Average ms per call of ``fn`` over ``steps`` back-to-back calls (HIP events on the
+    launch stream)."""
+    torch.cuda.synchronize()
+    hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        fn()
+    hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    return ev.elapsed(0, 1) / steps
+
+
+def device_info(torch):
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "hip_runtime": torch.version.hip, "rocm": rocm,
+            "torch": torch.__version__}
+
+
+def time_configs(args, rla, torch, workloads, hip, ev, stream):
+    """The other forward workloads of the method, each as its own line: the small fp32
+    case (launch-latency bound: microseconds per call), the dense bf16 batch (its 33.6 MB
+    fit the 256 MB Infinity Cache: timed back to back, i.e. cache-resident, and with a
+    512 MB buffer written between calls, i.e. from HBM), and the packed variable-length
+    bf16 workload. Roofline: q, k, v read and out written once over the whole call."""
+    dev = torch.device("cuda:0")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cases = (
+        ("small_fp32", workloads.c1_fp32_small, "RLA-2 causal forward fp32, B=1 H=2 L=256 d=32, one document"),
+        ("dense_bf16", workloads.c2_bf16_dense, "RLA-2 causal forward bf16, B=4 H=8 L=2048 d=64, one document per row"),
+        ("packed_bf16", workloads.c3_packed, "packed variable-length RLA-2 forward bf16, T=16384 H=16 d=128, "
+                                             "document lengths U{64..4096}"),
+    )
+    res = {}
+    kev = HipEvents(len(KERNELS) + 1)
+    for name, make, label in cases:
+        inp = make()
+        B, H, L, d = inp.q.shape
+        q, k, v, gq, gk = (t.to(dev) for t in (inp.q, inp.k, inp.v, inp.gamma_q, inp.gamma_k))
+        cu = None if inp.cu_seqlens is None else inp.cu_seqlens.to(dev)
+        out = torch.empty_like(q)
+        n_docs = 0 if cu is None else cu.numel() - 1
+        ws = torch.empty(max(rla.fwd_workspace_size(rla.make_desc(B, H, L, d, rla.F32 if q.dtype == torch.float32
+                                                                  else rla.BF16, cu, n_docs)), 1),
+                         dtype=torch.uint8, device=dev)
+
+        def run(events=None):
+            rla.fwd(q, k, v, gq, gk, cu, out=out, workspace=ws, events=events)
+
+        for _ in range(20):
+            run()
+        steps = max(args.steps, 50)
+        ms = timed_ms(hip, ev, stream, run, steps, torch)
+        # one call at a time after a 512 MB write: nothing of the inputs is left in the caches
+        ms_flushed = 0.0
+        per = [0.0] * len(KERNELS)
+        n_fl = min(steps, 30)
+        for i in range(n_fl):
+            flush.fill_(i & 255)
+            run(kev.arr)
+            ms_flushed += kev.elapsed(0, len(KERNELS))
+            for j in range(len(KERNELS)):
+                per[j] += kev.elapsed(j, j + 1)
+        ms_flushed /= n_fl
+        per = [x / n_fl for x in per]
+        es = q.element_size()
+        nbytes = B * H * L * d * es * 4
+        flops = B * H * L * (4 * d * d + 2 * 64 * d)
+        T = B * L
+        entry = {"workload": label, "dtype": "f32" if es == 4 else "bf16",
+                 "us_per_call": ms * 1e3, "tokens_per_s": T / (ms * 1e-3), "tflops": flops / (ms * 1e-3) / 1e12,
+                 "steps": steps, "us_per_call_from_hbm": ms_flushed * 1e3,
+                 "tokens_per_s_from_hbm": T / (ms_flushed * 1e-3),
+                 "kernel_us_from_hbm": dict(zip(KERNELS, [x * 1e3 for x in per]))}
+        for key, t in (("roofline", ms), ("roofline_from_hbm", ms_flushed)):
+            gbs = nbytes / (t * 1e-3) / 1e9
+            entry[key] = {"kernel": "whole forward", "bound": "latency" if name == "small_fp32" else "hbm",
+                          "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                          "algorithmic_bytes": nbytes}
+        if name == "dense_bf16":
+            entry["note"] = ("back-to-back calls read their 33.6 MB from the Infinity Cache (cache-resident); "
+                             "the _from_hbm figures write 512 MB between calls")
+        if name == "small_fp32":
+            entry["note"] = "four launches of a few microseconds each: launch latency, not bandwidth, sets the time"
+        res[name] = entry
+        del q, k, v, out, ws
+    del flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30, help="untimed steps (the clocks settle over the first tens of ms)")
+    ap.add_argument("--warmup", type=int, default=30, help="untimed steps right before the timed ones")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed forward steps for this long first (the clocks settle over the first tens of ms)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other forward workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-decode", action="store_true")
@@ -328,22 +446,14 @@ def main():
     def step(events=None):
         rla.fwd(q, k, v, gq, gk, seg_chunks=args.seg_chunks, out=out, workspace=ws, events=events)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"timing {args.steps} forward steps ...")
     ev = HipEvents(2)
     hip = ev.hip
     hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    torch.cuda.synchronize()
-    hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
-    for _ in range(args.steps):
-        step()
-    hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
-    torch.cuda.synchronize()
-    ms_step = ev.elapsed(0, 1) / args.steps
-
-    # per-kernel durations over the same number of steps (events recorded on the launch stream)
+    # the clocks first settle under this load (untimed, time-based); then the per-kernel pass
+    # (events recorded on the launch stream around each kernel), then the warm-up and the
+    # timed steps back to back: every step is the whole forward, nothing is skipped
+    settle_steps = settle(step, torch, args.settle_ms)
+    log(f"settled after {settle_steps} untimed steps; per-kernel pass ...")
     kev = HipEvents(len(KERNELS) + 1)
     per_kernel = [0.0] * len(KERNELS)
     for _ in range(args.steps):
@@ -351,7 +461,11 @@ def main():
         for i in range(len(KERNELS)):
             per_kernel[i] += kev.elapsed(i, i + 1)
     per_kernel = [x / args.steps for x in per_kernel]
-    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    log(f"timing {args.steps} forward steps ...")
+    ms_step = timed_ms(hip, ev, stream, step, args.steps, torch)
+    flags = rla.workspace_flags(ws)
 
     flops, nbytes = fwd_algorithmic(B, H, L, d)
     tokens_s = B * L / (ms_step * 1e-3)
@@ -379,11 +493,19 @@ def main():
         "mfma_frac": flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "path_hbm_gbs": nbytes / (ms_step * 1e-3) / 1e9,
         "kernel_ms": dict(zip(KERNELS, per_kernel)),
+        "kernel_sum_ms": sum(per_kernel),
+        "settle": {"ms": args.settle_ms, "steps": settle_steps},
+        "device_flags": flags,
+        "device": device_info(torch),
         "roofline": {"kernel": "chunk_out", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic("chunk_out_ws_kernel"), "algorithmic_bytes": nbytes},
         "relu_zero_fraction": {"q": zeros_q, "k": zeros_k},
     }
+
+    if not args.no_configs:
+        log("timing the other forward workloads ...")
+        result["configs"] = time_configs(args, rla, torch, workloads, hip, ev, stream)
 
     if not args.no_modes:
         result["modes"] = time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc)
@@ -406,7 +528,21 @@ def main():
         torch.cuda.synchronize()
         t_prefix = time.perf_counter() - t0
         T_prefix = int(dec.cu_prefix[-1])
-        del dec.prefix_k, dec.prefix_v
+        # the state build (segment map, chunk state, per-document sums) timed like the forward
+        sdesc = rla.make_desc(1, dec.prefix_k.shape[1], T_prefix, dec.prefix_k.shape[3], rla.BF16, cu,
+                              cu.numel() - 1)
+        sws = torch.empty(max(rla.fwd_workspace_size(sdesc), 1), dtype=torch.uint8, device=dev)
+
+        def build():
+            rla.state_from_prefix(dec.prefix_k, dec.prefix_v, dgk, cu, S=S, z=z, workspace=sws)
+
+        for _ in range(3):
+            build()
+        ms_build = timed_ms(hip, ev, stream, build, min(args.steps, 10), torch)
+        Hp, dp = dec.prefix_k.shape[1], dec.prefix_k.shape[3]
+        build_bytes = T_prefix * Hp * dp * 2 * 2 + S.numel() * 4 + z.numel() * 4
+        build_gbs = build_bytes / (ms_build * 1e-3) / 1e9
+        del dec.prefix_k, dec.prefix_v, sws
         torch.cuda.empty_cache()
         dq, dk, dv = dec.q.to(dev), dec.k.to(dev), dec.v.to(dev)
         pos = dec.prefix_lengths.to(dev)
@@ -429,7 +565,12 @@ def main():
             "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode_kernel"),
                          "algorithmic_bytes": dbytes},
-            "state_from_prefix": {"prefix_tokens": T_prefix, "wall_s_first_call": t_prefix},
+            "state_from_prefix": {"prefix_tokens": T_prefix, "wall_s_first_call": t_prefix, "ms_per_call": ms_build,
+                                  "roofline": {"kernel": "whole state build", "bound": "hbm",
+                                               "achieved": build_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                               "frac": build_gbs / HBM_PEAK_GBS,
+                                               "algorithmic_bytes": build_bytes,
+                                               "note": "prefix k, v read once (bf16), S and z written once"}},
         }
 
     if args.copy_calibration:

@@ -30,6 +30,9 @@
  *  - NaN/Inf inputs are not checked; they propagate to the outputs.
  *  - RLA2_ERR_HIP means a HIP launch failed; outputs are then undefined.
  *  - Supported head dimensions: 32, 64, 128. Supported chunk: 64.
+ *  - Sizes whose kernel grids would not fit one dispatch (more than 2^32 work-items in a
+ *    grid dimension: roughly 8 million segments, or about a million documents at d = 128)
+ *    return RLA2_ERR_BAD_SHAPE.
  */
 #ifndef RLA2_H_
 #define RLA2_H_
@@ -135,6 +138,37 @@ const char* rla2_status_string(rla2_status status);
 int32_t rla2_abi_version(void);
 
 /*
+ * Device-side checks. Every workspace starts with a small status header that the first
+ * launch of each call clears; the call's kernels raise these flags in it:
+ *  RLA2_FLAG_WAIT_EXHAUSTED  a bounded wait inside a kernel ran out (the four matrix waves of
+ *                            a workgroup meet on an LDS arrival counter in the bf16 forward
+ *                            and backward sweeps; every wait is bounded so that no wave can
+ *                            spin forever). The call's outputs are undefined.
+ *  RLA2_FLAG_PLAN_MISMATCH   rla2_bwd_chunked_saved: fwd_workspace was not last written by a
+ *                            forward whose plan matches desc (shape, segmentation, position
+ *                            offset, cu_seqlens contents, causal or bidirectional records).
+ *                            The backward then computed nothing; dq, dk, dv and the weight
+ *                            gradients are left unwritten.
+ * rla2_workspace_flags synchronises `stream`, then reads the flags of the last call that used
+ * `workspace` (workspace_bytes: its size, at least 256). RLA2_ERR_NULL_POINTER for a NULL
+ * workspace or flags, RLA2_ERR_WORKSPACE when it is misaligned or too small, RLA2_ERR_HIP
+ * when the stream or the copy fails.
+ */
+#define RLA2_FLAG_WAIT_EXHAUSTED 1u
+#define RLA2_FLAG_PLAN_MISMATCH 2u
+rla2_status rla2_workspace_flags(const void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                 uint32_t* flags);
+
+/*
+ * Test hook for the bounded waits above: the number of polls a matrix wave makes before it
+ * gives up at a meeting, for calls that start after this one (process-wide; the default is
+ * about 2 million polls, tens of milliseconds). 0 makes every meeting give up at once: the
+ * kernels still run to their normal end and raise RLA2_FLAG_WAIT_EXHAUSTED, and their
+ * outputs are garbage. Returns the previous value.
+ */
+uint32_t rla2_debug_set_wait_polls(uint32_t polls);
+
+/*
  * Workspace bytes rla2_fwd_chunked needs for `desc` (host call, no GPU work).
  * Writes *bytes; returns the same validation status the forward would.
  */
@@ -154,7 +188,8 @@ rla2_status rla2_fwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
  *  final_z      optional [N, H, d] fp32, z = sum_i k'_i; NULL = not exported.
  *  workspace    device scratch of at least rla2_fwd_workspace_size() bytes,
  *               256-byte aligned; contents on entry are ignored. After a causal
- *               forward with the Sum denominator it holds the segment table, the
+ *               forward with the Sum denominator it holds the status header (plan
+ *               stamp and flags, see rla2_workspace_flags), the segment table, the
  *               RoPE tables and every segment's prefix state, which
  *               rla2_bwd_chunked_saved reads in place of forming them again.
  * L == 0 or N == 0 is a valid no-op (final states of empty documents are 0).
@@ -249,9 +284,14 @@ rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
  * rla2_bwd_chunked without its state pass: the forward's states S_t, z_t (RLA page §4.2,
  * the states the backward of the layer reads) are taken from `fwd_workspace`, the
  * workspace of an rla2_fwd_chunked call with the same desc (causal, Sum denominator) and
- * the same k, v, gamma_k and initial state, not written since. What it holds is not
- * checked; it is only read, so one forward's workspace serves any number of backward
- * calls. Results are bitwise those of rla2_bwd_chunked.
+ * the same k, v, gamma_k and initial state, not written since. The plan stamp that forward
+ * left in the workspace header (shape, segmentation, position offset, scan mode and a
+ * checksum of the cu_seqlens contents) is compared on the device with this call's plan
+ * first: on a mismatch no backward kernel touches memory and the backward's own workspace
+ * reports RLA2_FLAG_PLAN_MISMATCH (rla2_workspace_flags); the tensors k, v, gamma_k and the
+ * initial state cannot be checked and remain the caller's contract. fwd_workspace is only
+ * read, so one forward's workspace serves any number of backward calls. Results are bitwise
+ * those of rla2_bwd_chunked.
  *  fwd_workspace        device pointer, 256-byte aligned, at least
  *                       rla2_fwd_workspace_size() bytes (fwd_workspace_bytes); it may
  *                       not overlap the outputs or `workspace` (RLA2_ERR_ALIAS).

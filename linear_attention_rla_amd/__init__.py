@@ -18,7 +18,8 @@ from typing import Optional
 import torch
 
 __all__ = ["fwd", "state_from_prefix", "decode_step", "fwd_workspace_size", "lib", "Rla2Error",
-           "FwdDesc", "LIB_PATH", "STATUS"]
+           "Rla2FlagError", "FwdDesc", "LIB_PATH", "STATUS", "workspace_flags", "set_check_flags",
+           "debug_set_wait_polls"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librla2.so")
 
@@ -27,6 +28,7 @@ STATUS = {0: "RLA2_OK", 1: "RLA2_ERR_NULL_POINTER", 2: "RLA2_ERR_BAD_SHAPE", 3: 
           8: "RLA2_ERR_BAD_SEQLENS", 9: "RLA2_ERR_MISALIGNED"}
 F32, BF16 = 0, 1
 DEN_SUM, DEN_L2 = 0, 1          # rla2_fwd_desc.denominator
+FLAG_WAIT_EXHAUSTED, FLAG_PLAN_MISMATCH = 1, 2   # rla2_workspace_flags
 L2_EPS = 1e-6                   # the original RLA's eps (RLA page §2.1)
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -35,6 +37,15 @@ class Rla2Error(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {lib().rla2_status_string(status).decode()}")
+
+
+class Rla2FlagError(RuntimeError):
+    """A device-side check of a call failed (flags of rla2_workspace_flags)."""
+    def __init__(self, flags: int, where: str):
+        self.flags = flags
+        names = [n for b, n in ((FLAG_WAIT_EXHAUSTED, "RLA2_FLAG_WAIT_EXHAUSTED"),
+                                (FLAG_PLAN_MISMATCH, "RLA2_FLAG_PLAN_MISMATCH")) if flags & b]
+        super().__init__(f"{where}: device-side check failed: {' | '.join(names) or flags}")
 
 
 class FwdDesc(ctypes.Structure):
@@ -85,6 +96,10 @@ def lib() -> ctypes.CDLL:
         L.rla2_feature_map_workspace_size.argtypes = [_DESC, _SZ]
         L.rla2_feature_map.restype = ctypes.c_int
         L.rla2_feature_map.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+        L.rla2_workspace_flags.restype = ctypes.c_int
+        L.rla2_workspace_flags.argtypes = [_P, ctypes.c_size_t, _P, ctypes.POINTER(ctypes.c_uint32)]
+        L.rla2_debug_set_wait_polls.restype = ctypes.c_uint32
+        L.rla2_debug_set_wait_polls.argtypes = [ctypes.c_uint32]
         L.rla2_decode_step.restype = ctypes.c_int
         L.rla2_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                        _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P]
@@ -107,6 +122,41 @@ def _check_dev(name: str, t: torch.Tensor, dtype=None):
 
 def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+_check_flags = False
+
+
+def set_check_flags(on: bool) -> bool:
+    """When on, every call that takes a workspace reads its device-side flags afterwards
+    (rla2_workspace_flags; this synchronises the stream) and raises Rla2FlagError if one is
+    set. Returns the previous setting."""
+    global _check_flags
+    prev, _check_flags = _check_flags, bool(on)
+    return prev
+
+
+def workspace_flags(workspace: torch.Tensor) -> int:
+    """Device-side flags of the last call that used ``workspace`` (synchronises the stream)."""
+    _check_dev("workspace", workspace, torch.uint8)
+    f = ctypes.c_uint32(0)
+    st = lib().rla2_workspace_flags(_ptr(workspace), workspace.numel(), _stream(workspace.device), ctypes.byref(f))
+    if st:
+        raise Rla2Error(st, "rla2_workspace_flags")
+    return f.value
+
+
+def debug_set_wait_polls(polls: int) -> int:
+    """Poll bound of the matrix waves' meetings for later calls (test hook); returns the
+    previous bound."""
+    return int(lib().rla2_debug_set_wait_polls(polls))
+
+
+def _after(workspace: torch.Tensor, nbytes: int, where: str):
+    if _check_flags and nbytes > 0:
+        f = workspace_flags(workspace)
+        if f:
+            raise Rla2FlagError(f, where)
 
 
 def make_desc(B, H, L, d, dtype, cu_seqlens=None, n_docs=0, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
@@ -198,6 +248,7 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
         st = lib().rla2_fwd_chunked_profiled(*args, events)
     if st:
         raise Rla2Error(st, "rla2_fwd_chunked")
+    _after(workspace, nbytes, "rla2_fwd_chunked")
     return (out, fS, fz) if return_final_state else out
 
 
@@ -226,6 +277,7 @@ def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0,
                                       _ptr(workspace), workspace.numel(), _stream(k.device))
     if st:
         raise Rla2Error(st, "rla2_state_from_prefix")
+    _after(workspace, n.value, "rla2_state_from_prefix")
     return S, z
 
 
@@ -287,6 +339,7 @@ def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunk
         st = lib().rla2_bwd_chunked_profiled(*args, events)
     if st:
         raise Rla2Error(st, "rla2_bwd_chunked")
+    _after(workspace, n.value, "rla2_bwd_chunked")
     return dq, dk, dv, dgq, dgk
 
 
@@ -320,6 +373,7 @@ def feature_map(q, k, gamma_q, gamma_k, cu_seqlens=None, *, rms_eps=1e-6, rope_b
                                 _ptr(k_out), _ptr(workspace), workspace.numel(), _stream(x.device))
     if st:
         raise Rla2Error(st, "rla2_feature_map")
+    _after(workspace, n.value, "rla2_feature_map")
     return q_out, k_out
 
 

@@ -3,6 +3,7 @@
 // any HIP call, so every error path can be exercised on a machine with no GPU.
 #include "rla2.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -15,7 +16,14 @@ namespace {
 
 using rla2::Plan;
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
+
+// Poll bound of the MMA waves' meetings inside the warp-specialised kernels (a debug hook
+// lets tests lower it; see rla2_debug_set_wait_polls).
+std::atomic<uint32_t> g_wait_polls{rla2::kDefaultWaitPolls};
+
+// HIP's dispatch takes the grid size in work-items per dimension as a 32-bit count.
+constexpr unsigned long long kMaxGridItems = 0xFFFFFFFFull;
 static_assert(RLA2_FWD_KERNELS == rla2::kNumFwdKernels, "kernel count of the profiled forward");
 static_assert(RLA2_BWD_KERNELS == rla2::kNumBwdKernels, "kernel count of the profiled backward");
 
@@ -111,10 +119,21 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   // with a position offset the first documents read a second set of chunk rows,
   // (initial_pos + 64 a) * theta, right after the plain set
   p->hi_off = p->initial_pos != 0 ? p->n_hi : 0;
+  // every launch's grid must fit the dispatch: the sweeps run up to 512 work-items per
+  // (segment, head), the state scan 256 per (document, 1024-float tile of a record), the
+  // set-up launch 1024 per 1024 RoPE entries (indexed in int32)
+  {
+    const unsigned long long tiles = ((unsigned long long)p->d * p->d + p->d + 1023) / 1024;
+    const unsigned long long rope = (unsigned long long)(rla2::kChunk + 2LL * p->n_hi) * (p->d / 2);
+    if ((unsigned long long)p->n_seg_max * 512 > kMaxGridItems ||
+        (unsigned long long)p->n_docs * tiles * 256 > kMaxGridItems || (rope / 1024 + 2) * 1024 > (unsigned long long)INT32_MAX)
+      return RLA2_ERR_BAD_SHAPE;
+  }
+  p->wait_polls = g_wait_polls.load(std::memory_order_relaxed);
 
   const size_t half = (size_t)p->d / 2;
   const size_t rec = (size_t)p->d * p->d + p->d;
-  size_t off = 0;
+  size_t off = rla2::kHdrBytes;  // the status header comes first
   p->off_tab = off;
   off = align_up(off + (size_t)p->n_seg_max * rla2::kTabInts * 4);
   p->off_docoff = off;
@@ -165,7 +184,25 @@ rla2_status finish(hipError_t e) {
 
 }  // namespace
 
+namespace rla2 {
+
+Stamp make_stamp(const Plan& p, int mode) {
+  Stamp st{};
+  const uint32_t f[] = {kStampMagic, (uint32_t)kAbiVersion, (uint32_t)p.B, (uint32_t)p.H, (uint32_t)p.L,
+                        (uint32_t)p.d, (uint32_t)p.dtype, (uint32_t)p.n_docs, (uint32_t)p.packed,
+                        (uint32_t)p.seg_len, (uint32_t)p.n_seg_max, (uint32_t)p.n_hi, (uint32_t)p.hi_off,
+                        (uint32_t)p.initial_pos, (uint32_t)mode | ((uint32_t)p.l2 << 8)};
+  static_assert(sizeof(f) / sizeof(f[0]) == kStampWords - 1, "the last stamp word is the checksum");
+  for (int i = 0; i < kStampWords - 1; ++i) st.w[i] = f[i];
+  return st;
+}
+
+}  // namespace rla2
+
 namespace {
+
+// The backward's supported modes: bf16 activations, causal, Sum denominator.
+bool bwd_supported(const Plan& p) { return p.dtype == RLA2_BF16 && !p.bidirectional && !p.l2; }
 
 // The backward entry points; `saved` (with `saved_bytes`) is the matching forward's workspace,
 // or null.
@@ -176,7 +213,7 @@ rla2_status bwd_impl(const rla2_fwd_desc* desc, const void* q, const void* k, co
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
-  if (p.dtype != RLA2_BF16 || p.bidirectional || p.l2) return RLA2_ERR_UNSUPPORTED;
+  if (!bwd_supported(p)) return RLA2_ERR_UNSUPPORTED;
   const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
   const size_t gam = (size_t)p.H * p.d * 4;
   if (act > 0 && (q == nullptr || k == nullptr || v == nullptr || dout == nullptr ||
@@ -241,6 +278,23 @@ const char* rla2_status_string(rla2_status s) {
 }
 
 int32_t rla2_abi_version(void) { return kAbiVersion; }
+
+uint32_t rla2_debug_set_wait_polls(uint32_t polls) {
+  return g_wait_polls.exchange(polls, std::memory_order_relaxed);
+}
+
+rla2_status rla2_workspace_flags(const void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                 uint32_t* flags) {
+  if (workspace == nullptr || flags == nullptr) return RLA2_ERR_NULL_POINTER;
+  if (workspace_bytes < rla2::kHdrBytes || (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
+    return RLA2_ERR_WORKSPACE;
+  uint32_t w[2] = {0u, 0u};
+  if (hipStreamSynchronize(stream) != hipSuccess) return RLA2_ERR_HIP;
+  if (hipMemcpy(w, workspace, sizeof(w), hipMemcpyDeviceToHost) != hipSuccess) return RLA2_ERR_HIP;
+  *flags = (w[rla2::HDR_WAIT] != 0u ? RLA2_FLAG_WAIT_EXHAUSTED : 0u) |
+           (w[rla2::HDR_MISMATCH] != 0u ? RLA2_FLAG_PLAN_MISMATCH : 0u);
+  return RLA2_OK;
+}
 
 rla2_status rla2_fwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
   if (bytes == nullptr) return RLA2_ERR_NULL_POINTER;
@@ -344,7 +398,7 @@ rla2_status rla2_bwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
-  if (p.dtype != RLA2_BF16 || p.bidirectional || p.l2) return RLA2_ERR_UNSUPPORTED;
+  if (!bwd_supported(p)) return RLA2_ERR_UNSUPPORTED;
   *bytes = p.bytes_bwd;
   return RLA2_OK;
 }
@@ -373,6 +427,7 @@ rla2_status rla2_bwd_chunked_saved(const rla2_fwd_desc* desc, const void* q, con
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
+  if (!bwd_supported(p)) return RLA2_ERR_UNSUPPORTED;
   if (p.bytes > 0 && fwd_workspace == nullptr) return RLA2_ERR_NULL_POINTER;
   return bwd_impl(desc, q, k, v, gamma_q, gamma_k, dout, dq, dk, dv, dgamma_q, dgamma_k, workspace,
                   workspace_bytes, p.bytes > 0 ? fwd_workspace : nullptr, fwd_workspace_bytes, stream, events);
@@ -430,7 +485,8 @@ rla2_status rla2_decode_step(int32_t N, int32_t H, int32_t d, int32_t dtype, con
   if (!supported_d(d)) return RLA2_ERR_UNSUPPORTED;
   if (dtype != RLA2_F32 && dtype != RLA2_BF16) return RLA2_ERR_UNSUPPORTED;
   if (!finite_pos(eps) || !finite_pos(rms_eps) || !finite_pos(rope_base)) return RLA2_ERR_BAD_VALUE;
-  if ((long long)N * H > INT32_MAX) return RLA2_ERR_BAD_SHAPE;
+  // one 256-thread workgroup per (sequence, head)
+  if ((unsigned long long)N * H * 256 > kMaxGridItems) return RLA2_ERR_BAD_SHAPE;
   const size_t act = (size_t)N * H * d * elem_bytes(dtype);
   if (act == 0) return RLA2_OK;
   if (q == nullptr || k == nullptr || v == nullptr || positions == nullptr || gamma_q == nullptr ||

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q,
     const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
     const float2* __restrict__ rope_hi, const float* __restrict__ den, const float* __restrict__ gd,
-    float* __restrict__ pstates, int H, int L, float rms_eps) {
+    float* __restrict__ pstates, int H, int L, float rms_eps, const uint32_t* __restrict__ hdr, TabLimits lim) {
   using G = Geo<true, D>;
   using R = Raw<true, D>;
   constexpr int BUF = kChunk * G::ROWP;
@@ -171,8 +171,9 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
   __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * G::HALF];  // RoPE rows of the chunks
 
   const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= *nseg) return;
-  const SegInfo si = read_seg(tab, seg);
+  if (!bwd_go(hdr) || seg >= *nseg) return;
+  const SegInfo si = read_seg_clamped(tab, seg, L, lim);
+  if (si.len == 0) return;  // only a corrupted table has empty segments
   if (si.pos0 == 0) return;  // a document's first segment: no earlier segment reads its total
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
     const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
     const float2* __restrict__ rope_hi, const float* __restrict__ states, uint16_t* __restrict__ dq,
     float* __restrict__ den_out, float* __restrict__ gd_out, float* __restrict__ bd_out, float* __restrict__ dg_part,
-    int H, int L, float rms_eps, float eps) {
+    int H, int L, float rms_eps, float eps, uint32_t* __restrict__ hdr, uint32_t polls, TabLimits lim) {
   using G = Geo<true, D>;
   using R = Raw<true, D>;
   constexpr int C2 = 32;                 // tokens per step
@@ -368,8 +369,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
   __shared__ unsigned sArrive;
 
   const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= *nseg) return;  // the whole workgroup leaves together
-  const SegInfo si = read_seg(tab, seg);
+  if (!bwd_go(hdr) || seg >= *nseg) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg_clamped(tab, seg, L, lim);
+  if (si.len == 0) return;  // only a corrupted table has empty segments
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ns = __builtin_amdgcn_readfirstlane((si.len + C2 - 1) / C2);  // sub-chunks
@@ -655,7 +657,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         qz = sum_rows4(qz);
       }
       meet += 4;
-      mma_wave_sync(&sArrive, meet, lane);
+      mma_wave_sync(&sArrive, meet, lane, polls, hdr);
       // ---- phase B (waves 0, 1): den, g.num, gd, B_tt, the B^T operand of query tile tt
       if (wave < 2) {
         float idot = 0.f;
@@ -690,7 +692,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         sB[tt * 64 + lane] = acc_frag<true>(x[0], x[1]);
       }
       meet += 4;
-      mma_wave_sync(&sArrive, meet, lane);
+      mma_wave_sync(&sArrive, meet, lane, polls, hdr);
       // ---- phase C: this wave's rows of dQ'^T, then the state
       if (wave < NW) {
         float* dqb = sdQ + (c & 1) * C2 * FP;
@@ -775,7 +777,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
     const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
     const float2* __restrict__ rope_hi, const float* __restrict__ pstates, const float* __restrict__ den,
     const float* __restrict__ gd, const float* __restrict__ bd, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    float* __restrict__ dg_part, int H, int L, float rms_eps) {
+    float* __restrict__ dg_part, int H, int L, float rms_eps, uint32_t* __restrict__ hdr, uint32_t polls,
+    TabLimits lim) {
   using G = Geo<true, D>;
   using R = Raw<true, D>;
   constexpr int C2 = 32;
@@ -801,8 +804,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
   __shared__ unsigned sArrive;
 
   const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= *nseg) return;  // the whole workgroup leaves together
-  const SegInfo si = read_seg(tab, seg);
+  if (!bwd_go(hdr) || seg >= *nseg) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg_clamped(tab, seg, L, lim);
+  if (si.len == 0) return;  // only a corrupted table has empty segments
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ns = __builtin_amdgcn_readfirstlane((si.len + C2 - 1) / C2);  // sub-chunks
@@ -1025,7 +1029,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           sBp[kt * 64 + lane] = acc_frag<true>(xb[0], xb[1]);
         }
         meet += 4;
-        mma_wave_sync(&sArrive, meet, lane);
+        mma_wave_sync(&sArrive, meet, lane, polls, hdr);
         // ---- phase B: this wave's rows of dK'^T and dV^T, then the states
         if (wave < NW) {
           float* dkb = sdK + pb * C2 * FP;
@@ -1137,11 +1141,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
 // bwd_dgamma: RMSNorm-weight gradients, the per-segment partials summed in segment order
 // (deterministic): part[(seg H + h) 2D + j] (q: j < D, k: D + j).
 
-__global__ void bwd_dgamma_kernel(const float* __restrict__ part, const int32_t* __restrict__ nseg, int H, int D,
-                                  float* __restrict__ dgq, float* __restrict__ dgk) {
+__global__ void bwd_dgamma_kernel(const float* __restrict__ part, const int32_t* __restrict__ nseg, int n_seg_max,
+                                  int H, int D, float* __restrict__ dgq, float* __restrict__ dgk,
+                                  const uint32_t* __restrict__ hdr) {
   const int h = blockIdx.x, j = threadIdx.x;
-  if (j >= 2 * D) return;
-  const int n = *nseg;
+  if (j >= 2 * D || !bwd_go(hdr)) return;
+  const int n = min(*nseg, n_seg_max);
   float acc = 0.f;
   for (int s = 0; s < n; ++s) acc += part[((size_t)s * H + h) * 2 * D + j];
   if (j < D) {
@@ -1163,8 +1168,14 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
     e = launch_fwd_states(p, a, s, ev);
     if (e != hipSuccess) return e;
   } else {
-    for (int i = 0; i < 3; ++i) mark(i);
+    // the forward's plan stamp against this plan: the backward kernels run only on a match
+    mark(0);
+    e = launch_saved_check(p, b.saved, a.ws, a.cu, SCAN_PREFIX, s);
+    if (e != hipSuccess) return e;
+    for (int i = 1; i < 3; ++i) mark(i);
   }
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(a.ws);
+  const TabLimits lim{p.packed ? 1 : p.B, p.seg_len, p.n_hi + p.hi_off};
   const char* fw = b.saved != nullptr ? b.saved : a.ws;
   if (p.n_seg_max == 0) {
     for (int i = 3; i <= kNumBwdKernels; ++i) mark(i);
@@ -1187,20 +1198,22 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   const dim3 grid(p.n_seg_max, p.H);
   mark(3);
   hipLaunchKernelGGL((bwd_dq_ws_kernel<D>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
-                     states, static_cast<uint16_t*>(b.dq), den, gd, bd, dgp, p.H, p.L, a.rms_eps, a.eps);
+                     states, static_cast<uint16_t*>(b.dq), den, gd, bd, dgp, p.H, p.L, a.rms_eps, a.eps, hdr,
+                     p.wait_polls, lim);
   mark(4);
   hipLaunchKernelGGL((bwd_pstate_kernel<D>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
-                     pstates, p.H, p.L, a.rms_eps);
+                     pstates, p.H, p.L, a.rms_eps, hdr, lim);
   mark(5);
-  e = launch_scan_suffix(p, fw, pstates, s);
+  e = launch_scan_suffix(p, fw, pstates, hdr, s);
   if (e != hipSuccess) return e;
   mark(6);
   hipLaunchKernelGGL((bwd_dkv_ws_kernel<D>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
                      pstates, den, gd, bd, static_cast<uint16_t*>(b.dk), static_cast<uint16_t*>(b.dv), dgp, p.H, p.L,
-                     a.rms_eps);
+                     a.rms_eps, hdr, p.wait_polls, lim);
   mark(7);
   if (b.dgamma_q != nullptr || b.dgamma_k != nullptr)
-    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3(p.H), dim3(2 * D), 0, s, dgp, nseg, p.H, D, b.dgamma_q, b.dgamma_k);
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3(p.H), dim3(2 * D), 0, s, dgp, nseg, p.n_seg_max, p.H, D, b.dgamma_q,
+                       b.dgamma_k, static_cast<const uint32_t*>(hdr));
   mark(8);
   return hipGetLastError();
 }

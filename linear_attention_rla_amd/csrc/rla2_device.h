@@ -511,15 +511,52 @@ __device__ __forceinline__ void store_cols(typename Elem<BF>::St* dst, const Raw
 // Arrival counter of the four MMA waves of a warp-specialised kernel: each wave adds 1 with
 // release semantics (its LDS writes land first), then polls with acquire semantics until the
 // count reaches `target` (all four have arrived at this meeting: the count only grows, so the
-// n-th meeting waits for 4 n). The poll is bounded (about 0.1 s) so that a wave can never spin
-// forever.
-__device__ __forceinline__ void mma_wave_sync(unsigned* cnt, unsigned target, int lane) {
+// n-th meeting waits for 4 n). The poll is bounded (`polls` rounds, tens of milliseconds at
+// the default) so that a wave can never spin forever; a wave that gives up records it in the
+// workspace header (HDR_WAIT, a plain vector store from lane 0) and goes on, so the kernel
+// still ends normally and the host can tell that the call's outputs are not valid.
+__device__ __forceinline__ void mma_wave_sync(unsigned* cnt, unsigned target, int lane, uint32_t polls,
+                                              uint32_t* hdr) {
   if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-  for (int spin = 0; spin < (1 << 21); ++spin) {
-    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) break;
+  for (uint32_t spin = 0; spin < polls; ++spin) {
+    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
     __builtin_amdgcn_s_sleep(1);
   }
+  if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+  if (lane == 0) hdr[HDR_WAIT] = 1u;
 }
+
+// Checksum of cu_seqlens[0 .. n_docs] (0 without cu_seqlens) for the plan stamp: a wrapping
+// sum of one mixed word per entry, so every thread order gives the same value. Called by all
+// threads of a 1024-thread workgroup; every thread gets the result.
+__device__ __forceinline__ uint32_t cu_mix(uint32_t j, uint32_t x) {
+  uint32_t h = x * 0x9E3779B1u + j * 0x85EBCA77u + 0x165667B1u;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  return h;
+}
+
+__device__ __forceinline__ uint32_t cu_checksum_block(const int32_t* __restrict__ cu, int n_docs) {
+  __shared__ uint32_t red[1024];
+  const int tid = threadIdx.x;
+  uint32_t acc = 0u;
+  if (cu != nullptr)
+    for (int j = tid; j <= n_docs; j += 1024) acc += cu_mix((uint32_t)j, (uint32_t)cu[j]);
+  red[tid] = acc;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (tid < off) red[tid] += red[tid + off];
+    __syncthreads();
+  }
+  const uint32_t total = red[0];
+  __syncthreads();
+  return total;
+}
+
+// The backward kernels' entry check: run only when the set-up launch of the call cleared them
+// to (HDR_GO of the backward's own workspace).
+__device__ __forceinline__ bool bwd_go(const uint32_t* hdr) { return hdr[HDR_GO] != 0u; }
 
 struct SegInfo {
   int row, start, len, pos0;
@@ -529,6 +566,27 @@ struct SegInfo {
 __device__ __forceinline__ SegInfo read_seg(const int32_t* tab, int seg) {
   const int4 a = *reinterpret_cast<const int4*>(tab + (size_t)seg * kTabInts);
   return SegInfo{a.x, a.y, a.z, a.w, tab[(size_t)seg * kTabInts + TAB_HIROW]};
+}
+
+// read_seg for a table that another call wrote (the backward reading a forward's workspace):
+// every field is clamped into the plan's ranges (row < rows, start + len <= L, len <= seg_len,
+// the segment's RoPE rows within the n_rope rows of the table), so even a corrupted table can
+// only give wrong numbers, never an access outside the tensors or the tables.
+struct TabLimits {
+  int rows;     // batch rows of the tensors (1 when packed)
+  int seg_len;  // tokens per segment at most
+  int n_rope;   // rows of the coarse RoPE table
+};
+
+__device__ __forceinline__ SegInfo read_seg_clamped(const int32_t* tab, int seg, int L, TabLimits lim) {
+  SegInfo si = read_seg(tab, seg);
+  si.row = min(max(si.row, 0), lim.rows - 1);
+  si.start = min(max(si.start, 0), L);
+  si.len = min(max(si.len, 0), min(lim.seg_len, L - si.start));
+  si.pos0 = max(si.pos0, 0);
+  const int nch = (si.len + kChunk - 1) / kChunk;
+  si.hirow = min(max(si.hirow, 0), max(lim.n_rope - nch, 0));
+  return si;
 }
 
 template <bool BF, int D, int ONLY = -1>  // ONLY >= 0: that token of the pair alone

@@ -14,6 +14,27 @@ constexpr int kMaxSegChunks = 64;   // chunks per segment at most (the state ker
 constexpr int kTabInts = 8;         // int32 fields per segment-table entry
 constexpr size_t kAlign = 256;
 
+// Every workspace starts with a status header of kHdrBytes (uint32 words):
+//   HDR_WAIT      1 after a bounded in-kernel wait of the call ran out (outputs undefined)
+//   HDR_MISMATCH  1 when a backward was handed a forward workspace whose plan stamp does not
+//                 match its own plan (nothing was computed)
+//   HDR_GO        1 when the backward kernels may run (set by the set-up launch)
+//   HDR_STAMP..   the plan stamp the set-up launch writes: kStampWords words, the last one a
+//                 checksum of cu_seqlens
+// The set-up launch of every call clears the flag words first.
+constexpr size_t kHdrBytes = 256;
+enum HdrWord { HDR_WAIT = 0, HDR_MISMATCH = 1, HDR_GO = 2, HDR_STAMP = 16 };
+constexpr int kStampWords = 16;
+constexpr uint32_t kStampMagic = 0x32414C52u;  // "RLA2"
+constexpr uint32_t kDefaultWaitPolls = 1u << 21;
+
+// Plan stamp: the fields a backward needs to match between its plan and the forward that
+// wrote a workspace it reads (word kStampWords - 1 is the cu_seqlens checksum, formed on the
+// device).
+struct Stamp {
+  uint32_t w[kStampWords];
+};
+
 // Segment-table entry fields (int32 each).
 // TAB_LAST: 1 for the last segment of its document.
 enum TabField { TAB_ROW = 0, TAB_START = 1, TAB_LEN = 2, TAB_POS0 = 3, TAB_DOC = 4, TAB_HIROW = 5, TAB_LAST = 6 };
@@ -39,7 +60,18 @@ struct Plan {
   // gradients of q and k
   size_t off_pstates, off_den, off_gd, off_bd, off_dgpart;
   size_t bytes_bwd;    // total backward workspace bytes
+  uint32_t wait_polls; // poll bound of the MMA waves' meetings (rla2_debug_set_wait_polls)
 };
+
+// What the state scan leaves in the segment records: SCAN_NONE segment totals (the state
+// build), SCAN_PREFIX each segment's exclusive prefix (the causal forward), SCAN_TOTAL the
+// document total in every record (the bidirectional forward), SCAN_SUFFIX the sum over the
+// later segments of the document (the backward's reverse states). SCAN_TABLES: a workspace
+// with the tables only (the feature map).
+enum ScanMode { SCAN_NONE = 0, SCAN_PREFIX = 1, SCAN_TOTAL = 2, SCAN_SUFFIX = 3, SCAN_TABLES = 4 };
+
+// The stamp of plan p for a workspace whose records hold scan mode `mode`.
+Stamp make_stamp(const Plan& p, int mode);
 
 struct FwdArgs {
   const int32_t* cu;   // device or null
@@ -70,7 +102,13 @@ struct BwdArgs {
 // forward's state pass; `ev`, optional, gets events 0..2 before the three launches); the
 // reverse scan of a second record set.
 hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
-hipError_t launch_scan_suffix(const Plan& p, const char* ws, float* states, hipStream_t s);
+// go_hdr: null, or the header whose HDR_GO must be set for the scan to run.
+hipError_t launch_scan_suffix(const Plan& p, const char* ws, float* states, const uint32_t* go_hdr,
+                              hipStream_t s);
+// The saved backward's set-up launch: compares the stamp in fwd_ws's header with
+// make_stamp(p, mode) and the checksum of cu, and writes ws's header (flags, HDR_GO).
+hipError_t launch_saved_check(const Plan& p, const char* fwd_ws, char* ws, const int32_t* cu, int mode,
+                              hipStream_t s);
 // the whole chunked backward (rla2_backward.hip); `ev` (optional) gets kNumBwdKernels + 1
 // events recorded around the kernels
 constexpr int kNumBwdKernels = 8;

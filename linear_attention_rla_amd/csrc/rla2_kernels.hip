@@ -123,14 +123,50 @@ __device__ __forceinline__ void rope_entry(int idx, float2* __restrict__ lo, flo
   else hi[(row - kChunk) * half + j] = v;
 }
 
-// prep: block 0 builds the segment table, blocks 1.. the RoPE tables (one launch for both).
+// prep: block 0 builds the segment table and the workspace's status header (flags cleared,
+// the backward's go word set, the plan stamp with the cu_seqlens checksum), blocks 1.. the
+// RoPE tables (one launch for all).
 __global__ __launch_bounds__(1024) void prep_kernel(const int32_t* __restrict__ cu, int n_docs, int L, int seg_len,
                                                     int n_seg_max, int32_t* __restrict__ tab,
                                                     int32_t* __restrict__ docoff, int32_t* __restrict__ nseg,
                                                     float2* __restrict__ lo, float2* __restrict__ hi, int half, int D,
-                                                    int n_hi, int hi_off, int pos_off, float base) {
-  if (blockIdx.x == 0) seg_map_block(cu, n_docs, L, seg_len, n_seg_max, hi_off, tab, docoff, nseg);
-  else rope_entry((blockIdx.x - 1) * 1024 + threadIdx.x, lo, hi, half, D, n_hi, hi_off, pos_off, base);
+                                                    int n_hi, int hi_off, int pos_off, float base,
+                                                    uint32_t* __restrict__ hdr, Stamp stamp) {
+  if (blockIdx.x == 0) {
+    seg_map_block(cu, n_docs, L, seg_len, n_seg_max, hi_off, tab, docoff, nseg);
+    const uint32_t sum = cu_checksum_block(cu, n_docs);
+    if (threadIdx.x < kStampWords)
+      hdr[HDR_STAMP + threadIdx.x] = threadIdx.x == kStampWords - 1 ? sum : stamp.w[threadIdx.x];
+    if (threadIdx.x == 0) {
+      hdr[HDR_WAIT] = 0u;
+      hdr[HDR_MISMATCH] = 0u;
+      hdr[HDR_GO] = 1u;
+    }
+  } else {
+    rope_entry((blockIdx.x - 1) * 1024 + threadIdx.x, lo, hi, half, D, n_hi, hi_off, pos_off, base);
+  }
+}
+
+// The saved backward's set-up: compare the plan stamp in the forward's workspace header with
+// this call's plan (and the checksum of this call's cu_seqlens), then clear the backward
+// workspace's flags and let its kernels run (HDR_GO) only on a match.
+__global__ __launch_bounds__(1024) void saved_check_kernel(const uint32_t* __restrict__ fwd_hdr,
+                                                           uint32_t* __restrict__ hdr, Stamp stamp,
+                                                           const int32_t* __restrict__ cu, int n_docs) {
+  const uint32_t sum = cu_checksum_block(cu, n_docs);
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  if (threadIdx.x < kStampWords) {
+    const uint32_t want = threadIdx.x == kStampWords - 1 ? sum : stamp.w[threadIdx.x];
+    if (fwd_hdr[HDR_STAMP + threadIdx.x] != want) atomicOr(&bad, 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    hdr[HDR_WAIT] = 0u;
+    hdr[HDR_MISMATCH] = bad ? 1u : 0u;
+    hdr[HDR_GO] = bad ? 0u : 1u;
+  }
 }
 
 // ----------------------------------------------------------------------------------------
@@ -466,13 +502,13 @@ __global__ __launch_bounds__(512, 1) void chunk_state_l2_kernel(
 // last to the first and replaces each total by the sum over the later segments of its
 // document (the reverse states of the backward; no initial state, no final export).
 
-enum ScanMode { SCAN_NONE = 0, SCAN_PREFIX = 1, SCAN_TOTAL = 2, SCAN_SUFFIX = 3 };
-
 __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ states, const int32_t* __restrict__ docoff,
                                                          int H, int D, int n_tiles, int mode,
                                                          float* __restrict__ final_S, float* __restrict__ final_z,
                                                          const float* __restrict__ init_S,
-                                                         const float* __restrict__ init_z, int init_all) {
+                                                         const float* __restrict__ init_z, int init_all,
+                                                         const uint32_t* __restrict__ go_hdr) {
+  if (go_hdr != nullptr && !bwd_go(go_hdr)) return;  // the backward's reverse scan after a failed check
   const int doc = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles, h = blockIdx.y;
   const int R4 = (D * D + D) / 4;
   const int e4 = tile * 256 + threadIdx.x;
@@ -968,7 +1004,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const float* __restrict__ gamma_q, const float* __restrict__ gamma_k, const int32_t* __restrict__ tab,
     const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
     const float* __restrict__ states, const float* __restrict__ astates, uint16_t* __restrict__ out, int H, int L,
-    float rms_eps, float eps) {
+    float rms_eps, float eps, uint32_t* __restrict__ hdr, uint32_t polls) {
   using G = Geo<true, D>;
   using St = uint16_t;
   using EL = Elem<true>;
@@ -1209,7 +1245,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
         }
       }
     }
-    mma_wave_sync(&sArrive, 4u * (unsigned)(st + 1), lane);
+    mma_wave_sync(&sArrive, 4u * (unsigned)(st + 1), lane, polls, hdr);
     if (work && wave < G::NW) {  // ---- output, then the state update
       Frag<true> Vf[G::CT][2];
 #pragma unroll
@@ -1709,7 +1745,7 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
   const int rope_entries = (kChunk + p.n_hi + p.hi_off) * half;
   hipLaunchKernelGGL(prep_kernel, dim3(1 + (rope_entries + 1023) / 1024), dim3(1024), 0, s, a.cu, p.n_docs, p.L,
                      p.seg_len, p.n_seg_max, tab, docoff, nseg, rlo, rhi, half, D, p.n_hi, p.hi_off, p.initial_pos,
-                     a.rope_base);
+                     a.rope_base, reinterpret_cast<uint32_t*>(a.ws), make_stamp(p, mode));
   mark(1);
   // the L2 forward also needs the records of A = sum k'k'^T
   const bool l2 = p.l2 && a.out != nullptr;
@@ -1737,12 +1773,13 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
   if (want_final || (mode != SCAN_NONE && p.n_seg_max > 0)) {
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
-                       n_tiles, mode, a.final_S, a.final_z, a.init_S, a.init_z, p.packed ? 0 : 1);
+                       n_tiles, mode, a.final_S, a.final_z, a.init_S, a.init_z, p.packed ? 0 : 1,
+                       static_cast<const uint32_t*>(nullptr));
   }
   if (l2 && mode == SCAN_PREFIX && p.n_seg_max > 0) {  // exclusive prefixes of A as well
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, astates, docoff, p.H, D,
                        n_tiles, (int)SCAN_PREFIX, (float*)nullptr, (float*)nullptr, (const float*)nullptr,
-                       (const float*)nullptr, 0);
+                       (const float*)nullptr, 0, static_cast<const uint32_t*>(nullptr));
   }
   return hipGetLastError();
 }
@@ -1772,7 +1809,7 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
       hipLaunchKernelGGL((chunk_out_ws_kernel<D, true>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
                          static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
                          a.gk, tab, nseg, rlo, rhi, states, astates, static_cast<St*>(a.out), p.H, p.L, a.rms_eps,
-                         a.eps);
+                         a.eps, reinterpret_cast<uint32_t*>(a.ws), p.wait_polls);
     } else {
       hipLaunchKernelGGL((chunk_out_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                          static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
@@ -1784,7 +1821,8 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
       hipLaunchKernelGGL((chunk_out_ws_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
                          static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
                          a.gk, tab, nseg, rlo, rhi, states, static_cast<const float*>(nullptr),
-                         static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+                         static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps, reinterpret_cast<uint32_t*>(a.ws),
+                         p.wait_polls);
     } else {
       hipLaunchKernelGGL((chunk_out_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                          static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
@@ -1808,7 +1846,7 @@ hipError_t run_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void* k
   const int rope_entries = (kChunk + p.n_hi + p.hi_off) * half;
   hipLaunchKernelGGL(prep_kernel, dim3(1 + (rope_entries + 1023) / 1024), dim3(1024), 0, s, a.cu, p.n_docs, p.L,
                      p.seg_len, p.n_seg_max, tab, docoff, nseg, rlo, rhi, half, D, p.n_hi, p.hi_off, p.initial_pos,
-                     a.rope_base);
+                     a.rope_base, reinterpret_cast<uint32_t*>(a.ws), make_stamp(p, SCAN_TABLES));
   if (p.n_seg_max > 0) {
     hipLaunchKernelGGL((feature_map_kernel<BF, D>), dim3(p.n_seg_max, p.H, 2), dim3(NT), 0, s,
                        static_cast<const St*>(a.q), static_cast<const St*>(a.k), a.gq, a.gk, tab, nseg, rlo, rhi,
@@ -1852,13 +1890,21 @@ hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hip
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_suffix(const Plan& p, const char* ws, float* states, hipStream_t s) {
+hipError_t launch_scan_suffix(const Plan& p, const char* ws, float* states, const uint32_t* go_hdr,
+                              hipStream_t s) {
   const int32_t* docoff = reinterpret_cast<const int32_t*>(ws + p.off_docoff);
   const int D = p.d;
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
   hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
                      n_tiles, (int)SCAN_SUFFIX, (float*)nullptr, (float*)nullptr, (const float*)nullptr,
-                     (const float*)nullptr, 0);
+                     (const float*)nullptr, 0, go_hdr);
+  return hipGetLastError();
+}
+
+hipError_t launch_saved_check(const Plan& p, const char* fwd_ws, char* ws, const int32_t* cu, int mode,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(saved_check_kernel, dim3(1), dim3(1024), 0, s, reinterpret_cast<const uint32_t*>(fwd_ws),
+                     reinterpret_cast<uint32_t*>(ws), make_stamp(p, mode), cu, p.n_docs);
   return hipGetLastError();
 }
 

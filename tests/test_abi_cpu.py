@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = rla.lib()
-    assert L.rla2_abi_version() == 3
+    assert L.rla2_abi_version() == 4
     for code, name in rla.STATUS.items():
         assert L.rla2_status_string(code).decode().startswith(name)
     assert L.rla2_status_string(99).decode() == "RLA2_ERR_UNKNOWN"
@@ -179,6 +179,8 @@ def test_decode_error_paths():
     assert call(z=A + 64 * MB + 4096) == ALIAS               # z inside S
     assert call(S=A + 8) == MISAL
     assert call(N=0, q=None, k=None, v=None, pos=None, S=None, z=None, out=None) == OK
+    # one 256-thread workgroup per (sequence, head): 2^20 x 32 x 256 work-items do not fit a grid
+    assert call(N=1 << 20, H=32) == SHAPE
 
 
 def test_validate_env_flag_rejects_unknown_values():
@@ -256,3 +258,53 @@ def test_backward_error_paths():
     assert call(dv=A + 328 * MB) == ALIAS                 # dv over dq
     assert call(dgk=A + 192 * MB) == ALIAS                # dgamma_k over gamma_q
     assert call(dout=A + 1024 * MB) == ALIAS              # an input inside the workspace
+
+
+def test_grid_sizes_that_do_not_fit_a_dispatch():
+    # The state scan runs 256 work-items per (document, 1024-float tile of a record): at d = 128
+    # a record has 17 tiles, so a million (here empty) documents exceed 2^32 work-items, while
+    # at d = 32 (2 tiles) they fit. Ten million documents exceed the sweeps' 512 work-items per
+    # segment at any d. Each is refused on the host, before any launch.
+    big = dict(B=1, L=0, cu_seqlens=A)
+    assert ws_size(desc(d=128, n_docs=1 << 20, **big))[0] == SHAPE
+    assert ws_size(desc(d=32, n_docs=1 << 20, **big))[0] == OK
+    assert ws_size(desc(d=32, n_docs=10_000_000, **big))[0] == SHAPE
+    assert fwd_call(desc(d=128, n_docs=1 << 20, **big)) == SHAPE
+
+
+def saved_call(d=None, fws=A + 1536 * MB, fws_bytes=1 << 30, q=A, k=A + 64 * MB, v=A + 128 * MB,
+               gq=A + 192 * MB, gk=A + 193 * MB, dout=A + 264 * MB, dq=A + 328 * MB, dk=A + 392 * MB,
+               dv=A + 456 * MB, dgq=A + 194 * MB, dgk=A + 195 * MB, ws=A + 1024 * MB, ws_bytes=1 << 29):
+    d = d or desc()
+    return rla.lib().rla2_bwd_chunked_saved(ctypes.byref(d), q, k, v, gq, gk, dout, dq, dk, dv, dgq, dgk, ws,
+                                            ws_bytes, fws, fws_bytes, None, None)
+
+
+def test_backward_from_forward_workspace_error_paths():
+    st, fwd_bytes = ws_size(desc())
+    assert st == OK
+    # the mode check comes first, as in rla2_bwd_chunked
+    assert saved_call(d=desc(dtype=rla.F32), fws=None) == UNSUP
+    assert saved_call(d=desc(bidirectional=1), fws=None) == UNSUP
+    assert saved_call(fws=None) == NULLP
+    assert saved_call(fws=A + 1536 * MB + 64) == WS                # not 256-byte aligned
+    assert saved_call(fws_bytes=fwd_bytes - 256) == WS             # smaller than the forward's workspace
+    assert saved_call(fws=A + 328 * MB) == ALIAS                   # dq over the forward's workspace
+    assert saved_call(fws=A + 1024 * MB + 4096) == ALIAS           # inside the backward's own workspace
+    assert saved_call(dout=None) == NULLP
+    assert saved_call(ws=None) == WS
+    # nothing to do: no forward workspace needed, no launch
+    assert saved_call(d=desc(B=0), fws=None, q=None, k=None, v=None, dout=None, dq=None, dk=None, dv=None,
+                      ws=None, ws_bytes=0) == OK
+
+
+def test_workspace_flags_and_wait_polls_hook():
+    L = rla.lib()
+    f = ctypes.c_uint32(7)
+    assert L.rla2_workspace_flags(None, 1 << 20, None, ctypes.byref(f)) == NULLP
+    assert L.rla2_workspace_flags(A, 1 << 20, None, None) == NULLP
+    assert L.rla2_workspace_flags(A + 64, 1 << 20, None, ctypes.byref(f)) == WS
+    assert L.rla2_workspace_flags(A, 100, None, ctypes.byref(f)) == WS
+    prev = L.rla2_debug_set_wait_polls(5)
+    assert L.rla2_debug_set_wait_polls(prev) == 5
+    assert prev > 1000

@@ -89,11 +89,13 @@ def test_backward_deterministic_and_dgamma_optional():
     inp = workloads.fwd_inputs(1, 2, 333, 128, torch.bfloat16, seed=61)
     dout = _dout(inp.q.shape, seed=62)
     a = _run(inp, dout)
-    b = _run(inp, dout)
+    for _ in range(50):  # bitwise determinism, 50 runs (segment-ordered sums, no atomics)
+        b = _run(inp, dout)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
     c = _run(inp, dout, want_dgamma=False)
-    for x, y, z in zip(a[:3], b[:3], c[:3]):
-        assert torch.equal(x, y) and torch.equal(x, z)
-    assert torch.equal(a[3], b[3]) and torch.equal(a[4], b[4])
+    for x, z in zip(a[:3], c[:3]):
+        assert torch.equal(x, z)
     assert c[3] is None and c[4] is None
 
 

@@ -60,10 +60,9 @@ def test_l2_packed_equals_unpacked_and_deterministic():
     inp = workloads.fwd_inputs(1, 2, 400, 128, torch.bfloat16, seed=71, lengths=[130, 200, 70])
     q, k, v, gq, gk, cu = _gpu(inp)
     a = rla.fwd(q, k, v, gq, gk, cu, l2_denominator=True)
-    b = rla.fwd(q, k, v, gq, gk, cu, l2_denominator=True)
     alone = rla.fwd(*(x[:, :, 130:330].contiguous() for x in (q, k, v)), gq, gk, l2_denominator=True)
-    torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    for _ in range(50):  # bitwise determinism, 50 runs
+        assert torch.equal(rla.fwd(q, k, v, gq, gk, cu, l2_denominator=True), a)
     assert torch.equal(a[:, :, 130:330], alone)
 
 

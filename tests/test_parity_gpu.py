@@ -179,7 +179,7 @@ def test_segment_length_invariance_and_determinism():
     for o in outs:
         assert row_rel_err(o, ref) <= TOL_BF16
     base = rla.fwd(q, k, v, gq, gk, seg_chunks=1)
-    for _ in range(20):  # bitwise determinism (no atomics anywhere on the path)
+    for _ in range(50):  # bitwise determinism, 50 runs (no atomics anywhere on the path)
         assert torch.equal(rla.fwd(q, k, v, gq, gk, seg_chunks=1), base)
 
 
