@@ -29,7 +29,7 @@
  *    q, k and v may overlap each other (they are only read).
  *  - NaN/Inf inputs are not checked; they propagate to the outputs.
  *  - RLA2_ERR_HIP means a HIP launch failed; outputs are then undefined.
- *  - Supported head dimensions: 32, 64, 128. Supported chunk: 64.
+ *  - Supported head dimensions: 32, 64, 128. Supported chunks: 16, 32, 64, 128.
  *  - Sizes whose kernel grids would not fit one dispatch (more than 2^32 work-items in a
  *    grid dimension: roughly 8 million segments, or about a million documents at d = 128)
  *    return RLA2_ERR_BAD_SHAPE.
@@ -65,10 +65,19 @@ typedef enum rla2_dtype { RLA2_F32 = 0, RLA2_BF16 = 1 } rla2_dtype;
  *  B, H, L, d   logical [B, H, L, d] of q, k, v (and out). With cu_seqlens the
  *               input is packed: B must be 1 and L is the total token count T.
  *  dtype        element type of q, k, v, out (rla2_dtype).
- *  chunk        tokens per chunk of the chunked evaluation; must be 64.
- *  seg_chunks   chunks per sequential segment of the sweep, 0..64 (a tuning knob
- *               that only changes fp32 summation order); 0 selects it
- *               automatically. Larger values return RLA2_ERR_BAD_VALUE.
+ *  chunk        C, tokens per chunk of the chunked evaluation: 16, 32, 64 or 128
+ *               (RLA2_ERR_UNSUPPORTED otherwise). Every query reads the state at the
+ *               start of its chunk and the keys of its chunk up to itself directly
+ *               (the associativity of RLA page §1 applied per chunk); C changes only
+ *               the rounding, not the result. 64 runs the tuned bf16 kernels; other
+ *               sizes, and fp32, run a generic kernel. The backward always works in
+ *               32-token steps of its own, whatever C.
+ *  seg_chunks   chunks per sequential segment of the sweep (a tuning knob that only
+ *               changes fp32 summation order); 0 selects it automatically. A segment
+ *               of seg_chunks * chunk tokens must be a multiple of 64 tokens and at
+ *               most 4096 (RLA2_ERR_BAD_VALUE otherwise): 0..64 for C = 64, multiples
+ *               of 4 up to 256 for C = 16, of 2 up to 128 for C = 32, 0..32 for
+ *               C = 128.
  *  eps          denominator offset, RLA page §3 uses 1e-4. Finite, > 0.
  *  rms_eps      RMSNorm epsilon (inside the square root). Finite, > 0.
  *  rope_base    RoPE base (10000 on the RLA-2 workloads). Finite, > 0.

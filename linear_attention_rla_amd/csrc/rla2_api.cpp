@@ -68,8 +68,11 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   if (d->cu_seqlens != nullptr && (d->B != 1 || d->n_docs < 0)) return RLA2_ERR_BAD_SHAPE;
   if (!supported_d(d->d)) return RLA2_ERR_UNSUPPORTED;
   if (d->dtype != RLA2_F32 && d->dtype != RLA2_BF16) return RLA2_ERR_UNSUPPORTED;
-  if (d->chunk != rla2::kChunk) return RLA2_ERR_UNSUPPORTED;
-  if (d->seg_chunks < 0 || d->seg_chunks > rla2::kMaxSegChunks) return RLA2_ERR_BAD_VALUE;
+  if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128) return RLA2_ERR_UNSUPPORTED;
+  // a segment is a whole number of chunks and of 64-token blocks, at most 64 blocks long
+  const long long seg_req = (long long)d->seg_chunks * d->chunk;
+  if (d->seg_chunks < 0 || seg_req > (long long)rla2::kMaxSegChunks * rla2::kChunk || seg_req % rla2::kChunk != 0)
+    return RLA2_ERR_BAD_VALUE;
   if (!finite_pos(d->eps) || !finite_pos(d->rms_eps) || !finite_pos(d->rope_base))
     return RLA2_ERR_BAD_VALUE;
   if (validate_mode() < 0) return RLA2_ERR_BAD_VALUE;
@@ -83,6 +86,7 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   if (d->H > 65535) return RLA2_ERR_BAD_SHAPE;  // heads are the grid's y dimension
 
   p->B = d->B;
+  p->chunk = d->chunk;
   p->H = d->H;
   p->L = d->L;
   p->d = d->d;
@@ -99,12 +103,13 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   // 256-CU part (fewer segments mean less fp32 state traffic through the
   // inter-segment scan and fewer pipeline fills; measured on the long-context
   // forward: 64-chunk segments 651 us, 32-chunk 693 us, 16-chunk 754 us).
+  const int seg_min = d->chunk > rla2::kChunk ? d->chunk : rla2::kChunk;
   int seg = 0;
   if (d->seg_chunks > 0) {
-    seg = d->seg_chunks * rla2::kChunk;
+    seg = (int)seg_req;
   } else {
-    seg = rla2::kChunk;
-    for (int cand = rla2::kMaxSegChunks * rla2::kChunk; cand >= rla2::kChunk; cand /= 2) {
+    seg = seg_min;
+    for (int cand = rla2::kMaxSegChunks * rla2::kChunk; cand >= seg_min; cand /= 2) {
       long long wg = (long long)rows * ((L + cand - 1) / cand) * (p->H > 0 ? p->H : 1);
       if (wg >= 512) { seg = cand; break; }
     }

@@ -8,7 +8,9 @@
 
 namespace rla2 {
 
-constexpr int kChunk = 64;          // tokens per chunk (one MFMA-tiled block)
+constexpr int kChunk = 64;          // tokens per block: the LDS tile of the chunk kernels, the unit of
+                                    // the segment table and of the coarse RoPE table (the chunk of
+                                    // the output sweep, Plan::chunk, may be 16, 32, 64 or 128)
 constexpr int kMaxSegChunks = 64;   // chunks per segment at most (the state kernel keeps a
                                     // segment's RoPE rows in LDS)
 constexpr int kTabInts = 8;         // int32 fields per segment-table entry
@@ -42,11 +44,12 @@ enum TabField { TAB_ROW = 0, TAB_START = 1, TAB_LEN = 2, TAB_POS0 = 3, TAB_DOC =
 // Everything a launch needs about the problem and the workspace carve-up.
 struct Plan {
   int B, H, L, d, dtype;
+  int chunk;           // tokens per chunk of the output sweep (16, 32, 64 or 128)
   bool bidirectional;  // every token reads its whole document's state
   int initial_pos;     // first position of the first document of each row
   int n_docs;          // documents (B when not packed)
   bool packed;         // cu_seqlens given
-  int seg_len;         // tokens per segment, multiple of kChunk
+  int seg_len;         // tokens per segment, multiple of kChunk and of chunk
   int n_seg_max;       // upper bound on segments (grid size of the sweep kernels)
   int n_hi;            // rows of the coarse RoPE table (positions / 64)
   int hi_off;          // 0, or n_hi when the first documents use the offset rows

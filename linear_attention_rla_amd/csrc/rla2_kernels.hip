@@ -592,30 +592,46 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
 }
 
 // ----------------------------------------------------------------------------------------
-// chunk_out: per (segment, head), sweep the chunks with the running state in accumulators.
-//
-// Per chunk, three phases separated by workgroup barriers:
-//   map   all 256 lanes: q', k' of two tokens each (shared rotation angles), q'.z per token;
-//         Q', K', V rows into LDS (bf16: the K'^T and V operands are read back with the
-//         transposing LDS read; fp32: K'^T and V^T are also stored transposed); then the next
-//         chunk's loads are issued
-//   score wave w: the causal score tile of query tile w (16 queries x keys <= 16w+15), rounded
-//         to the element type and stored in LDS as the B operand of A V; its row sums give
-//         1/(rowsum + q'.z + eps)
-//   out   wave w < NW (value columns [w*DVW, (w+1)*DVW)): O^T = S^T Q'^T + V^T A^T, so each
-//         lane holds 4 consecutive output columns of one row and writes them directly; then
-//         S += K'^T V in the accumulators; wave 0 also forms the column sums of K' against a
-//         ones operand and adds them to z.
-// Registers stay under 256 and LDS under 80 KB, so two workgroups share a CU.
+// chunk_out: per (segment, head), sweep the chunks of C tokens (C in {16, 32, 64, 128}) with the
+// running state in accumulators: every query reads the state at the start of its chunk and
+// the keys of its chunk up to itself directly (RLA page §3 formula, split by the associativity
+// of §1). LDS holds one 64-token block of Q', K', V at a time:
+//   C <= 64  one pass per block; the block holds 64 / C chunks, and inside it the state
+//            advances chunk by chunk in the output phase (S += K'_j^T V_j over the tokens of
+//            chunk j only); q'.z of a later chunk adds the fp32 scores of the block's earlier
+//            chunks (their keys are part of that chunk's z) to q'.z of the block start
+//   C = 128  a chunk is two blocks: pass (0, 0) gives the first block's queries from its own
+//            keys; passes (1, 0) and (1, 1) give the second block's queries from the keys of
+//            both blocks (the first block's k, v are loaded and mapped again), and advance the
+//            state with both blocks' keys
+// Per pass, three phases separated by workgroup barriers:
+//   map   all 256 lanes: q' (first pass of a query block, with q'.z per token) and k' of two
+//         tokens each, Q', K', V rows into LDS (bf16: the K'^T and V operands are read back
+//         with the transposing LDS read; fp32: K'^T and V^T are also stored transposed); then
+//         the next pass's loads are issued
+//   score wave w: the score tile of query tile w against the pass's keys, masked to the keys of
+//         the query's chunk up to itself, rounded to the element type and stored in LDS as
+//         the B operand of A V; row sums accumulate over the query block's passes, the last
+//         one gives 1/(rowsum + q'.z + eps)
+//   out   wave w < NW (value columns [w*DVW, (w+1)*DVW)): O^T = S^T Q'^T (first pass of the
+//         query block) + V^T A^T accumulated in registers over the passes, so each lane holds
+//         4 consecutive output columns of one row, written after the last pass; S += K'^T V in
+//         the accumulators; wave 0 also forms the column sums of K' against a ones operand and
+//         adds them to z.
+// Below d = 128 registers stay under 256 and LDS under 80 KB (bf16), so two workgroups share
+// a CU; at d = 128 one workgroup per CU holds the state in registers.
 //
 // L2 (the original RLA's denominator, sqrt(sum_i s_ti^2) + eps): the waves also carry the
 // second state A = sum k'k'^T (same column split), the score phase keeps the sum of the
-// squared weights, and a phase between score and out forms q'_t^T A_prev q'_t as
-// A_prev^T Q'^T (the shape of the S^T Q'^T term) dotted with q'_t, summed over the waves in
-// LDS (one more barrier); A advances with K' as the value operand. One workgroup per CU.
+// squared weights (and, for the earlier chunks of a block, of the squared fp32 scores), and
+// a phase between score and out (first pass of a query block) forms q'_t^T A q'_t as
+// A^T Q'^T (the shape of the S^T Q'^T term) dotted with q'_t, summed over the waves in LDS
+// (one more barrier); A advances with K' as the value operand. One workgroup per CU.
+//
+// The bf16 path with C = 64 runs chunk_out_ws_kernel below instead.
 
-template <bool BF, int D, bool L2 = false>
-__global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
+template <bool BF, int D, bool L2, int C>
+__global__ __launch_bounds__(NT, (L2 || D == 128) ? 1 : 2) void chunk_out_kernel(
     const typename Elem<BF>::St* __restrict__ q, const typename Elem<BF>::St* __restrict__ k,
     const typename Elem<BF>::St* __restrict__ v, const float* __restrict__ gamma_q,
     const float* __restrict__ gamma_k, const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg,
@@ -625,6 +641,11 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
   using G = Geo<BF, D>;
   using St = typename G::St;
   using EL = Elem<BF>;
+  static_assert(C == 16 || C == 32 || C == 64 || C == 128, "chunk");
+  constexpr int NB = C > kChunk ? C / kChunk : 1;  // 64-token blocks per chunk
+  constexpr int TPC = (C < kChunk ? C : kChunk) / 16;  // 16-row tiles per chunk inside a block
+  constexpr int NSUB = 4 / TPC;                    // chunks per block
+  constexpr int NP = NB * (NB + 1) / 2;            // passes per chunk
   constexpr int TD = BF ? 1 : D;  // rows of the transposed copies (fp32 only)
   __shared__ __attribute__((aligned(16))) St sQ[kChunk * G::ROWP];
   __shared__ __attribute__((aligned(16))) St sK[kChunk * G::ROWP];
@@ -635,7 +656,7 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
   __shared__ float sZ[D];
   __shared__ float sQz[kChunk];
   __shared__ float sInv[kChunk];
-  __shared__ float sQuad[L2 ? 4 * kChunk : 1];  // L2: each state wave's part of q'^T A_prev q'
+  __shared__ float sQuad[L2 ? 4 * kChunk : 1];  // L2: each state wave's part of q'^T A q'
   __shared__ float sRs2[L2 ? kChunk : 1];       // L2: sum of the squared weights
 
   const int seg = blockIdx.x, h = blockIdx.y;
@@ -662,6 +683,19 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
     if constexpr (BF) return lds_frag_tr(sV, G::ROWP, 32 * kb2, n0, lane);
     else return lds_frag<BF>(sVT, G::COLP, n0 + c16, kb2, g);
   };
+  // Only the tokens [16 half, 16 half + 16) of a 32-token k-block: the slot order puts tokens
+  // 4g + i in slots 0..3 and 16 + 4g + i in slots 4..7 (rla2_device.h), so the other half's
+  // slots are cleared (a chunk of 16 tokens inside a k-block).
+  auto keep_half = [&](Frag<BF> f, int half) -> Frag<BF> {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((j >> 2) != half) {
+        if constexpr (BF) f.v[j] = static_cast<__bf16>(0.0f);
+        else f.v[j] = 0.0f;
+      }
+    }
+    return f;
+  };
 
   // running state S (this wave's value columns) and z, from the exclusive prefix
   const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
@@ -675,7 +709,7 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
         S[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, rt, ct, lane));
   }
   if (tid < D) sZ[tid] = rec[D * D + tid];
-  floatx4 Ak[L2 ? G::RT : 1][G::CT];  // L2: A_prev, this wave's columns
+  floatx4 Ak[L2 ? G::RT : 1][G::CT];  // L2: A, this wave's columns
   if constexpr (L2) {
     const float* arec = astates + ((size_t)seg * H + h) * (size_t)(D * D + D);
     const int wv = wave < G::NW ? wave : 0;
@@ -686,55 +720,79 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
         Ak[rt][ct] = *reinterpret_cast<const floatx4*>(arec + rec_frag<BF, D>(wv, rt, ct, lane));
   }
 
+  // passes: chunk ch = p / NP; r = p % NP gives (query block qi, key block ki), ki <= qi
+  const int nblk = (si.len + kChunk - 1) / kChunk;
+  const int npass = (si.len + C - 1) / C * NP;
+  auto pass_blocks = [&](int p, int& qblk, int& kblk, int& qi, int& ki) {
+    const int ch = p / NP, r = p % NP;
+    qi = r == 0 ? 0 : (r <= 2 ? 1 : 2);  // NB <= 2
+    ki = r - qi * (qi + 1) / 2;
+    qblk = ch * NB + qi;
+    kblk = ch * NB + ki;
+  };
   Raw<BF, D> rq, rk, rv;
-  {
-    const int nv = min(kChunk, si.len);
-    load_raw<BF, D>(rq, qb, t0, m, nv);
-    load_raw<BF, D>(rk, kb, t0, m, nv);
-    load_raw<BF, D>(rv, vb, t0, m, nv);
-  }
-  for (int c0 = 0; c0 < si.len; c0 += kChunk) {
-    const int nv = min(kChunk, si.len - c0);
-    __syncthreads();  // B1: the previous chunk's LDS reads are done; its z update is visible
+  auto issue = [&](int p) {  // raw q (first pass of its query block), k, v of pass p
+    int qblk, kblk, qi, ki;
+    pass_blocks(p, qblk, kblk, qi, ki);
+    if (p >= npass || qblk >= nblk) return;
+    if (ki == 0) load_raw<BF, D>(rq, qb + (size_t)qblk * kChunk * D, t0, m, si.len - qblk * kChunk);
+    load_raw<BF, D>(rk, kb + (size_t)kblk * kChunk * D, t0, m, si.len - kblk * kChunk);
+    load_raw<BF, D>(rv, vb + (size_t)kblk * kChunk * D, t0, m, si.len - kblk * kChunk);
+  };
+  issue(0);
+
+  floatx4 O[NB > 1 ? G::CT : 1][4];  // C = 128: O^T tiles of the query block, summed over its passes
+  float rs_acc = 0.f, rs2_acc = 0.f, zrs = 0.f, zrs2 = 0.f;  // score waves: row sums of their tile
+
+  for (int p = 0; p < npass; ++p) {
+    int qblk, kblk, qi, ki;
+    pass_blocks(p, qblk, kblk, qi, ki);
+    if (qblk >= nblk) continue;  // the last chunk of the segment ends before this block
+    const bool first = ki == 0, last = ki == qi, upd = qi == NB - 1;
+    const int nvq = min(kChunk, si.len - qblk * kChunk);  // valid query rows of the block
+    __syncthreads();  // B1: the previous pass's LDS reads are done; its z update is visible
 
     // ---- map
     {
-      const float2* hirow = rope_hi + (size_t)(si.hirow + c0 / kChunk) * G::HALF;
-      // The RMSNorm weights and the in-chunk RoPE table are the same for every chunk; hiding
+      const float2* hq = rope_hi + (size_t)(si.hirow + qblk) * G::HALF;
+      const float2* hk = rope_hi + (size_t)(si.hirow + kblk) * G::HALF;
+      // The RMSNorm weights and the in-chunk RoPE table are the same for every block; hiding
       // their addresses from the optimiser keeps it from holding ~64 loaded values in
-      // registers across the whole sweep (they are re-read from cache each chunk instead).
+      // registers across the whole sweep (they are re-read from cache each pass instead).
       const float* gqi = gq;
       const float* gki = gk;
       const float2* loi = rope_lo;
       asm volatile("" : "+s"(gqi), "+s"(gki), "+s"(loi));
       Raw<BF, D> oq, ok;
-      feature_map_qk<BF, D>(rq, rk, oq, ok, gqi, gki, loi, hirow, t0, m, rms_eps);
-      store_rows<BF, D>(sQ, oq, t0, m);
+      if (first && qblk == kblk) {
+        feature_map_qk<BF, D>(rq, rk, oq, ok, gqi, gki, loi, hq, t0, m, rms_eps);
+      } else {
+        if (first) feature_map_pair<BF, D>(rq, oq, gqi, loi, hq, t0, m, rms_eps);
+        feature_map_pair<BF, D>(rk, ok, gki, loi, hk, t0, m, rms_eps);
+      }
+      if (first) {
+        store_rows<BF, D>(sQ, oq, t0, m);
+        // q'_t . z of the two tokens (z at the start of the block), from the rounded q'
+#pragma unroll
+        for (int tok = 0; tok < 2; ++tok) {
+          float pz = 0.f;
+#pragma unroll
+          for (int e = 0; e < G::E; ++e) {
+            const int j = m * G::E + e;
+            pz += oq.get(tok, 0, e) * sZ[j];
+            pz += oq.get(tok, 1, e) * sZ[j + G::HALF];
+          }
+          pz = sum8(pz);
+          if (m == 0) sQz[t0 + tok] = pz;
+        }
+      }
       store_rows<BF, D>(sK, ok, t0, m);
       if constexpr (!BF) store_cols<BF, D>(sKT, ok, t0, m);
-      // q'_t . z_prev of the two tokens, from the rounded q' the MFMA uses
-#pragma unroll
-      for (int tok = 0; tok < 2; ++tok) {
-        float p = 0.f;
-#pragma unroll
-        for (int e = 0; e < G::E; ++e) {
-          const int j = m * G::E + e;
-          p += oq.get(tok, 0, e) * sZ[j];
-          p += oq.get(tok, 1, e) * sZ[j + G::HALF];
-        }
-        p = sum8(p);
-        if (m == 0) sQz[t0 + tok] = p;
-      }
     }
     if constexpr (BF) store_rows<BF, D>(sV, rv, t0, m);
     else store_cols<BF, D>(sVT, rv, t0, m);
-    if (c0 + kChunk < si.len) {
-      const int nn = min(kChunk, si.len - c0 - kChunk);
-      load_raw<BF, D>(rq, qb + (size_t)(c0 + kChunk) * D, t0, m, nn);
-      load_raw<BF, D>(rk, kb + (size_t)(c0 + kChunk) * D, t0, m, nn);
-      load_raw<BF, D>(rv, vb + (size_t)(c0 + kChunk) * D, t0, m, nn);
-    }
-    __syncthreads();  // B2: chunk in LDS
+    issue(p + 1);
+    __syncthreads();  // B2: the pass's operands in LDS
 
     // ---- score: wave w owns query tile w
     {
@@ -742,65 +800,84 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
       Frag<BF> Qf[G::KB];
 #pragma unroll
       for (int kb2 = 0; kb2 < G::KB; ++kb2) Qf[kb2] = lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g);
-      // A^T tiles (rows = keys of tile kt, cols = queries of tile tt), causal: kt <= tt
+      if (first) rs_acc = rs2_acc = zrs = zrs2 = 0.f;
+      // A^T tiles (rows = keys of tile kt, cols = queries of tile tt)
       floatx4 At[4];
-      float rs = 0.f, rs2 = 0.f;
+      float rs = 0.f, rs2 = 0.f, zs = 0.f, zs2 = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (kt <= tt) {
+        // keys of an earlier block of the chunk: all weighted; same block: up to the query,
+        // weighted inside the query's chunk, through z (fp32 scores) in an earlier chunk
+        const bool earlier_blk = ki < qi;
+        const bool same_chunk = kt / TPC == tt / TPC;
+        if (earlier_blk || kt <= tt) {
 #pragma unroll
           for (int kb2 = 0; kb2 < G::KB; ++kb2)
             At[kt] = mma(lds_frag<BF>(sK, G::ROWP, kt * 16 + c16, kb2, g), Qf[kb2], At[kt]);
+          if (earlier_blk || same_chunk) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float a = At[kt][i];
-            if (kt == tt && 4 * g + i > c16) a = 0.f;   // key after the query token
-            a = EL::to_f(EL::from_f(a));                  // the weight the MFMA will use
-            At[kt][i] = a;
-            rs += a;
-            if constexpr (L2) rs2 = __builtin_fmaf(a, a, rs2);
+            for (int i = 0; i < 4; ++i) {
+              float a = At[kt][i];
+              if (!earlier_blk && kt == tt && 4 * g + i > c16) a = 0.f;  // key after the query token
+              a = EL::to_f(EL::from_f(a));                              // the weight the MFMA will use
+              At[kt][i] = a;
+              rs += a;
+              if constexpr (L2) rs2 = __builtin_fmaf(a, a, rs2);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              zs += At[kt][i];
+              if constexpr (L2) zs2 = __builtin_fmaf(At[kt][i], At[kt][i], zs2);
+            }
+            At[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
           }
         }
       }
-      rs = sum_rows4(rs);  // every lane with c16 == t holds the row sum of query 16*tt + t
-      sA[(tt * 2) * 64 + lane] = acc_frag<BF>(At[0], At[1]);
-      if (tt >= 2) sA[(tt * 2 + 1) * 64 + lane] = acc_frag<BF>(At[2], At[3]);
+      rs_acc += sum_rows4(rs);  // every lane with c16 == t holds the row sum of query 16*tt + t
+      if constexpr (TPC < 4) zrs += sum_rows4(zs);
       if constexpr (L2) {
-        rs2 = sum_rows4(rs2);
-        if (g == 0) sRs2[tt * 16 + c16] = rs2;
-      } else {
-        if (g == 0) sInv[tt * 16 + c16] = 1.0f / (rs + sQz[tt * 16 + c16] + eps);
+        rs2_acc += sum_rows4(rs2);
+        if constexpr (TPC < 4) zrs2 += sum_rows4(zs2);
+      }
+      sA[(tt * 2) * 64 + lane] = acc_frag<BF>(At[0], At[1]);
+      sA[(tt * 2 + 1) * 64 + lane] = acc_frag<BF>(At[2], At[3]);
+      if (last && g == 0) {
+        if constexpr (L2) sRs2[tt * 16 + c16] = rs2_acc + zrs2;
+        else sInv[tt * 16 + c16] = 1.0f / (rs_acc + zrs + sQz[tt * 16 + c16] + eps);
       }
     }
     __syncthreads();  // B3: score tiles and row reciprocals in LDS
 
-    if constexpr (L2) {  // ---- q'_t^T A_prev q'_t: this wave's columns a, all 64 queries
-      if (wave < G::NW) {
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (L2) {  // ---- q'_t^T A q'_t: this wave's columns a, all 64 queries
+      if (first) {
+        if (wave < G::NW) {
+          float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) {
-          Frag<BF> Aa[G::KB];  // A_prev^T (= A_prev) rounded to the element type as the A operand
+          for (int ct = 0; ct < G::CT; ++ct) {
+            Frag<BF> Aa[G::KB];  // A^T (= A) rounded to the element type as the A operand
 #pragma unroll
-          for (int kb2 = 0; kb2 < G::KB; ++kb2) Aa[kb2] = acc_frag<BF>(Ak[2 * kb2][ct], Ak[2 * kb2 + 1][ct]);
-          const int col = wave * G::DVW + ct * 16 + 4 * g;
+            for (int kb2 = 0; kb2 < G::KB; ++kb2) Aa[kb2] = acc_frag<BF>(Ak[2 * kb2][ct], Ak[2 * kb2 + 1][ct]);
+            const int col = wave * G::DVW + ct * 16 + 4 * g;
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              floatx4 y = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int kb2 = 0; kb2 < G::KB; ++kb2) y = mma(Aa[kb2], lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g), y);
+              const St* qrow = sQ + (tt * 16 + c16) * G::ROWP + col;  // q'_t at dims col .. col + 3
+#pragma unroll
+              for (int i = 0; i < 4; ++i) part[tt] = __builtin_fmaf(EL::to_f(qrow[i]), y[i], part[tt]);
+            }
+          }
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            floatx4 y = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb2 = 0; kb2 < G::KB; ++kb2) y = mma(Aa[kb2], lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g), y);
-            const St* qrow = sQ + (tt * 16 + c16) * G::ROWP + col;  // q'_t at dims col .. col + 3
-#pragma unroll
-            for (int i = 0; i < 4; ++i) part[tt] = __builtin_fmaf(EL::to_f(qrow[i]), y[i], part[tt]);
+            const float pp = sum_rows4(part[tt]);
+            if (g == 0) sQuad[wave * kChunk + tt * 16 + c16] = pp;
           }
         }
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const float p = sum_rows4(part[tt]);
-          if (g == 0) sQuad[wave * kChunk + tt * 16 + c16] = p;
-        }
+        __syncthreads();  // B4: every wave's part of the quadratic form in LDS
       }
-      __syncthreads();  // B4: every wave's part of the quadratic form in LDS
     }
     auto row_scale = [&](int t) -> float {  // 1 / den of query row t
       if constexpr (L2) {
@@ -821,55 +898,94 @@ __global__ __launch_bounds__(NT, L2 ? 1 : 2) void chunk_out_kernel(
         Vf[ct][0] = v_frag(wave * G::DVW + ct * 16, 0);
         Vf[ct][1] = v_frag(wave * G::DVW + ct * 16, 1);
       }
+      // S += K'^T V over the key tokens [16 * 4 j / NSUB, ...) of chunk j of the block (NSUB
+      // chunks per block), or over the whole block
+      auto advance = [&](int j) {
+        constexpr int NKB = NSUB == 1 ? 2 : 1;  // 32-token k-blocks of the update
 #pragma unroll
-      for (int ct = 0; ct < G::CT; ++ct) {
-        Frag<BF> Sa[G::KB];  // S^T rounded to the element type as the A operand
+        for (int x = 0; x < NKB; ++x) {
+          const int kb2 = NSUB == 1 ? x : (NSUB == 2 ? j : j / 2);
 #pragma unroll
-        for (int kb2 = 0; kb2 < G::KB; ++kb2) Sa[kb2] = acc_frag<BF>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
-        const int col = wave * G::DVW + ct * 16 + 4 * g;
-#pragma unroll 1
-        for (int tt = 0; tt < 4; ++tt) {
-          floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int rt = 0; rt < G::RT; ++rt) {
+            const Frag<BF> a = kt_frag(rt, kb2);
 #pragma unroll
-          for (int kb2 = 0; kb2 < G::KB; ++kb2) o = mma(Sa[kb2], lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g), o);
-          o = mma(Vf[ct][0], sA[(tt * 2) * 64 + lane], o);
-          if (tt >= 2) o = mma(Vf[ct][1], sA[(tt * 2 + 1) * 64 + lane], o);
-          const int t = tt * 16 + c16;  // this lane's query row; columns col .. col + 3
-          const float r = row_scale(t);
-          if (t < nv) {
-            St* dst = ob + (size_t)(c0 + t) * D + col;
-            if constexpr (BF) {
-              const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[0] * r, o[1] * r}, bf16x2));
-              const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[2] * r, o[3] * r}, bf16x2));
-              *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-            } else {
-              *reinterpret_cast<float4*>(dst) = make_float4(o[0] * r, o[1] * r, o[2] * r, o[3] * r);
+            for (int ct = 0; ct < G::CT; ++ct) {
+              const Frag<BF> b = NSUB == 4 ? keep_half(Vf[ct][kb2], j & 1) : Vf[ct][kb2];
+              S[rt][ct] = mma(a, b, S[rt][ct]);
+            }
+            if constexpr (L2) {  // A += K'^T K' (K' columns of this wave as the value operand)
+#pragma unroll
+              for (int ct = 0; ct < G::CT; ++ct) {
+                const Frag<BF> kc = kt_frag(wave * G::CT + ct, kb2);
+                Ak[rt][ct] = mma(a, NSUB == 4 ? keep_half(kc, j & 1) : kc, Ak[rt][ct]);
+              }
             }
           }
         }
-      }
-      // S += K'^T V; wave 0 also adds the column sums of K' to z (read again after B1)
+      };
+      // this lane's 4 output columns col .. col + 3 of query row 16 tt + c16, scaled by 1/den
+      auto store_tile = [&](floatx4 o, int tt, int ct) {
+        const int col = wave * G::DVW + ct * 16 + 4 * g;
+        const int t = tt * 16 + c16;
+        const float r = row_scale(t);
+        if (t < nvq) {
+          St* dst = ob + ((size_t)qblk * kChunk + t) * D + col;
+          if constexpr (BF) {
+            const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[0] * r, o[1] * r}, bf16x2));
+            const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[2] * r, o[3] * r}, bf16x2));
+            *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+          } else {
+            *reinterpret_cast<float4*>(dst) = make_float4(o[0] * r, o[1] * r, o[2] * r, o[3] * r);
+          }
+        }
+      };
 #pragma unroll
-      for (int rt = 0; rt < G::RT; ++rt) {
-        const Frag<BF> a0 = kt_frag(rt, 0);
-        const Frag<BF> a1 = kt_frag(rt, 1);
+      for (int j = 0; j < NSUB; ++j) {
 #pragma unroll
         for (int ct = 0; ct < G::CT; ++ct) {
-          S[rt][ct] = mma(a0, Vf[ct][0], S[rt][ct]);
-          S[rt][ct] = mma(a1, Vf[ct][1], S[rt][ct]);
-        }
-        if (wave == 0) {
-          const Frag<BF> ones = ones_frag<BF>();
-          floatx4 zc = mma(a0, ones, floatx4{0.f, 0.f, 0.f, 0.f});
-          zc = mma(a1, ones, zc);  // every column holds the sums of rows 16 rt + 4g + i
-          if (c16 < 4) sZ[rt * 16 + 4 * g + c16] += zc[c16];
-        }
-        if constexpr (L2) {  // A += K'^T K' (K' columns of this wave as the value operand)
+          Frag<BF> Sa[G::KB];  // S^T rounded to the element type as the A operand
+          if (first) {
 #pragma unroll
-          for (int ct = 0; ct < G::CT; ++ct) {
-            Ak[rt][ct] = mma(a0, kt_frag(wave * G::CT + ct, 0), Ak[rt][ct]);
-            Ak[rt][ct] = mma(a1, kt_frag(wave * G::CT + ct, 1), Ak[rt][ct]);
+            for (int kb2 = 0; kb2 < G::KB; ++kb2) Sa[kb2] = acc_frag<BF>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
           }
+#pragma unroll 1
+          for (int x = 0; x < TPC; ++x) {
+            const int tt = j * TPC + x;
+            floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (NB > 1) {
+              if (!first) o = O[ct][tt];
+            }
+            if (first) {
+#pragma unroll
+              for (int kb2 = 0; kb2 < G::KB; ++kb2) o = mma(Sa[kb2], lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g), o);
+            }
+            o = mma(Vf[ct][0], sA[(tt * 2) * 64 + lane], o);
+            o = mma(Vf[ct][1], sA[(tt * 2 + 1) * 64 + lane], o);
+            if constexpr (NB == 1) store_tile(o, tt, ct);  // one pass per query block
+            else O[ct][tt] = o;
+          }
+        }
+        if constexpr (NSUB > 1) advance(j);  // the next chunk of the block reads the advanced state
+      }
+      if constexpr (NSUB == 1) {
+        if (upd) advance(0);
+      }
+      if constexpr (NB > 1) {
+        if (last) {
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) store_tile(O[ct][tt], tt, ct);
+        }
+      }
+      // z += the column sums of the pass's K' (read again after B1), with the state update
+      if (wave == 0 && (NSUB > 1 || upd)) {
+        const Frag<BF> ones = ones_frag<BF>();
+#pragma unroll
+        for (int rt = 0; rt < G::RT; ++rt) {
+          floatx4 zc = mma(kt_frag(rt, 0), ones, floatx4{0.f, 0.f, 0.f, 0.f});
+          zc = mma(kt_frag(rt, 1), ones, zc);  // every column holds the sums of rows 16 rt + 4g + i
+          if (c16 < 4) sZ[rt * 16 + 4 * g + c16] += zc[c16];
         }
       }
     }
@@ -1803,31 +1919,26 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   if (fwd && p.n_seg_max > 0 && p.bidirectional) {
     hipLaunchKernelGGL((readout_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s, static_cast<const St*>(a.q),
                        a.gq, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
-  } else if (fwd && p.n_seg_max > 0 && p.l2) {
-    const float* astates = reinterpret_cast<const float*>(a.ws + p.off_astates);
-    if constexpr (BF) {
-      hipLaunchKernelGGL((chunk_out_ws_kernel<D, true>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
-                         static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
-                         a.gk, tab, nseg, rlo, rhi, states, astates, static_cast<St*>(a.out), p.H, p.L, a.rms_eps,
-                         a.eps, reinterpret_cast<uint32_t*>(a.ws), p.wait_polls);
-    } else {
-      hipLaunchKernelGGL((chunk_out_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
-                         static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
-                         a.gk, tab, nseg, rlo, rhi, states, astates, static_cast<St*>(a.out), p.H, p.L, a.rms_eps,
-                         a.eps);
-    }
   } else if (fwd && p.n_seg_max > 0) {
-    if constexpr (BF) {
-      hipLaunchKernelGGL((chunk_out_ws_kernel<D>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
-                         static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
-                         a.gk, tab, nseg, rlo, rhi, states, static_cast<const float*>(nullptr),
-                         static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps, reinterpret_cast<uint32_t*>(a.ws),
-                         p.wait_polls);
+    const float* astates = p.l2 ? reinterpret_cast<const float*>(a.ws + p.off_astates) : nullptr;
+    if (BF && p.chunk == kChunk) {
+      auto kern = p.l2 ? chunk_out_ws_kernel<D, true> : chunk_out_ws_kernel<D, false>;
+      hipLaunchKernelGGL(kern, dim3(p.n_seg_max, p.H), dim3(512), 0, s, static_cast<const uint16_t*>(a.q),
+                         static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.gq, a.gk, tab, nseg,
+                         rlo, rhi, states, astates, static_cast<uint16_t*>(a.out), p.H, p.L, a.rms_eps, a.eps,
+                         reinterpret_cast<uint32_t*>(a.ws), p.wait_polls);
     } else {
-      hipLaunchKernelGGL((chunk_out_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
-                         static_cast<const St*>(a.q), static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq,
-                         a.gk, tab, nseg, rlo, rhi, states, static_cast<const float*>(nullptr),
-                         static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+      auto pick = [&](auto c_const) {
+        constexpr int CC = decltype(c_const)::value;
+        return p.l2 ? chunk_out_kernel<BF, D, true, CC> : chunk_out_kernel<BF, D, false, CC>;
+      };
+      auto kern = p.chunk == 16 ? pick(std::integral_constant<int, 16>{})
+                : p.chunk == 32 ? pick(std::integral_constant<int, 32>{})
+                : p.chunk == 128 ? pick(std::integral_constant<int, 128>{})
+                                 : pick(std::integral_constant<int, 64>{});
+      hipLaunchKernelGGL(kern, dim3(p.n_seg_max, p.H), dim3(NT), 0, s, static_cast<const St*>(a.q),
+                         static_cast<const St*>(a.k), static_cast<const St*>(a.v), a.gq, a.gk, tab, nseg, rlo, rhi,
+                         states, astates, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
     }
   }
   mark(4);

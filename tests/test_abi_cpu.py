@@ -66,7 +66,12 @@ def ws_size(d):
 
 
 @pytest.mark.parametrize("kw,expect", [
-    (dict(d=48), UNSUP), (dict(d=256), UNSUP), (dict(dtype=2), UNSUP), (dict(chunk=32), UNSUP),
+    (dict(d=48), UNSUP), (dict(d=256), UNSUP), (dict(dtype=2), UNSUP), (dict(chunk=48), UNSUP),
+    (dict(chunk=8), UNSUP), (dict(chunk=256), UNSUP), (dict(chunk=0), UNSUP),
+    (dict(chunk=16, seg_chunks=3), VALUE), (dict(chunk=16, seg_chunks=260), VALUE),
+    (dict(chunk=32, seg_chunks=1), VALUE), (dict(chunk=128, seg_chunks=33), VALUE),
+    (dict(chunk=16, seg_chunks=4), OK), (dict(chunk=16, seg_chunks=256), OK), (dict(chunk=32, seg_chunks=2), OK),
+    (dict(chunk=128, seg_chunks=1), OK), (dict(chunk=128, seg_chunks=32), OK), (dict(chunk=128), OK),
     (dict(B=-1), SHAPE), (dict(L=-5), SHAPE), (dict(H=-1), SHAPE),
     (dict(eps=0.0), VALUE), (dict(eps=float("nan")), VALUE), (dict(rms_eps=-1.0), VALUE),
     (dict(rope_base=float("inf")), VALUE), (dict(seg_chunks=-1), VALUE), (dict(seg_chunks=65), VALUE),
