@@ -226,6 +226,24 @@ rla2_status rla2_fwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
                                       size_t workspace_bytes, hipStream_t stream,
                                       hipEvent_t* events);
 
+/*
+ * rla2_fwd_chunked for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same forward with no
+ * workspace argument. Its workspace is a file-scope device array of
+ * RLA2_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU the library runs on holds until the
+ * process ends; the call allocates nothing (its first call on a device only looks up the
+ * array's address there). Problems whose rla2_fwd_workspace_size exceeds that size return
+ * RLA2_ERR_WORKSPACE before anything is enqueued (the long-context forward of 32 heads x
+ * 65536 tokens at d = 128 needs about 35 MB). Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (on other streams or threads) race and must be serialised
+ * by the caller. The call's device-side flags (rla2_workspace_flags) stay in that array and
+ * cannot be read back. Arguments, outputs and other errors as for rla2_fwd_chunked.
+ */
+#define RLA2_NOALLOC_SCRATCH_BYTES (64u << 20)
+rla2_status rla2_fwd_chunked_noalloc(const rla2_fwd_desc* desc, const void* q, const void* k,
+                                     const void* v, const float* gamma_q, const float* gamma_k,
+                                     void* out, float* final_S, float* final_z, hipStream_t stream);
+
 /* Workspace bytes rla2_state_from_prefix needs for `desc`. */
 rla2_status rla2_state_from_prefix_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
 

@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.rla2_fwd_chunked.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.rla2_fwd_chunked_profiled.restype = ctypes.c_int
         L.rla2_fwd_chunked_profiled.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
+        L.rla2_fwd_chunked_noalloc.restype = ctypes.c_int
+        L.rla2_fwd_chunked_noalloc.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, _P, _P, _P]
         L.rla2_state_from_prefix.restype = ctypes.c_int
         L.rla2_state_from_prefix.argtypes = [_DESC, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.rla2_bwd_workspace_size.restype = ctypes.c_int
@@ -206,7 +208,8 @@ def fwd_workspace_size(desc: FwdDesc) -> int:
 
 def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=None, rms_eps=1e-6,
         rope_base=10000.0, return_final_state=False, out=None, workspace=None, events=None,
-        bidirectional=False, initial_S=None, initial_z=None, initial_pos=0, l2_denominator=False):
+        bidirectional=False, initial_S=None, initial_z=None, initial_pos=0, l2_denominator=False,
+        no_alloc=False):
     """Chunked RLA-2 forward (causal, or bidirectional). Returns ``out`` or
     ``(out, final_S, final_z)``.
 
@@ -217,7 +220,9 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
     ``initial_S [H, d, d]``, ``initial_z [H, d]`` (fp32, optional, together) start the
     first document of each row, whose positions begin at ``initial_pos``.
     ``events``: optional ctypes array of RLA2_FWD_KERNELS + 1 hipEvent_t handles; when
-    given, rla2_fwd_chunked_profiled records them around each kernel."""
+    given, rla2_fwd_chunked_profiled records them around each kernel. ``no_alloc``: call
+    rla2_fwd_chunked_noalloc (the library's own per-GPU scratch array as the workspace; no
+    ``workspace`` or ``events``); pass ``out`` (and nothing needs allocating here)."""
     for n_, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(n_, t, q.dtype)
     _check_dev("gamma_q", gamma_q, torch.float32)
@@ -237,6 +242,14 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
     if return_final_state:
         fS = torch.empty(N, desc.H, desc.d, desc.d, dtype=torch.float32, device=q.device)
         fz = torch.empty(N, desc.H, desc.d, dtype=torch.float32, device=q.device)
+    if no_alloc:
+        if workspace is not None or events is not None:
+            raise ValueError("no_alloc takes no workspace or events")
+        st = lib().rla2_fwd_chunked_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma_q),
+                                            _ptr(gamma_k), _ptr(out), _ptr(fS), _ptr(fz), _stream(q.device))
+        if st:
+            raise Rla2Error(st, "rla2_fwd_chunked_noalloc")
+        return (out, fS, fz) if return_final_state else out
     nbytes = fwd_workspace_size(desc)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librla2.so")
 SOURCES = [os.path.join(CSRC, "rla2_api.cpp"), os.path.join(CSRC, "rla2_kernels.hip"),
-           os.path.join(CSRC, "rla2_backward.hip")]
+           os.path.join(CSRC, "rla2_backward.hip"), os.path.join(CSRC, "rla2_noalloc.hip")]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU forms are kept out of the device code: the compiler still

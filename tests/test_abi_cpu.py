@@ -313,3 +313,18 @@ def test_workspace_flags_and_wait_polls_hook():
     prev = L.rla2_debug_set_wait_polls(5)
     assert L.rla2_debug_set_wait_polls(prev) == 5
     assert prev > 1000
+
+
+def test_no_alloc_forward_refuses_before_any_launch():
+    # the allocation-free forward validates like rla2_fwd_chunked, and a problem whose workspace
+    # exceeds its 64 MiB per-GPU array (64 heads x 65536 tokens at d = 128: 65 MiB) is refused
+    L = rla.lib()
+
+    def call(d):
+        return L.rla2_fwd_chunked_noalloc(ctypes.byref(d), A, A + 64 * MB, A + 128 * MB, A + 192 * MB,
+                                          A + 193 * MB, A + 256 * MB, None, None, None)
+
+    assert call(desc(B=1, H=64, L=65536, d=128)) == WS
+    assert call(desc(d=48)) == UNSUP
+    assert call(desc(eps=0.0)) == VALUE
+    assert ws_size(desc(B=1, H=32, L=65536, d=128))[1] < (64 << 20)   # the long-context forward fits
