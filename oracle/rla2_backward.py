@@ -1,4 +1,5 @@
-"""CPU oracle of the RLA-2 causal backward (fp64, plain PyTorch CPU ops + autograd).
+"""CPU oracle of the RLA-2 backward, causal and bidirectional (fp64, plain PyTorch CPU ops +
+autograd).
 
 TEST INFRASTRUCTURE ONLY, like ``rla2_oracle``: only the tests, ``smoke()`` and the
 bench's ``cpu_baseline`` leg may use it; it shares no code with the HIP path.
@@ -41,13 +42,15 @@ def feature_map_torch(x, gamma, positions, rms_eps=DEFAULT_RMS_EPS, base=DEFAULT
     return torch.relu(u)
 
 
-def attention_torch(qp, kp, v, eps=DEFAULT_EPS, S0=None, z0=None):
-    """Causal closed form for one document: out_t = sum_{i<=t} s_ti v_i / (sum_{i<=t} s_ti + eps),
-    with an initial state (S0 [d, d], z0 [d]) adding q'_t S0 to the numerator and q'_t . z0 to
-    the denominator (the scan's starting value, RLA page §4.1)."""
+def attention_torch(qp, kp, v, eps=DEFAULT_EPS, S0=None, z0=None, causal=True):
+    """Closed form for one document: out_t = sum_i s_ti v_i / (sum_i s_ti + eps) over the keys
+    i <= t (causal) or over the whole document (causal=False: RLA page §4.1, the scan's
+    whole-set constants), with an initial state (S0 [d, d], z0 [d]) adding q'_t S0 to the
+    numerator and q'_t . z0 to the denominator (the scan's starting value, RLA page §4.1)."""
     n = qp.shape[0]
     s = qp @ kp.T
-    s = torch.where(torch.tril(torch.ones(n, n, dtype=torch.bool)), s, torch.zeros_like(s))
+    if causal:
+        s = torch.where(torch.tril(torch.ones(n, n, dtype=torch.bool)), s, torch.zeros_like(s))
     num, den = s @ v, s.sum(dim=1, keepdim=True) + eps
     if S0 is not None:
         num = num + qp @ S0
@@ -56,10 +59,11 @@ def attention_torch(qp, kp, v, eps=DEFAULT_EPS, S0=None, z0=None):
 
 
 def fwd_torch(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
-              rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0):
-    """Differentiable closed-form causal forward over [B, H, L, d] (torch fp64 tensors).
-    The first document of each row starts at position ``initial_pos`` and from the
-    initial state (constants here: no gradient flows to them), as the forward oracle."""
+              rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0, causal=True):
+    """Differentiable closed-form forward over [B, H, L, d] (torch fp64 tensors), causal or
+    bidirectional (``causal=False``: every token reads its whole document). The first
+    document of each row starts at position ``initial_pos`` and from the initial state
+    (constants here: no gradient flows to them), as the forward oracle."""
     B, H, L, d = q.shape
     out = torch.zeros(B, H, L, d, dtype=torch.float64)
     first = first_documents(B, L, cu_seqlens)
@@ -75,48 +79,61 @@ def fwd_torch(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps=DEFAULT_EPS, rms_e
             qp = feature_map_torch(q[b, h, s0:s1], gamma_q[h], pos, rms_eps, rope_base)
             kp = feature_map_torch(k[b, h, s0:s1], gamma_k[h], pos, rms_eps, rope_base)
             out[b, h, s0:s1] = attention_torch(qp, kp, v[b, h, s0:s1], eps, S0[h] if init else None,
-                                               z0[h] if init else None)
+                                               z0[h] if init else None, causal)
     return out
 
 
 def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
-        rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0):
-    """Gradients (dq, dk, dv, dgamma_q, dgamma_k) of sum(out * dout), fp64 numpy arrays."""
+        rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0, causal=True):
+    """Gradients (dq, dk, dv, dgamma_q, dgamma_k) of sum(out * dout), fp64 numpy arrays, of the
+    causal or (``causal=False``) bidirectional forward."""
     leaves = [_t(x).requires_grad_(True) for x in (q, k, v, gamma_q, gamma_k)]
-    out = fwd_torch(*leaves, cu_seqlens, eps, rms_eps, rope_base, initial_S, initial_z, initial_pos)
+    out = fwd_torch(*leaves, cu_seqlens, eps, rms_eps, rope_base, initial_S, initial_z, initial_pos, causal)
     grads = torch.autograd.grad((out * _t(dout)).sum(), leaves, allow_unused=True)
     return tuple(np.zeros(tuple(x.shape)) if g is None else g.numpy() for g, x in zip(grads, leaves))
 
 
-def bwd_qk_prime(qp, kp, v, g, eps=DEFAULT_EPS):
+def bwd_qk_prime(qp, kp, v, g, eps=DEFAULT_EPS, causal=True):
     """The RLA page §4.2 backward for one document, from q', k' (fp64 numpy, [n, d]):
     states S_t = sum_{i<=t} k'_i v_i^T, z_t = sum_{i<=t} k'_i, num_t = S_t^T q'_t,
     gnum_t = g_t / (q'_t . z_t + eps), scale_t = -(g_t . num_t) / (q'_t . z_t + eps)^2;
     dq'_t = S_t gnum_t + scale_t z_t; with the suffix sums P_i = sum_{t>=i} q'_t gnum_t^T
-    and p_i = sum_{t>=i} scale_t q'_t: dk'_i = P_i v_i + p_i, dv_i = P_i^T k'_i."""
+    and p_i = sum_{t>=i} scale_t q'_t: dk'_i = P_i v_i + p_i, dv_i = P_i^T k'_i.
+    ``causal=False`` (the page's bidirectional branch): S, z are the whole document's sums
+    for every t, and P, p the whole document's sums of the same terms for every i."""
     n, d = qp.shape
     dqp, dkp, dv = np.zeros((n, d)), np.zeros((n, d)), np.zeros((n, d))
     S, z = np.zeros((d, d)), np.zeros(d)
     gnum, scale = np.zeros((n, d)), np.zeros(n)
+    if not causal:
+        for i in range(n):
+            S += np.outer(kp[i], v[i])
+            z += kp[i]
     for t in range(n):                                   # forward recursion
-        S += np.outer(kp[t], v[t])
-        z += kp[t]
+        if causal:
+            S += np.outer(kp[t], v[t])
+            z += kp[t]
         den = qp[t] @ z + eps
         num = S.T @ qp[t]
         gnum[t] = g[t] / den
         scale[t] = -(g[t] @ num) / den ** 2
         dqp[t] = S @ gnum[t] + scale[t] * z
     P, p = np.zeros((d, d)), np.zeros(d)
+    if not causal:
+        for t in range(n):
+            P += np.outer(qp[t], gnum[t])
+            p += scale[t] * qp[t]
     for i in range(n - 1, -1, -1):                       # suffix (reverse) recursion
-        P += np.outer(qp[i], gnum[i])
-        p += scale[i] * qp[i]
+        if causal:
+            P += np.outer(qp[i], gnum[i])
+            p += scale[i] * qp[i]
         dkp[i] = P @ v[i] + p
         dv[i] = P.T @ kp[i]
     return dqp, dkp, dv
 
 
 def bwd_one_document(q, k, v, g, gamma_q, gamma_k, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
-                     rope_base=DEFAULT_ROPE_BASE):
+                     rope_base=DEFAULT_ROPE_BASE, causal=True):
     """Gradients (dq, dk, dv, dgamma_q, dgamma_k) of sum(out * g) for ONE head's single
     document ``[n, d]`` (positions 0..n-1, no initial state), in time linear in n: the
     RLA page §4.2 recursions (``bwd_qk_prime``) give the gradients with respect to q', k'
@@ -128,7 +145,8 @@ def bwd_one_document(q, k, v, g, gamma_q, gamma_k, eps=DEFAULT_EPS, rms_eps=DEFA
     xq, xk, tq, tk = (_t(x).requires_grad_(True) for x in (q, k, gamma_q, gamma_k))
     qp = feature_map_torch(xq, tq, pos, rms_eps, rope_base)
     kp = feature_map_torch(xk, tk, pos, rms_eps, rope_base)
-    dqp, dkp, dv = bwd_qk_prime(qp.detach().numpy(), kp.detach().numpy(), _t(v).numpy(), _t(g).numpy(), eps)
+    dqp, dkp, dv = bwd_qk_prime(qp.detach().numpy(), kp.detach().numpy(), _t(v).numpy(), _t(g).numpy(), eps,
+                                causal)
     dq, dgq = torch.autograd.grad(qp, (xq, tq), torch.as_tensor(dqp))
     dk, dgk = torch.autograd.grad(kp, (xk, tk), torch.as_tensor(dkp))
     return dq.numpy(), dk.numpy(), dv, dgq.numpy(), dgk.numpy()

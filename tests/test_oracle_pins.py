@@ -467,6 +467,90 @@ def test_backward_one_document_matches_autograd():
         np.testing.assert_allclose(a, b2[0], rtol=1e-10, atol=1e-12)
     assert (ref[1] == 0).sum() == 0 and np.abs(ref[4]).min() > 0   # every gradient is exercised
 
+
+# --- the bidirectional backward (RLA page §4.1 causal=false, §4.2 bidirectional branch) ------
+
+def test_bidirectional_backward_matches_finite_differences():
+    r = np.random.default_rng(81)
+    B, H, L, d = 1, 1, 7, 4
+    cu = np.array([0, 3, 7])
+    args = [torch.tensor(r.normal(size=(B, H, L, d)), requires_grad=True) for _ in range(3)]
+    args += [torch.tensor(r.uniform(0.5, 1.5, size=(H, d)), requires_grad=True) for _ in range(2)]
+    assert torch.autograd.gradcheck(lambda *a: oracle.fwd_torch(*a, cu, causal=False), args, eps=1e-6, atol=1e-8,
+                                    rtol=1e-6)
+
+
+def test_bidirectional_backward_forward_is_the_pinned_forward():
+    # the differentiable bidirectional forward equals the forward oracle's bidirectional mode
+    # (pinned above by the document-state read-out), with and without an initial state
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 16, 8, 82, [5, 0, 11])
+    S0, z0 = workloads.initial_state(2, 8, seed=83)
+    S0, z0 = S0.double().numpy(), z0.double().numpy()
+    for kw in ({}, dict(initial_S=S0, initial_z=z0, initial_pos=9)):
+        out = oracle.fwd_torch(*(torch.tensor(x) for x in (q, k, v, gq, gk)), cu, causal=False, **kw)
+        ref = oracle.fwd(q, k, v, gq, gk, cu, causal=False, **kw)
+        np.testing.assert_allclose(out.numpy(), ref, rtol=1e-12, atol=1e-14)
+
+
+def test_bidirectional_backward_matches_page_formulas():
+    # the page's bidirectional branch (whole-document S, z for every query; whole-document
+    # sums P, p of q' gnum^T and scale q' for every key) equals autograd of the closed form
+    r = np.random.default_rng(84)
+    n, d = 13, 6
+    qp, kp = np.abs(r.normal(size=(n, d))), np.maximum(r.normal(size=(n, d)), 0)
+    v, g = r.normal(size=(n, d)), r.normal(size=(n, d))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (qp, kp, v))
+    out = oracle.rla2_backward.attention_torch(tq, tk, tv, causal=False)
+    gq, gk, gv = torch.autograd.grad((out * torch.tensor(g)).sum(), (tq, tk, tv))
+    dqp, dkp, dv = oracle.bwd_qk_prime(qp, kp, v, g, causal=False)
+    np.testing.assert_allclose(dqp, gq.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dkp, gk.numpy(), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dv, gv.numpy(), rtol=1e-11, atol=1e-12)
+    # no causal order: permuting the tokens permutes the gradients
+    perm = r.permutation(n)
+    for a, b2 in zip(oracle.bwd_qk_prime(qp[perm], kp[perm], v[perm], g[perm], causal=False), (dqp, dkp, dv)):
+        np.testing.assert_allclose(a, b2[perm], rtol=1e-11, atol=1e-12)
+
+
+def test_bidirectional_value_gradient_closed_form_and_isolation():
+    # dv_i = sum_{t in doc} s_ti / den_t g_t over the WHOLE document (not t >= i), and a
+    # cotangent on one document changes no gradient of another
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 20, 8, 85, [8, 12])
+    r = np.random.default_rng(86)
+    g = r.normal(size=q.shape)
+    dq, dk, dv, _, _ = oracle.bwd(q, k, v, gq, gk, g, cu, causal=False)
+    for (b, s0, s1) in oracle.documents(1, 20, cu):
+        for h in range(2):
+            pos = np.arange(s1 - s0)
+            qp = oracle.feature_map(q[b, h, s0:s1], gq[h], pos)
+            kp = oracle.feature_map(k[b, h, s0:s1], gk[h], pos)
+            s = qp @ kp.T
+            a = s / (s.sum(axis=1, keepdims=True) + oracle.DEFAULT_EPS)
+            np.testing.assert_allclose(dv[b, h, s0:s1], a.T @ g[b, h, s0:s1], rtol=1e-11, atol=1e-13)
+    g2 = g.copy()
+    g2[:, :, 8:] += r.normal(size=g2[:, :, 8:].shape)
+    dq2, dk2, dv2, _, _ = oracle.bwd(q, k, v, gq, gk, g2, cu, causal=False)
+    for a, b2 in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        np.testing.assert_array_equal(a[:, :, :8], b2[:, :, :8])
+    # in the causal mode a document's first key receives from every query, so its value
+    # gradient matches; a later key receives from the earlier queries only in this mode
+    dvc = oracle.bwd(q, k, v, gq, gk, g, cu)[2]
+    np.testing.assert_allclose(dvc[:, :, 0], dv[:, :, 0], rtol=1e-11, atol=1e-13)
+    assert np.abs(dvc[:, :, 1] - dv[:, :, 1]).max() > 1e-3
+
+
+def test_bidirectional_one_document_matches_autograd():
+    r = np.random.default_rng(87)
+    n, d = 30, 8
+    q, k, v, gq, gk, _ = _rand_case(1, 1, n, d, 88, None)
+    g = r.normal(size=q.shape)
+    ref = oracle.bwd(q, k, v, gq, gk, g, eps=1e-3, causal=False)
+    got = oracle.bwd_one_document(q[0, 0], k[0, 0], v[0, 0], g[0, 0], gq[0], gk[0], eps=1e-3, causal=False)
+    for a, b2 in zip(got[:3], ref[:3]):
+        np.testing.assert_allclose(a, b2[0, 0], rtol=1e-10, atol=1e-12)
+    for a, b2 in zip(got[3:], ref[3:]):
+        np.testing.assert_allclose(a, b2[0], rtol=1e-10, atol=1e-12)
+
 # --- the original RLA's L2 denominator (RLA page §2.1 closed form, §4.1 A state) -------
 
 @pytest.mark.parametrize("B,H,L,d,lengths", [(1, 2, 11, 6, [4, 7]), (2, 1, 9, 4, None), (1, 1, 8, 8, [1, 0, 7])])
