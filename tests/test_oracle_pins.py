@@ -532,11 +532,9 @@ def test_bidirectional_value_gradient_closed_form_and_isolation():
     dq2, dk2, dv2, _, _ = oracle.bwd(q, k, v, gq, gk, g2, cu, causal=False)
     for a, b2 in ((dq, dq2), (dk, dk2), (dv, dv2)):
         np.testing.assert_array_equal(a[:, :, :8], b2[:, :, :8])
-    # in the causal mode a document's first key receives from every query, so its value
-    # gradient matches; a later key receives from the earlier queries only in this mode
+    # the causal mode differs: there a document's last key receives from its own query only
     dvc = oracle.bwd(q, k, v, gq, gk, g, cu)[2]
-    np.testing.assert_allclose(dvc[:, :, 0], dv[:, :, 0], rtol=1e-11, atol=1e-13)
-    assert np.abs(dvc[:, :, 1] - dv[:, :, 1]).max() > 1e-3
+    assert np.abs(dvc[:, :, 7] - dv[:, :, 7]).max() > 1e-3
 
 
 def test_bidirectional_one_document_matches_autograd():
