@@ -266,19 +266,22 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
 rla2_status rla2_bwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
 
 /*
- * Chunked backward of the causal forward (RLA page §4.2 backward of the layer): with
- * g = dL/dout, gnum_t = g_t / (q'_t . z_t + eps), scale_t = -(g_t . num_t) / (q'_t . z_t +
- * eps)^2, dq'_t = S_t gnum_t + scale_t z_t and, with the suffix sums P_i = sum_{t >= i}
- * q'_t gnum_t^T and p_i = sum_{t >= i} scale_t q'_t (same document), dk'_i = P_i v_i + p_i,
- * dv_i = P_i^T k'_i; then through the ReLU (gate q' > 0), RoPE and RMSNorm to dq, dk and
- * the RMSNorm weights. The forward's states and g . num are recomputed from q, k, v (the
- * forward output is not an input). bf16 activations only (RLA2_ERR_UNSUPPORTED otherwise),
- * causal only (desc->bidirectional must be 0). An initial state and position offset in
- * desc are taken into account; the gradient with respect to the initial state is not formed.
- *  q, k, v       [B, H, L, d] bf16, the forward's inputs.
+ * Chunked backward of the forward (RLA page §4.2 backward of the layer): with g = dL/dout,
+ * gnum_t = g_t / (q'_t . z_t + eps), scale_t = -(g_t . num_t) / (q'_t . z_t + eps)^2,
+ * dq'_t = S_t gnum_t + scale_t z_t and, with the suffix sums P_i = sum_{t >= i} q'_t gnum_t^T
+ * and p_i = sum_{t >= i} scale_t q'_t (same document), dk'_i = P_i v_i + p_i,
+ * dv_i = P_i^T k'_i; then through the ReLU (gate q' > 0), RoPE and RMSNorm to dq, dk and the
+ * RMSNorm weights. desc->bidirectional = 1 differentiates the bidirectional forward (the
+ * page's bidirectional branch: S_t, z_t are the document's totals for every query, P_i, p_i
+ * the document's totals for every key). The forward's states and g . num are recomputed from
+ * q, k, v (the forward output is not an input). bf16 or fp32 activations; the Sum
+ * denominator only (RLA2_ERR_UNSUPPORTED for the L2 denominator). An initial state and
+ * position offset in desc are taken into account; the gradient with respect to the initial
+ * state is not formed. desc->chunk does not change the arithmetic of the backward.
+ *  q, k, v       [B, H, L, d] dtype, the forward's inputs.
  *  gamma_q/k     [H, d] fp32.
- *  dout          [B, H, L, d] bf16, dL/dout (read).
- *  dq, dk, dv    [B, H, L, d] bf16, written.
+ *  dout          [B, H, L, d] dtype, dL/dout (read).
+ *  dq, dk, dv    [B, H, L, d] dtype, written.
  *  dgamma_q/k    optional [H, d] fp32, written (NULL = not formed).
  *  workspace     at least rla2_bwd_workspace_size() bytes, 256-byte aligned.
  * Outputs must not overlap any input, each other or the workspace (RLA2_ERR_ALIAS).
@@ -310,8 +313,8 @@ rla2_status rla2_bwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
 /*
  * rla2_bwd_chunked without its state pass: the forward's states S_t, z_t (RLA page §4.2,
  * the states the backward of the layer reads) are taken from `fwd_workspace`, the
- * workspace of an rla2_fwd_chunked call with the same desc (causal, Sum denominator) and
- * the same k, v, gamma_k and initial state, not written since. The plan stamp that forward
+ * workspace of an rla2_fwd_chunked call with the same desc (causal or bidirectional, Sum
+ * denominator) and the same k, v, gamma_k and initial state, not written since. The plan stamp that forward
  * left in the workspace header (shape, segmentation, position offset, scan mode and a
  * checksum of the cu_seqlens contents) is compared on the device with this call's plan
  * first: on a mismatch no backward kernel touches memory and the backward's own workspace

@@ -296,8 +296,9 @@ def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0,
 
 def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
         rope_base=10000.0, initial_S=None, initial_z=None, initial_pos=0, want_dgamma=True, workspace=None,
-        out=None, events=None, fwd_workspace=None):
-    """Backward of the causal forward (bf16) for the same inputs; ``dout`` = dL/dout.
+        out=None, events=None, fwd_workspace=None, bidirectional=False):
+    """Backward of the forward (causal, or ``bidirectional``; bf16 or fp32) for the same inputs;
+    ``dout`` = dL/dout.
     Returns ``(dq, dk, dv, dgamma_q, dgamma_k)`` (the last two None unless ``want_dgamma``).
     ``out``: optional preallocated ``(dq, dk, dv, dgamma_q, dgamma_k)``; ``events``: optional
     ctypes array of RLA2_BWD_KERNELS + 1 hipEvent_t handles (rla2_bwd_chunked_profiled).
@@ -305,19 +306,19 @@ def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunk
     options, causal, Sum denominator), untouched since: its states are read instead of being
     formed again (rla2_bwd_chunked_saved; bitwise the same gradients)."""
     for n_, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
-        _check_dev(n_, t, torch.bfloat16)
+        _check_dev(n_, t, q.dtype)
         if t.shape != q.shape:
             raise ValueError(f"{n_} must have the shape of q")
     _check_dev("gamma_q", gamma_q, torch.float32)
     _check_dev("gamma_k", gamma_k, torch.float32)
-    desc = _fwd_desc(q, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base, False, initial_pos,
+    desc = _fwd_desc(q, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base, bidirectional, initial_pos,
                      initial_S, initial_z)
     if gamma_q.shape != (desc.H, desc.d) or gamma_k.shape != (desc.H, desc.d):
         raise ValueError("gamma_q and gamma_k must be [H, d]")
     if out is not None:
         dq, dk, dv, dgq, dgk = out
         for n_, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-            _check_dev(n_, t, torch.bfloat16)
+            _check_dev(n_, t, q.dtype)
             if t.shape != q.shape:
                 raise ValueError(f"{n_} must have the shape of q")
         for n_, t in (("dgamma_q", dgq), ("dgamma_k", dgk)):

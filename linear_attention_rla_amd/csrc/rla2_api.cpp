@@ -206,8 +206,9 @@ Stamp make_stamp(const Plan& p, int mode) {
 
 namespace {
 
-// The backward's supported modes: bf16 activations, causal, Sum denominator.
-bool bwd_supported(const Plan& p) { return p.dtype == RLA2_BF16 && !p.bidirectional && !p.l2; }
+// The backward's supported modes: bf16 or fp32 activations, causal or bidirectional, the Sum
+// denominator.
+bool bwd_supported(const Plan& p) { return !p.l2; }
 
 // The backward entry points; `saved` (with `saved_bytes`) is the matching forward's workspace,
 // or null.

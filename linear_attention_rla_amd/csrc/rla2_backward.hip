@@ -1156,6 +1156,804 @@ __global__ void bwd_dgamma_kernel(const float* __restrict__ part, const int32_t*
   }
 }
 
+// ----------------------------------------------------------------------------------------
+// Generic backward: fp32 activations in both modes and bf16 in the bidirectional mode (the
+// bf16 causal backward runs the warp-specialised sweeps above). Same formulas as the sweeps
+// (RLA page §4.2): with g = dL/dout, per query t the forward quantities are formed again,
+//   causal:         den_t = q'_t . z_prev + sum_{i<=t} a_ti + eps,
+//                   g . num_t = q'_t . (S_prev g_t) + sum_{i<=t} a_ti (g_t . v_i)
+//   bidirectional:  den_t = q'_t . z_doc + eps,  g . num_t = q'_t . (S_doc g_t)
+// (a_ti = the score rounded to the element type, as the forward uses it), gd_t = -(g . num_t) /
+// den_t^2, and
+//   dq'_t = (S g_t) / den_t + gd_t z + [causal] sum_{i<=t} k'_i B_ti,  B_ti = (g_t . v_i) / den_t
+//           + gd_t, with the self weight B_tt formed without its cancelling O(1) terms
+//   dk'_i = P v_i + p + [causal] sum_{t>=i} q'_t B_ti,  dv_i = P^T k'_i + [causal] sum_{t>=i}
+//           (a_ti / den_t) g_t
+// where P = sum_t Q^_t g_t^T, p = sum_t Q^_t (gd den)_t, Q^ = q'/den rounded to the element
+// type, summed over the later tokens of the document (causal: per segment in the dq kernel,
+// over the later segments by the suffix scan, over the later blocks in the dk/dv kernel) or
+// over the whole document (bidirectional: the total scan). 4 waves, blocks of 32 tokens,
+// lanes 0..127 map the query side (q, dout), lanes 128..255 the key side (k, v); states in
+// accumulators (the dq kernel holds S^T, whose tiles serve S g directly; the dk/dv kernel P
+// and P^T); bf16 states enter the products that can cancel (S g, P v) as value + remainder.
+
+constexpr int kTB = 32;  // tokens per block of the generic backward
+
+// Fragment of the transposed view of a row-major LDS array [k][n] (pitch in elements): lane
+// (c16, g) gets [k0 + 4g + j][n0 + c16] and [k0 + 16 + 4g + j][n0 + c16], j < 4 (the slot
+// order of lds_frag): the transposing LDS read for bf16, eight reads for fp32.
+template <bool BF>
+__device__ __forceinline__ Frag<BF> lds_frag_t(const typename Elem<BF>::St* base, int pitch, int k0, int n0,
+                                               int lane) {
+  if constexpr (BF) {
+    return lds_frag_tr(base, pitch, k0, n0, lane);
+  } else {
+    const int c16 = lane & 15, g = lane >> 4;
+    Frag<false> f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.v[j] = base[(k0 + 4 * g + j) * pitch + n0 + c16];
+      f.v[4 + j] = base[(k0 + 16 + 4 * g + j) * pitch + n0 + c16];
+    }
+    return f;
+  }
+}
+
+// The same slots scaled per token (slot token k0 + 4g + j, k0 + 16 + 4g + j) by w[token] and
+// rounded to the element type: the Q^ = q'/den operand from the q' rows.
+template <bool BF>
+__device__ __forceinline__ Frag<BF> scale_slots(Frag<BF> f, const float* w, int k0, int lane) {
+  const int g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float s = w[k0 + (j >> 2) * 16 + 4 * g + (j & 3)];
+    if constexpr (BF) f.v[j] = static_cast<__bf16>(static_cast<float>(f.v[j]) * s);
+    else f.v[j] = f.v[j] * s;
+  }
+  return f;
+}
+
+// An fp32 accumulator pair (rows 0..15 and 16..31 of a k-block) as an MFMA operand: bf16 value
+// and remainder (two products), fp32 exact (one).
+template <bool BF>
+struct OpPair {
+  Frag<BF> hi, lo;
+};
+template <bool BF, int D>
+__device__ __forceinline__ OpPair<BF> op_pair(floatx4 a, floatx4 b) {
+  OpPair<BF> r;
+  if constexpr (BF) split_frag<D>(a, b, r.hi, r.lo);
+  else r.hi = acc_frag_f(a, b);
+  return r;
+}
+template <bool BF>
+__device__ __forceinline__ floatx4 mma_pair(const OpPair<BF>& a, const Frag<BF>& b, floatx4 c) {
+  c = mma(a.hi, b, c);
+  if constexpr (BF) c = mma(a.lo, b, c);
+  return c;
+}
+
+// Operand whose every column holds w[token] (slot order), as an exact pair for fp32 or a bf16
+// value + remainder pair.
+template <bool BF>
+__device__ __forceinline__ OpPair<BF> token_cols(const float* w, int lane) {
+  OpPair<BF> r;
+  const int g = lane >> 4;
+  if constexpr (BF) {
+    token_col_frags(w, 0, g, r.hi, r.lo);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.hi.v[j] = w[4 * g + j];
+      r.hi.v[4 + j] = w[16 + 4 * g + j];
+    }
+  }
+  return r;
+}
+
+// Map backward of the lane's two tokens for either element type (see map_backward): dx' from
+// fp32 rows `dxp`, the pre-activation formed again exactly as the forward forms it (gamma,
+// in-chunk angle rows lo_base[t0 + tok], chunk row hi_row), the weight gradient accumulated
+// in dg1 / dg2, dx rounded to the element type in the lane's raw layout.
+template <bool BF, int D>
+__device__ __forceinline__ void map_backward_g(const Raw<BF, D>& r, Raw<BF, D>& dx, const float* dxp, int fp,
+                                               const float* gamma, const float2* lo_base, const float2* hi_row,
+                                               float rms_eps, int t0, int m, float (&dg1)[Geo<BF, D>::E],
+                                               float (&dg2)[Geo<BF, D>::E]) {
+  using G = Geo<BF, D>;
+  constexpr int E = G::E;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+    const float inv = rms_inv<BF, D>(r, tok, rms_eps);
+    const float2* lo = lo_base + (t0 + tok) * G::HALF;
+    float dy1[E], dy2[E];
+    float T = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = m * E + e;
+      const float2 cs = angle_sum(hi_row[j], lo[j]);
+      const float x1 = r.get(tok, 0, e), x2 = r.get(tok, 1, e);
+      float u1, u2;
+      rope_pair(x1, x2, inv, gamma[j], gamma[j + G::HALF], cs, u1, u2);
+      const float d1 = u1 > 0.f ? dxp[(t0 + tok) * fp + j] : 0.f;
+      const float d2 = u2 > 0.f ? dxp[(t0 + tok) * fp + G::HALF + j] : 0.f;
+      dy1[e] = __builtin_fmaf(d1, cs.x, d2 * cs.y);  // inverse rotation
+      dy2[e] = __builtin_fmaf(d2, cs.x, -(d1 * cs.y));
+      T = __builtin_fmaf(gamma[j] * dy1[e], x1, T);
+      T = __builtin_fmaf(gamma[j + G::HALF] * dy2[e], x2, T);
+      dg1[e] = __builtin_fmaf(dy1[e], x1 * inv, dg1[e]);
+      dg2[e] = __builtin_fmaf(dy2[e], x2 * inv, dg2[e]);
+    }
+    T = sum8(T);
+    const float coef = inv * inv * inv * T * (1.0f / D);
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const int j = m * E + e;
+      const float a0 = __builtin_fmaf(inv * gamma[j], dy1[e], -(coef * r.get(tok, 0, e)));
+      const float a1 = __builtin_fmaf(inv * gamma[j + 1], dy1[e + 1], -(coef * r.get(tok, 0, e + 1)));
+      const float b0 = __builtin_fmaf(inv * gamma[j + G::HALF], dy2[e], -(coef * r.get(tok, 1, e)));
+      const float b1 = __builtin_fmaf(inv * gamma[j + G::HALF + 1], dy2[e + 1], -(coef * r.get(tok, 1, e + 1)));
+      if constexpr (BF) {
+        dx.w[tok][0][e >> 1] = pack_bf2(a0, a1);
+        dx.w[tok][1][e >> 1] = pack_bf2(b0, b1);
+      } else {
+        dx.w[tok][0][e] = __float_as_uint(a0);
+        dx.w[tok][0][e + 1] = __float_as_uint(a1);
+        dx.w[tok][1][e] = __float_as_uint(b0);
+        dx.w[tok][1][e + 1] = __float_as_uint(b1);
+      }
+    }
+  }
+}
+
+// The lane's two tokens (rows t0, t0 + 1, first nv rows valid) to global memory.
+template <bool BF, int D>
+__device__ __forceinline__ void store_raw(const Raw<BF, D>& x, typename Elem<BF>::St* base, int t0, int m, int nv) {
+  using G = Geo<BF, D>;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok)
+    if (t0 + tok < nv)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        copy_bytes<G::E * G::ES>(base + (size_t)(t0 + tok) * D + hh * G::HALF + m * G::E, x.w[tok][hh]);
+}
+
+// The segment record's S (or P) as transposed tiles: tile (rt, ct) of wave w, lane (c16, g),
+// row i holds M[a][c] with a = w DVW + 16 ct + c16 and c = 16 rt + 4g + i, gathered from the
+// fragment-native record.
+template <bool BF, int D>
+__device__ __forceinline__ void load_rec_transposed(const float* rec, int w, int lane,
+                                                    floatx4 (&T)[Geo<BF, D>::RT][Geo<BF, D>::CT]) {
+  using G = Geo<BF, D>;
+  const int c16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < G::RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+      const int a = w * G::DVW + 16 * ct + c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = 16 * rt + 4 * g + i;
+        const int w2 = c / G::DVW, ct2 = (c % G::DVW) / 16, l2 = 16 * ((a % 16) / 4) + c % 16;
+        T[rt][ct][i] = rec[rec_frag<BF, D>(w2, a / 16, ct2, l2) + a % 4];
+      }
+    }
+}
+
+// RMSNorm-weight partials of the 128 lanes of one side (two waves): lanes sharing m, then the
+// waves, into dst[0 .. D). `red` holds 2 D floats of LDS; every thread calls it.
+template <int D, int E>
+__device__ __forceinline__ void write_dgamma(float (&dg1)[E], float (&dg2)[E], int side_wave, bool mine, int lane,
+                                             float* red, float* dst) {
+  const int m = lane & 7;
+  if (mine) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1) {
+        dg1[e] += __shfl_xor(dg1[e], o);
+        dg2[e] += __shfl_xor(dg2[e], o);
+      }
+    }
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        red[side_wave * D + m * E + e] = dg1[e];
+        red[side_wave * D + D / 2 + m * E + e] = dg2[e];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < D; i += NT) dst[i] = red[i] + red[D + i];
+}
+
+template <bool BF, int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 1) void gbwd_dq_kernel(
+    const typename Elem<BF>::St* __restrict__ q, const typename Elem<BF>::St* __restrict__ k,
+    const typename Elem<BF>::St* __restrict__ v, const typename Elem<BF>::St* __restrict__ dout,
+    const float* __restrict__ gamma_q, const float* __restrict__ gamma_k, const int32_t* __restrict__ tab,
+    const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
+    const float* __restrict__ states, typename Elem<BF>::St* __restrict__ dq, float* __restrict__ den_out,
+    float* __restrict__ gd_out, float* __restrict__ bd_out, float* __restrict__ pstates,
+    float* __restrict__ dg_part, int H, int L, float rms_eps, float eps, const uint32_t* __restrict__ hdr,
+    TabLimits lim) {
+  using G = Geo<BF, D>;
+  using St = typename G::St;
+  using EL = Elem<BF>;
+  constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E, NW = G::NW, P = G::ROWP, FP = D + 4;
+  constexpr int ZR = RT >= 4 ? RT / 4 : 1;  // row tiles of p per wave
+  __shared__ __attribute__((aligned(16))) St sQ[kTB * P];  // q'
+  __shared__ __attribute__((aligned(16))) St sG[kTB * P];  // dout
+  __shared__ __attribute__((aligned(16))) St sK[CAUSAL ? kTB * P : 8];
+  __shared__ __attribute__((aligned(16))) St sV[CAUSAL ? kTB * P : 8];
+  __shared__ __attribute__((aligned(16))) float sdQ[kTB * FP];  // dq' rows; also the weight partials
+  __shared__ float sZ[2 * D];  // z before the block, by block parity
+  __shared__ float sQz[kTB], sGs[4 * kTB], sInv[kTB], sGd[kTB], sBtt[kTB], sW[kTB];
+  __shared__ float sRx[kTB], sGx[kTB], sAtt[kTB], sGvt[kTB];
+  __shared__ floatx4 sGV[3 * 64];  // causal: g.v tiles (query tile, key tile) (0,0), (1,0), (1,1)
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (!bwd_go(hdr) || seg >= *nseg) return;
+  const SegInfo si = read_seg_clamped(tab, seg, L, lim);
+  if (si.len == 0) return;  // only a corrupted table has empty segments
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+  const int side = tid >> 7, t0 = 2 * ((tid & 127) >> 3), m = tid & 7;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const float* gq = gamma_q + (size_t)h * D;
+  const float* gk = gamma_k + (size_t)h * D;
+  const int wv = wave < NW ? wave : 0;  // waves without state columns keep a harmless copy
+  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+
+  floatx4 ST[RT][CT];  // S^T: rows = value dims, columns = this wave's key dims
+  load_rec_transposed<BF, D>(rec, wv, lane, ST);
+  if (tid < D) sZ[tid] = rec[D * D + tid];
+  floatx4 Pt[RT][CT];  // sum_t Q^_t g_t^T: rows = query dims a, columns = this wave's value dims
+  floatx4 pc[ZR];      // sum_t Q^_t (gd den)_t: row tiles wave ZR + z, every column
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) Pt[rt][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int z = 0; z < ZR; ++z) pc[z] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float dg1[E], dg2[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) dg1[e] = dg2[e] = 0.f;
+  Raw<BF, D> rq;  // query-side lanes: raw q of their tokens (for the map backward)
+
+  const int nblk = (si.len + kTB - 1) / kTB;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int nv = min(kTB, si.len - blk * kTB);
+    const int par = blk & 1;
+    const size_t row0 = tok0 + (size_t)blk * kTB;  // first token row of the block
+    const float2* hr = rope_hi + (size_t)(si.hirow + (blk >> 1)) * G::HALF;
+    const float2* lob = rope_lo + (size_t)par * kTB * G::HALF;
+    const float* zc = sZ + (CAUSAL ? par * D : 0);  // bidirectional: the document's z throughout
+    __syncthreads();  // the previous block's LDS reads are done
+
+    // ---- map: query side q', dout rows, q'.z; key side (causal) k', v rows
+    if (side == 0) {
+      Raw<BF, D> rg, oq;
+      load_raw<BF, D>(rq, q + row0 * D, t0, m, nv);
+      load_raw<BF, D>(rg, dout + row0 * D, t0, m, nv);
+      feature_map_pair<BF, D>(rq, oq, gq, lob, hr, t0, m, rms_eps);
+      store_rows<BF, D>(sQ, oq, t0, m);
+      store_rows<BF, D>(sG, rg, t0, m);
+#pragma unroll
+      for (int tok = 0; tok < 2; ++tok) {
+        float pz = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int j = m * E + e;
+          pz = __builtin_fmaf(oq.get(tok, 0, e), zc[j], pz);
+          pz = __builtin_fmaf(oq.get(tok, 1, e), zc[j + G::HALF], pz);
+        }
+        pz = sum8(pz);
+        if (m == 0) sQz[t0 + tok] = pz;
+      }
+    } else if constexpr (CAUSAL) {
+      Raw<BF, D> rk, rv, ok;
+      load_raw<BF, D>(rk, k + row0 * D, t0, m, nv);
+      load_raw<BF, D>(rv, v + row0 * D, t0, m, nv);
+      feature_map_pair<BF, D>(rk, ok, gk, lob, hr, t0, m, rms_eps);
+      store_rows<BF, D>(sK, ok, t0, m);
+      store_rows<BF, D>(sV, rv, t0, m);
+    }
+    __syncthreads();
+
+    // ---- A: Y = S G^T for this wave's key dims and its part of q'.(S g); causal score tiles
+    floatx4 Y[CT][2];
+    if (wave < NW) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        OpPair<BF> Sa[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) Sa[kb] = op_pair<BF, D>(ST[2 * kb][ct], ST[2 * kb + 1][ct]);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          floatx4 y = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) y = mma_pair<BF>(Sa[kb], lds_frag<BF>(sG, P, 16 * tt + c16, kb, g), y);
+          Y[ct][tt] = y;  // lane (t, g): rows a = wave DVW + 16 ct + 4g + i of query 16 tt + t
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        float part = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            part = __builtin_fmaf(EL::to_f(sQ[(16 * tt + c16) * P + wave * G::DVW + 16 * ct + 4 * g + i]),
+                                  Y[ct][tt][i], part);
+        part = sum_rows4(part);
+        if (g == 0) sGs[wave * kTB + 16 * tt + c16] = part;
+      }
+    }
+    if constexpr (CAUSAL) {
+      if (wave < 2) {  // query tile tt = wave against key tiles kt <= tt
+        const int tt = wave;
+        Frag<BF> Qf[KB], Gf[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          Qf[kb] = lds_frag<BF>(sQ, P, 16 * tt + c16, kb, g);
+          Gf[kb] = lds_frag<BF>(sG, P, 16 * tt + c16, kb, g);
+        }
+        float rx = 0.f, gx = 0.f, aself = 0.f, gvself = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          if (kt > tt) continue;
+          floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f}, gv = s;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            s = mma(lds_frag<BF>(sK, P, 16 * kt + c16, kb, g), Qf[kb], s);
+            gv = mma(lds_frag<BF>(sV, P, 16 * kt + c16, kb, g), Gf[kb], gv);
+          }
+          // lane (t, g): query 16 tt + t, keys 16 kt + 4g + i
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = 4 * g + i;
+            if (kt == tt && key > c16) {  // a key after the query
+              gv[i] = 0.f;
+              continue;
+            }
+            const float a = EL::to_f(EL::from_f(s[i]));  // the weight the forward uses
+            if (kt == tt && key == c16) {
+              aself = a;
+              gvself = gv[i];
+            } else {
+              rx += a;
+              gx = __builtin_fmaf(a, gv[i], gx);
+            }
+          }
+          sGV[(tt == 0 ? 0 : 1 + kt) * 64 + lane] = gv;
+        }
+        rx = sum_rows4(rx);
+        gx = sum_rows4(gx);
+        aself = sum_rows4(aself);
+        gvself = sum_rows4(gvself);
+        if (g == 0) {
+          const int t = 16 * tt + c16;
+          sRx[t] = rx;
+          sGx[t] = gx;
+          sAtt[t] = aself;
+          sGvt[t] = gvself;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- B: per token den, gd, the self weight B_tt (sums without the self term first), and the
+    // planes the dk/dv kernel reads
+    if (tid < kTB) {
+      const int t = tid;
+      float gs = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) gs += sGs[w * kTB + t];
+      float den, gd, btt = 0.f;
+      if constexpr (CAUSAL) {
+        const float denx = sQz[t] + sRx[t] + eps;  // without the self term
+        den = denx + sAtt[t];
+        const float gnx = gs + sGx[t];
+        const float gn = __builtin_fmaf(sAtt[t], sGvt[t], gnx);
+        const float inv = 1.0f / den;
+        gd = -gn * inv * inv;
+        btt = __builtin_fmaf(sGvt[t], denx, -gnx) * inv * inv;
+        if (t < nv) {
+          den_out[row0 + t] = den;
+          gd_out[row0 + t] = gd;
+          bd_out[row0 + t] = btt;
+        }
+      } else {
+        den = sQz[t] + eps;
+        const float inv = 1.0f / den;
+        gd = -gs * inv * inv;
+      }
+      sInv[t] = 1.0f / den;
+      sGd[t] = gd;
+      sBtt[t] = btt;
+      sW[t] = t < nv ? gd * den : 0.f;
+    }
+    __syncthreads();
+
+    // ---- C: dq' tiles; then the reverse-state totals and (causal) the state update
+    floatx4 dQ[CT][2];
+    if (wave < NW) {
+      Frag<BF> Kt[CT];  // K'^T rows a, keys of the block (causal)
+      if constexpr (CAUSAL) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) Kt[ct] = lds_frag_t<BF>(sK, P, 0, wave * G::DVW + 16 * ct, lane);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int t = 16 * tt + c16;
+        const float inv = sInv[t], gd = sGd[t];
+        Frag<BF> bf;  // B^T operand (keys x this lane's query t), causal
+        if constexpr (CAUSAL) {
+          floatx4 bt[2];
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            bt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (kt <= tt) {
+              const floatx4 gv = sGV[(tt == 0 ? 0 : 1 + kt) * 64 + lane];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int key = 4 * g + i;
+                float b = __builtin_fmaf(gv[i], inv, gd);
+                if (kt == tt && key == c16) b = sBtt[t];
+                if (kt == tt && key > c16) b = 0.f;
+                bt[kt][i] = b;
+              }
+            }
+          }
+          bf = acc_frag<BF>(bt[0], bt[1]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int a0 = wave * G::DVW + 16 * ct + 4 * g;
+          floatx4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = __builtin_fmaf(Y[ct][tt][i], inv, zc[a0 + i] * gd);
+          if constexpr (CAUSAL) o = mma(Kt[ct], bf, o);
+          dQ[ct][tt] = o;
+        }
+      }
+      // P += Q^^T G and p += Q^^T (gd den) over the block's queries
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const Frag<BF> qh = scale_slots<BF>(lds_frag_t<BF>(sQ, P, 0, 16 * rt, lane), sInv, 0, lane);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          Pt[rt][ct] = mma(qh, lds_frag_t<BF>(sG, P, 0, wave * G::DVW + 16 * ct, lane), Pt[rt][ct]);
+      }
+      if (wave * ZR < RT) {
+        const OpPair<BF> wcol = token_cols<BF>(sW, lane);
+#pragma unroll
+        for (int z = 0; z < ZR; ++z) {
+          const Frag<BF> qh = scale_slots<BF>(lds_frag_t<BF>(sQ, P, 0, 16 * (wave * ZR + z), lane), sInv, 0, lane);
+          pc[z] = mma(qh, wcol.hi, pc[z]);
+          if constexpr (BF) pc[z] = mma(qh, wcol.lo, pc[z]);
+        }
+      }
+      if constexpr (CAUSAL) {  // S^T += V^T K'
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const Frag<BF> vt = lds_frag_t<BF>(sV, P, 0, 16 * rt, lane);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct)
+            ST[rt][ct] = mma(vt, lds_frag_t<BF>(sK, P, 0, wave * G::DVW + 16 * ct, lane), ST[rt][ct]);
+        }
+      }
+    }
+    if constexpr (CAUSAL) {  // z for the next block (the other parity): z + the column sums of K'
+      for (int a = tid; a < D; a += NT) {
+        float cs = 0.f;
+        for (int i = 0; i < kTB; ++i) cs += EL::to_f(sK[i * P + a]);
+        sZ[(par ^ 1) * D + a] = zc[a] + cs;
+      }
+    }
+    if (wave < NW) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+          *reinterpret_cast<floatx4*>(&sdQ[(16 * tt + c16) * FP + wave * G::DVW + 16 * ct + 4 * g]) = dQ[ct][tt];
+    }
+    __syncthreads();
+
+    // ---- D: map backward of q
+    if (side == 0) {
+      Raw<BF, D> dx;
+      map_backward_g<BF, D>(rq, dx, sdQ, FP, gq, lob, hr, rms_eps, t0, m, dg1, dg2);
+      store_raw<BF, D>(dx, dq + row0 * D, t0, m, nv);
+    }
+  }
+  __syncthreads();
+
+  // the segment's reverse-state totals (fragment-native records; p where a record keeps z)
+  float* prec = pstates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  if (wave < NW) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+        *reinterpret_cast<floatx4*>(prec + rec_frag<BF, D>(wave, rt, ct, lane)) = Pt[rt][ct];
+  }
+  if (wave * ZR < RT && c16 < 4) {  // every column of pc holds the sums of rows 16 tile + 4g + i
+#pragma unroll
+    for (int z = 0; z < ZR; ++z) prec[D * D + (wave * ZR + z) * 16 + 4 * g + c16] = pc[z][c16];
+  }
+  write_dgamma<D, E>(dg1, dg2, wave, side == 0, lane, sdQ, dg_part + ((size_t)seg * H + h) * 2 * D);
+}
+
+template <bool BF, int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 1) void gbwd_dkv_kernel(
+    const typename Elem<BF>::St* __restrict__ q, const typename Elem<BF>::St* __restrict__ k,
+    const typename Elem<BF>::St* __restrict__ v, const typename Elem<BF>::St* __restrict__ dout,
+    const float* __restrict__ gamma_q, const float* __restrict__ gamma_k, const int32_t* __restrict__ tab,
+    const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
+    const float* __restrict__ pstates, const float* __restrict__ den, const float* __restrict__ gdp,
+    const float* __restrict__ bdp, typename Elem<BF>::St* __restrict__ dk, typename Elem<BF>::St* __restrict__ dv,
+    float* __restrict__ dg_part, int H, int L, float rms_eps, const uint32_t* __restrict__ hdr, TabLimits lim) {
+  using G = Geo<BF, D>;
+  using St = typename G::St;
+  using EL = Elem<BF>;
+  constexpr int RT = G::RT, CT = G::CT, KB = G::KB, E = G::E, NW = G::NW, P = G::ROWP, FP = D + 4;
+  __shared__ __attribute__((aligned(16))) St sK[kTB * P];  // k'
+  __shared__ __attribute__((aligned(16))) St sV[kTB * P];  // v
+  __shared__ __attribute__((aligned(16))) St sQ[CAUSAL ? kTB * P : 8];  // q'
+  __shared__ __attribute__((aligned(16))) St sG[CAUSAL ? kTB * P : 8];  // dout
+  __shared__ __attribute__((aligned(16))) float sdK[kTB * FP];  // dk' rows; also the weight partials
+  __shared__ float sP[2 * D];  // p after the block (causal: over the later tokens), by block parity
+  __shared__ float sI[kTB], sGd[kTB], sBd[kTB], sW[kTB];
+  __shared__ Frag<BF> sAop[2 * 64], sBop[2 * 64];  // causal, per key tile: A/den and B (queries x keys)
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (!bwd_go(hdr) || seg >= *nseg) return;
+  const SegInfo si = read_seg_clamped(tab, seg, L, lim);
+  if (si.len == 0) return;  // only a corrupted table has empty segments
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+  const int side = tid >> 7, t0 = 2 * ((tid & 127) >> 3), m = tid & 7;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const float* gq = gamma_q + (size_t)h * D;
+  const float* gk = gamma_k + (size_t)h * D;
+  const int wv = wave < NW ? wave : 0;
+  const float* rec = pstates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+
+  floatx4 Pm[RT][CT];  // P: rows = query dims a, columns = this wave's value dims (the record's map)
+  floatx4 PT[RT][CT];  // P^T: rows = value dims, columns = this wave's query dims
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      Pm[rt][ct] = *reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, rt, ct, lane));
+  load_rec_transposed<BF, D>(rec, wv, lane, PT);
+  if (tid < D) sP[tid] = rec[D * D + tid];
+  float dg1[E], dg2[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) dg1[e] = dg2[e] = 0.f;
+  Raw<BF, D> rk;  // key-side lanes: raw k of their tokens (for the map backward)
+
+  const int nblk = (si.len + kTB - 1) / kTB;
+  for (int j = 0; j < nblk; ++j) {
+    const int blk = CAUSAL ? nblk - 1 - j : j;  // causal: from the last block back
+    const int nv = min(kTB, si.len - blk * kTB);
+    const int par = j & 1;
+    const size_t row0 = tok0 + (size_t)blk * kTB;
+    const float2* hr = rope_hi + (size_t)(si.hirow + (blk >> 1)) * G::HALF;
+    const float2* lob = rope_lo + (size_t)(blk & 1) * kTB * G::HALF;
+    const float* pcur = sP + par * D;
+    __syncthreads();  // the previous block's LDS reads are done
+
+    // ---- map: key side k', v rows; query side (causal) q', dout rows and the per-token values
+    if (side == 1) {
+      Raw<BF, D> rv, ok;
+      load_raw<BF, D>(rk, k + row0 * D, t0, m, nv);
+      load_raw<BF, D>(rv, v + row0 * D, t0, m, nv);
+      feature_map_pair<BF, D>(rk, ok, gk, lob, hr, t0, m, rms_eps);
+      store_rows<BF, D>(sK, ok, t0, m);
+      store_rows<BF, D>(sV, rv, t0, m);
+    } else if constexpr (CAUSAL) {
+      Raw<BF, D> rq, rg, oq;
+      load_raw<BF, D>(rq, q + row0 * D, t0, m, nv);
+      load_raw<BF, D>(rg, dout + row0 * D, t0, m, nv);
+      feature_map_pair<BF, D>(rq, oq, gq, lob, hr, t0, m, rms_eps);
+      store_rows<BF, D>(sQ, oq, t0, m);
+      store_rows<BF, D>(sG, rg, t0, m);
+      if (m < 2) {
+        const int t = t0 + m;
+        const bool in = t < nv;
+        const float dn = in ? den[row0 + t] : 1.f, gd = in ? gdp[row0 + t] : 0.f;
+        sI[t] = 1.0f / dn;
+        sGd[t] = gd;
+        sBd[t] = in ? bdp[row0 + t] : 0.f;
+        sW[t] = gd * dn;
+      }
+    }
+    __syncthreads();
+
+    // ---- A (causal): per key tile kt = wave, the operands A/den and B over the block's queries
+    if constexpr (CAUSAL) {
+      if (wave < 2) {
+        const int kt = wave;
+        Frag<BF> Kf[KB], Vf[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          Kf[kb] = lds_frag<BF>(sK, P, 16 * kt + c16, kb, g);
+          Vf[kb] = lds_frag<BF>(sV, P, 16 * kt + c16, kb, g);
+        }
+        floatx4 ad[2], bd[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          ad[tt] = bd[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          if (tt < kt) continue;  // queries before the keys
+          floatx4 s = floatx4{0.f, 0.f, 0.f, 0.f}, gv = s;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            s = mma(lds_frag<BF>(sQ, P, 16 * tt + c16, kb, g), Kf[kb], s);
+            gv = mma(lds_frag<BF>(sG, P, 16 * tt + c16, kb, g), Vf[kb], gv);
+          }
+          // lane (i, g): key 16 kt + i, queries t = 16 tt + 4g + r
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * tt + 4 * g + r;
+            if (tt == kt && 4 * g + r < c16) continue;  // a query before the key
+            const float a = EL::to_f(EL::from_f(s[r]));  // the weight the forward uses
+            ad[tt][r] = a * sI[t];
+            bd[tt][r] = (tt == kt && 4 * g + r == c16) ? sBd[t] : __builtin_fmaf(gv[r], sI[t], sGd[t]);
+          }
+        }
+        sAop[kt * 64 + lane] = acc_frag<BF>(ad[0], ad[1]);
+        sBop[kt * 64 + lane] = acc_frag<BF>(bd[0], bd[1]);
+      }
+      __syncthreads();
+    }
+
+    // ---- B: dk' tiles (to LDS) and dv tiles (to memory); then (causal) P, P^T and p advance
+    if (wave < NW) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int a0 = wave * G::DVW + 16 * ct;
+        OpPair<BF> PTa[KB];  // P^T pairs: rows = this wave's query dims, contraction over value dims
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) PTa[kb] = op_pair<BF, D>(PT[2 * kb][ct], PT[2 * kb + 1][ct]);
+        Frag<BF> Qt;
+        if constexpr (CAUSAL) Qt = lds_frag_t<BF>(sQ, P, 0, a0, lane);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) o = mma_pair<BF>(PTa[kb], lds_frag<BF>(sV, P, 16 * kt + c16, kb, g), o);
+          if constexpr (CAUSAL) o = mma(Qt, sBop[kt * 64 + lane], o);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] += pcur[a0 + 4 * g + i];
+          *reinterpret_cast<floatx4*>(&sdK[(16 * kt + c16) * FP + a0 + 4 * g]) = o;
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        const int c0 = wave * G::DVW + 16 * ct;
+        Frag<BF> Pa[KB];  // P (value rows of this wave, contraction over query dims), rounded once
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) Pa[kb] = acc_frag<BF>(Pm[2 * kb][ct], Pm[2 * kb + 1][ct]);
+        Frag<BF> Gt;
+        if constexpr (CAUSAL) Gt = lds_frag_t<BF>(sG, P, 0, c0, lane);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          floatx4 o = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) o = mma(Pa[kb], lds_frag<BF>(sK, P, 16 * kt + c16, kb, g), o);
+          if constexpr (CAUSAL) o = mma(Gt, sAop[kt * 64 + lane], o);
+          const int i = 16 * kt + c16;  // key row; value columns c0 + 4g .. + 3
+          if (i < nv) {
+            St* dst = dv + (row0 + i) * D + c0 + 4 * g;
+            if constexpr (BF) {
+              *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf2(o[0], o[1]), pack_bf2(o[2], o[3]));
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+            }
+          }
+        }
+      }
+      if constexpr (CAUSAL) {  // P += Q^^T G and P^T += G^T Q^ over the block's queries
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const Frag<BF> qh = scale_slots<BF>(lds_frag_t<BF>(sQ, P, 0, 16 * rt, lane), sI, 0, lane);
+          const Frag<BF> gt = lds_frag_t<BF>(sG, P, 0, 16 * rt, lane);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            Pm[rt][ct] = mma(qh, lds_frag_t<BF>(sG, P, 0, wave * G::DVW + 16 * ct, lane), Pm[rt][ct]);
+            PT[rt][ct] = mma(gt, scale_slots<BF>(lds_frag_t<BF>(sQ, P, 0, wave * G::DVW + 16 * ct, lane), sI, 0, lane),
+                             PT[rt][ct]);
+          }
+        }
+      }
+    }
+    if constexpr (CAUSAL) {  // p for the next block (the other parity): p + sum_t Q^_t (gd den)_t
+      for (int a = tid; a < D; a += NT) {
+        float acc = 0.f;
+        for (int t = 0; t < kTB; ++t) acc = __builtin_fmaf(EL::to_f(EL::from_f(EL::to_f(sQ[t * P + a]) * sI[t])), sW[t], acc);
+        sP[(par ^ 1) * D + a] = pcur[a] + acc;
+      }
+    } else {
+      if (tid < D) sP[(par ^ 1) * D + tid] = pcur[tid];
+    }
+    __syncthreads();
+
+    // ---- C: map backward of k
+    if (side == 1) {
+      Raw<BF, D> dx;
+      map_backward_g<BF, D>(rk, dx, sdK, FP, gk, lob, hr, rms_eps, t0, m, dg1, dg2);
+      store_raw<BF, D>(dx, dk + row0 * D, t0, m, nv);
+    }
+  }
+  __syncthreads();
+  write_dgamma<D, E>(dg1, dg2, wave - 2, side == 1, lane, sdK, dg_part + ((size_t)seg * H + h) * 2 * D + D);
+}
+
+template <bool BF, int D, bool CAUSAL>
+hipError_t run_backward_generic(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s, hipEvent_t* ev) {
+  using St = typename Elem<BF>::St;
+  auto mark = [&](int i) {
+    if (ev != nullptr) (void)hipEventRecord(ev[i], s);
+  };
+  const int fmode = CAUSAL ? SCAN_PREFIX : SCAN_TOTAL;  // what the forward's records hold
+  hipError_t e = hipSuccess;
+  if (b.saved == nullptr) {
+    e = launch_fwd_states(p, a, s, ev, fmode);
+    if (e != hipSuccess) return e;
+  } else {
+    mark(0);
+    e = launch_saved_check(p, b.saved, a.ws, a.cu, fmode, s);
+    if (e != hipSuccess) return e;
+    for (int i = 1; i < 3; ++i) mark(i);
+  }
+  const char* fw = b.saved != nullptr ? b.saved : a.ws;
+  if (p.n_seg_max == 0) {
+    for (int i = 3; i <= kNumBwdKernels; ++i) mark(i);
+    return hipGetLastError();
+  }
+  uint32_t* hdr = reinterpret_cast<uint32_t*>(a.ws);
+  const TabLimits lim{p.packed ? 1 : p.B, p.seg_len, p.n_hi + p.hi_off};
+  const int32_t* tab = reinterpret_cast<const int32_t*>(fw + p.off_tab);
+  const int32_t* nseg = reinterpret_cast<const int32_t*>(fw + p.off_nseg);
+  const float2* rlo = reinterpret_cast<const float2*>(fw + p.off_rope_lo);
+  const float2* rhi = reinterpret_cast<const float2*>(fw + p.off_rope_hi);
+  const float* states = reinterpret_cast<const float*>(fw + p.off_states);
+  float* pstates = reinterpret_cast<float*>(a.ws + p.off_pstates);
+  float* den = reinterpret_cast<float*>(a.ws + p.off_den);
+  float* gd = reinterpret_cast<float*>(a.ws + p.off_gd);
+  float* bd = reinterpret_cast<float*>(a.ws + p.off_bd);
+  float* dgp = reinterpret_cast<float*>(a.ws + p.off_dgpart);
+  const St* q = static_cast<const St*>(a.q);
+  const St* k = static_cast<const St*>(a.k);
+  const St* v = static_cast<const St*>(a.v);
+  const St* g = static_cast<const St*>(b.dout);
+  const dim3 grid(p.n_seg_max, p.H);
+  mark(3);
+  hipLaunchKernelGGL((gbwd_dq_kernel<BF, D, CAUSAL>), grid, dim3(NT), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo,
+                     rhi, states, static_cast<St*>(b.dq), den, gd, bd, pstates, dgp, p.H, p.L, a.rms_eps, a.eps,
+                     static_cast<const uint32_t*>(hdr), lim);
+  mark(4);  // the reverse-state totals come from the dq kernel
+  mark(5);
+  e = launch_scan_records(p, fw, pstates, CAUSAL ? SCAN_SUFFIX : SCAN_TOTAL, hdr, s);
+  if (e != hipSuccess) return e;
+  mark(6);
+  hipLaunchKernelGGL((gbwd_dkv_kernel<BF, D, CAUSAL>), grid, dim3(NT), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo,
+                     rhi, static_cast<const float*>(pstates), static_cast<const float*>(den),
+                     static_cast<const float*>(gd), static_cast<const float*>(bd), static_cast<St*>(b.dk),
+                     static_cast<St*>(b.dv), dgp, p.H, p.L, a.rms_eps, static_cast<const uint32_t*>(hdr), lim);
+  mark(7);
+  if (b.dgamma_q != nullptr || b.dgamma_k != nullptr)
+    hipLaunchKernelGGL(bwd_dgamma_kernel, dim3(p.H), dim3(2 * D), 0, s, dgp, nseg, p.n_seg_max, p.H, D, b.dgamma_q,
+                       b.dgamma_k, static_cast<const uint32_t*>(hdr));
+  mark(8);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s, hipEvent_t* ev) {
   auto mark = [&](int i) {
@@ -1165,7 +1963,7 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   // the workspace of the matching forward (same plan, so the same offsets)
   hipError_t e = hipSuccess;
   if (b.saved == nullptr) {
-    e = launch_fwd_states(p, a, s, ev);
+    e = launch_fwd_states(p, a, s, ev, SCAN_PREFIX);
     if (e != hipSuccess) return e;
   } else {
     // the forward's plan stamp against this plan: the backward kernels run only on a match
@@ -1204,7 +2002,7 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   hipLaunchKernelGGL((bwd_pstate_kernel<D>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
                      pstates, p.H, p.L, a.rms_eps, hdr, lim);
   mark(5);
-  e = launch_scan_suffix(p, fw, pstates, hdr, s);
+  e = launch_scan_records(p, fw, pstates, SCAN_SUFFIX, hdr, s);
   if (e != hipSuccess) return e;
   mark(6);
   hipLaunchKernelGGL((bwd_dkv_ws_kernel<D>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
@@ -1221,11 +2019,18 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
 }  // namespace
 
 hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s, hipEvent_t* ev) {
+  const bool bf = p.dtype == 1, causal = !p.bidirectional;
+#define RLA2_BWD(DD)                                                                                  \
+  if (bf && causal) return run_backward<DD>(p, a, b, s, ev);                                        \
+  if (bf) return run_backward_generic<true, DD, false>(p, a, b, s, ev);                            \
+  return causal ? run_backward_generic<false, DD, true>(p, a, b, s, ev)                             \
+                : run_backward_generic<false, DD, false>(p, a, b, s, ev)
   switch (p.d) {
-    case 32: return run_backward<32>(p, a, b, s, ev);
-    case 64: return run_backward<64>(p, a, b, s, ev);
-    case 128: return run_backward<128>(p, a, b, s, ev);
+    case 32: RLA2_BWD(32);
+    case 64: RLA2_BWD(64);
+    case 128: RLA2_BWD(128);
   }
+#undef RLA2_BWD
   return hipErrorInvalidValue;
 }
 

@@ -101,13 +101,15 @@ struct BwdArgs {
                                // tables, prefix records), or null: the state pass runs again
 };
 
-// prep + chunk state + exclusive-prefix scan of the records (what the backward needs of the
-// forward's state pass; `ev`, optional, gets events 0..2 before the three launches); the
-// reverse scan of a second record set.
-hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev = nullptr);
-// go_hdr: null, or the header whose HDR_GO must be set for the scan to run.
-hipError_t launch_scan_suffix(const Plan& p, const char* ws, float* states, const uint32_t* go_hdr,
-                              hipStream_t s);
+// prep + chunk state + a scan of the records in mode `mode` (what the backward needs of the
+// forward's state pass: SCAN_PREFIX causal, SCAN_TOTAL bidirectional; `ev`, optional, gets
+// events 0..2 before the three launches).
+hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev, int mode);
+// A scan of a record set over the segments of each document (mode SCAN_SUFFIX or SCAN_TOTAL;
+// no initial state, no export); go_hdr: null, or the header whose HDR_GO must be set for the
+// scan to run.
+hipError_t launch_scan_records(const Plan& p, const char* ws, float* states, int mode, const uint32_t* go_hdr,
+                               hipStream_t s);
 // The saved backward's set-up launch: compares the stamp in fwd_ws's header with
 // make_stamp(p, mode) and the checksum of cu, and writes ws's header (flags, HDR_GO).
 hipError_t launch_saved_check(const Plan& p, const char* fwd_ws, char* ws, const int32_t* cu, int mode,

@@ -1991,23 +1991,23 @@ hipError_t launch_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEve
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev) {
+hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev, int mode) {
   const bool bf = p.dtype == 1;
   switch (p.d) {
-    case 32: return bf ? run_states<true, 32>(p, a, s, ev, SCAN_PREFIX) : run_states<false, 32>(p, a, s, ev, SCAN_PREFIX);
-    case 64: return bf ? run_states<true, 64>(p, a, s, ev, SCAN_PREFIX) : run_states<false, 64>(p, a, s, ev, SCAN_PREFIX);
-    case 128: return bf ? run_states<true, 128>(p, a, s, ev, SCAN_PREFIX) : run_states<false, 128>(p, a, s, ev, SCAN_PREFIX);
+    case 32: return bf ? run_states<true, 32>(p, a, s, ev, mode) : run_states<false, 32>(p, a, s, ev, mode);
+    case 64: return bf ? run_states<true, 64>(p, a, s, ev, mode) : run_states<false, 64>(p, a, s, ev, mode);
+    case 128: return bf ? run_states<true, 128>(p, a, s, ev, mode) : run_states<false, 128>(p, a, s, ev, mode);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_scan_suffix(const Plan& p, const char* ws, float* states, const uint32_t* go_hdr,
-                              hipStream_t s) {
+hipError_t launch_scan_records(const Plan& p, const char* ws, float* states, int mode, const uint32_t* go_hdr,
+                               hipStream_t s) {
   const int32_t* docoff = reinterpret_cast<const int32_t*>(ws + p.off_docoff);
   const int D = p.d;
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
   hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
-                     n_tiles, (int)SCAN_SUFFIX, (float*)nullptr, (float*)nullptr, (const float*)nullptr,
+                     n_tiles, mode, (float*)nullptr, (float*)nullptr, (const float*)nullptr,
                      (const float*)nullptr, 0, go_hdr);
   return hipGetLastError();
 }

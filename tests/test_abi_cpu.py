@@ -250,10 +250,11 @@ def test_backward_error_paths():
     full = ctypes.c_size_t(0)
     assert L.rla2_fwd_workspace_size(ctypes.byref(desc()), ctypes.byref(full)) == OK
     assert n.value > full.value                          # a second record set, den, gd and B_tt
-    assert L.rla2_bwd_workspace_size(ctypes.byref(desc(dtype=rla.F32)), ctypes.byref(n)) == UNSUP
-    assert L.rla2_bwd_workspace_size(ctypes.byref(desc(bidirectional=1)), ctypes.byref(n)) == UNSUP
-    assert call(d=desc(dtype=rla.F32)) == UNSUP
-    assert call(d=desc(bidirectional=1)) == UNSUP
+    # fp32 and the bidirectional mode have a backward; the L2 denominator has none
+    assert L.rla2_bwd_workspace_size(ctypes.byref(desc(dtype=rla.F32)), ctypes.byref(n)) == OK
+    assert L.rla2_bwd_workspace_size(ctypes.byref(desc(bidirectional=1)), ctypes.byref(n)) == OK
+    assert L.rla2_bwd_workspace_size(ctypes.byref(desc(denominator=rla.DEN_L2)), ctypes.byref(n)) == UNSUP
+    assert call(d=desc(denominator=rla.DEN_L2)) == UNSUP
     assert call(dout=None) == NULLP
     assert call(dv=None) == NULLP
     assert call(ws=None) == WS
@@ -289,8 +290,7 @@ def test_backward_from_forward_workspace_error_paths():
     st, fwd_bytes = ws_size(desc())
     assert st == OK
     # the mode check comes first, as in rla2_bwd_chunked
-    assert saved_call(d=desc(dtype=rla.F32), fws=None) == UNSUP
-    assert saved_call(d=desc(bidirectional=1), fws=None) == UNSUP
+    assert saved_call(d=desc(denominator=rla.DEN_L2), fws=None) == UNSUP
     assert saved_call(fws=None) == NULLP
     assert saved_call(fws=A + 1536 * MB + 64) == WS                # not 256-byte aligned
     assert saved_call(fws_bytes=fwd_bytes - 256) == WS             # smaller than the forward's workspace
