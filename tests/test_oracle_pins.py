@@ -637,3 +637,71 @@ def test_l2_rows_matches_full():
     for b in range(2):
         np.testing.assert_allclose(oracle.fwd_l2_rows(q, k, v, gq, gk, b, 1, [32, 0, 7], eps=1e-3),
                                    full[b, 1, [0, 7, 32]], rtol=1e-13)
+
+
+def test_l2_initial_state_continues_the_sequence():
+    # RLA page §4.1 (A0, B0 start the first document): the L2 forward of X from the state of
+    # its prefix P -- S = sum k'v^T and A = sum k'k'^T over P -- at position offset |P| equals
+    # the rows of X in the forward over P ++ X; the recurrence started from the same state
+    # agrees; and the quadratic form of the prefix's A is the sum of the squared scores
+    q, k, v, gq, gk, _ = _rand_case(1, 2, 17, 6, 91, None)
+    nP = 7
+    P = (slice(None), slice(None), slice(0, nP))
+    X = (slice(None), slice(None), slice(nP, None))
+    whole = oracle.fwd_l2(q, k, v, gq, gk, eps=1e-3)
+    S, _ = oracle.state_from_prefix(k[P], v[P], gk)
+    A = oracle.second_state_from_prefix(k[P], gk)
+    cont = oracle.fwd_l2(q[X], k[X], v[X], gq, gk, eps=1e-3, initial_S=S[0], initial_A=A[0], initial_pos=nP)
+    np.testing.assert_allclose(cont, whole[X], rtol=1e-11, atol=1e-13)
+    rec = oracle.fwd_l2_recurrent(q[X], k[X], v[X], gq, gk, eps=1e-3, initial_S=S[0], initial_A=A[0],
+                                  initial_pos=nP)
+    np.testing.assert_allclose(rec, cont, rtol=1e-11, atol=1e-13)
+    r = np.random.default_rng(92)
+    for h in range(2):
+        kp = oracle.feature_map(k[0, h, :nP], gk[h], np.arange(nP))
+        x = np.abs(r.normal(size=6))
+        np.testing.assert_allclose(x @ A[0, h] @ x, ((kp @ x) ** 2).sum(), rtol=1e-12)
+    # packed: the initial state starts document 0 only
+    cu = np.array([0, 5, 17])
+    S0, A0 = np.abs(r.normal(size=(2, 6, 6))), np.abs(r.normal(size=(2, 6, 6)))
+    with_init = oracle.fwd_l2(q, k, v, gq, gk, cu, initial_S=S0, initial_A=A0, initial_pos=4)
+    without = oracle.fwd_l2(q, k, v, gq, gk, cu)
+    np.testing.assert_array_equal(with_init[:, :, 5:], without[:, :, 5:])
+    assert not np.allclose(with_init[:, :, :5], without[:, :, :5])
+
+
+def test_l2_bidirectional_mode():
+    # causal=false (RLA page §4.1): every row is the read-out of its document's whole states,
+    # q' S / (sqrt(q' A q') + eps), formed here from the state sums; the last row of each
+    # document equals the causal output there; documents stay isolated; a later token changes
+    # an earlier row
+    q, k, v, gq, gk, cu = _rand_case(1, 2, 23, 8, 93, [7, 16])
+    r = np.random.default_rng(94)
+    S0 = np.abs(r.normal(size=(2, 8, 8)))
+    A0 = np.abs(r.normal(size=(2, 8, 8)))
+    A0 = A0 @ A0.transpose(0, 2, 1)
+    for init in ({}, dict(initial_S=S0, initial_A=A0, initial_pos=3)):
+        bi = oracle.fwd_l2(q, k, v, gq, gk, cu, causal=False, **init)
+        ca = oracle.fwd_l2(q, k, v, gq, gk, cu, **init)
+        St, _ = oracle.state_from_prefix(k, v, gk, cu, initial_S=init.get("initial_S"), initial_pos=init.get(
+            "initial_pos", 0))
+        At = oracle.second_state_from_prefix(k, gk, cu, initial_A=init.get("initial_A"),
+                                             initial_pos=init.get("initial_pos", 0))
+        for j, (_, s0, s1) in enumerate(oracle.documents(1, 23, cu)):
+            start = init.get("initial_pos", 0) if j == 0 else 0
+            for h in range(2):
+                qp = oracle.feature_map(q[0, h, s0:s1], gq[h], start + np.arange(s1 - s0))
+                quad = np.einsum("ta,ab,tb->t", qp, At[j, h], qp)
+                ref = (qp @ St[j, h]) / (np.sqrt(quad) + oracle.DEFAULT_L2_EPS)[:, None]
+                np.testing.assert_allclose(bi[0, h, s0:s1], ref, rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(bi[0, :, s1 - 1], ca[0, :, s1 - 1], rtol=1e-12, atol=1e-14)
+        rows = [0, 6, 7, 15, 22]
+        for h in range(2):
+            np.testing.assert_allclose(oracle.fwd_l2_rows(q, k, v, gq, gk, 0, h, rows, cu, causal=False, **init),
+                                       bi[0, h, rows], rtol=1e-13, atol=1e-15)
+    v2 = v.copy()
+    v2[0, :, 20] += 5.0
+    a = oracle.fwd_l2(q, k, v2, gq, gk, cu, causal=False)
+    b = oracle.fwd_l2(q, k, v, gq, gk, cu, causal=False)
+    assert not np.allclose(a[0, :, 8], b[0, :, 8])
+    np.testing.assert_array_equal(a[0, :, :7], b[0, :, :7])
