@@ -110,17 +110,25 @@ typedef enum rla2_dtype { RLA2_F32 = 0, RLA2_BF16 = 1 } rla2_dtype;
  *               initial_pos + L must fit in int32 (RLA2_ERR_BAD_VALUE otherwise).
  *  denominator  RLA2_DEN_SUM (0): the RLA-2 denominator q'_t . z_t + eps (RLA page
  *               §3). RLA2_DEN_L2 (1): the original RLA's L2 denominator (RLA page
- *               §2.1), out_t = sum_{i<=t} s_ti v_i / (sqrt(sum_{i<=t} s_ti^2) + eps),
- *               s_ti = q'_t . k'_i over the same causal same-document range, formed
- *               from the second state A_t = sum_{i<=t} k'_i k'_i^T (RLA page §4.1):
- *               sum_i s_ti^2 = q'_t^T A_t q'_t; the page's eps for it is 1e-6. The L2
- *               mode is a causal forward only: with bidirectional = 1, an initial
- *               state or initial_pos != 0 the forward returns RLA2_ERR_UNSUPPORTED,
- *               and so does the backward. The state build ignores it (S and z do not
- *               depend on the denominator). Other values return RLA2_ERR_BAD_VALUE.
+ *               §2.1), out_t = sum_i s_ti v_i / (sqrt(sum_i s_ti^2) + eps),
+ *               s_ti = q'_t . k'_i over the same key range (causal or the whole
+ *               document), formed from the second state A = sum_i k'_i k'_i^T (RLA
+ *               page §4.1): sum_i s_ti^2 = q'_t^T A q'_t; the page's eps for it is
+ *               1e-6. The backward of the L2 mode is not built (RLA2_ERR_UNSUPPORTED).
+ *               Other values return RLA2_ERR_BAD_VALUE.
+ *  initial_A    L2 mode only (RLA2_ERR_BAD_VALUE otherwise): optional DEVICE fp32
+ *               [H, d, d], the second state A0 that starts the first document of each
+ *               row with initial_S (RLA page §4.1: A0 and B0 together; with an initial
+ *               state in the L2 mode it is required, RLA2_ERR_NULL_POINTER otherwise).
+ *               Read only; symmetric in exact arithmetic (A0[a][b] = sum k'[a] k'[b]).
+ *  final_A      L2 mode only (RLA2_ERR_BAD_VALUE otherwise): optional DEVICE fp32
+ *               [N, H, d, d] output, each document's second state after its last token
+ *               (plus initial_A for the first document of each row): written by
+ *               rla2_fwd_chunked and by rla2_state_from_prefix; NULL = not exported.
  * The number of documents N is n_docs with cu_seqlens, B without.
  * A zero-initialised descriptor tail (bidirectional = initial_pos = 0, NULL
- * initial state, denominator = RLA2_DEN_SUM) is the plain causal forward.
+ * initial state, denominator = RLA2_DEN_SUM, NULL initial_A and final_A) is the plain
+ * causal forward.
  */
 typedef struct rla2_fwd_desc {
   int32_t B, H, L, d;
@@ -135,6 +143,8 @@ typedef struct rla2_fwd_desc {
   const float* initial_S;
   const float* initial_z;
   int32_t denominator;
+  const float* initial_A;
+  float* final_A;
 } rla2_fwd_desc;
 
 #define RLA2_DEN_SUM 0
@@ -252,7 +262,9 @@ rla2_status rla2_state_from_prefix_workspace_size(const rla2_fwd_desc* desc, siz
  * S = sum_i k'_i (x) v_i, z = sum_i k'_i (RLA page §3 state; §4.2 forward_step
  * keeps exactly this pair as its cache). q is not needed. The first document of
  * each row starts from desc->initial_S/initial_z at desc->initial_pos, as in the
- * forward; desc->bidirectional is validated but does not change the result.
+ * forward; desc->bidirectional is validated but does not change the result. In the L2
+ * mode a non-NULL desc->final_A also receives each document's second state
+ * A = sum_i k'_i k'_i^T (starting from desc->initial_A): the cache of an L2 continuation.
  *  k, v     [B, H, L, d] dtype (packed [1, H, T, d] with cu_seqlens).
  *  gamma_k  [H, d] fp32.
  *  S        [N, H, d, d] fp32, written.   z  [N, H, d] fp32, written.

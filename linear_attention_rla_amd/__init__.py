@@ -55,7 +55,8 @@ class FwdDesc(ctypes.Structure):
                 ("eps", ctypes.c_float), ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
                 ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
                 ("bidirectional", ctypes.c_int32), ("initial_pos", ctypes.c_int32),
-                ("initial_S", ctypes.c_void_p), ("initial_z", ctypes.c_void_p), ("denominator", ctypes.c_int32)]
+                ("initial_S", ctypes.c_void_p), ("initial_z", ctypes.c_void_p), ("denominator", ctypes.c_int32),
+                ("initial_A", ctypes.c_void_p), ("final_A", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -163,11 +164,12 @@ def _after(workspace: torch.Tensor, nbytes: int, where: str):
 
 def make_desc(B, H, L, d, dtype, cu_seqlens=None, n_docs=0, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
               rope_base=10000.0, bidirectional=False, initial_pos=0, initial_S=None, initial_z=None,
-              denominator=DEN_SUM) -> FwdDesc:
-    return FwdDesc(B, H, L, d, dtype, chunk, seg_chunks, eps, rms_eps, rope_base,
-                   None if cu_seqlens is None else cu_seqlens.data_ptr(), n_docs, int(bool(bidirectional)),
-                   initial_pos, None if initial_S is None else initial_S.data_ptr(),
-                   None if initial_z is None else initial_z.data_ptr(), denominator)
+              denominator=DEN_SUM, initial_A=None, final_A=None) -> FwdDesc:
+    def ptr(t):
+        return None if t is None else t.data_ptr()
+    return FwdDesc(B, H, L, d, dtype, chunk, seg_chunks, eps, rms_eps, rope_base, ptr(cu_seqlens), n_docs,
+                   int(bool(bidirectional)), initial_pos, ptr(initial_S), ptr(initial_z), denominator,
+                   ptr(initial_A), ptr(final_A))
 
 
 def _initial_state(x: torch.Tensor, initial_S, initial_z):
@@ -183,7 +185,8 @@ def _initial_state(x: torch.Tensor, initial_S, initial_z):
 
 
 def _fwd_desc(x: torch.Tensor, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base, bidirectional=False,
-              initial_pos=0, initial_S=None, initial_z=None, denominator=DEN_SUM) -> FwdDesc:
+              initial_pos=0, initial_S=None, initial_z=None, denominator=DEN_SUM, initial_A=None,
+              final_A=None) -> FwdDesc:
     if x.dim() != 4:
         raise ValueError("expected [B, H, L, d]")
     if x.dtype not in _DTYPES:
@@ -194,8 +197,12 @@ def _fwd_desc(x: torch.Tensor, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope
         _check_dev("cu_seqlens", cu_seqlens, torch.int32)
         n_docs = cu_seqlens.numel() - 1
     _initial_state(x, initial_S, initial_z)
+    if initial_A is not None:
+        _check_dev("initial_A", initial_A, torch.float32)
+        if initial_A.shape != (H, d, d):
+            raise ValueError("initial_A must be [H, d, d]")
     return make_desc(B, H, L, d, _DTYPES[x.dtype], cu_seqlens, n_docs, chunk, seg_chunks, eps, rms_eps, rope_base,
-                     bidirectional, initial_pos, initial_S, initial_z, denominator)
+                     bidirectional, initial_pos, initial_S, initial_z, denominator, initial_A, final_A)
 
 
 def fwd_workspace_size(desc: FwdDesc) -> int:
@@ -209,13 +216,14 @@ def fwd_workspace_size(desc: FwdDesc) -> int:
 def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=None, rms_eps=1e-6,
         rope_base=10000.0, return_final_state=False, out=None, workspace=None, events=None,
         bidirectional=False, initial_S=None, initial_z=None, initial_pos=0, l2_denominator=False,
-        no_alloc=False):
+        no_alloc=False, initial_A=None, return_final_A=False):
     """Chunked RLA-2 forward (causal, or bidirectional). Returns ``out`` or
     ``(out, final_S, final_z)``.
 
     ``l2_denominator``: the original RLA's ``sqrt(sum_i s_ti^2) + eps`` in place of the Sum
-    denominator (causal, no initial state or offset). ``eps`` defaults to 1e-4 (Sum) or
-    1e-6 (L2).
+    denominator; its second state starts from ``initial_A [H, d, d]`` (with ``initial_S``),
+    and ``return_final_A`` appends each document's final second state to the result.
+    ``eps`` defaults to 1e-4 (Sum) or 1e-6 (L2).
 
     ``initial_S [H, d, d]``, ``initial_z [H, d]`` (fp32, optional, together) start the
     first document of each row, whose positions begin at ``initial_pos``.
@@ -229,15 +237,19 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
     _check_dev("gamma_k", gamma_k, torch.float32)
     if eps is None:
         eps = L2_EPS if l2_denominator else 1e-4
+    B, H, L, d = q.shape
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    fA = None
+    if return_final_A:
+        fA = torch.empty(N, H, d, d, dtype=torch.float32, device=q.device)
     desc = _fwd_desc(q, cu_seqlens, chunk, seg_chunks, eps, rms_eps, rope_base, bidirectional, initial_pos,
-                     initial_S, initial_z, DEN_L2 if l2_denominator else DEN_SUM)
+                     initial_S, initial_z, DEN_L2 if l2_denominator else DEN_SUM, initial_A, fA)
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError("q, k, v shapes differ")
     if gamma_q.shape != (desc.H, desc.d) or gamma_k.shape != (desc.H, desc.d):
         raise ValueError("gamma_q and gamma_k must be [H, d]")
     if out is None:
         out = torch.empty_like(q)
-    N = desc.n_docs if cu_seqlens is not None else desc.B
     fS = fz = None
     if return_final_state:
         fS = torch.empty(N, desc.H, desc.d, desc.d, dtype=torch.float32, device=q.device)
@@ -249,7 +261,7 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
                                             _ptr(gamma_k), _ptr(out), _ptr(fS), _ptr(fz), _stream(q.device))
         if st:
             raise Rla2Error(st, "rla2_fwd_chunked_noalloc")
-        return (out, fS, fz) if return_final_state else out
+        return _fwd_result(out, fS, fz, fA, return_final_state, return_final_A)
     nbytes = fwd_workspace_size(desc)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
@@ -262,20 +274,29 @@ def fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, e
     if st:
         raise Rla2Error(st, "rla2_fwd_chunked")
     _after(workspace, nbytes, "rla2_fwd_chunked")
-    return (out, fS, fz) if return_final_state else out
+    return _fwd_result(out, fS, fz, fA, return_final_state, return_final_A)
+
+
+def _fwd_result(out, fS, fz, fA, with_state, with_A):
+    res = (out,) + ((fS, fz) if with_state else ()) + ((fA,) if with_A else ())
+    return res if len(res) > 1 else out
 
 
 def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0, rms_eps=1e-6,
                       rope_base=10000.0, S=None, z=None, workspace=None, initial_S=None, initial_z=None,
-                      initial_pos=0):
+                      initial_pos=0, l2_second_state=False, initial_A=None):
     """Per-document state after its last token (starting from the optional initial
-    state for the first document of each row). Returns ``(S, z)``."""
+    state for the first document of each row). Returns ``(S, z)``, or ``(S, z, A)`` with
+    ``l2_second_state`` (the L2 mode's A = sum k'k'^T, starting from ``initial_A``)."""
     _check_dev("k", k)
     _check_dev("v", v, k.dtype)
     _check_dev("gamma_k", gamma_k, torch.float32)
+    B, H, L, d = k.shape
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else B
+    A = torch.empty(N, H, d, d, dtype=torch.float32, device=k.device) if l2_second_state else None
     desc = _fwd_desc(k, cu_seqlens, chunk, seg_chunks, 1e-4, rms_eps, rope_base, False, initial_pos,
-                     initial_S, initial_z)
-    N = desc.n_docs if cu_seqlens is not None else desc.B
+                     initial_S, initial_z, DEN_L2 if (l2_second_state or initial_A is not None) else DEN_SUM,
+                     initial_A, A)
     if S is None:
         S = torch.empty(N, desc.H, desc.d, desc.d, dtype=torch.float32, device=k.device)
     if z is None:
@@ -291,7 +312,7 @@ def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0,
     if st:
         raise Rla2Error(st, "rla2_state_from_prefix")
     _after(workspace, n.value, "rla2_state_from_prefix")
-    return S, z
+    return (S, z, A) if l2_second_state else (S, z)
 
 
 def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,

@@ -16,7 +16,7 @@ namespace {
 
 using rla2::Plan;
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 
 // Poll bound of the MMA waves' meetings inside the warp-specialised kernels (a debug hook
 // lets tests lower it; see rla2_debug_set_wait_polls).
@@ -80,6 +80,10 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   if (d->initial_pos < 0 || (long long)d->initial_pos + d->L > INT32_MAX) return RLA2_ERR_BAD_VALUE;
   if ((d->initial_S == nullptr) != (d->initial_z == nullptr)) return RLA2_ERR_NULL_POINTER;
   if (d->denominator != RLA2_DEN_SUM && d->denominator != RLA2_DEN_L2) return RLA2_ERR_BAD_VALUE;
+  // the second state exists in the L2 mode only, and there starts with the first state
+  if (d->denominator != RLA2_DEN_L2 && (d->initial_A != nullptr || d->final_A != nullptr)) return RLA2_ERR_BAD_VALUE;
+  if (d->denominator == RLA2_DEN_L2 && (d->initial_S == nullptr) != (d->initial_A == nullptr))
+    return RLA2_ERR_NULL_POINTER;
   // every token index and every segment index must stay within int32 on device
   const long long tokens = (long long)d->B * d->L;
   if (tokens > INT32_MAX || (long long)d->B * d->H > INT32_MAX) return RLA2_ERR_BAD_SHAPE;
@@ -330,8 +334,6 @@ rla2_status rla2_fwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   Plan p;
   rla2_status st = plan_desc(desc, &p);
   if (st != RLA2_OK) return st;
-  // the L2 denominator is built for the plain causal forward only
-  if (p.l2 && (p.bidirectional || desc->initial_S != nullptr || p.initial_pos != 0)) return RLA2_ERR_UNSUPPORTED;
   const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
   const size_t gam = (size_t)p.H * p.d * 4;
   const size_t fsb = (size_t)p.n_docs * p.H * p.d * p.d * 4;
@@ -343,17 +345,21 @@ rla2_status rla2_fwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   if (p.bytes > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return RLA2_ERR_WORKSPACE;
   if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
     return RLA2_ERR_WORKSPACE;
-  if (misaligned({q, k, v, out, gamma_q, gamma_k, final_S, final_z, desc->initial_S, desc->initial_z}))
+  if (misaligned({q, k, v, out, gamma_q, gamma_k, final_S, final_z, desc->initial_S, desc->initial_z,
+                  desc->initial_A, desc->final_A}))
     return RLA2_ERR_MISALIGNED;
-  const Range o{out, act}, fs{final_S, fsb}, fz{final_z, fzb}, ws{workspace, p.bytes};
+  const Range o{out, act}, fs{final_S, fsb}, fz{final_z, fzb}, fa{desc->final_A, fsb}, ws{workspace, p.bytes};
   const Range ins[] = {{q, act}, {k, act}, {v, act}, {gamma_q, gam}, {gamma_k, gam},
                        {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4},
-                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4}};
+                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4},
+                       {desc->initial_A, (size_t)p.H * p.d * p.d * 4}};
+  const Range outs[] = {o, fs, fz, fa, ws};
   for (const Range& r : ins)
-    if (overlap(o, r) || overlap(fs, r) || overlap(fz, r) || overlap(ws, r)) return RLA2_ERR_ALIAS;
-  if (overlap(o, fs) || overlap(o, fz) || overlap(fs, fz) || overlap(o, ws) || overlap(fs, ws) ||
-      overlap(fz, ws))
-    return RLA2_ERR_ALIAS;
+    for (const Range& x : outs)
+      if (overlap(x, r)) return RLA2_ERR_ALIAS;
+  for (size_t i = 0; i < 5; ++i)
+    for (size_t j = i + 1; j < 5; ++j)
+      if (overlap(outs[i], outs[j])) return RLA2_ERR_ALIAS;
   if (p.packed && validate_mode() == 1) {
     st = check_seqlens(p, desc->cu_seqlens, stream);
     if (st != RLA2_OK) return st;
@@ -361,7 +367,7 @@ rla2_status rla2_fwd_chunked_profiled(const rla2_fwd_desc* desc, const void* q, 
   if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
   rla2::FwdArgs a{desc->cu_seqlens, q, k, v, gamma_q, gamma_k, out, final_S, final_z,
                   desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
-                  static_cast<char*>(workspace)};
+                  static_cast<char*>(workspace), desc->initial_A, desc->final_A};
   return finish(rla2::launch_chunked(p, a, stream, events));
 }
 
@@ -381,13 +387,19 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
   if (p.bytes > 0 && (workspace == nullptr || workspace_bytes < p.bytes)) return RLA2_ERR_WORKSPACE;
   if (workspace != nullptr && (reinterpret_cast<uintptr_t>(workspace) % rla2::kAlign) != 0)
     return RLA2_ERR_WORKSPACE;
-  if (misaligned({k, v, gamma_k, S, z, desc->initial_S, desc->initial_z})) return RLA2_ERR_MISALIGNED;
-  const Range rs{S, sb}, rz{z, zb}, ws{workspace, p.bytes};
+  if (misaligned({k, v, gamma_k, S, z, desc->initial_S, desc->initial_z, desc->initial_A, desc->final_A}))
+    return RLA2_ERR_MISALIGNED;
+  const Range rs{S, sb}, rz{z, zb}, ra{desc->final_A, sb}, ws{workspace, p.bytes};
   const Range ins[] = {{k, act}, {v, act}, {gamma_k, gam}, {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4},
-                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4}};
+                       {desc->initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->initial_z, (size_t)p.H * p.d * 4},
+                       {desc->initial_A, (size_t)p.H * p.d * p.d * 4}};
+  const Range outs[] = {rs, rz, ra, ws};
   for (const Range& r : ins)
-    if (overlap(rs, r) || overlap(rz, r) || overlap(ws, r)) return RLA2_ERR_ALIAS;
-  if (overlap(rs, rz) || overlap(rs, ws) || overlap(rz, ws)) return RLA2_ERR_ALIAS;
+    for (const Range& x : outs)
+      if (overlap(x, r)) return RLA2_ERR_ALIAS;
+  for (size_t i = 0; i < 4; ++i)
+    for (size_t j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return RLA2_ERR_ALIAS;
   if (p.packed && validate_mode() == 1) {
     st = check_seqlens(p, desc->cu_seqlens, stream);
     if (st != RLA2_OK) return st;
@@ -395,7 +407,7 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
   if (p.n_docs == 0 || p.H == 0) return RLA2_OK;
   rla2::FwdArgs a{desc->cu_seqlens, nullptr, k, v, nullptr, gamma_k, nullptr, S, z,
                   desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
-                  static_cast<char*>(workspace)};
+                  static_cast<char*>(workspace), desc->initial_A, desc->final_A};
   return finish(rla2::launch_chunked(p, a, stream));
 }
 

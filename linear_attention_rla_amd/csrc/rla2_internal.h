@@ -85,6 +85,8 @@ struct FwdArgs {
   const float *init_S, *init_z;  // optional initial state, [H, d, d] and [H, d]
   float eps, rms_eps, rope_base;
   char* ws;
+  const float* init_A = nullptr;  // L2 mode: optional initial second state, [H, d, d]
+  float* final_A = nullptr;       // L2 mode: optional export of the second state, [N, H, d, d]
 };
 
 // Launch the whole chunked forward (out != null) or the state build (out == null).

@@ -530,7 +530,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
     if (e < D * D) {
       const float* src = init_S + (size_t)h * D * D + (size_t)row * D + col;
       run = make_float4(src[0], src[D], src[2 * D], src[3 * D]);
-    } else {
+    } else if (init_z != nullptr) {  // (the L2 mode's A records have no z: it stays zero)
       run = *reinterpret_cast<const float4*>(init_z + (size_t)h * D + (e - D * D));
     }
   }
@@ -1654,6 +1654,117 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
 }
 
 // ----------------------------------------------------------------------------------------
+// readout_l2 (bidirectional forward with the original RLA's L2 denominator): per (segment,
+// head), every token reads its document's whole states, out_t = q'_t S_doc / (sqrt(q'_t^T
+// A_doc q'_t) + eps) (RLA page §2.1 closed form over the whole document, §4.1 causal=false).
+// Both document states arrive in the segment's records (S, then A); the state waves round them
+// once to the MFMA operand type. Per 64-token block: every lane maps two tokens of q into LDS;
+// wave w < NW forms O^T = S^T Q'^T and A^T Q'^T for its columns, dots the latter with q' for its
+// part of the quadratic form; after a barrier the rows are scaled and written.
+
+template <bool BF, int D>
+__global__ __launch_bounds__(NT, (D == 128) ? 1 : 2) void readout_l2_kernel(
+    const typename Elem<BF>::St* __restrict__ q, const float* __restrict__ gamma_q, const int32_t* __restrict__ tab,
+    const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
+    const float* __restrict__ states, const float* __restrict__ astates, typename Elem<BF>::St* __restrict__ out,
+    int H, int L, float rms_eps, float eps) {
+  using G = Geo<BF, D>;
+  using St = typename G::St;
+  using EL = Elem<BF>;
+  __shared__ __attribute__((aligned(16))) St sQ[kChunk * G::ROWP];
+  __shared__ float sQuad[4 * kChunk];
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t0 = 2 * (tid >> 3), m = tid & 7;
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const float* gq = gamma_q + (size_t)h * D;
+  const int wv = wave < G::NW ? wave : 0;  // waves without state columns keep a harmless copy
+  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  const float* arec = astates + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  Frag<BF> Sa[G::KB][G::CT], Aa[G::KB][G::CT];  // S^T, A^T (= A) as A operands, this wave's columns
+#pragma unroll
+  for (int kb2 = 0; kb2 < G::KB; ++kb2)
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+      auto tile = [&](const float* r, int rt) {
+        return *reinterpret_cast<const floatx4*>(r + rec_frag<BF, D>(wv, rt, ct, lane));
+      };
+      Sa[kb2][ct] = acc_frag<BF>(tile(rec, 2 * kb2), tile(rec, 2 * kb2 + 1));
+      Aa[kb2][ct] = acc_frag<BF>(tile(arec, 2 * kb2), tile(arec, 2 * kb2 + 1));
+    }
+  const int nblk = (si.len + kChunk - 1) / kChunk;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int nv = min(kChunk, si.len - blk * kChunk);
+    __syncthreads();  // the previous block's LDS reads are done
+    {
+      Raw<BF, D> rq, oq;
+      load_raw<BF, D>(rq, q + (tok0 + (size_t)blk * kChunk) * D, t0, m, nv);
+      feature_map_pair<BF, D>(rq, oq, gq, rope_lo, rope_hi + (size_t)(si.hirow + blk) * G::HALF, t0, m, rms_eps);
+      store_rows<BF, D>(sQ, oq, t0, m);
+    }
+    __syncthreads();
+    floatx4 o[G::CT][4];
+    if (wave < G::NW) {
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ct = 0; ct < G::CT; ++ct) {
+        const int col = wave * G::DVW + ct * 16 + 4 * g;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          floatx4 x = floatx4{0.f, 0.f, 0.f, 0.f}, y = x;
+#pragma unroll
+          for (int kb2 = 0; kb2 < G::KB; ++kb2) {
+            const Frag<BF> qf = lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g);
+            x = mma(Sa[kb2][ct], qf, x);
+            y = mma(Aa[kb2][ct], qf, y);
+          }
+          o[ct][tt] = x;
+          const St* qrow = sQ + (tt * 16 + c16) * G::ROWP + col;  // q'_t at dims col .. col + 3
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part[tt] = __builtin_fmaf(EL::to_f(qrow[i]), y[i], part[tt]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const float pp = sum_rows4(part[tt]);
+        if (g == 0) sQuad[wave * kChunk + tt * 16 + c16] = pp;
+      }
+    }
+    __syncthreads();
+    if (wave < G::NW) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int t = tt * 16 + c16;
+        float quad = 0.f;
+#pragma unroll
+        for (int w = 0; w < G::NW; ++w) quad += sQuad[w * kChunk + t];
+        const float r = 1.0f / (__builtin_sqrtf(quad) + eps);
+        if (t < nv) {
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) {
+            const int col = wave * G::DVW + ct * 16 + 4 * g;
+            St* dst = out + (tok0 + (size_t)blk * kChunk + t) * D + col;
+            const floatx4 x = o[ct][tt];
+            if constexpr (BF) {
+              const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{x[0] * r, x[1] * r}, bf16x2));
+              const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{x[2] * r, x[3] * r}, bf16x2));
+              *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+            } else {
+              *reinterpret_cast<float4*>(dst) = make_float4(x[0] * r, x[1] * r, x[2] * r, x[3] * r);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------------------
 // feature_map: the preamble alone, x' = ReLU(RoPE(RMSNorm(x))) materialised. Per (segment,
 // head, tensor): the same lane mapping and device functions as the chunk kernels (two
 // tokens per 8 lanes), so x' is bitwise what the forward forms internally; raw x and the
@@ -1863,12 +1974,12 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
                      p.seg_len, p.n_seg_max, tab, docoff, nseg, rlo, rhi, half, D, p.n_hi, p.hi_off, p.initial_pos,
                      a.rope_base, reinterpret_cast<uint32_t*>(a.ws), make_stamp(p, mode));
   mark(1);
-  // the L2 forward also needs the records of A = sum k'k'^T
-  const bool l2 = p.l2 && a.out != nullptr;
+  // the L2 forward (and the export of its final A) also needs the records of A = sum k'k'^T
+  const bool l2 = p.l2 && (a.out != nullptr || a.final_A != nullptr);
   float* astates = reinterpret_cast<float*>(a.ws + p.off_astates);
   // The exclusive prefixes never read the total of a document's last segment: unless the
   // final states are exported, that segment's state is not formed.
-  const bool want_final = a.final_S != nullptr || a.final_z != nullptr;
+  const bool want_final = a.final_S != nullptr || a.final_z != nullptr || a.final_A != nullptr;
   const int skip_last = mode == SCAN_PREFIX && !want_final;
   if (p.n_seg_max > 0) {
     if (l2 && BF) {
@@ -1892,10 +2003,10 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
                        n_tiles, mode, a.final_S, a.final_z, a.init_S, a.init_z, p.packed ? 0 : 1,
                        static_cast<const uint32_t*>(nullptr));
   }
-  if (l2 && mode == SCAN_PREFIX && p.n_seg_max > 0) {  // exclusive prefixes of A as well
+  if (l2 && (a.final_A != nullptr || (mode != SCAN_NONE && p.n_seg_max > 0))) {  // A the same way, from A0
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, astates, docoff, p.H, D,
-                       n_tiles, (int)SCAN_PREFIX, (float*)nullptr, (float*)nullptr, (const float*)nullptr,
-                       (const float*)nullptr, 0, static_cast<const uint32_t*>(nullptr));
+                       n_tiles, mode, a.final_A, (float*)nullptr, a.init_A, (const float*)nullptr,
+                       p.packed ? 0 : 1, static_cast<const uint32_t*>(nullptr));
   }
   return hipGetLastError();
 }
@@ -1916,7 +2027,12 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   hipError_t e = run_states<BF, D>(p, a, s, ev, mode);
   if (e != hipSuccess) return e;
   mark(3);
-  if (fwd && p.n_seg_max > 0 && p.bidirectional) {
+  if (fwd && p.n_seg_max > 0 && p.bidirectional && p.l2) {
+    hipLaunchKernelGGL((readout_l2_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                       static_cast<const St*>(a.q), a.gq, tab, nseg, rlo, rhi, states,
+                       reinterpret_cast<const float*>(a.ws + p.off_astates), static_cast<St*>(a.out), p.H, p.L,
+                       a.rms_eps, a.eps);
+  } else if (fwd && p.n_seg_max > 0 && p.bidirectional) {
     hipLaunchKernelGGL((readout_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s, static_cast<const St*>(a.q),
                        a.gq, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
   } else if (fwd && p.n_seg_max > 0) {

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = rla.lib()
-    assert L.rla2_abi_version() == 4
+    assert L.rla2_abi_version() == 5
     for code, name in rla.STATUS.items():
         assert L.rla2_status_string(code).decode().startswith(name)
     assert L.rla2_status_string(99).decode() == "RLA2_ERR_UNKNOWN"
@@ -53,9 +53,11 @@ def desc(**kw):
     base.update(kw)
     cu = base.pop("cu_seqlens")
     init_S, init_z = base.pop("initial_S", None), base.pop("initial_z", None)
+    init_A, final_A = base.pop("initial_A", None), base.pop("final_A", None)
     d = rla.FwdDesc(**{k: v for k, v in base.items()})
     d.cu_seqlens = cu
     d.initial_S, d.initial_z = init_S, init_z
+    d.initial_A, d.final_A = init_A, final_A
     return d
 
 
@@ -127,15 +129,26 @@ def test_fwd_error_paths():
 
 
 def test_l2_denominator_paths():
-    # the L2 mode needs a second record set (A = sum k'k'^T): a larger workspace; it is a plain
-    # causal forward only, and the backward rejects it
+    # the L2 mode needs a second record set (A = sum k'k'^T): a larger workspace; its second
+    # state starts with the first one (initial_A with initial_S) and exists in this mode only;
+    # the backward rejects it
     st, plain = ws_size(desc())
     st2, l2 = ws_size(desc(denominator=rla.DEN_L2))
     assert st == st2 == OK and l2 > plain
     assert fwd_call(desc(denominator=rla.DEN_L2), ws_bytes=plain) == WS
-    assert fwd_call(desc(denominator=rla.DEN_L2, bidirectional=1)) == UNSUP
-    assert fwd_call(desc(denominator=rla.DEN_L2, initial_pos=5)) == UNSUP
-    assert fwd_call(desc(denominator=rla.DEN_L2, initial_S=A + 400 * MB, initial_z=A + 401 * MB)) == UNSUP
+    init = dict(initial_S=A + 400 * MB, initial_z=A + 401 * MB)
+    assert ws_size(desc(denominator=rla.DEN_L2, bidirectional=1))[0] == OK
+    assert ws_size(desc(denominator=rla.DEN_L2, initial_pos=5))[0] == OK
+    assert ws_size(desc(denominator=rla.DEN_L2, **init))[0] == NULLP               # A0 missing
+    assert ws_size(desc(denominator=rla.DEN_L2, initial_A=A + 402 * MB))[0] == NULLP  # S0 missing
+    assert ws_size(desc(denominator=rla.DEN_L2, initial_A=A + 402 * MB, **init))[0] == OK
+    assert ws_size(desc(initial_A=A + 402 * MB, **init))[0] == VALUE              # no A in the Sum mode
+    assert ws_size(desc(final_A=A + 402 * MB))[0] == VALUE
+    l2i = desc(denominator=rla.DEN_L2, initial_A=A + 402 * MB, **init)
+    assert fwd_call(l2i, out=A + 402 * MB) == ALIAS                               # output over A0
+    assert fwd_call(desc(denominator=rla.DEN_L2, final_A=A + 64 * MB)) == ALIAS    # A export over k
+    assert fwd_call(desc(denominator=rla.DEN_L2, final_A=A + 300 * MB), fS=A + 300 * MB) == ALIAS
+    assert fwd_call(desc(denominator=rla.DEN_L2, final_A=A + 402 * MB + 4)) == MISAL
     n = ctypes.c_size_t(0)
     assert rla.lib().rla2_bwd_workspace_size(ctypes.byref(desc(denominator=rla.DEN_L2)), ctypes.byref(n)) == UNSUP
     # the state build does not depend on the denominator

@@ -112,3 +112,86 @@ def test_l2_packed_workload_sampled():
         worst = max(worst, row_rel_err(out[0, h, rows], ref))
     print(f"L2 packed T={T} sampled: max row rel err {worst:.3e}")
     assert worst <= TOL_BF16
+
+
+# --- the whole-document range and the initial second state (RLA page §4.1) -----------------
+
+def _psd(H, d, seed):
+    """A symmetric positive semi-definite [H, d, d] second state (a sum of outer products)."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.rand(H, 3 * d, d, generator=g)
+    return (x.transpose(1, 2) @ x) / d
+
+
+@pytest.mark.parametrize("B,H,L,d,dtype,lengths,bidir,pos,with_init,chunk", [
+    (1, 2, 256, 32, torch.float32, None, True, 0, False, 64),
+    (1, 2, 190, 64, torch.float32, [60, 0, 1, 129], True, 7, True, 64),
+    (2, 2, 300, 64, torch.bfloat16, None, True, 0, True, 64),
+    (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], True, 0, False, 64),
+    (1, 1, 200, 128, torch.float32, None, False, 1000, True, 64),
+    (2, 2, 129, 32, torch.bfloat16, None, False, 65, True, 64),
+    (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], False, 37, True, 64),
+    (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], False, 37, True, 32),
+    (1, 2, 300, 64, torch.float32, [100, 200], False, 3, True, 128),
+])
+def test_l2_whole_document_and_initial_state(B, H, L, d, dtype, lengths, bidir, pos, with_init, chunk):
+    inp = workloads.fwd_inputs(B, H, L, d, dtype, seed=800 + L + d + pos % 7, lengths=lengths)
+    q, k, v, gq, gk, cu = _gpu(inp)
+    kw, okw = {}, {}
+    if with_init:
+        S0, _ = workloads.initial_state(H, d, seed=L)
+        A0 = _psd(H, d, seed=L)
+        z0 = torch.zeros(H, d)
+        kw = dict(initial_S=S0.to(DEV), initial_z=z0.to(DEV), initial_A=A0.to(DEV))
+        okw = dict(initial_S=f64(S0), initial_A=f64(A0))
+    out, fS, fz, fA = rla.fwd(q, k, v, gq, gk, cu, l2_denominator=True, bidirectional=bidir, initial_pos=pos,
+                              chunk=chunk, return_final_state=True, return_final_A=True, **kw)
+    torch.cuda.synchronize()
+    cu_np = None if lengths is None else inp.cu_seqlens.numpy()
+    ref = oracle.fwd_l2(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.gamma_q), f64(inp.gamma_k), cu_np,
+                        oracle.DEFAULT_L2_EPS, inp.rms_eps, inp.rope_base, causal=not bidir, initial_pos=pos, **okw)
+    err = row_rel_err(out, ref)
+    print(f"L2 [{B},{H},{L},{d}] {dtype} docs={lengths} bidir={bidir} pos={pos} init={with_init} chunk={chunk}: "
+          f"max row rel err {err:.3e}")
+    assert err <= _tol(inp)
+    A_ref = oracle.second_state_from_prefix(f64(inp.k), f64(inp.gamma_k), cu_np, inp.rms_eps, inp.rope_base,
+                                            okw.get("initial_A"), pos)
+    from helpers import mat_rel_err
+    assert mat_rel_err(fA, A_ref) <= _tol(inp)
+    # the state build exports the same second state
+    S1, z1, A1 = rla.state_from_prefix(k, v, gk, cu, initial_pos=pos, l2_second_state=True, chunk=chunk, **kw)
+    assert torch.equal(A1, fA) and torch.equal(S1, fS) and torch.equal(z1, fz)
+
+
+def test_l2_prefill_continuation_matches_whole_sequence():
+    # a context P summarised by the state build (S and the second state A), then X run from it
+    # with positions continuing at len(P): the rows of X in one L2 forward over P ++ X
+    H, d, p, n = 2, 128, 333, 200
+    whole = workloads.fwd_inputs(1, H, p + n, d, torch.bfloat16, seed=87)
+    q, k, v, gq, gk, _ = _gpu(whole)
+    S0, z0, A0 = rla.state_from_prefix(k[:, :, :p].contiguous(), v[:, :, :p].contiguous(), gk, l2_second_state=True)
+    out = rla.fwd(q[:, :, p:].contiguous(), k[:, :, p:].contiguous(), v[:, :, p:].contiguous(), gq, gk,
+                  initial_S=S0[0].contiguous(), initial_z=z0[0].contiguous(), initial_A=A0[0].contiguous(),
+                  initial_pos=p, l2_denominator=True)
+    full = rla.fwd(q, k, v, gq, gk, l2_denominator=True)
+    torch.cuda.synchronize()
+    ref = oracle.fwd_l2(f64(whole.q), f64(whole.k), f64(whole.v), f64(whole.gamma_q), f64(whole.gamma_k))[:, :, p:]
+    err = row_rel_err(out, ref)
+    print(f"L2 continuation after {p} tokens: max row rel err {err:.3e} (whole-sequence GPU "
+          f"{row_rel_err(full[:, :, p:], ref):.3e})")
+    assert err <= TOL_BF16
+
+
+def test_l2_bidirectional_long_context_sampled():
+    inp = workloads.c4_long()
+    q, k, v, gq, gk, _ = _gpu(inp)
+    out = rla.fwd(q, k, v, gq, gk, l2_denominator=True, bidirectional=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp.q.shape[2], 16, seed=13)
+    worst = 0.0
+    for h in (0, 31):
+        ref = oracle.fwd_l2_rows(inp.q, inp.k, inp.v, f64(inp.gamma_q), f64(inp.gamma_k), 0, h, rows,
+                                 rms_eps=inp.rms_eps, rope_base=inp.rope_base, causal=False)
+        worst = max(worst, row_rel_err(out[0, h, rows], ref))
+    print(f"L2 bidirectional long context sampled: max row rel err {worst:.3e}")
+    assert worst <= TOL_BF16
