@@ -620,21 +620,32 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         Frag<true> Qf[KB], Gt[KB];  // the query tile's rows (read again: no runtime register index)
         floatx4 zq = floatx4{0.f, 0.f, 0.f, 0.f};
         const Frag<true>* zf = sZf + (c & 1) * KB * 64;
+        Frag<true> Zf[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           Qf[kb] = lds_frag_c(cQ, QP, t, kb, g);
           Gt[kb] = lds_frag_c(cG, QP, t, kb, g);
-          zq = mma(zf[kb * 64 + lane], Qf[kb], zq);
+          Zf[kb] = zf[kb * 64 + lane];
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) zq = mma(Zf[kb], Qf[kb], zq);
         if (g == 0) qz = zq[0] + zq[1];  // q'_t . z (rows 0, 1 of Z Q'^T)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           At[kt] = Bt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
           if (kt <= tt) {
+            Frag<true> Kt[KB], Vt[KB];  // key tile kt's rows, requested before its MFMAs
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
-              At[kt] = mma(lds_frag_c(cK, QP, kt * 16 + c16, kb, g), Qf[kb], At[kt]);
-              Bt[kt] = mma(lds_frag_c(cV, QP, kt * 16 + c16, kb, g), Gt[kb], Bt[kt]);
+              Kt[kb] = lds_frag_c(cK, QP, kt * 16 + c16, kb, g);
+              Vt[kb] = lds_frag_c(cV, QP, kt * 16 + c16, kb, g);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+              At[kt] = mma(Kt[kb], Qf[kb], At[kt]);
+              Bt[kt] = mma(Vt[kb], Gt[kb], Bt[kt]);
             }
           }
         }
@@ -691,35 +702,53 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
           }
         sB[tt * 64 + lane] = acc_frag<true>(x[0], x[1]);
       }
+      // the K' column fragments (for dQ' and the state update) and this wave's z values do not
+      // depend on phase B: requested before the meeting
+      Frag<true> Kc[CT];
+      float4 zv[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        Kc[ct] = lds_frag_tr(cK, QP, 0, (wave & 3) * G::DVW + 16 * ct, lane);
+        zv[ct] = *reinterpret_cast<const float4*>(zc + (wave & 3) * G::DVW + 16 * ct + 4 * g);
+      }
       meet += 4;
       mma_wave_sync(&sArrive, meet, lane, polls, hdr);
       // ---- phase C: this wave's rows of dQ'^T, then the state
       if (wave < NW) {
         float* dqb = sdQ + (c & 1) * C2 * FP;
+        float invs[2], gds[2];
+        Frag<true> bfs[2];
+#pragma unroll
+        for (int tq = 0; tq < 2; ++tq) {
+          invs[tq] = sInv[tq * 16 + c16];
+          gds[tq] = sGd[tq * 16 + c16];
+          bfs[tq] = sB[tq * 64 + lane];
+        }
+        Frag<true> avn[2];  // the state update's row fragments, one tile ahead
+        avn[0] = lds_frag_tr_s8(cV, QP, 0, 0, lane);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tq = 0; tq < 2; ++tq) {
           const int tc = tq * 16 + c16;  // query column of the tiles
-          const float inv = sInv[tc], gdv = sGd[tc];
-          const Frag<true> bf = sB[tq * 64 + lane];
+          const float inv = invs[tq], gdv = gds[tq];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             const int a0 = wave * G::DVW + 16 * ct + 4 * g;
             floatx4 acc = Y[ct][tq];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc[i], inv, gdv * zc[a0 + i]);
-            acc = mma(lds_frag_tr(cK, QP, 0, wave * G::DVW + 16 * ct, lane), bf, acc);
+            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc[i], inv, gdv * zv[ct][i]);
+            acc = mma(Kc[ct], bfs[tq], acc);
             *reinterpret_cast<floatx4*>(dqb + tc * FP + a0) = acc;
           }
         }
         // S^T += V^T K' (the 32 tokens are one k-block)
-        Frag<true> Kc[CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) Kc[ct] = lds_frag_tr(cK, QP, 0, wave * G::DVW + 16 * ct, lane);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          const Frag<true> av = lds_frag_tr_s8(cV, QP, 0, 32 * (rt / 2) + 4 * (rt % 2), lane);
+          const int cur = rt & 1, nxt = cur ^ 1;
+          if (rt + 1 < RT) avn[nxt] = lds_frag_tr_s8(cV, QP, 0, 32 * ((rt + 1) / 2) + 4 * ((rt + 1) % 2), lane);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) ST[rt][ct] = mma(av, Kc[ct], ST[rt][ct]);
+          for (int ct = 0; ct < CT; ++ct) ST[rt][ct] = mma(avn[cur], Kc[ct], ST[rt][ct]);
         }
       }
     }
@@ -1001,6 +1030,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
             Kf[kb] = lds_frag_c(cK, QP, key, kb, g);
             Vf[kb] = lds_frag_c(cV, QP, key, kb, g);
           }
+          // 1/den, gd and B_tt of the lane's four query rows of each query tile: one 16-byte
+          // read per tile and value, requested with the fragments, used through selects
+          float4 ri4[2], gd4[2], bd4[2];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt) {
+            ri4[tt] = *reinterpret_cast<const float4*>(cI + tt * 16 + 4 * g);
+            gd4[tt] = *reinterpret_cast<const float4*>(sGd + pb * C2 + tt * 16 + 4 * g);
+            bd4[tt] = *reinterpret_cast<const float4*>(sBd + pb * C2 + tt * 16 + 4 * g);
+          }
+          __builtin_amdgcn_sched_barrier(0);
           floatx4 Aq[2], Bq[2];  // rows = queries of tile tt, column = this lane's key
 #pragma unroll
           for (int tt = 0; tt < 2; ++tt) {
@@ -1018,85 +1057,117 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int t = tt * 16 + 4 * g + i;
               const bool after = tt > kt || (tt == kt && 4 * g + i > c16);
               const bool self = tt == kt && 4 * g + i == c16;
-              const float ri = cI[t];
+              const float ri = ri4[tt][i];
               xa[tt][i] = (after || self) ? Aq[tt][i] * ri : 0.f;
-              xb[tt][i] = after ? __builtin_fmaf(Bq[tt][i], ri, sGd[pb * C2 + t]) : (self ? sBd[pb * C2 + t] : 0.f);
+              xb[tt][i] = after ? __builtin_fmaf(Bq[tt][i], ri, gd4[tt][i]) : (self ? bd4[tt][i] : 0.f);
             }
           sAp[kt * 64 + lane] = acc_frag<true>(xa[0], xa[1]);
           sBp[kt * 64 + lane] = acc_frag<true>(xb[0], xb[1]);
         }
         meet += 4;
         mma_wave_sync(&sArrive, meet, lane, polls, hdr);
-        // ---- phase B: this wave's rows of dK'^T and dV^T, then the states
+        // ---- phase B: this wave's rows of dK'^T and dV^T, then the states. The k-blocks are the
+        // outer loop, so every V and K' fragment is read once for both column tiles, and each
+        // k-block's fragments are requested one k-block ahead (the last k-block requests the
+        // operands of the closing terms); the per-accumulator MFMA order is that of the plain
+        // loops (k-blocks in order, then the closing term).
         if (wave < NW) {
           float* dkb = sdK + pb * C2 * FP;
+          floatx4 y[CT][2], z[CT][2];  // dK'^T and dV^T tiles (column tile ct, key tile kt)
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            floatx4 y[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+          for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              Frag<true> ph, pl;
-              split_frag<D>(PT[2 * kb][ct], PT[2 * kb + 1][ct], ph, pl);
+            for (int kt = 0; kt < 2; ++kt) y[ct][kt] = z[ct][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+          Frag<true> fv[2][2], fk[2][2];  // V and K' fragments of a k-block, by k-block parity
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            fv[0][kt] = lds_frag_c(cV, QP, kt * 16 + c16, 0, g);
+            fk[0][kt] = lds_frag_c(cK, QP, kt * 16 + c16, 0, g);
+          }
+          Frag<true> qt[CT], gt[CT], bq[2], aq[2];  // operands of the closing terms
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const int cur = kb & 1, nxt = cur ^ 1;
+            if (kb + 1 < KB) {
 #pragma unroll
               for (int kt = 0; kt < 2; ++kt) {
-                const Frag<true> vr = lds_frag_c(cV, QP, kt * 16 + c16, kb, g);
-                y[kt] = mma(ph, vr, y[kt]);
-                y[kt] = mma(pl, vr, y[kt]);
+                fv[nxt][kt] = lds_frag_c(cV, QP, kt * 16 + c16, kb + 1, g);
+                fk[nxt][kt] = lds_frag_c(cK, QP, kt * 16 + c16, kb + 1, g);
+              }
+            } else {
+#pragma unroll
+              for (int ct = 0; ct < CT; ++ct) {
+                qt[ct] = lds_frag_tr(cQ, QP, 0, wave * G::DVW + 16 * ct, lane);
+                gt[ct] = lds_frag_tr(cG, QP, 0, wave * G::DVW + 16 * ct, lane);
+              }
+#pragma unroll
+              for (int kt = 0; kt < 2; ++kt) {
+                bq[kt] = sBp[kt * 64 + lane];
+                aq[kt] = sAp[kt * 64 + lane];
               }
             }
-            const int a0 = wave * G::DVW + 16 * ct + 4 * g;
-            const Frag<true> qt = lds_frag_tr(cQ, QP, 0, wave * G::DVW + 16 * ct, lane);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-              y[kt] = mma(qt, sBp[kt * 64 + lane], y[kt]);
+            for (int ct = 0; ct < CT; ++ct) {
+              Frag<true> ph, pl;
+              split_frag<D>(PT[2 * kb][ct], PT[2 * kb + 1][ct], ph, pl);
+              // the value gradient has no cancelling terms: P rounded to bf16 once is enough there
+              const Frag<true> pm = acc_frag<true>(PM[2 * kb][ct], PM[2 * kb + 1][ct]);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) y[kt][i] += pc[a0 + i];
-              *reinterpret_cast<floatx4*>(dkb + (kt * 16 + c16) * FP + a0) = y[kt];
+              for (int kt = 0; kt < 2; ++kt) {
+                y[ct][kt] = mma(ph, fv[cur][kt], y[ct][kt]);
+                y[ct][kt] = mma(pl, fv[cur][kt], y[ct][kt]);
+                z[ct][kt] = mma(pm, fk[cur][kt], z[ct][kt]);
+              }
             }
           }
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            floatx4 z[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-              // the value gradient has no cancelling terms: P rounded to bf16 once is enough here
-              const Frag<true> ph = acc_frag<true>(PM[2 * kb][ct], PM[2 * kb + 1][ct]);
-#pragma unroll
-              for (int kt = 0; kt < 2; ++kt) z[kt] = mma(ph, lds_frag_c(cK, QP, kt * 16 + c16, kb, g), z[kt]);
-            }
-            const int v0 = wave * G::DVW + 16 * ct + 4 * g;
-            const Frag<true> gt = lds_frag_tr(cG, QP, 0, wave * G::DVW + 16 * ct, lane);
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-              z[kt] = mma(gt, sAp[kt * 64 + lane], z[kt]);
-              const int key = kt * 16 + c16;
-              // keys past the segment are dropped; these 8-byte pieces of a row come from four
-              // waves, so they carry the default cache policy and meet in L2 as whole lines (with
-              // the streaming policy the partial lines went to memory: 1174 -> 1058 us per call
-              // measured on the 16K-token backward)
-              const int off = ((c * C2 + key) * D + v0) * 2;
-              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf2(z[kt][0], z[kt][1]), pack_bf2(z[kt][2], z[kt][3])},
-                                                    rdv, key < nv ? off : seg_bytes, 0, 0);
-            }
-          }
-          // P^T += G^T Q^ and P += Q^^T G (the 32 tokens are one k-block)
-          Frag<true> Hc[CT], Gc[CT];
+          // the reverse-state update's row fragments, requested while the closing terms run
+          Frag<true> Hc[CT], Gc[CT], grn[2], hrn[2];
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             Hc[ct] = lds_frag_tr(cH, QP, 0, wave * G::DVW + 16 * ct, lane);
             Gc[ct] = lds_frag_tr(cG, QP, 0, wave * G::DVW + 16 * ct, lane);
           }
+          grn[0] = lds_frag_tr_s8(cG, QP, 0, 0, lane);
+          hrn[0] = lds_frag_tr_s8(cH, QP, 0, 0, lane);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) {
+            const int a0 = wave * G::DVW + 16 * ct + 4 * g;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              y[ct][kt] = mma(qt[ct], bq[kt], y[ct][kt]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) y[ct][kt][i] += pc[a0 + i];
+              *reinterpret_cast<floatx4*>(dkb + (kt * 16 + c16) * FP + a0) = y[ct][kt];
+              z[ct][kt] = mma(gt[ct], aq[kt], z[ct][kt]);
+              const int key = kt * 16 + c16;
+              // keys past the segment are dropped; these 8-byte pieces of a row come from four
+              // waves, so they carry the default cache policy and meet in L2 as whole lines (with
+              // the streaming policy the partial lines went to memory: 1174 -> 1058 us per call
+              // measured on the 16K-token backward)
+              const int off = ((c * C2 + key) * D + a0) * 2;
+              __builtin_amdgcn_raw_buffer_store_b64(
+                  u32x2{pack_bf2(z[ct][kt][0], z[ct][kt][1]), pack_bf2(z[ct][kt][2], z[ct][kt][3])}, rdv,
+                  key < nv ? off : seg_bytes, 0, 0);
+            }
+          }
+          // P^T += G^T Q^ and P += Q^^T G (the 32 tokens are one k-block); each row tile's two
+          // fragments are requested one tile ahead
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            const Frag<true> gr = lds_frag_tr_s8(cG, QP, 0, 32 * (rt / 2) + 4 * (rt % 2), lane);
-            const Frag<true> hr = lds_frag_tr_s8(cH, QP, 0, 32 * (rt / 2) + 4 * (rt % 2), lane);
+            const int cur = rt & 1, nxt = cur ^ 1;
+            if (rt + 1 < RT) {
+              grn[nxt] = lds_frag_tr_s8(cG, QP, 0, 32 * ((rt + 1) / 2) + 4 * ((rt + 1) % 2), lane);
+              hrn[nxt] = lds_frag_tr_s8(cH, QP, 0, 32 * ((rt + 1) / 2) + 4 * ((rt + 1) % 2), lane);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
-              PT[rt][ct] = mma(gr, Hc[ct], PT[rt][ct]);
-              PM[rt][ct] = mma(hr, Gc[ct], PM[rt][ct]);
+              PT[rt][ct] = mma(grn[cur], Hc[ct], PT[rt][ct]);
+              PM[rt][ct] = mma(hrn[cur], Gc[ct], PM[rt][ct]);
             }
           }
         }
@@ -1104,12 +1175,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           Frag<true> w_hi, w_lo;
           token_col_frags(sW + pb * C2, 0, g, w_hi, w_lo);
           float* pn = sP + ((j + 1) & 1) * D;
+          // every row tile's fragment and old p value requested together
+          Frag<true> hrs[RT];
+          float pold[RT];
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) {
-            const Frag<true> hr = lds_frag_tr(cH, QP, 0, 16 * rt, lane);
-            floatx4 pv = mma(hr, w_hi, floatx4{0.f, 0.f, 0.f, 0.f});
-            pv = mma(hr, w_lo, pv);
-            if (c16 < 4) pn[rt * 16 + 4 * g + c16] = pc[rt * 16 + 4 * g + c16] + pv[c16];
+            hrs[rt] = lds_frag_tr(cH, QP, 0, 16 * rt, lane);
+            pold[rt] = pc[rt * 16 + 4 * g + (c16 & 3)];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            floatx4 pv = mma(hrs[rt], w_hi, floatx4{0.f, 0.f, 0.f, 0.f});
+            pv = mma(hrs[rt], w_lo, pv);
+            if (c16 < 4) pn[rt * 16 + 4 * g + c16] = pold[rt] + pv[c16];
           }
         }
       }
