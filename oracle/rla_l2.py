@@ -152,3 +152,33 @@ def fwd_l2_recurrent(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps: float = DE
                 quad = sum(qp[a] * A[a, c] * qp[c] for a in range(d) for c in range(d))
                 out[b, h, t] = num / (np.sqrt(quad) + eps)
     return out
+
+
+def decode_step_l2(q, k, v, positions, gamma_q, gamma_k, S, A, z=None, eps: float = DEFAULT_L2_EPS,
+                   rms_eps: float = DEFAULT_RMS_EPS, rope_base: float = DEFAULT_ROPE_BASE):
+    """One token per sequence from a given state with the L2 denominator (RLA page §4.2
+    forward_step with the §2.1 closed form; the second state is the A of the §4.1 scan).
+
+    ``q, k, v``: ``[N, H, d]``; ``positions``: ``[N]``; ``S, A [N, H, d, d]`` (and, if given,
+    ``z [N, H, d]``) are the states before the token. The state is updated first
+    (``S += k' (x) v``, ``A += k' (x) k'``, ``z += k'``), then read:
+    ``out = q' S / (sqrt(q'^T A q') + eps)``. Returns ``(out, S_new, A_new, z_new)`` (``z_new``
+    is None without ``z``); inputs are not modified.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, H, d = q.shape
+    S_new = _f64(S).copy()
+    A_new = _f64(A).copy()
+    z_new = None if z is None else _f64(z).copy()
+    out = np.zeros((N, H, d))
+    for n in range(N):
+        p = np.array([int(positions[n])])
+        for h in range(H):
+            qp = feature_map(q[n, h][None], _f64(gamma_q)[h], p, rms_eps, rope_base)[0]
+            kp = feature_map(k[n, h][None], _f64(gamma_k)[h], p, rms_eps, rope_base)[0]
+            S_new[n, h] += np.outer(kp, v[n, h])
+            A_new[n, h] += np.outer(kp, kp)
+            if z_new is not None:
+                z_new[n, h] += kp
+            out[n, h] = (qp @ S_new[n, h]) / (np.sqrt(qp @ A_new[n, h] @ qp) + eps)
+    return out, S_new, A_new, z_new

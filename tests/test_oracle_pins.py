@@ -705,3 +705,45 @@ def test_l2_bidirectional_mode():
     b = oracle.fwd_l2(q, k, v, gq, gk, cu, causal=False)
     assert not np.allclose(a[0, :, 8], b[0, :, 8])
     np.testing.assert_array_equal(a[0, :, :7], b[0, :, :7])
+
+
+def test_l2_decode_step_continues_the_sequence():
+    # RLA page §4.2 forward_step with the §2.1 denominator: the states of a prefix (S of §3,
+    # A of the §4.1 scan) followed by one decode step give the closed form's last row over the
+    # whole sequence, and the updated states are those of the whole sequence; from zero states
+    # the step is the first token (s v / (s + eps), s = q'.k').
+    H, d = 2, 8
+    lens = [5, 1, 9]
+    r = np.random.default_rng(37)
+    gq, gk = r.uniform(0.5, 1.5, size=(H, d)), r.uniform(0.5, 1.5, size=(H, d))
+    seqs = [r.normal(size=(3, H, n + 1, d)) for n in lens]
+    pk = np.concatenate([s[1][:, :-1] for s in seqs], axis=1)[None]
+    pv = np.concatenate([s[2][:, :-1] for s in seqs], axis=1)[None]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    S0, z0 = oracle.state_from_prefix(pk, pv, gk, cu)
+    A0 = oracle.second_state_from_prefix(pk, gk, cu)
+    qn, kn, vn = (np.stack([s[i][:, -1] for s in seqs]) for i in range(3))
+    out, S1, A1, z1 = oracle.decode_step_l2(qn, kn, vn, np.array(lens), gq, gk, S0, A0, z0, eps=1e-3)
+    for n, s in enumerate(seqs):
+        full = oracle.fwd_l2(s[0][None], s[1][None], s[2][None], gq, gk, eps=1e-3)
+        np.testing.assert_allclose(out[n], full[0, :, -1], rtol=1e-12, atol=1e-14)
+        Sf, zf = oracle.state_from_prefix(s[1][None], s[2][None], gk)
+        np.testing.assert_allclose(S1[n], Sf[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(z1[n], zf[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(A1[n], oracle.second_state_from_prefix(s[1][None], gk)[0], rtol=1e-12, atol=1e-14)
+    # without z the same output and states; the Sum step's z update is the same as here
+    out2, S2, A2, z2 = oracle.decode_step_l2(qn, kn, vn, np.array(lens), gq, gk, S0, A0, eps=1e-3)
+    assert z2 is None
+    np.testing.assert_array_equal(out2, out)
+    np.testing.assert_array_equal(A2, A1)
+    _, _, zs = oracle.decode_step(qn, kn, vn, np.array(lens), gq, gk, S0, z0)
+    np.testing.assert_allclose(zs, z1, rtol=1e-12, atol=1e-14)
+    # zero states: the first token of a document
+    Z = np.zeros_like(S0)
+    o0, _, _, _ = oracle.decode_step_l2(qn, kn, vn, np.zeros(len(lens)), gq, gk, Z, Z, eps=1e-3)
+    for n in range(len(lens)):
+        for h in range(H):
+            qp = oracle.feature_map(qn[n, h][None], gq[h], np.array([0]))[0]
+            kp = oracle.feature_map(kn[n, h][None], gk[h], np.array([0]))[0]
+            sc = qp @ kp
+            np.testing.assert_allclose(o0[n, h], sc * vn[n, h] / (sc + 1e-3), rtol=1e-12, atol=1e-14)
