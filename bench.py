@@ -91,6 +91,12 @@ def fwd_algorithmic(B, H, L, d, chunk=64):
     return th * (4 * d * d + 2 * chunk * d), th * 4 * d * 2
 
 
+def decode_l2_algorithmic(N, H, d):
+    """Per (sequence, head): S and A read + written (2*2*4*d^2), z read + written (2*4*d), q, k,
+    v read and out written in bf16 (8*d) bytes."""
+    return N * H * (16 * d * d + 8 * d + 8 * d)
+
+
 def decode_algorithmic(N, H, d):
     """Per (sequence, head): S read + written (2*4*d^2), z read + written (2*4*d),
     q, k, v read and out written in bf16 (8*d) bytes; 4*d^2 flops."""
@@ -542,6 +548,8 @@ def main():
         Hp, dp = dec.prefix_k.shape[1], dec.prefix_k.shape[3]
         build_bytes = T_prefix * Hp * dp * 2 * 2 + S.numel() * 4 + z.numel() * 4
         build_gbs = build_bytes / (ms_build * 1e-3) / 1e9
+        # the L2 mode's states (S, z and the second state A) of the same prefixes, untimed
+        S2, z2, A2 = rla.state_from_prefix(dec.prefix_k, dec.prefix_v, dgk, cu, l2_second_state=True)
         del dec.prefix_k, dec.prefix_v, sws
         torch.cuda.empty_cache()
         dq, dk, dv = dec.q.to(dev), dec.k.to(dev), dec.v.to(dev)
@@ -556,6 +564,16 @@ def main():
         hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
         torch.cuda.synchronize()
         ms_dec = ev.elapsed(0, 1) / args.steps
+        for _ in range(args.warmup):
+            rla.decode_step_l2(dq, dk, dv, pos, dgq, dgk, S2, A2, z2, out=dout)
+        torch.cuda.synchronize()
+        hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(args.steps):
+            rla.decode_step_l2(dq, dk, dv, pos, dgq, dgk, S2, A2, z2, out=dout)
+        hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        ms_dec_l2 = ev.elapsed(0, 1) / args.steps
+        del S2, z2, A2
         N, Hd, dd = dq.shape
         dflops, dbytes = decode_algorithmic(N, Hd, dd)
         gbs = dbytes / (ms_dec * 1e-3) / 1e9
@@ -565,6 +583,15 @@ def main():
             "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode_kernel"),
                          "algorithmic_bytes": dbytes},
+            "l2_denominator": {
+                "workload": "the same decode step with the L2 denominator sqrt(q'^T A q') + 1e-6: S, A and z in place",
+                "ms_per_step": ms_dec_l2, "tokens_per_s": N / (ms_dec_l2 * 1e-3),
+                "roofline": {"kernel": "decode (L2)", "bound": "hbm",
+                             "achieved": decode_l2_algorithmic(N, Hd, dd) / (ms_dec_l2 * 1e-3) / 1e9,
+                             "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": decode_l2_algorithmic(N, Hd, dd) / (ms_dec_l2 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "traffic": measured_traffic("decode_kernel_l2"),
+                             "algorithmic_bytes": decode_l2_algorithmic(N, Hd, dd)}},
             "state_from_prefix": {"prefix_tokens": T_prefix, "wall_s_first_call": t_prefix, "ms_per_call": ms_build,
                                   "roofline": {"kernel": "whole state build", "bound": "hbm",
                                                "achieved": build_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

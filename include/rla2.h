@@ -389,6 +389,27 @@ rla2_status rla2_decode_step(int32_t N, int32_t H, int32_t d, int32_t dtype, con
                              float rope_base, float eps, float* S, float* z, void* out,
                              hipStream_t stream);
 
+/*
+ * One decode step with the original RLA's L2 denominator (RLA page §4.2 forward_step
+ * with the §2.1 closed form; the second state is the A of the §4.1 scan): the feature
+ * map of the new token at its position, then the state update first (S += k' (x) v,
+ * A += k' (x) k', z += k' when z is given), then the read-out
+ * out = q' S / (sqrt(q'^T A q') + eps), eps the L2 constant (1e-6 on the page).
+ *  q, k, v, positions, gamma_q/k, out   as in rla2_decode_step.
+ *  S, A        [N, H, d, d] fp32, updated IN PLACE (A: the states of
+ *              rla2_state_from_prefix's final_A in the L2 mode).
+ *  z           [N, H, d] fp32, updated in place, or NULL (the L2 read-out does not
+ *              use it).
+ * Errors as rla2_decode_step; A must not be NULL (RLA2_ERR_NULL_POINTER), and S, A,
+ * z and out must not overlap each other or an input (RLA2_ERR_ALIAS). N == 0 is a
+ * valid no-op.
+ */
+rla2_status rla2_decode_step_l2(int32_t N, int32_t H, int32_t d, int32_t dtype, const void* q,
+                                const void* k, const void* v, const int32_t* positions,
+                                const float* gamma_q, const float* gamma_k, float rms_eps,
+                                float rope_base, float eps, float* S, float* A, float* z,
+                                void* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

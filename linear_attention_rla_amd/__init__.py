@@ -8,6 +8,7 @@ Entry points (same names as the C ABI in include/rla2.h):
   fwd(q, k, v, gamma_q, gamma_k, cu_seqlens=None, ...)        -> rla2_fwd_chunked
   state_from_prefix(k, v, gamma_k, cu_seqlens=None, ...)      -> rla2_state_from_prefix
   decode_step(q, k, v, positions, gamma_q, gamma_k, S, z,...) -> rla2_decode_step
+  decode_step_l2(q, k, v, positions, gamma_q, gamma_k, S, A,...) -> rla2_decode_step_l2
 """
 from __future__ import annotations
 
@@ -17,7 +18,7 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fwd", "state_from_prefix", "decode_step", "fwd_workspace_size", "lib", "Rla2Error",
+__all__ = ["fwd", "state_from_prefix", "decode_step", "decode_step_l2", "fwd_workspace_size", "lib", "Rla2Error",
            "Rla2FlagError", "FwdDesc", "LIB_PATH", "STATUS", "workspace_flags", "set_check_flags",
            "debug_set_wait_polls"]
 
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
         L.rla2_decode_step.restype = ctypes.c_int
         L.rla2_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                        _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P, _P, _P]
+        L.rla2_decode_step_l2.restype = ctypes.c_int
+        L.rla2_decode_step_l2.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                          _P, _P, _P, _P, ctypes.c_float, ctypes.c_float, ctypes.c_float, _P, _P,
+                                          _P, _P, _P]
         _lib = L
     return _lib
 
@@ -436,4 +441,36 @@ def decode_step(q, k, v, positions, gamma_q, gamma_k, S, z, *, eps=1e-4, rms_eps
                                 _stream(q.device))
     if st:
         raise Rla2Error(st, "rla2_decode_step")
+    return out
+
+
+def decode_step_l2(q, k, v, positions, gamma_q, gamma_k, S, A, z=None, *, eps=1e-6, rms_eps=1e-6,
+                   rope_base=10000.0, out=None):
+    """One decode token per sequence with the L2 denominator; updates ``S``, ``A`` (and ``z``
+    when given) in place. Returns ``out``."""
+    for n_, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n_, t, q.dtype)
+    if q.dim() != 3 or q.dtype not in _DTYPES:
+        raise ValueError("expected q, k, v [N, H, d] of float32 or bfloat16")
+    _check_dev("positions", positions, torch.int32)
+    _check_dev("S", S, torch.float32)
+    _check_dev("A", A, torch.float32)
+    if z is not None:
+        _check_dev("z", z, torch.float32)
+    _check_dev("gamma_q", gamma_q, torch.float32)
+    _check_dev("gamma_k", gamma_k, torch.float32)
+    N, H, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape or S.shape != (N, H, d, d) or A.shape != (N, H, d, d):
+        raise ValueError("shape mismatch between q, k, v, S, A")
+    if z is not None and z.shape != (N, H, d):
+        raise ValueError("shape mismatch of z")
+    if positions.shape != (N,) or gamma_q.shape != (H, d) or gamma_k.shape != (H, d):
+        raise ValueError("shape mismatch of positions or RMSNorm weights")
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib().rla2_decode_step_l2(N, H, d, _DTYPES[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(positions),
+                                   _ptr(gamma_q), _ptr(gamma_k), rms_eps, rope_base, eps, _ptr(S), _ptr(A),
+                                   _ptr(z), _ptr(out), _stream(q.device))
+    if st:
+        raise Rla2Error(st, "rla2_decode_step_l2")
     return out

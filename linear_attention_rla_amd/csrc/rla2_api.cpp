@@ -16,7 +16,7 @@ namespace {
 
 using rla2::Plan;
 
-constexpr int32_t kAbiVersion = 5;
+constexpr int32_t kAbiVersion = 6;
 
 // Poll bound of the MMA waves' meetings inside the warp-specialised kernels (a debug hook
 // lets tests lower it; see rla2_debug_set_wait_polls).
@@ -519,7 +519,35 @@ rla2_status rla2_decode_step(int32_t N, int32_t H, int32_t d, int32_t dtype, con
     if (overlap(o, r) || overlap(rs, r) || overlap(rz, r)) return RLA2_ERR_ALIAS;
   if (overlap(o, rs) || overlap(o, rz) || overlap(rs, rz)) return RLA2_ERR_ALIAS;
   return finish(rla2::launch_decode(N, H, d, dtype, q, k, v, positions, gamma_q, gamma_k, rms_eps,
-                                    rope_base, eps, S, z, out, stream));
+                                    rope_base, eps, S, z, nullptr, out, stream));
+}
+
+rla2_status rla2_decode_step_l2(int32_t N, int32_t H, int32_t d, int32_t dtype, const void* q,
+                                const void* k, const void* v, const int32_t* positions,
+                                const float* gamma_q, const float* gamma_k, float rms_eps,
+                                float rope_base, float eps, float* S, float* A, float* z, void* out,
+                                hipStream_t stream) {
+  if (N < 0 || H < 0 || d < 0) return RLA2_ERR_BAD_SHAPE;
+  if (!supported_d(d)) return RLA2_ERR_UNSUPPORTED;
+  if (dtype != RLA2_F32 && dtype != RLA2_BF16) return RLA2_ERR_UNSUPPORTED;
+  if (!finite_pos(eps) || !finite_pos(rms_eps) || !finite_pos(rope_base)) return RLA2_ERR_BAD_VALUE;
+  if ((unsigned long long)N * H * 256 > kMaxGridItems) return RLA2_ERR_BAD_SHAPE;
+  const size_t act = (size_t)N * H * d * elem_bytes(dtype);
+  if (act == 0) return RLA2_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || positions == nullptr || gamma_q == nullptr ||
+      gamma_k == nullptr || S == nullptr || A == nullptr || out == nullptr)
+    return RLA2_ERR_NULL_POINTER;
+  if (misaligned({q, k, v, out, gamma_q, gamma_k, S, A, z})) return RLA2_ERR_MISALIGNED;
+  const size_t sb = (size_t)N * H * d * d * 4, zb = (size_t)N * H * d * 4, gam = (size_t)H * d * 4;
+  const Range o{out, act}, rs{S, sb}, ra{A, sb}, rz{z, z != nullptr ? zb : 0};
+  const Range ins[] = {{q, act}, {k, act}, {v, act}, {positions, (size_t)N * 4}, {gamma_q, gam},
+                       {gamma_k, gam}};
+  for (const Range& r : ins)
+    if (overlap(o, r) || overlap(rs, r) || overlap(ra, r) || overlap(rz, r)) return RLA2_ERR_ALIAS;
+  if (overlap(o, rs) || overlap(o, ra) || overlap(o, rz) || overlap(rs, ra) || overlap(rs, rz) || overlap(ra, rz))
+    return RLA2_ERR_ALIAS;
+  return finish(rla2::launch_decode(N, H, d, dtype, q, k, v, positions, gamma_q, gamma_k, rms_eps,
+                                    rope_base, eps, S, z, A, out, stream));
 }
 
 }  // extern "C"

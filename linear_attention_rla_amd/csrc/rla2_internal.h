@@ -125,9 +125,11 @@ hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hi
 // The feature map alone: prep, then q' and k' (either input may be null).
 hipError_t launch_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void* k_out, hipStream_t s);
 
+// One decode step: the Sum denominator when A is null (z required), the L2 denominator with
+// the second state A otherwise (z optional).
 hipError_t launch_decode(int N, int H, int d, int dtype, const void* q, const void* k,
                          const void* v, const int32_t* pos, const float* gq, const float* gk,
-                         float rms_eps, float rope_base, float eps, float* S, float* z,
+                         float rms_eps, float rope_base, float eps, float* S, float* z, float* A,
                          void* out, hipStream_t s);
 
 }  // namespace rla2

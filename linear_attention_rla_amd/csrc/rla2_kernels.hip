@@ -1839,28 +1839,40 @@ __global__ __launch_bounds__(NT, 2) void feature_map_kernel(
 // frequencies come from the host in fp64 and the angle is formed in fp64). Then every
 // thread updates D/RG rows of a 4-column strip of S in place and accumulates its share of
 // q'S; the partial read-outs meet in LDS.
+// L2: the same thread also holds its rows of the second state A (RLA page §4.1: A = sum
+// k' k'^T), updates them with k' (x) k' and accumulates its share of q'^T A q' (RLA page
+// §2.1: the squared scores summed, read from the updated state); the denominator is the
+// square root of the workgroup's sum plus eps. z is then optional (updated when given).
 
 struct Theta {
   double t[64];  // base^(-2j/d), j < d/2, computed on the host in fp64
 };
 
-template <bool BF, int D>
-__global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St* __restrict__ q,
+template <bool BF, int D, bool L2>
+constexpr int decode_threads() {  // L2 (d >= 64): twice the threads, each with half the rows of S and A
+  return (L2 && D >= 64) ? 512 : 256;
+}
+
+template <bool BF, int D, bool L2>
+__global__ __launch_bounds__((decode_threads<BF, D, L2>())) void decode_kernel(const typename Elem<BF>::St* __restrict__ q,
                                                      const typename Elem<BF>::St* __restrict__ k,
                                                      const typename Elem<BF>::St* __restrict__ v,
                                                      const int32_t* __restrict__ positions,
                                                      const float* __restrict__ gamma_q,
                                                      const float* __restrict__ gamma_k, float rms_eps, Theta th,
                                                      float eps, float* __restrict__ S, float* __restrict__ z,
+                                                     float* __restrict__ A,
                                                      typename Elem<BF>::St* __restrict__ out, int H) {
   using EL = Elem<BF>;
+  constexpr int NT = decode_threads<BF, D, L2>();
   constexpr int HALF = D / 2;
   constexpr int C4 = D / 4;           // 4-column strips
-  constexpr int RG = 256 / C4;        // row groups
+  constexpr int RG = NT / C4;         // row groups
   constexpr int RPT = D / RG;         // rows per thread
+  static_assert(RPT >= 1 && RG * RPT == D && HALF <= 64, "decode tiling");
   __shared__ float sq[D], sk[D], sv[D];
   __shared__ float part[RG][D];
-  __shared__ float sden[4];
+  __shared__ float sden[NT / 64];
 
   const int nh = blockIdx.x;          // n * H + h
   const int n = nh / H, h = nh % H;
@@ -1875,9 +1887,17 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St
 #pragma unroll
   for (int r = 0; r < RPT; ++r)
     st[r] = *(reinterpret_cast<const floatx4*>(Sp + (size_t)(rg + r * RG) * D) + c4);
+  floatx4 sa[L2 ? RPT : 1];
+  float* Ap = L2 ? A + (size_t)nh * D * D : nullptr;
+  if constexpr (L2) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+      sa[r] = *(reinterpret_cast<const floatx4*>(Ap + (size_t)(rg + r * RG) * D) + c4);
+  }
+  const bool has_z = !L2 || z != nullptr;
   float zold = 0.f, vv = 0.f;
   if (tid < D) {
-    zold = z[base + tid];
+    if (has_z) zold = z[base + tid];
     vv = EL::to_f(v[base + tid]);
   }
   float x1 = 0.f, x2 = 0.f, gm1 = 0.f, gm2 = 0.f;
@@ -1910,6 +1930,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St
 
   const float v0 = sv[4 * c4], v1 = sv[4 * c4 + 1], v2 = sv[4 * c4 + 2], v3 = sv[4 * c4 + 3];
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  float quad = 0.f;  // L2: this thread's share of q'^T A q'
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const int row = rg + r * RG;
@@ -1924,19 +1945,31 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St
     a1 += qr * x[1];
     a2 += qr * x[2];
     a3 += qr * x[3];
+    if constexpr (L2) {
+      floatx4 y = sa[r];
+      float rq = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] += kr * sk[4 * c4 + i];
+        rq += y[i] * sq[4 * c4 + i];
+      }
+      __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(Ap + (size_t)row * D) + c4);
+      quad += qr * rq;
+    }
   }
   part[rg][4 * c4] = a0;
   part[rg][4 * c4 + 1] = a1;
   part[rg][4 * c4 + 2] = a2;
   part[rg][4 * c4 + 3] = a3;
 
-  // z += k'; den = q' . z_new
+  // z += k'; Sum: den = q' . z_new; L2: den = sqrt(q'^T A_new q') + eps
   float dz = 0.f;
-  if (tid < D) {
+  if (tid < D && has_z) {
     const float zn = zold + sk[tid];
     z[base + tid] = zn;
-    dz = sq[tid] * zn;
+    if constexpr (!L2) dz = sq[tid] * zn;
   }
+  if constexpr (L2) dz = quad;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) dz += __shfl_xor(dz, o);
   if (lane == 0) sden[wave] = dz;
@@ -1945,7 +1978,10 @@ __global__ __launch_bounds__(256) void decode_kernel(const typename Elem<BF>::St
     float num = 0.f;
 #pragma unroll
     for (int r = 0; r < RG; ++r) num += part[r][tid];
-    const float den = sden[0] + sden[1] + sden[2] + sden[3] + eps;
+    float red = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) red += sden[w];
+    const float den = L2 ? sqrtf(red) + eps : red + eps;
     out[base + tid] = EL::from_f(num / den);
   }
 }
@@ -2085,13 +2121,20 @@ hipError_t run_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void* k
 template <bool BF, int D>
 hipError_t run_decode(int N, int H, const void* q, const void* k, const void* v, const int32_t* pos,
                       const float* gq, const float* gk, float rms_eps, float rope_base, float eps, float* S,
-                      float* z, void* out, hipStream_t s) {
+                      float* z, float* A, void* out, hipStream_t s) {
   using St = typename Elem<BF>::St;
   Theta th{};
   for (int j = 0; j < D / 2; ++j) th.t[j] = std::pow((double)rope_base, -2.0 * (double)j / (double)D);
-  hipLaunchKernelGGL((decode_kernel<BF, D>), dim3(N * H), dim3(256), 0, s, static_cast<const St*>(q),
-                     static_cast<const St*>(k), static_cast<const St*>(v), pos, gq, gk, rms_eps, th, eps, S, z,
-                     static_cast<St*>(out), H);
+  if (A != nullptr)
+    hipLaunchKernelGGL((decode_kernel<BF, D, true>), dim3(N * H), dim3(decode_threads<BF, D, true>()), 0, s,
+                       static_cast<const St*>(q),
+                       static_cast<const St*>(k), static_cast<const St*>(v), pos, gq, gk, rms_eps, th, eps, S, z,
+                       A, static_cast<St*>(out), H);
+  else
+    hipLaunchKernelGGL((decode_kernel<BF, D, false>), dim3(N * H), dim3(decode_threads<BF, D, false>()), 0, s,
+                       static_cast<const St*>(q),
+                       static_cast<const St*>(k), static_cast<const St*>(v), pos, gq, gk, rms_eps, th, eps, S, z,
+                       nullptr, static_cast<St*>(out), H);
   return hipGetLastError();
 }
 
@@ -2147,11 +2190,11 @@ hipError_t launch_feature_map(const Plan& p, const FwdArgs& a, void* q_out, void
 
 hipError_t launch_decode(int N, int H, int d, int dtype, const void* q, const void* k, const void* v,
                          const int32_t* pos, const float* gq, const float* gk, float rms_eps, float rope_base,
-                         float eps, float* S, float* z, void* out, hipStream_t s) {
+                         float eps, float* S, float* z, float* A, void* out, hipStream_t s) {
   const bool bf = dtype == 1;
 #define RLA2_DEC(DD)                                                                                           \
-  return bf ? run_decode<true, DD>(N, H, q, k, v, pos, gq, gk, rms_eps, rope_base, eps, S, z, out, s)         \
-            : run_decode<false, DD>(N, H, q, k, v, pos, gq, gk, rms_eps, rope_base, eps, S, z, out, s)
+  return bf ? run_decode<true, DD>(N, H, q, k, v, pos, gq, gk, rms_eps, rope_base, eps, S, z, A, out, s)      \
+            : run_decode<false, DD>(N, H, q, k, v, pos, gq, gk, rms_eps, rope_base, eps, S, z, A, out, s)
   switch (d) {
     case 32: RLA2_DEC(32);
     case 64: RLA2_DEC(64);

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = rla.lib()
-    assert L.rla2_abi_version() == 5
+    assert L.rla2_abi_version() == 6
     for code, name in rla.STATUS.items():
         assert L.rla2_status_string(code).decode().startswith(name)
     assert L.rla2_status_string(99).decode() == "RLA2_ERR_UNKNOWN"
@@ -198,6 +198,31 @@ def test_decode_error_paths():
     assert call(S=A + 8) == MISAL
     assert call(N=0, q=None, k=None, v=None, pos=None, S=None, z=None, out=None) == OK
     # one 256-thread workgroup per (sequence, head): 2^20 x 32 x 256 work-items do not fit a grid
+    assert call(N=1 << 20, H=32) == SHAPE
+
+
+def test_decode_l2_error_paths():
+    L = rla.lib()
+
+    def call(N=4, H=2, d=128, dt=rla.BF16, q=A, k=A + MB, v=A + 2 * MB, pos=A + 3 * MB, gq=A + 4 * MB,
+             gk=A + 5 * MB, rms=1e-6, base=1e4, eps=1e-6, S=A + 64 * MB, Am=A + 256 * MB, z=A + 128 * MB,
+             out=A + 192 * MB):
+        return L.rla2_decode_step_l2(N, H, d, dt, q, k, v, pos, gq, gk, rms, base, eps, S, Am, z, out, None)
+
+    assert call(N=-1) == SHAPE
+    assert call(d=96) == UNSUP
+    assert call(dt=5) == UNSUP
+    assert call(eps=0.0) == VALUE
+    assert call(base=float("inf")) == VALUE
+    assert call(Am=None) == NULLP                            # the second state is required
+    assert call(S=None) == NULLP
+    assert call(q=None) == NULLP
+    assert call(Am=A + 64 * MB + 4096) == ALIAS              # A inside S
+    assert call(z=A + 256 * MB) == ALIAS                     # z inside A
+    assert call(out=A + 256 * MB) == ALIAS                   # out over A
+    assert call(Am=A + 3 * MB) == ALIAS                      # A over the positions
+    assert call(Am=A + 256 * MB + 8) == MISAL
+    assert call(N=0, q=None, k=None, v=None, pos=None, S=None, Am=None, z=None, out=None) == OK
     assert call(N=1 << 20, H=32) == SHAPE
 
 

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from helpers import TOL_BF16, TOL_F32, f64, row_rel_err, sample_rows
+from helpers import TOL_BF16, TOL_F32, f64, mat_rel_err, row_rel_err, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -195,3 +195,81 @@ def test_l2_bidirectional_long_context_sampled():
         worst = max(worst, row_rel_err(out[0, h, rows], ref))
     print(f"L2 bidirectional long context sampled: max row rel err {worst:.3e}")
     assert worst <= TOL_BF16
+
+
+# --- the decode step with the L2 denominator (RLA page §4.2 forward_step, §2.1, §4.1 A) ---
+
+@pytest.mark.parametrize("d,dtype", [(32, torch.float32), (64, torch.bfloat16), (128, torch.bfloat16),
+                                     (128, torch.float32)])
+@pytest.mark.parametrize("with_z", [True, False])
+def test_l2_decode_small(d, dtype, with_z):
+    dec = workloads.decode_inputs(6, 3, d, 300, seed=19 + d, dtype=dtype)
+    pk, pv = dec.prefix_k.to(DEV), dec.prefix_v.to(DEV)
+    cu = dec.cu_prefix.to(DEV)
+    gq, gk = dec.gamma_q.to(DEV), dec.gamma_k.to(DEV)
+    S, z, A = rla.state_from_prefix(pk, pv, gk, cu, seg_chunks=1, l2_second_state=True)
+    torch.cuda.synchronize()
+    cun = dec.cu_prefix.numpy()
+    S_ref, z_ref = oracle.state_from_prefix(f64(dec.prefix_k), f64(dec.prefix_v), f64(dec.gamma_k), cun)
+    A_ref = oracle.second_state_from_prefix(f64(dec.prefix_k), f64(dec.gamma_k), cun)
+    t = TOL_F32 if dtype == torch.float32 else TOL_BF16
+    assert mat_rel_err(A, A_ref) <= t
+    z_in = z if with_z else None
+    z_before = z.clone()
+    out = rla.decode_step_l2(dec.q.to(DEV), dec.k.to(DEV), dec.v.to(DEV), dec.prefix_lengths.to(DEV), gq, gk,
+                             S, A, z_in)
+    torch.cuda.synchronize()
+    o_ref, S1, A1, z1 = oracle.decode_step_l2(f64(dec.q), f64(dec.k), f64(dec.v), dec.prefix_lengths.numpy(),
+                                              f64(dec.gamma_q), f64(dec.gamma_k), S_ref, A_ref, z_ref)
+    err = row_rel_err(out, o_ref)
+    print(f"L2 decode d={d} {dtype} z={with_z} out err {err:.3e}")
+    assert err <= t
+    assert mat_rel_err(S, S1) <= t and mat_rel_err(A, A1) <= t
+    if with_z:
+        assert mat_rel_err(z, z1, 1) <= t
+    else:
+        assert torch.equal(z, z_before)  # z untouched without it
+
+
+def test_l2_decode_continues_the_forward():
+    # the L2 state of a prefix followed by one L2 decode step gives the L2 forward's last row
+    H, d, n = 4, 128, 517
+    inp = workloads.fwd_inputs(1, H, n + 1, d, torch.bfloat16, seed=57)
+    q, k, v, gq, gk, _ = _gpu(inp)
+    full = rla.fwd(q, k, v, gq, gk, l2_denominator=True)
+    S, z, A = rla.state_from_prefix(k[:, :, :n].contiguous(), v[:, :, :n].contiguous(), gk, l2_second_state=True)
+    pos = torch.tensor([n], dtype=torch.int32, device=DEV)
+    last = rla.decode_step_l2(q[:, :, n].contiguous(), k[:, :, n].contiguous(), v[:, :, n].contiguous(), pos,
+                              gq, gk, S, A)
+    torch.cuda.synchronize()
+    assert row_rel_err(last, full[:, :, n]) <= TOL_BF16
+    ref = oracle.fwd_l2_rows(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.gamma_q), f64(inp.gamma_k), 0, 0, [n])
+    assert row_rel_err(last[0, 0], ref[0]) <= TOL_BF16
+
+
+def test_l2_decode_full_size_sampled():
+    # the decode workload (256 sequences x 32 heads, d = 128, prefixes of U{1..8192} tokens) with
+    # the L2 denominator; six sequences checked against the oracle one by one
+    dec = workloads.c5_decode(device=DEV)
+    cu = dec.cu_prefix.to(DEV)
+    gq, gk = dec.gamma_q.to(DEV), dec.gamma_k.to(DEV)
+    S, z, A = rla.state_from_prefix(dec.prefix_k, dec.prefix_v, gk, cu, l2_second_state=True)
+    A0 = A.clone()
+    pos = dec.prefix_lengths.to(DEV)
+    out = rla.decode_step_l2(dec.q.to(DEV), dec.k.to(DEV), dec.v.to(DEV), pos, gq, gk, S, A, z)
+    torch.cuda.synchronize()
+    cun = dec.cu_prefix.numpy()
+    r = np.random.default_rng(7)
+    for n in sorted(set([0, 255] + r.integers(0, 256, size=4).tolist())):
+        s0, s1 = int(cun[n]), int(cun[n + 1])
+        pk = f64(dec.prefix_k[:, :, s0:s1])
+        pv = f64(dec.prefix_v[:, :, s0:s1])
+        S_ref, z_ref = oracle.state_from_prefix(pk, pv, f64(dec.gamma_k))
+        A_ref = oracle.second_state_from_prefix(pk, f64(dec.gamma_k))
+        assert mat_rel_err(A0[n], A_ref[0]) <= TOL_BF16, f"second state of sequence {n}"
+        o_ref, S1, A1, z1 = oracle.decode_step_l2(f64(dec.q[n:n + 1]), f64(dec.k[n:n + 1]), f64(dec.v[n:n + 1]),
+                                                  np.array([s1 - s0]), f64(dec.gamma_q), f64(dec.gamma_k),
+                                                  S_ref, A_ref, z_ref)
+        assert row_rel_err(out[n], o_ref[0]) <= TOL_BF16, f"L2 decode output of sequence {n}"
+        assert mat_rel_err(S[n], S1[0]) <= TOL_BF16 and mat_rel_err(A[n], A1[0]) <= TOL_BF16
+        assert mat_rel_err(z[n], z1[0], 1) <= TOL_BF16
