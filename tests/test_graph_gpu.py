@@ -1,0 +1,59 @@
+"""The forward captured in a HIP graph and replayed.
+
+The allocation-free entry point exists for callers such as graph capture; this test captures it
+(and the workspace forward with a caller-owned workspace) once and replays the graph with new
+inputs copied into the captured buffers between replays, with eager work and synchronisations
+in between. Every replay must equal, bitwise, an eager call on the same inputs: the same kernels
+run in the same order, and nothing in the captured calls is a memset or a host-side copy (the set-up
+launch clears the status header with a kernel).
+"""
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import linear_attention_rla_amd as rla
+
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("no_alloc", [True, False])
+@pytest.mark.parametrize("B,H,L,d,dtype,lengths,chunk", [
+    (2, 4, 300, 64, torch.bfloat16, None, 64),
+    (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], 64),
+    (1, 2, 256, 32, torch.float32, None, 32),
+])
+def test_forward_graph_replays_equal_eager(no_alloc, B, H, L, d, dtype, lengths, chunk):
+    inps = [workloads.fwd_inputs(B, H, L, d, dtype, seed=700 + i + L, lengths=lengths) for i in range(3)]
+    q, k, v = (x.to(DEV) for x in (inps[0].q, inps[0].k, inps[0].v))
+    gq, gk = inps[0].gamma_q.to(DEV), inps[0].gamma_k.to(DEV)
+    cu = None if lengths is None else inps[0].cu_seqlens.to(DEV)
+    out = torch.empty_like(q)
+    ws = None
+    if not no_alloc:
+        desc = rla.make_desc(B, H, L, d, rla.BF16 if dtype == torch.bfloat16 else rla.F32, cu,
+                             0 if lengths is None else len(lengths), chunk=chunk)
+        ws = torch.empty(max(rla.fwd_workspace_size(desc), 1), dtype=torch.uint8, device=DEV)
+    prev = rla.set_check_flags(False)  # reading the flags synchronises the stream: not inside a capture
+    try:
+        run = lambda: rla.fwd(q, k, v, gq, gk, cu, chunk=chunk, out=out, no_alloc=no_alloc, workspace=ws)  # noqa: E731
+        run()  # eager first call (the scratch array's address is looked up on the first call per device)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        for i in (1, 2, 0, 1):
+            q.copy_(inps[i].q)
+            k.copy_(inps[i].k)
+            v.copy_(inps[i].v)
+            g.replay()
+            torch.cuda.synchronize()
+            got = out.clone()
+            ref = rla.fwd(q, k, v, gq, gk, cu, chunk=chunk)  # eager, its own workspace
+            torch.cuda.synchronize()
+            assert torch.equal(got, ref), f"replay with inputs {i}"
+    finally:
+        rla.set_check_flags(prev)
