@@ -1945,16 +1945,21 @@ __global__ __launch_bounds__((decode_threads<BF, D, L2>())) void decode_kernel(c
     a1 += qr * x[1];
     a2 += qr * x[2];
     a3 += qr * x[3];
-    if constexpr (L2) {
-      floatx4 y = sa[r];
-      float rq = 0.f;
+  }
+  if constexpr (L2) {  // A after S: one store stream at a time (401 -> 391 us on the 256 x 32 workload)
+    const float k0 = sk[4 * c4], k1 = sk[4 * c4 + 1], k2 = sk[4 * c4 + 2], k3 = sk[4 * c4 + 3];
+    const float q0 = sq[4 * c4], q1 = sq[4 * c4 + 1], q2 = sq[4 * c4 + 2], q3 = sq[4 * c4 + 3];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        y[i] += kr * sk[4 * c4 + i];
-        rq += y[i] * sq[4 * c4 + i];
-      }
+    for (int r = 0; r < RPT; ++r) {
+      const int row = rg + r * RG;
+      const float kr = sk[row], qr = sq[row];
+      floatx4 y = sa[r];
+      y[0] += kr * k0;
+      y[1] += kr * k1;
+      y[2] += kr * k2;
+      y[3] += kr * k3;
       __builtin_nontemporal_store(y, reinterpret_cast<floatx4*>(Ap + (size_t)row * D) + c4);
-      quad += qr * rq;
+      quad += qr * (y[0] * q0 + y[1] * q1 + y[2] * q2 + y[3] * q3);
     }
   }
   part[rg][4 * c4] = a0;
