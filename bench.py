@@ -148,12 +148,17 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
         "bidirectional": dict(bidirectional=True),
         "continuation": dict(initial_S=S0, initial_z=z0, initial_pos=L),
         "l2_denominator": dict(l2_denominator=True),
+        "l2_bidirectional": dict(l2_denominator=True, bidirectional=True),
+        "chunk_16": dict(chunk=16),
+        "chunk_32": dict(chunk=32),
+        "chunk_128": dict(chunk=128),
     }
-    l2_desc = rla.make_desc(B, H, L, d, rla.BF16, seg_chunks=args.seg_chunks, denominator=rla.DEN_L2)
-    ws_l2 = torch.empty(rla.fwd_workspace_size(l2_desc), dtype=torch.uint8, device=q.device)
     res = {}
     for name, kw in modes.items():
-        wsm = ws_l2 if name == "l2_denominator" else ws
+        mdesc = rla.make_desc(B, H, L, d, rla.BF16, seg_chunks=args.seg_chunks, chunk=kw.get("chunk", 64),
+                              bidirectional=kw.get("bidirectional", False),
+                              denominator=rla.DEN_L2 if kw.get("l2_denominator") else rla.DEN_SUM)
+        wsm = torch.empty(max(rla.fwd_workspace_size(mdesc), 1), dtype=torch.uint8, device=q.device)
 
         def run(events=None):
             rla.fwd(q, k, v, gq, gk, seg_chunks=args.seg_chunks, out=out, workspace=wsm, events=events, **kw)
@@ -174,13 +179,15 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
                 per[i] += kev.elapsed(i, i + 1)
         per = [x / steps for x in per]
         t_out = per[KERNELS.index("chunk_out")]
-        if name == "bidirectional":  # read-out: q read and out written once, bf16
+        if name in ("bidirectional", "l2_bidirectional"):  # read-out: q read and out written once, bf16
             nbytes = B * H * L * d * 2 * 2
-            kern, traffic = "readout", measured_traffic("readout_kernel")
+            kern = "readout" if name == "bidirectional" else "readout_l2"
+            traffic = measured_traffic("readout_kernel") if name == "bidirectional" else None
         else:
             nbytes = fwd_algorithmic(B, H, L, d)[1]
             kern = "chunk_out"
-            traffic = measured_traffic("chunk_out_ws_kernel_l2" if name == "l2_denominator" else "chunk_out_ws_kernel")
+            traffic = {"l2_denominator": measured_traffic("chunk_out_ws_kernel_l2"),
+                       "continuation": measured_traffic("chunk_out_ws_kernel")}.get(name)
         gbs = nbytes / (t_out * 1e-3) / 1e9
         res[name] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3), "steps": steps,
                      "kernel_ms": dict(zip(KERNELS[:-1] + [kern], per)),
@@ -192,6 +199,11 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
                                        "(initial state per head, positions 65536..131071)")
     res["l2_denominator"]["workload"] = ("long-context causal forward with the L2 denominator "
                                          "sqrt(sum s^2) + 1e-6, B=1 H=32 L=65536 d=128 bf16")
+    res["l2_bidirectional"]["workload"] = ("long-context bidirectional forward with the L2 denominator "
+                                           "(whole-document S and A), B=1 H=32 L=65536 d=128 bf16")
+    for c in (16, 32, 128):
+        res[f"chunk_{c}"]["workload"] = (f"long-context causal forward with {c}-token chunks (generic "
+                                         "output kernel), B=1 H=32 L=65536 d=128 bf16")
     return res
 
 
@@ -297,6 +309,30 @@ def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
     ms_saved = ev.elapsed(0, 1) / steps
     res["with_forward_states"] = {"ms_per_call": ms_saved, "tokens_per_s": B * L / (ms_saved * 1e-3),
                                   "steps": steps, "note": "states read from the forward's workspace"}
+    # the bidirectional mode's backward (every token reads its document's whole states)
+    bdesc = rla.make_desc(B, H, L, d, rla.BF16, bidirectional=True)
+    nb = ctypes.c_size_t(0)
+    rla.lib().rla2_bwd_workspace_size(ctypes.byref(bdesc), ctypes.byref(nb))
+    wsb = torch.empty(max(nb.value, 1), dtype=torch.uint8, device=q.device)
+
+    def run_bidir():
+        rla.bwd(q, k, v, gq, gk, dout, out=outs, workspace=wsb, bidirectional=True)
+
+    for _ in range(3):
+        run_bidir()
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        run_bidir()
+    ev.hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms_bi = ev.elapsed(0, 1) / steps
+    res["bidirectional"] = {
+        "workload": "backward of the long-context bidirectional forward (B=1 H=32 L=65536 d=128 bf16)",
+        "ms_per_call": ms_bi, "tokens_per_s": B * L / (ms_bi * 1e-3), "steps": steps,
+        "roofline": {"kernel": "whole backward", "bound": "hbm", "achieved": need / (ms_bi * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": need / (ms_bi * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "algorithmic_bytes": need}}
     return res
 
 

@@ -1478,13 +1478,19 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
 // two chunks are in flight in registers. q'.z: bf16, one more MFMA tile per state wave, z as
 // the bf16 pair hi + lo (rows 4i hold hi, rows 4i + 1 lo, so every lane's accumulator has
 // both for its token; products exact, fp32 sums); fp32, a dot product in the map step.
+// L2 (the original RLA's denominator over the whole document, RLA page §2.1, §4.1 causal=false):
+// out_t = q'_t S_doc / (sqrt(q'_t^T A_doc q'_t) + eps). The second document state A arrives in
+// its own records; the state waves also hold it as MFMA operands, form A Q'^T beside S^T Q'^T and
+// dot it with q' for their part of each row's quadratic form (LDS, by chunk parity). The rows are
+// staged unnormalised and scaled by 1/(sqrt(q'^T A q') + eps) as they leave in the next step,
+// after the barrier that completes the quadratic forms (bf16: rounded twice, <= 2 2^-9 relative).
 
-template <bool BF, int D>
-__global__ __launch_bounds__(NT, 2) void readout_kernel(
+template <bool BF, int D, bool L2>
+__global__ __launch_bounds__(NT, (L2 && D == 128) ? 1 : 2) void readout_kernel(
     const typename Elem<BF>::St* __restrict__ q, const float* __restrict__ gamma_q, const int32_t* __restrict__ tab,
     const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
-    const float* __restrict__ states, typename Elem<BF>::St* __restrict__ out, int H, int L, float rms_eps,
-    float eps) {
+    const float* __restrict__ states, const float* __restrict__ astates, typename Elem<BF>::St* __restrict__ out,
+    int H, int L, float rms_eps, float eps) {
   using G = Geo<BF, D>;
   using St = typename G::St;
   using R = Raw<BF, D>;
@@ -1497,6 +1503,7 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
   __shared__ __attribute__((aligned(16))) St sO[2 * BUF];
   __shared__ __attribute__((aligned(16))) float sZ[D];
   __shared__ float sInv[2 * kChunk];
+  __shared__ float sQuad[L2 ? 2 * 4 * kChunk : 1];  // L2: each state wave's part of q'^T A q', by chunk parity
 
   const int seg = blockIdx.x, h = blockIdx.y;
   if (seg >= *nseg) return;  // the whole workgroup leaves together
@@ -1525,21 +1532,26 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
   // S^T as the A operand of O^T = S^T Q'^T, value columns of this wave (bf16: read into the
   // contiguous-order tile map, whose slots match the 16-byte Q' fragments)
   Frag<BF> sa[G::KB][G::CT];
+  Frag<BF> aa[L2 ? G::KB : 1][G::CT];  // L2: A (symmetric, so A^T) in the same tile map
   {
     const int wv = wave < G::NW ? wave : 0;
-    auto tile = [&](int rt, int ct) {
-      if constexpr (BF) return *reinterpret_cast<const floatx4*>(rec + rec_frag_c<D>(wv, rt, ct, lane));
-      else return *reinterpret_cast<const floatx4*>(rec + rec_frag<BF, D>(wv, rt, ct, lane));
+    auto tile = [&](const float* r, int rt, int ct) {
+      if constexpr (BF) return *reinterpret_cast<const floatx4*>(r + rec_frag_c<D>(wv, rt, ct, lane));
+      else return *reinterpret_cast<const floatx4*>(r + rec_frag<BF, D>(wv, rt, ct, lane));
     };
+    const float* arec = L2 ? astates + ((size_t)seg * H + h) * (size_t)(D * D + D) : nullptr;
 #pragma unroll
     for (int kb2 = 0; kb2 < G::KB; ++kb2)
 #pragma unroll
-      for (int ct = 0; ct < G::CT; ++ct) sa[kb2][ct] = acc_frag<BF>(tile(2 * kb2, ct), tile(2 * kb2 + 1, ct));
+      for (int ct = 0; ct < G::CT; ++ct) {
+        sa[kb2][ct] = acc_frag<BF>(tile(rec, 2 * kb2, ct), tile(rec, 2 * kb2 + 1, ct));
+        if constexpr (L2) aa[kb2][ct] = acc_frag<BF>(tile(arec, 2 * kb2, ct), tile(arec, 2 * kb2 + 1, ct));
+      }
   }
   // bf16: z as the A operand of the q'.z tile, contiguous slot order (slot (g, j) of k-block kb
   // is dim 32 kb + 8g + j): rows 4i hold bf16(z), rows 4i + 1 the residual, the rest zeros
   Frag<true> zfr[BF ? G::KB : 1];
-  if constexpr (BF) {
+  if constexpr (BF && !L2) {
 #pragma unroll
     for (int kb2 = 0; kb2 < G::KB; ++kb2)
 #pragma unroll
@@ -1563,7 +1575,7 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
       R o;
       feature_map_lane<BF, D, tok>(r, o, g1, g2, lo, hi, rms_eps);
       store_rows<BF, D, tok>(sQ + (c & 1) * BUFQ, o, t0, m, QP);
-      if constexpr (!BF) {  // fp32: q'.z here, against z in LDS
+      if constexpr (!BF && !L2) {  // fp32: q'.z here, against z in LDS
         float p = 0.f;
 #pragma unroll
         for (int e = 0; e < G::E; ++e) {
@@ -1583,12 +1595,16 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
   auto mma_chunk = [&](int c) {
     const St* cQ = sQ + (c & 1) * BUFQ;
     St* cO = sO + (c & 1) * BUF;
-    floatx4 o4[G::CT][4], dn[4];
+    floatx4 o4[G::CT][4], dn[4], y4[L2 ? G::CT : 1][4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       dn[t4] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) o4[ct][t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (L2) {
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) y4[ct][t4] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
     }
 #pragma unroll
     for (int kb2 = 0; kb2 < G::KB; ++kb2)
@@ -1598,14 +1614,32 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
         if constexpr (BF) qf = lds_frag_c(cQ, QP, t4 * 16 + c16, kb2, g);
         else qf = lds_frag<BF>(cQ, QP, t4 * 16 + c16, kb2, g);
 #pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) o4[ct][t4] = mma(sa[kb2][ct], qf, o4[ct][t4]);
-        if constexpr (BF) dn[t4] = mma(zfr[kb2], qf, dn[t4]);
+        for (int ct = 0; ct < G::CT; ++ct) {
+          o4[ct][t4] = mma(sa[kb2][ct], qf, o4[ct][t4]);
+          if constexpr (L2) y4[ct][t4] = mma(aa[kb2][ct], qf, y4[ct][t4]);
+        }
+        if constexpr (BF && !L2) dn[t4] = mma(zfr[kb2], qf, dn[t4]);
       }
+    if constexpr (L2) {  // this wave's part of q'^T A q' for every row of the chunk
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        float part = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          const St* qrow = cQ + (t4 * 16 + c16) * QP + wave * G::DVW + ct * 16 + 4 * g;  // q' at the columns
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part = __builtin_fmaf(Elem<BF>::to_f(qrow[i]), y4[ct][t4][i], part);
+        }
+        part = sum_rows4(part);
+        if (g == 0) sQuad[((c & 1) * 4 + wave) * kChunk + t4 * 16 + c16] = part;
+      }
+    }
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const int t = t4 * 16 + c16;  // this lane's row; columns col .. col + 3
       float rr;
-      if constexpr (BF) rr = 1.0f / (dn[t4][0] + dn[t4][1] + eps);
+      if constexpr (L2) rr = 1.f;  // scaled as the row leaves
+      else if constexpr (BF) rr = 1.0f / (dn[t4][0] + dn[t4][1] + eps);
       else rr = sInv[(c & 1) * kChunk + t];
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) {
@@ -1627,8 +1661,23 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
 #pragma unroll
     for (int i = tid; i < kChunk * PPR; i += NT) {
       const int rr = i / PPR, pc = i % PPR;
-      __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(cO + rr * G::ROWP + pc * EPP), ro,
-                                             ((c * kChunk + rr) * D + pc * EPP) * G::ES, 0, kLoadStream);
+      u32x4 piece = *reinterpret_cast<const u32x4*>(cO + rr * G::ROWP + pc * EPP);
+      if constexpr (L2) {  // 1/(sqrt(q'^T A q') + eps) of the row, from the state waves' parts
+        float quad = 0.f;
+#pragma unroll
+        for (int w = 0; w < G::NW; ++w) quad += sQuad[((c & 1) * 4 + w) * kChunk + rr];
+        const float sc = 1.0f / (__builtin_sqrtf(quad) + eps);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (BF) {
+            piece[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(
+                float2v{__uint_as_float(piece[j] << 16) * sc, __uint_as_float(piece[j] & 0xffff0000u) * sc}, bf16x2));
+          } else {
+            piece[j] = __float_as_uint(__uint_as_float(piece[j]) * sc);
+          }
+        }
+      }
+      __builtin_amdgcn_raw_buffer_store_b128(piece, ro, ((c * kChunk + rr) * D + pc * EPP) * G::ES, 0, kLoadStream);
     }
   };
   R set0, set1;
@@ -1650,117 +1699,6 @@ __global__ __launch_bounds__(NT, 2) void readout_kernel(
     if (c + 1 < nch && wave < G::NW) mma_chunk(c + 1);
     store_chunk(c);
     __syncthreads();
-  }
-}
-
-// ----------------------------------------------------------------------------------------
-// readout_l2 (bidirectional forward with the original RLA's L2 denominator): per (segment,
-// head), every token reads its document's whole states, out_t = q'_t S_doc / (sqrt(q'_t^T
-// A_doc q'_t) + eps) (RLA page §2.1 closed form over the whole document, §4.1 causal=false).
-// Both document states arrive in the segment's records (S, then A); the state waves round them
-// once to the MFMA operand type. Per 64-token block: every lane maps two tokens of q into LDS;
-// wave w < NW forms O^T = S^T Q'^T and A^T Q'^T for its columns, dots the latter with q' for its
-// part of the quadratic form; after a barrier the rows are scaled and written.
-
-template <bool BF, int D>
-__global__ __launch_bounds__(NT, (D == 128) ? 1 : 2) void readout_l2_kernel(
-    const typename Elem<BF>::St* __restrict__ q, const float* __restrict__ gamma_q, const int32_t* __restrict__ tab,
-    const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
-    const float* __restrict__ states, const float* __restrict__ astates, typename Elem<BF>::St* __restrict__ out,
-    int H, int L, float rms_eps, float eps) {
-  using G = Geo<BF, D>;
-  using St = typename G::St;
-  using EL = Elem<BF>;
-  __shared__ __attribute__((aligned(16))) St sQ[kChunk * G::ROWP];
-  __shared__ float sQuad[4 * kChunk];
-
-  const int seg = blockIdx.x, h = blockIdx.y;
-  if (seg >= *nseg) return;
-  const SegInfo si = read_seg(tab, seg);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t0 = 2 * (tid >> 3), m = tid & 7;
-  const int c16 = lane & 15, g = lane >> 4;
-  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
-  const float* gq = gamma_q + (size_t)h * D;
-  const int wv = wave < G::NW ? wave : 0;  // waves without state columns keep a harmless copy
-  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
-  const float* arec = astates + ((size_t)seg * H + h) * (size_t)(D * D + D);
-  Frag<BF> Sa[G::KB][G::CT], Aa[G::KB][G::CT];  // S^T, A^T (= A) as A operands, this wave's columns
-#pragma unroll
-  for (int kb2 = 0; kb2 < G::KB; ++kb2)
-#pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct) {
-      auto tile = [&](const float* r, int rt) {
-        return *reinterpret_cast<const floatx4*>(r + rec_frag<BF, D>(wv, rt, ct, lane));
-      };
-      Sa[kb2][ct] = acc_frag<BF>(tile(rec, 2 * kb2), tile(rec, 2 * kb2 + 1));
-      Aa[kb2][ct] = acc_frag<BF>(tile(arec, 2 * kb2), tile(arec, 2 * kb2 + 1));
-    }
-  const int nblk = (si.len + kChunk - 1) / kChunk;
-  for (int blk = 0; blk < nblk; ++blk) {
-    const int nv = min(kChunk, si.len - blk * kChunk);
-    __syncthreads();  // the previous block's LDS reads are done
-    {
-      Raw<BF, D> rq, oq;
-      load_raw<BF, D>(rq, q + (tok0 + (size_t)blk * kChunk) * D, t0, m, nv);
-      feature_map_pair<BF, D>(rq, oq, gq, rope_lo, rope_hi + (size_t)(si.hirow + blk) * G::HALF, t0, m, rms_eps);
-      store_rows<BF, D>(sQ, oq, t0, m);
-    }
-    __syncthreads();
-    floatx4 o[G::CT][4];
-    if (wave < G::NW) {
-      float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ct = 0; ct < G::CT; ++ct) {
-        const int col = wave * G::DVW + ct * 16 + 4 * g;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          floatx4 x = floatx4{0.f, 0.f, 0.f, 0.f}, y = x;
-#pragma unroll
-          for (int kb2 = 0; kb2 < G::KB; ++kb2) {
-            const Frag<BF> qf = lds_frag<BF>(sQ, G::ROWP, tt * 16 + c16, kb2, g);
-            x = mma(Sa[kb2][ct], qf, x);
-            y = mma(Aa[kb2][ct], qf, y);
-          }
-          o[ct][tt] = x;
-          const St* qrow = sQ + (tt * 16 + c16) * G::ROWP + col;  // q'_t at dims col .. col + 3
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part[tt] = __builtin_fmaf(EL::to_f(qrow[i]), y[i], part[tt]);
-        }
-      }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const float pp = sum_rows4(part[tt]);
-        if (g == 0) sQuad[wave * kChunk + tt * 16 + c16] = pp;
-      }
-    }
-    __syncthreads();
-    if (wave < G::NW) {
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int t = tt * 16 + c16;
-        float quad = 0.f;
-#pragma unroll
-        for (int w = 0; w < G::NW; ++w) quad += sQuad[w * kChunk + t];
-        const float r = 1.0f / (__builtin_sqrtf(quad) + eps);
-        if (t < nv) {
-#pragma unroll
-          for (int ct = 0; ct < G::CT; ++ct) {
-            const int col = wave * G::DVW + ct * 16 + 4 * g;
-            St* dst = out + (tok0 + (size_t)blk * kChunk + t) * D + col;
-            const floatx4 x = o[ct][tt];
-            if constexpr (BF) {
-              const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{x[0] * r, x[1] * r}, bf16x2));
-              const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{x[2] * r, x[3] * r}, bf16x2));
-              *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-            } else {
-              *reinterpret_cast<float4*>(dst) = make_float4(x[0] * r, x[1] * r, x[2] * r, x[3] * r);
-            }
-          }
-        }
-      }
-    }
   }
 }
 
@@ -2069,13 +2007,14 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   if (e != hipSuccess) return e;
   mark(3);
   if (fwd && p.n_seg_max > 0 && p.bidirectional && p.l2) {
-    hipLaunchKernelGGL((readout_l2_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+    hipLaunchKernelGGL((readout_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                        static_cast<const St*>(a.q), a.gq, tab, nseg, rlo, rhi, states,
                        reinterpret_cast<const float*>(a.ws + p.off_astates), static_cast<St*>(a.out), p.H, p.L,
                        a.rms_eps, a.eps);
   } else if (fwd && p.n_seg_max > 0 && p.bidirectional) {
-    hipLaunchKernelGGL((readout_kernel<BF, D>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s, static_cast<const St*>(a.q),
-                       a.gq, tab, nseg, rlo, rhi, states, static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
+    hipLaunchKernelGGL((readout_kernel<BF, D, false>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
+                       static_cast<const St*>(a.q), a.gq, tab, nseg, rlo, rhi, states, nullptr,
+                       static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
   } else if (fwd && p.n_seg_max > 0) {
     const float* astates = p.l2 ? reinterpret_cast<const float*>(a.ws + p.off_astates) : nullptr;
     if (BF && p.chunk == kChunk) {
