@@ -327,9 +327,15 @@ def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
     ev.hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     ms_bi = ev.elapsed(0, 1) / steps
+    per_bi = [0.0] * len(BWD_KERNELS)
+    for _ in range(steps):
+        rla.bwd(q, k, v, gq, gk, dout, out=outs, workspace=wsb, bidirectional=True, events=ev.arr)
+        for i in range(len(BWD_KERNELS)):
+            per_bi[i] += ev.elapsed(i, i + 1)
     res["bidirectional"] = {
         "workload": "backward of the long-context bidirectional forward (B=1 H=32 L=65536 d=128 bf16)",
         "ms_per_call": ms_bi, "tokens_per_s": B * L / (ms_bi * 1e-3), "steps": steps,
+        "kernel_ms": dict(zip(BWD_KERNELS, [x / steps for x in per_bi])),
         "roofline": {"kernel": "whole backward", "bound": "hbm", "achieved": need / (ms_bi * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": need / (ms_bi * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "algorithmic_bytes": need}}

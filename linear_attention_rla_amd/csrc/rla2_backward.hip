@@ -154,7 +154,7 @@ __device__ __forceinline__ void map_backward(const Raw<true, D>& r, Raw<true, D>
 // sum_t Q^_t g_t^T (d x d, fragment-native like the forward records) and sum_t Q^_t gd_t den_t
 // (where the z of a forward record sits); Q^_t = bf16(q'_t / den_t), den and gd from bwd_dq.
 
-template <int D>
+template <int D, bool ALL>
 __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q,
     const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
@@ -174,7 +174,9 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
   if (!bwd_go(hdr) || seg >= *nseg) return;
   const SegInfo si = read_seg_clamped(tab, seg, L, lim);
   if (si.len == 0) return;  // only a corrupted table has empty segments
-  if (si.pos0 == 0) return;  // a document's first segment: no earlier segment reads its total
+  // causal: a document's first segment is skipped (no earlier segment reads its total);
+  // bidirectional (ALL): every segment's total goes into the document's
+  if (!ALL && si.pos0 == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
@@ -336,7 +338,7 @@ __device__ __forceinline__ void split_frag(floatx4 a, floatx4 b, Frag<true>& hi,
                                           pack_bf2(b[2] - bf_lo(h3), b[3] - bf_hi(h3))});
 }
 
-template <int D>
+template <int D, bool BIDIR>
 __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
@@ -476,8 +478,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
     auto issue = [&](R (&x)[3], float2 (&hr)[E], int c) {
       hi_row(hr, c, m);
       load_raw_buf<true, D>(x[0], rq, c * C2 + t0, m);
-      load_raw_buf<true, D>(x[1], rk, c * C2 + t0, m);
-      load_raw_buf<true, D>(x[2], rv, c * C2 + t0, m);
+      if constexpr (!BIDIR) {  // the bidirectional dq needs no k or v (no scores, no state update)
+        load_raw_buf<true, D>(x[1], rk, c * C2 + t0, m);
+        load_raw_buf<true, D>(x[2], rv, c * C2 + t0, m);
+      }
     };
     auto fstep = [&](int st, R (&x)[3], float2 (&hr)[E]) {
       if (st < ns) {
@@ -486,7 +490,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
 #pragma unroll
         for (int tok = 0; tok < 2; ++tok) {
           const float invq = rms_inv<true, D>(x[0], tok, rms_eps);
-          const float invk = rms_inv<true, D>(x[1], tok, rms_eps);
+          const float invk = BIDIR ? 0.f : rms_inv<true, D>(x[1], tok, rms_eps);
 #pragma unroll
           for (int e = 0; e < E; e += 2) {
             float q1[2], q2[2], k1[2], k2[2];
@@ -494,15 +498,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
             for (int y = 0; y < 2; ++y) {
               const float2 cs = angle_sum(hr[e + y], lo[tok][e + y]);
               rope_pair(x[0].get(tok, 0, e + y), x[0].get(tok, 1, e + y), invq, gq1[e + y], gq2[e + y], cs, q1[y], q2[y]);
-              rope_pair(x[1].get(tok, 0, e + y), x[1].get(tok, 1, e + y), invk, gk1[e + y], gk2[e + y], cs, k1[y], k2[y]);
+              if constexpr (!BIDIR)
+                rope_pair(x[1].get(tok, 0, e + y), x[1].get(tok, 1, e + y), invk, gk1[e + y], gk2[e + y], cs, k1[y], k2[y]);
             }
             put_pairs<true, D>(oq, tok, e, q1, q2);
-            put_pairs<true, D>(ok, tok, e, k1, k2);
+            if constexpr (!BIDIR) put_pairs<true, D>(ok, tok, e, k1, k2);
           }
         }
         store_rows<true, D>(sQ + b, oq, t0, m, QP);
-        store_rows<true, D>(sK + b, ok, t0, m, QP);
-        store_rows<true, D>(sV + b, x[2], t0, m, QP);
+        if constexpr (!BIDIR) {
+          store_rows<true, D>(sK + b, ok, t0, m, QP);
+          store_rows<true, D>(sV + b, x[2], t0, m, QP);
+        }
         store_rows<true, D>(sRq + (st % 3) * BUF, x[0], t0, m);
       }
       issue(x, hr, st + 2);  // into the registers just consumed
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       const uint16_t* cK = sK + (c & 1) * BUFQ;
       const uint16_t* cV = sV + (c & 1) * BUFQ;
       const uint16_t* cG = sG + (c & 1) * BUFQ;
-      const float* zc = sZ + (c & 1) * D;
+      const float* zc = sZ + (BIDIR ? 0 : (c & 1) * D);  // bidirectional: the document's z throughout
       // ---- phase A: this wave's rows of S G^T (state as a bf16 pair) and its part of q'.(S g)
       floatx4 Y[CT][2];
       Frag<true> Gf[2][KB];
@@ -591,7 +598,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
           if (g == 0) sIdot[wave * C2 + tt * 16 + c16] = part;
         }
       }
-      if (wave >= 2) {  // z after this sub-chunk, into the other parity
+      if (!BIDIR && wave >= 2) {  // z after this sub-chunk, into the other parity
         const Frag<true> ones = ones_frag<true>();
         float* zn = sZ + ((c + 1) & 1) * D;
         uint16_t* zf16 = reinterpret_cast<uint16_t*>(sZf + ((c + 1) & 1) * KB * 64);
@@ -619,7 +626,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       if (wave < 2) {
         Frag<true> Qf[KB], Gt[KB];  // the query tile's rows (read again: no runtime register index)
         floatx4 zq = floatx4{0.f, 0.f, 0.f, 0.f};
-        const Frag<true>* zf = sZf + (c & 1) * KB * 64;
+        const Frag<true>* zf = sZf + (BIDIR ? 0 : (c & 1) * KB * 64);
         Frag<true> Zf[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -634,7 +641,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
           At[kt] = Bt[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-          if (kt <= tt) {
+          if (!BIDIR && kt <= tt) {  // bidirectional: the block's keys are inside the document's states
             Frag<true> Kt[KB], Vt[KB];  // key tile kt's rows, requested before its MFMAs
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
@@ -700,7 +707,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
             const bool self = kt == tt && 4 * g + i == c16;
             x[kt][i] = before ? __builtin_fmaf(Bt[kt][i], inv, gdv) : (self ? bdv : 0.f);
           }
-        sB[tt * 64 + lane] = acc_frag<true>(x[0], x[1]);
+        if constexpr (!BIDIR) sB[tt * 64 + lane] = acc_frag<true>(x[0], x[1]);
       }
       // the K' column fragments (for dQ' and the state update) and this wave's z values do not
       // depend on phase B: requested before the meeting
@@ -708,7 +715,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       float4 zv[CT];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        Kc[ct] = lds_frag_tr(cK, QP, 0, (wave & 3) * G::DVW + 16 * ct, lane);
+        if constexpr (!BIDIR) Kc[ct] = lds_frag_tr(cK, QP, 0, (wave & 3) * G::DVW + 16 * ct, lane);
         zv[ct] = *reinterpret_cast<const float4*>(zc + (wave & 3) * G::DVW + 16 * ct + 4 * g);
       }
       meet += 4;
@@ -722,10 +729,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         for (int tq = 0; tq < 2; ++tq) {
           invs[tq] = sInv[tq * 16 + c16];
           gds[tq] = sGd[tq * 16 + c16];
-          bfs[tq] = sB[tq * 64 + lane];
+          if constexpr (!BIDIR) bfs[tq] = sB[tq * 64 + lane];
         }
         Frag<true> avn[2];  // the state update's row fragments, one tile ahead
-        avn[0] = lds_frag_tr_s8(cV, QP, 0, 0, lane);
+        if constexpr (!BIDIR) avn[0] = lds_frag_tr_s8(cV, QP, 0, 0, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tq = 0; tq < 2; ++tq) {
@@ -737,18 +744,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
             floatx4 acc = Y[ct][tq];
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(acc[i], inv, gdv * zv[ct][i]);
-            acc = mma(Kc[ct], bfs[tq], acc);
+            if constexpr (!BIDIR) acc = mma(Kc[ct], bfs[tq], acc);
             *reinterpret_cast<floatx4*>(dqb + tc * FP + a0) = acc;
           }
         }
-        // S^T += V^T K' (the 32 tokens are one k-block)
+        // S^T += V^T K' (the 32 tokens are one k-block); bidirectional: the state is the document's
+        if constexpr (!BIDIR) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const int cur = rt & 1, nxt = cur ^ 1;
-          if (rt + 1 < RT) avn[nxt] = lds_frag_tr_s8(cV, QP, 0, 32 * ((rt + 1) / 2) + 4 * ((rt + 1) % 2), lane);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int rt = 0; rt < RT; ++rt) {
+            const int cur = rt & 1, nxt = cur ^ 1;
+            if (rt + 1 < RT) avn[nxt] = lds_frag_tr_s8(cV, QP, 0, 32 * ((rt + 1) / 2) + 4 * ((rt + 1) % 2), lane);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) ST[rt][ct] = mma(avn[cur], Kc[ct], ST[rt][ct]);
+            for (int ct = 0; ct < CT; ++ct) ST[rt][ct] = mma(avn[cur], Kc[ct], ST[rt][ct]);
+          }
         }
       }
     }
@@ -799,7 +808,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
 //          the map backward of k for sub-chunk j - 2 from its dk' rows and the ring.
 // One workgroup barrier per step; the MMA waves also meet once among themselves.
 
-template <int D>
+template <int D, bool BIDIR>
 __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q, const float* __restrict__ gamma_k,
@@ -883,9 +892,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
     }
     float2 lo[2][E], hr[E];  // angles of the sub-chunk mapped back next, loaded a step ahead
     R ga, gb;  // raw dout of an even / odd step
-    auto issue = [&](R& x, int j) { load_raw_buf<true, D>(x, rg, sub_ld(j) * C2 + t0, m); };
+    // (the bidirectional dk, dv need no dout: P and p are the document's totals)
+    auto issue = [&](R& x, int j) {
+      if constexpr (!BIDIR) load_raw_buf<true, D>(x, rg, sub_ld(j) * C2 + t0, m);
+    };
     auto bstep = [&](int st, R& x) {
-      if (st < ns) store_rows<true, D>(sG + (st & 1) * BUFQ, x, t0, m, QP);
+      if (!BIDIR && st < ns) store_rows<true, D>(sG + (st & 1) * BUFQ, x, t0, m, QP);
       issue(x, st + 2);
       const int j = st - 2;
       if (j >= 0 && j < ns) {
@@ -922,14 +934,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
     R xa[3], xb[3];  // raw q, k, v of an even / odd step
     auto issue = [&](R (&x)[3], float2 (&hr)[E], float (&tv)[3][2], int j) {
       hi_row(hr, sub(j), m);
-      load_raw_buf<true, D>(x[0], rq, sub_ld(j) * C2 + t0, m);
+      if constexpr (!BIDIR) load_raw_buf<true, D>(x[0], rq, sub_ld(j) * C2 + t0, m);
       load_raw_buf<true, D>(x[1], rk, sub_ld(j) * C2 + t0, m);
       load_raw_buf<true, D>(x[2], rv, sub_ld(j) * C2 + t0, m);
+      if constexpr (!BIDIR) {
 #pragma unroll
-      for (int tok = 0; tok < 2; ++tok) {  // den, gd, bd (tokens past the segment read 0 and weigh nothing)
-        tv[0][tok] = load_tok(rd, sub_ld(j) * C2 + t0 + tok);
-        tv[1][tok] = load_tok(rw, sub_ld(j) * C2 + t0 + tok);
-        tv[2][tok] = load_tok(rb, sub_ld(j) * C2 + t0 + tok);
+        for (int tok = 0; tok < 2; ++tok) {  // den, gd, bd (tokens past the segment read 0 and weigh nothing)
+          tv[0][tok] = load_tok(rd, sub_ld(j) * C2 + t0 + tok);
+          tv[1][tok] = load_tok(rw, sub_ld(j) * C2 + t0 + tok);
+          tv[2][tok] = load_tok(rb, sub_ld(j) * C2 + t0 + tok);
+        }
       }
     };
     auto fstep = [&](int st, R (&x)[3], float2 (&hr)[E], float (&tv)[3][2]) {
@@ -938,7 +952,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
         R oq, ok, oh;
 #pragma unroll
         for (int tok = 0; tok < 2; ++tok) {
-          const float invq = rms_inv<true, D>(x[0], tok, rms_eps);
+          const float invq = BIDIR ? 0.f : rms_inv<true, D>(x[0], tok, rms_eps);
           const float invk = rms_inv<true, D>(x[1], tok, rms_eps);
 #pragma unroll
           for (int e = 0; e < E; e += 2) {
@@ -946,22 +960,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
 #pragma unroll
             for (int y = 0; y < 2; ++y) {
               const float2 cs = angle_sum(hr[e + y], lo[tok][e + y]);
-              rope_pair(x[0].get(tok, 0, e + y), x[0].get(tok, 1, e + y), invq, gq1[e + y], gq2[e + y], cs, q1[y], q2[y]);
+              if constexpr (!BIDIR)
+                rope_pair(x[0].get(tok, 0, e + y), x[0].get(tok, 1, e + y), invq, gq1[e + y], gq2[e + y], cs, q1[y], q2[y]);
               rope_pair(x[1].get(tok, 0, e + y), x[1].get(tok, 1, e + y), invk, gk1[e + y], gk2[e + y], cs, k1[y], k2[y]);
             }
-            put_pairs<true, D>(oq, tok, e, q1, q2);
+            if constexpr (!BIDIR) put_pairs<true, D>(oq, tok, e, q1, q2);
             put_pairs<true, D>(ok, tok, e, k1, k2);
           }
         }
         const float dn[2] = {tv[0][0], tv[0][1]}, gdl[2] = {tv[1][0], tv[1][1]}, bdl[2] = {tv[2][0], tv[2][1]};
         const float inv[2] = {dn[0] > 0.f ? 1.0f / dn[0] : 0.f, dn[1] > 0.f ? 1.0f / dn[1] : 0.f};
-        scale_raw<D>(oq, oh, inv);
-        store_rows<true, D>(sQ + b, oq, t0, m, QP);
+        if constexpr (!BIDIR) {
+          scale_raw<D>(oq, oh, inv);
+          store_rows<true, D>(sQ + b, oq, t0, m, QP);
+          store_rows<true, D>(sH + b, oh, t0, m, QP);
+        }
         store_rows<true, D>(sK + b, ok, t0, m, QP);
         store_rows<true, D>(sV + b, x[2], t0, m, QP);
-        store_rows<true, D>(sH + b, oh, t0, m, QP);
         store_rows<true, D>(sRk + (st % 3) * BUF, x[1], t0, m);
-        if (m == 0) {
+        if (!BIDIR && m == 0) {
 #pragma unroll
           for (int tok = 0; tok < 2; ++tok) {
             const int ix = (st & 1) * C2 + t0 + tok;
@@ -1019,9 +1036,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
         const uint16_t* cG = sG + pb * BUFQ;
         const uint16_t* cH = sH + pb * BUFQ;
         const float* cI = sI + pb * C2;
-        const float* pc = sP + pb * D;
-        // ---- phase A (waves 0, 1): key tile kt = wave
-        if (wave < 2) {
+        const float* pc = sP + (BIDIR ? 0 : pb * D);  // bidirectional: the document's p throughout
+        // ---- phase A (waves 0, 1): key tile kt = wave (the bidirectional sweep has no
+        // in-block terms: every query's contribution is in the document's P and p)
+        if (!BIDIR && wave < 2) {
           const int kt = wave;
           const int key = kt * 16 + c16;
           Frag<true> Kf[KB], Vf[KB];
@@ -1066,8 +1084,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           sAp[kt * 64 + lane] = acc_frag<true>(xa[0], xa[1]);
           sBp[kt * 64 + lane] = acc_frag<true>(xb[0], xb[1]);
         }
-        meet += 4;
-        mma_wave_sync(&sArrive, meet, lane, polls, hdr);
+        if constexpr (!BIDIR) {
+          meet += 4;
+          mma_wave_sync(&sArrive, meet, lane, polls, hdr);
+        }
         // ---- phase B: this wave's rows of dK'^T and dV^T, then the states. The k-blocks are the
         // outer loop, so every V and K' fragment is read once for both column tiles, and each
         // k-block's fragments are requested one k-block ahead (the last k-block requests the
@@ -1096,7 +1116,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
                 fv[nxt][kt] = lds_frag_c(cV, QP, kt * 16 + c16, kb + 1, g);
                 fk[nxt][kt] = lds_frag_c(cK, QP, kt * 16 + c16, kb + 1, g);
               }
-            } else {
+            } else if constexpr (!BIDIR) {
 #pragma unroll
               for (int ct = 0; ct < CT; ++ct) {
                 qt[ct] = lds_frag_tr(cQ, QP, 0, wave * G::DVW + 16 * ct, lane);
@@ -1125,24 +1145,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
           }
           // the reverse-state update's row fragments, requested while the closing terms run
           Frag<true> Hc[CT], Gc[CT], grn[2], hrn[2];
+          if constexpr (!BIDIR) {
 #pragma unroll
-          for (int ct = 0; ct < CT; ++ct) {
-            Hc[ct] = lds_frag_tr(cH, QP, 0, wave * G::DVW + 16 * ct, lane);
-            Gc[ct] = lds_frag_tr(cG, QP, 0, wave * G::DVW + 16 * ct, lane);
+            for (int ct = 0; ct < CT; ++ct) {
+              Hc[ct] = lds_frag_tr(cH, QP, 0, wave * G::DVW + 16 * ct, lane);
+              Gc[ct] = lds_frag_tr(cG, QP, 0, wave * G::DVW + 16 * ct, lane);
+            }
+            grn[0] = lds_frag_tr_s8(cG, QP, 0, 0, lane);
+            hrn[0] = lds_frag_tr_s8(cH, QP, 0, 0, lane);
           }
-          grn[0] = lds_frag_tr_s8(cG, QP, 0, 0, lane);
-          hrn[0] = lds_frag_tr_s8(cH, QP, 0, 0, lane);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) {
             const int a0 = wave * G::DVW + 16 * ct + 4 * g;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-              y[ct][kt] = mma(qt[ct], bq[kt], y[ct][kt]);
+              if constexpr (!BIDIR) y[ct][kt] = mma(qt[ct], bq[kt], y[ct][kt]);
 #pragma unroll
               for (int i = 0; i < 4; ++i) y[ct][kt][i] += pc[a0 + i];
               *reinterpret_cast<floatx4*>(dkb + (kt * 16 + c16) * FP + a0) = y[ct][kt];
-              z[ct][kt] = mma(gt[ct], aq[kt], z[ct][kt]);
+              if constexpr (!BIDIR) z[ct][kt] = mma(gt[ct], aq[kt], z[ct][kt]);
               const int key = kt * 16 + c16;
               // keys past the segment are dropped; these 8-byte pieces of a row come from four
               // waves, so they carry the default cache policy and meet in L2 as whole lines (with
@@ -1155,9 +1177,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
             }
           }
           // P^T += G^T Q^ and P += Q^^T G (the 32 tokens are one k-block); each row tile's two
-          // fragments are requested one tile ahead
+          // fragments are requested one tile ahead. Bidirectional: the states are the document's.
 #pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
+          for (int rt = 0; rt < (BIDIR ? 0 : RT); ++rt) {
             const int cur = rt & 1, nxt = cur ^ 1;
             if (rt + 1 < RT) {
               grn[nxt] = lds_frag_tr_s8(cG, QP, 0, 32 * ((rt + 1) / 2) + 4 * ((rt + 1) % 2), lane);
@@ -1171,7 +1193,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkv_ws_kernel(
             }
           }
         }
-        if (wave == 0) {  // p after this sub-chunk, into the other parity: p += Q^^T (gd den)
+        if (!BIDIR && wave == 0) {  // p after this sub-chunk, into the other parity: p += Q^^T (gd den)
           Frag<true> w_hi, w_lo;
           token_col_frags(sW + pb * C2, 0, g, w_hi, w_lo);
           float* pn = sP + ((j + 1) & 1) * D;
@@ -1240,8 +1262,8 @@ __global__ void bwd_dgamma_kernel(const float* __restrict__ part, const int32_t*
 }
 
 // ----------------------------------------------------------------------------------------
-// Generic backward: fp32 activations in both modes and bf16 in the bidirectional mode (the
-// bf16 causal backward runs the warp-specialised sweeps above). Same formulas as the sweeps
+// Generic backward: fp32 activations in both modes (bf16 runs the warp-specialised sweeps
+// above, causal and bidirectional). Same formulas as the sweeps
 // (RLA page §4.2): with g = dL/dout, per query t the forward quantities are formed again,
 //   causal:         den_t = q'_t . z_prev + sum_{i<=t} a_ti + eps,
 //                   g . num_t = q'_t . (S_prev g_t) + sum_{i<=t} a_ti (g_t . v_i)
@@ -2037,21 +2059,23 @@ hipError_t run_backward_generic(const Plan& p, const FwdArgs& a, const BwdArgs& 
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool BIDIR>
 hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s, hipEvent_t* ev) {
   auto mark = [&](int i) {
     if (ev != nullptr) (void)hipEventRecord(ev[i], s);
   };
-  // the forward's segment table, RoPE tables and prefix records: formed again, or read from
-  // the workspace of the matching forward (same plan, so the same offsets)
+  // the forward's segment table, RoPE tables and state records (causal: the prefix before each
+  // segment; bidirectional: the document's totals): formed again, or read from the workspace of
+  // the matching forward (same plan, so the same offsets)
+  const int fmode = BIDIR ? SCAN_TOTAL : SCAN_PREFIX;
   hipError_t e = hipSuccess;
   if (b.saved == nullptr) {
-    e = launch_fwd_states(p, a, s, ev, SCAN_PREFIX);
+    e = launch_fwd_states(p, a, s, ev, fmode);
     if (e != hipSuccess) return e;
   } else {
     // the forward's plan stamp against this plan: the backward kernels run only on a match
     mark(0);
-    e = launch_saved_check(p, b.saved, a.ws, a.cu, SCAN_PREFIX, s);
+    e = launch_saved_check(p, b.saved, a.ws, a.cu, fmode, s);
     if (e != hipSuccess) return e;
     for (int i = 1; i < 3; ++i) mark(i);
   }
@@ -2078,17 +2102,17 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   const auto* g = static_cast<const uint16_t*>(b.dout);
   const dim3 grid(p.n_seg_max, p.H);
   mark(3);
-  hipLaunchKernelGGL((bwd_dq_ws_kernel<D>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
+  hipLaunchKernelGGL((bwd_dq_ws_kernel<D, BIDIR>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
                      states, static_cast<uint16_t*>(b.dq), den, gd, bd, dgp, p.H, p.L, a.rms_eps, a.eps, hdr,
                      p.wait_polls, lim);
   mark(4);
-  hipLaunchKernelGGL((bwd_pstate_kernel<D>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
+  hipLaunchKernelGGL((bwd_pstate_kernel<D, BIDIR>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
                      pstates, p.H, p.L, a.rms_eps, hdr, lim);
   mark(5);
-  e = launch_scan_records(p, fw, pstates, SCAN_SUFFIX, hdr, s);
+  e = launch_scan_records(p, fw, pstates, BIDIR ? SCAN_TOTAL : SCAN_SUFFIX, hdr, s);
   if (e != hipSuccess) return e;
   mark(6);
-  hipLaunchKernelGGL((bwd_dkv_ws_kernel<D>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
+  hipLaunchKernelGGL((bwd_dkv_ws_kernel<D, BIDIR>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
                      pstates, den, gd, bd, static_cast<uint16_t*>(b.dk), static_cast<uint16_t*>(b.dv), dgp, p.H, p.L,
                      a.rms_eps, hdr, p.wait_polls, lim);
   mark(7);
@@ -2104,8 +2128,7 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
 hipError_t launch_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipStream_t s, hipEvent_t* ev) {
   const bool bf = p.dtype == 1, causal = !p.bidirectional;
 #define RLA2_BWD(DD)                                                                                  \
-  if (bf && causal) return run_backward<DD>(p, a, b, s, ev);                                        \
-  if (bf) return run_backward_generic<true, DD, false>(p, a, b, s, ev);                            \
+  if (bf) return causal ? run_backward<DD, false>(p, a, b, s, ev) : run_backward<DD, true>(p, a, b, s, ev); \
   return causal ? run_backward_generic<false, DD, true>(p, a, b, s, ev)                             \
                 : run_backward_generic<false, DD, false>(p, a, b, s, ev)
   switch (p.d) {
