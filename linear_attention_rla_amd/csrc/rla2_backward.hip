@@ -116,6 +116,11 @@ __device__ __forceinline__ void map_backward(const Raw<true, D>& r, Raw<true, D>
   constexpr int E = G::E;
 #pragma unroll
   for (int tok = 0; tok < 2; ++tok) {
+    // the lane's dx' values of both halves, read whole and gated below (a read behind the gate
+    // compiles to one masked 4-byte read per value)
+    float dp1[E], dp2[E];
+    copy_bytes<E * 4>(dp1, dxp + (t0 + tok) * fp + m * E);
+    copy_bytes<E * 4>(dp2, dxp + (t0 + tok) * fp + G::HALF + m * E);
     const float inv = rms_inv<true, D>(r, tok, rms_eps);
     float dy1[E], dy2[E];
     float T = 0.f;
@@ -125,8 +130,8 @@ __device__ __forceinline__ void map_backward(const Raw<true, D>& r, Raw<true, D>
       const float x1 = r.get(tok, 0, e), x2 = r.get(tok, 1, e);
       float u1, u2;
       rope_pair(x1, x2, inv, g1[e], g2[e], cs, u1, u2);
-      const float d1 = u1 > 0.f ? dxp[(t0 + tok) * fp + m * E + e] : 0.f;
-      const float d2 = u2 > 0.f ? dxp[(t0 + tok) * fp + G::HALF + m * E + e] : 0.f;
+      const float d1 = u1 > 0.f ? dp1[e] : 0.f;
+      const float d2 = u2 > 0.f ? dp2[e] : 0.f;
       dy1[e] = __builtin_fmaf(d1, cs.x, d2 * cs.y);     // inverse rotation
       dy2[e] = __builtin_fmaf(d2, cs.x, -(d1 * cs.y));
       T = __builtin_fmaf(g1[e] * dy1[e], x1, T);
