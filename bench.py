@@ -182,7 +182,7 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
         if name in ("bidirectional", "l2_bidirectional"):  # read-out: q read and out written once, bf16
             nbytes = B * H * L * d * 2 * 2
             kern = "readout" if name == "bidirectional" else "readout_l2"
-            traffic = measured_traffic("readout_kernel") if name == "bidirectional" else None
+            traffic = measured_traffic("readout_kernel" if name == "bidirectional" else "readout_kernel_l2")
         else:
             nbytes = fwd_algorithmic(B, H, L, d)[1]
             kern = "chunk_out"
@@ -336,6 +336,13 @@ def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
         "workload": "backward of the long-context bidirectional forward (B=1 H=32 L=65536 d=128 bf16)",
         "ms_per_call": ms_bi, "tokens_per_s": B * L / (ms_bi * 1e-3), "steps": steps,
         "kernel_ms": dict(zip(BWD_KERNELS, [x / steps for x in per_bi])),
+        # the sweeps in this mode: dq reads q, dout and writes dq and the per-token den, gd, B_tt;
+        # dk, dv read k, v and write dk, dv (no scores: every token reads the document's totals)
+        **{name: {"bound": "hbm", "achieved": nb / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                  "frac": nb / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": nb,
+                  "traffic": measured_traffic(name + "_bidir_kernel")}
+           for name, nb, t in (("bwd_dq", (3 * row + 12) * th, per_bi[BWD_KERNELS.index("bwd_dq")] / steps),
+                               ("bwd_dkv", 4 * row * th, per_bi[BWD_KERNELS.index("bwd_dkv")] / steps))},
         "roofline": {"kernel": "whole backward", "bound": "hbm", "achieved": need / (ms_bi * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": need / (ms_bi * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "algorithmic_bytes": need}}

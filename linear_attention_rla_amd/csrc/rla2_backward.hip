@@ -49,14 +49,6 @@
 namespace rla2 {
 namespace {
 
-// bf16 pair, round to nearest even
-__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2));
-}
-// the two bf16 halves of a packed word as floats
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 // q'/den per token, rounded to bf16 (the query operand of the reverse states); inv = 1/den.
 template <int D, int ONLY = -1>  // ONLY >= 0: that token of the pair alone
 __device__ __forceinline__ void scale_raw(const Raw<true, D>& x, Raw<true, D>& o, const float (&inv)[2]) {

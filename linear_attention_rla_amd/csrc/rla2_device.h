@@ -45,6 +45,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// bf16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{a, b}, bf16x2));
+}
+// the two bf16 halves of a packed word as floats
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 template <bool BF>
 struct Elem;
 template <>
@@ -611,6 +619,119 @@ __device__ __forceinline__ void store_raw_buf(const Raw<BF, D>& r, __amdgpu_buff
         __builtin_amdgcn_raw_buffer_store_b32(r.w[t][hh][0], rs, off, 0, kLoadStream);
       }
     }
+}
+
+// ----------------------------------------------------------------------------------------
+// Token-split tiles for kernels in which a token's result depends only on its own rows and on
+// document states that do not change along the sweep (here the bidirectional read-out with the
+// L2 denominator). A wave takes 16 tokens; lane (t = l % 16, g = l / 16) holds
+// token t's dims 32 kb + 8g + j, j < 8, of every k-block kb < d/32. That set is at once
+//  - the B-operand slots of the token's row in k-block kb (slot j = contraction index 8g + j),
+//  - the rows the lane receives in the output tiles 2p, 2p + 1 of a product whose tile 2p + h,
+//    row 4g + i stands for dim 32 p + 8g + 4h + i (so output dims 32 p + 8g .. + 7 are one
+//    16-byte piece of the token's row),
+//  - closed under the rotate-half pairing for d >= 64 (dims a and a + d/2 sit in k-blocks kb and
+//    kb + d/64 of the same lane),
+// so a token goes from its raw row to its stored result in the lane's registers; a per-token
+// reduction is a sum over the four lanes t + 16g (sum_rows4). The constant states enter as
+// A-operand fragments in LDS, built once per workgroup from the record (ql_operands).
+
+template <int D>
+struct QL {
+  static_assert(D >= 64 && D % 64 == 0, "rotate-half pairs must stay in the lane");
+  static constexpr int KB = D / 32;  // k-blocks: 16-byte pieces of a lane's part of a row
+  static constexpr int NP = KB / 2;  // k-blocks of the first RoPE half
+  static constexpr int R = D / 16;   // 16-dim output tiles
+};
+
+// Raw row piece of token `tok` (segment-relative) through a range-checked buffer resource:
+// tokens past the segment read zeros.
+template <int D>
+__device__ __forceinline__ void ql_load(u32x4 (&x)[D / 32], __amdgpu_buffer_rsrc_t rs, int tok, int g) {
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb)
+    x[kb] = __builtin_amdgcn_raw_buffer_load_b128(rs, (tok * D + 32 * kb + 8 * g) * 2, 0, kLoadStream);
+}
+
+// element j < 8 of a 16-byte bf16 piece
+__device__ __forceinline__ float ql_elem(const u32x4& x, int j) {
+  return __uint_as_float(j & 1 ? (x[j >> 1] & 0xffff0000u) : (x[j >> 1] << 16));
+}
+
+// 1/rms of the token (the four lanes of the token together)
+template <int D>
+__device__ __forceinline__ float ql_rms_inv(const u32x4 (&x)[D / 32], float rms_eps) {
+  float part[4] = {0.f, 0.f, 0.f, 0.f};  // four independent chains
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // through a scalar: a bit cast applied to the vector element itself compiled to element
+      // 0 for every w (hipcc 7.2)
+      const uint32_t word = x[kb][w];
+      const bf16x2 p = __builtin_bit_cast(bf16x2, word);
+      part[w] = __builtin_amdgcn_fdot2_f32_bf16(p, p, part[w], false);
+    }
+  float ss = (part[0] + part[1]) + (part[2] + part[3]);
+  ss = sum_rows4(ss);
+  return rsqrtf(__builtin_fmaf(ss, 1.0f / D, rms_eps));
+}
+
+// x' = ReLU(RoPE(RMSNorm(x))) of the lane's dims, rounded to bf16, as B-operand fragments;
+// gam[kb][j] = gamma of dim 32 kb + 8g + j, cs[kb][j] (kb < d/64) = (cos, sin) of the token's
+// angle for the pair (32 kb + 8g + j, + d/2). The arithmetic is the chunk kernels' (rope_pair,
+// then ReLU of the RNE rounding as a 16-bit signed max).
+template <int D>
+__device__ __forceinline__ void ql_map(const u32x4 (&x)[D / 32], float inv, const float (&gam)[D / 32][8],
+                                       const float2 (&cs)[D / 64][8], Frag<true> (&xf)[D / 32]) {
+  constexpr int NP = D / 64;
+  const i16x2 zero = i16x2{0, 0};
+#pragma unroll
+  for (int kb = 0; kb < NP; ++kb) {
+    u32x4 w1, w2;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      float u1[2], u2[2];
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        rope_pair(ql_elem(x[kb], j + y), ql_elem(x[kb + NP], j + y), inv, gam[kb][j + y], gam[kb + NP][j + y],
+                  cs[kb][j + y], u1[y], u2[y]);
+      w1[j >> 1] = __builtin_bit_cast(
+          uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2, __builtin_convertvector(float2v{u1[0], u1[1]}, bf16x2)), zero));
+      w2[j >> 1] = __builtin_bit_cast(
+          uint32_t, __builtin_elementwise_max(__builtin_bit_cast(i16x2, __builtin_convertvector(float2v{u2[0], u2[1]}, bf16x2)), zero));
+    }
+    xf[kb].v = __builtin_bit_cast(bf16x8, w1);
+    xf[kb + NP].v = __builtin_bit_cast(bf16x8, w2);
+  }
+}
+
+// A-operand fragments of a d x d record state M (fragment-native, rec_frag) for products
+// over token-split tiles, written to LDS as [tile T][k-block kb][lane] 16-byte fragments
+// (8 bf16 each). TRANS: the operand is M^T (its rows are M's columns, the contraction runs
+// over M's rows), else M. Each element is rounded to bf16 into `hi` and, when `lo` is given,
+// the rest (element - hi) rounded to bf16 into `lo`, so hi + lo carries ~16 significant bits.
+// Operand row r lands in tile 2 (r / 32) + (r / 4) % 2, row 4 ((r % 32) / 8) + r % 4 (the output
+// dims of the tiles above); contraction index c in k-block c / 32, slot 8 ((c % 32) / 8) + c % 8.
+template <int D, bool TRANS>
+__device__ __forceinline__ void ql_operands(uint16_t* hi, uint16_t* lo, const float* rec, int tid, int nthr) {
+  using G = Geo<true, D>;
+  constexpr int KB = D / 32;
+  for (int e = tid; e < D * D; e += nthr) {
+    const int i = e & 3, l = (e >> 2) & 63;
+    int rest = e >> 8;
+    const int ct = rest % G::CT;
+    rest /= G::CT;
+    const int rt = rest % G::RT, w = rest / G::RT;
+    const int a = 16 * rt + 4 * (l >> 4) + i, v = w * G::DVW + 16 * ct + (l & 15);
+    const int r = TRANS ? v : a, c = TRANS ? a : v;
+    const int T = 2 * (r >> 5) + ((r >> 2) & 1), m = 4 * ((r & 31) >> 3) + (r & 3);
+    const int idx = ((T * KB + (c >> 5)) * 64 + 16 * ((c & 31) >> 3) + m) * 8 + (c & 7);
+    const float x = rec[e];
+    const uint16_t hb = f2bf(x);
+    hi[idx] = hb;
+    if (lo != nullptr) lo[idx] = f2bf(x - bf2f(hb));
+  }
 }
 
 }  // namespace

@@ -1703,6 +1703,131 @@ __global__ __launch_bounds__(NT, (L2 && D == 128) ? 1 : 2) void readout_kernel(
 }
 
 // ----------------------------------------------------------------------------------------
+// readout_l2_ql (bidirectional forward with the L2 denominator, bf16, d = 64 or 128): the
+// read-out on token-split tiles. Every output row needs only its own q and the document's
+// states, so each wave carries whole 16-token tiles from the raw q to the stored row in
+// registers (the lane layout of QL above): RMS statistic over the token's four lanes, RoPE
+// and ReLU in the lane, O^T = S^T Q'^T and A Q'^T on the MFMA with S^T and A (A is symmetric;
+// both rounded once to bf16) as A operands that the workgroup builds in LDS from the segment's
+// records, q'^T A q' in the lane and over its four lanes, and the row stored as 16-byte
+// pieces. The loop has no barrier and no LDS traffic besides those operand reads and the
+// segment's RoPE and gamma rows. 8 waves, one workgroup per CU; wave w takes the 16-token tile
+// w % 4 of chunks w / 4, w / 4 + 2, ..., two tiles per pass, so a lane's in-chunk position,
+// and with it its row of the fine RoPE table, is fixed for the whole loop.
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void readout_l2_ql_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ gamma_q, const int32_t* __restrict__ tab,
+    const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
+    const float* __restrict__ states, const float* __restrict__ astates, uint16_t* __restrict__ out, int H, int L,
+    float rms_eps, float eps) {
+  using Q = QL<D>;
+  constexpr int KB = Q::KB, NP = Q::NP, R = Q::R, HALF = D / 2;
+  __shared__ Frag<true> sS[R * KB * 64];  // S^T operands [tile][k-block][lane]
+  __shared__ Frag<true> sA[R * KB * 64];  // A operands
+  __shared__ __attribute__((aligned(16))) float2 sHi[kMaxSegChunks * HALF];  // the segment's RoPE chunk rows
+  __shared__ __attribute__((aligned(16))) float sGam[D];  // gamma_q of the head
+
+  const int seg = blockIdx.x, h = blockIdx.y;
+  if (seg >= *nseg) return;  // the whole workgroup leaves together
+  const SegInfo si = read_seg(tab, seg);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
+  const int c16 = lane & 15, g = lane >> 4;
+  const size_t tok0 = ((size_t)si.row * H + h) * (size_t)L + si.start;
+  const int seg_bytes = si.len * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void*)(q + tok0 * D), 0, seg_bytes, kBufFlags);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc((void*)(out + tok0 * D), 0, seg_bytes, kBufFlags);
+  const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
+  ql_operands<D, true>(reinterpret_cast<uint16_t*>(sS), nullptr, rec, tid, 512);
+  ql_operands<D, true>(reinterpret_cast<uint16_t*>(sA), nullptr, astates + ((size_t)seg * H + h) * (size_t)(D * D + D),
+                       tid, 512);
+  for (int i = tid; i < min(nch, kMaxSegChunks) * HALF; i += 512) sHi[i] = rope_hi[(size_t)si.hirow * HALF + i];
+  if (tid < D) sGam[tid] = gamma_q[(size_t)h * D + tid];
+  const int pos = (wave & 3) * 16 + c16;  // the lane's in-chunk position
+  float2 lo[NP][8];
+#pragma unroll
+  for (int kb = 0; kb < NP; ++kb)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lo[kb][j] = rope_lo[pos * HALF + 32 * kb + 8 * g + j];
+  __syncthreads();  // operands, gamma and RoPE rows in LDS
+
+  // two tiles per pass, tile u of chunk c + 2u (chunks past the segment read zeros and are never
+  // stored), so that every operand fragment read from LDS serves both
+  // each tile's registers are refilled with its tile of the next pass as soon as the tile is
+  // mapped, so the raw q of the next pass is in flight during this pass's products and stores
+  auto pass = [&](int c, u32x4 (&x0)[KB], u32x4 (&x1)[KB]) {
+    // the operands are read from LDS per pass: kept in registers across the loop (the
+    // compiler's choice, as the LDS does not change) they would take 128 VGPRs at d = 128
+    asm volatile("" ::: "memory");
+    Frag<true> qf[2][KB];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4(&x)[KB] = u ? x1 : x0;
+      const int cu = min(c + 2 * u, nch - 1);  // the RoPE row (a chunk past the segment maps zeros)
+      const float inv = ql_rms_inv<D>(x, rms_eps);
+      float2 cs[NP][8];
+#pragma unroll
+      for (int kb = 0; kb < NP; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) cs[kb][j] = angle_sum(sHi[cu * HALF + 32 * kb + 8 * g + j], lo[kb][j]);
+      float gam[KB][8];  // gamma at the lane's dims (LDS broadcast reads)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) copy_bytes<32>(gam[kb], sGam + 32 * kb + 8 * g);
+      ql_map<D>(x, inv, gam, cs, qf[u]);
+      ql_load<D>(x, rq, (c + 4 + 2 * u) * kChunk + pos, g);
+    }
+    floatx4 o[2][R];
+    float quad[2][2] = {{0.f, 0.f}, {0.f, 0.f}};  // two chains per tile
+#pragma unroll
+    for (int t = 0; t < R; ++t) {
+      o[0][t] = o[1][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const Frag<true> f = sS[(t * KB + kb) * 64 + lane];
+        o[0][t] = mma(f, qf[0][kb], o[0][t]);
+        o[1][t] = mma(f, qf[1][kb], o[1][t]);
+      }
+      // q'^T A q' from A Q'^T: tile 2p + h row 4g + i is dim 32 p + 8g + 4h + i
+      floatx4 y[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const Frag<true> f = sA[(t * KB + kb) * 64 + lane];
+        y[0] = mma(f, qf[0][kb], y[0]);
+        y[1] = mma(f, qf[1][kb], y[1]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          quad[u][t & 1] = __builtin_fmaf(static_cast<float>(qf[u][t >> 1].v[4 * (t & 1) + i]), y[u][i], quad[u][t & 1]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float rr = 1.0f / (__builtin_sqrtf(sum_rows4(quad[u][0] + quad[u][1])) + eps);
+      const int tok = (c + 2 * u) * kChunk + pos;
+#pragma unroll
+      for (int p = 0; p < KB; ++p) {
+        u32x4 w;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          w[2 * hh] = pack_bf2(o[u][2 * p + hh][0] * rr, o[u][2 * p + hh][1] * rr);
+          w[2 * hh + 1] = pack_bf2(o[u][2 * p + hh][2] * rr, o[u][2 * p + hh][3] * rr);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, (tok * D + 32 * p + 8 * g) * 2, 0, 0);  // past the segment: dropped
+      }
+    }
+  };
+  // chunks c0, c0 + 2, ... in passes of two
+  const int c0 = wave >> 2;
+  u32x4 xa[KB], xb[KB];
+  ql_load<D>(xa, rq, c0 * kChunk + pos, g);
+  ql_load<D>(xb, rq, (c0 + 2) * kChunk + pos, g);
+  for (int c = c0; c < nch; c += 4) pass(c, xa, xb);
+}
+
+// ----------------------------------------------------------------------------------------
 // feature_map: the preamble alone, x' = ReLU(RoPE(RMSNorm(x))) materialised. Per (segment,
 // head, tensor): the same lane mapping and device functions as the chunk kernels (two
 // tokens per 8 lanes), so x' is bitwise what the forward forms internally; raw x and the
@@ -2006,7 +2131,15 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
   hipError_t e = run_states<BF, D>(p, a, s, ev, mode);
   if (e != hipSuccess) return e;
   mark(3);
-  if (fwd && p.n_seg_max > 0 && p.bidirectional && p.l2) {
+  if (fwd && p.n_seg_max > 0 && p.bidirectional && p.l2 && BF && D >= 64) {
+    // the token-split read-out: 344 -> 267 us on the long-context workload (the column-split
+    // one runs one wave per SIMD there); with the Sum denominator the column-split read-out is
+    // the faster (207 against 240 us), so it keeps that mode
+    hipLaunchKernelGGL((readout_l2_ql_kernel<(D >= 64 ? D : 64)>), dim3(p.n_seg_max, p.H), dim3(512), 0, s,
+                       static_cast<const uint16_t*>(a.q), a.gq, tab, nseg, rlo, rhi, states,
+                       reinterpret_cast<const float*>(a.ws + p.off_astates), static_cast<uint16_t*>(a.out), p.H, p.L,
+                       a.rms_eps, a.eps);
+  } else if (fwd && p.n_seg_max > 0 && p.bidirectional && p.l2) {
     hipLaunchKernelGGL((readout_kernel<BF, D, true>), dim3(p.n_seg_max, p.H), dim3(NT), 0, s,
                        static_cast<const St*>(a.q), a.gq, tab, nseg, rlo, rhi, states,
                        reinterpret_cast<const float*>(a.ws + p.off_astates), static_cast<St*>(a.out), p.H, p.L,

@@ -134,7 +134,7 @@ def test_backward_modes_deterministic(bidir):
         inp = workloads.fwd_inputs(1, 2, 333, 128, dtype, seed=2400, lengths=[100, 233])
         dout = workloads.cotangent(inp.q.shape, seed=2401).to(dtype)
         a = _run(inp, dout, bidir)
-        for _ in range(20):
+        for _ in range(50):  # bitwise determinism, 50 runs (segment-ordered sums, no atomics)
             b = _run(inp, dout, bidir)
             for x, y in zip(a, b):
                 assert torch.equal(x, y)
@@ -175,3 +175,28 @@ def test_bidirectional_backward_packed_workload_sampled():
     print("bwd bidir packed T=16384 sampled: " + " ".join(f"{n_} {e:.2e}" for n_, e in worst.items()))
     for n_, e in worst.items():
         assert e <= TOL_BF16, (n_, e)
+
+
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.bfloat16), (32, torch.float32)])
+@pytest.mark.parametrize("bidir", [False, True])
+def test_backward_with_a_large_eps(d, dtype, bidir):
+    # With the default eps the scale of q' all but cancels in the output (numerator and
+    # denominator are both linear in q'), and so, largely, in the gradients; with eps of the
+    # size of the denominator the gradients depend on it, so this checks the backward's RMS
+    # statistic of q too: the oracle's gradients move by >= 10x the bar when gamma_q doubles.
+    inp = workloads.fwd_inputs(1, 2, 300, d, dtype, seed=950 + d, lengths=[120, 1, 179])
+    dout = workloads.cotangent(inp.q.shape, seed=951 + d).to(dtype)
+    eps = 300.0
+    cu = inp.cu_seqlens.to(DEV)
+    q, k, v, gq, gk = (x.to(DEV) for x in (inp.q, inp.k, inp.v, inp.gamma_q, inp.gamma_k))
+    got = rla.bwd(q, k, v, gq, gk, dout.to(DEV), cu, eps=eps, bidirectional=bidir)
+    torch.cuda.synchronize()
+    cu_np = inp.cu_seqlens.numpy()
+    args = (f64(inp.q), f64(inp.k), f64(inp.v))
+    ref = oracle.bwd(*args, f64(inp.gamma_q), f64(inp.gamma_k), f64(dout), cu_np, eps, inp.rms_eps, inp.rope_base,
+                     causal=not bidir)
+    ref2 = oracle.bwd(*args, 2 * f64(inp.gamma_q), f64(inp.gamma_k), f64(dout), cu_np, eps, inp.rms_eps,
+                      inp.rope_base, causal=not bidir)
+    tol = TOL_F32 if dtype == torch.float32 else TOL_BF16
+    assert grad_row_err(torch.from_numpy(ref2[0]), ref[0]) >= 10 * tol
+    _check(got, ref, dtype, f"bwd {'bidir' if bidir else 'causal'} eps={eps} [1,2,300,{d}] {dtype}", bidir)

@@ -348,6 +348,8 @@ def _oracle_opts(inp, **kw):
     (1, 1, 190, 64, torch.float32, None, True, 0, 2),
     (1, 2, 150, 32, torch.float32, [20, 130], False, 12345, 1),
     (2, 1, 129, 32, torch.bfloat16, None, True, 70000, 0),
+    (1, 2, 1000, 128, torch.bfloat16, [300, 1, 699], True, 0, 1),
+    (2, 2, 700, 64, torch.bfloat16, None, True, 5, 3),
 ])
 @pytest.mark.parametrize("with_init", [False, True])
 def test_initial_state_and_bidirectional(B, H, L, d, dtype, lengths, bidir, pos, seg_chunks, with_init):
@@ -464,3 +466,45 @@ def test_feature_map_c4_size_sampled():
         zq.append(_check_feature_map(qo[0, h, rows], f64(inp.q[0, h, rows]), f64(inp.gamma_q[h]), rows, torch.bfloat16))
         _check_feature_map(ko[0, h, rows], f64(inp.k[0, h, rows]), f64(inp.gamma_k[h]), rows, torch.bfloat16)
     print(f"long-context feature map: fraction of exact zeros in q' {np.mean(zq):.3f}")
+
+
+def test_bidirectional_long_context_sampled():
+    # the long-context workload (one 65536-token document per head) in the bidirectional mode
+    inp = workloads.c4_long()
+    q, k, v, gq, gk, _ = on_gpu(inp)
+    out = rla.fwd(q, k, v, gq, gk, bidirectional=True)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp.q.shape[2], 16, seed=17)
+    worst = 0.0
+    for h in (0, 31):
+        ref = oracle.fwd_rows(inp.q, inp.k, inp.v, f64(inp.gamma_q), f64(inp.gamma_k), 0, h, rows, None, inp.eps,
+                              inp.rms_eps, inp.rope_base, causal=False)
+        worst = max(worst, row_rel_err(out[0, h, rows], ref))
+    print(f"bidirectional long context sampled: max row rel err {worst:.3e}")
+    assert worst <= TOL_BF16
+
+
+@pytest.mark.parametrize("d,dtype", [(128, torch.bfloat16), (64, torch.bfloat16), (32, torch.bfloat16),
+                                     (32, torch.float32)])
+@pytest.mark.parametrize("bidir", [False, True])
+@pytest.mark.parametrize("l2", [False, True])
+def test_query_scale_seen_with_a_large_eps(d, dtype, bidir, l2):
+    # Both denominators are homogeneous in q' (degree 1, like the numerator), so with the
+    # default eps a wrong scale of q' (e.g. a wrong RMS statistic of q) all but cancels in the
+    # output. With eps of the size of the denominator the output depends on that scale: the
+    # oracle's output moves by >= 10x the bar when gamma_q doubles, and every forward kernel
+    # must still match it.
+    inp = workloads.fwd_inputs(1, 2, 300, d, dtype, seed=900 + d, lengths=[120, 1, 179])
+    eps = 10.0 if l2 else 300.0
+    q, k, v, gq, gk, cu = on_gpu(inp)
+    out = rla.fwd(q, k, v, gq, gk, cu, eps=eps, bidirectional=bidir, l2_denominator=l2)
+    torch.cuda.synchronize()
+    f = oracle.fwd_l2 if l2 else oracle.fwd
+    args = (f64(inp.q), f64(inp.k), f64(inp.v))
+    cu_np = inp.cu_seqlens.numpy()
+    ref = f(*args, f64(inp.gamma_q), f64(inp.gamma_k), cu_np, eps=eps, causal=not bidir)
+    ref2 = f(*args, 2 * f64(inp.gamma_q), f64(inp.gamma_k), cu_np, eps=eps, causal=not bidir)
+    assert row_rel_err(torch.from_numpy(ref2), ref) >= 10 * tol(inp)
+    err = row_rel_err(out, ref)
+    print(f"d={d} {dtype} bidir={bidir} l2={l2} eps={eps}: max row rel err {err:.3e}")
+    assert err <= tol(inp)
