@@ -146,6 +146,55 @@ __device__ __forceinline__ void map_backward(const Raw<true, D>& r, Raw<true, D>
 }
 
 
+// map_backward with the forward mapper's results handed over: the ReLU gates of the lane's
+// elements (gate[tok] bit 2e: dim m E + e, bit 2e + 1: its partner + D/2) and 1/rms of each
+// token, as the forward mapper formed them for the same rows, so the pre-activation is not
+// formed again; the arithmetic from the inverse rotation on is map_backward's, and so are the
+// results, bit for bit.
+template <int D>
+__device__ __forceinline__ void map_backward_gated(const Raw<true, D>& r, Raw<true, D>& dx, const float* dxp, int fp,
+                                                   const float (&g1)[Geo<true, D>::E], const float (&g2)[Geo<true, D>::E],
+                                                   const float2 (&lo)[2][Geo<true, D>::E],
+                                                   const float2 (&hi)[Geo<true, D>::E], const float (&invs)[2],
+                                                   const uint32_t (&gate)[2], int t0, int m,
+                                                   float (&dg1)[Geo<true, D>::E], float (&dg2)[Geo<true, D>::E]) {
+  using G = Geo<true, D>;
+  constexpr int E = G::E;
+#pragma unroll
+  for (int tok = 0; tok < 2; ++tok) {
+    float dp1[E], dp2[E];
+    copy_bytes<E * 4>(dp1, dxp + (t0 + tok) * fp + m * E);
+    copy_bytes<E * 4>(dp2, dxp + (t0 + tok) * fp + G::HALF + m * E);
+    const float inv = invs[tok];
+    float dy1[E], dy2[E];
+    float T = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float2 cs = angle_sum(hi[e], lo[tok][e]);
+      const float x1 = r.get(tok, 0, e), x2 = r.get(tok, 1, e);
+      const float d1 = (gate[tok] >> (2 * e)) & 1u ? dp1[e] : 0.f;
+      const float d2 = (gate[tok] >> (2 * e + 1)) & 1u ? dp2[e] : 0.f;
+      dy1[e] = __builtin_fmaf(d1, cs.x, d2 * cs.y);     // inverse rotation
+      dy2[e] = __builtin_fmaf(d2, cs.x, -(d1 * cs.y));
+      T = __builtin_fmaf(g1[e] * dy1[e], x1, T);
+      T = __builtin_fmaf(g2[e] * dy2[e], x2, T);
+      dg1[e] = __builtin_fmaf(dy1[e], x1 * inv, dg1[e]);
+      dg2[e] = __builtin_fmaf(dy2[e], x2 * inv, dg2[e]);
+    }
+    T = sum8(T);
+    const float coef = inv * inv * inv * T * (1.0f / D);
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const float a0 = __builtin_fmaf(inv * g1[e], dy1[e], -(coef * r.get(tok, 0, e)));
+      const float a1 = __builtin_fmaf(inv * g1[e + 1], dy1[e + 1], -(coef * r.get(tok, 0, e + 1)));
+      const float b0 = __builtin_fmaf(inv * g2[e], dy2[e], -(coef * r.get(tok, 1, e)));
+      const float b1 = __builtin_fmaf(inv * g2[e + 1], dy2[e + 1], -(coef * r.get(tok, 1, e + 1)));
+      dx.w[tok][0][e >> 1] = pack_bf2(a0, a1);
+      dx.w[tok][1][e >> 1] = pack_bf2(b0, b1);
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------------------
 // bwd_pstate: per (segment, head), the segment's totals of the reverse states,
 // sum_t Q^_t g_t^T (d x d, fragment-native like the forward records) and sum_t Q^_t gd_t den_t
@@ -357,6 +406,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t sV[2 * BUFQ];
   __shared__ __attribute__((aligned(16))) uint16_t sG[2 * BUFQ];
   __shared__ __attribute__((aligned(16))) uint16_t sRq[3 * BUF];  // raw q rows, ring of three
+  // bidirectional: the forward mapper's ReLU gates (a word per lane and token) and 1/rms per
+  // token, beside the raw rows in the ring, for the backward mappers
+  __shared__ uint32_t sGate[BIDIR ? 3 * C2 * 8 : 1];
+  __shared__ float sRinv[BIDIR ? 3 * C2 : 1];
   __shared__ __attribute__((aligned(16))) float sdQ[2 * C2 * FP];
   __shared__ Frag<true> sB[2 * 64];                    // B^T operands of query tiles 0, 1
   __shared__ __attribute__((aligned(16))) float sZ[2 * D];  // z before the sub-chunk, by parity
@@ -443,7 +496,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
       if (c >= 0 && c < ns) {
         R xq, dx;
         load_rows<D>(sRq + (c % 3) * BUF, t0, m, xq);
-        map_backward<D>(xq, dx, sdQ + (c & 1) * C2 * FP, FP, gq1, gq2, lo, hr, rms_eps, t0, m, dg1, dg2);
+        if constexpr (BIDIR) {
+          const float invs[2] = {sRinv[(c % 3) * C2 + t0], sRinv[(c % 3) * C2 + t0 + 1]};
+          const uint32_t gates[2] = {sGate[((c % 3) * C2 + t0) * 8 + m], sGate[((c % 3) * C2 + t0 + 1) * 8 + m]};
+          map_backward_gated<D>(xq, dx, sdQ + (c & 1) * C2 * FP, FP, gq1, gq2, lo, hr, invs, gates, t0, m, dg1, dg2);
+        } else {
+          map_backward<D>(xq, dx, sdQ + (c & 1) * C2 * FP, FP, gq1, gq2, lo, hr, rms_eps, t0, m, dg1, dg2);
+        }
         store_raw_buf<true, D>(dx, rdq, c * C2 + t0, m);  // rows past the segment are dropped
       }
       hi_row(hr, st - 1, m);  // the angles of sub-chunk st - 1, mapped back in the next step
@@ -488,6 +547,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
         for (int tok = 0; tok < 2; ++tok) {
           const float invq = rms_inv<true, D>(x[0], tok, rms_eps);
           const float invk = BIDIR ? 0.f : rms_inv<true, D>(x[1], tok, rms_eps);
+          uint32_t gm = 0u;  // bidirectional: the gates of the lane's elements
 #pragma unroll
           for (int e = 0; e < E; e += 2) {
             float q1[2], q2[2], k1[2], k2[2];
@@ -497,9 +557,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_ws_kernel(
               rope_pair(x[0].get(tok, 0, e + y), x[0].get(tok, 1, e + y), invq, gq1[e + y], gq2[e + y], cs, q1[y], q2[y]);
               if constexpr (!BIDIR)
                 rope_pair(x[1].get(tok, 0, e + y), x[1].get(tok, 1, e + y), invk, gk1[e + y], gk2[e + y], cs, k1[y], k2[y]);
+              if constexpr (BIDIR)
+                gm |= (q1[y] > 0.f ? 1u : 0u) << (2 * (e + y)) | (q2[y] > 0.f ? 2u : 0u) << (2 * (e + y));
             }
             put_pairs<true, D>(oq, tok, e, q1, q2);
             if constexpr (!BIDIR) put_pairs<true, D>(ok, tok, e, k1, k2);
+          }
+          if constexpr (BIDIR) {
+            sGate[((st % 3) * C2 + t0 + tok) * 8 + m] = gm;
+            if (m == 0) sRinv[(st % 3) * C2 + t0 + tok] = invq;
           }
         }
         store_rows<true, D>(sQ + b, oq, t0, m, QP);
