@@ -1020,12 +1020,17 @@ __global__ __launch_bounds__(NT, (L2 || D == 128) ? 1 : 2) void chunk_out_kernel
 // result as the next chunk's z operand (zf_next, the other buffer of the pair). Every LDS
 // operand is requested before the first MFMA.
 // L2: no q'.z and no column sums; the row's sum of squared weights goes to sInv instead.
-template <int D, int TT, int Z0, int Z1, int NZR, bool L2 = false>
+// Chunks of C < 64 tokens (C / 16 query tiles each): only the key tiles of the query tile's own
+// chunk become weights; the keys of the step's earlier chunks reach the query through the state,
+// which the MMA waves advance between the chunks, so the denominator takes their scores, unrounded
+// (Sum: the scores; L2: their squares), in place of q'.(z they added).
+template <int D, int TT, int Z0, int Z1, int NZR, bool L2 = false, int C = 64>
 __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK, int qp, const Frag<true>* sZf,
                                          Frag<true>* zf_next, float (&zreg)[NZR], Frag<true>* sA, float* sInv,
                                          float eps, int lane) {
   using G = Geo<true, D>;
   constexpr int KB = G::KB, NZ = Z1 - Z0, NP = TT / 2 + 1;
+  constexpr int KT0 = (TT / (C / 16)) * (C / 16);  // first key tile of the query tile's chunk
   static_assert(!L2 || NZ == 0, "");
   static_assert(NZ <= NZR, "");
   const int c16 = lane & 15, g = lane >> 4;
@@ -1066,8 +1071,9 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int kt = 2 * b + (i >> 1), r = 2 * (i & 1);
-      pw[b][i] = kt <= TT ? __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{At[kt % (TT + 1)][r], At[kt % (TT + 1)][r + 1]}, bf16x2))
-                          : 0u;
+      pw[b][i] = kt <= TT && kt >= KT0
+                     ? __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{At[kt % (TT + 1)][r], At[kt % (TT + 1)][r + 1]}, bf16x2))
+                     : 0u;
     }
   float rs = 0.f;
   const bf16x2 ones2 = bf16x2{static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
@@ -1079,6 +1085,10 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
       // Sum: the weights against ones; L2: the weights against themselves (sum of squares)
       rs = __builtin_amdgcn_fdot2_f32_bf16(w2, L2 ? w2 : ones2, rs, false);
     }
+#pragma unroll
+  for (int kt = 0; kt < KT0; ++kt)  // the step's earlier chunks (C < 64)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rs = L2 ? __builtin_fmaf(At[kt][i], At[kt][i], rs) : rs + At[kt][i];
   if constexpr (!L2) {
     if (g == 0) rs += zq[0] + zq[1];  // q'.z of query 16 TT + c16 (rows 0, 1 of Z Q'^T)
   }
@@ -1114,7 +1124,7 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
 // parts go to LDS) and advance A with its K'; the chunk's numerators are staged unnormalised
 // with the rows' sums of squared weights, and one step later each output row is scaled by
 // 1 / (sqrt(sum) + eps) as it leaves for memory. Nothing new waits inside a step.
-template <int D, bool L2 = false>
+template <int D, bool L2 = false, int C = 64>
 __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ gamma_q, const float* __restrict__ gamma_k, const int32_t* __restrict__ tab,
@@ -1345,19 +1355,19 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       if constexpr (L2) {
         float* rs2 = sRs2 + (st & 1) * kChunk;
         switch (wave) {
-          case 0: ws_score<D, 0, 0, 0, NZR, true>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
-          case 1: ws_score<D, 1, 0, 0, NZR, true>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
-          case 2: ws_score<D, 2, 0, 0, NZR, true>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
-          default: ws_score<D, 3, 0, 0, NZR, true>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
+          case 0: ws_score<D, 0, 0, 0, NZR, true, C>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
+          case 1: ws_score<D, 1, 0, 0, NZR, true, C>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
+          case 2: ws_score<D, 2, 0, 0, NZR, true, C>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
+          default: ws_score<D, 3, 0, 0, NZR, true, C>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
         }
       } else {
         const Frag<true>* zf = sZf + (c & 1) * G::KB * 64;  // z before chunk c
         Frag<true>* zn = sZf + ((c + 1) & 1) * G::KB * 64;  // z before chunk c + 1
         switch (wave) {
-          case 0: ws_score<D, 0, 0, Z1, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
-          case 1: ws_score<D, 1, Z1, Z2, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
-          case 2: ws_score<D, 2, Z2, Z3, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
-          default: ws_score<D, 3, Z3, G::RT, NZR>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          case 0: ws_score<D, 0, 0, Z1, NZR, false, C>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          case 1: ws_score<D, 1, Z1, Z2, NZR, false, C>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          case 2: ws_score<D, 2, Z2, Z3, NZR, false, C>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          default: ws_score<D, 3, Z3, G::RT, NZR, false, C>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
         }
       }
     }
@@ -1369,36 +1379,64 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
         Vf[ct][0] = lds_frag_tr(cV, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
         Vf[ct][1] = lds_frag_tr(cV, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
       }
-      // O^T for all 64 rows and this wave's columns: each Q' fragment is read once and
-      // serves every column tile
+      // S += K'^T V over the step's chunk u (C = 64: the whole step; C = 32: k-block u; C = 16:
+      // half of k-block u / 2, the other half's slots of the V operand zeroed)
+      constexpr int TPS = C / 16, NSUB = kChunk / C;  // query tiles per chunk, chunks per step
+      auto advance = [&](int u) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          if (C == 32 && kb2 != u) continue;
+          if (C == 16 && kb2 != u / 2) continue;
+          Frag<true> vb[G::CT];
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) {
+            vb[ct] = Vf[ct][kb2];
+            if constexpr (C == 16) {  // slots j < 4: tokens 32 kb2 + 4g + j; j >= 4: 16 further
+#pragma unroll
+              for (int j = 0; j < 4; ++j) vb[ct].v[(u & 1) ? j : 4 + j] = static_cast<__bf16>(0.f);
+            }
+          }
+#pragma unroll
+          for (int rt = 0; rt < G::RT; ++rt) {
+            const Frag<true> a = lds_frag_tr_s8(cK, QP, 32 * kb2, 32 * (rt / 2) + 4 * (rt % 2), lane);
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) S[rt][ct] = mma(a, vb[ct], S[rt][ct]);
+          }
+        }
+      };
+      // O^T for the 64 rows and this wave's columns, chunk by chunk: the query tiles of chunk u
+      // read the state before chunk u (advanced past the step's earlier chunks) and the weights
+      // of chunk u's own keys; each Q' fragment is read once and serves every column tile
       floatx4 o[G::CT][4];
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) o[ct][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb2 = 0; kb2 < G::KB; ++kb2) {
-        Frag<true> sa[G::CT];  // S^T rounded to bf16 as the A operand
+      for (int u = 0; u < NSUB; ++u) {
+        if (u > 0) advance(u - 1);
 #pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) sa[ct] = acc_frag<true>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
+        for (int kb2 = 0; kb2 < G::KB; ++kb2) {
+          Frag<true> sa[G::CT];  // S^T rounded to bf16 as the A operand
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const Frag<true> qf = lds_frag_c(cQ, QP, tt * 16 + c16, kb2, g);
+          for (int ct = 0; ct < G::CT; ++ct) sa[ct] = acc_frag<true>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
 #pragma unroll
-          for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(sa[ct], qf, o[ct][tt]);
+          for (int tt = u * TPS; tt < (u + 1) * TPS; ++tt) {
+            const Frag<true> qf = lds_frag_c(cQ, QP, tt * 16 + c16, kb2, g);
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(sa[ct], qf, o[ct][tt]);
+          }
         }
-      }
+        // the weights of the chunk's keys: key-tile pairs b (tiles 2b, 2b + 1) from the
+        // chunk's first pair up to the query tile's
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const Frag<true> a0 = sA[(tt * 2) * 64 + lane];
+        for (int tt = u * TPS; tt < (u + 1) * TPS; ++tt)
 #pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(Vf[ct][0], a0, o[ct][tt]);
-      }
+          for (int b = (u * TPS) / 2; b <= tt / 2; ++b) {
+            const Frag<true> ab = sA[(tt * 2 + b) * 64 + lane];
 #pragma unroll
-      for (int tt = 2; tt < 4; ++tt) {
-        const Frag<true> a1 = sA[(tt * 2 + 1) * 64 + lane];
-#pragma unroll
-        for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(Vf[ct][1], a1, o[ct][tt]);
+            for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(Vf[ct][b], ab, o[ct][tt]);
+          }
       }
       // each lane holds 4 consecutive columns of one row: 8-byte range-checked stores (rows
       // past the segment fall outside the buffer range and are dropped)
@@ -1414,15 +1452,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
           *reinterpret_cast<uint2*>(sO + (c & 1) * BUF + t * G::ROWP + col) = make_uint2(w0, w1);
         }
       }
-      // S += K'^T V
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int rt = 0; rt < G::RT; ++rt) {
-          const Frag<true> a = lds_frag_tr_s8(cK, QP, 32 * kb2, 32 * (rt / 2) + 4 * (rt % 2), lane);
-#pragma unroll
-          for (int ct = 0; ct < G::CT; ++ct) S[rt][ct] = mma(a, Vf[ct][kb2], S[rt][ct]);
-        }
+      advance(NSUB - 1);  // the step's last chunk (C = 64: the whole step)
       if constexpr (L2) {  // q'^T A_prev q' of chunk c (this wave's columns, to LDS), then A += K'^T K'
         Frag<true> aa[G::KB][G::CT];  // A_prev (symmetric) rounded to bf16 as the A operand
 #pragma unroll
@@ -2150,8 +2180,14 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
                        static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
   } else if (fwd && p.n_seg_max > 0) {
     const float* astates = p.l2 ? reinterpret_cast<const float*>(a.ws + p.off_astates) : nullptr;
-    if (BF && p.chunk == kChunk) {
-      auto kern = p.l2 ? chunk_out_ws_kernel<D, true> : chunk_out_ws_kernel<D, false>;
+    if (BF && p.chunk <= kChunk) {  // C = 16, 32, 64: the warp-specialised kernel
+      auto pick = [&](auto c_const) {
+        constexpr int CC = decltype(c_const)::value;
+        return p.l2 ? chunk_out_ws_kernel<D, true, CC> : chunk_out_ws_kernel<D, false, CC>;
+      };
+      auto kern = p.chunk == 16 ? pick(std::integral_constant<int, 16>{})
+                : p.chunk == 32 ? pick(std::integral_constant<int, 32>{})
+                                : pick(std::integral_constant<int, 64>{});
       hipLaunchKernelGGL(kern, dim3(p.n_seg_max, p.H), dim3(512), 0, s, static_cast<const uint16_t*>(a.q),
                          static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.gq, a.gk, tab, nseg,
                          rlo, rhi, states, astates, static_cast<uint16_t*>(a.out), p.H, p.L, a.rms_eps, a.eps,

@@ -142,3 +142,26 @@ def test_chunk_dense_bf16_workload_sampled(chunk):
         worst = max(worst, row_rel_err(out[b, h, rows], ref))
     print(f"dense bf16 workload chunk {chunk}: max row rel err {worst:.3e}")
     assert worst <= TOL_BF16
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("l2", [False, True])
+def test_chunk_long_context_sampled(chunk, l2):
+    # the long-context workload (B=1, H=32, L=65536, d=128) at the smaller chunk sizes, which run
+    # the warp-specialised kernel with the state advanced between the chunks of each 64-token step
+    inp = workloads.c4_long()
+    q, k, v, gq, gk, _ = _gpu(inp)
+    out = rla.fwd(q, k, v, gq, gk, chunk=chunk, l2_denominator=l2)
+    torch.cuda.synchronize()
+    rows = sample_rows(inp.q.shape[2], 16, seed=chunk + l2, chunk=chunk)
+    worst = 0.0
+    for h in (0, 31):
+        if l2:
+            ref = oracle.fwd_l2_rows(inp.q, inp.k, inp.v, f64(inp.gamma_q), f64(inp.gamma_k), 0, h, rows,
+                                     rms_eps=inp.rms_eps, rope_base=inp.rope_base)
+        else:
+            ref = oracle.fwd_rows(inp.q, inp.k, inp.v, f64(inp.gamma_q), f64(inp.gamma_k), 0, h, rows, None, inp.eps,
+                                  inp.rms_eps, inp.rope_base)
+        worst = max(worst, row_rel_err(out[0, h, rows], ref))
+    print(f"long context chunk {chunk} l2={l2}: max row rel err {worst:.3e}")
+    assert worst <= TOL_BF16
