@@ -83,6 +83,18 @@ def measured_traffic(kernel):
     return None
 
 
+def auto_seg_len(B, H, L, chunk=64):
+    """The library's automatic segment length for a dense [B, H, L, d] input: the longest
+    power-of-two number of 64-token blocks (at most 64) that still gives 512 workgroups."""
+    seg_min = max(chunk, 64)
+    cand = 64 * 64
+    while cand >= seg_min:
+        if B * ((L + cand - 1) // cand) * max(H, 1) >= 512:
+            return cand
+        cand //= 2
+    return seg_min
+
+
 def fwd_algorithmic(B, H, L, d, chunk=64):
     """Algorithmic work of the chunked forward per token-head: state build 2d^2,
     inter-chunk read-out 2d^2, causal intra-chunk part 2*C*d flops; q, k, v read and
@@ -349,6 +361,56 @@ def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
     return res
 
 
+# traffic mix of each kernel a roofline names: (streams read, streams written, in place)
+STREAM_MIX = {"r1w1": (1, 1, 0), "r2w0": (2, 0, 0), "r2w1": (2, 1, 0), "r2w2": (2, 2, 0), "r3w1": (3, 1, 0),
+              "r4w1": (4, 1, 0), "r4w2": (4, 2, 0), "r1w1_in_place": (1, 1, 1)}
+
+
+def plain_stream_rates(torch, hip, ev, stream, gib=1.0, steps=20):
+    """GB/s that a plain streaming kernel (libstream_ref.so: nothing but non-temporal 16-byte
+    loads and stores, four vectors per lane in flight) reaches for each traffic mix on 1 GiB
+    streams, the faster of its two access patterns (grid-stride loop; one 16 KB block per
+    workgroup): the practical reference beside the datasheet peak for a kernel moving the same
+    mix of bytes (a reference, not a bound). Returns ({mix: GB/s}, {mix: [GB/s per pattern]})."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "linear_attention_rla_amd", "libstream_ref.so"))
+    f = lib.rla2_stream_ref
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p),
+                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    n_vec = int(gib * (1 << 30)) // 16
+    dev = torch.device("cuda:0")
+    ins = [torch.zeros(n_vec * 4, dtype=torch.float32, device=dev) for _ in range(4)]
+    outs = [torch.empty(n_vec * 4, dtype=torch.float32, device=dev) for _ in range(2)]
+    sink = torch.zeros(n_vec // 1024 + 4096, dtype=torch.float32, device=dev)  # a float per workgroup
+    in_arr = (ctypes.c_void_p * 4)(*[t.data_ptr() for t in ins])
+    out_arr = (ctypes.c_void_p * 2)(*[t.data_ptr() for t in outs])
+    rates, per_pattern = {}, {}
+    for name, (r, w, ip) in STREAM_MIX.items():
+        per_pattern[name] = []
+        for pattern in (0, 1):
+            def run():
+                rc = f(r, w, ip, pattern, in_arr, out_arr, n_vec, ctypes.c_void_p(sink.data_ptr()), 2048,
+                       ctypes.c_void_p(stream.cuda_stream))
+                assert rc == 0, f"rla2_stream_ref({name}, pattern {pattern}) failed: {rc}"
+            for _ in range(5):
+                run()
+            ms = timed_ms(hip, ev, stream, run, steps, torch)
+            per_pattern[name].append(n_vec * 16 * (r + w) / (ms * 1e-3) / 1e9)
+        rates[name] = max(per_pattern[name])
+    del ins, outs, sink
+    torch.cuda.empty_cache()
+    return rates, per_pattern
+
+
+def add_plain_stream(roof, rates, mix):
+    """Sets, in a roofline dict, the plain streaming kernel's rate for the kernel's traffic mix
+    and the kernel's fraction of it."""
+    if roof is None or rates is None or mix not in rates:
+        return
+    roof["plain_stream"] = {"mix": mix, "achieved": rates[mix], "unit": "GB/s",
+                            "frac": roof["achieved"] / rates[mix]}
+
+
 def settle(step, torch, ms_target):
     """Untimed steps for at least ``ms_target`` ms of wall time, so that the clocks have
     settled under load before anything is timed. Returns the number of steps run."""
@@ -476,6 +538,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--seg-chunks", type=int, default=0)
+    ap.add_argument("--no-plain-stream", action="store_true",
+                    help="skip the plain streaming reference kernels (the measured practical HBM rates)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         log("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md, sharding).")
@@ -558,17 +622,43 @@ def main():
         "relu_zero_fraction": {"q": zeros_q, "k": zeros_k},
     }
 
+    rates = None
+    if not args.no_plain_stream:
+        log("timing the plain streaming reference kernels ...")
+        rates, per_pattern = plain_stream_rates(torch, hip, ev, stream)
+        result["plain_stream_gbs"] = {"best": rates, "grid_stride_and_16KB_blocks": per_pattern}
+        add_plain_stream(result["roofline"], rates, "r3w1")
+        # the state pass reads k, v of every segment but each document's last (whose total no
+        # prefix needs) and writes one fp32 record per segment and head
+        seg = args.seg_chunks * 64 if args.seg_chunks else auto_seg_len(B, H, L)
+        n_seg = (L + seg - 1) // seg
+        cs_bytes = B * H * (L - min(seg, L)) * d * 2 * 2 + B * H * (n_seg - 1) * (d * d + d) * 4
+        t_cs = per_kernel[KERNELS.index("chunk_state")]
+        result["chunk_state_roofline"] = {
+            "kernel": "chunk_state", "bound": "hbm", "achieved": cs_bytes / (t_cs * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": cs_bytes / (t_cs * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "algorithmic_bytes": cs_bytes, "traffic": measured_traffic("chunk_state_kernel")}
+        add_plain_stream(result["chunk_state_roofline"], rates, "r2w0")
+
     if not args.no_configs:
         log("timing the other forward workloads ...")
         result["configs"] = time_configs(args, rla, torch, workloads, hip, ev, stream)
 
     if not args.no_modes:
         result["modes"] = time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc)
+        for name, m in result["modes"].items():
+            add_plain_stream(m["roofline"], rates, "r1w1" if m["roofline"]["kernel"].startswith("readout") else "r3w1")
         result["prologue"] = time_prologue(args, rla, torch, hip, ev, stream, q, k, gq, gk)
+        add_plain_stream(result["prologue"]["roofline"], rates, "r2w2")
 
     if not args.no_backward:
         log("timing the backward ...")
         result["backward"] = time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk)
+        bw = result["backward"]
+        add_plain_stream(bw["bwd_dq"], rates, "r4w1")
+        add_plain_stream(bw["bwd_dkv"], rates, "r4w2")
+        add_plain_stream(bw["bidirectional"]["bwd_dq"], rates, "r2w1")
+        add_plain_stream(bw["bidirectional"]["bwd_dkv"], rates, "r2w2")
         torch.cuda.empty_cache()
 
     if not args.no_decode:
@@ -648,6 +738,11 @@ def main():
                                                "algorithmic_bytes": build_bytes,
                                                "note": "prefix k, v read once (bf16), S and z written once"}},
         }
+
+    if "decode" in result:
+        add_plain_stream(result["decode"]["roofline"], rates, "r1w1_in_place")
+        add_plain_stream(result["decode"]["l2_denominator"]["roofline"], rates, "r1w1_in_place")
+        add_plain_stream(result["decode"]["state_from_prefix"]["roofline"], rates, "r2w0")
 
     if args.copy_calibration:
         # a plain streaming kernel of known size (reads 1 GiB, writes 1 GiB): the
