@@ -534,6 +534,19 @@ __device__ __forceinline__ void mma_wave_sync(unsigned* cnt, unsigned target, in
   if (lane == 0) hdr[HDR_WAIT] = 1u;
 }
 
+// The other side of a hand-over counter: a wave that only waits (it does not arrive) until the
+// count reaches `target`, with the same bounded poll and the same record in the header when
+// the bound runs out. The waves that hand over add to the counter with release semantics after
+// their last access to the memory being handed over.
+__device__ __forceinline__ void wait_count(unsigned* cnt, unsigned target, int lane, uint32_t polls, uint32_t* hdr) {
+  for (uint32_t spin = 0; spin < polls; ++spin) {
+    if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+  if (lane == 0) hdr[HDR_WAIT] = 1u;
+}
+
 // Checksum of cu_seqlens[0 .. n_docs] (0 without cu_seqlens) for the plan stamp: a wrapping
 // sum of one mixed word per entry, so every thread order gives the same value. Called by all
 // threads of a 1024-thread workgroup; every thread gets the result.

@@ -628,7 +628,8 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
 // A^T Q'^T (the shape of the S^T Q'^T term) dotted with q'_t, summed over the waves in LDS
 // (one more barrier); A advances with K' as the value operand. One workgroup per CU.
 //
-// The bf16 path with C = 64 runs chunk_out_ws_kernel below instead.
+// The bf16 path runs chunk_out_ws_kernel below instead (C = 16, 32, 64, and 128 with the Sum
+// denominator); this kernel serves fp32 and the L2 denominator at C = 128.
 
 template <bool BF, int D, bool L2, int C>
 __global__ __launch_bounds__(NT, (L2 || D == 128) ? 1 : 2) void chunk_out_kernel(
@@ -1010,6 +1011,13 @@ __global__ __launch_bounds__(NT, (L2 || D == 128) ? 1 : 2) void chunk_out_kernel
 // Inside the step the MMA waves also meet among themselves (score tiles and row reciprocals
 // of every query tile are complete before anyone forms outputs) on an LDS arrival counter,
 // which the mappers never wait on.
+// Chunks of 128 tokens (Sum denominator) are two consecutive 64-token blocks: every query of
+// the second block reads all 64 keys of the first block directly (RLA page §3 formula inside
+// the chunk), and the state and z advance once per chunk, after its second block. While the
+// MMA waves process a second block they read the first block's K' and V from the other
+// parity's buffers and put the cross-block weights in that parity's Q' buffer; in that step
+// the mappers map the next block into registers and store it only after all four MMA waves
+// have released those buffers (sRelease, a bounded wait like the MMA waves' meeting).
 
 // Score phase of MMA wave TT (query tile TT of the chunk): the causal tiles K'_kt Q'_TT^T
 // (kt <= TT) and Z Q'_TT^T, the diagonal tile masked, every weight rounded to bf16 once
@@ -1024,15 +1032,22 @@ __global__ __launch_bounds__(NT, (L2 || D == 128) ? 1 : 2) void chunk_out_kernel
 // chunk become weights; the keys of the step's earlier chunks reach the query through the state,
 // which the MMA waves advance between the chunks, so the denominator takes their scores, unrounded
 // (Sum: the scores; L2: their squares), in place of q'.(z they added).
-template <int D, int TT, int Z0, int Z1, int NZR, bool L2 = false, int C = 64>
+// Chunks of C = 128 tokens (two 64-token blocks; Sum only): on the second block (CROSS) the
+// query tile also scores all 64 keys of the chunk's first block (cKx) without a mask, packs
+// those weights the same way into sAx and adds them to its row sum; z stays at the chunk's
+// start for both blocks, so on the first block (ZADV false) the lanes that keep z add the
+// block's column sums to zreg but write the unchanged z as the next block's operand.
+template <int D, int TT, int Z0, int Z1, int NZR, bool L2 = false, int C = 64, bool CROSS = false, bool ZADV = true>
 __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK, int qp, const Frag<true>* sZf,
                                          Frag<true>* zf_next, float (&zreg)[NZR], Frag<true>* sA, float* sInv,
-                                         float eps, int lane) {
+                                         float eps, int lane, const uint16_t* cKx = nullptr,
+                                         Frag<true>* sAx = nullptr) {
   using G = Geo<true, D>;
   constexpr int KB = G::KB, NZ = Z1 - Z0, NP = TT / 2 + 1;
-  constexpr int KT0 = (TT / (C / 16)) * (C / 16);  // first key tile of the query tile's chunk
+  constexpr int KT0 = C >= 64 ? 0 : (TT / (C / 16)) * (C / 16);  // first key tile of the query tile's chunk
   static_assert(!L2 || NZ == 0, "");
   static_assert(NZ <= NZR, "");
+  static_assert(!CROSS || (C == 128 && !L2), "cross-block weights: chunks of 128 tokens, Sum denominator");
   const int c16 = lane & 15, g = lane >> 4;
   Frag<true> Qf[KB], Kf[TT + 1][KB], Zf[KB], Ct[NZ > 0 ? NZ : 1][2];
 #pragma unroll
@@ -1089,6 +1104,30 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
   for (int kt = 0; kt < KT0; ++kt)  // the step's earlier chunks (C < 64)
 #pragma unroll
     for (int i = 0; i < 4; ++i) rs = L2 ? __builtin_fmaf(At[kt][i], At[kt][i], rs) : rs + At[kt][i];
+  if constexpr (CROSS) {  // the chunk's first block: all four key tiles, packed as pairs 0, 1
+    floatx4 Ax[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) Ax[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb2 = 0; kb2 < KB; ++kb2) {
+      Frag<true> Kx[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) Kx[kt] = lds_frag_c(cKx, qp, kt * 16 + c16, kb2, g);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) Ax[kt] = mma(Kx[kt], Qf[kb2], Ax[kt]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      uint32_t px[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kt = 2 * b + (i >> 1), r = 2 * (i & 1);
+        px[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{Ax[kt][r], Ax[kt][r + 1]}, bf16x2));
+        rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, px[i]), ones2, rs, false);
+      }
+      *reinterpret_cast<u32x4*>(&sAx[(TT * 2 + b) * 64 + lane]) = u32x4{px[0], px[1], px[2], px[3]};
+    }
+  }
   if constexpr (!L2) {
     if (g == 0) rs += zq[0] + zq[1];  // q'.z of query 16 TT + c16 (rows 0, 1 of Z Q'^T)
   }
@@ -1107,9 +1146,11 @@ __device__ __forceinline__ void ws_score(const uint16_t* cQ, const uint16_t* cK,
         // dim 16 T + 4g + i (T = Z0 + z) sits in fragment T / 2, slot 4 (g % 2) + i of lane
         // 16 (2 (T % 2) + g / 2) (bf16 of z) and of the lane after it (the remainder)
         const int T = Z0 + z;
+        const float zold = zreg[z];
         zreg[z] += c16 == 0 ? zc[0] : c16 == 1 ? zc[1] : c16 == 2 ? zc[2] : zc[3];
-        const __bf16 hi = static_cast<__bf16>(zreg[z]);
-        const __bf16 lo = static_cast<__bf16>(zreg[z] - static_cast<float>(hi));
+        const float zw = ZADV ? zreg[z] : zold;  // the next block's z operand
+        const __bf16 hi = static_cast<__bf16>(zw);
+        const __bf16 lo = static_cast<__bf16>(zw - static_cast<float>(hi));
         uint16_t* zf16 = reinterpret_cast<uint16_t*>(zf_next + (T / 2) * 64 + 16 * (2 * (T % 2) + g / 2));
         zf16[4 * (g % 2) + c16] = __builtin_bit_cast(uint16_t, hi);
         zf16[8 + 4 * (g % 2) + c16] = __builtin_bit_cast(uint16_t, lo);
@@ -1131,6 +1172,7 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
     const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo, const float2* __restrict__ rope_hi,
     const float* __restrict__ states, const float* __restrict__ astates, uint16_t* __restrict__ out, int H, int L,
     float rms_eps, float eps, uint32_t* __restrict__ hdr, uint32_t polls) {
+  static_assert(!(L2 && C == 128), "chunks of 128 tokens with the L2 denominator run the generic kernel");
   using G = Geo<true, D>;
   using St = uint16_t;
   using EL = Elem<true>;
@@ -1150,6 +1192,11 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   // chunk c in buffer c % 2
   __shared__ Frag<true> sZf[2 * G::KB * 64];
   __shared__ unsigned sArrive;  // MMA-wave arrivals (mma_wave_sync)
+  __shared__ unsigned sRelease;  // C = 128: the MMA waves' releases of the first block's buffers
+  // C = 128: the cross-block weights of a chunk's second block go into the first block's Q'
+  // buffer, which nothing reads in that step; at d = 32 that buffer is too small for them
+  constexpr bool XOWN = C == 128 && BUFQ * 2 < 4 * 2 * 64 * 16;
+  __shared__ Frag<true> sXown[XOWN ? 4 * 2 * 64 : 1];
   // L2, by step parity: rows' sums of squared weights (MMA waves) and the mappers' parts of
   // q'^T A_prev q', for the chunk the MMA waves processed in that step
   __shared__ float sRs2[L2 ? 2 * kChunk : 1];
@@ -1171,6 +1218,9 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   const int seg_bytes = si.len * D * 2;
   const float* rec = states + ((size_t)seg * H + h) * (size_t)(D * D + D);
   if (tid == 0) sArrive = 0u;
+  if constexpr (C == 128) {
+    if (tid == 0) sRelease = 0u;
+  }
   // z operand fragments (contiguous slot order): slot (g, j) of fragment kb holds dim
   // kb*32 + 8g + j; lane 16g holds bf16(z) there, lane 16g + 1 the residual, every other lane
   // zeros (written once). The initial z goes to buffer 0 (lane l converts dims 2l, 2l + 1);
@@ -1266,12 +1316,20 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       // The registers of chunk st are refilled with chunk cn as they free up: v (no mapping)
       // first, then q and k one token at a time, then the RoPE row, so the loads leave early.
       const int cn = st + 2;
-      if (st < nch) store_rows<true, D>(sV + bm, r[2], t0, m);
-      load_raw_buf<true, D>(r[2], rv, cn * kChunk + t0, m);
+      // C = 128: while the MMA waves process the second block of a chunk they still read the
+      // first block's K' and V, and use the first block's Q' buffer for the cross-block weights,
+      // all in the buffers of this step's parity; so in those steps (st even, the MMA waves on
+      // block st - 1) every row of block st is held in registers and stored only once the MMA
+      // waves have released the buffers (4 releases per such step on sRelease)
+      const bool defer = C == 128 && (st & 1) == 0 && st >= 2 && st < nch;
+      if (!defer) {
+        if (st < nch) store_rows<true, D>(sV + bm, r[2], t0, m);
+        load_raw_buf<true, D>(r[2], rv, cn * kChunk + t0, m);
+      }
+      R oq, ok;  // both tokens when deferred, else token by token
       auto map_tok = [&](auto tok_c) {
         constexpr int tok = decltype(tok_c)::value;
         if (st < nch) {
-          R oq, ok;  // token tok only
           const float invq = rms_inv<true, D>(r[0], tok, rms_eps);
           const float invk = rms_inv<true, D>(r[1], tok, rms_eps);
 #pragma unroll
@@ -1288,14 +1346,25 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
             put_pairs<true, D>(oq, tok, e, q1, q2);
             put_pairs<true, D>(ok, tok, e, k1, k2);
           }
-          store_rows<true, D, tok>(sQ + (st & 1) * BUFQ, oq, t0, m, QP);
-          store_rows<true, D, tok>(sK + (st & 1) * BUFQ, ok, t0, m, QP);
+          if (!defer) {
+            store_rows<true, D, tok>(sQ + (st & 1) * BUFQ, oq, t0, m, QP);
+            store_rows<true, D, tok>(sK + (st & 1) * BUFQ, ok, t0, m, QP);
+          }
         }
         load_raw_buf<true, D, tok>(r[0], rq, cn * kChunk + t0, m);
         load_raw_buf<true, D, tok>(r[1], rk, cn * kChunk + t0, m);
       };
       map_tok(std::integral_constant<int, 0>{});
       map_tok(std::integral_constant<int, 1>{});
+      if constexpr (C == 128) {
+        if (defer) {
+          wait_count(&sRelease, 4u * (unsigned)(st / 2), lane, polls, hdr);
+          store_rows<true, D>(sV + bm, r[2], t0, m);
+          store_rows<true, D>(sQ + (st & 1) * BUFQ, oq, t0, m, QP);
+          store_rows<true, D>(sK + (st & 1) * BUFQ, ok, t0, m, QP);
+          load_raw_buf<true, D>(r[2], rv, cn * kChunk + t0, m);
+        }
+      }
       copy_bytes<G::E * 8>(hi, hi0 + (size_t)min(cn, nch - 1) * G::HALF);
       if constexpr (L2) store_rows_out(st, wave - 4, std::integral_constant<int, 4>{});
       else if constexpr (NWS == 8) store_rows_out(st, wave, std::integral_constant<int, 8>{});
@@ -1360,6 +1429,29 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
           case 2: ws_score<D, 2, 0, 0, NZR, true, C>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
           default: ws_score<D, 3, 0, 0, NZR, true, C>(cQ, cK, QP, sZf, sZf, zreg, sA, rs2, eps, lane); break;
         }
+      } else if constexpr (C == 128) {
+        // block c of its chunk: the first (c even) or the second (c odd, with the first block's
+        // keys in the other parity's K' buffer, its cross-block weights into the other parity's
+        // Q' buffer, which no one reads in this step)
+        const Frag<true>* zf = sZf + (c & 1) * G::KB * 64;  // z at the chunk's start
+        Frag<true>* zn = sZf + ((c + 1) & 1) * G::KB * 64;
+        const St* cKx = sK + (st & 1) * BUFQ;
+        Frag<true>* sAx = XOWN ? sXown : reinterpret_cast<Frag<true>*>(sQ + (st & 1) * BUFQ);
+        if (c & 1) {
+          switch (wave) {
+            case 0: ws_score<D, 0, 0, Z1, NZR, false, C, true, true>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane, cKx, sAx); break;
+            case 1: ws_score<D, 1, Z1, Z2, NZR, false, C, true, true>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane, cKx, sAx); break;
+            case 2: ws_score<D, 2, Z2, Z3, NZR, false, C, true, true>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane, cKx, sAx); break;
+            default: ws_score<D, 3, Z3, G::RT, NZR, false, C, true, true>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane, cKx, sAx); break;
+          }
+        } else {
+          switch (wave) {
+            case 0: ws_score<D, 0, 0, Z1, NZR, false, C, false, false>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+            case 1: ws_score<D, 1, Z1, Z2, NZR, false, C, false, false>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+            case 2: ws_score<D, 2, Z2, Z3, NZR, false, C, false, false>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+            default: ws_score<D, 3, Z3, G::RT, NZR, false, C, false, false>(cQ, cK, QP, zf, zn, zreg, sA, sInv, eps, lane); break;
+          }
+        }
       } else {
         const Frag<true>* zf = sZf + (c & 1) * G::KB * 64;  // z before chunk c
         Frag<true>* zn = sZf + ((c + 1) & 1) * G::KB * 64;  // z before chunk c + 1
@@ -1372,7 +1464,94 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
       }
     }
     mma_wave_sync(&sArrive, 4u * (unsigned)(st + 1), lane, polls, hdr);
-    if (work && wave < G::NW) {  // ---- output, then the state update
+    if constexpr (C == 128) {
+      if (work && wave < G::NW) {  // ---- output, then (second block) the chunk's state update
+        const bool second = (c & 1) != 0;
+        Frag<true> Vf[G::CT][2];
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct) {
+          Vf[ct][0] = lds_frag_tr(cV, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
+          Vf[ct][1] = lds_frag_tr(cV, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
+        }
+        floatx4 o[G::CT][4];
+#pragma unroll
+        for (int ct = 0; ct < G::CT; ++ct)
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) o[ct][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // S^T Q'^T with the state at the chunk's start (it advances only after the second block)
+#pragma unroll
+        for (int kb2 = 0; kb2 < G::KB; ++kb2) {
+          Frag<true> sa[G::CT];
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) sa[ct] = acc_frag<true>(S[2 * kb2][ct], S[2 * kb2 + 1][ct]);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            const Frag<true> qf = lds_frag_c(cQ, QP, tt * 16 + c16, kb2, g);
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(sa[ct], qf, o[ct][tt]);
+          }
+        }
+        // the block's own keys (key-tile pairs up to the query tile's)
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int b = 0; b <= tt / 2; ++b) {
+            const Frag<true> ab = sA[(tt * 2 + b) * 64 + lane];
+#pragma unroll
+            for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(Vf[ct][b], ab, o[ct][tt]);
+          }
+        const St* pK = sK + (st & 1) * BUFQ;  // the chunk's first block (second block only)
+        const St* pV = sV + (st & 1) * BUF;
+        const Frag<true>* sAx = XOWN ? sXown : reinterpret_cast<const Frag<true>*>(sQ + (st & 1) * BUFQ);
+        Frag<true> Vp[G::CT][2];
+        if (second) {  // the first block's keys: every key-tile pair, for every query tile
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) {
+            Vp[ct][0] = lds_frag_tr(pV, G::ROWP, 0, wave * G::DVW + ct * 16, lane);
+            Vp[ct][1] = lds_frag_tr(pV, G::ROWP, 32, wave * G::DVW + ct * 16, lane);
+          }
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              const Frag<true> ab = sAx[(tt * 2 + b) * 64 + lane];
+#pragma unroll
+              for (int ct = 0; ct < G::CT; ++ct) o[ct][tt] = mma(Vp[ct][b], ab, o[ct][tt]);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const int t = tt * 16 + c16;
+          const float rr = sInv[t];
+#pragma unroll
+          for (int ct = 0; ct < G::CT; ++ct) {
+            const int col = wave * G::DVW + ct * 16 + 4 * g;
+            const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[ct][tt][0] * rr, o[ct][tt][1] * rr}, bf16x2));
+            const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{o[ct][tt][2] * rr, o[ct][tt][3] * rr}, bf16x2));
+            *reinterpret_cast<uint2*>(sO + (c & 1) * BUF + t * G::ROWP + col) = make_uint2(w0, w1);
+          }
+        }
+        if (second) {  // S += K'^T V over both blocks of the chunk
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            const St* kb = blk == 0 ? pK : cK;
+#pragma unroll
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+              for (int rt = 0; rt < G::RT; ++rt) {
+                const Frag<true> a = lds_frag_tr_s8(kb, QP, 32 * kb2, 32 * (rt / 2) + 4 * (rt % 2), lane);
+#pragma unroll
+                for (int ct = 0; ct < G::CT; ++ct) S[rt][ct] = mma(a, blk == 0 ? Vp[ct][kb2] : Vf[ct][kb2], S[rt][ct]);
+              }
+            }
+          }
+        }
+      }
+      // every MMA wave hands the first block's buffers back to the mappers after the second
+      // block (its last reads of them are above; the release orders them before the count)
+      if (work && (c & 1) && lane == 0)
+        __hip_atomic_fetch_add(&sRelease, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else if (work && wave < G::NW) {  // ---- output, then the state update
       Frag<true> Vf[G::CT][2];
 #pragma unroll
       for (int ct = 0; ct < G::CT; ++ct) {
@@ -2180,14 +2359,15 @@ hipError_t run_chunked(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_
                        static_cast<St*>(a.out), p.H, p.L, a.rms_eps, a.eps);
   } else if (fwd && p.n_seg_max > 0) {
     const float* astates = p.l2 ? reinterpret_cast<const float*>(a.ws + p.off_astates) : nullptr;
-    if (BF && p.chunk <= kChunk) {  // C = 16, 32, 64: the warp-specialised kernel
+    if (BF && (p.chunk <= kChunk || !p.l2)) {  // C = 16, 32, 64 (and 128 with the Sum denominator): warp-specialised
       auto pick = [&](auto c_const) {
         constexpr int CC = decltype(c_const)::value;
         return p.l2 ? chunk_out_ws_kernel<D, true, CC> : chunk_out_ws_kernel<D, false, CC>;
       };
       auto kern = p.chunk == 16 ? pick(std::integral_constant<int, 16>{})
                 : p.chunk == 32 ? pick(std::integral_constant<int, 32>{})
-                                : pick(std::integral_constant<int, 64>{});
+                : p.chunk == 128 ? chunk_out_ws_kernel<D, false, 128>
+                                 : pick(std::integral_constant<int, 64>{});
       hipLaunchKernelGGL(kern, dim3(p.n_seg_max, p.H), dim3(512), 0, s, static_cast<const uint16_t*>(a.q),
                          static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v), a.gq, a.gk, tab, nseg,
                          rlo, rhi, states, astates, static_cast<uint16_t*>(a.out), p.H, p.L, a.rms_eps, a.eps,

@@ -60,10 +60,15 @@ def test_exhausted_wait_is_reported_and_kernels_end():
     inp, (q, k, v, gq, gk), cu, dout = _inputs(L=700, H=4, d=128, seed=7)
     desc = rla.make_desc(1, 4, 700, 128, rla.BF16)
     fws, bws = _ws(desc), _ws(desc, backward=True)
+    # 128-token chunks: the mappers also wait for the first block's buffers (256-token segments)
+    ws128 = _ws(rla.make_desc(1, 4, 700, 128, rla.BF16, chunk=128, seg_chunks=2))
     prev = rla.debug_set_wait_polls(0)
     try:
         with pytest.raises(rla.Rla2FlagError) as e:
             rla.fwd(q, k, v, gq, gk, workspace=fws, seg_chunks=1)
+        assert e.value.flags == rla.FLAG_WAIT_EXHAUSTED
+        with pytest.raises(rla.Rla2FlagError) as e:
+            rla.fwd(q, k, v, gq, gk, workspace=ws128, chunk=128, seg_chunks=2)
         assert e.value.flags == rla.FLAG_WAIT_EXHAUSTED
         with pytest.raises(rla.Rla2FlagError) as e:
             rla.bwd(q, k, v, gq, gk, dout, workspace=bws, seg_chunks=1)
@@ -74,6 +79,9 @@ def test_exhausted_wait_is_reported_and_kernels_end():
     out = rla.fwd(q, k, v, gq, gk, workspace=fws, seg_chunks=1)
     assert rla.workspace_flags(fws) == 0
     ref = oracle.fwd(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.gamma_q), f64(inp.gamma_k))
+    assert row_rel_err(out, ref) <= TOL_BF16
+    out = rla.fwd(q, k, v, gq, gk, workspace=ws128, chunk=128, seg_chunks=2)
+    assert rla.workspace_flags(ws128) == 0
     assert row_rel_err(out, ref) <= TOL_BF16
     rla.bwd(q, k, v, gq, gk, dout, workspace=bws, seg_chunks=1)
     assert rla.workspace_flags(bws) == 0
