@@ -214,7 +214,7 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
     res["l2_bidirectional"]["workload"] = ("long-context bidirectional forward with the L2 denominator "
                                            "(whole-document S and A), B=1 H=32 L=65536 d=128 bf16")
     for c in (16, 32, 128):
-        res[f"chunk_{c}"]["workload"] = (f"long-context causal forward with {c}-token chunks (generic "
+        res[f"chunk_{c}"]["workload"] = (f"long-context causal forward with {c}-token chunks (warp-specialised "
                                          "output kernel), B=1 H=32 L=65536 d=128 bf16")
     return res
 
