@@ -676,7 +676,7 @@ def main():
         # the state build (segment map, chunk state, per-document sums) timed like the forward
         sdesc = rla.make_desc(1, dec.prefix_k.shape[1], T_prefix, dec.prefix_k.shape[3], rla.BF16, cu,
                               cu.numel() - 1)
-        sws = torch.empty(max(rla.fwd_workspace_size(sdesc), 1), dtype=torch.uint8, device=dev)
+        sws = torch.empty(max(rla.state_from_prefix_workspace_size(sdesc), 1), dtype=torch.uint8, device=dev)
 
         def build():
             rla.state_from_prefix(dec.prefix_k, dec.prefix_v, dgk, cu, S=S, z=z, workspace=sws)

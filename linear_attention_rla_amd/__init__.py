@@ -18,7 +18,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fwd", "state_from_prefix", "decode_step", "decode_step_l2", "fwd_workspace_size", "lib", "Rla2Error",
+__all__ = ["fwd", "state_from_prefix", "decode_step", "decode_step_l2", "fwd_workspace_size",
+           "state_from_prefix_workspace_size", "lib", "Rla2Error",
            "Rla2FlagError", "FwdDesc", "LIB_PATH", "STATUS", "workspace_flags", "set_check_flags",
            "debug_set_wait_polls"]
 
@@ -215,6 +216,14 @@ def fwd_workspace_size(desc: FwdDesc) -> int:
     st = lib().rla2_fwd_workspace_size(ctypes.byref(desc), ctypes.byref(n))
     if st:
         raise Rla2Error(st, "rla2_fwd_workspace_size")
+    return n.value
+
+
+def state_from_prefix_workspace_size(desc: FwdDesc) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().rla2_state_from_prefix_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    if st:
+        raise Rla2Error(st, "rla2_state_from_prefix_workspace_size")
     return n.value
 
 

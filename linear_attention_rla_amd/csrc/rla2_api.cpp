@@ -61,8 +61,42 @@ bool overlap(Range a, Range b) {
   return x < y + b.n && y < x + a.n;
 }
 
-// Shared checks of a forward / state-build descriptor. Fills the plan on success.
-rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
+// Automatic segment length for the bf16 path. The output kernel runs one workgroup per
+// (segment, head), 256 of them resident at once at d >= 64 (LDS and registers allow one per
+// CU) and 512 at d = 32; a segment of n 64-token blocks costs it about n + 4 steps (n, plus
+// the pipeline's fill and drain and the first loads' latency). The state pass runs two
+// workgroups per CU over every segment but each document's last, at about half a step per
+// block. The modelled time is the sum of rounds of resident workgroups times the steps of
+// one, for both. Dense input has rows * ceil(L / seg) segments per head; for packed input
+// each document's last segment is partial, so the count is taken as ceil(T / seg) plus half
+// a segment per document. Ties go to the longer segment (fewer records through the scan).
+// Measured against the segment lengths it replaces: [4, 8, 2048, 64] 42.5 -> 31.8 us (256
+// instead of 128 tokens), the packed [1, 16, 16384, 128] workload 147 -> 115 us (640 instead
+// of 512); the long-context workload keeps 4096.
+int auto_seg_len(long long rows, long long L, long long H, long long n_docs, bool packed, int d, int seg_min) {
+  const long long slots = d == 32 ? 512 : 256;
+  long long best_cost = -1;
+  int best = seg_min;
+  for (int seg = seg_min; seg <= rla2::kMaxSegChunks * rla2::kChunk; seg += seg_min) {
+    const long long per = (L + seg - 1) / seg;
+    const long long nseg2 = packed ? 2 * per + n_docs : 2 * rows * per;  // twice the segments per head
+    const long long out_wg = nseg2 * H / 2;
+    const long long state_wg = nseg2 > 2 * n_docs ? (nseg2 - 2 * n_docs) * H / 2 : 0;
+    const long long blocks = seg / rla2::kChunk;
+    const long long cost2 = 2 * ((out_wg + slots - 1) / slots) * (blocks + 4) +  // twice the modelled time
+                            ((state_wg + 511) / 512) * blocks;
+    if (best_cost < 0 || cost2 <= best_cost) {
+      best_cost = cost2;
+      best = seg;
+    }
+  }
+  return best;
+}
+
+// Shared checks of a forward / state-build descriptor. Fills the plan on success. The state
+// build (no output kernel: every segment's total goes through the scan) keeps the
+// 512-workgroup rule for its automatic segment length, which gives it the fewest records.
+rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p, bool state_build = false) {
   if (d == nullptr) return RLA2_ERR_NULL_POINTER;
   if (d->B < 0 || d->H < 0 || d->L < 0 || d->d < 0) return RLA2_ERR_BAD_SHAPE;
   if (d->cu_seqlens != nullptr && (d->B != 1 || d->n_docs < 0)) return RLA2_ERR_BAD_SHAPE;
@@ -102,15 +136,17 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p) {
   p->n_docs = p->packed ? d->n_docs : d->B;
   const int rows = p->packed ? 1 : p->B;
   const long long L = p->L;
-  // Segment length: the sweep kernels run one workgroup per (segment, head), so
-  // pick the longest segment that still gives 512 workgroups, two per CU of the
-  // 256-CU part (fewer segments mean less fp32 state traffic through the
-  // inter-segment scan and fewer pipeline fills; measured on the long-context
+  // Segment length: the sweep kernels run one workgroup per (segment, head). The bf16 path
+  // takes the modelled best (auto_seg_len); otherwise the longest segment that still gives 512
+  // workgroups, two per CU of the 256-CU part (fewer segments mean less fp32 state traffic
+  // through the inter-segment scan and fewer pipeline fills; measured on the long-context
   // forward: 64-chunk segments 651 us, 32-chunk 693 us, 16-chunk 754 us).
   const int seg_min = d->chunk > rla2::kChunk ? d->chunk : rla2::kChunk;
   int seg = 0;
   if (d->seg_chunks > 0) {
     seg = (int)seg_req;
+  } else if (d->dtype == RLA2_BF16 && !state_build) {
+    seg = auto_seg_len(rows, L, d->H, p->n_docs, p->packed, d->d, seg_min);
   } else {
     seg = seg_min;
     for (int cand = rla2::kMaxSegChunks * rla2::kChunk; cand >= seg_min; cand /= 2) {
@@ -316,7 +352,12 @@ rla2_status rla2_fwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
 }
 
 rla2_status rla2_state_from_prefix_workspace_size(const rla2_fwd_desc* desc, size_t* bytes) {
-  return rla2_fwd_workspace_size(desc, bytes);
+  if (bytes == nullptr) return RLA2_ERR_NULL_POINTER;
+  Plan p;
+  rla2_status st = plan_desc(desc, &p, true);
+  if (st != RLA2_OK) return st;
+  *bytes = p.bytes;
+  return RLA2_OK;
 }
 
 rla2_status rla2_fwd_chunked(const rla2_fwd_desc* desc, const void* q, const void* k,
@@ -375,7 +416,7 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
                                    const float* gamma_k, float* S, float* z, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
   Plan p;
-  rla2_status st = plan_desc(desc, &p);
+  rla2_status st = plan_desc(desc, &p, true);
   if (st != RLA2_OK) return st;
   const size_t act = (size_t)p.B * p.H * p.L * p.d * elem_bytes(p.dtype);
   const size_t gam = (size_t)p.H * p.d * 4;

@@ -58,7 +58,7 @@ def test_flags_clear_after_normal_calls():
 
 def test_exhausted_wait_is_reported_and_kernels_end():
     inp, (q, k, v, gq, gk), cu, dout = _inputs(L=700, H=4, d=128, seed=7)
-    desc = rla.make_desc(1, 4, 700, 128, rla.BF16)
+    desc = rla.make_desc(1, 4, 700, 128, rla.BF16, seg_chunks=1)  # the segmentation of every call below
     fws, bws = _ws(desc), _ws(desc, backward=True)
     # 128-token chunks: the mappers also wait for the first block's buffers (256-token segments)
     ws128 = _ws(rla.make_desc(1, 4, 700, 128, rla.BF16, chunk=128, seg_chunks=2))
