@@ -199,7 +199,8 @@ def time_modes(args, rla, torch, hip, ev, stream, q, k, v, gq, gk, out, ws, desc
             nbytes = fwd_algorithmic(B, H, L, d)[1]
             kern = "chunk_out"
             traffic = {"l2_denominator": measured_traffic("chunk_out_ws_kernel_l2"),
-                       "continuation": measured_traffic("chunk_out_ws_kernel")}.get(name)
+                       "continuation": measured_traffic("chunk_out_ws_kernel"),
+                       "chunk_128": measured_traffic("chunk_out_ws_kernel_c128")}.get(name)
         gbs = nbytes / (t_out * 1e-3) / 1e9
         res[name] = {"ms_per_step": ms, "tokens_per_s": B * L / (ms * 1e-3), "steps": steps,
                      "kernel_ms": dict(zip(KERNELS[:-1] + [kern], per)),
