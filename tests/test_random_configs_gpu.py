@@ -97,3 +97,43 @@ def test_random_configuration(i):
                                     okw.get("initial_S"), z_init, c["pos"])
     assert mat_rel_err(fS, S) <= tol
     assert mat_rel_err(fz, z, 1) <= tol
+
+
+N_BWD_CASES = 16
+
+
+def _bwd_case(i):
+    r = np.random.default_rng(73_000 + i)
+    c = dict(d=int(r.choice([32, 64, 128])), dtype=torch.float32 if r.random() < 0.4 else torch.bfloat16,
+             bidir=bool(r.random() < 0.4), H=int(r.integers(1, 3)), seed=9_500 + i)
+    if r.random() < 0.5:
+        n = int(r.integers(2, 6))
+        lengths = [int(r.choice(SPECIAL)) if r.random() < 0.5 else int(r.integers(0, 300)) for _ in range(n)]
+        lengths.append(int(r.integers(20, 200)))  # at least one document of typical size
+        c.update(B=1, L=sum(lengths), lengths=lengths)
+    else:
+        c.update(B=int(r.integers(1, 3)), L=int(r.integers(20, 400)), lengths=None)
+    c["seg_chunks"] = 0 if r.random() < 0.5 else int(r.integers(1, 6))
+    c["init"] = bool(r.random() < 0.3)
+    c["pos"] = int(r.integers(0, 70_000)) if c["init"] else 0
+    return c
+
+
+@pytest.mark.parametrize("i", range(N_BWD_CASES))
+def test_random_backward_configuration(i):
+    from test_backward_modes_gpu import _check, _run
+    c = _bwd_case(i)
+    d, H, B, L = c["d"], c["H"], c["B"], c["L"]
+    inp = workloads.fwd_inputs(B, H, L, d, c["dtype"], seed=c["seed"], lengths=c["lengths"])
+    dout = workloads.cotangent(inp.q.shape, seed=c["seed"] + 1).to(c["dtype"])
+    S0 = z0 = None
+    kw = {}
+    if c["init"]:
+        S0, z0 = workloads.initial_state(H, d, seed=c["seed"], scale=0.1)
+        kw = dict(initial_S=f64(S0), initial_z=f64(z0), initial_pos=c["pos"])
+        S0, z0 = S0.to(DEV), z0.to(DEV)
+    got = _run(inp, dout, c["bidir"], c["seg_chunks"], S0, z0, c["pos"])
+    cu_np = None if c["lengths"] is None else inp.cu_seqlens.numpy()
+    ref = oracle.bwd(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.gamma_q), f64(inp.gamma_k), f64(dout), cu_np,
+                     inp.eps, inp.rms_eps, inp.rope_base, causal=not c["bidir"], **kw)
+    _check(got, ref, c["dtype"], f"backward case {i}: {c}", c["bidir"])
