@@ -69,11 +69,15 @@ typedef enum rla2_dtype { RLA2_F32 = 0, RLA2_BF16 = 1 } rla2_dtype;
  *               (RLA2_ERR_UNSUPPORTED otherwise). Every query reads the state at the
  *               start of its chunk and the keys of its chunk up to itself directly
  *               (the associativity of RLA page §1 applied per chunk); C changes only
- *               the rounding, not the result. 64 runs the tuned bf16 kernels; other
- *               sizes, and fp32, run a generic kernel. The backward always works in
- *               32-token steps of its own, whatever C.
+ *               the rounding, not the result. In bf16 every size runs the
+ *               warp-specialised output kernel (except 128 with the L2 denominator);
+ *               fp32 runs a generic kernel. The backward always works in 32-token
+ *               steps of its own, whatever C.
  *  seg_chunks   chunks per sequential segment of the sweep (a tuning knob that only
- *               changes fp32 summation order); 0 selects it automatically. A segment
+ *               changes fp32 summation order); 0 selects it automatically (bf16: the
+ *               length a model of the sweeps' rounds of resident workgroups times
+ *               their steps rates fastest; fp32 and the state build: the longest that
+ *               still gives 512 workgroups). A segment
  *               of seg_chunks * chunk tokens must be a multiple of 64 tokens and at
  *               most 4096 (RLA2_ERR_BAD_VALUE otherwise): 0..64 for C = 64, multiples
  *               of 4 up to 256 for C = 16, of 2 up to 128 for C = 32, 0..32 for
