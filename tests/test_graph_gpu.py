@@ -25,6 +25,7 @@ DEV = "cuda"
     (2, 4, 300, 64, torch.bfloat16, None, 64),
     (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], 64),
     (1, 2, 256, 32, torch.float32, None, 32),
+    (1, 2, 450, 128, torch.bfloat16, [200, 1, 249], 128),
 ])
 def test_forward_graph_replays_equal_eager(no_alloc, B, H, L, d, dtype, lengths, chunk):
     inps = [workloads.fwd_inputs(B, H, L, d, dtype, seed=700 + i + L, lengths=lengths) for i in range(3)]
