@@ -359,6 +359,37 @@ def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
         "roofline": {"kernel": "whole backward", "bound": "hbm", "achieved": need / (ms_bi * 1e-3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": need / (ms_bi * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "algorithmic_bytes": need}}
+    # the backward of the other bf16 workloads (automatic segmentation, as the forward)
+    res["configs"] = {}
+    for cname, make, label in (("dense_bf16", workloads.c2_bf16_dense, "B=4 H=8 L=2048 d=64"),
+                               ("packed_bf16", workloads.c3_packed, "packed T=16384 H=16 d=128")):
+        ci = make()
+        cq, ck, cv, cgq, cgk = (x.to(q.device) for x in (ci.q, ci.k, ci.v, ci.gamma_q, ci.gamma_k))
+        ccu = None if ci.cu_seqlens is None else ci.cu_seqlens.to(q.device)
+        cdout = workloads.cotangent(cq.shape, seed=5, device=str(q.device))
+        couts = (torch.empty_like(cq), torch.empty_like(ck), torch.empty_like(cv), torch.empty_like(cgq),
+                 torch.empty_like(cgk))
+
+        def run_c():
+            rla.bwd(cq, ck, cv, cgq, cgk, cdout, ccu, out=couts)
+
+        for _ in range(5):
+            run_c()
+        torch.cuda.synchronize()
+        ev.hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(steps):
+            run_c()
+        ev.hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        ms_c = ev.elapsed(0, 1) / steps
+        cB, cH, cL, cd = cq.shape
+        cneed = 7 * cd * 2 * cB * cH * cL
+        res["configs"][cname] = {
+            "workload": f"backward of the {label} bf16 forward, seeded N(0,1) cotangent",
+            "ms_per_call": ms_c, "tokens_per_s": cB * cL / (ms_c * 1e-3), "steps": steps,
+            "roofline": {"kernel": "whole backward", "bound": "hbm", "achieved": cneed / (ms_c * 1e-3) / 1e9,
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": cneed / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes": cneed}}
     return res
 
 
