@@ -73,3 +73,23 @@ def sample_rows(L: int, n_random: int, seed: int, chunk: int = 64) -> np.ndarray
         rows.update({c - 1, c, c + 1})
     rows.update(r.integers(0, L, size=n_random).tolist())
     return np.array(sorted(x for x in rows if 0 <= x < L))
+
+
+def scaled_row_err(got, ref, scale) -> float:
+    """Max over rows of ||got - ref||_inf / max(||ref_row||_inf, scale_row), ``scale`` one
+    value per row (the size of the terms a row is a difference of). A row whose reference and
+    scale are both exactly zero must be exactly zero."""
+    got, ref = f64(got), f64(ref)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    g = got.reshape(-1, got.shape[-1])
+    r = ref.reshape(-1, ref.shape[-1])
+    s = np.asarray(scale, dtype=np.float64).reshape(-1)
+    assert s.shape[0] == r.shape[0]
+    num = np.abs(g - r).max(axis=1)
+    den = np.maximum(np.abs(r).max(axis=1), s)
+    zero = den == 0
+    if (num[zero] != 0).any():
+        return float("inf")
+    if (~zero).sum() == 0:
+        return 0.0
+    return float((num[~zero] / den[~zero]).max())

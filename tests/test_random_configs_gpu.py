@@ -121,7 +121,7 @@ def _bwd_case(i):
 
 @pytest.mark.parametrize("i", range(N_BWD_CASES))
 def test_random_backward_configuration(i):
-    from test_backward_modes_gpu import _check, _run
+    from test_backward_modes_gpu import _check, _parts, _run
     c = _bwd_case(i)
     d, H, B, L = c["d"], c["H"], c["B"], c["L"]
     inp = workloads.fwd_inputs(B, H, L, d, c["dtype"], seed=c["seed"], lengths=c["lengths"])
@@ -136,4 +136,4 @@ def test_random_backward_configuration(i):
     cu_np = None if c["lengths"] is None else inp.cu_seqlens.numpy()
     ref = oracle.bwd(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.gamma_q), f64(inp.gamma_k), f64(dout), cu_np,
                      inp.eps, inp.rms_eps, inp.rope_base, causal=not c["bidir"], **kw)
-    _check(got, ref, c["dtype"], f"backward case {i}: {c}", c["bidir"])
+    _check(got, ref, c["dtype"], f"backward case {i}: {c}", c["bidir"], _parts(inp, dout, c["bidir"], **kw))
