@@ -9,6 +9,8 @@ Entry points (same names as the C ABI in include/rla2.h):
   state_from_prefix(k, v, gamma_k, cu_seqlens=None, ...)      -> rla2_state_from_prefix
   decode_step(q, k, v, positions, gamma_q, gamma_k, S, z,...) -> rla2_decode_step
   decode_step_l2(q, k, v, positions, gamma_q, gamma_k, S, A,...) -> rla2_decode_step_l2
+  bwd(q, k, v, gamma_q, gamma_k, dout, ...)                   -> rla2_bwd_chunked(_saved)
+  attention(q, k, v, gamma_q, gamma_k, ...): torch.autograd over fwd and the saved bwd
 """
 from __future__ import annotations
 
@@ -18,7 +20,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["fwd", "state_from_prefix", "decode_step", "decode_step_l2", "fwd_workspace_size",
+__all__ = ["fwd", "bwd", "attention", "feature_map", "state_from_prefix", "decode_step", "decode_step_l2",
+           "fwd_workspace_size",
            "state_from_prefix_workspace_size", "lib", "Rla2Error",
            "Rla2FlagError", "FwdDesc", "LIB_PATH", "STATUS", "workspace_flags", "set_check_flags",
            "debug_set_wait_polls"]
@@ -391,6 +394,57 @@ def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunk
     _after(workspace, n.value, "rla2_bwd_chunked")
     return dq, dk, dv, dgq, dgk
 
+
+
+class _Rla2Function(torch.autograd.Function):
+    """rla2_fwd_chunked forward; backward by rla2_bwd_chunked_saved on the forward's own
+    workspace (its states are not formed again). Marshalling only."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gamma_q, gamma_k, cu_seqlens, chunk, bidirectional, initial_S, initial_z,
+                initial_pos):
+        nbytes = fwd_workspace_size(_fwd_desc(q, cu_seqlens, chunk, 0, 1e-4, 1e-6, 10000.0, bidirectional,
+                                              initial_pos, initial_S, initial_z))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+        out = fwd(q, k, v, gamma_q, gamma_k, cu_seqlens, chunk=chunk, bidirectional=bidirectional,
+                  initial_S=initial_S, initial_z=initial_z, initial_pos=initial_pos, workspace=workspace)
+        ctx.save_for_backward(q, k, v, gamma_q, gamma_k)
+        ctx.extra = (cu_seqlens, chunk, bidirectional, initial_S, initial_z, initial_pos, workspace)
+        return out
+
+    @staticmethod
+    @torch.autograd.function.once_differentiable
+    def backward(ctx, dout):
+        q, k, v, gamma_q, gamma_k = ctx.saved_tensors
+        cu_seqlens, chunk, bidirectional, initial_S, initial_z, initial_pos, workspace = ctx.extra
+        want_dgamma = ctx.needs_input_grad[3] or ctx.needs_input_grad[4]
+        dq, dk, dv, dgq, dgk = bwd(q, k, v, gamma_q, gamma_k, dout.contiguous(), cu_seqlens, chunk=chunk,
+                                   bidirectional=bidirectional, initial_S=initial_S, initial_z=initial_z,
+                                   initial_pos=initial_pos, want_dgamma=want_dgamma, fwd_workspace=workspace)
+        ctx.extra = None  # the forward's workspace is released after its one backward
+        need = ctx.needs_input_grad
+        return (dq if need[0] else None, dk if need[1] else None, dv if need[2] else None,
+                dgq if need[3] else None, dgk if need[4] else None, None, None, None, None, None, None)
+
+
+def attention(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, bidirectional=False, initial_S=None,
+              initial_z=None, initial_pos=0):
+    """Differentiable RLA-2 layer core (Sum denominator, eps 1e-4, RMSNorm eps 1e-6, RoPE base
+    10000): ``out`` as ``fwd``, with gradients for q, k, v and the RMSNorm weights through
+    torch.autograd. The forward's workspace (segment states, RoPE tables) is kept until the
+    backward, which reads it (rla2_bwd_chunked_saved), then released; a second backward through
+    the same graph is refused by autograd as usual. ``initial_S``/``initial_z`` start the first
+    document of each row but take no gradient (the library does not form it): passing one that
+    requires grad raises."""
+    for n_, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n_, t, q.dtype)
+    _check_dev("gamma_q", gamma_q, torch.float32)
+    _check_dev("gamma_k", gamma_k, torch.float32)
+    for n_, t in (("initial_S", initial_S), ("initial_z", initial_z), ("cu_seqlens", cu_seqlens)):
+        if t is not None and t.requires_grad:
+            raise ValueError(f"{n_} takes no gradient here")
+    return _Rla2Function.apply(q, k, v, gamma_q, gamma_k, cu_seqlens, chunk, bidirectional, initial_S,
+                               initial_z, initial_pos)
 
 def feature_map(q, k, gamma_q, gamma_k, cu_seqlens=None, *, rms_eps=1e-6, rope_base=10000.0, initial_pos=0,
                 q_out=None, k_out=None, workspace=None):

@@ -246,6 +246,8 @@ def test_binding_refuses_cpu_tensors():
         rla.fwd(x, x, x, g, g)
     with pytest.raises(ValueError, match="GPU tensor"):
         rla.decode_step(x[0], x[0], x[0], torch.zeros(1, dtype=torch.int32), g, g, x, x[0, 0])
+    with pytest.raises(ValueError, match="GPU tensor"):
+        rla.attention(x.requires_grad_(True), x, x, g, g)
 
 
 def test_feature_map_error_paths():
