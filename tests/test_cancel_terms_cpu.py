@@ -1,5 +1,5 @@
 """The error scale of the bidirectional fp32 gradient bar (cancel_terms) against the oracle:
-its two parts add up to oracle.bwd's q and k gradients, and in a one-token document they
+its two parts add up to oracle.bwd's q, k and weight gradients, and in a one-token document they
 cancel to eps / den of their size, which is what the bar allows for."""
 import numpy as np
 import torch
@@ -25,18 +25,20 @@ def _inputs(lengths, init):
 def test_parts_add_up_to_the_oracle_gradient():
     for init in (False, True):
         inp, args, kw = _inputs([40, 0, 1, 23], init)
-        qn, qd, kn, kd = cancel_terms.bidir_parts(*args, inp.eps, inp.rms_eps, inp.rope_base, **kw)
+        parts = cancel_terms.bidir_parts(*args, inp.eps, inp.rms_eps, inp.rope_base, **kw)
         ref = oracle.bwd(*args, inp.eps, inp.rms_eps, inp.rope_base, causal=False, **kw)
-        for got, want in ((qn + qd, ref[0]), (kn + kd, ref[1])):
-            assert np.abs(got - want).max() <= 1e-12 * np.abs(want).max()
-        Tq, Tk = cancel_terms.bidir_part_sizes(*args, inp.eps, inp.rms_eps, inp.rope_base, **kw)
+        for (a, b), want in zip(parts, (ref[0], ref[1], ref[3], ref[4])):
+            assert np.abs(a + b - want).max() <= 1e-12 * np.abs(want).max()
+        Tq, Tk, Tgq, Tgk = cancel_terms.bidir_part_sizes(*args, inp.eps, inp.rms_eps, inp.rope_base, **kw)
         assert np.all(Tq >= 0.5 * np.abs(ref[0]).max(axis=-1))  # a row is at most the sum of its parts
         assert np.all(Tk >= 0.5 * np.abs(ref[1]).max(axis=-1))
+        assert np.all(Tgq >= 0.5 * np.abs(ref[3]).max(axis=-1))
+        assert np.all(Tgk >= 0.5 * np.abs(ref[4]).max(axis=-1))
 
 
 def test_one_token_document_parts_cancel():
     inp, args, kw = _inputs([40, 1, 23], False)
-    qn, qd, kn, kd = cancel_terms.bidir_parts(*args, inp.eps, inp.rms_eps, inp.rope_base)
+    (qn, qd), (kn, kd), _, _ = cancel_terms.bidir_parts(*args, inp.eps, inp.rms_eps, inp.rope_base)
     t = 40  # the one-token document: out = v exactly up to eps, so its gradient is eps-sized
     for a, b in ((qn, qd), (kn, kd)):
         size = np.abs(a[0, :, t]).max()
