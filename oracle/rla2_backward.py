@@ -8,7 +8,7 @@ bench's ``cpu_baseline`` leg may use it; it shares no code with the HIP path.
 the Sum denominator of §2.3; the preamble q' = ReLU(RoPE(RMSNorm(q))) of §1/§3; the
 causal, same-document key range of §4.1), and ``bwd`` differentiates it with
 autograd: the gradients of ``sum(out * dout)`` with respect to q, k, v and the two
-RMSNorm weights. ``bwd_qk_prime`` restates the layer backward the RLA page gives in
+RMSNorm weights, and optionally the initial state (S0, z0) of §4.1's scan inputs. ``bwd_qk_prime`` restates the layer backward the RLA page gives in
 §4.2 (gnum = g / (q.z + eps), scale = -r / (q.z + eps)^2 with r = g . num,
 gQ = B^T gnum + scale * z, and the suffix sums for the key and value gradients) for
 the gradients with respect to q' and k' and v, as an independent formulation that the
@@ -62,13 +62,18 @@ def fwd_torch(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps=DEFAULT_EPS, rms_e
               rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0, causal=True):
     """Differentiable closed-form forward over [B, H, L, d] (torch fp64 tensors), causal or
     bidirectional (``causal=False``: every token reads its whole document). The first
-    document of each row starts at position ``initial_pos`` and from the initial state
-    (constants here: no gradient flows to them), as the forward oracle."""
+    document of each row starts at position ``initial_pos`` and from the initial state, as
+    the forward oracle; ``initial_S`` / ``initial_z`` given as fp64 tensors that require grad
+    stay in the graph (their gradient is the sum over the rows' first documents)."""
     B, H, L, d = q.shape
     out = torch.zeros(B, H, L, d, dtype=torch.float64)
     first = first_documents(B, L, cu_seqlens)
     with_init = initial_S is not None or initial_z is not None
     S0, z0 = (torch.as_tensor(x) for x in _initial(initial_S, initial_z, H, d))
+    if isinstance(initial_S, torch.Tensor) and initial_S.requires_grad:  # a leaf of the caller's graph
+        S0 = initial_S.reshape(H, d, d)
+    if isinstance(initial_z, torch.Tensor) and initial_z.requires_grad:
+        z0 = initial_z.reshape(H, d)
     for j, (b, s0, s1) in enumerate(documents(B, L, cu_seqlens)):
         if s1 <= s0:
             continue
@@ -84,11 +89,19 @@ def fwd_torch(q, k, v, gamma_q, gamma_k, cu_seqlens=None, eps=DEFAULT_EPS, rms_e
 
 
 def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, eps=DEFAULT_EPS, rms_eps=DEFAULT_RMS_EPS,
-        rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0, causal=True):
+        rope_base=DEFAULT_ROPE_BASE, initial_S=None, initial_z=None, initial_pos=0, causal=True,
+        initial_grads=False):
     """Gradients (dq, dk, dv, dgamma_q, dgamma_k) of sum(out * dout), fp64 numpy arrays, of the
-    causal or (``causal=False``) bidirectional forward."""
+    causal or (``causal=False``) bidirectional forward. ``initial_grads``: also the gradients
+    with respect to the initial state, (..., dinitial_S [H, d, d], dinitial_z [H, d]), the
+    state taken as zero where it is absent (the same forward)."""
     leaves = [_t(x).requires_grad_(True) for x in (q, k, v, gamma_q, gamma_k)]
-    out = fwd_torch(*leaves, cu_seqlens, eps, rms_eps, rope_base, initial_S, initial_z, initial_pos, causal)
+    if initial_grads:
+        H, d = q.shape[1], q.shape[3]
+        S0, z0 = _initial(initial_S, initial_z, H, d)
+        initial_S, initial_z = _t(S0).requires_grad_(True), _t(z0).requires_grad_(True)
+        leaves += [initial_S, initial_z]
+    out = fwd_torch(*leaves[:5], cu_seqlens, eps, rms_eps, rope_base, initial_S, initial_z, initial_pos, causal)
     grads = torch.autograd.grad((out * _t(dout)).sum(), leaves, allow_unused=True)
     return tuple(np.zeros(tuple(x.shape)) if g is None else g.numpy() for g, x in zip(grads, leaves))
 

@@ -439,6 +439,12 @@ def test_backward_initial_state_is_a_continuation():
     cont = oracle.bwd(q[X], k[X], v[X], gq, gk, g[X], initial_S=S[0], initial_z=z[0], initial_pos=nP)
     for a, b2 in zip(whole[:3], cont[:3]):
         np.testing.assert_allclose(a[X], b2, rtol=1e-10, atol=1e-12)
+    # and the prefix's value rows reach X's loss only through S_P: dv_i = dS0^T k'_i there
+    dS0 = oracle.bwd(q[X], k[X], v[X], gq, gk, g[X], initial_S=S[0], initial_z=z[0], initial_pos=nP,
+                     initial_grads=True)[5]
+    for h in range(H):
+        kp = oracle.feature_map(k[0, h, :nP], gk[h], np.arange(nP))
+        np.testing.assert_allclose(whole[2][0, h, :nP], kp @ dS0[h], rtol=1e-10, atol=1e-12)
     # the forward of the differentiable oracle with an initial state equals the forward oracle
     S0, z0 = workloads.initial_state(H, d, seed=57)
     S0, z0 = S0.double().numpy(), z0.double().numpy()
@@ -448,6 +454,63 @@ def test_backward_initial_state_is_a_continuation():
     ref = oracle.fwd(q, k, v, gq, gk, cu, initial_S=S0, initial_z=z0, initial_pos=40)
     np.testing.assert_allclose(out.numpy(), ref, rtol=1e-11, atol=1e-13)
 
+
+
+def test_backward_initial_state_gradient_closed_form():
+    # out_t = q'_t S_t / (q'_t . z_t + eps) with S_t = S0 + (keys up to t, or the whole
+    # document) and z_t likewise from z0 (RLA page §4.1: the initial state enters the first
+    # document of each row only), so d out_t / d S0 = q'_t (x) e / den_t and
+    # d out_t / d z0 = -out_t q'_t^T / den_t: dS0 = sum_t q'_t g_t^T / den_t and
+    # dz0 = -sum_t (g_t . out_t) / den_t q'_t over the rows' first documents
+    r = np.random.default_rng(58)
+    H, d, pos = 2, 6, 3
+    for causal in (True, False):
+        for B, L, cu in ((2, 11, None), (1, 16, np.array([0, 5, 16])), (1, 16, np.array([0, 0, 9, 16]))):
+            q, k, v, gq, gk, _ = _rand_case(B, H, L, d, 59 + L, None)
+            g = r.normal(size=q.shape)
+            S0 = r.normal(size=(H, d, d))
+            z0 = r.uniform(0.5, 1.5, size=(H, d))
+            got = oracle.bwd(q, k, v, gq, gk, g, cu, initial_S=S0, initial_z=z0, initial_pos=pos, causal=causal,
+                             initial_grads=True)
+            out = oracle.fwd(q, k, v, gq, gk, cu, initial_S=S0, initial_z=z0, initial_pos=pos, causal=causal)
+            dS0, dz0 = np.zeros((H, d, d)), np.zeros((H, d))
+            firsts = [(b, 0, L) for b in range(B)] if cu is None else [(0, int(cu[0]), int(cu[1]))]
+            for b, s0, s1 in firsts:
+                n = s1 - s0
+                for h in range(H):
+                    qp = oracle.feature_map(q[b, h, s0:s1], gq[h], pos + np.arange(n))
+                    kp = oracle.feature_map(k[b, h, s0:s1], gk[h], pos + np.arange(n))
+                    zt = z0[h] + (np.cumsum(kp, axis=0) if causal else np.broadcast_to(kp.sum(axis=0), kp.shape))
+                    den = (qp * zt).sum(axis=1) + oracle.DEFAULT_EPS
+                    gg, oo = g[b, h, s0:s1], out[b, h, s0:s1]
+                    dS0[h] += (qp / den[:, None]).T @ gg
+                    dz0[h] -= ((gg * oo).sum(axis=1) / den) @ qp
+            np.testing.assert_allclose(got[5], dS0, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(got[6], dz0, rtol=1e-10, atol=1e-12)
+            if cu is not None and cu[1] == 0:  # an empty first document: no output reads the state
+                assert not got[5].any() and not got[6].any()
+            # without an initial state the gradients are those at S0 = 0, z0 = 0 (the same forward)
+            plain = oracle.bwd(q, k, v, gq, gk, g, cu, causal=causal, initial_grads=True)
+            zero = oracle.bwd(q, k, v, gq, gk, g, cu, initial_S=0 * S0, initial_z=0 * z0, causal=causal,
+                              initial_grads=True)
+            for a, b2 in zip(plain, zero):
+                np.testing.assert_allclose(a, b2, rtol=1e-12, atol=1e-14)
+
+
+def test_backward_initial_state_gradient_finite_differences():
+    # autograd through the initial state against central finite differences (gradcheck), dense
+    # rows (every row starts from the state) and packed documents (the first one only)
+    r = np.random.default_rng(60)
+    H, d = 2, 4
+    for cu, B, L in ((None, 2, 5), (np.array([0, 3, 7]), 1, 7)):
+        x = [torch.tensor(r.normal(size=(B, H, L, d))) for _ in range(3)]
+        gam = [torch.tensor(r.uniform(0.5, 1.5, size=(H, d))) for _ in range(2)]
+        S0 = torch.tensor(r.normal(size=(H, d, d)), requires_grad=True)
+        z0 = torch.tensor(r.uniform(0.5, 1.5, size=(H, d)), requires_grad=True)
+        for causal in (True, False):
+            fn = lambda S, z: oracle.fwd_torch(*x, *gam, cu, initial_S=S, initial_z=z, initial_pos=2,  # noqa: E731
+                                               causal=causal)
+            assert torch.autograd.gradcheck(fn, (S0, z0), eps=1e-6, atol=1e-8, rtol=1e-6)
 
 
 def test_backward_one_document_matches_autograd():
