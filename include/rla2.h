@@ -129,10 +129,22 @@ typedef enum rla2_dtype { RLA2_F32 = 0, RLA2_BF16 = 1 } rla2_dtype;
  *               [N, H, d, d] output, each document's second state after its last token
  *               (plus initial_A for the first document of each row): written by
  *               rla2_fwd_chunked and by rla2_state_from_prefix; NULL = not exported.
+ *  grad_initial_S, grad_initial_z  read by the backward calls only (the other calls
+ *               ignore them): optional DEVICE fp32 [H, d, d] and [H, d] outputs, the
+ *               gradients of the loss with respect to initial_S and initial_z (each may be
+ *               NULL = not formed; the state is taken as zero where initial_S is NULL, which
+ *               is the same forward). The initial state enters the first document of each
+ *               row (RLA page §4.1), so with g = dL/dout, den_t = q'_t . z_t + eps:
+ *               grad_initial_S[h] = sum_t q'_t g_t^T / den_t and grad_initial_z[h] =
+ *               -sum_t (g_t . out_t) / den_t q'_t over the tokens of those documents, summed
+ *               over the rows in row order (deterministic) -- the backward's reverse state
+ *               at each such document's first token. Written, not accumulated; 16-byte
+ *               aligned (RLA2_ERR_MISALIGNED) and overlapping no other buffer
+ *               (RLA2_ERR_ALIAS).
  * The number of documents N is n_docs with cu_seqlens, B without.
  * A zero-initialised descriptor tail (bidirectional = initial_pos = 0, NULL
- * initial state, denominator = RLA2_DEN_SUM, NULL initial_A and final_A) is the plain
- * causal forward.
+ * initial state, denominator = RLA2_DEN_SUM, NULL initial_A and final_A, NULL
+ * gradient outputs) is the plain causal forward.
  */
 typedef struct rla2_fwd_desc {
   int32_t B, H, L, d;
@@ -149,6 +161,8 @@ typedef struct rla2_fwd_desc {
   int32_t denominator;
   const float* initial_A;
   float* final_A;
+  float* grad_initial_S;
+  float* grad_initial_z;
 } rla2_fwd_desc;
 
 #define RLA2_DEN_SUM 0
@@ -293,7 +307,10 @@ rla2_status rla2_bwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
  * q, k, v (the forward output is not an input). bf16 or fp32 activations; the Sum
  * denominator only (RLA2_ERR_UNSUPPORTED for the L2 denominator). An initial state and
  * position offset in desc are taken into account; the gradient with respect to the initial
- * state is not formed. desc->chunk does not change the arithmetic of the backward.
+ * state goes to desc->grad_initial_S / grad_initial_z when they are set (the reverse states
+ * P, p at each first document's first token: the suffix scan's whole-document totals, summed
+ * over the rows by one more small launch). desc->chunk does not change the arithmetic of the
+ * backward.
  *  q, k, v       [B, H, L, d] dtype, the forward's inputs.
  *  gamma_q/k     [H, d] fp32.
  *  dout          [B, H, L, d] dtype, dL/dout (read).

@@ -61,7 +61,8 @@ class FwdDesc(ctypes.Structure):
                 ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
                 ("bidirectional", ctypes.c_int32), ("initial_pos", ctypes.c_int32),
                 ("initial_S", ctypes.c_void_p), ("initial_z", ctypes.c_void_p), ("denominator", ctypes.c_int32),
-                ("initial_A", ctypes.c_void_p), ("final_A", ctypes.c_void_p)]
+                ("initial_A", ctypes.c_void_p), ("final_A", ctypes.c_void_p),
+                ("grad_initial_S", ctypes.c_void_p), ("grad_initial_z", ctypes.c_void_p)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -334,7 +335,7 @@ def state_from_prefix(k, v, gamma_k, cu_seqlens=None, *, chunk=64, seg_chunks=0,
 
 def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunks=0, eps=1e-4, rms_eps=1e-6,
         rope_base=10000.0, initial_S=None, initial_z=None, initial_pos=0, want_dgamma=True, workspace=None,
-        out=None, events=None, fwd_workspace=None, bidirectional=False):
+        out=None, events=None, fwd_workspace=None, bidirectional=False, initial_state_grad=False):
     """Backward of the forward (causal, or ``bidirectional``; bf16 or fp32) for the same inputs;
     ``dout`` = dL/dout.
     Returns ``(dq, dk, dv, dgamma_q, dgamma_k)`` (the last two None unless ``want_dgamma``).
@@ -342,7 +343,10 @@ def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunk
     ctypes array of RLA2_BWD_KERNELS + 1 hipEvent_t handles (rla2_bwd_chunked_profiled).
     ``fwd_workspace``: the ``workspace`` tensor of the matching ``fwd`` call (same inputs and
     options, causal, Sum denominator), untouched since: its states are read instead of being
-    formed again (rla2_bwd_chunked_saved; bitwise the same gradients)."""
+    formed again (rla2_bwd_chunked_saved; bitwise the same gradients). ``initial_state_grad``:
+    also the gradients with respect to ``initial_S`` [H, d, d] and ``initial_z`` [H, d] (the
+    desc's grad_initial_S / grad_initial_z; a zero state where none is given), appended to the
+    result."""
     for n_, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _check_dev(n_, t, q.dtype)
         if t.shape != q.shape:
@@ -353,6 +357,11 @@ def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunk
                      initial_S, initial_z)
     if gamma_q.shape != (desc.H, desc.d) or gamma_k.shape != (desc.H, desc.d):
         raise ValueError("gamma_q and gamma_k must be [H, d]")
+    gS = gz = None
+    if initial_state_grad:
+        gS = torch.empty(desc.H, desc.d, desc.d, dtype=torch.float32, device=q.device)
+        gz = torch.empty(desc.H, desc.d, dtype=torch.float32, device=q.device)
+        desc.grad_initial_S, desc.grad_initial_z = _ptr(gS), _ptr(gz)
     if out is not None:
         dq, dk, dv, dgq, dgk = out
         for n_, t in (("dq", dq), ("dk", dk), ("dv", dv)):
@@ -392,7 +401,7 @@ def bwd(q, k, v, gamma_q, gamma_k, dout, cu_seqlens=None, *, chunk=64, seg_chunk
     if st:
         raise Rla2Error(st, "rla2_bwd_chunked")
     _after(workspace, n.value, "rla2_bwd_chunked")
-    return dq, dk, dv, dgq, dgk
+    return (dq, dk, dv, dgq, dgk) + ((gS, gz) if initial_state_grad else ())
 
 
 
@@ -409,7 +418,8 @@ class _Rla2Function(torch.autograd.Function):
         out = fwd(q, k, v, gamma_q, gamma_k, cu_seqlens, chunk=chunk, bidirectional=bidirectional,
                   initial_S=initial_S, initial_z=initial_z, initial_pos=initial_pos, workspace=workspace)
         ctx.save_for_backward(q, k, v, gamma_q, gamma_k)
-        ctx.extra = (cu_seqlens, chunk, bidirectional, initial_S, initial_z, initial_pos, workspace)
+        detach = (lambda t: None if t is None else t.detach())  # noqa: E731
+        ctx.extra = (cu_seqlens, chunk, bidirectional, detach(initial_S), detach(initial_z), initial_pos, workspace)
         return out
 
     @staticmethod
@@ -417,14 +427,17 @@ class _Rla2Function(torch.autograd.Function):
     def backward(ctx, dout):
         q, k, v, gamma_q, gamma_k = ctx.saved_tensors
         cu_seqlens, chunk, bidirectional, initial_S, initial_z, initial_pos, workspace = ctx.extra
-        want_dgamma = ctx.needs_input_grad[3] or ctx.needs_input_grad[4]
-        dq, dk, dv, dgq, dgk = bwd(q, k, v, gamma_q, gamma_k, dout.contiguous(), cu_seqlens, chunk=chunk,
-                                   bidirectional=bidirectional, initial_S=initial_S, initial_z=initial_z,
-                                   initial_pos=initial_pos, want_dgamma=want_dgamma, fwd_workspace=workspace)
-        ctx.extra = None  # the forward's workspace is released after its one backward
         need = ctx.needs_input_grad
+        want_init = need[8] or need[9]
+        res = bwd(q, k, v, gamma_q, gamma_k, dout.contiguous(), cu_seqlens, chunk=chunk,
+                  bidirectional=bidirectional, initial_S=initial_S, initial_z=initial_z, initial_pos=initial_pos,
+                  want_dgamma=need[3] or need[4], fwd_workspace=workspace, initial_state_grad=want_init)
+        dq, dk, dv, dgq, dgk = res[:5]
+        gS, gz = res[5:] if want_init else (None, None)
+        ctx.extra = None  # the forward's workspace is released after its one backward
         return (dq if need[0] else None, dk if need[1] else None, dv if need[2] else None,
-                dgq if need[3] else None, dgk if need[4] else None, None, None, None, None, None, None)
+                dgq if need[3] else None, dgk if need[4] else None, None, None, None,
+                gS if need[8] else None, gz if need[9] else None, None)
 
 
 def attention(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, bidirectional=False, initial_S=None,
@@ -433,16 +446,16 @@ def attention(q, k, v, gamma_q, gamma_k, cu_seqlens=None, *, chunk=64, bidirecti
     10000): ``out`` as ``fwd``, with gradients for q, k, v and the RMSNorm weights through
     torch.autograd. The forward's workspace (segment states, RoPE tables) is kept until the
     backward, which reads it (rla2_bwd_chunked_saved), then released; a second backward through
-    the same graph is refused by autograd as usual. ``initial_S``/``initial_z`` start the first
-    document of each row but take no gradient (the library does not form it): passing one that
-    requires grad raises."""
+    the same graph is refused by autograd as usual. ``initial_S`` [H, d, d] / ``initial_z``
+    [H, d] (fp32, together) start the first document of each row and take gradients too
+    (the desc's grad_initial_S / grad_initial_z), so a chain of segments can be trained
+    through the states it hands on."""
     for n_, t in (("q", q), ("k", k), ("v", v)):
         _check_dev(n_, t, q.dtype)
     _check_dev("gamma_q", gamma_q, torch.float32)
     _check_dev("gamma_k", gamma_k, torch.float32)
-    for n_, t in (("initial_S", initial_S), ("initial_z", initial_z), ("cu_seqlens", cu_seqlens)):
-        if t is not None and t.requires_grad:
-            raise ValueError(f"{n_} takes no gradient here")
+    if cu_seqlens is not None and cu_seqlens.requires_grad:
+        raise ValueError("cu_seqlens takes no gradient")
     return _Rla2Function.apply(q, k, v, gamma_q, gamma_k, cu_seqlens, chunk, bidirectional, initial_S,
                                initial_z, initial_pos)
 

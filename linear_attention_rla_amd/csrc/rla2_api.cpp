@@ -16,7 +16,7 @@ namespace {
 
 using rla2::Plan;
 
-constexpr int32_t kAbiVersion = 6;
+constexpr int32_t kAbiVersion = 7;
 
 // Poll bound of the MMA waves' meetings inside the warp-specialised kernels (a debug hook
 // lets tests lower it; see rla2_debug_set_wait_polls).
@@ -206,6 +206,8 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p, bool state_build = false)
   off = align_up(off + tokh * 4);
   p->off_dgpart = off;
   off = align_up(off + (size_t)p->n_seg_max * p->H * p->d * 2 * 4);
+  p->off_ginit = off;
+  off = align_up(off + (size_t)(p->packed ? 1 : p->B) * p->H * rec * 4);
   p->bytes_bwd = (p->n_docs == 0 || p->H == 0) ? 0 : off;
   return RLA2_OK;
 }
@@ -273,9 +275,11 @@ rla2_status bwd_impl(const rla2_fwd_desc* desc, const void* q, const void* k, co
   if (saved != nullptr && (saved_bytes < p.bytes || (reinterpret_cast<uintptr_t>(saved) % rla2::kAlign) != 0))
     return RLA2_ERR_WORKSPACE;
   if (misaligned({q, k, v, dout, dq, dk, dv, gamma_q, gamma_k, dgamma_q, dgamma_k, desc->initial_S,
-                  desc->initial_z}))
+                  desc->initial_z, desc->grad_initial_S, desc->grad_initial_z}))
     return RLA2_ERR_MISALIGNED;
-  const Range outs[] = {{dq, act}, {dk, act}, {dv, act}, {dgamma_q, gam}, {dgamma_k, gam}};
+  const Range outs[] = {{dq, act}, {dk, act}, {dv, act}, {dgamma_q, gam}, {dgamma_k, gam},
+                        {desc->grad_initial_S, (size_t)p.H * p.d * p.d * 4}, {desc->grad_initial_z, gam}};
+  constexpr size_t n_outs = sizeof(outs) / sizeof(outs[0]);
   const Range ws{workspace, p.bytes_bwd};
   const Range ins[] = {{q, act}, {k, act}, {v, act}, {dout, act}, {gamma_q, gam}, {gamma_k, gam},
                        {desc->cu_seqlens, ((size_t)p.n_docs + 1) * 4},
@@ -286,9 +290,9 @@ rla2_status bwd_impl(const rla2_fwd_desc* desc, const void* q, const void* k, co
     for (const Range& o : outs)
       if (overlap(o, r)) return RLA2_ERR_ALIAS;
   }
-  for (size_t i = 0; i < 5; ++i) {
+  for (size_t i = 0; i < n_outs; ++i) {
     if (overlap(outs[i], ws)) return RLA2_ERR_ALIAS;
-    for (size_t j = i + 1; j < 5; ++j)
+    for (size_t j = i + 1; j < n_outs; ++j)
       if (overlap(outs[i], outs[j])) return RLA2_ERR_ALIAS;
   }
   if (p.packed && validate_mode() == 1) {
@@ -299,7 +303,8 @@ rla2_status bwd_impl(const rla2_fwd_desc* desc, const void* q, const void* k, co
   rla2::FwdArgs a{desc->cu_seqlens, q, k, v, gamma_q, gamma_k, nullptr, nullptr, nullptr,
                   desc->initial_S, desc->initial_z, desc->eps, desc->rms_eps, desc->rope_base,
                   static_cast<char*>(workspace)};
-  rla2::BwdArgs b{dout, dq, dk, dv, dgamma_q, dgamma_k, static_cast<const char*>(saved)};
+  rla2::BwdArgs b{dout, dq, dk, dv, dgamma_q, dgamma_k, static_cast<const char*>(saved), desc->grad_initial_S,
+                  desc->grad_initial_z};
   return finish(rla2::launch_backward(p, a, b, stream, events));
 }
 

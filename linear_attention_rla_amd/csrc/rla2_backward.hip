@@ -205,7 +205,8 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const float* __restrict__ gamma_q,
     const int32_t* __restrict__ tab, const int32_t* __restrict__ nseg, const float2* __restrict__ rope_lo,
     const float2* __restrict__ rope_hi, const float* __restrict__ den, const float* __restrict__ gd,
-    float* __restrict__ pstates, int H, int L, float rms_eps, const uint32_t* __restrict__ hdr, TabLimits lim) {
+    float* __restrict__ pstates, int H, int L, float rms_eps, const uint32_t* __restrict__ hdr, TabLimits lim,
+    int first_too) {
   using G = Geo<true, D>;
   using R = Raw<true, D>;
   constexpr int BUF = kChunk * G::ROWP;
@@ -220,9 +221,11 @@ __global__ __launch_bounds__(256, 2) void bwd_pstate_kernel(
   if (!bwd_go(hdr) || seg >= *nseg) return;
   const SegInfo si = read_seg_clamped(tab, seg, L, lim);
   if (si.len == 0) return;  // only a corrupted table has empty segments
-  // causal: a document's first segment is skipped (no earlier segment reads its total);
-  // bidirectional (ALL): every segment's total goes into the document's
-  if (!ALL && si.pos0 == 0) return;
+  // causal: a document's first segment is skipped (no earlier segment reads its total) unless
+  // first_too asks for the whole-document totals of the documents that start from the initial
+  // state (each row's segment at token 0); bidirectional (ALL): every segment's total goes into
+  // the document's
+  if (!ALL && si.pos0 == 0 && !(first_too && si.start == 0)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = __builtin_amdgcn_readfirstlane((si.len + kChunk - 1) / kChunk);
@@ -2080,8 +2083,11 @@ hipError_t run_backward_generic(const Plan& p, const FwdArgs& a, const BwdArgs& 
     for (int i = 1; i < 3; ++i) mark(i);
   }
   const char* fw = b.saved != nullptr ? b.saved : a.ws;
+  // the whole-document reverse totals of the documents that start from the initial state
+  float* ginit = b.ginit_S != nullptr || b.ginit_z != nullptr ? reinterpret_cast<float*>(a.ws + p.off_ginit) : nullptr;
   if (p.n_seg_max == 0) {
     for (int i = 3; i <= kNumBwdKernels; ++i) mark(i);
+    if (ginit != nullptr) return launch_initial_grad(p, ginit, b, reinterpret_cast<const uint32_t*>(a.ws), s);
     return hipGetLastError();
   }
   uint32_t* hdr = reinterpret_cast<uint32_t*>(a.ws);
@@ -2107,8 +2113,12 @@ hipError_t run_backward_generic(const Plan& p, const FwdArgs& a, const BwdArgs& 
                      static_cast<const uint32_t*>(hdr), lim);
   mark(4);  // the reverse-state totals come from the dq kernel
   mark(5);
-  e = launch_scan_records(p, fw, pstates, CAUSAL ? SCAN_SUFFIX : SCAN_TOTAL, hdr, s);
+  e = launch_scan_records(p, fw, pstates, CAUSAL ? SCAN_SUFFIX : SCAN_TOTAL, hdr, s, ginit);
   if (e != hipSuccess) return e;
+  if (ginit != nullptr) {
+    e = launch_initial_grad(p, ginit, b, hdr, s);
+    if (e != hipSuccess) return e;
+  }
   mark(6);
   hipLaunchKernelGGL((gbwd_dkv_kernel<BF, D, CAUSAL>), grid, dim3(NT), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo,
                      rhi, static_cast<const float*>(pstates), static_cast<const float*>(den),
@@ -2145,8 +2155,11 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
   uint32_t* hdr = reinterpret_cast<uint32_t*>(a.ws);
   const TabLimits lim{p.packed ? 1 : p.B, p.seg_len, p.n_hi + p.hi_off};
   const char* fw = b.saved != nullptr ? b.saved : a.ws;
+  // the whole-document reverse totals of the documents that start from the initial state
+  float* ginit = b.ginit_S != nullptr || b.ginit_z != nullptr ? reinterpret_cast<float*>(a.ws + p.off_ginit) : nullptr;
   if (p.n_seg_max == 0) {
     for (int i = 3; i <= kNumBwdKernels; ++i) mark(i);
+    if (ginit != nullptr) return launch_initial_grad(p, ginit, b, reinterpret_cast<const uint32_t*>(a.ws), s);
     return hipGetLastError();
   }
   const int32_t* tab = reinterpret_cast<const int32_t*>(fw + p.off_tab);
@@ -2170,10 +2183,14 @@ hipError_t run_backward(const Plan& p, const FwdArgs& a, const BwdArgs& b, hipSt
                      p.wait_polls, lim);
   mark(4);
   hipLaunchKernelGGL((bwd_pstate_kernel<D, BIDIR>), grid, dim3(256), 0, s, q, g, a.gq, tab, nseg, rlo, rhi, den, gd,
-                     pstates, p.H, p.L, a.rms_eps, hdr, lim);
+                     pstates, p.H, p.L, a.rms_eps, hdr, lim, ginit != nullptr ? 1 : 0);
   mark(5);
-  e = launch_scan_records(p, fw, pstates, BIDIR ? SCAN_TOTAL : SCAN_SUFFIX, hdr, s);
+  e = launch_scan_records(p, fw, pstates, BIDIR ? SCAN_TOTAL : SCAN_SUFFIX, hdr, s, ginit);
   if (e != hipSuccess) return e;
+  if (ginit != nullptr) {
+    e = launch_initial_grad(p, ginit, b, hdr, s);
+    if (e != hipSuccess) return e;
+  }
   mark(6);
   hipLaunchKernelGGL((bwd_dkv_ws_kernel<D, BIDIR>), grid, dim3(512), 0, s, q, k, v, g, a.gq, a.gk, tab, nseg, rlo, rhi,
                      pstates, den, gd, bd, static_cast<uint16_t*>(b.dk), static_cast<uint16_t*>(b.dv), dgp, p.H, p.L,

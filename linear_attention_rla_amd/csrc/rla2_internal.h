@@ -62,6 +62,9 @@ struct Plan {
   // weight on its own key per token-head; per-(segment, head) partial RMSNorm-weight
   // gradients of q and k
   size_t off_pstates, off_den, off_gd, off_bd, off_dgpart;
+  // backward: the reverse-state totals of the documents that start from the initial state
+  // (one per row; packed: one), row-major [rows][H][d][d] then [rows][H][d]
+  size_t off_ginit;
   size_t bytes_bwd;    // total backward workspace bytes
   uint32_t wait_polls; // poll bound of the MMA waves' meetings (rla2_debug_set_wait_polls)
 };
@@ -101,6 +104,8 @@ struct BwdArgs {
   float *dgamma_q, *dgamma_k;  // written, [H, d] (null: not formed)
   const char* saved;           // the matching causal forward's workspace (segment table, RoPE
                                // tables, prefix records), or null: the state pass runs again
+  float *ginit_S, *ginit_z;    // written, [H, d, d] and [H, d]: the gradient with respect to the
+                               // initial state (null: not formed)
 };
 
 // prep + chunk state + a scan of the records in mode `mode` (what the backward needs of the
@@ -108,9 +113,14 @@ struct BwdArgs {
 // events 0..2 before the three launches).
 hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t* ev, int mode);
 // A scan of a record set over the segments of each document (mode SCAN_SUFFIX or SCAN_TOTAL;
-// no initial state, no export); go_hdr: null, or the header whose HDR_GO must be set for the
-// scan to run.
+// no initial state); go_hdr: null, or the header whose HDR_GO must be set for the scan to run.
+// `totals` (null: none) receives the whole-document totals of the documents that start from
+// the initial state, row-major, laid out as at Plan::off_ginit.
 hipError_t launch_scan_records(const Plan& p, const char* ws, float* states, int mode, const uint32_t* go_hdr,
+                               hipStream_t s, float* totals = nullptr);
+// The gradient with respect to the initial state: the row sums (in row order) of the totals
+// launch_scan_records exported, into b.ginit_S / b.ginit_z.
+hipError_t launch_initial_grad(const Plan& p, const float* totals, const struct BwdArgs& b, const uint32_t* go_hdr,
                                hipStream_t s);
 // The saved backward's set-up launch: compares the stamp in fwd_ws's header with
 // make_stamp(p, mode) and the checksum of cu, and writes ws's header (flags, HDR_GO).

@@ -500,14 +500,18 @@ __global__ __launch_bounds__(512, 1) void chunk_state_l2_kernel(
 // bidirectional forward), SCAN_NONE leaves the records alone (the state build). The
 // inclusive end is the document's final state. SCAN_SUFFIX walks the segments from the
 // last to the first and replaces each total by the sum over the later segments of its
-// document (the reverse states of the backward; no initial state, no final export).
+// document (the reverse states of the backward; no initial state). The export of the
+// inclusive end goes to every document's own slot of final_S / final_z, or, with
+// export_first, only for the documents that start from the initial state, one slot per row
+// (the backward's gradient with respect to the initial state: the whole document's reverse
+// state).
 
 __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ states, const int32_t* __restrict__ docoff,
                                                          int H, int D, int n_tiles, int mode,
                                                          float* __restrict__ final_S, float* __restrict__ final_z,
                                                          const float* __restrict__ init_S,
                                                          const float* __restrict__ init_z, int init_all,
-                                                         const uint32_t* __restrict__ go_hdr) {
+                                                         int export_first, const uint32_t* __restrict__ go_hdr) {
   if (go_hdr != nullptr && !bwd_go(go_hdr)) return;  // the backward's reverse scan after a failed check
   const int doc = blockIdx.x / n_tiles, tile = blockIdx.x % n_tiles, h = blockIdx.y;
   const int R4 = (D * D + D) / 4;
@@ -524,6 +528,19 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
     col = w * (D / NW) + 16 * ct + ln % 16;
   }
   const int s0 = docoff[doc], s1 = docoff[doc + 1];
+  const bool exp = (final_S != nullptr || final_z != nullptr) && (!export_first || init_all || doc == 0);
+  const int xdoc = export_first && !init_all ? 0 : doc;  // the export slot
+  auto put_end = [&](float4 r) {
+    if (final_S != nullptr && e < D * D) {  // fragment-native record -> row-major [d][d]
+      float* dst = final_S + ((size_t)xdoc * H + h) * D * D + (size_t)row * D + col;
+      dst[0] = r.x;
+      dst[D] = r.y;
+      dst[2 * D] = r.z;
+      dst[3 * D] = r.w;
+    }
+    if (final_z != nullptr && e >= D * D)
+      *reinterpret_cast<float4*>(final_z + ((size_t)xdoc * H + h) * D + (e - D * D)) = r;
+  };
   float4* st = reinterpret_cast<float4*>(states);
   float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
   if (init_S != nullptr && (init_all || doc == 0)) {
@@ -540,9 +557,9 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
       const int cnt = min(kBatch, s - s0 + 1);
       float4 val[kBatch];
 #pragma unroll
-      for (int j = 0; j < kBatch; ++j) {  // the first record's total is never needed (it may be unset)
+      for (int j = 0; j < kBatch; ++j) {  // the first record's total is needed for the export only
         val[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j < cnt && s - j > s0) val[j] = st[((size_t)(s - j) * H + h) * R4 + e4];
+        if (j < cnt && (s - j > s0 || exp)) val[j] = st[((size_t)(s - j) * H + h) * R4 + e4];
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
@@ -555,6 +572,7 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
         }
       }
     }
+    if (exp) put_end(run);
     return;
   }
   // the prefix mode without an export never needs the last record's total (it may be unset)
@@ -580,15 +598,26 @@ __global__ __launch_bounds__(256) void state_scan_kernel(float* __restrict__ sta
   }
   if (mode == SCAN_TOTAL)
     for (int s = s0; s < s1; ++s) st[((size_t)s * H + h) * R4 + e4] = run;
-  if (final_S != nullptr && e < D * D) {  // fragment-native record -> row-major [d][d]
-    float* dst = final_S + ((size_t)doc * H + h) * D * D + (size_t)row * D + col;
-    dst[0] = run.x;
-    dst[D] = run.y;
-    dst[2 * D] = run.z;
-    dst[3 * D] = run.w;
+  if (exp) put_end(run);
+}
+
+// The gradient with respect to the initial state: per element of [H][d][d] and [H][d], the
+// sum over the rows (in row order) of the totals the scan exported with export_first.
+__global__ __launch_bounds__(256) void initial_grad_kernel(const float* __restrict__ totals, int rows, int H, int D,
+                                                           float* __restrict__ gS, float* __restrict__ gz,
+                                                           const uint32_t* __restrict__ go_hdr) {
+  if (go_hdr != nullptr && !bwd_go(go_hdr)) return;
+  const size_t nS = (size_t)H * D * D, nz = (size_t)H * D;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  float acc = 0.f;
+  if (i < nS) {
+    for (int r = 0; r < rows; ++r) acc += totals[(size_t)r * nS + i];
+    if (gS != nullptr) gS[i] = acc;
+  } else if (i < nS + nz) {
+    const float* tz = totals + (size_t)rows * nS;
+    for (int r = 0; r < rows; ++r) acc += tz[(size_t)r * nz + (i - nS)];
+    if (gz != nullptr) gz[i - nS] = acc;
   }
-  if (final_z != nullptr && e >= D * D)
-    *reinterpret_cast<float4*>(final_z + ((size_t)doc * H + h) * D + (e - D * D)) = run;
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1175,7 +1204,6 @@ __global__ __launch_bounds__(512, 1) void chunk_out_ws_kernel(
   static_assert(!(L2 && C == 128), "chunks of 128 tokens with the L2 denominator run the generic kernel");
   using G = Geo<true, D>;
   using St = uint16_t;
-  using EL = Elem<true>;
   using R = Raw<true, D>;
   constexpr int BUF = kChunk * G::ROWP;  // elements of one V or output buffer
   // Q' and K' rows at a pitch of D + 16: the 16-byte row-fragment reads (lds_frag_c) and the
@@ -2313,13 +2341,13 @@ hipError_t run_states(const Plan& p, const FwdArgs& a, hipStream_t s, hipEvent_t
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
   if (want_final || (mode != SCAN_NONE && p.n_seg_max > 0)) {
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
-                       n_tiles, mode, a.final_S, a.final_z, a.init_S, a.init_z, p.packed ? 0 : 1,
+                       n_tiles, mode, a.final_S, a.final_z, a.init_S, a.init_z, p.packed ? 0 : 1, 0,
                        static_cast<const uint32_t*>(nullptr));
   }
   if (l2 && (a.final_A != nullptr || (mode != SCAN_NONE && p.n_seg_max > 0))) {  // A the same way, from A0
     hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, astates, docoff, p.H, D,
                        n_tiles, mode, a.final_A, (float*)nullptr, a.init_A, (const float*)nullptr,
-                       p.packed ? 0 : 1, static_cast<const uint32_t*>(nullptr));
+                       p.packed ? 0 : 1, 0, static_cast<const uint32_t*>(nullptr));
   }
   return hipGetLastError();
 }
@@ -2454,13 +2482,24 @@ hipError_t launch_fwd_states(const Plan& p, const FwdArgs& a, hipStream_t s, hip
 }
 
 hipError_t launch_scan_records(const Plan& p, const char* ws, float* states, int mode, const uint32_t* go_hdr,
-                               hipStream_t s) {
+                               hipStream_t s, float* totals) {
   const int32_t* docoff = reinterpret_cast<const int32_t*>(ws + p.off_docoff);
   const int D = p.d;
   const int n_tiles = ((D * D + D) / 4 + 255) / 256;
+  const int rows = p.packed ? 1 : p.B;
+  float* tz = totals != nullptr ? totals + (size_t)rows * p.H * D * D : nullptr;
   hipLaunchKernelGGL(state_scan_kernel, dim3(p.n_docs * n_tiles, p.H), dim3(256), 0, s, states, docoff, p.H, D,
-                     n_tiles, mode, (float*)nullptr, (float*)nullptr, (const float*)nullptr,
-                     (const float*)nullptr, 0, go_hdr);
+                     n_tiles, mode, totals, tz, (const float*)nullptr, (const float*)nullptr, p.packed ? 0 : 1,
+                     totals != nullptr ? 1 : 0, go_hdr);
+  return hipGetLastError();
+}
+
+hipError_t launch_initial_grad(const Plan& p, const float* totals, const BwdArgs& b, const uint32_t* go_hdr,
+                               hipStream_t s) {
+  const size_t n = (size_t)p.H * p.d * (p.d + 1);
+  const int rows = p.n_seg_max > 0 ? (p.packed ? 1 : p.B) : 0;  // no segments: no token reads the state
+  hipLaunchKernelGGL(initial_grad_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, totals, rows, p.H, p.d,
+                     b.ginit_S, b.ginit_z, go_hdr);
   return hipGetLastError();
 }
 

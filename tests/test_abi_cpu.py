@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = rla.lib()
-    assert L.rla2_abi_version() == 6
+    assert L.rla2_abi_version() == 7
     for code, name in rla.STATUS.items():
         assert L.rla2_status_string(code).decode().startswith(name)
     assert L.rla2_status_string(99).decode() == "RLA2_ERR_UNKNOWN"
@@ -304,6 +304,12 @@ def test_backward_error_paths():
     assert call(dv=A + 328 * MB) == ALIAS                 # dv over dq
     assert call(dgk=A + 192 * MB) == ALIAS                # dgamma_k over gamma_q
     assert call(dout=A + 1024 * MB) == ALIAS              # an input inside the workspace
+    # the gradient with respect to the initial state: outputs like the others
+    assert call(d=desc(grad_initial_S=A + 196 * MB + 4)) == MISAL
+    assert call(d=desc(grad_initial_z=A + 328 * MB)) == ALIAS         # over dq
+    assert call(d=desc(grad_initial_S=A + 196 * MB, grad_initial_z=A + 196 * MB + 64)) == ALIAS  # each other
+    assert call(d=desc(grad_initial_S=A + 1024 * MB)) == ALIAS        # inside the workspace
+    assert call(d=desc(grad_initial_S=A, grad_initial_z=A + 196 * MB)) == ALIAS  # over q
 
 
 def test_grid_sizes_that_do_not_fit_a_dispatch():

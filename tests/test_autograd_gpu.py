@@ -3,7 +3,8 @@ rla2_bwd_chunked_saved on the forward's workspace) against the fp64 oracle: the 
 forward and the gradients of q, k, v and both RMSNorm weights (RLA page §4.2 backward of the
 layer), to the same bars as the direct backward calls; bitwise equality with rla2_bwd_chunked
 (states formed again) for the same cotangent; only the requested gradients are formed; a
-non-contiguous cotangent (the gradient of a sum) is taken as its values.
+non-contiguous cotangent (the gradient of a sum) is taken as its values. The gradients of the
+initial state through attention() are checked with the rest of that gradient.
 """
 import pytest
 import torch
@@ -82,10 +83,3 @@ def test_only_requested_gradients_and_sum_cotangent():
         loss.backward()
         loss.backward()
 
-
-def test_refuses_gradient_of_initial_state():
-    inp = workloads.fwd_inputs(1, 1, 64, 32, torch.bfloat16, seed=4800)
-    S0, z0 = workloads.initial_state(1, 32, seed=4801, scale=0.1)
-    args = [x.to(DEV) for x in (inp.q, inp.k, inp.v, inp.gamma_q, inp.gamma_k)]
-    with pytest.raises(ValueError):
-        rla.attention(*args, initial_S=S0.to(DEV).requires_grad_(True), initial_z=z0.to(DEV))
