@@ -5,7 +5,8 @@ accepts: head dim, dtype, chunk size (16, 32, 64, 128), denominator (Sum or L2),
 bidirectional, dense rows or packed documents (with empty and one-token documents and lengths
 around the 64-token blocks and 128-token chunks), automatic or explicit segment length, and an
 initial state at a position offset. Every output row is held to the dtype's bar, exact zeros
-stay exact, and the exported final states are checked too. The cases are fixed (seeded), so a
+stay exact, and the exported final states are checked too; the backward cases with an initial
+state also check its gradient. The cases are fixed (seeded), so a
 failure names a reproducible configuration.
 """
 import numpy as np
@@ -135,5 +136,19 @@ def test_random_backward_configuration(i):
     got = _run(inp, dout, c["bidir"], c["seg_chunks"], S0, z0, c["pos"])
     cu_np = None if c["lengths"] is None else inp.cu_seqlens.numpy()
     ref = oracle.bwd(f64(inp.q), f64(inp.k), f64(inp.v), f64(inp.gamma_q), f64(inp.gamma_k), f64(dout), cu_np,
-                     inp.eps, inp.rms_eps, inp.rope_base, causal=not c["bidir"], **kw)
-    _check(got, ref, c["dtype"], f"backward case {i}: {c}", c["bidir"], _parts(inp, dout, c["bidir"], **kw))
+                     inp.eps, inp.rms_eps, inp.rope_base, causal=not c["bidir"], initial_grads=True, **kw)
+    _check(got, ref[:5], c["dtype"], f"backward case {i}: {c}", c["bidir"], _parts(inp, dout, c["bidir"], **kw))
+    if c["init"]:  # the initial state's gradient as well; the other gradients are the same bits
+        cu = None if c["lengths"] is None else inp.cu_seqlens.to(DEV)
+        q, k, v, gq, gk = (x.to(DEV) for x in (inp.q, inp.k, inp.v, inp.gamma_q, inp.gamma_k))
+        full = rla.bwd(q, k, v, gq, gk, dout.to(DEV), cu, seg_chunks=c["seg_chunks"], initial_S=S0, initial_z=z0,
+                       initial_pos=c["pos"], bidirectional=c["bidir"], initial_state_grad=True)
+        torch.cuda.synchronize()
+        for a, b in zip(full[:5], got):
+            assert torch.equal(a, b)
+        tol = TOL_F32 if c["dtype"] == torch.float32 else TOL_BF16
+        empty_first = c["lengths"] is not None and c["lengths"][0] == 0
+        if empty_first:
+            assert not full[5].any() and not full[6].any()
+        else:
+            assert mat_rel_err(full[5], ref[5]) <= tol and mat_rel_err(full[6], ref[6], 1) <= tol
