@@ -292,7 +292,8 @@ rla2_status rla2_state_from_prefix(const rla2_fwd_desc* desc, const void* k, con
                                    const float* gamma_k, float* S, float* z, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes rla2_bwd_chunked needs for `desc`. */
+/* Workspace bytes rla2_bwd_chunked needs for `desc` (more when desc->grad_initial_S or
+ * grad_initial_z is set: one whole-document reverse total per row). */
 rla2_status rla2_bwd_workspace_size(const rla2_fwd_desc* desc, size_t* bytes);
 
 /*

@@ -206,8 +206,9 @@ rla2_status plan_desc(const rla2_fwd_desc* d, Plan* p, bool state_build = false)
   off = align_up(off + tokh * 4);
   p->off_dgpart = off;
   off = align_up(off + (size_t)p->n_seg_max * p->H * p->d * 2 * 4);
-  p->off_ginit = off;
-  off = align_up(off + (size_t)(p->packed ? 1 : p->B) * p->H * rec * 4);
+  p->off_ginit = off;  // only when the backward is asked for the initial state's gradient
+  if (d->grad_initial_S != nullptr || d->grad_initial_z != nullptr)
+    off = align_up(off + (size_t)(p->packed ? 1 : p->B) * p->H * rec * 4);
   p->bytes_bwd = (p->n_docs == 0 || p->H == 0) ? 0 : off;
   return RLA2_OK;
 }

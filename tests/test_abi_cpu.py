@@ -304,7 +304,13 @@ def test_backward_error_paths():
     assert call(dv=A + 328 * MB) == ALIAS                 # dv over dq
     assert call(dgk=A + 192 * MB) == ALIAS                # dgamma_k over gamma_q
     assert call(dout=A + 1024 * MB) == ALIAS              # an input inside the workspace
-    # the gradient with respect to the initial state: outputs like the others
+    # the gradient with respect to the initial state: outputs like the others; its workspace
+    # (one whole-document total of d*d + d floats per row and head) only when asked for
+    more = ctypes.c_size_t(0)
+    assert L.rla2_bwd_workspace_size(ctypes.byref(desc()), ctypes.byref(n)) == OK
+    assert L.rla2_bwd_workspace_size(ctypes.byref(desc(grad_initial_z=A)), ctypes.byref(more)) == OK
+    assert 2 * 4 * (64 * 64 + 64) * 4 <= more.value - n.value < 2 * 4 * (64 * 64 + 64) * 4 + 512
+    assert call(d=desc(grad_initial_S=A + 196 * MB), ws_bytes=n.value) == WS  # sized without it
     assert call(d=desc(grad_initial_S=A + 196 * MB + 4)) == MISAL
     assert call(d=desc(grad_initial_z=A + 328 * MB)) == ALIAS         # over dq
     assert call(d=desc(grad_initial_S=A + 196 * MB, grad_initial_z=A + 196 * MB + 64)) == ALIAS  # each other
