@@ -99,3 +99,46 @@ def test_backward_graph_replays_equal_eager(B, H, L, d, dtype, lengths, bidir):
                 assert torch.equal(x, y), f"replay with inputs {i}: {n_}"
     finally:
         rla.set_check_flags(prev)
+
+
+@pytest.mark.parametrize("B,H,L,d,dtype,lengths,bidir", [
+    (2, 2, 300, 64, torch.bfloat16, None, False),
+    (1, 2, 250, 128, torch.bfloat16, [70, 0, 1, 179], True),
+    (1, 2, 190, 32, torch.float32, [129, 61], False),
+])
+def test_backward_with_initial_state_gradient_graph_replays_equal_eager(B, H, L, d, dtype, lengths, bidir):
+    # the backward that also forms the initial state's gradient (its row-sum launch included),
+    # captured once and replayed with new inputs, cotangent and initial state: every output of
+    # every replay equals an eager call bitwise
+    inps = [workloads.fwd_inputs(B, H, L, d, dtype, seed=870 + i + L, lengths=lengths) for i in range(3)]
+    douts = [workloads.cotangent(inps[0].q.shape, seed=880 + i).to(dtype) for i in range(3)]
+    states = [workloads.initial_state(H, d, seed=890 + i, scale=0.1) for i in range(3)]
+    q, k, v = (x.to(DEV) for x in (inps[0].q, inps[0].k, inps[0].v))
+    g = douts[0].to(DEV)
+    S0, z0 = (x.to(DEV) for x in states[0])
+    gq, gk = inps[0].gamma_q.to(DEV), inps[0].gamma_k.to(DEV)
+    cu = None if lengths is None else inps[0].cu_seqlens.to(DEV)
+    outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(gq), torch.empty_like(gk))
+    ws = torch.empty(1 << 26, dtype=torch.uint8, device=DEV)  # more than any of these calls needs
+    kw = dict(initial_S=S0, initial_z=z0, initial_pos=33, bidirectional=bidir, initial_state_grad=True)
+    prev = rla.set_check_flags(False)  # reading the flags synchronises the stream: not inside a capture
+    try:
+        run = lambda: rla.bwd(q, k, v, gq, gk, g, cu, out=outs, workspace=ws, **kw)  # noqa: E731
+        run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            captured = run()  # its two initial-state gradients live in the graph's memory pool
+        for i in (1, 2, 0, 1):
+            for dst, src in ((q, inps[i].q), (k, inps[i].k), (v, inps[i].v), (g, douts[i]), (S0, states[i][0]),
+                             (z0, states[i][1])):
+                dst.copy_(src)
+            graph.replay()
+            torch.cuda.synchronize()
+            got = [t.clone() for t in captured]
+            ref = rla.bwd(q, k, v, gq, gk, g, cu, **kw)  # eager, its own buffers
+            torch.cuda.synchronize()
+            for n_, x, y in zip(("dq", "dk", "dv", "dgamma_q", "dgamma_k", "dS0", "dz0"), got, ref):
+                assert torch.equal(x, y), f"replay with inputs {i}: {n_}"
+    finally:
+        rla.set_check_flags(prev)
