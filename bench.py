@@ -322,6 +322,28 @@ def time_backward(args, rla, torch, workloads, stream, q, k, v, gq, gk):
     ms_saved = ev.elapsed(0, 1) / steps
     res["with_forward_states"] = {"ms_per_call": ms_saved, "tokens_per_s": B * L / (ms_saved * 1e-3),
                                   "steps": steps, "note": "states read from the forward's workspace"}
+    # the same, also forming the gradient with respect to the initial state (here a zero state)
+    gdesc = rla.make_desc(B, H, L, d, rla.BF16)
+    gdesc.grad_initial_z = 1  # any non-null pointer: the size call only sees that it is asked for
+    ng = ctypes.c_size_t(0)
+    rla.lib().rla2_bwd_workspace_size(ctypes.byref(gdesc), ctypes.byref(ng))
+    wsg = torch.empty(max(ng.value, 1), dtype=torch.uint8, device=q.device)
+
+    def run_init_grad():
+        rla.bwd(q, k, v, gq, gk, dout, out=outs, workspace=wsg, fwd_workspace=fws, initial_state_grad=True)
+
+    for _ in range(3):
+        run_init_grad()
+    torch.cuda.synchronize()
+    ev.hip.hipEventRecord(ev.arr[0], ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        run_init_grad()
+    ev.hip.hipEventRecord(ev.arr[1], ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    ms_ig = ev.elapsed(0, 1) / steps
+    res["with_forward_states"]["with_initial_state_grad"] = {
+        "ms_per_call": ms_ig, "steps": steps,
+        "note": "also dL/dinitial_S and dL/dinitial_z (each row's first segment total, its export and row sum)"}
     # the bidirectional mode's backward (every token reads its document's whole states)
     bdesc = rla.make_desc(B, H, L, d, rla.BF16, bidirectional=True)
     nb = ctypes.c_size_t(0)
